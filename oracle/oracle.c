@@ -1,0 +1,203 @@
+/*
+ * CPU oracle for the MoE expert-parallel layout / dispatch / combine path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. It shares no code with the GPU path
+ * and must never be used as a fallback for it.
+ *
+ * Plain, single-threaded loops that write out the definitions:
+ *
+ *  - layout: from the get_dispatch_layout API page (sgl-kernel-npu deep_ep
+ *    docs), sections "Parameters" and "Return Values": topk_idx is int64
+ *    [num_tokens, num_topk]; num_tokens_per_rank is int32 [num_ranks], the
+ *    number of tokens assigned to each rank; num_tokens_per_expert is int32
+ *    [num_experts], the number of tokens each expert receives;
+ *    is_token_in_rank is bool [num_tokens, num_ranks]. Section "Notes":
+ *    num_experts must divide evenly over the ranks.
+ *  - expert -> rank map: DeepEP legacy test analysis page, low-latency
+ *    per-expert check excerpt: local expert i of rank r has global id
+ *    r * num_local_experts + i, i.e. contiguous blocks, rank(e) = e / L.
+ *  - "-1 means not selected": DeepEP Python interface notes ("4 Python接口"),
+ *    section "Dispatch API", input parameter topk_idx.
+ *  - expert_alignment: same section; per-expert receive counts are rounded up
+ *    to a multiple of it (default 1).
+ *  - dispatch moves each token's row to the receivers of its selected experts
+ *    (same page, opening paragraph of "Dispatch API"); this oracle's receive
+ *    buffer holds one contiguous segment per expert, segments in ascending
+ *    expert id (so rank-major, local-expert-minor, like the low-latency
+ *    packed per-local-expert buffers), rows inside a segment in ascending
+ *    (token, slot) order. recv_src_idx maps a received row back to its token,
+ *    the role the handle's receive-index tensor plays on the legacy test
+ *    analysis page ("legacy.py" handle excerpt).
+ *  - combine: legacy test analysis page, low-latency combine check excerpt:
+ *    the combined row is x scaled by the sum of the token's weights with
+ *    unselected (-1) slots masked to 0; for general expert outputs y that is
+ *    out[t] = sum over selected k of w[t,k] * y[row of (t,k)].
+ *    The sum is formed in double: each product of an fp32 weight and a bf16
+ *    value is exact in double, and the sum of at most 16 of them is within
+ *    about 2^-49 of the terms' magnitude, far below bf16 spacing (2^-8
+ *    relative). It is then rounded once to the nearest bf16, ties to even.
+ *
+ * Where the pages are silent the readings are:
+ *  - a slot counts once per slot, so a token that repeats an expert sends two
+ *    rows to it (the second ordered after the first);
+ *  - num_tokens_per_rank counts distinct tokens (column sums of
+ *    is_token_in_rank);
+ *  - the row order inside a segment is ascending (token, slot);
+ *  - padding rows (alignment) and rows past the data carry recv_src_idx = -1
+ *    and their contents are unspecified;
+ *  - num_tokens = 0 is allowed and gives all-zero counts.
+ *
+ * Status: 0 ok, -1 invalid argument (size or index out of range), -2 capacity
+ * too small.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL -1
+#define ORACLE_ECAPACITY -2
+
+/* Checks of the sizes named on the get_dispatch_layout API page:
+ * num_topk in [1,16], num_experts in [1,512], num_ranks at most 384,
+ * num_experts divisible by num_ranks; every topk_idx entry in [-1, E). */
+static int check_routing(const int64_t* idx, int64_t T, int K, int E, int R) {
+    if (T < 0 || K < 1 || K > 16 || E < 1 || E > 512 || R < 1 || R > 384 || E % R != 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < T * (int64_t)K; ++i)
+        if (idx[i] < -1 || idx[i] >= E) return ORACLE_EINVAL;
+    return ORACLE_OK;
+}
+
+int oracle_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R,
+                  int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank) {
+    int rc = check_routing(topk_idx, T, K, E, R);
+    if (rc) return rc;
+    int L = E / R;
+    for (int e = 0; e < E; ++e) num_tokens_per_expert[e] = 0;
+    for (int64_t i = 0; i < T * (int64_t)R; ++i) is_token_in_rank[i] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            if (e < 0) continue;
+            num_tokens_per_expert[e] += 1;
+            is_token_in_rank[t * R + e / L] = 1;
+        }
+    }
+    for (int r = 0; r < R; ++r) {
+        int32_t n = 0;
+        for (int64_t t = 0; t < T; ++t) n += is_token_in_rank[t * R + r];
+        num_tokens_per_rank[r] = n;
+    }
+    return ORACLE_OK;
+}
+
+/* Rows a receive buffer needs for any routing of this size: every slot
+ * selected plus the worst alignment padding of every expert. */
+int64_t oracle_capacity(int64_t T, int K, int E, int A) {
+    return T * (int64_t)K + (int64_t)E * (int64_t)(A - 1);
+}
+
+/* Dispatch: expert_offset [E+1], dst_row [T,K], recv_src_idx [cap], and,
+ * when recv_x is non-NULL, the received rows [cap, H] (bf16 bit patterns).
+ * x may be NULL when recv_x is NULL. */
+int oracle_dispatch(const uint16_t* x, int64_t T, int64_t H, const int64_t* topk_idx, int K, int E, int R, int A,
+                    int32_t* expert_offset, int32_t* dst_row, int32_t* recv_src_idx, int64_t cap, uint16_t* recv_x) {
+    int rc = check_routing(topk_idx, T, K, E, R);
+    if (rc) return rc;
+    if (A < 1 || H < 0) return ORACLE_EINVAL;
+    if (cap < oracle_capacity(T, K, E, A)) return ORACLE_ECAPACITY;
+
+    /* received rows per expert, one per selected slot */
+    int64_t* cnt = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    int64_t* fill = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    for (int64_t t = 0; t < T; ++t)
+        for (int k = 0; k < K; ++k)
+            if (topk_idx[t * K + k] >= 0) cnt[topk_idx[t * K + k]] += 1;
+
+    /* segment of expert e starts after the aligned sizes of experts 0..e-1 */
+    expert_offset[0] = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t aligned = (cnt[e] + A - 1) / A * A;
+        expert_offset[e + 1] = (int32_t)(expert_offset[e] + aligned);
+    }
+
+    for (int64_t r = 0; r < cap; ++r) recv_src_idx[r] = -1;
+    for (int e = 0; e < E; ++e) fill[e] = expert_offset[e];
+
+    /* walk the slots in ascending (token, slot) order; each takes the next
+     * free row of its expert's segment */
+    for (int64_t t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            if (e < 0) {
+                dst_row[t * K + k] = -1;
+                continue;
+            }
+            int64_t row = fill[e];
+            fill[e] += 1;
+            dst_row[t * K + k] = (int32_t)row;
+            recv_src_idx[row] = (int32_t)t;
+            if (recv_x)
+                for (int64_t h = 0; h < H; ++h) recv_x[row * H + h] = x[t * H + h];
+        }
+    }
+    free(cnt);
+    free(fill);
+    return ORACLE_OK;
+}
+
+static double bf16_bits_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Nearest bf16 to v, ties to even, as a bit pattern. bf16 has 8 exponent bits
+ * (bias 127) and 7 stored fraction bits: in the binade [2^p, 2^(p+1)) with
+ * p >= -126 its values are spaced 2^(p-7); below 2^-126 (subnormals) they are
+ * spaced 2^-133. The largest finite value is (2 - 2^-7) * 2^127; anything that
+ * rounds to 2^128 or beyond is infinity. */
+uint16_t oracle_bf16_round(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    if (isinf(a)) return sign | 0x7F80;
+    int e2;
+    frexp(a, &e2);      /* a = m * 2^e2, m in [0.5, 1): a in [2^(e2-1), 2^e2) */
+    int p = e2 - 1;     /* binade exponent */
+    if (p < -126) p = -126;
+    double q = ldexp(1.0, p - 7);           /* spacing of bf16 values here */
+    double n = nearbyint(a / q);            /* a/q is exact; round to nearest, ties even */
+    double r = n * q;
+    if (r >= 0x1.0p128) return sign | 0x7F80;
+    float f = (float)r;                     /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* Combine: out[t] = bf16( sum over k with dst_row[t,k] >= 0 of
+ * w[t,k] * y[dst_row[t,k]] ), summed in double in ascending k from +0.
+ * y has `rows` rows of H bf16 values. A token with no selected slot gives +0. */
+int oracle_combine(const uint16_t* y, int64_t rows, int64_t H, const int32_t* dst_row, const float* w,
+                   int64_t T, int K, uint16_t* out) {
+    if (T < 0 || K < 1 || H < 0 || rows < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < T * (int64_t)K; ++i)
+        if (dst_row[i] < -1 || dst_row[i] >= rows) return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) {
+                int32_t row = dst_row[t * K + k];
+                if (row < 0) continue;
+                acc += (double)w[t * K + k] * bf16_bits_to_double(y[(int64_t)row * H + h]);
+            }
+            out[t * H + h] = oracle_bf16_round(acc);
+        }
+    }
+    return ORACLE_OK;
+}
