@@ -1,0 +1,259 @@
+"""MoE expert-parallel layout / dispatch / combine on AMD MI355X (gfx950).
+
+A thin binding over libcgd, whose C ABI is declared in include/cgd.h. This
+module only marshals arguments: every step of the path runs in libcgd's HIP
+kernels, on the caller's current HIP stream. PyTorch supplies device memory
+and streams.
+
+    ntpr, _, ntpe, is_token_in_rank, _ = get_dispatch_layout(topk_idx, num_experts, num_ranks)
+    recv_x, handle = dispatch(x, topk_idx, num_experts, num_ranks)
+    recv_x2, _ = dispatch(x2, handle=handle)            # cached: reuses the layout
+    combined = combine(expert_out, handle, topk_weights)
+
+The calls follow the DeepEP-style Buffer API described by the DeepEP Python
+interface notes ("4 Python接口", section "Dispatch API") and the
+get_dispatch_layout API page ("Interface", "Return Values"); the tuple order of
+get_dispatch_layout is kept, with None in the num_tokens_per_rdma_rank and
+event slots (single node, stream-ordered calls).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+__all__ = ["get_dispatch_layout", "dispatch", "combine", "DispatchHandle", "CgdError", "library_path",
+           "dispatch_capacity", "load"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libcgd.so")
+
+CGD_OK = 0
+_STATUS = {-1: "invalid argument", -2: "capacity", -3: "workspace", -4: "HIP error"}
+
+
+class CgdError(RuntimeError):
+    """A libcgd call returned a non-OK status."""
+
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"{call}: {_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def load():
+    """Load libcgd.so (building it first only if no build exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.cgd_version.restype = ctypes.c_char_p
+    lib.cgd_version.argtypes = []
+    lib.cgd_last_error.restype = ctypes.c_char_p
+    lib.cgd_last_error.argtypes = []
+    lib.cgd_layout_workspace_bytes.restype = sz
+    lib.cgd_layout_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.cgd_dispatch_workspace_bytes.restype = sz
+    lib.cgd_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.cgd_dispatch_capacity.restype = i64
+    lib.cgd_dispatch_capacity.argtypes = [i64, i32, i32, i32]
+    lib.cgd_get_dispatch_layout.restype = i32
+    lib.cgd_get_dispatch_layout.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch.restype = i32
+    lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_cached.restype = i32
+    lib.cgd_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
+    lib.cgd_combine.restype = i32
+    lib.cgd_combine.argtypes = [vp, i64, i32, vp, vp, i64, i32, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _check(call: str, status: int):
+    if status != CGD_OK:
+        raise CgdError(call, status, load().cgd_last_error().decode())
+
+
+def _dev_tensor(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+# One zero-initialised workspace per (device, stream, kind). libcgd leaves a
+# workspace zeroed after every call, and calls on one stream are ordered, so a
+# workspace is reused for every later call on that stream.
+_workspaces: dict = {}
+
+
+def _workspace(device: torch.device, kind: str, nbytes: int) -> torch.Tensor:
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream, kind)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def dispatch_capacity(num_tokens: int, num_topk: int, num_experts: int, expert_alignment: int = 1) -> int:
+    cap = int(load().cgd_dispatch_capacity(num_tokens, num_topk, num_experts, expert_alignment))
+    if cap < 0:
+        raise ValueError("invalid sizes for a receive buffer")
+    return cap
+
+
+def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int):
+    """-> (num_tokens_per_rank int32 [R], None, num_tokens_per_expert int32 [E],
+    is_token_in_rank bool [T,R], None)."""
+    lib = load()
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    with torch.cuda.device(dev):
+        ntpr = torch.empty(num_ranks, dtype=torch.int32, device=dev)
+        ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        itr = torch.empty((T, num_ranks), dtype=torch.bool, device=dev)
+        nbytes = lib.cgd_layout_workspace_bytes(T, K, num_experts, num_ranks)
+        ws = _workspace(dev, "layout", nbytes)
+        _check("cgd_get_dispatch_layout",
+               lib.cgd_get_dispatch_layout(_ptr(topk_idx), T, K, num_experts, num_ranks, _ptr(ntpr), _ptr(ntpe),
+                                           _ptr(itr), _ptr(ws), ws.numel(), _stream(dev)))
+    return ntpr, None, ntpe, itr, None
+
+
+@dataclass
+class DispatchHandle:
+    """Layout of one dispatch, reusable for cached dispatch and for combine.
+
+    expert_offset int32 [E+1]: segment of expert e is rows [off[e], off[e+1]).
+    recv_src_idx  int32 [recv_capacity]: source token of each row, -1 if none.
+    dst_row       int32 [T, K]: receive row of each slot, -1 if not selected.
+    """
+    expert_offset: torch.Tensor
+    recv_src_idx: torch.Tensor
+    dst_row: torch.Tensor
+    num_experts: int
+    num_ranks: int
+    expert_alignment: int
+    recv_capacity: int
+
+    @property
+    def num_tokens(self) -> int:
+        return self.dst_row.shape[0]
+
+    @property
+    def num_topk(self) -> int:
+        return self.dst_row.shape[1]
+
+    def num_recv_tokens_per_expert_list(self) -> list:
+        """Aligned rows per expert as a host list (copies to the host and waits)."""
+        off = self.expert_offset.cpu().tolist()
+        return [b - a for a, b in zip(off[:-1], off[1:])]
+
+
+def dispatch(x: torch.Tensor, topk_idx: torch.Tensor | None = None, num_experts: int | None = None,
+             num_ranks: int | None = None, expert_alignment: int = 1, handle: DispatchHandle | None = None,
+             recv_capacity: int | None = None, recv_x: torch.Tensor | None = None):
+    """Scatter each token's row into the receive segments of its experts.
+
+    Non-cached (handle=None): needs topk_idx, num_experts, num_ranks; returns
+    (recv_x [recv_capacity, H] bf16, DispatchHandle). Cached (handle given,
+    topk_idx None): reuses the handle's layout; returns (recv_x, handle).
+    recv_capacity defaults to the worst case for the sizes, so no device-to-host
+    copy is needed; rows past handle.expert_offset[-1] are unused.
+    """
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    dev = x.device
+    with torch.cuda.device(dev):
+        if handle is not None:
+            if topk_idx is not None:
+                raise ValueError("cached dispatch takes handle and no topk_idx")
+            if handle.num_tokens != T:
+                raise ValueError("x has a different number of tokens than the handle")
+            cap = handle.recv_capacity
+            if recv_x is None:
+                recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+            _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+            if recv_x.shape != (cap, H):
+                raise ValueError("recv_x must be [recv_capacity, hidden]")
+            _check("cgd_dispatch_cached",
+                   lib.cgd_dispatch_cached(_ptr(x), T, H, handle.num_topk, _ptr(handle.dst_row), _ptr(recv_x), cap,
+                                           _stream(dev)))
+            return recv_x, handle
+
+        if topk_idx is None or num_experts is None or num_ranks is None:
+            raise ValueError("non-cached dispatch needs topk_idx, num_experts and num_ranks")
+        _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+        if topk_idx.shape[0] != T or topk_idx.device != dev:
+            raise ValueError("topk_idx must be [num_tokens, num_topk] on x's device")
+        K = topk_idx.shape[1]
+        need = int(lib.cgd_dispatch_capacity(T, K, num_experts, expert_alignment))
+        cap = need if recv_capacity is None else int(recv_capacity)
+        if recv_x is None:
+            recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+        if recv_x.shape[1] != H or recv_x.shape[0] != cap:
+            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        dst = torch.empty((T, K), dtype=torch.int32, device=dev)
+        nbytes = lib.cgd_dispatch_workspace_bytes(T, K, num_experts)
+        ws = _workspace(dev, "dispatch", nbytes)
+        _check("cgd_dispatch",
+               lib.cgd_dispatch(_ptr(x), T, H, _ptr(topk_idx), K, num_experts, num_ranks, expert_alignment,
+                                _ptr(recv_x), cap, _ptr(off), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(),
+                                _stream(dev)))
+    return recv_x, DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+
+
+def combine(expert_out: torch.Tensor, handle: DispatchHandle, topk_weights: torch.Tensor,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """combined[t] = bf16( sum_k w[t,k] * expert_out[dst_row[t,k]] ), fp32 accumulation."""
+    lib = load()
+    _dev_tensor(expert_out, "expert_out", torch.bfloat16, 2)
+    _dev_tensor(topk_weights, "topk_weights", torch.float32, 2)
+    T, K = handle.dst_row.shape
+    if topk_weights.shape != (T, K):
+        raise ValueError("topk_weights must be [num_tokens, num_topk]")
+    rows, H = expert_out.shape
+    dev = expert_out.device
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(out, "out", torch.bfloat16, 2)
+        if out.shape != (T, H):
+            raise ValueError("out must be [num_tokens, hidden]")
+        _check("cgd_combine",
+               lib.cgd_combine(_ptr(expert_out), rows, H, _ptr(handle.dst_row), _ptr(topk_weights), T, K, _ptr(out),
+                               _stream(dev)))
+    return out

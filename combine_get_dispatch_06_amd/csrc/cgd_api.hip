@@ -1,0 +1,172 @@
+// C-ABI entry points of libcgd: argument checks, workspace sizing, launches.
+// Declarations and the contract of every call are in include/cgd.h.
+#include "cgd.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "cgd_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t err, const char* what) {
+    return fail(CGD_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Limits of the get_dispatch_layout API page ("Parameters", "Notes").
+int check_routing_sizes(int64_t T, int K, int E, int R) {
+    if (T < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %lld)", (long long)T);
+    if (K < 1 || K > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16] (got %d)", K);
+    if (E < 1 || E > cgd::kMaxExperts)
+        return fail(CGD_ERR_INVALID_ARG, "num_experts must be in [1,512] (got %d)", E);
+    if (R < 1 || R > cgd::kMaxRanks) return fail(CGD_ERR_INVALID_ARG, "num_ranks must be in [1,384] (got %d)", R);
+    if (E % R != 0)
+        return fail(CGD_ERR_INVALID_ARG, "num_experts (%d) must be divisible by num_ranks (%d)", E, R);
+    if (T * (int64_t)K > INT32_MAX) return fail(CGD_ERR_INVALID_ARG, "num_tokens * num_topk exceeds INT32_MAX");
+    return CGD_OK;
+}
+
+int check_hidden(int H) {
+    if (H < 8 || H % 8 != 0) return fail(CGD_ERR_INVALID_ARG, "hidden must be a positive multiple of 8 (got %d)", H);
+    return CGD_OK;
+}
+
+int64_t capacity_of(int64_t T, int K, int E, int A) {
+    if (T < 0 || K < 1 || E < 1 || A < 1) return -1;
+    const int64_t cap = T * (int64_t)K + (int64_t)E * (int64_t)(A - 1);
+    if (A > INT32_MAX / E || cap > INT32_MAX) return -1;
+    return cap;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cgd_version(void) { return "cgd 0.1.0 (gfx950)"; }
+
+const char* cgd_last_error(void) { return g_last_error.c_str(); }
+
+size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks) {
+    if (num_tokens < 0 || num_topk < 1 || num_experts < 1 || num_experts > cgd::kMaxExperts || num_ranks < 1 ||
+        num_ranks > cgd::kMaxRanks)
+        return 0;
+    return cgd::layout_workspace_bytes(num_tokens, num_experts, num_ranks);
+}
+
+size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
+    if (num_tokens < 0 || num_topk < 1 || num_experts < 1 || num_experts > cgd::kMaxExperts) return 0;
+    return cgd::dispatch_workspace_bytes(num_tokens, num_experts);
+}
+
+int64_t cgd_dispatch_capacity(int64_t num_tokens, int num_topk, int num_experts, int expert_alignment) {
+    return capacity_of(num_tokens, num_topk, num_experts, expert_alignment);
+}
+
+int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                            int num_ranks, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_rank, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    int rc = check_routing_sizes(num_tokens, num_topk, num_experts, num_ranks);
+    if (rc) return rc;
+    if (!num_tokens_per_rank || !num_tokens_per_expert)
+        return fail(CGD_ERR_INVALID_ARG, "null count output pointer");
+    if (num_tokens > 0 && (!topk_idx || !is_token_in_rank))
+        return fail(CGD_ERR_INVALID_ARG, "null topk_idx or is_token_in_rank pointer");
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(num_tokens_per_expert, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned topk_idx or count output");
+    if (!aligned(is_token_in_rank, 16)) return fail(CGD_ERR_INVALID_ARG, "is_token_in_rank must be 16-byte aligned");
+    const size_t need = cgd::layout_workspace_bytes(num_tokens, num_experts, num_ranks);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "layout workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    hipError_t err = cgd::launch_layout(topk_idx, num_tokens, num_topk, num_experts, num_ranks, num_tokens_per_rank,
+                                        num_tokens_per_expert, is_token_in_rank, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "layout launch");
+    return CGD_OK;
+}
+
+int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                 int num_experts, int num_ranks, int expert_alignment, void* recv_x, int64_t recv_capacity,
+                 int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_routing_sizes(num_tokens, num_topk, num_experts, num_ranks);
+    if (rc) return rc;
+    if ((rc = check_hidden(hidden))) return rc;
+    if (expert_alignment < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
+    const int64_t need_rows = capacity_of(num_tokens, num_topk, num_experts, expert_alignment);
+    if (need_rows < 0) return fail(CGD_ERR_INVALID_ARG, "receive capacity for these sizes exceeds INT32_MAX");
+    if (recv_capacity < need_rows || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
+                    (long long)recv_capacity);
+    if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
+    if (num_tokens > 0 && (!x || !topk_idx || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null input pointer");
+    if (recv_capacity > 0 && (!recv_x || !recv_src_idx)) return fail(CGD_ERR_INVALID_ARG, "null receive pointer");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
+    const size_t need = cgd::dispatch_workspace_bytes(num_tokens, num_experts);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    hipError_t err = cgd::launch_dispatch(x, num_tokens, hidden, topk_idx, num_topk, num_experts, expert_alignment,
+                                          recv_x, recv_capacity, expert_offset, recv_src_idx, dst_row, workspace,
+                                          stream);
+    if (err != hipSuccess) return hip_fail(err, "dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_dispatch_cached(const void* x, int64_t num_tokens, int hidden, int num_topk, const int32_t* dst_row,
+                        void* recv_x, int64_t recv_capacity, hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_topk < 1 || num_topk > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16]");
+    int rc = check_hidden(hidden);
+    if (rc) return rc;
+    if (recv_capacity < 0 || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
+    if (num_tokens > 0 && (!x || !dst_row || (recv_capacity > 0 && !recv_x)))
+        return fail(CGD_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+    if (!aligned(dst_row, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned dst_row");
+    hipError_t err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity,
+                                                 stream);
+    if (err != hipSuccess) return hip_fail(err, "cached dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_combine(const void* expert_out, int64_t recv_capacity, int hidden, const int32_t* dst_row,
+                const float* topk_weights, int64_t num_tokens, int num_topk, void* combined_x,
+                hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_topk < 1 || num_topk > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16]");
+    int rc = check_hidden(hidden);
+    if (rc) return rc;
+    if (recv_capacity < 0 || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
+    if (num_tokens > 0 && (!dst_row || !topk_weights || !combined_x || (recv_capacity > 0 && !expert_out)))
+        return fail(CGD_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(expert_out, 16) || !aligned(combined_x, 16))
+        return fail(CGD_ERR_INVALID_ARG, "expert_out and combined_x must be 16-byte aligned");
+    if (!aligned(dst_row, 4) || !aligned(topk_weights, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
+    hipError_t err = cgd::launch_combine(expert_out, recv_capacity, hidden, dst_row, topk_weights, num_tokens,
+                                         num_topk, combined_x, stream);
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return CGD_OK;
+}
+
+}  // extern "C"

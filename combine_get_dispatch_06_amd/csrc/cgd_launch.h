@@ -1,0 +1,38 @@
+// Internal launchers of libcgd (host side). Arguments are validated by the
+// C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cgd {
+
+// Size limits of the get_dispatch_layout API ("Parameters", "Notes").
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxRanks = 384;
+
+// Tokens per block of the layout kernel and per tile of the dispatch ranking.
+constexpr int kLayoutTile = 256;
+constexpr int kRankTile = 256;
+constexpr size_t kTicketBytes = 256;  // ticket word, padded to keep arrays 256-B aligned
+
+int64_t layout_blocks(int64_t T);
+size_t layout_workspace_bytes(int64_t T, int E, int R);
+size_t dispatch_workspace_bytes(int64_t T, int E);
+
+hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R, int32_t* ntpr, int32_t* ntpe,
+                         uint8_t* itr, void* workspace, hipStream_t stream);
+
+hipError_t launch_dispatch(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
+                           void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
+                           int32_t* dst_row, void* workspace, hipStream_t stream);
+
+hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
+                                  int64_t cap, hipStream_t stream);
+
+hipError_t launch_combine(const void* expert_out, int64_t cap, int H, const int32_t* dst_row, const float* w,
+                          int64_t T, int K, void* out, hipStream_t stream);
+
+}  // namespace cgd

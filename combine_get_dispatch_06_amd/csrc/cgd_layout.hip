@@ -1,0 +1,167 @@
+// get_dispatch_layout on gfx950.
+//
+// Computes, from topk_idx [T,K] (get_dispatch_layout API page, "Return
+// Values"): per-expert slot counts, per-rank distinct-token counts and the
+// is_token_in_rank matrix. Rank r owns experts [r*L, (r+1)*L) (DeepEP legacy
+// test analysis page, low-latency per-expert check).
+//
+// One launch. Each block takes 256 tokens, one per thread:
+//   1. the tile's topk_idx is staged in LDS with coalesced loads;
+//   2. each thread adds its slots to an LDS expert histogram and builds the
+//      bitmask of ranks its token touches;
+//   3. distinct tokens per rank: per wave, one ballot per rank and a popcount
+//      of the lanes whose token holds it;
+//   4. the tile's is_token_in_rank rows (a contiguous byte range) are written
+//      with 16-byte stores;
+//   5. blocks publish their partial counts; the last block to finish sums
+//      them into the outputs (no pre-zeroed outputs, no second launch).
+// The NPU implementation on the API page ("Internal Logic", "Multi-Core
+// Strategy") also splits tokens over cores and aggregates partial results
+// across cores; here the aggregation is a last-block-done reduction.
+#include "cgd_device.h"
+#include "cgd_launch.h"
+
+namespace cgd {
+
+template <int RW>  // 64-bit words of the per-token rank mask: 1 (R <= 64) or 6 (R <= 384)
+__global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K,
+                                                             int E, int R, int L, int32_t* __restrict__ ntpr,
+                                                             int32_t* __restrict__ ntpe, uint8_t* __restrict__ itr,
+                                                             int32_t* __restrict__ partial,
+                                                             unsigned int* __restrict__ ticket) {
+    __shared__ int32_t s_idx[kLayoutTile * kMaxTopk];
+    __shared__ uint64_t s_mask[kLayoutTile * RW];
+    __shared__ int32_t s_hist[kMaxExperts];
+    __shared__ int32_t s_rank[kMaxRanks];
+
+    const int tid = threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.x * kLayoutTile;
+    const int nt = (int)max<int64_t>(0, min<int64_t>(kLayoutTile, T - t0));
+
+    for (int i = tid; i < E; i += kLayoutTile) s_hist[i] = 0;
+    for (int i = tid; i < R; i += kLayoutTile) s_rank[i] = 0;
+    {
+        const int64_t* src = topk_idx + t0 * K;
+        const int n = nt * K;
+        for (int i = tid; i < n; i += kLayoutTile) {
+            const int64_t e = src[i];
+            s_idx[i] = (e >= 0 && e < E) ? (int32_t)e : -1;
+        }
+    }
+    __syncthreads();
+
+    uint64_t m[RW];
+#pragma unroll
+    for (int w = 0; w < RW; ++w) m[w] = 0;
+    if (tid < nt) {
+        for (int k = 0; k < K; ++k) {
+            const int e = s_idx[tid * K + k];
+            if (e >= 0) {
+                atomicAdd(&s_hist[e], 1);
+                const int r = e / L;
+#pragma unroll
+                for (int w = 0; w < RW; ++w)
+                    if ((r >> 6) == w) m[w] |= 1ull << (r & 63);
+            }
+        }
+    }
+
+    // distinct tokens per rank: ballot over the wave's tokens, lane (r % 64)
+    // keeps the popcount for rank r
+    const int lane = lane_id();
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+        const int rbeg = w * kWave;
+        const int rend = min(R, rbeg + kWave);
+        int cnt = 0;
+        for (int r = rbeg; r < rend; ++r) {
+            const uint64_t b = ballot((m[w] >> (r & 63)) & 1ull);
+            if (lane == (r & 63)) cnt = __popcll(b);
+        }
+        if (rbeg + lane < rend && cnt) atomicAdd(&s_rank[rbeg + lane], cnt);
+        s_mask[tid * RW + w] = m[w];
+    }
+    __syncthreads();
+
+    // is_token_in_rank rows of this tile: bytes [t0*R, (t0+nt)*R), 16 at a time.
+    // t0*R is a multiple of 16 because kLayoutTile is.
+    {
+        const int64_t nbytes = (int64_t)nt * R;
+        uint8_t* out = itr + t0 * R;
+        for (int64_t c = tid; c * 16 < nbytes; c += kLayoutTile) {
+            const int64_t b0 = c * 16;
+            int tok = (int)(b0 / R);
+            int r = (int)(b0 - (int64_t)tok * R);
+            const int nb = (int)min<int64_t>(16, nbytes - b0);
+            uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j < nb) {
+                    const uint32_t bit = (uint32_t)(s_mask[tok * RW + (r >> 6)] >> (r & 63)) & 1u;
+                    wd[j >> 2] |= bit << ((j & 3) * 8);
+                }
+                if (++r == R) {
+                    r = 0;
+                    ++tok;
+                }
+            }
+            if (nb == 16) {
+                *reinterpret_cast<uint4*>(out + b0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            } else {
+                for (int j = 0; j < nb; ++j) out[b0 + j] = (uint8_t)(wd[j >> 2] >> ((j & 3) * 8));
+            }
+        }
+    }
+
+    if (gridDim.x == 1) {
+        for (int i = tid; i < E; i += kLayoutTile) ntpe[i] = s_hist[i];
+        for (int i = tid; i < R; i += kLayoutTile) ntpr[i] = s_rank[i];
+        return;
+    }
+
+    const int W = E + R;
+    int32_t* mine = partial + (int64_t)blockIdx.x * W;
+    for (int i = tid; i < E; i += kLayoutTile) mine[i] = s_hist[i];
+    for (int i = tid; i < R; i += kLayoutTile) mine[E + i] = s_rank[i];
+    if (!last_block_done(ticket)) return;
+
+    const int nblk = gridDim.x;
+    for (int i = tid; i < W; i += kLayoutTile) {
+        int s = 0;
+        int b = 0;
+        for (; b + 4 <= nblk; b += 4) {
+            const int32_t* p = partial + (int64_t)b * W + i;
+            s += p[0] + p[W] + p[2 * W] + p[3 * W];
+        }
+        for (; b < nblk; ++b) s += partial[(int64_t)b * W + i];
+        if (i < E)
+            ntpe[i] = s;
+        else
+            ntpr[i - E] = s;
+    }
+    reset_ticket(ticket);
+}
+
+int64_t layout_blocks(int64_t T) { return T <= 0 ? 1 : (T + kLayoutTile - 1) / kLayoutTile; }
+
+size_t layout_workspace_bytes(int64_t T, int E, int R) {
+    const size_t arr = (size_t)layout_blocks(T) * (size_t)(E + R) * sizeof(int32_t);
+    return kTicketBytes + (arr + 255) / 256 * 256;
+}
+
+hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R, int32_t* ntpr, int32_t* ntpe,
+                         uint8_t* itr, void* workspace, hipStream_t stream) {
+    unsigned int* ticket = reinterpret_cast<unsigned int*>(workspace);
+    int32_t* partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + kTicketBytes);
+    const dim3 grid((unsigned)layout_blocks(T)), block(kLayoutTile);
+    const int L = E / R;
+    if (R <= 64)
+        hipLaunchKernelGGL(layout_kernel<1>, grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
+                           partial, ticket);
+    else
+        hipLaunchKernelGGL(layout_kernel<6>, grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
+                           partial, ticket);
+    return hipGetLastError();
+}
+
+}  // namespace cgd

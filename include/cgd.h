@@ -1,0 +1,151 @@
+/*
+ * cgd.h - C ABI of libcgd: the MoE expert-parallel layout / dispatch / combine
+ * hot path on one AMD MI355X (gfx950).
+ *
+ * The operations follow the DeepEP-style expert-parallel layer described by:
+ *   - the get_dispatch_layout API page (sgl-kernel-npu deep_ep docs),
+ *     sections "Parameters", "Return Values" and "Notes";
+ *   - the DeepEP Python interface notes ("4 Python接口"), section "Dispatch API"
+ *     (inputs, outputs, cached mode, expert_alignment, async/event handling);
+ *   - the DeepEP legacy test analysis page: layout cross-check excerpt,
+ *     low-latency per-expert check (expert id = rank * num_local_experts + i),
+ *     low-latency combine check (x scaled by the sum of unmasked weights),
+ *     and the handle layouts of the legacy.py excerpts.
+ *
+ * The "ranks" are logical partitions of the expert set inside one device:
+ * rank r owns experts [r*L, (r+1)*L) with L = num_experts / num_ranks.
+ *
+ * Conventions for every call:
+ *   - Every pointer argument is a DEVICE pointer, except where noted. The
+ *     caller allocates and frees all memory, including workspaces; the library
+ *     never allocates device memory and never synchronises the stream.
+ *   - Every call only enqueues kernels on `stream` and returns (the pages'
+ *     async_finish=True). The caller orders work with its own events
+ *     (hipEventRecord / hipStreamWaitEvent), which replaces the pages'
+ *     previous_event / EventOverlap objects. Inputs must stay alive and
+ *     unmodified until the stream has passed the call.
+ *   - Pointers to bf16 rows and the is_token_in_rank output must be 16-byte
+ *     aligned; other pointers must be aligned to their element type.
+ *   - bf16 data are IEEE bfloat16 bit patterns (uint16 storage).
+ *   - Return value: CGD_OK, or a negative cgd_status; then nothing was
+ *     enqueued (except for CGD_ERR_HIP, where a launch failed) and
+ *     cgd_last_error() returns a message for the calling thread.
+ *   - Argument limits mirror the get_dispatch_layout API page: num_topk in
+ *     [1,16], num_experts in [1,512], num_ranks in [1,384], num_experts a
+ *     multiple of num_ranks. num_tokens may be 0 (a documented extension:
+ *     all counts are then zero). hidden must be a positive multiple of 8.
+ *   - Device-side data preconditions are not checked on the host: topk_idx
+ *     entries are expected in [-1, num_experts). A value outside that range
+ *     is treated as -1 (not selected) by every kernel, so it never causes an
+ *     out-of-bounds access.
+ */
+#ifndef CGD_H
+#define CGD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CGD_OK = 0,
+    CGD_ERR_INVALID_ARG = -1, /* a size, pointer or alignment is invalid */
+    CGD_ERR_CAPACITY = -2,    /* recv_capacity is below cgd_dispatch_capacity() */
+    CGD_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required */
+    CGD_ERR_HIP = -4          /* a HIP launch failed */
+} cgd_status;
+
+/* Library version string (host pointer, static storage). */
+const char* cgd_version(void);
+
+/* Message for the last non-OK status returned on the calling thread
+ * (host pointer, valid until the next call on that thread). */
+const char* cgd_last_error(void);
+
+/* Workspace bytes cgd_get_dispatch_layout needs for these sizes (host only;
+ * 0 if the sizes are invalid). The workspace must be zero-filled before its
+ * first use; every completed call leaves it zero-filled again, so one
+ * workspace serves any number of calls that are ordered on one stream.
+ * Calls that may run concurrently need separate workspaces. */
+size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
+
+/* Workspace bytes cgd_dispatch needs (host only; 0 if invalid). Same
+ * zero-fill and reuse rules as the layout workspace. */
+size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts);
+
+/* Rows a receive buffer needs for ANY routing of these sizes (host only):
+ * num_tokens * num_topk + num_experts * (expert_alignment - 1), or -1 if the
+ * sizes are invalid or the result exceeds INT32_MAX. Knowing this on the host
+ * means no device-to-host copy is needed before dispatch, the purpose of the
+ * pages' num_worst_tokens argument (Python interface notes, "Dispatch API"). */
+int64_t cgd_dispatch_capacity(int64_t num_tokens, int num_topk, int num_experts, int expert_alignment);
+
+/* get_dispatch_layout (get_dispatch_layout API page, "Return Values"):
+ *   topk_idx               int64 [num_tokens, num_topk], row-major; -1 = not selected
+ *   num_tokens_per_rank    int32 [num_ranks]   out: distinct tokens with >= 1 expert on the rank
+ *   num_tokens_per_expert  int32 [num_experts] out: selected slots per expert
+ *   is_token_in_rank       uint8 [num_tokens, num_ranks] row-major, out: 1 if the token
+ *                          selects an expert of the rank, else 0 (torch.bool storage)
+ *   workspace              >= cgd_layout_workspace_bytes(...) bytes, see above
+ * The pages' num_tokens_per_rdma_rank output is not produced (it is None for a
+ * single node). Outputs are fully overwritten. */
+int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                            int num_ranks, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_rank, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Dispatch (Python interface notes, "Dispatch API", non-cached mode):
+ * places every selected (token, slot) pair in a contiguous receive segment of
+ * its expert and copies the token's bf16 row there.
+ *   x                  bf16 [num_tokens, hidden]
+ *   topk_idx           int64 [num_tokens, num_topk]; -1 = not selected
+ *   expert_alignment   >= 1; each expert's segment size is its row count
+ *                      rounded up to a multiple of this value
+ *   recv_x             bf16 [recv_capacity, hidden] out: row dst_row[t,k] = x[t], bit for bit;
+ *                      alignment-padding rows and rows past the data are not written
+ *   recv_capacity      rows of recv_x and recv_src_idx; >= cgd_dispatch_capacity(...)
+ *   expert_offset      int32 [num_experts + 1] out: segment e is rows
+ *                      [expert_offset[e], expert_offset[e+1]); segments are in
+ *                      ascending expert id, hence grouped by rank
+ *   recv_src_idx       int32 [recv_capacity] out: source token of each data row, -1 elsewhere
+ *   dst_row            int32 [num_tokens, num_topk] out: receive row of each slot, -1 if
+ *                      not selected. Inside a segment rows follow ascending (token, slot)
+ *   workspace          >= cgd_dispatch_workspace_bytes(...) bytes
+ * (expert_offset, recv_src_idx, dst_row) is the handle for cached dispatch and
+ * for combine. Counts are derived from topk_idx itself, so the layout outputs
+ * are not inputs here and cannot disagree with the routing. */
+int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                 int num_experts, int num_ranks, int expert_alignment, void* recv_x, int64_t recv_capacity,
+                 int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Cached dispatch (Python interface notes, "Dispatch API", handle reuse):
+ * copies rows with a dst_row from an earlier cgd_dispatch, skipping the
+ * layout work. recv_x[dst_row[t,k]] = x[t] for every dst_row[t,k] in
+ * [0, recv_capacity); other entries are skipped. */
+int cgd_dispatch_cached(const void* x, int64_t num_tokens, int hidden, int num_topk, const int32_t* dst_row,
+                        void* recv_x, int64_t recv_capacity, hipStream_t stream);
+
+/* Combine (legacy test analysis page, low-latency combine check):
+ *   combined_x[t] = bf16( sum over k with dst_row[t,k] >= 0, ascending k, of
+ *                         topk_weights[t,k] * expert_out[dst_row[t,k]] )
+ * accumulated in fp32 with fused multiply-add from +0 and rounded to nearest
+ * even. A token with no selected slot gives +0.
+ *   expert_out     bf16 [recv_capacity, hidden]
+ *   dst_row        int32 [num_tokens, num_topk] from cgd_dispatch; entries outside
+ *                  [-1, recv_capacity) are treated as -1
+ *   topk_weights   fp32 [num_tokens, num_topk]
+ *   combined_x     bf16 [num_tokens, hidden] out */
+int cgd_combine(const void* expert_out, int64_t recv_capacity, int hidden, const int32_t* dst_row,
+                const float* topk_weights, int64_t num_tokens, int num_topk, void* combined_x,
+                hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CGD_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+sizes buffers on the host and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_get_dispatch_06_amd as cgd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cgd.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cgd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted([
+        "cgd_version", "cgd_last_error", "cgd_layout_workspace_bytes", "cgd_dispatch_workspace_bytes",
+        "cgd_dispatch_capacity", "cgd_get_dispatch_layout", "cgd_dispatch", "cgd_dispatch_cached", "cgd_combine",
+    ])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cgd.load()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", cgd.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (cgd_\w+)", out))
+    assert set(_declared_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    # the embedded offload bundle names its target
+    blob = open(cgd.library_path(), "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_version():
+    assert b"gfx950" in cgd.load().cgd_version()
+
+
+def test_capacity_and_workspace_sizes():
+    lib = cgd.load()
+    assert lib.cgd_dispatch_capacity(4096, 8, 256, 1) == 32768
+    assert lib.cgd_dispatch_capacity(5, 3, 8, 4) == 39
+    assert lib.cgd_dispatch_capacity(0, 2, 8, 16) == 8 * 15
+    assert lib.cgd_dispatch_capacity(10, 2, 8, 0) == -1
+    assert lib.cgd_dispatch_capacity(1 << 30, 16, 8, 1) == -1
+    assert cgd.dispatch_capacity(32768, 16, 512) == 524288
+    for T in (0, 1, 255, 256, 257, 32768):
+        ws = lib.cgd_layout_workspace_bytes(T, 8, 256, 8)
+        blocks = max(1, -(-T // 256))
+        assert ws >= 256 + blocks * (256 + 8) * 4 and ws % 256 == 0
+        wd = lib.cgd_dispatch_workspace_bytes(T, 8, 256)
+        assert wd >= 256 + blocks * 256 * 4 and wd % 256 == 0
+    assert lib.cgd_layout_workspace_bytes(10, 8, 513, 1) == 0
+    assert lib.cgd_dispatch_workspace_bytes(10, 0, 8) == 0
+
+
+def _vp(v):
+    return ctypes.c_void_p(v)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("T,K,E,R,status", [
+    (-1, 8, 256, 8, -1), (16, 0, 256, 8, -1), (16, 17, 256, 8, -1), (16, 8, 0, 8, -1), (16, 8, 513, 8, -1),
+    (16, 8, 768, 384, -1), (16, 8, 770, 385, -1), (16, 8, 256, 3, -1), (16, 8, 256, 8, -3),
+])
+def test_layout_rejects_bad_arguments(T, K, E, R, status):
+    lib = cgd.load()
+    # last case: valid sizes but no workspace -> CGD_ERR_WORKSPACE
+    rc = lib.cgd_get_dispatch_layout(_vp(FAKE), T, K, E, R, _vp(FAKE), _vp(FAKE), _vp(FAKE), None, 0, None)
+    assert rc == status
+    assert lib.cgd_last_error()
+
+
+def test_layout_rejects_misaligned_outputs():
+    lib = cgd.load()
+    rc = lib.cgd_get_dispatch_layout(_vp(FAKE), 16, 8, 256, 8, _vp(FAKE), _vp(FAKE), _vp(FAKE + 1), _vp(FAKE),
+                                     1 << 20, None)
+    assert rc == -1 and b"16-byte" in lib.cgd_last_error()
+
+
+def test_dispatch_rejects_bad_arguments():
+    lib = cgd.load()
+    ok = dict(x=FAKE, T=64, H=128, idx=FAKE, K=4, E=16, R=4, A=1, recv=FAKE, cap=256, off=FAKE, src=FAKE, dst=FAKE,
+              ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.cgd_dispatch(_vp(a["x"]), a["T"], a["H"], _vp(a["idx"]), a["K"], a["E"], a["R"], a["A"],
+                                _vp(a["recv"]), a["cap"], _vp(a["off"]), _vp(a["src"]), _vp(a["dst"]),
+                                _vp(a["ws"]) if a["ws"] else None, a["wsb"], None)
+
+    assert call(H=12) == -1          # hidden not a multiple of 8
+    assert call(H=0) == -1
+    assert call(A=0) == -1           # alignment
+    assert call(cap=255) == -2       # capacity below T*K
+    assert call(A=2, cap=256) == -2  # capacity below T*K + E*(A-1)
+    assert call(x=FAKE + 8) == -1    # x not 16-byte aligned
+    assert call(ws=0) == -3          # missing workspace
+    assert call(wsb=16) == -3        # workspace too small
+    assert call(E=15) == -1          # E % R
+    assert call(K=17) == -1
+
+
+def test_cached_dispatch_and_combine_reject_bad_arguments():
+    lib = cgd.load()
+    assert lib.cgd_dispatch_cached(_vp(FAKE), 8, 100, 2, _vp(FAKE), _vp(FAKE), 16, None) == -1
+    assert lib.cgd_dispatch_cached(_vp(FAKE), 8, 128, 0, _vp(FAKE), _vp(FAKE), 16, None) == -1
+    assert lib.cgd_dispatch_cached(_vp(FAKE), -1, 128, 2, _vp(FAKE), _vp(FAKE), 16, None) == -1
+    assert lib.cgd_combine(_vp(FAKE), 16, 128, _vp(FAKE), _vp(FAKE), 8, 17, _vp(FAKE), None) == -1
+    assert lib.cgd_combine(_vp(FAKE), 16, 128, _vp(FAKE), _vp(FAKE + 2), 8, 2, _vp(FAKE), None) == -1
+    assert lib.cgd_combine(_vp(FAKE), 16, 128, None, _vp(FAKE), 8, 2, _vp(FAKE), None) == -1
+    assert lib.cgd_combine(_vp(FAKE), -5, 128, _vp(FAKE), _vp(FAKE), 8, 2, _vp(FAKE), None) == -2
+
+
+def test_product_path_does_not_touch_the_oracle():
+    # the binding and the HIP sources never import, load or include the oracle
+    pkg = os.path.join(ROOT, "combine_get_dispatch_06_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+    assert "oracle" not in open(HEADER).read().lower()

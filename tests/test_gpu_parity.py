@@ -1,0 +1,234 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Layout, counts, offsets, dst_row, recv_src_idx and received rows must be
+bit-exact; combine must be within 1e-2 relative (bf16 output, fp32
+accumulation). Every input comes from the seeded generator; every expected
+value from the oracle."""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import combine_get_dispatch_06_amd as cgd
+import oracle
+import synth
+from gpu_util import (DEV, bf16_to_f64, check_combine, dev_bf16, dev_f32, dev_i64, host_bits, say,
+                      term_magnitude)
+
+pytestmark = pytest.mark.gpu
+
+FULL_ORACLE_ROWS = 40_000_000  # recv_x elements up to which the oracle copies every row
+
+
+def _run_layout(idx_np, E, R):
+    ntpr, _, ntpe, itr, _ = cgd.get_dispatch_layout(dev_i64(idx_np), E, R)
+    torch.cuda.synchronize()
+    return ntpr.cpu().numpy(), ntpe.cpu().numpy(), itr.cpu().numpy()
+
+
+def _check_layout(idx_np, E, R):
+    g = _run_layout(idx_np, E, R)
+    o = oracle.layout(idx_np, E, R)
+    np.testing.assert_array_equal(g[0], o[0])
+    np.testing.assert_array_equal(g[1], o[1])
+    np.testing.assert_array_equal(g[2], o[2])
+
+
+def _check_rows_on_device(recv_x, x_dev, dst_np):
+    """recv_x[dst[t,k]] == x[t] bit for bit for every selected slot (chunked)."""
+    T, K = dst_np.shape
+    sel_t, sel_k = np.nonzero(dst_np >= 0)
+    rows = dst_np[sel_t, sel_k]
+    step = 1 << 16
+    for i in range(0, len(rows), step):
+        r = torch.from_numpy(rows[i:i + step].astype(np.int64)).to(DEV)
+        t = torch.from_numpy(sel_t[i:i + step].astype(np.int64)).to(DEV)
+        a = recv_x.view(torch.int16).index_select(0, r)
+        b = x_dev.view(torch.int16).index_select(0, t)
+        assert torch.equal(a, b), f"row mismatch in slots {i}..{i + step}"
+
+
+def _dispatch_and_check(w, idx_np, x_np, align=1, cap=None):
+    x_dev = dev_bf16(x_np)
+    idx_dev = dev_i64(idx_np)
+    recv_x, h = cgd.dispatch(x_dev, idx_dev, w.E, w.R, expert_alignment=align, recv_capacity=cap)
+    torch.cuda.synchronize()
+    want_rows = x_np.size * w.K <= FULL_ORACLE_ROWS
+    o = oracle.dispatch(x_np if want_rows else None, idx_np, w.E, w.R, align=align, cap=h.recv_capacity,
+                        hidden=w.H, with_rows=want_rows)
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    if want_rows:
+        g = host_bits(recv_x)
+        data = o["recv_src_idx"] >= 0  # padding rows are unspecified
+        np.testing.assert_array_equal(g[data], o["recv_x"][data])
+    else:
+        _check_rows_on_device(recv_x, x_dev, o["dst_row"])
+    return x_dev, recv_x, h, o
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_parity(name):
+    w = synth.WORKLOADS[name]
+    say(f"[parity] {name}: T={w.T} H={w.H} K={w.K} E={w.E} R={w.R} routing={w.routing}")
+    inp = synth.make_inputs(w, seed=0)
+    _check_layout(inp["topk_idx"], w.E, w.R)
+    say(f"[parity] {name}: layout ok")
+    x_dev, recv_x, h, o = _dispatch_and_check(w, inp["topk_idx"], inp["x"])
+    say(f"[parity] {name}: dispatch ok")
+
+    # identity experts + softmax weights: combine(dispatch(x)) == x exactly
+    wt_dev = dev_f32(inp["topk_weights"])
+    back = cgd.combine(recv_x, h, wt_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), x_dev.view(torch.int16))
+    say(f"[parity] {name}: identity round trip ok")
+
+    # independent expert outputs: oracle on all tokens, or on a sample at the largest sizes
+    cap = h.recv_capacity
+    y_np = synth.make_expert_out(w, cap, seed=0)
+    out = cgd.combine(dev_bf16(y_np), h, wt_dev)
+    torch.cuda.synchronize()
+    got = host_bits(out)
+    dst = o["dst_row"]
+    if w.T * w.H * w.K <= 300_000_000:
+        tok = np.arange(w.T)
+    else:
+        tok = np.unique(np.random.default_rng(1).integers(0, w.T, 512))
+    exp = oracle.combine(y_np, dst[tok], inp["topk_weights"][tok])
+    frac = check_combine(got[tok], exp, term_magnitude(y_np, dst[tok], inp["topk_weights"][tok]))
+    say(f"[parity] {name}: combine ok on {len(tok)} tokens, bit-identical fraction {frac:.6f}")
+    assert frac > 0.99
+
+
+def test_cached_dispatch_matches_fresh_dispatch():
+    w = synth.WORKLOADS["prefill"].replace(T=1000)
+    inp = synth.make_inputs(w, seed=3)
+    x_dev, recv_x, h, o = _dispatch_and_check(w, inp["topk_idx"], inp["x"])
+    x2 = synth.make_x(w.replace(name="prefill-second-batch"), seed=3)
+    recv2, h2 = cgd.dispatch(dev_bf16(x2), handle=h)
+    torch.cuda.synchronize()
+    assert h2 is h
+    o2 = oracle.dispatch(x2, inp["topk_idx"], w.E, w.R)
+    g = host_bits(recv2)
+    data = o2["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(g[data], o2["recv_x"][data])
+
+
+def _edge(T, K, E, R, H, align=1, p_neg=0.0, dup=False, seed=0, all_to=None, cap_extra=0):
+    rng = np.random.default_rng(seed)
+    if all_to is not None:
+        idx = np.full((T, K), -1, np.int64)
+        idx[:, 0] = all_to
+    elif dup:
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int64)
+    else:
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64) if T else \
+            np.zeros((0, K), np.int64)
+    if p_neg:
+        idx[rng.random((T, K)) < p_neg] = -1
+    w = synth.Workload("edge", T=T, H=H, K=K, E=E, R=R, align=align)
+    x = synth.normal_bf16(synth.stream_key(seed, 99, 1), T * H).reshape(T, H)
+    wts = synth.softmax_weights(synth.stream_key(seed, 99, 3), T, K)
+    return w, idx, x, wts
+
+
+EDGE_CASES = {
+    "T=1": dict(T=1, K=8, E=256, R=8, H=7168),
+    "ragged_T=300": dict(T=300, K=8, E=256, R=8, H=512),
+    "ragged_T=1025_neg": dict(T=1025, K=6, E=96, R=12, H=136, p_neg=0.3),
+    "all_minus_one_rows": dict(T=257, K=4, E=16, R=4, H=64, p_neg=0.9),
+    "duplicates": dict(T=513, K=8, E=8, R=2, H=64, dup=True),
+    "K=1": dict(T=777, K=1, E=32, R=4, H=8),
+    "K=16_E=512_R=64": dict(T=700, K=16, E=512, R=64, H=256),
+    "R=1": dict(T=300, K=4, E=64, R=1, H=64),
+    "R=E=384": dict(T=600, K=9, E=384, R=384, H=64),
+    "R=E=8": dict(T=90, K=3, E=8, R=8, H=64),
+    "E=1": dict(T=100, K=1, E=1, R=1, H=32),
+    "H=8": dict(T=513, K=2, E=4, R=2, H=8),
+    "align16": dict(T=1000, K=8, E=256, R=8, H=64, align=16),
+    "align32_neg": dict(T=333, K=4, E=64, R=16, H=24, align=32, p_neg=0.2),
+    "one_hot_expert": dict(T=2000, K=3, E=64, R=8, H=32, all_to=37),
+    "extra_capacity": dict(T=200, K=4, E=32, R=4, H=40, cap_extra=1000),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE_CASES))
+def test_edge_case_parity(case):
+    spec = dict(EDGE_CASES[case])
+    cap_extra = spec.pop("cap_extra", 0)
+    w, idx, x, wts = _edge(**spec)
+    say(f"[edge] {case}")
+    _check_layout(idx, w.E, w.R)
+    cap = oracle.capacity(w.T, w.K, w.E, w.align) + cap_extra
+    x_dev, recv_x, h, o = _dispatch_and_check(w, idx, x, align=w.align, cap=cap)
+    y = synth.normal_bf16(synth.stream_key(7, 99, 5), cap * w.H).reshape(cap, w.H)
+    out = cgd.combine(dev_bf16(y), h, dev_f32(wts))
+    torch.cuda.synchronize()
+    exp = oracle.combine(y, o["dst_row"], wts)
+    frac = check_combine(host_bits(out), exp, term_magnitude(y, o["dst_row"], wts))
+    assert frac > 0.99
+    # tokens with no selected slot combine to +0
+    empty = (idx < 0).all(axis=1)
+    assert (host_bits(out)[empty] == 0).all()
+
+
+def test_zero_tokens():
+    w, idx, x, wts = _edge(T=0, K=4, E=16, R=4, H=64)
+    ntpr, ntpe, itr = _run_layout(idx, w.E, w.R)
+    assert ntpr.tolist() == [0] * 4 and ntpe.tolist() == [0] * 16 and itr.shape == (0, 4)
+    recv_x, h = cgd.dispatch(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
+                             torch.empty((0, 4), dtype=torch.int64, device=DEV), 16, 4, expert_alignment=4)
+    out = cgd.combine(recv_x, h, torch.empty((0, 4), dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert h.expert_offset.cpu().tolist() == [0] * 17
+    assert (h.recv_src_idx.cpu().numpy() == -1).all() and h.recv_capacity == 16 * 3
+    assert out.shape == (0, 64)
+
+
+def test_one_workspace_serves_many_sizes():
+    # the self-resetting workspace must be left zeroed by every call
+    for T in (1000, 3, 4096, 257, 1):
+        w, idx, x, wts = _edge(T=T, K=8, E=256, R=8, H=64, seed=T)
+        _check_layout(idx, w.E, w.R)
+        _dispatch_and_check(w, idx, x)
+
+
+def _digest(*ts):
+    h = hashlib.sha256()
+    for t in ts:
+        h.update(t.contiguous().view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def test_determinism_20_repeats():
+    w = synth.WORKLOADS["prefill"]
+    inp = synth.make_inputs(w, seed=5)
+    x, idx, wt = dev_bf16(inp["x"]), dev_i64(inp["topk_idx"]), dev_f32(inp["topk_weights"])
+    ref = None
+    for i in range(20):
+        ntpr, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx, w.E, w.R)
+        recv_x, h = cgd.dispatch(x, idx, w.E, w.R)
+        out = cgd.combine(recv_x, h, wt)
+        torch.cuda.synchronize()
+        d = _digest(ntpr, ntpe, itr, h.expert_offset, h.dst_row, h.recv_src_idx, recv_x, out)
+        if ref is None:
+            ref = d
+        assert d == ref, f"repeat {i} differs"
+
+
+def test_seeds_sweep_prefill_and_skewed():
+    for name in ("prefill", "skewed"):
+        w = synth.WORKLOADS[name]
+        for seed in (1, 2, 3, 4):
+            idx = synth.make_topk_idx(w, seed)
+            _check_layout(idx, w.E, w.R)
+            idx_dev = dev_i64(idx)
+            x_small = torch.zeros((w.T, 8), dtype=torch.bfloat16, device=DEV)
+            _, h = cgd.dispatch(x_small, idx_dev, w.E, w.R)
+            torch.cuda.synchronize()
+            o = oracle.dispatch(None, idx, w.E, w.R, with_rows=False)
+            np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+            np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
