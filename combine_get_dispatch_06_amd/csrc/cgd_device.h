@@ -50,26 +50,47 @@ __device__ __forceinline__ void store_nt(uint4* p, const uint4& v) {
     __builtin_nontemporal_store(v.w, &p->w);
 }
 
-// Last-block-done handshake across the whole grid (blocks may sit on
-// different XCDs, each with its own L2). Every thread publishes its global
-// writes with a device-scope fence, then one thread takes a ticket; the block
-// that takes the last ticket sees all other blocks' writes after its own
-// acquire fence, and resets the ticket for the next launch.
-__device__ __forceinline__ bool last_block_done(unsigned int* ticket) {
+// Copy n (<= ITEMS * blockDim.x) routing entries of one tile into LDS as
+// int32, entries outside [0, E) becoming -1. All global loads of a thread are
+// issued before any LDS store, so the tile costs one memory round trip.
+template <int ITEMS>
+__device__ __forceinline__ void stage_routing(const int64_t* __restrict__ src, int n, int E, int32_t* dst) {
+    int64_t v[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int i = threadIdx.x + j * blockDim.x;
+        v[j] = (i < n) ? src[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int i = threadIdx.x + j * blockDim.x;
+        if (i < n) dst[i] = (v[j] >= 0 && v[j] < E) ? (int32_t)v[j] : -1;
+    }
+}
+
+// Cross-block synchronisation. Blocks of one grid may sit on different XCDs,
+// each with its own L2. On gfx950 a device-scope release writes back the XCD's
+// L2 and a device-scope acquire invalidates it, so each is issued once per
+// block by thread 0, ordered with the block's other waves by a barrier.
+
+// Last-block-done handshake among `nblocks` blocks: each block publishes its
+// writes and takes a ticket; the block that takes the last ticket acquires
+// every other block's writes and must reset the ticket (reset_ticket).
+__device__ __forceinline__ bool last_block_done(unsigned int* ticket, unsigned int nblocks) {
     __shared__ bool s_last;
-    __threadfence();
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned int prev = atomicAdd(ticket, 1u);
-        s_last = (prev == gridDim.x - 1);
+        const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == nblocks - 1);
     }
     __syncthreads();
-    if (s_last) __threadfence();
     return s_last;
 }
 
+__device__ __forceinline__ bool last_block_done(unsigned int* ticket) { return last_block_done(ticket, gridDim.x); }
+
 __device__ __forceinline__ void reset_ticket(unsigned int* ticket) {
-    if (threadIdx.x == 0) atomicExch(ticket, 0u);
+    if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace cgd

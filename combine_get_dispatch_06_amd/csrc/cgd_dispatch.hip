@@ -7,26 +7,27 @@
 // a segment, rows follow ascending (token, slot), which makes the permutation
 // unique and independent of scheduling.
 //
-// Two launches:
+// Two launches, no block ever waits for another:
 //   rank_kernel     one block per tile of 256 tokens (4 waves, one token per
 //                   lane). For each slot it finds the number of earlier slots
-//                   of the tile with the same expert: inside a wave with
-//                   wavefront ballots (a "multi-split": lanes whose expert
-//                   agrees with mine on every bit of the expert id are my
-//                   peers; popcount of the peers below my lane), across the
-//                   tile's waves with an LDS histogram and a prefix over
-//                   waves. It writes the tile's expert histogram and a packed
-//                   (expert, rank-in-tile) word per slot. The last block to
-//                   finish turns the tile histograms into per-tile bases
-//                   (column prefix over tiles), computes the aligned segment
-//                   offsets with a block prefix scan, and marks padding rows.
+//                   of the tile with the same expert. When no token of the
+//                   tile repeats an expert, each wave sets one bit per (expert,
+//                   lane) in a 64-bit LDS mask per expert; the rank is the
+//                   popcount of the mask below the lane plus the rows of
+//                   earlier waves. Otherwise it counts slot by slot with
+//                   wavefront ballots (a "multi-split" over the bits of the
+//                   expert id). It writes a packed (expert, rank-in-tile) word
+//                   per slot and the tile's expert histogram. The last block
+//                   to finish turns the histograms into per-tile bases (column
+//                   prefix over tiles plus the aligned segment offsets from a
+//                   block prefix scan) and marks padding rows.
 //   scatter_kernel  one wave per token: lanes 0..K-1 turn their slot into a
-//                   final row (tile base + rank-in-tile), record dst_row and
-//                   recv_src_idx, then the whole wave streams the token's row
+//                   final row (tile base + rank-in-tile) and record dst_row
+//                   and recv_src_idx; the wave streams the token's row
 //                   through registers in 16-byte vectors and stores it to the
 //                   K destination rows with non-temporal stores. The row is
 //                   read from HBM once however many experts it goes to.
-// Cached dispatch runs scatter_kernel alone on a stored dst_row.
+// Cached dispatch runs the scatter kernel on a stored final dst_row.
 #include "cgd_device.h"
 #include "cgd_launch.h"
 
@@ -34,108 +35,166 @@ namespace cgd {
 
 constexpr int kRankWaves = kRankTile / kWave;
 constexpr int kPackBits = 13;  // rank inside a tile < 256 * 16 = 4096 < 2^13
-constexpr int kScatterWaves = 4;
+#ifndef CGD_SCATTER_WAVES
+#define CGD_SCATTER_WAVES 4
+#endif
+#ifndef CGD_SCATTER_U
+#define CGD_SCATTER_U 4
+#endif
+#ifndef CGD_SCATTER_NT
+#define CGD_SCATTER_NT 1
+#endif
+constexpr int kScatterWaves = CGD_SCATTER_WAVES;  // tokens (waves) per scatter block
+constexpr int kBatch = 16;                        // loads in flight per thread when summing columns
 
-template <int KT>
-__global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int E,
+// LDS of the rank kernel, carved from dynamic shared memory sized for (E, K).
+size_t rank_lds_bytes(int E, int K) {
+    return (size_t)kRankWaves * E * 8      // tok: lanes of a wave holding expert e
+           + (size_t)kRankWaves * E * 4    // pre: rows of expert e in earlier waves of the tile
+           + (size_t)kRankTile * K * 4     // slot: routing of the tile, then packed rows
+           + (size_t)(E + 1) * 4           // off: segment offsets (last block)
+           + kRankWaves * 4 + 16;          // wsum
+}
+
+// Expert of a slot word during the duplicate-aware count (-1: not selected).
+__device__ __forceinline__ int slot_expert(int v) { return v < 0 ? -1 : (v & 0xFFFF); }
+
+// Slot loops read the routing from LDS, which keeps the kernel light on
+// registers for any num_topk.
+__global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
                                                          int ebits, int A, int32_t* __restrict__ dst_row,
                                                          int32_t* __restrict__ tile_base,
                                                          int32_t* __restrict__ expert_offset,
                                                          int32_t* __restrict__ recv_src_idx,
                                                          unsigned int* __restrict__ ticket) {
-    __shared__ int32_t s_idx[kRankTile * KT];
-    __shared__ int32_t s_wh[kRankWaves][kMaxExperts];
-    __shared__ int32_t s_off[kMaxExperts + 1];
-    __shared__ int32_t s_wsum[kRankWaves];
+    extern __shared__ __align__(16) char lds[];
+    unsigned long long* s_tok = reinterpret_cast<unsigned long long*>(lds);
+    int32_t* s_pre = reinterpret_cast<int32_t*>(s_tok + kRankWaves * E);
+    int32_t* s_slot = s_pre + kRankWaves * E;
+    int32_t* s_off = s_slot + kRankTile * K;
+    int32_t* s_wsum = s_off + E + 1;
+    const int tile = blockIdx.x;
+    const int ntiles = gridDim.x;
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = lane_id();
-    const int64_t t0 = (int64_t)blockIdx.x * kRankTile;
+    const int64_t t0 = (int64_t)tile * kRankTile;
     const int nt = (int)max<int64_t>(0, min<int64_t>(kRankTile, T - t0));
 
-    for (int i = tid; i < kRankWaves * kMaxExperts; i += kRankTile) (&s_wh[0][0])[i] = 0;
-    {
-        const int64_t* src = topk_idx + t0 * KT;
-        const int n = nt * KT;
-        for (int i = tid; i < n; i += kRankTile) {
-            const int64_t e = src[i];
-            s_idx[i] = (e >= 0 && e < E) ? (int32_t)e : -1;
-        }
+    for (int i = tid; i < kRankWaves * E; i += kRankTile) {
+        s_tok[i] = 0ull;
+        s_pre[i] = 0;
     }
+    stage_routing<kMaxTopk>(topk_idx + t0 * K, nt * K, E, s_slot);
     __syncthreads();
 
-    int e[KT], rk[KT];
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        e[k] = (tid < nt) ? s_idx[tid * KT + k] : -1;
-        rk[k] = 0;
-    }
-
-    // rank inside the wave: earlier lanes (tokens) holding my expert in any
-    // slot, plus earlier slots of my own token holding it
+    int32_t* my = s_slot + tid * K;  // this token's K slots
+    const bool mine = tid < nt;
     const uint64_t lt = lanemask_lt();
+    const uint64_t bit = 1ull << lane;
+    int e[kMaxTopk];
 #pragma unroll
-    for (int kp = 0; kp < KT; ++kp) {
-        const uint64_t valid = ballot(e[kp] >= 0);
-        uint64_t bits[10];
+    for (int k = 0; k < kMaxTopk; ++k) e[k] = (mine && k < K) ? my[k] : -1;
+
+    // ---- 1. rank of every slot inside the tile; tile histogram ----
+    // Each wave sets one bit per (expert, lane) in a 64-bit LDS mask per
+    // expert. The previous mask returned by the atomic also tells whether this
+    // token already holds the expert in an earlier slot.
+    bool dup = false;
 #pragma unroll
-        for (int b = 0; b < 10; ++b) bits[b] = (b < ebits) ? ballot((e[kp] >> b) & 1) : 0ull;
+    for (int k = 0; k < kMaxTopk; ++k)
+        if (e[k] >= 0) dup |= (atomicOr(&s_tok[wave * E + e[k]], bit) & bit) != 0;
+    if (!__syncthreads_or(dup)) {
+        // Every token holds an expert at most once: the rank of (t,k) among
+        // the tile's rows of expert e is the number of earlier tokens holding
+        // e: the lanes below mine in my wave's mask plus earlier waves' rows.
+        for (int x = tid; x < E; x += kRankTile) {
+            int run = 0;
 #pragma unroll
-        for (int k = 0; k < KT; ++k) {
-            uint64_t peers = valid;
-#pragma unroll
-            for (int b = 0; b < 10; ++b)
-                if (b < ebits) peers &= ((e[k] >> b) & 1) ? bits[b] : ~bits[b];
-            rk[k] += __popcll(peers & lt) + ((kp < k && e[kp] == e[k]) ? 1 : 0);
+            for (int w = 0; w < kRankWaves; ++w) {
+                s_pre[w * E + x] = run;
+                run += __popcll(s_tok[w * E + x]);
+            }
+            tile_base[(int64_t)tile * E + x] = run;
         }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k)
+            if (e[k] >= 0)
+                my[k] = (e[k] << kPackBits) | (s_pre[wave * E + e[k]] + __popcll(s_tok[wave * E + e[k]] & lt));
+    } else {
+        // Some token repeats an expert: count slot by slot. Lanes whose k'-th
+        // expert agrees with my k-th expert on every bit of the expert id are
+        // its peers in column k' ("multi-split" ballots); peers below my lane
+        // plus my own earlier equal slots give the rank inside the wave. Until
+        // the wave prefixes are known a slot word holds expert | rank << 16.
+        for (int k = 0; k < K; ++k) {
+            const int e = mine ? slot_expert(my[k]) : -1;
+            int rk = 0;
+            for (int kp = 0; kp < K; ++kp) {
+                const int ep = mine ? slot_expert(my[kp]) : -1;
+                uint64_t peers = ballot(ep >= 0);
+                for (int b = 0; b < ebits; ++b) {
+                    const uint64_t col = ballot((ep >> b) & 1);
+                    peers &= ((e >> b) & 1) ? col : ~col;
+                }
+                rk += __popcll(peers & lt) + ((kp < k && ep == e) ? 1 : 0);
+            }
+            if (e >= 0) {
+                atomicAdd(&s_pre[wave * E + e], 1);
+                my[k] = e | (rk << 16);
+            }
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += kRankTile) {
+            int run = 0;
+#pragma unroll
+            for (int w = 0; w < kRankWaves; ++w) {
+                const int c = s_pre[w * E + x];
+                s_pre[w * E + x] = run;
+                run += c;
+            }
+            tile_base[(int64_t)tile * E + x] = run;
+        }
+        __syncthreads();
+        if (mine)
+            for (int k = 0; k < K; ++k) {
+                const int v = my[k];
+                if (v >= 0) {
+                    const int e = v & 0xFFFF;
+                    my[k] = (e << kPackBits) | ((v >> 16) + s_pre[wave * E + e]);
+                }
+            }
     }
 
-#pragma unroll
-    for (int k = 0; k < KT; ++k)
-        if (e[k] >= 0) atomicAdd(&s_wh[wave][e[k]], 1);
-    __syncthreads();
-
-    // per expert: prefix over the tile's waves; the total is the tile histogram
-    for (int x = tid; x < E; x += kRankTile) {
-        int run = 0;
-#pragma unroll
-        for (int w = 0; w < kRankWaves; ++w) {
-            const int c = s_wh[w][x];
-            s_wh[w][x] = run;
-            run += c;
-        }
-        tile_base[(int64_t)blockIdx.x * E + x] = run;
-    }
-    __syncthreads();
-
-    // packed (expert, rank-in-tile) per slot, staged in LDS for coalesced stores
-#pragma unroll
-    for (int k = 0; k < KT; ++k)
-        if (tid < nt) s_idx[tid * KT + k] = (e[k] >= 0) ? ((e[k] << kPackBits) | (s_wh[wave][e[k]] + rk[k])) : -1;
     __syncthreads();
     {
-        int32_t* out = dst_row + t0 * KT;
-        const int n = nt * KT;
-        for (int i = tid; i < n; i += kRankTile) out[i] = s_idx[i];
+        int32_t* out = dst_row + t0 * K;
+        const int n = nt * K;
+        for (int i = tid; i < n; i += kRankTile) out[i] = s_slot[i];
     }
 
     if (!last_block_done(ticket)) return;
 
-    // ---- last block: tile bases, segment offsets, padding rows ----
-    const int ntiles = gridDim.x;
-    // 1. rows per expert = sum of the tile histograms
+    // ---- 2. last block: segment offsets and per-tile bases ----
+    // rows per expert = sum of the tile histograms
     for (int x = tid; x < E; x += kRankTile) {
-        int s = 0;
-        for (int b = 0; b < ntiles; ++b) s += tile_base[(int64_t)b * E + x];
-        s_wh[0][x] = s;
+        int sum = 0;
+        for (int b0 = 0; b0 < ntiles; b0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) v[j] = (b0 + j < ntiles) ? tile_base[(int64_t)(b0 + j) * E + x] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) sum += v[j];
+        }
+        s_pre[x] = sum;
     }
     __syncthreads();
-    // 2. exclusive scan of the aligned sizes: thread i owns entries 2i, 2i+1
-    {
+    {  // exclusive scan of the aligned sizes: thread i owns entries 2i, 2i+1
         const int i0 = 2 * tid, i1 = 2 * tid + 1;
-        const int c0 = (i0 < E) ? (s_wh[0][i0] + A - 1) / A * A : 0;
-        const int c1 = (i1 < E) ? (s_wh[0][i1] + A - 1) / A * A : 0;
+        const int c0 = (i0 < E) ? (s_pre[i0] + A - 1) / A * A : 0;
+        const int c1 = (i1 < E) ? (s_pre[i1] + A - 1) / A * A : 0;
         const int own = c0 + c1;
         int inc = own;
 #pragma unroll
@@ -153,14 +212,18 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         if (tid == kRankTile - 1) s_off[E] = before + inc;  // entries >= E add 0
     }
     __syncthreads();
-    // 3. per-tile bases (segment offset + rows of earlier tiles), padding rows
+    // per-tile bases (segment offset + rows of earlier tiles), padding rows
     for (int x = tid; x < E; x += kRankTile) {
         int run = s_off[x];
-        for (int b = 0; b < ntiles; ++b) {
-            int32_t* p = tile_base + (int64_t)b * E + x;
-            const int h = *p;
-            *p = run;
-            run += h;
+        for (int b0 = 0; b0 < ntiles; b0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) v[j] = (b0 + j < ntiles) ? tile_base[(int64_t)(b0 + j) * E + x] : 0;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (b0 + j < ntiles) tile_base[(int64_t)(b0 + j) * E + x] = run;
+                run += v[j];
+            }
         }
         for (int r = run; r < s_off[x + 1]; ++r) recv_src_idx[r] = -1;
     }
@@ -168,17 +231,65 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     reset_ticket(ticket);
 }
 
-// One wave per token. PACKED: dst_row holds rank_kernel's packed words and is
-// rewritten with final rows (non-cached dispatch); otherwise dst_row holds
-// final rows and is only read (cached dispatch).
-template <int KM, int U, bool PACKED>
-__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(
-    const uint4* __restrict__ x, int64_t T, int nvec, int K, int32_t* __restrict__ dst_row,
-    const int32_t* __restrict__ tile_base, int E, int32_t* __restrict__ recv_src_idx,
-    const int32_t* __restrict__ expert_offset, int64_t cap, uint4* __restrict__ recv_x) {
-    const int wave = threadIdx.x / kWave;
+// Stores the token's row (nvec 16-byte vectors) to its destination rows dk[]
+// (entries < 0 skipped). The first PF vectors per lane are already in pre[];
+// the rest stream through registers U vectors per lane at a time.
+template <int KM, int U, int PF>
+__device__ __forceinline__ void store_row(const uint4* __restrict__ xr, int nvec, const int (&dk)[KM],
+                                          uint4* __restrict__ recv_x, const uint4 (&pre)[PF]) {
     const int lane = lane_id();
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        if (dk[k] < 0) continue;
+        uint4* dr = recv_x + (int64_t)dk[k] * nvec;
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            const int v = u * kWave + lane;
+            if (v < nvec) {
+                if (CGD_SCATTER_NT)
+                    store_nt(dr + v, pre[u]);
+                else
+                    dr[v] = pre[u];
+            }
+        }
+    }
+    for (int v0 = PF * kWave; v0 < nvec; v0 += U * kWave) {
+        uint4 buf[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < nvec) buf[u] = xr[v];
+        }
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+            if (dk[k] < 0) continue;
+            uint4* dr = recv_x + (int64_t)dk[k] * nvec;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * kWave + lane;
+                if (v < nvec) {
+                    if (CGD_SCATTER_NT)
+                        store_nt(dr + v, buf[u]);
+                    else
+                        dr[v] = buf[u];
+                }
+            }
+        }
+    }
+}
 
+// One wave per token. PACKED: dst_row holds rank_kernel's packed words and is
+// rewritten with final rows, and recv_src_idx is filled (non-cached
+// dispatch); otherwise dst_row holds final rows and is only read (cached
+// dispatch).
+template <int KM, int U, bool PACKED>
+__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t T, int nvec,
+                                                                      int K, int32_t* __restrict__ dst_row,
+                                                                      const int32_t* __restrict__ tile_base, int E,
+                                                                      int32_t* __restrict__ recv_src_idx,
+                                                                      const int32_t* __restrict__ expert_offset,
+                                                                      int64_t cap, uint4* __restrict__ recv_x) {
+    const int lane = lane_id();
     if (PACKED) {
         // rows past the data carry no source token
         const int64_t n = expert_offset[E];
@@ -186,10 +297,15 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(
         for (int64_t r = n + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < cap; r += stride)
             recv_src_idx[r] = -1;
     }
-
-    const int64_t t = (int64_t)blockIdx.x * kScatterWaves + wave;
+    const int64_t t = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     if (t >= T) return;
-
+    const uint4* xr = x + t * nvec;
+    uint4 pre[U];  // first pass of the row, loaded before the indices arrive
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int v = u * kWave + lane;
+        if (v < nvec) pre[u] = xr[v];
+    }
     int d = -1;
     if (lane < K) {
         const int p = dst_row[t * K + lane];
@@ -209,39 +325,13 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(
     int dk[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) dk[k] = __shfl(d, k, kWave);
-
-    const uint4* xr = x + t * nvec;
-    for (int v0 = 0; v0 < nvec; v0 += U * kWave) {
-        uint4 buf[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * kWave + lane;
-            if (v < nvec) buf[u] = xr[v];
-        }
-#pragma unroll
-        for (int k = 0; k < KM; ++k) {
-            if (dk[k] < 0) continue;
-            uint4* dr = recv_x + (int64_t)dk[k] * nvec;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * kWave + lane;
-                if (v < nvec) store_nt(dr + v, buf[u]);
-            }
-        }
-    }
+    store_row<KM, U, U>(xr, nvec, dk, recv_x, pre);
 }
 
 size_t dispatch_workspace_bytes(int64_t T, int E) {
     const int64_t ntiles = T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile;
     const size_t arr = (size_t)ntiles * (size_t)E * sizeof(int32_t);
     return kTicketBytes + (arr + 255) / 256 * 256;
-}
-
-template <int KT>
-static void launch_rank(dim3 grid, hipStream_t s, const int64_t* idx, int64_t T, int E, int ebits, int A,
-                        int32_t* dst_row, int32_t* tile_base, int32_t* off, int32_t* src, unsigned int* ticket) {
-    hipLaunchKernelGGL(rank_kernel<KT>, grid, dim3(kRankTile), 0, s, idx, T, E, ebits, A, dst_row, tile_base, off,
-                       src, ticket);
 }
 
 template <bool PACKED>
@@ -252,17 +342,17 @@ static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int n
     const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint4* rv = reinterpret_cast<uint4*>(recv_x);
-#define CGD_SCATTER(KM, U) \
-    hipLaunchKernelGGL((scatter_kernel<KM, U, PACKED>), grid, block, 0, s, xv, T, nvec, K, dst_row, tile_base, E, \
-                       src, off, cap, rv)
+#define CGD_SCATTER(KM)                                                                                            \
+    hipLaunchKernelGGL((scatter_kernel<KM, CGD_SCATTER_U, PACKED>), grid, block, 0, s, xv, T, nvec, K, dst_row,     \
+                       tile_base, E, src, off, cap, rv)
     if (K <= 2)
-        CGD_SCATTER(2, 8);
+        CGD_SCATTER(2);
     else if (K <= 4)
-        CGD_SCATTER(4, 8);
+        CGD_SCATTER(4);
     else if (K <= 8)
-        CGD_SCATTER(8, 8);
+        CGD_SCATTER(8);
     else
-        CGD_SCATTER(16, 8);
+        CGD_SCATTER(16);
 #undef CGD_SCATTER
 }
 
@@ -271,22 +361,11 @@ hipError_t launch_dispatch(const void* x, int64_t T, int H, const int64_t* topk_
                            int32_t* dst_row, void* workspace, hipStream_t stream) {
     unsigned int* ticket = reinterpret_cast<unsigned int*>(workspace);
     int32_t* tile_base = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + kTicketBytes);
-    const dim3 grid((unsigned)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile));
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
-    switch (K) {
-#define CGD_RANK_CASE(KT) \
-    case KT:              \
-        launch_rank<KT>(grid, stream, topk_idx, T, E, ebits, A, dst_row, tile_base, expert_offset, recv_src_idx, ticket); \
-        break;
-        CGD_RANK_CASE(1) CGD_RANK_CASE(2) CGD_RANK_CASE(3) CGD_RANK_CASE(4)
-        CGD_RANK_CASE(5) CGD_RANK_CASE(6) CGD_RANK_CASE(7) CGD_RANK_CASE(8)
-        CGD_RANK_CASE(9) CGD_RANK_CASE(10) CGD_RANK_CASE(11) CGD_RANK_CASE(12)
-        CGD_RANK_CASE(13) CGD_RANK_CASE(14) CGD_RANK_CASE(15) CGD_RANK_CASE(16)
-#undef CGD_RANK_CASE
-        default:
-            return hipErrorInvalidValue;
-    }
+    const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
+    hipLaunchKernelGGL(rank_kernel, dim3(ntiles), dim3(kRankTile), rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
+                       ebits, A, dst_row, tile_base, expert_offset, recv_src_idx, ticket);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     launch_scatter<true>(T, K, stream, x, H / 8, dst_row, tile_base, E, recv_src_idx, expert_offset, cap, recv_x);

@@ -33,36 +33,34 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     __shared__ uint64_t s_mask[kLayoutTile * RW];
     __shared__ int32_t s_hist[kMaxExperts];
     __shared__ int32_t s_rank[kMaxRanks];
+    __shared__ int16_t s_rank_of[kMaxExperts];  // rank owning expert e
 
     const int tid = threadIdx.x;
     const int64_t t0 = (int64_t)blockIdx.x * kLayoutTile;
     const int nt = (int)max<int64_t>(0, min<int64_t>(kLayoutTile, T - t0));
 
-    for (int i = tid; i < E; i += kLayoutTile) s_hist[i] = 0;
-    for (int i = tid; i < R; i += kLayoutTile) s_rank[i] = 0;
-    {
-        const int64_t* src = topk_idx + t0 * K;
-        const int n = nt * K;
-        for (int i = tid; i < n; i += kLayoutTile) {
-            const int64_t e = src[i];
-            s_idx[i] = (e >= 0 && e < E) ? (int32_t)e : -1;
-        }
+    for (int i = tid; i < E; i += kLayoutTile) {
+        s_hist[i] = 0;
+        s_rank_of[i] = (int16_t)(i / L);
     }
+    for (int i = tid; i < R; i += kLayoutTile) s_rank[i] = 0;
+    stage_routing<kMaxTopk>(topk_idx + t0 * K, nt * K, E, s_idx);
     __syncthreads();
 
+    int e[kMaxTopk];
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) e[k] = (tid < nt && k < K) ? s_idx[tid * K + k] : -1;
     uint64_t m[RW];
 #pragma unroll
     for (int w = 0; w < RW; ++w) m[w] = 0;
-    if (tid < nt) {
-        for (int k = 0; k < K; ++k) {
-            const int e = s_idx[tid * K + k];
-            if (e >= 0) {
-                atomicAdd(&s_hist[e], 1);
-                const int r = e / L;
 #pragma unroll
-                for (int w = 0; w < RW; ++w)
-                    if ((r >> 6) == w) m[w] |= 1ull << (r & 63);
-            }
+    for (int k = 0; k < kMaxTopk; ++k) {
+        if (e[k] >= 0) {
+            atomicAdd(&s_hist[e[k]], 1);
+            const int r = s_rank_of[e[k]];
+#pragma unroll
+            for (int w = 0; w < RW; ++w)
+                if ((r >> 6) == w) m[w] |= 1ull << (r & 63);
         }
     }
 
@@ -127,13 +125,15 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
 
     const int nblk = gridDim.x;
     for (int i = tid; i < W; i += kLayoutTile) {
+        // loads issued 16 at a time: few round trips however many blocks
         int s = 0;
-        int b = 0;
-        for (; b + 4 <= nblk; b += 4) {
-            const int32_t* p = partial + (int64_t)b * W + i;
-            s += p[0] + p[W] + p[2 * W] + p[3 * W];
+        for (int b0 = 0; b0 < nblk; b0 += 16) {
+            int v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = (b0 + j < nblk) ? partial[(int64_t)(b0 + j) * W + i] : 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s += v[j];
         }
-        for (; b < nblk; ++b) s += partial[(int64_t)b * W + i];
         if (i < E)
             ntpe[i] = s;
         else
