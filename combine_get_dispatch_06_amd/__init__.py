@@ -24,8 +24,8 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["get_dispatch_layout", "dispatch", "combine", "DispatchHandle", "CgdError", "library_path",
-           "dispatch_capacity", "load"]
+__all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply", "combine", "DispatchHandle",
+           "CgdError", "library_path", "dispatch_capacity", "load"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -73,6 +73,10 @@ def load():
     lib.cgd_get_dispatch_layout.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch.restype = i32
     lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_plan.restype = i32
+    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_apply.restype = i32
+    lib.cgd_dispatch_apply.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_cached.restype = i32
     lib.cgd_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
     lib.cgd_combine.restype = i32
@@ -234,6 +238,60 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor | None = None, num_experts:
                                 _ptr(recv_x), cap, _ptr(off), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(),
                                 _stream(dev)))
     return recv_x, DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+
+
+@dataclass
+class DispatchPlan:
+    """Result of dispatch_plan: the handle-to-be plus the workspace that
+    dispatch_apply must receive. Not a valid handle until applied."""
+    handle: DispatchHandle
+    workspace: torch.Tensor
+    num_tokens: int
+
+
+def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expert_alignment: int = 1,
+                  recv_capacity: int | None = None) -> DispatchPlan:
+    """First step of dispatch: receive-buffer layout from the routing alone."""
+    lib = load()
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    with torch.cuda.device(dev):
+        need = int(lib.cgd_dispatch_capacity(T, K, num_experts, expert_alignment))
+        cap = need if recv_capacity is None else int(recv_capacity)
+        off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        dst = torch.empty((T, K), dtype=torch.int32, device=dev)
+        nbytes = lib.cgd_dispatch_workspace_bytes(T, K, num_experts)
+        ws = _workspace(dev, "dispatch", nbytes)
+        _check("cgd_dispatch_plan",
+               lib.cgd_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap, _ptr(off),
+                                     _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+    h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+    return DispatchPlan(h, ws, T)
+
+
+def dispatch_apply(x: torch.Tensor, plan: DispatchPlan, recv_x: torch.Tensor | None = None):
+    """Second step of dispatch: finalise the handle and copy rows.
+    Returns (recv_x, handle)."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    h = plan.handle
+    if T != plan.num_tokens:
+        raise ValueError("x has a different number of tokens than the plan")
+    dev = x.device
+    with torch.cuda.device(dev):
+        if recv_x is None:
+            recv_x = torch.empty((h.recv_capacity, H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+        if recv_x.shape != (h.recv_capacity, H):
+            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        _check("cgd_dispatch_apply",
+               lib.cgd_dispatch_apply(_ptr(x), T, H, h.num_topk, h.num_experts, h.recv_capacity, _ptr(recv_x),
+                                      _ptr(h.expert_offset), _ptr(h.recv_src_idx), _ptr(h.dst_row),
+                                      _ptr(plan.workspace), plan.workspace.numel(), _stream(dev)))
+    return recv_x, h
 
 
 def combine(expert_out: torch.Tensor, handle: DispatchHandle, topk_weights: torch.Tensor,

@@ -101,33 +101,92 @@ int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num
     return CGD_OK;
 }
 
+// Checks shared by the dispatch entry points.
+static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
+                           const int32_t* expert_offset, const int32_t* recv_src_idx, const int32_t* dst_row,
+                           const void* workspace, size_t workspace_bytes) {
+    int rc = check_routing_sizes(T, K, E, R);
+    if (rc) return rc;
+    if (A < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
+    const int64_t need_rows = capacity_of(T, K, E, A);
+    if (need_rows < 0) return fail(CGD_ERR_INVALID_ARG, "receive capacity for these sizes exceeds INT32_MAX");
+    if (cap < need_rows || cap > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
+                    (long long)cap);
+    if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
+    if (T > 0 && (!topk_idx || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null topk_idx or dst_row");
+    if (cap > 0 && !recv_src_idx) return fail(CGD_ERR_INVALID_ARG, "null recv_src_idx");
+    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
+    const size_t need = cgd::dispatch_workspace_bytes(T, E);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    return CGD_OK;
+}
+
+static int check_apply_args(const void* x, int64_t T, int H, int K, int E, int64_t cap, const void* recv_x,
+                            const int32_t* expert_offset, const int32_t* recv_src_idx, const int32_t* dst_row,
+                            const void* workspace, size_t workspace_bytes) {
+    if (T < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (K < 1 || K > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16] (got %d)", K);
+    if (E < 1 || E > cgd::kMaxExperts) return fail(CGD_ERR_INVALID_ARG, "num_experts must be in [1,512] (got %d)", E);
+    int rc = check_hidden(H);
+    if (rc) return rc;
+    if (cap < 0 || cap > INT32_MAX) return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
+    if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
+    if (T > 0 && (!x || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null x or dst_row");
+    if (cap > 0 && (!recv_x || !recv_src_idx)) return fail(CGD_ERR_INVALID_ARG, "null receive pointer");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+    if (!aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
+    const size_t need = cgd::dispatch_workspace_bytes(T, E);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    return CGD_OK;
+}
+
+int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
+                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
+                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+    if (rc) return rc;
+    hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
+                                               expert_offset, recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
+    return CGD_OK;
+}
+
+int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,
+                       int32_t* dst_row, const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x, expert_offset,
+                              recv_src_idx, dst_row, workspace, workspace_bytes);
+    if (rc) return rc;
+    hipError_t err = cgd::launch_dispatch_apply(x, num_tokens, hidden, num_topk, num_experts, recv_x, recv_capacity,
+                                                expert_offset, recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "dispatch apply launch");
+    return CGD_OK;
+}
+
 int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
                  int num_experts, int num_ranks, int expert_alignment, void* recv_x, int64_t recv_capacity,
                  int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
-    int rc = check_routing_sizes(num_tokens, num_topk, num_experts, num_ranks);
+    int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
+                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
     if (rc) return rc;
-    if ((rc = check_hidden(hidden))) return rc;
-    if (expert_alignment < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
-    const int64_t need_rows = capacity_of(num_tokens, num_topk, num_experts, expert_alignment);
-    if (need_rows < 0) return fail(CGD_ERR_INVALID_ARG, "receive capacity for these sizes exceeds INT32_MAX");
-    if (recv_capacity < need_rows || recv_capacity > INT32_MAX)
-        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
-                    (long long)recv_capacity);
-    if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
-    if (num_tokens > 0 && (!x || !topk_idx || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null input pointer");
-    if (recv_capacity > 0 && (!recv_x || !recv_src_idx)) return fail(CGD_ERR_INVALID_ARG, "null receive pointer");
-    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
-    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
-        return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
-    const size_t need = cgd::dispatch_workspace_bytes(num_tokens, num_experts);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-        return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                    workspace_bytes);
-    hipError_t err = cgd::launch_dispatch(x, num_tokens, hidden, topk_idx, num_topk, num_experts, expert_alignment,
-                                          recv_x, recv_capacity, expert_offset, recv_src_idx, dst_row, workspace,
-                                          stream);
-    if (err != hipSuccess) return hip_fail(err, "dispatch launch");
+    if ((rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x, expert_offset,
+                               recv_src_idx, dst_row, workspace, workspace_bytes)))
+        return rc;
+    hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
+                                               expert_offset, recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
+    err = cgd::launch_dispatch_apply(x, num_tokens, hidden, num_topk, num_experts, recv_x, recv_capacity,
+                                     expert_offset, recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "dispatch apply launch");
     return CGD_OK;
 }
 

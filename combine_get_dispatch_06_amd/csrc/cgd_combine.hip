@@ -5,15 +5,17 @@
 // (DeepEP legacy test analysis page, low-latency combine check: the result is
 // x scaled by the sum of the unmasked weights when experts are identities).
 //
-// Work is split into (token, column chunk) pieces, one wave each: a chunk is
-// 64*U 16-byte vectors (1 KB per U) of the row. Many short-lived waves keep
-// the gathered reads well spread over the HBM channels (measured ~10% faster
-// at the prefill shape than one long-lived wave per token). Lanes 0..K-1 read
-// the token's K rows and weights and broadcast them; each lane then issues its
-// K*U gathered 16-byte loads before any arithmetic, accumulates in fp32 with
-// fused multiply-add in ascending k from +0, converts to bf16 with round to
-// nearest even, and writes its chunk once. Expert rows are read with
-// non-temporal loads (each is read exactly once).
+// Work is split into (token, column chunk) items, a chunk being 64*U
+// 16-byte vectors (1 KB per U) of the row, one wave each; blocks start in
+// item order, so the gathers in flight stay close together. Residency is
+// capped at 5 blocks per CU (an LDS reservation): fewer concurrent gathers per
+// CU and many short items measured faster than one long-lived wave per token
+// or full occupancy.
+// Lanes 0..K-1 read the token's K rows and weights and broadcast them; each
+// lane then issues its K*U gathered 16-byte loads before any arithmetic,
+// accumulates in fp32 with fused multiply-add in ascending k from +0,
+// converts to bf16 with round to nearest even, and writes its chunk once.
+// Expert rows are read with non-temporal loads (each is read exactly once).
 #include "cgd_device.h"
 #include "cgd_launch.h"
 
@@ -28,7 +30,12 @@ namespace cgd {
 #ifndef CGD_COMBINE_NT
 #define CGD_COMBINE_NT 1
 #endif
-constexpr int kCombineWaves = CGD_COMBINE_WAVES;  // tokens (waves) per block
+// Occupancy cap: each block reserves this much (unused) LDS, so at most
+// 160 KB / CGD_COMBINE_LDS_CAP blocks share a CU (5 at 32 KB).
+#ifndef CGD_COMBINE_LDS_CAP
+#define CGD_COMBINE_LDS_CAP (32 * 1024)
+#endif
+constexpr int kCombineWaves = CGD_COMBINE_WAVES;  // waves per block
 
 template <int KM, int U>
 __global__ __launch_bounds__(kCombineWaves* kWave) void combine_kernel(const uint4* __restrict__ y, int64_t cap,
@@ -38,64 +45,66 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void combine_kernel(const uin
                                                                         uint4* __restrict__ out) {
     const int lane = lane_id();
     const int64_t g = (int64_t)blockIdx.x * kCombineWaves + threadIdx.x / kWave;
-    const int64_t t = g / nchunk;
-    if (t >= T) return;
-    const int v0 = (int)(g - t * nchunk) * (U * kWave);
+    {
+        const int64_t t = g / nchunk;
+        if (t >= T) return;
+        const int v0 = (int)(g - t * nchunk) * (U * kWave);
 
-    int d = -1;
-    float wt = 0.0f;
-    if (lane < K) {
-        const int p = dst_row[t * K + lane];
-        d = (p >= 0 && p < cap) ? p : -1;
-        wt = w[t * K + lane];
-    }
-    int dk[KM];
-    float wk[KM];
-#pragma unroll
-    for (int k = 0; k < KM; ++k) {
-        dk[k] = __shfl(d, k, kWave);
-        wk[k] = __shfl(wt, k, kWave);
-    }
-
-    uint4 buf[KM][U];
-#pragma unroll
-    for (int k = 0; k < KM; ++k) {
-        if (dk[k] < 0) continue;
-        const uint4* yr = y + (int64_t)dk[k] * nvec;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * kWave + lane;
-            if (v < nvec) buf[k][u] = CGD_COMBINE_NT ? load_nt(yr + v) : yr[v];
+        int d = -1;
+        float wt = 0.0f;
+        if (lane < K) {
+            const int p = dst_row[t * K + lane];
+            d = (p >= 0 && p < cap) ? p : -1;
+            wt = w[t * K + lane];
         }
-    }
-    uint4* orow = out + t * nvec;
+        int dk[KM];
+        float wk[KM];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * kWave + lane;
-        if (v >= nvec) continue;
-        float acc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+        for (int k = 0; k < KM; ++k) {
+            dk[k] = __shfl(d, k, kWave);
+            wk[k] = __shfl(wt, k, kWave);
+        }
+
+        uint4 buf[KM][U];
 #pragma unroll
         for (int k = 0; k < KM; ++k) {
             if (dk[k] < 0) continue;
-            const uint4 q = buf[k][u];
-            const float s = wk[k];
-            acc[0] = __builtin_fmaf(s, bf16_lo(q.x), acc[0]);
-            acc[1] = __builtin_fmaf(s, bf16_hi(q.x), acc[1]);
-            acc[2] = __builtin_fmaf(s, bf16_lo(q.y), acc[2]);
-            acc[3] = __builtin_fmaf(s, bf16_hi(q.y), acc[3]);
-            acc[4] = __builtin_fmaf(s, bf16_lo(q.z), acc[4]);
-            acc[5] = __builtin_fmaf(s, bf16_hi(q.z), acc[5]);
-            acc[6] = __builtin_fmaf(s, bf16_lo(q.w), acc[6]);
-            acc[7] = __builtin_fmaf(s, bf16_hi(q.w), acc[7]);
+            const uint4* yr = y + (int64_t)dk[k] * nvec;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * kWave + lane;
+                if (v < nvec) buf[k][u] = CGD_COMBINE_NT ? load_nt(yr + v) : yr[v];
+            }
         }
-        uint4 r;
-        r.x = pack_bf16x2(acc[0], acc[1]);
-        r.y = pack_bf16x2(acc[2], acc[3]);
-        r.z = pack_bf16x2(acc[4], acc[5]);
-        r.w = pack_bf16x2(acc[6], acc[7]);
-        store_nt(orow + v, r);
+        uint4* orow = out + t * nvec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v >= nvec) continue;
+            float acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KM; ++k) {
+                if (dk[k] < 0) continue;
+                const uint4 q = buf[k][u];
+                const float s = wk[k];
+                acc[0] = __builtin_fmaf(s, bf16_lo(q.x), acc[0]);
+                acc[1] = __builtin_fmaf(s, bf16_hi(q.x), acc[1]);
+                acc[2] = __builtin_fmaf(s, bf16_lo(q.y), acc[2]);
+                acc[3] = __builtin_fmaf(s, bf16_hi(q.y), acc[3]);
+                acc[4] = __builtin_fmaf(s, bf16_lo(q.z), acc[4]);
+                acc[5] = __builtin_fmaf(s, bf16_hi(q.z), acc[5]);
+                acc[6] = __builtin_fmaf(s, bf16_lo(q.w), acc[6]);
+                acc[7] = __builtin_fmaf(s, bf16_hi(q.w), acc[7]);
+            }
+            uint4 r;
+            r.x = pack_bf16x2(acc[0], acc[1]);
+            r.y = pack_bf16x2(acc[2], acc[3]);
+            r.z = pack_bf16x2(acc[4], acc[5]);
+            r.w = pack_bf16x2(acc[6], acc[7]);
+            store_nt(orow + v, r);
+        }
     }
 }
 
@@ -108,10 +117,10 @@ hipError_t launch_combine(const void* expert_out, int64_t cap, int H, const int3
 #define CGD_COMBINE(KM, U)                                                                                          \
     do {                                                                                                            \
         const int nchunk = (nvec + U * kWave - 1) / (U * kWave);                                                    \
-        const int64_t waves = T * nchunk;                                                                           \
-        const dim3 grid((unsigned)((waves + kCombineWaves - 1) / kCombineWaves)), block(kCombineWaves * kWave);     \
-        hipLaunchKernelGGL((combine_kernel<KM, U>), grid, block, 0, stream, yv, cap, nvec, nchunk, dst_row, w, T, K, \
-                           ov);                                                                                     \
+        const int64_t blocks = (T * nchunk + kCombineWaves - 1) / kCombineWaves;                                    \
+        const dim3 grid((unsigned)blocks), block(kCombineWaves * kWave);                                            \
+        hipLaunchKernelGGL((combine_kernel<KM, U>), grid, block, CGD_COMBINE_LDS_CAP, stream, yv, cap, nvec, nchunk,  \
+                           dst_row, w, T, K, ov);                                                                   \
     } while (0)
     if (K <= 2)
         CGD_COMBINE(2, CGD_COMBINE_U);

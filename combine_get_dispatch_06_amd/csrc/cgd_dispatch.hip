@@ -313,8 +313,10 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
             if (p >= 0) {
                 const int ex = p >> kPackBits;
                 const int lr = p & ((1 << kPackBits) - 1);
-                d = tile_base[(t / kRankTile) * E + ex] + lr;
-                if (d >= cap) d = -1;  // cannot happen for a consistent workspace; never write outside recv_x
+                // a consistent plan gives ex < E and d < cap; never read or
+                // write outside the workspace or recv_x otherwise
+                d = (ex < E) ? tile_base[(t / kRankTile) * E + ex] + lr : -1;
+                if (d >= cap) d = -1;
                 if (d >= 0) recv_src_idx[d] = (int32_t)t;
             }
             dst_row[t * K + lane] = d;
@@ -356,9 +358,8 @@ static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int n
 #undef CGD_SCATTER
 }
 
-hipError_t launch_dispatch(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
-                           void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
-                           int32_t* dst_row, void* workspace, hipStream_t stream) {
+hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
+                                int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream) {
     unsigned int* ticket = reinterpret_cast<unsigned int*>(workspace);
     int32_t* tile_base = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + kTicketBytes);
     int ebits = 0;
@@ -366,8 +367,14 @@ hipError_t launch_dispatch(const void* x, int64_t T, int H, const int64_t* topk_
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
     hipLaunchKernelGGL(rank_kernel, dim3(ntiles), dim3(kRankTile), rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
                        ebits, A, dst_row, tile_base, expert_offset, recv_src_idx, ticket);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, void* recv_x, int64_t cap,
+                                 const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
+                                 const void* workspace, hipStream_t stream) {
+    const int32_t* tile_base =
+        reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(workspace) + kTicketBytes);
     launch_scatter<true>(T, K, stream, x, H / 8, dst_row, tile_base, E, recv_src_idx, expert_offset, cap, recv_x);
     return hipGetLastError();
 }

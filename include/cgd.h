@@ -123,6 +123,29 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
                  int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
 
+/* Dispatch in two steps on one stream: cgd_dispatch is exactly
+ * cgd_dispatch_plan followed by cgd_dispatch_apply with the same sizes,
+ * capacity, workspace and output pointers. The plan needs only the routing,
+ * like the notify stage that precedes data movement in the pages' dispatch
+ * (the diagnostic-probes PR page, "Implementation": notify kernels before the
+ * dispatch data kernels; the first-call latency blog page: tensor sizes are
+ * notified in advance), so a caller may enqueue it early.
+ *   cgd_dispatch_plan   writes expert_offset, the -1 entries of recv_src_idx
+ *                       for alignment padding rows, an intermediate dst_row
+ *                       (not yet a handle) and per-tile bases in the workspace.
+ *   cgd_dispatch_apply  turns dst_row into final rows, records recv_src_idx of
+ *                       every data row (and -1 past the data), and copies rows.
+ * Between the two calls the workspace, dst_row and expert_offset must not be
+ * modified or used by another call. Mismatched arguments between the calls
+ * give wrong rows but never an access outside the given buffers. */
+int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
+                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                       int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,
+                       int32_t* dst_row, const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Cached dispatch (Python interface notes, "Dispatch API", handle reuse):
  * copies rows with a dst_row from an earlier cgd_dispatch, skipping the
  * layout work. recv_x[dst_row[t,k]] = x[t] for every dst_row[t,k] in

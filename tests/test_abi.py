@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     assert names == sorted([
         "cgd_version", "cgd_last_error", "cgd_layout_workspace_bytes", "cgd_dispatch_workspace_bytes",
-        "cgd_dispatch_capacity", "cgd_get_dispatch_layout", "cgd_dispatch", "cgd_dispatch_cached", "cgd_combine",
+        "cgd_dispatch_capacity", "cgd_get_dispatch_layout", "cgd_dispatch", "cgd_dispatch_plan",
+        "cgd_dispatch_apply", "cgd_dispatch_cached", "cgd_combine",
     ])
 
 
@@ -111,6 +112,24 @@ def test_dispatch_rejects_bad_arguments():
     assert call(wsb=16) == -3        # workspace too small
     assert call(E=15) == -1          # E % R
     assert call(K=17) == -1
+
+
+def test_plan_and_apply_reject_bad_arguments():
+    lib = cgd.load()
+    lib.cgd_dispatch_plan.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.cgd_dispatch_apply.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    f = _vp(FAKE)
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, 1 << 20, None) == -2
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, None, 0, None) == -3
+    assert lib.cgd_dispatch_apply(f, 64, 12, 4, 16, 256, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_apply(f, 64, 128, 4, 513, 256, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_apply(f, 64, 128, 4, 16, 256, _vp(FAKE + 4), f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_apply(f, 64, 128, 4, 16, 256, f, f, f, f, f, 16, None) == -3
 
 
 def test_cached_dispatch_and_combine_reject_bad_arguments():

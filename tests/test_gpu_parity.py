@@ -117,6 +117,21 @@ def test_cached_dispatch_matches_fresh_dispatch():
     np.testing.assert_array_equal(g[data], o2["recv_x"][data])
 
 
+def test_plan_then_apply_equals_dispatch():
+    w = synth.WORKLOADS["prefill"].replace(T=1500, H=1024)
+    inp = synth.make_inputs(w.replace(name="prefill"), seed=9)
+    idx, x_np = inp["topk_idx"][:w.T], synth.make_x(w, seed=9)
+    plan = cgd.dispatch_plan(dev_i64(idx), w.E, w.R, expert_alignment=4)
+    recv_x, h = cgd.dispatch_apply(dev_bf16(x_np), plan)
+    torch.cuda.synchronize()
+    o = oracle.dispatch(x_np, idx, w.E, w.R, align=4)
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    data = o["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
+
+
 def _edge(T, K, E, R, H, align=1, p_neg=0.0, dup=False, seed=0, all_to=None, cap_extra=0):
     rng = np.random.default_rng(seed)
     if all_to is not None:
