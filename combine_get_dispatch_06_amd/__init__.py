@@ -74,7 +74,7 @@ def load():
     lib.cgd_dispatch.restype = i32
     lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_plan.restype = i32
-    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_apply.restype = i32
     lib.cgd_dispatch_apply.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_cached.restype = i32
@@ -266,7 +266,7 @@ def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expe
         ws = _workspace(dev, "dispatch", nbytes)
         _check("cgd_dispatch_plan",
                lib.cgd_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap, _ptr(off),
-                                     _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+                                     _ptr(src), _ptr(ws), ws.numel(), _stream(dev)))
     h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
     return DispatchPlan(h, ws, T)
 

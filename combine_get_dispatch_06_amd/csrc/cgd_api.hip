@@ -71,7 +71,7 @@ size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_expe
 
 size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
     if (num_tokens < 0 || num_topk < 1 || num_experts < 1 || num_experts > cgd::kMaxExperts) return 0;
-    return cgd::dispatch_workspace_bytes(num_tokens, num_experts);
+    return cgd::dispatch_workspace_bytes(num_tokens, num_topk, num_experts);
 }
 
 int64_t cgd_dispatch_capacity(int64_t num_tokens, int num_topk, int num_experts, int expert_alignment) {
@@ -103,8 +103,8 @@ int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num
 
 // Checks shared by the dispatch entry points.
 static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
-                           const int32_t* expert_offset, const int32_t* recv_src_idx, const int32_t* dst_row,
-                           const void* workspace, size_t workspace_bytes) {
+                           const int32_t* expert_offset, const int32_t* recv_src_idx, const void* workspace,
+                           size_t workspace_bytes) {
     int rc = check_routing_sizes(T, K, E, R);
     if (rc) return rc;
     if (A < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
@@ -114,11 +114,11 @@ static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int
         return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
                     (long long)cap);
     if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
-    if (T > 0 && (!topk_idx || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null topk_idx or dst_row");
+    if (T > 0 && !topk_idx) return fail(CGD_ERR_INVALID_ARG, "null topk_idx");
     if (cap > 0 && !recv_src_idx) return fail(CGD_ERR_INVALID_ARG, "null recv_src_idx");
-    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
+    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4))
         return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
-    const size_t need = cgd::dispatch_workspace_bytes(T, E);
+    const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
@@ -140,7 +140,7 @@ static int check_apply_args(const void* x, int64_t T, int H, int K, int E, int64
     if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
     if (!aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
         return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
-    const size_t need = cgd::dispatch_workspace_bytes(T, E);
+    const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
@@ -149,12 +149,12 @@ static int check_apply_args(const void* x, int64_t T, int H, int K, int E, int64
 
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
                       int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
-                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+                             expert_offset, recv_src_idx, workspace, workspace_bytes);
     if (rc) return rc;
     hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
-                                               expert_offset, recv_src_idx, dst_row, workspace, stream);
+                                               expert_offset, recv_src_idx, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     return CGD_OK;
 }
@@ -176,13 +176,13 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
                  int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+                             expert_offset, recv_src_idx, workspace, workspace_bytes);
     if (rc) return rc;
     if ((rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x, expert_offset,
                                recv_src_idx, dst_row, workspace, workspace_bytes)))
         return rc;
     hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
-                                               expert_offset, recv_src_idx, dst_row, workspace, stream);
+                                               expert_offset, recv_src_idx, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     err = cgd::launch_dispatch_apply(x, num_tokens, hidden, num_topk, num_experts, recv_x, recv_capacity,
                                      expert_offset, recv_src_idx, dst_row, workspace, stream);

@@ -18,15 +18,15 @@
 //                   wavefront ballots (a "multi-split" over the bits of the
 //                   expert id). It writes a packed (expert, rank-in-tile) word
 //                   per slot and the tile's expert histogram. The last block
-//                   to finish turns the histograms into per-tile bases (column
-//                   prefix over tiles plus the aligned segment offsets from a
-//                   block prefix scan) and marks padding rows.
-//   scatter_kernel  one wave per token: lanes 0..K-1 turn their slot into a
-//                   final row (tile base + rank-in-tile) and record dst_row
-//                   and recv_src_idx; the wave streams the token's row
-//                   through registers in 16-byte vectors and stores it to the
-//                   K destination rows with non-temporal stores. The row is
-//                   read from HBM once however many experts it goes to.
+//                   to finish turns the histograms into per-tile bases (rows of
+//                   the expert in earlier tiles, one pass) and the aligned
+//                   segment offsets (block prefix scan), and marks padding rows.
+//   scatter_kernel  one wave per (token, column chunk): lanes 0..K-1 turn
+//                   their slot into a final row (segment offset + tile base +
+//                   rank in tile); the chunk's 16-byte vectors are loaded once
+//                   and stored to the K destination rows with non-temporal
+//                   stores. Each row is read from HBM once however many
+//                   experts it goes to.
 // Cached dispatch runs the scatter kernel on a stored final dst_row.
 #include "cgd_device.h"
 #include "cgd_launch.h"
@@ -62,7 +62,7 @@ __device__ __forceinline__ int slot_expert(int v) { return v < 0 ? -1 : (v & 0xF
 // Slot loops read the routing from LDS, which keeps the kernel light on
 // registers for any num_topk.
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
-                                                         int ebits, int A, int32_t* __restrict__ dst_row,
+                                                         int ebits, int A, int32_t* __restrict__ slot_pack,
                                                          int32_t* __restrict__ tile_base,
                                                          int32_t* __restrict__ expert_offset,
                                                          int32_t* __restrict__ recv_src_idx,
@@ -170,25 +170,30 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
 
     __syncthreads();
     {
-        int32_t* out = dst_row + t0 * K;
+        int32_t* out = slot_pack + t0 * K;
         const int n = nt * K;
         for (int i = tid; i < n; i += kRankTile) out[i] = s_slot[i];
     }
 
     if (!last_block_done(ticket)) return;
 
-    // ---- 2. last block: segment offsets and per-tile bases ----
-    // rows per expert = sum of the tile histograms
+    // ---- 2. last block: per-tile bases and segment offsets ----
+    // one pass over the tile histograms: each becomes the rows of its expert
+    // in earlier tiles (the apply adds the segment offset), and the column
+    // total is the expert's row count
     for (int x = tid; x < E; x += kRankTile) {
-        int sum = 0;
+        int run = 0;
         for (int b0 = 0; b0 < ntiles; b0 += kBatch) {
             int v[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) v[j] = (b0 + j < ntiles) ? tile_base[(int64_t)(b0 + j) * E + x] : 0;
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) sum += v[j];
+            for (int j = 0; j < kBatch; ++j) {
+                if (b0 + j < ntiles) tile_base[(int64_t)(b0 + j) * E + x] = run;
+                run += v[j];
+            }
         }
-        s_pre[x] = sum;
+        s_pre[x] = run;
     }
     __syncthreads();
     {  // exclusive scan of the aligned sizes: thread i owns entries 2i, 2i+1
@@ -212,79 +217,25 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         if (tid == kRankTile - 1) s_off[E] = before + inc;  // entries >= E add 0
     }
     __syncthreads();
-    // per-tile bases (segment offset + rows of earlier tiles), padding rows
-    for (int x = tid; x < E; x += kRankTile) {
-        int run = s_off[x];
-        for (int b0 = 0; b0 < ntiles; b0 += kBatch) {
-            int v[kBatch];
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) v[j] = (b0 + j < ntiles) ? tile_base[(int64_t)(b0 + j) * E + x] : 0;
-#pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                if (b0 + j < ntiles) tile_base[(int64_t)(b0 + j) * E + x] = run;
-                run += v[j];
-            }
-        }
-        for (int r = run; r < s_off[x + 1]; ++r) recv_src_idx[r] = -1;
-    }
+    // padding rows after each segment's data
+    for (int x = tid; x < E; x += kRankTile)
+        for (int r = s_off[x] + s_pre[x]; r < s_off[x + 1]; ++r) recv_src_idx[r] = -1;
     for (int x = tid; x <= E; x += kRankTile) expert_offset[x] = s_off[x];
     reset_ticket(ticket);
 }
 
-// Stores the token's row (nvec 16-byte vectors) to its destination rows dk[]
-// (entries < 0 skipped). The first PF vectors per lane are already in pre[];
-// the rest stream through registers U vectors per lane at a time.
-template <int KM, int U, int PF>
-__device__ __forceinline__ void store_row(const uint4* __restrict__ xr, int nvec, const int (&dk)[KM],
-                                          uint4* __restrict__ recv_x, const uint4 (&pre)[PF]) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int k = 0; k < KM; ++k) {
-        if (dk[k] < 0) continue;
-        uint4* dr = recv_x + (int64_t)dk[k] * nvec;
-#pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int v = u * kWave + lane;
-            if (v < nvec) {
-                if (CGD_SCATTER_NT)
-                    store_nt(dr + v, pre[u]);
-                else
-                    dr[v] = pre[u];
-            }
-        }
-    }
-    for (int v0 = PF * kWave; v0 < nvec; v0 += U * kWave) {
-        uint4 buf[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int v = v0 + u * kWave + lane;
-            if (v < nvec) buf[u] = xr[v];
-        }
-#pragma unroll
-        for (int k = 0; k < KM; ++k) {
-            if (dk[k] < 0) continue;
-            uint4* dr = recv_x + (int64_t)dk[k] * nvec;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int v = v0 + u * kWave + lane;
-                if (v < nvec) {
-                    if (CGD_SCATTER_NT)
-                        store_nt(dr + v, buf[u]);
-                    else
-                        dr[v] = buf[u];
-                }
-            }
-        }
-    }
-}
-
-// One wave per token. PACKED: dst_row holds rank_kernel's packed words and is
-// rewritten with final rows, and recv_src_idx is filled (non-cached
-// dispatch); otherwise dst_row holds final rows and is only read (cached
-// dispatch).
+// One wave per (token, column chunk of U*64 16-byte vectors). With PACKED
+// (dispatch apply) the wave turns the plan's packed slot words into final rows
+// (tile base + rank in tile); the token's chunk-0 wave also records dst_row
+// and recv_src_idx. Without PACKED (cached dispatch) dst_row already holds
+// final rows. Lanes 0..K-1 broadcast the K rows; each lane loads its U
+// vectors once and stores them to every destination row with non-temporal
+// stores. Many short waves in token order keep every CU busy even for a few
+// tokens and keep the writes in flight close together.
 template <int KM, int U, bool PACKED>
 __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t T, int nvec,
-                                                                      int K, int32_t* __restrict__ dst_row,
+                                                                      int nchunk, int K, const int32_t* __restrict__ slot,
+                                                                      int32_t* __restrict__ dst_row,
                                                                       const int32_t* __restrict__ tile_base, int E,
                                                                       int32_t* __restrict__ recv_src_idx,
                                                                       const int32_t* __restrict__ expert_offset,
@@ -297,29 +248,34 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
         for (int64_t r = n + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < cap; r += stride)
             recv_src_idx[r] = -1;
     }
-    const int64_t t = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
+    const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
+    const int64_t t = g / nchunk;
     if (t >= T) return;
+    const int c = (int)(g - t * nchunk);
+    const int v0 = c * U * kWave;
     const uint4* xr = x + t * nvec;
-    uint4 pre[U];  // first pass of the row, loaded before the indices arrive
+    uint4 buf[U];  // loaded before the indices arrive
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int v = u * kWave + lane;
-        if (v < nvec) pre[u] = xr[v];
+        const int v = v0 + u * kWave + lane;
+        if (v < nvec) buf[u] = xr[v];
     }
     int d = -1;
     if (lane < K) {
-        const int p = dst_row[t * K + lane];
+        const int p = slot[t * K + lane];
         if (PACKED) {
             if (p >= 0) {
                 const int ex = p >> kPackBits;
                 const int lr = p & ((1 << kPackBits) - 1);
                 // a consistent plan gives ex < E and d < cap; never read or
                 // write outside the workspace or recv_x otherwise
-                d = (ex < E) ? tile_base[(t / kRankTile) * E + ex] + lr : -1;
+                d = (ex < E) ? expert_offset[ex] + tile_base[(t / kRankTile) * E + ex] + lr : -1;
                 if (d >= cap) d = -1;
+            }
+            if (c == 0) {
+                dst_row[t * K + lane] = d;
                 if (d >= 0) recv_src_idx[d] = (int32_t)t;
             }
-            dst_row[t * K + lane] = d;
         } else {
             d = (p >= 0 && p < cap) ? p : -1;
         }
@@ -327,25 +283,47 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
     int dk[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) dk[k] = __shfl(d, k, kWave);
-    store_row<KM, U, U>(xr, nvec, dk, recv_x, pre);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        if (dk[k] < 0) continue;
+        uint4* dr = recv_x + (int64_t)dk[k] * nvec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v < nvec) {
+                if (CGD_SCATTER_NT)
+                    store_nt(dr + v, buf[u]);
+                else
+                    dr[v] = buf[u];
+            }
+        }
+    }
 }
 
-size_t dispatch_workspace_bytes(int64_t T, int E) {
+// Dispatch workspace: ticket | tile bases int32 [tiles, E] | packed slot
+// words int32 [T, K] (plan -> apply).
+static size_t tile_bytes(int64_t T, int E) {
     const int64_t ntiles = T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile;
-    const size_t arr = (size_t)ntiles * (size_t)E * sizeof(int32_t);
-    return kTicketBytes + (arr + 255) / 256 * 256;
+    return ((size_t)ntiles * (size_t)E * sizeof(int32_t) + 255) / 256 * 256;
 }
 
-template <bool PACKED>
-static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, int32_t* dst_row,
-                           const int32_t* tile_base, int E, int32_t* src, const int32_t* off, int64_t cap,
-                           void* recv_x) {
-    const int64_t blocks = T <= 0 ? 1 : (T + kScatterWaves - 1) / kScatterWaves;
+size_t dispatch_workspace_bytes(int64_t T, int K, int E) {
+    const size_t slots = ((size_t)(T > 0 ? T : 0) * (size_t)K * sizeof(int32_t) + 255) / 256 * 256;
+    return kTicketBytes + tile_bytes(T, E) + slots;
+}
+
+template <bool PACKED, int U>
+static void launch_scatter_u(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
+                             int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
+                             int64_t cap, void* recv_x) {
+    const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
+    const int64_t waves = T * nchunk;
+    const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
     const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint4* rv = reinterpret_cast<uint4*>(recv_x);
 #define CGD_SCATTER(KM)                                                                                            \
-    hipLaunchKernelGGL((scatter_kernel<KM, CGD_SCATTER_U, PACKED>), grid, block, 0, s, xv, T, nvec, K, dst_row,     \
+    hipLaunchKernelGGL((scatter_kernel<KM, U, PACKED>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot, dst_row,    \
                        tile_base, E, src, off, cap, rv)
     if (K <= 2)
         CGD_SCATTER(2);
@@ -358,32 +336,51 @@ static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int n
 #undef CGD_SCATTER
 }
 
+// Chunks of 4 vectors per lane (4 KB per wave) unless that leaves fewer than
+// kMinScatterWaves waves, as for a decode batch: then 1 vector per lane.
+constexpr int64_t kMinScatterWaves = 4096;
+
+template <bool PACKED>
+static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
+                           int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
+                           int64_t cap, void* recv_x) {
+    constexpr int U = CGD_SCATTER_U;
+    const int64_t waves = T * ((nvec + U * kWave - 1) / (U * kWave));
+    if (waves >= kMinScatterWaves)
+        launch_scatter_u<PACKED, U>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x);
+    else
+        launch_scatter_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x);
+}
+
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
-                                int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream) {
-    unsigned int* ticket = reinterpret_cast<unsigned int*>(workspace);
-    int32_t* tile_base = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + kTicketBytes);
+                                int32_t* recv_src_idx, void* workspace, hipStream_t stream) {
+    char* ws = reinterpret_cast<char*>(workspace);
+    unsigned int* ticket = reinterpret_cast<unsigned int*>(ws);
+    int32_t* tile_base = reinterpret_cast<int32_t*>(ws + kTicketBytes);
+    int32_t* slot_pack = reinterpret_cast<int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
     hipLaunchKernelGGL(rank_kernel, dim3(ntiles), dim3(kRankTile), rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
-                       ebits, A, dst_row, tile_base, expert_offset, recv_src_idx, ticket);
+                       ebits, A, slot_pack, tile_base, expert_offset, recv_src_idx, ticket);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, void* recv_x, int64_t cap,
                                  const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
                                  const void* workspace, hipStream_t stream) {
-    const int32_t* tile_base =
-        reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(workspace) + kTicketBytes);
-    launch_scatter<true>(T, K, stream, x, H / 8, dst_row, tile_base, E, recv_src_idx, expert_offset, cap, recv_x);
+    const char* ws = reinterpret_cast<const char*>(workspace);
+    const int32_t* tile_base = reinterpret_cast<const int32_t*>(ws + kTicketBytes);
+    const int32_t* slot_pack = reinterpret_cast<const int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
+    launch_scatter<true>(T, K, stream, x, H / 8, slot_pack, dst_row, tile_base, E, recv_src_idx, expert_offset, cap,
+                         recv_x);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
                                   int64_t cap, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    launch_scatter<false>(T, K, stream, x, H / 8, const_cast<int32_t*>(dst_row), nullptr, 0, nullptr, nullptr, cap,
-                          recv_x);
+    launch_scatter<false>(T, K, stream, x, H / 8, dst_row, nullptr, nullptr, 0, nullptr, nullptr, cap, recv_x);
     return hipGetLastError();
 }
 

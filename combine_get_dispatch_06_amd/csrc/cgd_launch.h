@@ -20,13 +20,13 @@ constexpr size_t kTicketBytes = 256;  // ticket word, padded to keep arrays 256-
 
 int64_t layout_blocks(int64_t T);
 size_t layout_workspace_bytes(int64_t T, int E, int R);
-size_t dispatch_workspace_bytes(int64_t T, int E);
+size_t dispatch_workspace_bytes(int64_t T, int K, int E);
 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R, int32_t* ntpr, int32_t* ntpe,
                          uint8_t* itr, void* workspace, hipStream_t stream);
 
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
-                                int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream);
+                                int32_t* recv_src_idx, void* workspace, hipStream_t stream);
 
 hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, void* recv_x, int64_t cap,
                                  const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,

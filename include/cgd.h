@@ -73,8 +73,8 @@ const char* cgd_last_error(void);
  * Calls that may run concurrently need separate workspaces. */
 size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
 
-/* Workspace bytes cgd_dispatch needs (host only; 0 if invalid). Same
- * zero-fill and reuse rules as the layout workspace. */
+/* Workspace bytes cgd_dispatch (and the plan/apply pair) needs (host only;
+ * 0 if invalid). Same zero-fill and reuse rules as the layout workspace. */
 size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts);
 
 /* Rows a receive buffer needs for ANY routing of these sizes (host only):
@@ -131,16 +131,16 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
  * dispatch data kernels; the first-call latency blog page: tensor sizes are
  * notified in advance), so a caller may enqueue it early.
  *   cgd_dispatch_plan   writes expert_offset, the -1 entries of recv_src_idx
- *                       for alignment padding rows, an intermediate dst_row
- *                       (not yet a handle) and per-tile bases in the workspace.
- *   cgd_dispatch_apply  turns dst_row into final rows, records recv_src_idx of
- *                       every data row (and -1 past the data), and copies rows.
- * Between the two calls the workspace, dst_row and expert_offset must not be
- * modified or used by another call. Mismatched arguments between the calls
- * give wrong rows but never an access outside the given buffers. */
+ *                       for alignment padding rows, and each slot's place
+ *                       (per-tile bases, packed slot words) in the workspace.
+ *   cgd_dispatch_apply  writes dst_row, the recv_src_idx of every data row
+ *                       (and -1 past the data), and copies rows.
+ * Between the two calls the workspace and expert_offset must not be modified
+ * or used by another call. Mismatched arguments between the calls give wrong
+ * rows but never an access outside the given buffers. */
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
                       int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
-                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
                        int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,

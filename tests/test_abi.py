@@ -60,7 +60,7 @@ def test_capacity_and_workspace_sizes():
         blocks = max(1, -(-T // 256))
         assert ws >= 256 + blocks * (256 + 8) * 4 and ws % 256 == 0
         wd = lib.cgd_dispatch_workspace_bytes(T, 8, 256)
-        assert wd >= 256 + blocks * 256 * 4 and wd % 256 == 0
+        assert wd >= 256 + blocks * 256 * 4 + T * 8 * 4 and wd % 256 == 0
     assert lib.cgd_layout_workspace_bytes(10, 8, 513, 1) == 0
     assert lib.cgd_dispatch_workspace_bytes(10, 0, 8) == 0
 
@@ -117,15 +117,15 @@ def test_dispatch_rejects_bad_arguments():
 def test_plan_and_apply_reject_bad_arguments():
     lib = cgd.load()
     lib.cgd_dispatch_plan.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.cgd_dispatch_apply.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     f = _vp(FAKE)
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, 1 << 20, None) == -2
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, None, 0, None) == -3
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, 1 << 20, None) == -2
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, None, 0, None) == -3
     assert lib.cgd_dispatch_apply(f, 64, 12, 4, 16, 256, f, f, f, f, f, 1 << 20, None) == -1
     assert lib.cgd_dispatch_apply(f, 64, 128, 4, 513, 256, f, f, f, f, f, 1 << 20, None) == -1
     assert lib.cgd_dispatch_apply(f, 64, 128, 4, 16, 256, _vp(FAKE + 4), f, f, f, f, 1 << 20, None) == -1
