@@ -49,6 +49,13 @@ def _load():
         lib.oracle_bf16_round.restype = ctypes.c_uint16
         lib.oracle_combine.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp]
         lib.oracle_combine.restype = i32
+        lib.oracle_normal_capacity.argtypes = [i64, i32, i32]
+        lib.oracle_normal_capacity.restype = i64
+        lib.oracle_dispatch_normal.argtypes = [vp, i64, i64, vp, vp, vp, vp, i32, i32, i32, i32, i64,
+                                               vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_dispatch_normal.restype = i32
+        lib.oracle_combine_normal.argtypes = [vp, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, vp]
+        lib.oracle_combine_normal.restype = i32
         _lib = lib
     return _lib
 
@@ -127,3 +134,63 @@ def combine(y: np.ndarray, dst_row: np.ndarray, topk_weights: np.ndarray) -> np.
     if rc:
         raise OracleError(rc)
     return out
+
+
+def normal_capacity(T: int, K: int, R: int) -> int:
+    return int(_load().oracle_normal_capacity(T, K, R))
+
+
+def dispatch_normal(x: np.ndarray | None, is_token_in_rank: np.ndarray, num_experts: int, num_topk: int,
+                    num_tokens_per_expert: np.ndarray | None = None, topk_idx: np.ndarray | None = None,
+                    topk_weights: np.ndarray | None = None, align: int = 1, cap: int | None = None,
+                    hidden: int = 0):
+    """Rank-granular dispatch. -> dict(rank_offset [R+1], send_row [T,R], recv_src_idx [cap],
+    recv_topk_idx [cap,K] int64 | None, recv_topk_weights [cap,K] f32 | None,
+    num_recv_tokens_per_expert [E] | None, recv_x [cap,H] uint16 | None)."""
+    itr = _c(is_token_in_rank, np.uint8)
+    T, R = itr.shape
+    K = num_topk
+    if cap is None:
+        cap = normal_capacity(T, K, R)
+    xs = None if x is None else _c(x, np.uint16)
+    H = hidden if xs is None else xs.shape[1]
+    ntpe = None if num_tokens_per_expert is None else _c(num_tokens_per_expert, np.int32)
+    idx = None if topk_idx is None else _c(topk_idx, np.int64)
+    w = None if topk_weights is None else _c(topk_weights, np.float32)
+    if (idx is None) != (w is None):
+        raise ValueError("topk_idx and topk_weights go together")
+    off = np.zeros(R + 1, np.int32)
+    send = np.zeros((T, R), np.int32)
+    src = np.zeros(max(cap, 0), np.int32)
+    ridx = None if idx is None else np.zeros((max(cap, 0), K), np.int64)
+    rw = None if idx is None else np.zeros((max(cap, 0), K), np.float32)
+    nre = None if ntpe is None else np.zeros(num_experts, np.int32)
+    recv = None if xs is None else np.zeros((max(cap, 0), H), np.uint16)
+    rc = _load().oracle_dispatch_normal(_p(xs), T, H, _p(itr), _p(ntpe), _p(idx), _p(w), K, num_experts, R,
+                                        align, cap, _p(off), _p(send), _p(src), _p(ridx), _p(rw), _p(nre),
+                                        _p(recv))
+    if rc:
+        raise OracleError(rc)
+    return {"rank_offset": off, "send_row": send, "recv_src_idx": src, "recv_topk_idx": ridx,
+            "recv_topk_weights": rw, "num_recv_tokens_per_expert": nre, "recv_x": recv}
+
+
+def combine_normal(y: np.ndarray, send_row: np.ndarray, recv_topk_weights: np.ndarray | None = None,
+                   bias_0: np.ndarray | None = None, bias_1: np.ndarray | None = None, num_topk: int = 1):
+    """Rank-granular combine. -> (combined_x uint16 [T,H], combined_topk_weights f32 [T,K] | None)."""
+    ys = _c(y, np.uint16)
+    send = _c(send_row, np.int32)
+    T, R = send.shape
+    rows, H = ys.shape
+    rw = None if recv_topk_weights is None else _c(recv_topk_weights, np.float32)
+    K = num_topk if rw is None else rw.shape[1]
+    b0 = None if bias_0 is None else _c(bias_0, np.uint16)
+    b1 = None if bias_1 is None else _c(bias_1, np.uint16)
+    out = np.zeros((T, H), np.uint16)
+    cw = np.zeros((T, K), np.float32)
+    zero_w = np.zeros((max(rows, 1), K), np.float32)
+    rc = _load().oracle_combine_normal(_p(ys), rows, H, _p(send), _p(rw if rw is not None else zero_w), _p(b0),
+                                       _p(b1), T, K, R, _p(out), _p(cw))
+    if rc:
+        raise OracleError(rc)
+    return out, (None if rw is None else cw)

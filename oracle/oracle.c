@@ -201,3 +201,126 @@ int oracle_combine(const uint16_t* y, int64_t rows, int64_t H, const int32_t* ds
     }
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Rank-granular ("normal mode") dispatch and combine.
+ *
+ * DeepEP legacy test analysis page: the normal-mode dispatch call site returns
+ * recv_x, recv_topk_idx, recv_topk_weights, the per-expert receive counts and
+ * a handle; check_data walks the received rows rank by rank through the
+ * receive prefix sums and expects every row of rank i's range to come from a
+ * token routed to rank i; the normal-mode combine call adds bias = (bias_0,
+ * bias_1) and returns combined_x and combined_topk_weights, and its check
+ * divides (combined_x - bias_0 - bias_1) by is_token_in_rank.sum(1) to get x
+ * back. DeepEP Python interface notes, "Dispatch API": recv_topk_idx
+ * [num_recv, num_topk] int64 and recv_topk_weights [num_recv, num_topk]
+ * float accompany recv_x; -1 means not selected; the per-expert counts are
+ * aligned to expert_alignment.
+ *
+ * Readings: a token is received once by every rank that is_token_in_rank
+ * flags for it; rank r's rows form one segment, segments in rank order, rows
+ * in ascending token order; in a received row, slot k keeps its expert as a
+ * rank-local id (e - r*L) and its weight when the expert is on rank r, else
+ * -1 and 0; rows past the data carry src -1, ids -1, weights 0; the
+ * per-expert receive counts are the layout's counts rounded up to
+ * expert_alignment. topk_idx / topk_weights may be absent (NULL), as in the
+ * pages' dispatch calls without top-k; then no recv_topk_* is produced.
+ * --------------------------------------------------------------------------- */
+
+/* A token reaches at most min(K, R) ranks, so T * min(K, R) rows hold any
+ * routing (the num_worst_tokens bound of the Dispatch API notes). */
+int64_t oracle_normal_capacity(int64_t T, int K, int R) { return T * (int64_t)(K < R ? K : R); }
+
+int oracle_dispatch_normal(const uint16_t* x, int64_t T, int64_t H, const uint8_t* is_token_in_rank,
+                           const int32_t* num_tokens_per_expert, const int64_t* topk_idx, const float* topk_weights,
+                           int K, int E, int R, int A, int64_t cap, int32_t* rank_offset, int32_t* send_row,
+                           int32_t* recv_src_idx, int64_t* recv_topk_idx, float* recv_topk_weights,
+                           int32_t* num_recv_tokens_per_expert, uint16_t* recv_x) {
+    if (T < 0 || K < 1 || K > 16 || E < 1 || E > 512 || R < 1 || R > 384 || E % R != 0) return ORACLE_EINVAL;
+    if (A < 1 || H < 0 || cap < 0) return ORACLE_EINVAL;
+    if (topk_idx) {
+        int rc = check_routing(topk_idx, T, K, E, R);
+        if (rc) return rc;
+    }
+    int L = E / R;
+
+    /* rows per rank: the tokens flagged for it */
+    int64_t total = 0;
+    rank_offset[0] = 0;
+    for (int r = 0; r < R; ++r) {
+        int64_t c = 0;
+        for (int64_t t = 0; t < T; ++t) c += is_token_in_rank[t * R + r] != 0;
+        total += c;
+        rank_offset[r + 1] = (int32_t)total;
+    }
+    if (total > cap) return ORACLE_ECAPACITY;
+    if (num_tokens_per_expert)
+        for (int e = 0; e < E; ++e)
+            num_recv_tokens_per_expert[e] = (num_tokens_per_expert[e] + A - 1) / A * A;
+
+    for (int64_t row = 0; row < cap; ++row) {
+        recv_src_idx[row] = -1;
+        if (topk_idx)
+            for (int k = 0; k < K; ++k) {
+                recv_topk_idx[row * K + k] = -1;
+                recv_topk_weights[row * K + k] = 0.0f;
+            }
+    }
+    /* each rank takes its flagged tokens in ascending order */
+    for (int r = 0; r < R; ++r) {
+        int64_t row = rank_offset[r];
+        for (int64_t t = 0; t < T; ++t) {
+            if (!is_token_in_rank[t * R + r]) {
+                send_row[t * R + r] = -1;
+                continue;
+            }
+            send_row[t * R + r] = (int32_t)row;
+            recv_src_idx[row] = (int32_t)t;
+            if (topk_idx)
+                for (int k = 0; k < K; ++k) {
+                    int64_t e = topk_idx[t * K + k];
+                    if (e >= 0 && e / L == r) {
+                        recv_topk_idx[row * K + k] = e - (int64_t)r * L;
+                        recv_topk_weights[row * K + k] = topk_weights[t * K + k];
+                    }
+                }
+            if (recv_x)
+                for (int64_t h = 0; h < H; ++h) recv_x[row * H + h] = x[t * H + h];
+            row += 1;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Normal-mode combine: out[t] = bf16( sum over ranks r that received t of
+ * y[send_row[t,r]] + bias_0[t] + bias_1[t] ) (biases optional, NULL = none),
+ * summed in double and rounded once; combined_topk_weights[t,k] = sum over
+ * those rows of recv_topk_weights[row, k]. */
+int oracle_combine_normal(const uint16_t* y, int64_t rows, int64_t H, const int32_t* send_row,
+                          const float* recv_topk_weights, const uint16_t* bias0, const uint16_t* bias1, int64_t T,
+                          int K, int R, uint16_t* out, float* combined_topk_weights) {
+    if (T < 0 || K < 1 || R < 1 || H < 0 || rows < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < T * (int64_t)R; ++i)
+        if (send_row[i] < -1 || send_row[i] >= rows) return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int r = 0; r < R; ++r) {
+                int32_t row = send_row[t * R + r];
+                if (row >= 0) acc += bf16_bits_to_double(y[(int64_t)row * H + h]);
+            }
+            if (bias0) acc += bf16_bits_to_double(bias0[t * H + h]);
+            if (bias1) acc += bf16_bits_to_double(bias1[t * H + h]);
+            out[t * H + h] = oracle_bf16_round(acc);
+        }
+        for (int k = 0; k < K; ++k) {
+            double wsum = 0.0;
+            for (int r = 0; r < R; ++r) {
+                int32_t row = send_row[t * R + r];
+                if (row >= 0) wsum += recv_topk_weights[(int64_t)row * K + k];
+            }
+            combined_topk_weights[t * K + k] = (float)wsum;
+        }
+    }
+    return ORACLE_OK;
+}
