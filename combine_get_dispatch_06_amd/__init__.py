@@ -25,7 +25,8 @@ from dataclasses import dataclass
 import torch
 
 __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply", "combine", "DispatchHandle",
-           "CgdError", "library_path", "dispatch_capacity", "load"]
+           "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
+           "normal_dispatch", "normal_combine"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -81,6 +82,17 @@ def load():
     lib.cgd_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
     lib.cgd_combine.restype = i32
     lib.cgd_combine.argtypes = [vp, i64, i32, vp, vp, i64, i32, vp, vp]
+    lib.cgd_normal_workspace_bytes.restype = sz
+    lib.cgd_normal_workspace_bytes.argtypes = [i64, i32]
+    lib.cgd_normal_capacity.restype = i64
+    lib.cgd_normal_capacity.argtypes = [i64, i32, i32]
+    lib.cgd_normal_dispatch.restype = i32
+    lib.cgd_normal_dispatch.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp,
+                                        vp, vp, vp, sz, vp]
+    lib.cgd_normal_dispatch_cached.restype = i32
+    lib.cgd_normal_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
+    lib.cgd_normal_combine.restype = i32
+    lib.cgd_normal_combine.argtypes = [vp, i64, i32, vp, i64, i32, vp, i32, vp, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -315,3 +327,163 @@ def combine(expert_out: torch.Tensor, handle: DispatchHandle, topk_weights: torc
                lib.cgd_combine(_ptr(expert_out), rows, H, _ptr(handle.dst_row), _ptr(topk_weights), T, K, _ptr(out),
                                _stream(dev)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Rank-granular ("normal mode") dispatch and combine: one received row per
+# (token, flagged rank), the DeepEP normal-mode receive layout.
+# ---------------------------------------------------------------------------
+
+def normal_capacity(num_tokens: int, num_topk: int, num_ranks: int) -> int:
+    cap = int(load().cgd_normal_capacity(num_tokens, num_topk, num_ranks))
+    if cap < 0:
+        raise ValueError("invalid sizes for a receive buffer")
+    return cap
+
+
+@dataclass
+class NormalHandle:
+    """Layout of one normal-mode dispatch, reusable for cached dispatch and combine.
+
+    rank_offset  int32 [R+1]: rows of rank r are [rank_offset[r], rank_offset[r+1]).
+    recv_src_idx int32 [recv_capacity]: source token of each row, -1 if none.
+    send_row     int32 [T, R]: the token's row on each rank, -1 if not sent.
+    """
+    rank_offset: torch.Tensor
+    recv_src_idx: torch.Tensor
+    send_row: torch.Tensor
+    num_topk: int
+    recv_capacity: int
+
+    @property
+    def num_tokens(self) -> int:
+        return self.send_row.shape[0]
+
+    @property
+    def num_ranks(self) -> int:
+        return self.send_row.shape[1]
+
+
+def normal_dispatch(x: torch.Tensor, is_token_in_rank: torch.Tensor | None = None,
+                    num_tokens_per_expert: torch.Tensor | None = None, topk_idx: torch.Tensor | None = None,
+                    topk_weights: torch.Tensor | None = None, num_experts: int | None = None,
+                    num_topk: int | None = None, expert_alignment: int = 1, handle: NormalHandle | None = None,
+                    recv_capacity: int | None = None, recv_x: torch.Tensor | None = None):
+    """Send each token once to every rank flagged in is_token_in_rank.
+
+    Non-cached: -> (recv_x, recv_topk_idx | None, recv_topk_weights | None,
+    num_recv_tokens_per_expert | None, NormalHandle). num_experts is needed;
+    num_topk comes from topk_idx, else must be given (it sizes the capacity).
+    Cached (handle given): -> (recv_x, None, None, None, handle).
+    """
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    dev = x.device
+    with torch.cuda.device(dev):
+        if handle is not None:
+            if is_token_in_rank is not None or topk_idx is not None:
+                raise ValueError("cached normal dispatch takes a handle and no layout")
+            if handle.num_tokens != T:
+                raise ValueError("x has a different number of tokens than the handle")
+            cap = handle.recv_capacity
+            if recv_x is None:
+                recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+            _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+            if recv_x.shape != (cap, H):
+                raise ValueError("recv_x must be [recv_capacity, hidden]")
+            _check("cgd_normal_dispatch_cached",
+                   lib.cgd_normal_dispatch_cached(_ptr(x), T, H, handle.num_ranks, _ptr(handle.send_row),
+                                                  _ptr(recv_x), cap, _stream(dev)))
+            return recv_x, None, None, None, handle
+
+        if is_token_in_rank is None or num_experts is None:
+            raise ValueError("non-cached normal dispatch needs is_token_in_rank and num_experts")
+        _dev_tensor(is_token_in_rank, "is_token_in_rank", torch.bool, 2)
+        if is_token_in_rank.shape[0] != T:
+            raise ValueError("is_token_in_rank must be [num_tokens, num_ranks]")
+        R = is_token_in_rank.shape[1]
+        if (topk_idx is None) != (topk_weights is None):
+            raise ValueError("topk_idx and topk_weights go together")
+        if topk_idx is not None:
+            _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+            _dev_tensor(topk_weights, "topk_weights", torch.float32, 2)
+            if topk_idx.shape[0] != T or topk_weights.shape != topk_idx.shape:
+                raise ValueError("topk_idx and topk_weights must be [num_tokens, num_topk]")
+            K = topk_idx.shape[1]
+        elif num_topk is not None:
+            K = int(num_topk)
+        else:
+            raise ValueError("num_topk is needed when dispatching without top-k")
+        if num_tokens_per_expert is not None:
+            _dev_tensor(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, 1)
+            if num_tokens_per_expert.shape[0] != num_experts:
+                raise ValueError("num_tokens_per_expert must be [num_experts]")
+        need = int(lib.cgd_normal_capacity(T, K, R))
+        cap = need if recv_capacity is None else int(recv_capacity)
+        if recv_x is None:
+            recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+        if recv_x.shape != (cap, H):
+            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        off = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        send = torch.empty((T, R), dtype=torch.int32, device=dev)
+        ridx = rw = nre = None
+        if topk_idx is not None:
+            ridx = torch.empty((max(cap, 0), K), dtype=torch.int64, device=dev)
+            rw = torch.empty((max(cap, 0), K), dtype=torch.float32, device=dev)
+        if num_tokens_per_expert is not None:
+            nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        nbytes = lib.cgd_normal_workspace_bytes(T, R)
+        ws = _workspace(dev, "normal", nbytes)
+        _check("cgd_normal_dispatch",
+               lib.cgd_normal_dispatch(_ptr(x), T, H, _ptr(is_token_in_rank), _ptr(num_tokens_per_expert),
+                                       _ptr(topk_idx), _ptr(topk_weights), K, num_experts, R, expert_alignment,
+                                       _ptr(recv_x), cap, _ptr(off), _ptr(src), _ptr(send), _ptr(ridx), _ptr(rw),
+                                       _ptr(nre), _ptr(ws), ws.numel(), _stream(dev)))
+    return recv_x, ridx, rw, nre, NormalHandle(off, src, send, K, cap)
+
+
+def normal_combine(expert_out: torch.Tensor, handle: NormalHandle, recv_topk_weights: torch.Tensor | None = None,
+                   bias=None, out: torch.Tensor | None = None):
+    """combined[t] = bf16( sum over t's rows, ascending rank, + bias_0[t] + bias_1[t] ), fp32 sum.
+
+    bias: None, a tensor, or a tuple of up to two bf16 [T, H] tensors.
+    -> (combined_x, combined_topk_weights | None)."""
+    lib = load()
+    _dev_tensor(expert_out, "expert_out", torch.bfloat16, 2)
+    rows, H = expert_out.shape
+    T, R = handle.send_row.shape
+    K = handle.num_topk
+    dev = expert_out.device
+    if bias is None:
+        bias = ()
+    elif isinstance(bias, torch.Tensor):
+        bias = (bias,)
+    bias = tuple(b for b in bias if b is not None)
+    if len(bias) > 2:
+        raise ValueError("at most two bias tensors")
+    for i, b in enumerate(bias):
+        _dev_tensor(b, f"bias_{i}", torch.bfloat16, 2)
+        if b.shape != (T, H):
+            raise ValueError("bias tensors must be [num_tokens, hidden]")
+    b0 = bias[0] if len(bias) > 0 else None
+    b1 = bias[1] if len(bias) > 1 else None
+    with torch.cuda.device(dev):
+        cw = None
+        if recv_topk_weights is not None:
+            _dev_tensor(recv_topk_weights, "recv_topk_weights", torch.float32, 2)
+            if recv_topk_weights.shape != (rows, K):
+                raise ValueError("recv_topk_weights must be [recv_rows, num_topk]")
+            cw = torch.empty((T, K), dtype=torch.float32, device=dev)
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(out, "out", torch.bfloat16, 2)
+        if out.shape != (T, H):
+            raise ValueError("out must be [num_tokens, hidden]")
+        _check("cgd_normal_combine",
+               lib.cgd_normal_combine(_ptr(expert_out), rows, H, _ptr(handle.send_row), T, R,
+                                      _ptr(recv_topk_weights), K, _ptr(b0), _ptr(b1), _ptr(out), _ptr(cw),
+                                      _stream(dev)))
+    return out, cw

@@ -47,6 +47,13 @@ int check_hidden(int H) {
     return CGD_OK;
 }
 
+// A token reaches at most min(K, R) ranks.
+int64_t normal_capacity_of(int64_t T, int K, int R) {
+    if (T < 0 || K < 1 || R < 1) return -1;
+    const int64_t cap = T * (int64_t)(K < R ? K : R);
+    return cap > INT32_MAX ? -1 : cap;
+}
+
 int64_t capacity_of(int64_t T, int K, int E, int A) {
     if (T < 0 || K < 1 || E < 1 || A < 1) return -1;
     const int64_t cap = T * (int64_t)K + (int64_t)E * (int64_t)(A - 1);
@@ -225,6 +232,110 @@ int cgd_combine(const void* expert_out, int64_t recv_capacity, int hidden, const
     hipError_t err = cgd::launch_combine(expert_out, recv_capacity, hidden, dst_row, topk_weights, num_tokens,
                                          num_topk, combined_x, stream);
     if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return CGD_OK;
+}
+
+size_t cgd_normal_workspace_bytes(int64_t num_tokens, int num_ranks) {
+    if (num_tokens < 0 || num_ranks < 1 || num_ranks > cgd::kMaxRanks) return 0;
+    return cgd::normal_workspace_bytes(num_tokens, num_ranks);
+}
+
+int64_t cgd_normal_capacity(int64_t num_tokens, int num_topk, int num_ranks) {
+    return normal_capacity_of(num_tokens, num_topk, num_ranks);
+}
+
+int cgd_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const uint8_t* is_token_in_rank,
+                        const int32_t* num_tokens_per_expert, const int64_t* topk_idx, const float* topk_weights,
+                        int num_topk, int num_experts, int num_ranks, int expert_alignment, void* recv_x,
+                        int64_t recv_capacity, int32_t* rank_offset, int32_t* recv_src_idx, int32_t* send_row,
+                        int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const int64_t T = num_tokens;
+    const int K = num_topk, E = num_experts, R = num_ranks;
+    int rc = check_routing_sizes(T, K, E, R);
+    if (rc) return rc;
+    if ((rc = check_hidden(hidden))) return rc;
+    if (expert_alignment < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
+    const int64_t need_rows = normal_capacity_of(T, K, R);
+    if (need_rows < 0) return fail(CGD_ERR_INVALID_ARG, "receive capacity for these sizes exceeds INT32_MAX");
+    if (recv_capacity < need_rows || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
+                    (long long)recv_capacity);
+    if (!rank_offset) return fail(CGD_ERR_INVALID_ARG, "null rank_offset");
+    if (T > 0 && (!x || !is_token_in_rank || !send_row)) return fail(CGD_ERR_INVALID_ARG, "null x, is_token_in_rank or send_row");
+    if (recv_capacity > 0 && (!recv_x || !recv_src_idx)) return fail(CGD_ERR_INVALID_ARG, "null receive pointer");
+    // with top-k: recv_topk_* are given (both), and so are topk_* unless
+    // there are no tokens (an empty tensor may have a null data pointer)
+    const bool with_topk = recv_topk_idx != nullptr || recv_topk_weights != nullptr;
+    if (with_topk && (!recv_topk_idx || !recv_topk_weights))
+        return fail(CGD_ERR_INVALID_ARG, "recv_topk_idx and recv_topk_weights go together");
+    if (T > 0 && ((topk_idx != nullptr) != with_topk || (topk_weights != nullptr) != with_topk))
+        return fail(CGD_ERR_INVALID_ARG,
+                    "topk_idx, topk_weights, recv_topk_idx and recv_topk_weights must be all given or all null");
+    if (!with_topk && (topk_idx || topk_weights))
+        return fail(CGD_ERR_INVALID_ARG, "topk_idx given without recv_topk_idx / recv_topk_weights");
+    if ((num_tokens_per_expert == nullptr) != (num_recv_tokens_per_expert == nullptr))
+        return fail(CGD_ERR_INVALID_ARG, "num_tokens_per_expert and num_recv_tokens_per_expert go together");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+    if (!aligned(topk_idx, 8) || !aligned(recv_topk_idx, 8) || !aligned(topk_weights, 4) ||
+        !aligned(recv_topk_weights, 4) || !aligned(rank_offset, 4) || !aligned(recv_src_idx, 4) ||
+        !aligned(send_row, 4) || !aligned(num_tokens_per_expert, 4) || !aligned(num_recv_tokens_per_expert, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned index or weight pointer");
+    const size_t need = cgd::normal_workspace_bytes(T, R);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "normal dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    hipError_t err = cgd::launch_normal_dispatch(x, T, hidden, is_token_in_rank, num_tokens_per_expert, topk_idx,
+                                                 topk_weights, K, E, R, expert_alignment, recv_x, recv_capacity,
+                                                 rank_offset, recv_src_idx, send_row, recv_topk_idx,
+                                                 recv_topk_weights, num_recv_tokens_per_expert, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_normal_dispatch_cached(const void* x, int64_t num_tokens, int hidden, int num_ranks, const int32_t* send_row,
+                               void* recv_x, int64_t recv_capacity, hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_ranks < 1 || num_ranks > cgd::kMaxRanks) return fail(CGD_ERR_INVALID_ARG, "num_ranks must be in [1,384]");
+    int rc = check_hidden(hidden);
+    if (rc) return rc;
+    if (recv_capacity < 0 || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
+    if (num_tokens > 0 && (!x || !send_row || (recv_capacity > 0 && !recv_x)))
+        return fail(CGD_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+    if (!aligned(send_row, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned send_row");
+    hipError_t err = cgd::launch_normal_dispatch_cached(x, num_tokens, hidden, num_ranks, send_row, recv_x,
+                                                        recv_capacity, stream);
+    if (err != hipSuccess) return hip_fail(err, "cached normal dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_normal_combine(const void* expert_out, int64_t recv_rows, int hidden, const int32_t* send_row,
+                       int64_t num_tokens, int num_ranks, const float* recv_topk_weights, int num_topk,
+                       const void* bias_0, const void* bias_1, void* combined_x, float* combined_topk_weights,
+                       hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_ranks < 1 || num_ranks > cgd::kMaxRanks) return fail(CGD_ERR_INVALID_ARG, "num_ranks must be in [1,384]");
+    if (num_topk < 1 || num_topk > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16]");
+    int rc = check_hidden(hidden);
+    if (rc) return rc;
+    if (recv_rows < 0 || recv_rows > INT32_MAX) return fail(CGD_ERR_CAPACITY, "recv_rows must be in [0, INT32_MAX]");
+    // the weight pair goes together; an empty tensor may have a null pointer
+    if (num_tokens > 0 && recv_topk_weights && !combined_topk_weights)
+        return fail(CGD_ERR_INVALID_ARG, "recv_topk_weights given without combined_topk_weights");
+    if (num_tokens > 0 && recv_rows > 0 && combined_topk_weights && !recv_topk_weights)
+        return fail(CGD_ERR_INVALID_ARG, "combined_topk_weights requested without recv_topk_weights");
+    if (num_tokens > 0 && (!send_row || !combined_x || (recv_rows > 0 && !expert_out)))
+        return fail(CGD_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(expert_out, 16) || !aligned(combined_x, 16) || !aligned(bias_0, 16) || !aligned(bias_1, 16))
+        return fail(CGD_ERR_INVALID_ARG, "expert_out, bias and combined_x must be 16-byte aligned");
+    if (!aligned(send_row, 4) || !aligned(recv_topk_weights, 4) || !aligned(combined_topk_weights, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned index or weight pointer");
+    hipError_t err = cgd::launch_normal_combine(expert_out, recv_rows, hidden, send_row, num_tokens, num_ranks,
+                                                recv_topk_weights, num_topk, bias_0, bias_1, combined_x,
+                                                combined_topk_weights, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal combine launch");
     return CGD_OK;
 }
 

@@ -71,23 +71,59 @@ __device__ __forceinline__ void stage_routing(const int64_t* __restrict__ src, i
 // Cross-block synchronisation. Blocks of one grid may sit on different XCDs,
 // each with its own L2. On gfx950 a device-scope release writes back the XCD's
 // L2 and a device-scope acquire invalidates it, so each is issued once per
-// block by thread 0, ordered with the block's other waves by a barrier.
+// block by thread 0, ordered with the block's other waves by a barrier. A
+// workgroup barrier does not wait for a wave's outstanding vector stores, and
+// thread 0's release waits only for its own wave's, so every wave first waits
+// until its stores are acknowledged by L2; thread 0 then waits for the L2
+// write-back itself before taking the ticket. These waits are explicit
+// (s_waitcnt with all counters 0), which the compiler keeps as written.
 
 // Last-block-done handshake among `nblocks` blocks: each block publishes its
 // writes and takes a ticket; the block that takes the last ticket acquires
 // every other block's writes and must reset the ticket (reset_ticket).
 __device__ __forceinline__ bool last_block_done(unsigned int* ticket, unsigned int nblocks) {
     __shared__ bool s_last;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __builtin_amdgcn_s_waitcnt(0);
+        const unsigned int prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == nblocks - 1);
+        if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     return s_last;
 }
 
 __device__ __forceinline__ bool last_block_done(unsigned int* ticket) { return last_block_done(ticket, gridDim.x); }
+
+// Exclusive prefix sum of n <= 2 * kRankTile integers v(0..n-1) by a block
+// of kRankTile threads: out[i] = v(0) + ... + v(i-1) for i <= n (out[n] is the
+// total). Thread i owns entries 2i and 2i+1; a wavefront scan with shuffles
+// and one LDS word per wave combine them. v is evaluated once per entry.
+template <class F>
+__device__ __forceinline__ void block_exclusive_scan2(int n, F v, int32_t* out, int32_t* s_wsum) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int i0 = 2 * tid, i1 = 2 * tid + 1;
+    const int c0 = (i0 < n) ? v(i0) : 0;
+    const int c1 = (i1 < n) ? v(i1) : 0;
+    const int own = c0 + c1;
+    int inc = own;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += u;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    const int excl = before + inc - own;
+    if (i0 < n) out[i0] = excl;
+    if (i1 < n) out[i1] = excl + c0;
+    if (tid == kRankTile - 1) out[n] = before + inc;  // entries >= n add 0
+}
 
 __device__ __forceinline__ void reset_ticket(unsigned int* ticket) {
     if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -196,26 +196,8 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         s_pre[x] = run;
     }
     __syncthreads();
-    {  // exclusive scan of the aligned sizes: thread i owns entries 2i, 2i+1
-        const int i0 = 2 * tid, i1 = 2 * tid + 1;
-        const int c0 = (i0 < E) ? (s_pre[i0] + A - 1) / A * A : 0;
-        const int c1 = (i1 < E) ? (s_pre[i1] + A - 1) / A * A : 0;
-        const int own = c0 + c1;
-        int inc = own;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int v = __shfl_up(inc, d, kWave);
-            if (lane >= d) inc += v;
-        }
-        if (lane == kWave - 1) s_wsum[wave] = inc;
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wave; ++w) before += s_wsum[w];
-        const int excl = before + inc - own;
-        if (i0 < E) s_off[i0] = excl;
-        if (i1 < E) s_off[i1] = excl + c0;
-        if (tid == kRankTile - 1) s_off[E] = before + inc;  // entries >= E add 0
-    }
+    // segment offsets: exclusive scan of the aligned sizes
+    block_exclusive_scan2(E, [&](int x) { return (s_pre[x] + A - 1) / A * A; }, s_off, s_wsum);
     __syncthreads();
     // padding rows after each segment's data
     for (int x = tid; x < E; x += kRankTile)
@@ -243,7 +225,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
     const int lane = lane_id();
     if (PACKED) {
         // rows past the data carry no source token
-        const int64_t n = expert_offset[E];
+        const int64_t n = max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
         const int64_t stride = (int64_t)gridDim.x * blockDim.x;
         for (int64_t r = n + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < cap; r += stride)
             recv_src_idx[r] = -1;
@@ -270,7 +252,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
                 // a consistent plan gives ex < E and d < cap; never read or
                 // write outside the workspace or recv_x otherwise
                 d = (ex < E) ? expert_offset[ex] + tile_base[(t / kRankTile) * E + ex] + lr : -1;
-                if (d >= cap) d = -1;
+                if (d < 0 || d >= cap) d = -1;
             }
             if (c == 0) {
                 dst_row[t * K + lane] = d;

@@ -167,6 +167,83 @@ int cgd_combine(const void* expert_out, int64_t recv_capacity, int hidden, const
                 const float* topk_weights, int64_t num_tokens, int num_topk, void* combined_x,
                 hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Rank-granular ("normal mode") dispatch and combine.
+ *
+ * A token is received once by every rank that is_token_in_rank flags for it,
+ * rather than once per selected expert (DeepEP legacy test analysis page:
+ * normal-mode dispatch call with the layout tensors, check_data walking the
+ * per-rank receive prefix sums, normal-mode combine check dividing
+ * combined_x - bias_0 - bias_1 by is_token_in_rank.sum(1); DeepEP Python
+ * interface notes, "Dispatch API": recv_topk_idx, recv_topk_weights and the
+ * aligned per-expert receive counts). Rank r's rows are
+ * [rank_offset[r], rank_offset[r+1]), ranks in order, rows inside a rank in
+ * ascending token order.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes cgd_normal_dispatch needs (host only; 0 if invalid). Same
+ * zero-fill and reuse rules as the layout workspace. */
+size_t cgd_normal_workspace_bytes(int64_t num_tokens, int num_ranks);
+
+/* Rows a rank-granular receive buffer needs for ANY routing of these sizes
+ * (host only): num_tokens * min(num_topk, num_ranks), since a token reaches at
+ * most that many ranks; -1 if invalid or above INT32_MAX. */
+int64_t cgd_normal_capacity(int64_t num_tokens, int num_topk, int num_ranks);
+
+/* Normal-mode dispatch (Python interface notes, "Dispatch API", non-cached
+ * mode, with the layout outputs as inputs):
+ *   x                      bf16 [num_tokens, hidden]
+ *   is_token_in_rank       uint8 [num_tokens, num_ranks] (torch.bool storage), from
+ *                          cgd_get_dispatch_layout; a row may flag at most num_topk ranks
+ *   num_tokens_per_expert  int32 [num_experts] from the layout, or NULL
+ *   topk_idx, topk_weights int64 / fp32 [num_tokens, num_topk], or both NULL (dispatch
+ *                          without top-k: then recv_topk_idx / recv_topk_weights are NULL too;
+ *                          with num_tokens = 0 they may be NULL either way)
+ *   recv_x                 bf16 [recv_capacity, hidden] out: row send_row[t,r] = x[t]; rows
+ *                          past the data are not written
+ *   recv_capacity          >= cgd_normal_capacity(...)
+ *   rank_offset            int32 [num_ranks + 1] out
+ *   recv_src_idx           int32 [recv_capacity] out: source token of each row, -1 past the data
+ *   send_row               int32 [num_tokens, num_ranks] out: the token's row on each rank, -1
+ *                          where not flagged (the analogue of the pages' send_head)
+ *   recv_topk_idx          int64 [recv_capacity, num_topk] out: slot k of a row on rank r holds
+ *                          e - r*L when the token's expert e lives on rank r, else -1; -1 past the data
+ *   recv_topk_weights      fp32 [recv_capacity, num_topk] out: the slot's weight where
+ *                          recv_topk_idx is kept, else 0
+ *   num_recv_tokens_per_expert int32 [num_experts] out (iff num_tokens_per_expert): counts
+ *                          rounded up to expert_alignment (alignment only affects these counts)
+ * (rank_offset, recv_src_idx, send_row) is the handle for cached dispatch and combine.
+ * A malformed is_token_in_rank (more than num_topk flags in a row) never
+ * causes an access outside the buffers: rows at or past recv_capacity are
+ * dropped (send_row -1). */
+int cgd_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const uint8_t* is_token_in_rank,
+                        const int32_t* num_tokens_per_expert, const int64_t* topk_idx, const float* topk_weights,
+                        int num_topk, int num_experts, int num_ranks, int expert_alignment, void* recv_x,
+                        int64_t recv_capacity, int32_t* rank_offset, int32_t* recv_src_idx, int32_t* send_row,
+                        int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Cached normal-mode dispatch (handle reuse): recv_x[send_row[t,r]] = x[t] for
+ * every send_row entry in [0, recv_capacity); other entries are skipped. */
+int cgd_normal_dispatch_cached(const void* x, int64_t num_tokens, int hidden, int num_ranks, const int32_t* send_row,
+                               void* recv_x, int64_t recv_capacity, hipStream_t stream);
+
+/* Normal-mode combine (legacy test analysis page, normal-mode combine call and
+ * check):
+ *   combined_x[t] = bf16( sum over r ascending with send_row[t,r] >= 0 of
+ *                         expert_out[send_row[t,r]]  + bias_0[t] + bias_1[t] )
+ * summed in fp32 from +0 in that order, rounded once to nearest even.
+ *   expert_out             bf16 [recv_rows, hidden]; send_row entries outside [-1, recv_rows)
+ *                          are treated as -1
+ *   recv_topk_weights      fp32 [recv_rows, num_topk] or NULL
+ *   bias_0, bias_1         bf16 [num_tokens, hidden] each, or NULL (no term)
+ *   combined_topk_weights  fp32 [num_tokens, num_topk] out (iff recv_topk_weights): sum over
+ *                          the token's rows, ascending rank, of recv_topk_weights[row, k] */
+int cgd_normal_combine(const void* expert_out, int64_t recv_rows, int hidden, const int32_t* send_row,
+                       int64_t num_tokens, int num_ranks, const float* recv_topk_weights, int num_topk,
+                       const void* bias_0, const void* bias_1, void* combined_x, float* combined_topk_weights,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

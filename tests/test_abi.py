@@ -24,7 +24,8 @@ def test_header_declares_the_boundary():
     assert names == sorted([
         "cgd_version", "cgd_last_error", "cgd_layout_workspace_bytes", "cgd_dispatch_workspace_bytes",
         "cgd_dispatch_capacity", "cgd_get_dispatch_layout", "cgd_dispatch", "cgd_dispatch_plan",
-        "cgd_dispatch_apply", "cgd_dispatch_cached", "cgd_combine",
+        "cgd_dispatch_apply", "cgd_dispatch_cached", "cgd_combine", "cgd_normal_workspace_bytes",
+        "cgd_normal_capacity", "cgd_normal_dispatch", "cgd_normal_dispatch_cached", "cgd_normal_combine",
     ])
 
 
@@ -141,6 +142,75 @@ def test_cached_dispatch_and_combine_reject_bad_arguments():
     assert lib.cgd_combine(_vp(FAKE), 16, 128, _vp(FAKE), _vp(FAKE + 2), 8, 2, _vp(FAKE), None) == -1
     assert lib.cgd_combine(_vp(FAKE), 16, 128, None, _vp(FAKE), 8, 2, _vp(FAKE), None) == -1
     assert lib.cgd_combine(_vp(FAKE), -5, 128, _vp(FAKE), _vp(FAKE), 8, 2, _vp(FAKE), None) == -2
+
+
+def test_normal_capacity_and_workspace_sizes():
+    lib = cgd.load()
+    assert lib.cgd_normal_capacity(4096, 8, 8) == 32768
+    assert lib.cgd_normal_capacity(128, 8, 16) == 1024   # min(K, R) = K
+    assert lib.cgd_normal_capacity(100, 8, 2) == 200     # min(K, R) = R
+    assert lib.cgd_normal_capacity(0, 4, 4) == 0
+    assert lib.cgd_normal_capacity(-1, 4, 4) == -1
+    assert lib.cgd_normal_capacity(1 << 30, 16, 64) == -1
+    assert cgd.normal_capacity(5, 3, 4) == 15
+    for T in (0, 1, 63, 64, 255, 256, 257, 32768):
+        for R in (1, 8, 64, 384):
+            ws = lib.cgd_normal_workspace_bytes(T, R)
+            groups = -(-T // 64)
+            tiles = max(1, -(-T // 256))
+            assert ws >= 256 + groups * R * 12 + tiles * R * 4 and ws % 256 == 0
+    assert lib.cgd_normal_workspace_bytes(10, 0) == 0
+    assert lib.cgd_normal_workspace_bytes(10, 385) == 0
+
+
+def test_normal_dispatch_rejects_bad_arguments():
+    lib = cgd.load()
+    ok = dict(x=FAKE, T=64, H=128, itr=FAKE, ntpe=FAKE, idx=FAKE, w=FAKE, K=4, E=16, R=4, A=1, recv=FAKE, cap=256,
+              off=FAKE, src=FAKE, send=FAKE, ridx=FAKE, rw=FAKE, nre=FAKE, ws=FAKE, wsb=1 << 20)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        p = lambda k: _vp(a[k]) if a[k] else None  # noqa: E731
+        return lib.cgd_normal_dispatch(p("x"), a["T"], a["H"], p("itr"), p("ntpe"), p("idx"), p("w"), a["K"],
+                                       a["E"], a["R"], a["A"], p("recv"), a["cap"], p("off"), p("src"), p("send"),
+                                       p("ridx"), p("rw"), p("nre"), p("ws"), a["wsb"], None)
+
+    assert call(H=12) == -1             # hidden not a multiple of 8
+    assert call(A=0) == -1              # alignment
+    assert call(cap=255) == -2          # capacity below T * min(K, R)
+    assert call(E=15) == -1             # E % R
+    assert call(K=17) == -1
+    assert call(idx=0) == -1            # top-k pointers all or none
+    assert call(ridx=0) == -1
+    assert call(ridx=0, rw=0) == -1     # topk_idx given without outputs
+    assert call(T=0, idx=0, w=0, cap=0, ws=0) == -3  # no tokens: null topk_* allowed (fails on workspace)
+    assert call(nre=0) == -1            # counts in and out together
+    assert call(itr=0) == -1
+    assert call(x=FAKE + 8) == -1       # x not 16-byte aligned
+    assert call(ridx=FAKE + 4) == -1    # int64 output misaligned
+    assert call(ws=0) == -3             # missing workspace
+    assert call(wsb=16) == -3           # workspace too small
+    assert lib.cgd_last_error()
+
+
+def test_normal_cached_and_combine_reject_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    assert lib.cgd_normal_dispatch_cached(f, 8, 100, 2, f, f, 16, None) == -1
+    assert lib.cgd_normal_dispatch_cached(f, 8, 128, 0, f, f, 16, None) == -1
+    assert lib.cgd_normal_dispatch_cached(f, 8, 128, 385, f, f, 16, None) == -1
+    assert lib.cgd_normal_dispatch_cached(f, 8, 128, 2, f, f, -1, None) == -2
+    assert lib.cgd_normal_dispatch_cached(f, 8, 128, 2, _vp(FAKE + 2), f, 16, None) == -1
+    # expert_out, rows, H, send_row, T, R, recv_w, K, bias_0, bias_1, out, out_w
+    assert lib.cgd_normal_combine(f, 16, 100, f, 8, 2, f, 2, None, None, f, f, None) == -1
+    assert lib.cgd_normal_combine(f, 16, 128, f, 8, 2, f, 17, None, None, f, f, None) == -1
+    assert lib.cgd_normal_combine(f, 16, 128, f, 8, 2, f, 2, None, None, f, None, None) == -1  # weights in, none out
+    assert lib.cgd_normal_combine(f, 16, 128, f, 8, 2, None, 2, None, None, f, f, None) == -1  # out, no weights in
+    # no tokens: nothing is enqueued, and empty tensors may come with null pointers
+    assert lib.cgd_normal_combine(f, 10, 64, None, 0, 4, f, 4, None, None, None, None, None) == 0
+    assert lib.cgd_normal_combine(f, 16, 128, f, 8, 2, None, 2, _vp(FAKE + 8), None, f, None, None) == -1
+    assert lib.cgd_normal_combine(f, -1, 128, f, 8, 2, None, 2, None, None, f, None, None) == -2
+    assert lib.cgd_normal_combine(f, 16, 128, None, 8, 2, None, 2, None, None, f, None, None) == -1
 
 
 def test_product_path_does_not_touch_the_oracle():
