@@ -26,7 +26,7 @@ import torch
 
 __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply", "combine", "DispatchHandle",
            "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
-           "normal_dispatch", "normal_combine"]
+           "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -89,6 +89,11 @@ def load():
     lib.cgd_normal_dispatch.restype = i32
     lib.cgd_normal_dispatch.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp,
                                         vp, vp, vp, sz, vp]
+    lib.cgd_normal_dispatch_plan.restype = i32
+    lib.cgd_normal_dispatch_plan.argtypes = [vp, i64, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+    lib.cgd_normal_dispatch_apply.restype = i32
+    lib.cgd_normal_dispatch_apply.argtypes = [vp, i64, i32, vp, vp, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp,
+                                              sz, vp]
     lib.cgd_normal_dispatch_cached.restype = i32
     lib.cgd_normal_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
     lib.cgd_normal_combine.restype = i32
@@ -443,6 +448,87 @@ def normal_dispatch(x: torch.Tensor, is_token_in_rank: torch.Tensor | None = Non
                                        _ptr(recv_x), cap, _ptr(off), _ptr(src), _ptr(send), _ptr(ridx), _ptr(rw),
                                        _ptr(nre), _ptr(ws), ws.numel(), _stream(dev)))
     return recv_x, ridx, rw, nre, NormalHandle(off, src, send, K, cap)
+
+
+@dataclass
+class NormalPlan:
+    """Result of normal_dispatch_plan: rank offsets, aligned per-expert counts
+    and the workspace that normal_dispatch_apply must receive."""
+    rank_offset: torch.Tensor
+    num_recv_tokens_per_expert: torch.Tensor | None
+    workspace: torch.Tensor
+    num_tokens: int
+    num_experts: int
+
+
+def normal_dispatch_plan(is_token_in_rank: torch.Tensor, num_tokens_per_expert: torch.Tensor | None = None,
+                         num_experts: int | None = None, expert_alignment: int = 1) -> NormalPlan:
+    """First step of normal dispatch: rank offsets from is_token_in_rank alone."""
+    lib = load()
+    _dev_tensor(is_token_in_rank, "is_token_in_rank", torch.bool, 2)
+    T, R = is_token_in_rank.shape
+    if num_experts is None:
+        raise ValueError("num_experts is needed")
+    dev = is_token_in_rank.device
+    with torch.cuda.device(dev):
+        nre = None
+        if num_tokens_per_expert is not None:
+            _dev_tensor(num_tokens_per_expert, "num_tokens_per_expert", torch.int32, 1)
+            if num_tokens_per_expert.shape[0] != num_experts:
+                raise ValueError("num_tokens_per_expert must be [num_experts]")
+            nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        off = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        ws = _workspace(dev, "normal", lib.cgd_normal_workspace_bytes(T, R))
+        _check("cgd_normal_dispatch_plan",
+               lib.cgd_normal_dispatch_plan(_ptr(is_token_in_rank), T, R, _ptr(num_tokens_per_expert), num_experts,
+                                            expert_alignment, _ptr(off), _ptr(nre), _ptr(ws), ws.numel(),
+                                            _stream(dev)))
+    return NormalPlan(off, nre, ws, T, num_experts)
+
+
+def normal_dispatch_apply(x: torch.Tensor, plan: NormalPlan, topk_idx: torch.Tensor | None = None,
+                          topk_weights: torch.Tensor | None = None, num_topk: int | None = None,
+                          recv_capacity: int | None = None, recv_x: torch.Tensor | None = None):
+    """Second step of normal dispatch: rows and per-row outputs.
+    -> (recv_x, recv_topk_idx | None, recv_topk_weights | None, num_recv_tokens_per_expert | None, NormalHandle)."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    if T != plan.num_tokens:
+        raise ValueError("x has a different number of tokens than the plan")
+    R = plan.rank_offset.shape[0] - 1
+    if (topk_idx is None) != (topk_weights is None):
+        raise ValueError("topk_idx and topk_weights go together")
+    if topk_idx is not None:
+        _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+        _dev_tensor(topk_weights, "topk_weights", torch.float32, 2)
+        if topk_idx.shape[0] != T or topk_weights.shape != topk_idx.shape:
+            raise ValueError("topk_idx and topk_weights must be [num_tokens, num_topk]")
+        K = topk_idx.shape[1]
+    elif num_topk is not None:
+        K = int(num_topk)
+    else:
+        raise ValueError("num_topk is needed when dispatching without top-k")
+    dev = x.device
+    with torch.cuda.device(dev):
+        cap = int(lib.cgd_normal_capacity(T, K, R)) if recv_capacity is None else int(recv_capacity)
+        if recv_x is None:
+            recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+        if recv_x.shape != (cap, H):
+            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        send = torch.empty((T, R), dtype=torch.int32, device=dev)
+        ridx = rw = None
+        if topk_idx is not None:
+            ridx = torch.empty((max(cap, 0), K), dtype=torch.int64, device=dev)
+            rw = torch.empty((max(cap, 0), K), dtype=torch.float32, device=dev)
+        _check("cgd_normal_dispatch_apply",
+               lib.cgd_normal_dispatch_apply(_ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K, plan.num_experts,
+                                             R, _ptr(recv_x), cap, _ptr(plan.rank_offset), _ptr(src), _ptr(send),
+                                             _ptr(ridx), _ptr(rw), _ptr(plan.workspace), plan.workspace.numel(),
+                                             _stream(dev)))
+    return recv_x, ridx, rw, plan.num_recv_tokens_per_expert, NormalHandle(plan.rank_offset, src, send, K, cap)
 
 
 def normal_combine(expert_out: torch.Tensor, handle: NormalHandle, recv_topk_weights: torch.Tensor | None = None,

@@ -244,52 +244,120 @@ int64_t cgd_normal_capacity(int64_t num_tokens, int num_topk, int num_ranks) {
     return normal_capacity_of(num_tokens, num_topk, num_ranks);
 }
 
+// Checks of the normal-mode plan (routing-independent sizes and the layout inputs).
+static int check_normal_plan_args(const uint8_t* itr, int64_t T, int R, const int32_t* ntpe, int E, int A,
+                                  const int32_t* rank_offset, const int32_t* nrecv, const void* workspace,
+                                  size_t workspace_bytes) {
+    if (T < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %lld)", (long long)T);
+    if (E < 1 || E > cgd::kMaxExperts)
+        return fail(CGD_ERR_INVALID_ARG, "num_experts must be in [1,512] (got %d)", E);
+    if (R < 1 || R > cgd::kMaxRanks) return fail(CGD_ERR_INVALID_ARG, "num_ranks must be in [1,384] (got %d)", R);
+    if (E % R != 0)
+        return fail(CGD_ERR_INVALID_ARG, "num_experts (%d) must be divisible by num_ranks (%d)", E, R);
+    if (A < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
+    if (!rank_offset) return fail(CGD_ERR_INVALID_ARG, "null rank_offset");
+    if (T > 0 && !itr) return fail(CGD_ERR_INVALID_ARG, "null is_token_in_rank");
+    if ((ntpe == nullptr) != (nrecv == nullptr))
+        return fail(CGD_ERR_INVALID_ARG, "num_tokens_per_expert and num_recv_tokens_per_expert go together");
+    if (!aligned(rank_offset, 4) || !aligned(ntpe, 4) || !aligned(nrecv, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned count pointer");
+    const size_t need = cgd::normal_workspace_bytes(T, R);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "normal dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    return CGD_OK;
+}
+
+// Checks of the normal-mode apply (rows and per-row outputs).
+static int check_normal_apply_args(const void* x, int64_t T, int H, const int64_t* topk_idx, const float* topk_w,
+                                   int K, int E, int R, const void* recv_x, int64_t cap, const int32_t* rank_offset,
+                                   const int32_t* recv_src_idx, const int32_t* send_row, const int64_t* recv_topk_idx,
+                                   const float* recv_topk_w, const void* workspace, size_t workspace_bytes) {
+    int rc = check_routing_sizes(T, K, E, R);
+    if (rc) return rc;
+    if ((rc = check_hidden(H))) return rc;
+    const int64_t need_rows = normal_capacity_of(T, K, R);
+    if (need_rows < 0) return fail(CGD_ERR_INVALID_ARG, "receive capacity for these sizes exceeds INT32_MAX");
+    if (cap < need_rows || cap > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
+                    (long long)cap);
+    if (!rank_offset) return fail(CGD_ERR_INVALID_ARG, "null rank_offset");
+    if (T > 0 && (!x || !send_row)) return fail(CGD_ERR_INVALID_ARG, "null x or send_row");
+    if (cap > 0 && (!recv_x || !recv_src_idx)) return fail(CGD_ERR_INVALID_ARG, "null receive pointer");
+    // with top-k: recv_topk_* are given (both), and so are topk_* unless
+    // there are no tokens (an empty tensor may have a null data pointer)
+    const bool with_topk = recv_topk_idx != nullptr || recv_topk_w != nullptr;
+    if (with_topk && (!recv_topk_idx || !recv_topk_w))
+        return fail(CGD_ERR_INVALID_ARG, "recv_topk_idx and recv_topk_weights go together");
+    if (T > 0 && ((topk_idx != nullptr) != with_topk || (topk_w != nullptr) != with_topk))
+        return fail(CGD_ERR_INVALID_ARG,
+                    "topk_idx, topk_weights, recv_topk_idx and recv_topk_weights must be all given or all null");
+    if (!with_topk && (topk_idx || topk_w))
+        return fail(CGD_ERR_INVALID_ARG, "topk_idx given without recv_topk_idx / recv_topk_weights");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+    if (!aligned(topk_idx, 8) || !aligned(recv_topk_idx, 8) || !aligned(topk_w, 4) || !aligned(recv_topk_w, 4) ||
+        !aligned(rank_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(send_row, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned index or weight pointer");
+    const size_t need = cgd::normal_workspace_bytes(T, R);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "normal dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    return CGD_OK;
+}
+
+int cgd_normal_dispatch_plan(const uint8_t* is_token_in_rank, int64_t num_tokens, int num_ranks,
+                             const int32_t* num_tokens_per_expert, int num_experts, int expert_alignment,
+                             int32_t* rank_offset, int32_t* num_recv_tokens_per_expert, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_normal_plan_args(is_token_in_rank, num_tokens, num_ranks, num_tokens_per_expert, num_experts,
+                                    expert_alignment, rank_offset, num_recv_tokens_per_expert, workspace,
+                                    workspace_bytes);
+    if (rc) return rc;
+    hipError_t err = cgd::launch_normal_plan(is_token_in_rank, num_tokens, num_ranks, num_tokens_per_expert,
+                                             num_experts, expert_alignment, rank_offset, num_recv_tokens_per_expert,
+                                             workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal dispatch plan launch");
+    return CGD_OK;
+}
+
+int cgd_normal_dispatch_apply(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                              const float* topk_weights, int num_topk, int num_experts, int num_ranks, void* recv_x,
+                              int64_t recv_capacity, const int32_t* rank_offset, int32_t* recv_src_idx,
+                              int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_weights,
+                              const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_normal_apply_args(x, num_tokens, hidden, topk_idx, topk_weights, num_topk, num_experts, num_ranks,
+                                     recv_x, recv_capacity, rank_offset, recv_src_idx, send_row, recv_topk_idx,
+                                     recv_topk_weights, workspace, workspace_bytes);
+    if (rc) return rc;
+    hipError_t err = cgd::launch_normal_apply(x, num_tokens, hidden, topk_idx, topk_weights, num_topk, num_experts,
+                                              num_ranks, recv_x, recv_capacity, rank_offset, recv_src_idx, send_row,
+                                              recv_topk_idx, recv_topk_weights, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal dispatch apply launch");
+    return CGD_OK;
+}
+
 int cgd_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const uint8_t* is_token_in_rank,
                         const int32_t* num_tokens_per_expert, const int64_t* topk_idx, const float* topk_weights,
                         int num_topk, int num_experts, int num_ranks, int expert_alignment, void* recv_x,
                         int64_t recv_capacity, int32_t* rank_offset, int32_t* recv_src_idx, int32_t* send_row,
                         int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    const int64_t T = num_tokens;
-    const int K = num_topk, E = num_experts, R = num_ranks;
-    int rc = check_routing_sizes(T, K, E, R);
+    int rc = check_normal_plan_args(is_token_in_rank, num_tokens, num_ranks, num_tokens_per_expert, num_experts,
+                                    expert_alignment, rank_offset, num_recv_tokens_per_expert, workspace,
+                                    workspace_bytes);
     if (rc) return rc;
-    if ((rc = check_hidden(hidden))) return rc;
-    if (expert_alignment < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
-    const int64_t need_rows = normal_capacity_of(T, K, R);
-    if (need_rows < 0) return fail(CGD_ERR_INVALID_ARG, "receive capacity for these sizes exceeds INT32_MAX");
-    if (recv_capacity < need_rows || recv_capacity > INT32_MAX)
-        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
-                    (long long)recv_capacity);
-    if (!rank_offset) return fail(CGD_ERR_INVALID_ARG, "null rank_offset");
-    if (T > 0 && (!x || !is_token_in_rank || !send_row)) return fail(CGD_ERR_INVALID_ARG, "null x, is_token_in_rank or send_row");
-    if (recv_capacity > 0 && (!recv_x || !recv_src_idx)) return fail(CGD_ERR_INVALID_ARG, "null receive pointer");
-    // with top-k: recv_topk_* are given (both), and so are topk_* unless
-    // there are no tokens (an empty tensor may have a null data pointer)
-    const bool with_topk = recv_topk_idx != nullptr || recv_topk_weights != nullptr;
-    if (with_topk && (!recv_topk_idx || !recv_topk_weights))
-        return fail(CGD_ERR_INVALID_ARG, "recv_topk_idx and recv_topk_weights go together");
-    if (T > 0 && ((topk_idx != nullptr) != with_topk || (topk_weights != nullptr) != with_topk))
-        return fail(CGD_ERR_INVALID_ARG,
-                    "topk_idx, topk_weights, recv_topk_idx and recv_topk_weights must be all given or all null");
-    if (!with_topk && (topk_idx || topk_weights))
-        return fail(CGD_ERR_INVALID_ARG, "topk_idx given without recv_topk_idx / recv_topk_weights");
-    if ((num_tokens_per_expert == nullptr) != (num_recv_tokens_per_expert == nullptr))
-        return fail(CGD_ERR_INVALID_ARG, "num_tokens_per_expert and num_recv_tokens_per_expert go together");
-    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
-    if (!aligned(topk_idx, 8) || !aligned(recv_topk_idx, 8) || !aligned(topk_weights, 4) ||
-        !aligned(recv_topk_weights, 4) || !aligned(rank_offset, 4) || !aligned(recv_src_idx, 4) ||
-        !aligned(send_row, 4) || !aligned(num_tokens_per_expert, 4) || !aligned(num_recv_tokens_per_expert, 4))
-        return fail(CGD_ERR_INVALID_ARG, "misaligned index or weight pointer");
-    const size_t need = cgd::normal_workspace_bytes(T, R);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-        return fail(CGD_ERR_WORKSPACE, "normal dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                    workspace_bytes);
-    hipError_t err = cgd::launch_normal_dispatch(x, T, hidden, is_token_in_rank, num_tokens_per_expert, topk_idx,
-                                                 topk_weights, K, E, R, expert_alignment, recv_x, recv_capacity,
-                                                 rank_offset, recv_src_idx, send_row, recv_topk_idx,
-                                                 recv_topk_weights, num_recv_tokens_per_expert, workspace, stream);
-    if (err != hipSuccess) return hip_fail(err, "normal dispatch launch");
+    if ((rc = check_normal_apply_args(x, num_tokens, hidden, topk_idx, topk_weights, num_topk, num_experts, num_ranks,
+                                      recv_x, recv_capacity, rank_offset, recv_src_idx, send_row, recv_topk_idx,
+                                      recv_topk_weights, workspace, workspace_bytes)))
+        return rc;
+    hipError_t err = cgd::launch_normal_plan(is_token_in_rank, num_tokens, num_ranks, num_tokens_per_expert,
+                                             num_experts, expert_alignment, rank_offset, num_recv_tokens_per_expert,
+                                             workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal dispatch plan launch");
+    err = cgd::launch_normal_apply(x, num_tokens, hidden, topk_idx, topk_weights, num_topk, num_experts, num_ranks,
+                                   recv_x, recv_capacity, rank_offset, recv_src_idx, send_row, recv_topk_idx,
+                                   recv_topk_weights, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal dispatch apply launch");
     return CGD_OK;
 }
 

@@ -44,6 +44,9 @@ constexpr int kPackBits = 13;  // rank inside a tile < 256 * 16 = 4096 < 2^13
 #ifndef CGD_SCATTER_NT
 #define CGD_SCATTER_NT 1
 #endif
+#ifndef CGD_SCATTER_READLANE
+#define CGD_SCATTER_READLANE 1
+#endif
 constexpr int kScatterWaves = CGD_SCATTER_WAVES;  // tokens (waves) per scatter block
 constexpr int kBatch = 16;                        // loads in flight per thread when summing columns
 
@@ -264,7 +267,13 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
     }
     int dk[KM];
 #pragma unroll
-    for (int k = 0; k < KM; ++k) dk[k] = __shfl(d, k, kWave);
+    for (int k = 0; k < KM; ++k) {
+#if CGD_SCATTER_READLANE
+        dk[k] = __builtin_amdgcn_readlane(d, k);
+#else
+        dk[k] = __shfl(d, k, kWave);
+#endif
+    }
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
         if (dk[k] < 0) continue;

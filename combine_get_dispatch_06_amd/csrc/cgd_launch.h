@@ -40,11 +40,13 @@ hipError_t launch_combine(const void* expert_out, int64_t cap, int H, const int3
 
 size_t normal_workspace_bytes(int64_t T, int R);
 
-hipError_t launch_normal_dispatch(const void* x, int64_t T, int H, const uint8_t* itr, const int32_t* ntpe,
-                                  const int64_t* topk_idx, const float* topk_w, int K, int E, int R, int A,
-                                  void* recv_x, int64_t cap, int32_t* rank_offset, int32_t* recv_src_idx,
-                                  int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w, int32_t* nrecv,
-                                  void* workspace, hipStream_t stream);
+hipError_t launch_normal_plan(const uint8_t* itr, int64_t T, int R, const int32_t* ntpe, int E, int A,
+                              int32_t* rank_offset, int32_t* nrecv, void* workspace, hipStream_t stream);
+
+hipError_t launch_normal_apply(const void* x, int64_t T, int H, const int64_t* topk_idx, const float* topk_w, int K,
+                               int E, int R, void* recv_x, int64_t cap, const int32_t* rank_offset,
+                               int32_t* recv_src_idx, int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w,
+                               const void* workspace, hipStream_t stream);
 
 hipError_t launch_normal_dispatch_cached(const void* x, int64_t T, int H, int R, const int32_t* send_row,
                                          void* recv_x, int64_t cap, hipStream_t stream);

@@ -32,14 +32,32 @@
 
 namespace cgd {
 
-constexpr int kNormGroups = kRankTile / kWave;  // token groups (waves) per tile
-constexpr int kFlagBatch = 16;                   // flag bytes in flight per thread
-constexpr int kTileBatch = 16;                   // tile counts in flight per thread
-constexpr int kNormScatterWaves = 4;             // waves per scatter block
-constexpr int kNormCombineWaves = 4;             // waves per combine block
-constexpr int kGatherBatch = 8;                  // rows in flight per combine wave
-// Occupancy cap of the combine (an LDS reservation per block, 5 blocks/CU).
-constexpr size_t kNormCombineLds = 32 * 1024;
+#ifndef CGD_NORMAL_COMBINE_LDS
+#define CGD_NORMAL_COMBINE_LDS (32 * 1024)
+#endif
+#ifndef CGD_NORMAL_COMBINE_U
+#define CGD_NORMAL_COMBINE_U 2
+#endif
+#ifndef CGD_NORMAL_COMBINE_WAVES
+#define CGD_NORMAL_COMBINE_WAVES 4
+#endif
+#ifndef CGD_NORMAL_GATHER
+#define CGD_NORMAL_GATHER 8
+#endif
+#ifndef CGD_NORMAL_SCATTER_U
+#define CGD_NORMAL_SCATTER_U 1
+#endif
+#ifndef CGD_NORMAL_READLANE
+#define CGD_NORMAL_READLANE 0
+#endif
+constexpr int kNormGroups = kRankTile / kWave;              // token groups (waves) per tile
+constexpr int kFlagBatch = 16;                               // flag bytes in flight per thread
+constexpr int kTileBatch = 16;                               // tile counts in flight per thread
+constexpr int kNormScatterWaves = 4;                         // waves per scatter block
+constexpr int kNormCombineWaves = CGD_NORMAL_COMBINE_WAVES;  // waves per combine block
+constexpr int kGatherBatch = CGD_NORMAL_GATHER;              // rows in flight per combine wave
+// Occupancy cap of the combine: an LDS reservation per block.
+constexpr size_t kNormCombineLds = CGD_NORMAL_COMBINE_LDS;
 
 // Normal workspace: ticket | group words u64 [G, R] | group bases int32 [G, R]
 // | tile counts, then tile bases, int32 [tiles, R]; G = ceil(T / 64).
@@ -291,7 +309,11 @@ __global__ __launch_bounds__(kNormCombineWaves* kWave) void normal_combine_kerne
             for (int i = 0; i < kGatherBatch; ++i) {
                 dk[i] = -1;
                 if (m) {
+#if CGD_NORMAL_READLANE
+                    dk[i] = __builtin_amdgcn_readlane(d, __builtin_ctzll(m));
+#else
                     dk[i] = __shfl(d, __builtin_ctzll(m), kWave);
+#endif
                     m &= m - 1;
                 }
             }
@@ -380,27 +402,31 @@ static void launch_normal_scatter(const void* x, int64_t T, int nvec, int R, con
                                   const int32_t* rank_offset, int32_t* send_row, int32_t* recv_src_idx,
                                   const int64_t* topk_idx, const float* topk_w, int K, int E, int64_t* recv_topk_idx,
                                   float* recv_topk_w, int64_t cap, void* recv_x, hipStream_t s) {
-    const int64_t waves4 = T * ((nvec + 4 * kWave - 1) / (4 * kWave));
-    if (waves4 >= kNormMinWaves)
-        launch_normal_scatter_u<CACHED, 4>(x, T, nvec, R, w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w,
+    constexpr int U = CGD_NORMAL_SCATTER_U;
+    const int64_t wavesU = T * ((nvec + U * kWave - 1) / (U * kWave));
+    if (wavesU >= kNormMinWaves)
+        launch_normal_scatter_u<CACHED, U>(x, T, nvec, R, w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w,
                                            K, E, recv_topk_idx, recv_topk_w, cap, recv_x, s);
     else
         launch_normal_scatter_u<CACHED, 1>(x, T, nvec, R, w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w,
                                            K, E, recv_topk_idx, recv_topk_w, cap, recv_x, s);
 }
 
-hipError_t launch_normal_dispatch(const void* x, int64_t T, int H, const uint8_t* itr, const int32_t* ntpe,
-                                  const int64_t* topk_idx, const float* topk_w, int K, int E, int R, int A,
-                                  void* recv_x, int64_t cap, int32_t* rank_offset, int32_t* recv_src_idx,
-                                  int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w, int32_t* nrecv,
-                                  void* workspace, hipStream_t stream) {
+hipError_t launch_normal_plan(const uint8_t* itr, int64_t T, int R, const int32_t* ntpe, int E, int A,
+                              int32_t* rank_offset, int32_t* nrecv, void* workspace, hipStream_t stream) {
     const NormalWs w = normal_ws(workspace, T, R);
     int64_t G, tiles;
     normal_sizes(T, R, &G, &tiles);
     hipLaunchKernelGGL(normal_plan_kernel, dim3((unsigned)tiles), dim3(kRankTile), 0, stream, itr, T, R, ntpe, nrecv,
                        E, A, w.grp_bal, w.grp_pre, w.tile_base, rank_offset, w.ticket);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    return hipGetLastError();
+}
+
+hipError_t launch_normal_apply(const void* x, int64_t T, int H, const int64_t* topk_idx, const float* topk_w, int K,
+                               int E, int R, void* recv_x, int64_t cap, const int32_t* rank_offset,
+                               int32_t* recv_src_idx, int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w,
+                               const void* workspace, hipStream_t stream) {
+    const NormalWs w = normal_ws(const_cast<void*>(workspace), T, R);
     launch_normal_scatter<false>(x, T, H / 8, R, &w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w, K, E,
                                  recv_topk_idx, recv_topk_w, cap, recv_x, stream);
     return hipGetLastError();
@@ -418,7 +444,7 @@ hipError_t launch_normal_combine(const void* expert_out, int64_t rows, int H, co
                                  int R, const float* recv_w, int K, const void* bias0, const void* bias1, void* out,
                                  float* out_w, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    constexpr int U = 1;
+    constexpr int U = CGD_NORMAL_COMBINE_U;
     const int nvec = H / 8;
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t blocks = (T * nchunk + kNormCombineWaves - 1) / kNormCombineWaves;

@@ -223,6 +223,29 @@ int cgd_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const uin
                         int64_t* recv_topk_idx, float* recv_topk_weights, int32_t* num_recv_tokens_per_expert,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Normal-mode dispatch in two steps on one stream: cgd_normal_dispatch is
+ * exactly cgd_normal_dispatch_plan followed by cgd_normal_dispatch_apply with
+ * the same sizes, workspace and outputs (the notify stage before the data
+ * stage, as for cgd_dispatch_plan / cgd_dispatch_apply).
+ *   cgd_normal_dispatch_plan   reads is_token_in_rank (and num_tokens_per_expert),
+ *                              writes rank_offset (and num_recv_tokens_per_expert)
+ *                              and each token's place in the workspace.
+ *   cgd_normal_dispatch_apply  writes send_row, recv_src_idx, recv_topk_idx,
+ *                              recv_topk_weights and copies rows.
+ * Between the two calls the workspace and rank_offset must not be modified or
+ * used by another call. Mismatched arguments give wrong rows but never an
+ * access outside the given buffers. */
+int cgd_normal_dispatch_plan(const uint8_t* is_token_in_rank, int64_t num_tokens, int num_ranks,
+                             const int32_t* num_tokens_per_expert, int num_experts, int expert_alignment,
+                             int32_t* rank_offset, int32_t* num_recv_tokens_per_expert, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+int cgd_normal_dispatch_apply(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                              const float* topk_weights, int num_topk, int num_experts, int num_ranks, void* recv_x,
+                              int64_t recv_capacity, const int32_t* rank_offset, int32_t* recv_src_idx,
+                              int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_weights,
+                              const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Cached normal-mode dispatch (handle reuse): recv_x[send_row[t,r]] = x[t] for
  * every send_row entry in [0, recv_capacity); other entries are skipped. */
 int cgd_normal_dispatch_cached(const void* x, int64_t num_tokens, int hidden, int num_ranks, const int32_t* send_row,

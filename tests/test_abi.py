@@ -26,6 +26,7 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_capacity", "cgd_get_dispatch_layout", "cgd_dispatch", "cgd_dispatch_plan",
         "cgd_dispatch_apply", "cgd_dispatch_cached", "cgd_combine", "cgd_normal_workspace_bytes",
         "cgd_normal_capacity", "cgd_normal_dispatch", "cgd_normal_dispatch_cached", "cgd_normal_combine",
+        "cgd_normal_dispatch_plan", "cgd_normal_dispatch_apply",
     ])
 
 
@@ -190,6 +191,25 @@ def test_normal_dispatch_rejects_bad_arguments():
     assert call(ridx=FAKE + 4) == -1    # int64 output misaligned
     assert call(ws=0) == -3             # missing workspace
     assert call(wsb=16) == -3           # workspace too small
+    assert lib.cgd_last_error()
+
+
+def test_normal_plan_and_apply_reject_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    # itr, T, R, ntpe, E, A, rank_offset, nrecv, ws, wsb
+    assert lib.cgd_normal_dispatch_plan(f, 64, 4, f, 16, 0, f, f, f, 1 << 20, None) == -1   # alignment
+    assert lib.cgd_normal_dispatch_plan(f, 64, 3, f, 16, 1, f, f, f, 1 << 20, None) == -1   # E % R
+    assert lib.cgd_normal_dispatch_plan(f, 64, 4, f, 16, 1, f, None, f, 1 << 20, None) == -1  # counts pair
+    assert lib.cgd_normal_dispatch_plan(None, 64, 4, f, 16, 1, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_normal_dispatch_plan(f, 64, 4, f, 16, 1, f, f, None, 0, None) == -3
+    assert lib.cgd_normal_dispatch_plan(f, 64, 4, f, 16, 1, f, f, f, 16, None) == -3
+    # x, T, H, idx, w, K, E, R, recv, cap, off, src, send, ridx, rw, ws, wsb
+    assert lib.cgd_normal_dispatch_apply(f, 64, 12, f, f, 4, 16, 4, f, 256, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_normal_dispatch_apply(f, 64, 128, f, f, 4, 16, 4, f, 255, f, f, f, f, f, f, 1 << 20, None) == -2
+    assert lib.cgd_normal_dispatch_apply(f, 64, 128, None, f, 4, 16, 4, f, 256, f, f, f, f, f, f, 1 << 20,
+                                         None) == -1
+    assert lib.cgd_normal_dispatch_apply(f, 64, 128, f, f, 4, 16, 4, f, 256, f, f, f, f, f, None, 0, None) == -3
     assert lib.cgd_last_error()
 
 

@@ -237,6 +237,23 @@ def test_normal_extra_capacity_and_zero_tokens():
     assert (rw.cpu().numpy() == 0).all() and out.shape == (0, 64) and cw.shape == (0, 4)
 
 
+def test_normal_plan_then_apply_equals_dispatch():
+    w = synth.WORKLOADS["prefill"].replace(T=1500, H=1024)
+    idx = synth.make_topk_idx(w.replace(name="prefill"), seed=9)[:w.T]
+    wts = synth.make_weights(w.replace(name="prefill"), seed=9)[:w.T]
+    x_np = synth.make_x(w, seed=9)
+    _, ntpe, itr = _layout(idx, w.E, w.R)
+    plan = cgd.normal_dispatch_plan(itr, ntpe, num_experts=w.E, expert_alignment=16)
+    recv_x, ridx, rw, nre, h = cgd.normal_dispatch_apply(dev_bf16(x_np), plan, dev_i64(idx), dev_f32(wts))
+    torch.cuda.synchronize()
+    o = oracle.dispatch_normal(x_np, itr.cpu().numpy(), w.E, w.K, ntpe.cpu().numpy(), idx, wts, align=16)
+    for got, key in ((h.rank_offset, "rank_offset"), (h.send_row, "send_row"), (h.recv_src_idx, "recv_src_idx"),
+                     (ridx, "recv_topk_idx"), (rw, "recv_topk_weights"), (nre, "num_recv_tokens_per_expert")):
+        np.testing.assert_array_equal(got.cpu().numpy(), o[key])
+    data = o["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
+
+
 def test_normal_cached_matches_fresh():
     w = synth.WORKLOADS["prefill"].replace(T=1000)
     inp = synth.make_inputs(w, seed=3)
