@@ -56,6 +56,14 @@ def _load():
         lib.oracle_dispatch_normal.restype = i32
         lib.oracle_combine_normal.argtypes = [vp, i64, i64, vp, vp, vp, vp, i64, i32, i32, vp, vp]
         lib.oracle_combine_normal.restype = i32
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = ctypes.c_float
+        lib.oracle_cast_to_fp8.argtypes = [vp, i64, i64, i32, vp, vp]
+        lib.oracle_cast_to_fp8.restype = i32
+        lib.oracle_cast_back.argtypes = [vp, vp, i64, i64, i32, vp]
+        lib.oracle_cast_back.restype = i32
         _lib = lib
     return _lib
 
@@ -194,3 +202,39 @@ def combine_normal(y: np.ndarray, send_row: np.ndarray, recv_topk_weights: np.nd
     if rc:
         raise OracleError(rc)
     return out, (None if rw is None else cw)
+
+
+SCALE_F32, SCALE_POW2, SCALE_UE8M0 = 0, 1, 2
+
+
+def e4m3_encode(v: float) -> int:
+    return int(_load().oracle_e4m3_encode(float(v)))
+
+
+def e4m3_decode(c: int) -> float:
+    return float(_load().oracle_e4m3_decode(int(c)))
+
+
+def cast_to_fp8(x: np.ndarray, scale_format: int = SCALE_F32):
+    """Per-token FP8 cast. x: bf16 bits uint16 [T, H], H % 128 == 0.
+    -> (codes uint8 [T, H], scales float32 [T, H/128] or uint8 exponent bytes for UE8M0)."""
+    xs = _c(x, np.uint16)
+    T, H = xs.shape
+    q = np.zeros((T, H), np.uint8)
+    sc = np.zeros((T, H // 128), np.uint8 if scale_format == SCALE_UE8M0 else np.float32)
+    rc = _load().oracle_cast_to_fp8(_p(xs), T, H, scale_format, _p(q), _p(sc))
+    if rc:
+        raise OracleError(rc)
+    return q, sc
+
+
+def cast_back(q: np.ndarray, scales: np.ndarray, scale_format: int = SCALE_F32) -> np.ndarray:
+    """-> bf16 bits uint16 [T, H]."""
+    qs = _c(q, np.uint8)
+    T, H = qs.shape
+    sc = _c(scales, np.uint8 if scale_format == SCALE_UE8M0 else np.float32)
+    out = np.zeros((T, H), np.uint16)
+    rc = _load().oracle_cast_back(_p(qs), _p(sc), T, H, scale_format, _p(out))
+    if rc:
+        raise OracleError(rc)
+    return out

@@ -324,3 +324,129 @@ int oracle_combine_normal(const uint16_t* y, int64_t rows, int64_t H, const int3
     }
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * FP8 payload: per-token cast to OCP e4m3fn with one scale per 128 channels,
+ * and the cast back to bf16.
+ *
+ * Pages: DeepEP Python interface notes, "Dispatch API": x may be the tuple
+ * (x_e4m3 float8_e4m3fn [T, H], x_scales float [T, H/128]) with H divisible
+ * by 128, and recv_x is then such a tuple too. DeepEP legacy test analysis
+ * page, test data excerpt: per_token_cast_to_fp8 turns a bf16 x into that
+ * tuple (its scales may be stored column-major), per_token_cast_back restores
+ * bf16; the low-latency dispatch has round_scale and use_ue8m0 options.
+ *
+ * The pages do not print the cast itself. Reading taken: for each token and
+ * each block of 128 channels, amax = max |x| over the block, floored at 1e-4
+ * so that a block of zeros keeps a positive scale.
+ *   scale format 0 (fp32):      s = amax / 448, codes e4m3(x * (448 / amax)),
+ *                               so the block's largest magnitude maps to 448,
+ *                               the largest finite e4m3fn value;
+ *   scale format 1 (round_scale): s = 2^k, the smallest power of two with
+ *                               s >= amax / 448, codes e4m3(x * 2^-k);
+ *   scale format 2 (UE8M0):     as format 1, the scale stored as the byte
+ *                               k + 127 (an unsigned 8-bit exponent).
+ * Cast back: bf16(e4m3 value * s), the product in fp32.
+ * Every step is fp32 arithmetic (the 8-bit codes are decided in fp32):
+ * 448 / amax and amax / 448 are correctly rounded fp32 divisions, x times the
+ * multiplier one fp32 product, clamped to [-448, 448] before encoding.
+ *
+ * e4m3fn (OCP 8-bit floating point specification, E4M3): 1 sign bit, 4
+ * exponent bits with bias 7, 3 fraction bits. Exponent field e in 1..15 gives
+ * (1 + f/8) * 2^(e-7), except e = 15, f = 7, which is NaN; so the largest
+ * finite value is 1.75 * 2^8 = 448. Exponent field 0 gives subnormals
+ * f/8 * 2^-6. There are no infinities. Rounding is to nearest, ties to even.
+ * Scales are written row-major [T, H/128].
+ * --------------------------------------------------------------------------- */
+
+#define ORACLE_E4M3_MAX 448.0
+
+/* Nearest e4m3fn code to v (ties to even); |v| above 448 saturates to 448. */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    if (isnan(v)) return 0x7F;
+    if (a > ORACLE_E4M3_MAX) a = ORACLE_E4M3_MAX;
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2); /* a in [2^(e2-1), 2^e2) */
+    int p = e2 - 1;
+    if (p < -6) p = -6;                /* below 2^-6 the spacing is that of subnormals */
+    double q = ldexp(1.0, p - 3);      /* spacing of e4m3 values in this binade */
+    double r = nearbyint(a / q) * q;   /* a/q is exact; round to nearest, ties even */
+    if (r == 0.0) return sign;
+    frexp(r, &e2);                     /* r may have moved up to the next binade */
+    p = e2 - 1;
+    if (p < -6) return sign | (uint8_t)(r / ldexp(1.0, -9)); /* subnormal: f = r / 2^-9 */
+    int frac = (int)(r / ldexp(1.0, p - 3)) - 8;              /* r = (8 + f) * 2^(p-3) */
+    return sign | (uint8_t)((p + 7) << 3) | (uint8_t)frac;
+}
+
+float oracle_e4m3_decode(uint8_t c) {
+    int e = (c >> 3) & 15, f = c & 7;
+    if (e == 15 && f == 7) return NAN;
+    double m = (e == 0) ? ldexp((double)f, -9) : ldexp((double)(8 + f), e - 10);
+    return (float)((c & 0x80) ? -m : m);
+}
+
+static float bf16_bits_to_float(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Smallest k with 2^k >= s (s > 0, finite). */
+static int ceil_log2f(float s) {
+    int e;
+    float m = frexpf(s, &e); /* s = m * 2^e, m in [0.5, 1) */
+    return (m == 0.5f) ? e - 1 : e;
+}
+
+int oracle_cast_to_fp8(const uint16_t* x, int64_t T, int64_t H, int scale_format, uint8_t* q, void* scales) {
+    if (T < 0 || H < 0 || H % 128 != 0 || scale_format < 0 || scale_format > 2) return ORACLE_EINVAL;
+    int64_t nb = H / 128;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + t * H + b * 128;
+            float amax = 0.0f;
+            for (int j = 0; j < 128; ++j) amax = fmaxf(amax, fabsf(bf16_bits_to_float(xb[j])));
+            if (amax < 1e-4f) amax = 1e-4f;
+            float mul;
+            if (scale_format == 0) {
+                mul = 448.0f / amax;
+                ((float*)scales)[t * nb + b] = amax / 448.0f;
+            } else {
+                int k = ceil_log2f(amax / 448.0f);
+                mul = ldexpf(1.0f, -k);
+                if (scale_format == 1)
+                    ((float*)scales)[t * nb + b] = ldexpf(1.0f, k);
+                else
+                    ((uint8_t*)scales)[t * nb + b] = (uint8_t)(k + 127);
+            }
+            for (int j = 0; j < 128; ++j) {
+                float v = bf16_bits_to_float(xb[j]) * mul;
+                if (v > 448.0f) v = 448.0f;
+                if (v < -448.0f) v = -448.0f;
+                q[t * H + b * 128 + j] = oracle_e4m3_encode(v);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+int oracle_cast_back(const uint8_t* q, const void* scales, int64_t T, int64_t H, int scale_format, uint16_t* out) {
+    if (T < 0 || H < 0 || H % 128 != 0 || scale_format < 0 || scale_format > 2) return ORACLE_EINVAL;
+    int64_t nb = H / 128;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t b = 0; b < nb; ++b) {
+            float s = (scale_format == 2) ? ldexpf(1.0f, (int)((const uint8_t*)scales)[t * nb + b] - 127)
+                                          : ((const float*)scales)[t * nb + b];
+            for (int j = 0; j < 128; ++j) {
+                int64_t i = t * H + b * 128 + j;
+                float v = oracle_e4m3_decode(q[i]) * s;
+                out[i] = oracle_bf16_round((double)v);
+            }
+        }
+    return ORACLE_OK;
+}
