@@ -26,7 +26,8 @@ import torch
 
 __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply", "combine", "DispatchHandle",
            "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
-           "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine"]
+           "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine",
+           "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -94,6 +95,22 @@ def load():
     lib.cgd_normal_dispatch_apply.restype = i32
     lib.cgd_normal_dispatch_apply.argtypes = [vp, i64, i32, vp, vp, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp,
                                               sz, vp]
+    lib.cgd_cast_to_fp8.restype = i32
+    lib.cgd_cast_to_fp8.argtypes = [vp, i64, i32, vp, vp, i64, i64, i32, vp]
+    lib.cgd_cast_back.restype = i32
+    lib.cgd_cast_back.argtypes = [vp, vp, i64, i64, i32, i64, i32, vp, vp]
+    lib.cgd_dispatch_apply_fp8.restype = i32
+    lib.cgd_dispatch_apply_fp8.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp,
+                                           sz, vp]
+    lib.cgd_dispatch_apply_cast_fp8.restype = i32
+    lib.cgd_dispatch_apply_cast_fp8.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_cached_fp8.restype = i32
+    lib.cgd_dispatch_cached_fp8.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, vp, vp, vp, i64, vp]
+    lib.cgd_normal_dispatch_apply_fp8.restype = i32
+    lib.cgd_normal_dispatch_apply_fp8.argtypes = [vp, vp, i64, i64, i32, i64, i32, vp, vp, i32, i32, i32, vp, vp,
+                                                  i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.cgd_normal_dispatch_cached_fp8.restype = i32
+    lib.cgd_normal_dispatch_cached_fp8.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, vp, vp, vp, i64, vp]
     lib.cgd_normal_dispatch_cached.restype = i32
     lib.cgd_normal_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
     lib.cgd_normal_combine.restype = i32
@@ -142,6 +159,75 @@ def _workspace(device: torch.device, kind: str, nbytes: int) -> torch.Tensor:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+# ---------------------------------------------------------------------------
+# FP8 payload: (codes float8_e4m3fn [T, H], scales [T, H/128]) tuples.
+# ---------------------------------------------------------------------------
+SCALE_F32, SCALE_POW2, SCALE_UE8M0 = 0, 1, 2
+
+
+def _fp8_parts(x, name: str = "x"):
+    """Validate an FP8 tuple -> (codes uint8 view, scales, scale format for
+    moving them, token stride, block stride)."""
+    if not (isinstance(x, tuple) and len(x) == 2):
+        raise TypeError(f"{name} must be a (codes, scales) tuple")
+    q, sc = x
+    if not isinstance(q, torch.Tensor) or q.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"{name} codes must be float8_e4m3fn (or uint8)")
+    if q.dim() != 2 or not q.is_contiguous() or q.device.type != "cuda":
+        raise ValueError(f"{name} codes must be a contiguous 2-D GPU tensor")
+    if not isinstance(sc, torch.Tensor) or sc.dtype not in (torch.float32, torch.uint8) or sc.dim() != 2:
+        raise TypeError(f"{name} scales must be a 2-D float32 (or uint8 UE8M0) tensor")
+    T, H = q.shape
+    if H % 128 != 0 or tuple(sc.shape) != (T, H // 128) or sc.device != q.device:
+        raise ValueError(f"{name} scales must be [num_tokens, hidden/128] on the codes' device")
+    fmt = SCALE_UE8M0 if sc.dtype == torch.uint8 else SCALE_F32
+    return q.view(torch.uint8), sc, fmt, sc.stride(0), sc.stride(1)
+
+
+def _fp8_empty(rows: int, H: int, fmt: int, dev):
+    q = torch.empty((rows, H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn)
+    sc = torch.empty((rows, H // 128), dtype=torch.uint8 if fmt == SCALE_UE8M0 else torch.float32, device=dev)
+    return q, sc
+
+
+def per_token_cast_to_fp8(x: torch.Tensor, scale_format: int = SCALE_F32, column_major_scales: bool = False):
+    """bf16 [T, H] -> (codes float8_e4m3fn [T, H], scales [T, H/128]); the
+    scales are fp32 (formats 0, 1) or UE8M0 bytes (format 2), optionally laid
+    out column-major (a transposed view of a [H/128, T] buffer)."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    T, H = x.shape
+    dev = x.device
+    with torch.cuda.device(dev):
+        q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        sdt = torch.uint8 if scale_format == SCALE_UE8M0 else torch.float32
+        if column_major_scales:
+            sc = torch.empty((H // 128, T), dtype=sdt, device=dev).t()
+        else:
+            sc = torch.empty((T, H // 128), dtype=sdt, device=dev)
+        _check("cgd_cast_to_fp8",
+               lib.cgd_cast_to_fp8(_ptr(x), T, H, _ptr(q), _ptr(sc), sc.stride(0), sc.stride(1), scale_format,
+                                   _stream(dev)))
+    return q.view(torch.float8_e4m3fn), sc
+
+
+def per_token_cast_back(x, scale_format: int | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """(codes, scales) -> bf16 [T, H]. scale_format defaults to the scales'
+    dtype (uint8: UE8M0, float32: fp32 scale)."""
+    lib = load()
+    q, sc, fmt, st, sb = _fp8_parts(x)
+    if scale_format is not None:
+        fmt = scale_format
+    T, H = q.shape
+    dev = q.device
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(out, "out", torch.bfloat16, 2)
+        _check("cgd_cast_back", lib.cgd_cast_back(_ptr(q), _ptr(sc), st, sb, fmt, T, H, _ptr(out), _stream(dev)))
+    return out
 
 
 def dispatch_capacity(num_tokens: int, num_topk: int, num_experts: int, expert_alignment: int = 1) -> int:
@@ -200,21 +286,44 @@ class DispatchHandle:
         return [b - a for a, b in zip(off[:-1], off[1:])]
 
 
-def dispatch(x: torch.Tensor, topk_idx: torch.Tensor | None = None, num_experts: int | None = None,
+def _recv_fp8(recv_x, cap: int, H: int, fmt: int, dev):
+    if recv_x is None:
+        return _fp8_empty(cap, H, fmt, dev)
+    q, sc, _, st, sb = _fp8_parts(recv_x, "recv_x")
+    if q.shape != (cap, H) or not sc.is_contiguous():
+        raise ValueError("recv_x must be ([recv_capacity, hidden] codes, row-major [recv_capacity, hidden/128] scales)")
+    return recv_x
+
+
+def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = None,
              num_ranks: int | None = None, expert_alignment: int = 1, handle: DispatchHandle | None = None,
-             recv_capacity: int | None = None, recv_x: torch.Tensor | None = None):
+             recv_capacity: int | None = None, recv_x=None, cast_fp8: int | None = None):
     """Scatter each token's row into the receive segments of its experts.
 
+    x is bf16 [T, H], or the FP8 tuple (codes [T, H], scales [T, H/128]);
+    with cast_fp8 = a scale format, a bf16 x is cast to FP8 on the way.
     Non-cached (handle=None): needs topk_idx, num_experts, num_ranks; returns
-    (recv_x [recv_capacity, H] bf16, DispatchHandle). Cached (handle given,
-    topk_idx None): reuses the handle's layout; returns (recv_x, handle).
-    recv_capacity defaults to the worst case for the sizes, so no device-to-host
-    copy is needed; rows past handle.expert_offset[-1] are unused.
+    (recv_x, DispatchHandle). Cached (handle given, topk_idx None): reuses the
+    handle's layout; returns (recv_x, handle). recv_x is [recv_capacity, H]
+    bf16, or an FP8 tuple for FP8 payloads. recv_capacity defaults to the
+    worst case for the sizes, so no device-to-host copy is needed; rows past
+    handle.expert_offset[-1] are unused.
     """
     lib = load()
-    _dev_tensor(x, "x", torch.bfloat16, 2)
-    T, H = x.shape
-    dev = x.device
+    fp8 = isinstance(x, tuple)
+    if fp8:
+        q, sc, fmt, st, sb = _fp8_parts(x)
+        T, H = q.shape
+        dev = q.device
+    else:
+        _dev_tensor(x, "x", torch.bfloat16, 2)
+        T, H = x.shape
+        dev = x.device
+    if handle is None and (fp8 or cast_fp8 is not None):
+        if topk_idx is None or num_experts is None or num_ranks is None:
+            raise ValueError("non-cached dispatch needs topk_idx, num_experts and num_ranks")
+        plan = dispatch_plan(topk_idx, num_experts, num_ranks, expert_alignment, recv_capacity)
+        return dispatch_apply(x, plan, recv_x=recv_x, cast_fp8=cast_fp8)
     with torch.cuda.device(dev):
         if handle is not None:
             if topk_idx is not None:
@@ -222,6 +331,13 @@ def dispatch(x: torch.Tensor, topk_idx: torch.Tensor | None = None, num_experts:
             if handle.num_tokens != T:
                 raise ValueError("x has a different number of tokens than the handle")
             cap = handle.recv_capacity
+            if fp8:
+                recv_x = _recv_fp8(recv_x, cap, H, fmt, dev)
+                _check("cgd_dispatch_cached_fp8",
+                       lib.cgd_dispatch_cached_fp8(_ptr(q), _ptr(sc), st, sb, fmt, T, H, handle.num_topk,
+                                                   _ptr(handle.dst_row), _ptr(recv_x[0]), _ptr(recv_x[1]), cap,
+                                                   _stream(dev)))
+                return recv_x, handle
             if recv_x is None:
                 recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
             _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
@@ -288,24 +404,48 @@ def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expe
     return DispatchPlan(h, ws, T)
 
 
-def dispatch_apply(x: torch.Tensor, plan: DispatchPlan, recv_x: torch.Tensor | None = None):
+def dispatch_apply(x, plan: DispatchPlan, recv_x=None, cast_fp8: int | None = None):
     """Second step of dispatch: finalise the handle and copy rows.
-    Returns (recv_x, handle)."""
+    x: bf16 [T, H] or an FP8 tuple; cast_fp8 (a scale format) casts a bf16 x
+    on the way. Returns (recv_x, handle), recv_x an FP8 tuple for FP8 payloads."""
     lib = load()
-    _dev_tensor(x, "x", torch.bfloat16, 2)
-    T, H = x.shape
     h = plan.handle
+    fp8 = isinstance(x, tuple)
+    if fp8:
+        q, sc, fmt, st, sb = _fp8_parts(x)
+        T, H = q.shape
+        dev = q.device
+    else:
+        _dev_tensor(x, "x", torch.bfloat16, 2)
+        T, H = x.shape
+        dev = x.device
     if T != plan.num_tokens:
         raise ValueError("x has a different number of tokens than the plan")
-    dev = x.device
+    cap = h.recv_capacity
     with torch.cuda.device(dev):
+        if fp8:
+            recv_x = _recv_fp8(recv_x, cap, H, fmt, dev)
+            _check("cgd_dispatch_apply_fp8",
+                   lib.cgd_dispatch_apply_fp8(_ptr(q), _ptr(sc), st, sb, fmt, T, H, h.num_topk, h.num_experts, cap,
+                                              _ptr(recv_x[0]), _ptr(recv_x[1]), _ptr(h.expert_offset),
+                                              _ptr(h.recv_src_idx), _ptr(h.dst_row), _ptr(plan.workspace),
+                                              plan.workspace.numel(), _stream(dev)))
+            return recv_x, h
+        if cast_fp8 is not None:
+            recv_x = _recv_fp8(recv_x, cap, H, cast_fp8, dev)
+            _check("cgd_dispatch_apply_cast_fp8",
+                   lib.cgd_dispatch_apply_cast_fp8(_ptr(x), T, H, h.num_topk, h.num_experts, cast_fp8, cap,
+                                                   _ptr(recv_x[0]), _ptr(recv_x[1]), _ptr(h.expert_offset),
+                                                   _ptr(h.recv_src_idx), _ptr(h.dst_row), _ptr(plan.workspace),
+                                                   plan.workspace.numel(), _stream(dev)))
+            return recv_x, h
         if recv_x is None:
-            recv_x = torch.empty((h.recv_capacity, H), dtype=torch.bfloat16, device=dev)
+            recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
         _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
-        if recv_x.shape != (h.recv_capacity, H):
+        if recv_x.shape != (cap, H):
             raise ValueError("recv_x must be [recv_capacity, hidden]")
         _check("cgd_dispatch_apply",
-               lib.cgd_dispatch_apply(_ptr(x), T, H, h.num_topk, h.num_experts, h.recv_capacity, _ptr(recv_x),
+               lib.cgd_dispatch_apply(_ptr(x), T, H, h.num_topk, h.num_experts, cap, _ptr(recv_x),
                                       _ptr(h.expert_offset), _ptr(h.recv_src_idx), _ptr(h.dst_row),
                                       _ptr(plan.workspace), plan.workspace.numel(), _stream(dev)))
     return recv_x, h
@@ -382,6 +522,27 @@ def normal_dispatch(x: torch.Tensor, is_token_in_rank: torch.Tensor | None = Non
     Cached (handle given): -> (recv_x, None, None, None, handle).
     """
     lib = load()
+    if isinstance(x, tuple):
+        q, sc, fmt, st, sb = _fp8_parts(x)
+        T, H = q.shape
+        dev = q.device
+        if handle is None:
+            if is_token_in_rank is None or num_experts is None:
+                raise ValueError("non-cached normal dispatch needs is_token_in_rank and num_experts")
+            plan = normal_dispatch_plan(is_token_in_rank, num_tokens_per_expert, num_experts, expert_alignment)
+            return normal_dispatch_apply(x, plan, topk_idx, topk_weights, num_topk, recv_capacity, recv_x)
+        if is_token_in_rank is not None or topk_idx is not None:
+            raise ValueError("cached normal dispatch takes a handle and no layout")
+        if handle.num_tokens != T:
+            raise ValueError("x has a different number of tokens than the handle")
+        with torch.cuda.device(dev):
+            cap = handle.recv_capacity
+            recv_x = _recv_fp8(recv_x, cap, H, fmt, dev)
+            _check("cgd_normal_dispatch_cached_fp8",
+                   lib.cgd_normal_dispatch_cached_fp8(_ptr(q), _ptr(sc), st, sb, fmt, T, H, handle.num_ranks,
+                                                      _ptr(handle.send_row), _ptr(recv_x[0]), _ptr(recv_x[1]), cap,
+                                                      _stream(dev)))
+        return recv_x, None, None, None, handle
     _dev_tensor(x, "x", torch.bfloat16, 2)
     T, H = x.shape
     dev = x.device
@@ -492,8 +653,15 @@ def normal_dispatch_apply(x: torch.Tensor, plan: NormalPlan, topk_idx: torch.Ten
     """Second step of normal dispatch: rows and per-row outputs.
     -> (recv_x, recv_topk_idx | None, recv_topk_weights | None, num_recv_tokens_per_expert | None, NormalHandle)."""
     lib = load()
-    _dev_tensor(x, "x", torch.bfloat16, 2)
-    T, H = x.shape
+    fp8 = isinstance(x, tuple)
+    if fp8:
+        q, sc, fmt, st, sb = _fp8_parts(x)
+        T, H = q.shape
+        dev = q.device
+    else:
+        _dev_tensor(x, "x", torch.bfloat16, 2)
+        T, H = x.shape
+        dev = x.device
     if T != plan.num_tokens:
         raise ValueError("x has a different number of tokens than the plan")
     R = plan.rank_offset.shape[0] - 1
@@ -509,25 +677,35 @@ def normal_dispatch_apply(x: torch.Tensor, plan: NormalPlan, topk_idx: torch.Ten
         K = int(num_topk)
     else:
         raise ValueError("num_topk is needed when dispatching without top-k")
-    dev = x.device
     with torch.cuda.device(dev):
         cap = int(lib.cgd_normal_capacity(T, K, R)) if recv_capacity is None else int(recv_capacity)
-        if recv_x is None:
-            recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
-        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
-        if recv_x.shape != (cap, H):
-            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        if fp8:
+            recv_x = _recv_fp8(recv_x, max(cap, 0), H, fmt, dev)
+        else:
+            if recv_x is None:
+                recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
+            _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+            if recv_x.shape != (cap, H):
+                raise ValueError("recv_x must be [recv_capacity, hidden]")
         src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
         send = torch.empty((T, R), dtype=torch.int32, device=dev)
         ridx = rw = None
         if topk_idx is not None:
             ridx = torch.empty((max(cap, 0), K), dtype=torch.int64, device=dev)
             rw = torch.empty((max(cap, 0), K), dtype=torch.float32, device=dev)
-        _check("cgd_normal_dispatch_apply",
-               lib.cgd_normal_dispatch_apply(_ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K, plan.num_experts,
-                                             R, _ptr(recv_x), cap, _ptr(plan.rank_offset), _ptr(src), _ptr(send),
-                                             _ptr(ridx), _ptr(rw), _ptr(plan.workspace), plan.workspace.numel(),
-                                             _stream(dev)))
+        if fp8:
+            _check("cgd_normal_dispatch_apply_fp8",
+                   lib.cgd_normal_dispatch_apply_fp8(_ptr(q), _ptr(sc), st, sb, fmt, T, H, _ptr(topk_idx),
+                                                     _ptr(topk_weights), K, plan.num_experts, R, _ptr(recv_x[0]),
+                                                     _ptr(recv_x[1]), cap, _ptr(plan.rank_offset), _ptr(src),
+                                                     _ptr(send), _ptr(ridx), _ptr(rw), _ptr(plan.workspace),
+                                                     plan.workspace.numel(), _stream(dev)))
+        else:
+            _check("cgd_normal_dispatch_apply",
+                   lib.cgd_normal_dispatch_apply(_ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K,
+                                                 plan.num_experts, R, _ptr(recv_x), cap, _ptr(plan.rank_offset),
+                                                 _ptr(src), _ptr(send), _ptr(ridx), _ptr(rw), _ptr(plan.workspace),
+                                                 plan.workspace.numel(), _stream(dev)))
     return recv_x, ridx, rw, plan.num_recv_tokens_per_expert, NormalHandle(plan.rank_offset, src, send, K, cap)
 
 

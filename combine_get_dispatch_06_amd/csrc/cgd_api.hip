@@ -61,6 +61,23 @@ int64_t capacity_of(int64_t T, int K, int E, int A) {
     return cap;
 }
 
+// FP8 payload: rows of H e4m3 bytes with H % 128 == 0, one scale per block
+// of 128 channels (4-byte fp32, or 1-byte UE8M0 for format 2).
+int check_fp8(int H, int fmt) {
+    if (H < 128 || H % 128 != 0)
+        return fail(CGD_ERR_INVALID_ARG, "FP8 payload needs hidden to be a positive multiple of 128 (got %d)", H);
+    if (fmt < CGD_SCALE_F32 || fmt > CGD_SCALE_UE8M0)
+        return fail(CGD_ERR_INVALID_ARG, "scale_format must be 0, 1 or 2 (got %d)", fmt);
+    return CGD_OK;
+}
+
+int check_scales(const void* scales, int64_t st, int64_t sb, int fmt, bool needed) {
+    if (needed && !scales) return fail(CGD_ERR_INVALID_ARG, "null scales");
+    if (st < 0 || sb < 0) return fail(CGD_ERR_INVALID_ARG, "scale strides must be >= 0");
+    if (!aligned(scales, fmt == CGD_SCALE_UE8M0 ? 1 : 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned scales");
+    return CGD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -404,6 +421,143 @@ int cgd_normal_combine(const void* expert_out, int64_t recv_rows, int hidden, co
                                                 recv_topk_weights, num_topk, bias_0, bias_1, combined_x,
                                                 combined_topk_weights, stream);
     if (err != hipSuccess) return hip_fail(err, "normal combine launch");
+    return CGD_OK;
+}
+
+int cgd_cast_to_fp8(const void* x, int64_t num_tokens, int hidden, void* x_fp8, void* x_scales,
+                    int64_t scale_stride_token, int64_t scale_stride_block, int scale_format, hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if ((rc = check_scales(x_scales, scale_stride_token, scale_stride_block, scale_format, num_tokens > 0))) return rc;
+    if (num_tokens > 0 && (!x || !x_fp8)) return fail(CGD_ERR_INVALID_ARG, "null x or x_fp8");
+    if (!aligned(x, 16) || !aligned(x_fp8, 16)) return fail(CGD_ERR_INVALID_ARG, "x and x_fp8 must be 16-byte aligned");
+    hipError_t err = cgd::launch_cast_to_fp8(x, num_tokens, hidden, x_fp8, x_scales, scale_stride_token,
+                                             scale_stride_block, scale_format, stream);
+    if (err != hipSuccess) return hip_fail(err, "cast launch");
+    return CGD_OK;
+}
+
+int cgd_cast_back(const void* x_fp8, const void* x_scales, int64_t scale_stride_token, int64_t scale_stride_block,
+                  int scale_format, int64_t num_tokens, int hidden, void* out, hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if ((rc = check_scales(x_scales, scale_stride_token, scale_stride_block, scale_format, num_tokens > 0))) return rc;
+    if (num_tokens > 0 && (!x_fp8 || !out)) return fail(CGD_ERR_INVALID_ARG, "null x_fp8 or out");
+    if (!aligned(x_fp8, 16) || !aligned(out, 16)) return fail(CGD_ERR_INVALID_ARG, "x_fp8 and out must be 16-byte aligned");
+    hipError_t err = cgd::launch_cast_back(x_fp8, x_scales, scale_stride_token, scale_stride_block, scale_format,
+                                           num_tokens, hidden, out, stream);
+    if (err != hipSuccess) return hip_fail(err, "cast back launch");
+    return CGD_OK;
+}
+
+int cgd_dispatch_apply_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                           int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
+                           int num_experts, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
+                           const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
+                           const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if ((rc = check_apply_args(x_fp8, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x_fp8,
+                               expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes)))
+        return rc;
+    if ((rc = check_scales(x_scales, scale_stride_token, scale_stride_block, scale_format, num_tokens > 0))) return rc;
+    if ((rc = check_scales(recv_scales, 0, 0, scale_format, recv_capacity > 0))) return rc;
+    hipError_t err = cgd::launch_dispatch_apply_fp8(x_fp8, x_scales, scale_stride_token, scale_stride_block,
+                                                    scale_format, num_tokens, hidden, num_topk, num_experts,
+                                                    recv_x_fp8, recv_scales, recv_capacity, expert_offset,
+                                                    recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "FP8 dispatch apply launch");
+    return CGD_OK;
+}
+
+int cgd_dispatch_apply_cast_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                int scale_format, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
+                                const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
+                                const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if ((rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x_fp8, expert_offset,
+                               recv_src_idx, dst_row, workspace, workspace_bytes)))
+        return rc;
+    if ((rc = check_scales(recv_scales, 0, 0, scale_format, recv_capacity > 0))) return rc;
+    hipError_t err = cgd::launch_dispatch_apply_cast_fp8(x, num_tokens, hidden, num_topk, num_experts, scale_format,
+                                                         recv_x_fp8, recv_scales, recv_capacity, expert_offset,
+                                                         recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "FP8 cast dispatch apply launch");
+    return CGD_OK;
+}
+
+int cgd_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                            int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
+                            const int32_t* dst_row, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                            hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_topk < 1 || num_topk > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16]");
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if (recv_capacity < 0 || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
+    if (num_tokens > 0 && (!x_fp8 || !dst_row || (recv_capacity > 0 && !recv_x_fp8)))
+        return fail(CGD_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x_fp8, 16) || !aligned(recv_x_fp8, 16))
+        return fail(CGD_ERR_INVALID_ARG, "x_fp8 and recv_x_fp8 must be 16-byte aligned");
+    if (!aligned(dst_row, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned dst_row");
+    if ((rc = check_scales(x_scales, scale_stride_token, scale_stride_block, scale_format, num_tokens > 0))) return rc;
+    if ((rc = check_scales(recv_scales, 0, 0, scale_format, num_tokens > 0 && recv_capacity > 0))) return rc;
+    hipError_t err = cgd::launch_dispatch_cached_fp8(x_fp8, x_scales, scale_stride_token, scale_stride_block,
+                                                     scale_format, num_tokens, hidden, num_topk, dst_row, recv_x_fp8,
+                                                     recv_scales, recv_capacity, stream);
+    if (err != hipSuccess) return hip_fail(err, "cached FP8 dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_normal_dispatch_apply_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                                  int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden,
+                                  const int64_t* topk_idx, const float* topk_weights, int num_topk, int num_experts,
+                                  int num_ranks, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                  const int32_t* rank_offset, int32_t* recv_src_idx, int32_t* send_row,
+                                  int64_t* recv_topk_idx, float* recv_topk_weights, const void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if ((rc = check_normal_apply_args(x_fp8, num_tokens, hidden, topk_idx, topk_weights, num_topk, num_experts,
+                                      num_ranks, recv_x_fp8, recv_capacity, rank_offset, recv_src_idx, send_row,
+                                      recv_topk_idx, recv_topk_weights, workspace, workspace_bytes)))
+        return rc;
+    if ((rc = check_scales(x_scales, scale_stride_token, scale_stride_block, scale_format, num_tokens > 0))) return rc;
+    if ((rc = check_scales(recv_scales, 0, 0, scale_format, recv_capacity > 0))) return rc;
+    hipError_t err = cgd::launch_normal_apply_fp8(x_fp8, x_scales, scale_stride_token, scale_stride_block,
+                                                  scale_format, num_tokens, hidden, topk_idx, topk_weights, num_topk,
+                                                  num_experts, num_ranks, recv_x_fp8, recv_scales, recv_capacity,
+                                                  rank_offset, recv_src_idx, send_row, recv_topk_idx,
+                                                  recv_topk_weights, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "FP8 normal dispatch apply launch");
+    return CGD_OK;
+}
+
+int cgd_normal_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                                   int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden,
+                                   int num_ranks, const int32_t* send_row, void* recv_x_fp8, void* recv_scales,
+                                   int64_t recv_capacity, hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_ranks < 1 || num_ranks > cgd::kMaxRanks) return fail(CGD_ERR_INVALID_ARG, "num_ranks must be in [1,384]");
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if (recv_capacity < 0 || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
+    if (num_tokens > 0 && (!x_fp8 || !send_row || (recv_capacity > 0 && !recv_x_fp8)))
+        return fail(CGD_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x_fp8, 16) || !aligned(recv_x_fp8, 16))
+        return fail(CGD_ERR_INVALID_ARG, "x_fp8 and recv_x_fp8 must be 16-byte aligned");
+    if (!aligned(send_row, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned send_row");
+    if ((rc = check_scales(x_scales, scale_stride_token, scale_stride_block, scale_format, num_tokens > 0))) return rc;
+    if ((rc = check_scales(recv_scales, 0, 0, scale_format, num_tokens > 0 && recv_capacity > 0))) return rc;
+    hipError_t err = cgd::launch_normal_dispatch_cached_fp8(x_fp8, x_scales, scale_stride_token, scale_stride_block,
+                                                            scale_format, num_tokens, hidden, num_ranks, send_row,
+                                                            recv_x_fp8, recv_scales, recv_capacity, stream);
+    if (err != hipSuccess) return hip_fail(err, "cached FP8 normal dispatch launch");
     return CGD_OK;
 }
 

@@ -32,6 +32,78 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, b);
 }
 
+// ---- FP8 (OCP e4m3fn) payload -------------------------------------------
+// One scale per token and block of 128 channels (kFp8Block). Scale formats:
+// 0 fp32 amax/448; 1 fp32 power of two (the smallest 2^k >= amax/448);
+// 2 that power of two as the byte k + 127 (UE8M0). Every step is fp32, with
+// correctly rounded division, so the 8-bit codes are decided exactly as the
+// format's definition states.
+constexpr int kFp8Block = 128;
+constexpr float kE4m3Max = 448.0f;  // largest finite e4m3fn value
+
+struct Fp8Scale {
+    float mul;      // multiplier applied before encoding
+    float scale;    // dequantisation scale (fp32 formats)
+    uint32_t ue8m0; // biased exponent byte (format 2)
+};
+
+__device__ __forceinline__ Fp8Scale fp8_block_scale(float amax, int fmt) {
+    amax = amax < 1e-4f ? 1e-4f : amax;  // a block of zeros keeps a positive scale
+    Fp8Scale r;
+    if (fmt == 0) {
+        r.mul = kE4m3Max / amax;
+        r.scale = amax / kE4m3Max;
+        r.ue8m0 = 0;
+    } else {
+        int e;
+        const float m = frexpf(amax / kE4m3Max, &e);
+        const int k = (m == 0.5f) ? e - 1 : e;
+        r.mul = ldexpf(1.0f, -k);
+        r.scale = ldexpf(1.0f, k);
+        r.ue8m0 = (uint32_t)(k + 127);
+    }
+    return r;
+}
+
+// Max over the 16 lanes of an aligned lane group (one 128-channel block when
+// each lane holds 8 channels).
+__device__ __forceinline__ float group16_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 8, kWave));
+    v = fmaxf(v, __shfl_xor(v, 4, kWave));
+    v = fmaxf(v, __shfl_xor(v, 2, kWave));
+    v = fmaxf(v, __shfl_xor(v, 1, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float clamp_e4m3(float v) {
+    v = v > kE4m3Max ? kE4m3Max : v;  // NaN passes through unchanged
+    return v < -kE4m3Max ? -kE4m3Max : v;
+}
+
+// Four fp32 values -> four e4m3fn bytes (element 0 in the low byte). gfx950's
+// conversion rounds to nearest even but does not saturate, hence the clamp.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(a), clamp_e4m3(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(c), clamp_e4m3(d), w, true);
+    return (uint32_t)w;
+}
+
+// Absolute max of the 8 bf16 values of a 16-byte vector.
+__device__ __forceinline__ float absmax_bf16x8(const uint4& q) {
+    float m = fmaxf(fabsf(bf16_lo(q.x)), fabsf(bf16_hi(q.x)));
+    m = fmaxf(m, fmaxf(fabsf(bf16_lo(q.y)), fabsf(bf16_hi(q.y))));
+    m = fmaxf(m, fmaxf(fabsf(bf16_lo(q.z)), fabsf(bf16_hi(q.z))));
+    return fmaxf(m, fmaxf(fabsf(bf16_lo(q.w)), fabsf(bf16_hi(q.w))));
+}
+
+// 8 bf16 values times mul -> 8 e4m3fn bytes.
+__device__ __forceinline__ uint2 quantize_bf16x8(const uint4& q, float mul) {
+    uint2 r;
+    r.x = pack_e4m3x4(bf16_lo(q.x) * mul, bf16_hi(q.x) * mul, bf16_lo(q.y) * mul, bf16_hi(q.y) * mul);
+    r.y = pack_e4m3x4(bf16_lo(q.z) * mul, bf16_hi(q.z) * mul, bf16_lo(q.w) * mul, bf16_hi(q.w) * mul);
+    return r;
+}
+
 // Streaming 16-byte global accesses: data touched once should not displace
 // reusable lines in L2 / MALL.
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
@@ -48,6 +120,41 @@ __device__ __forceinline__ void store_nt(uint4* p, const uint4& v) {
     __builtin_nontemporal_store(v.y, &p->y);
     __builtin_nontemporal_store(v.z, &p->z);
     __builtin_nontemporal_store(v.w, &p->w);
+}
+
+__device__ __forceinline__ uint2 load_nt(const uint2* p) {
+    uint2 v;
+    v.x = __builtin_nontemporal_load(&p->x);
+    v.y = __builtin_nontemporal_load(&p->y);
+    return v;
+}
+
+__device__ __forceinline__ void store_nt(uint2* p, const uint2& v) {
+    __builtin_nontemporal_store(v.x, &p->x);
+    __builtin_nontemporal_store(v.y, &p->y);
+}
+
+// Optional per-row side payload moved with dispatched rows (the FP8 scales):
+// nsb elements of sbytes (4 or 1) bytes per token at src + t*st + j*sb
+// (element strides, so column-major scales work too), copied to
+// dst[row * nsb + j].
+struct SideRows {
+    const void* src;
+    int64_t st, sb;
+    int nsb;
+    int sbytes;
+    void* dst;
+};
+
+// Copy token t's side payload to receive row `row` (lanes stride the elements).
+__device__ __forceinline__ void copy_side_row(const SideRows& s, int64_t t, int64_t row, int lane) {
+    for (int j = lane; j < s.nsb; j += kWave) {
+        const int64_t i = t * s.st + (int64_t)j * s.sb;
+        if (s.sbytes == 4)
+            static_cast<float*>(s.dst)[row * s.nsb + j] = static_cast<const float*>(s.src)[i];
+        else
+            static_cast<uint8_t*>(s.dst)[row * s.nsb + j] = static_cast<const uint8_t*>(s.src)[i];
+    }
 }
 
 // Copy n (<= ITEMS * blockDim.x) routing entries of one tile into LDS as

@@ -209,6 +209,26 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     reset_ticket(ticket);
 }
 
+// Rows past the data carry no source token (grid-stride over all threads).
+__device__ __forceinline__ void fill_tail(int32_t* __restrict__ recv_src_idx, const int32_t* __restrict__ expert_offset,
+                                          int E, int64_t cap) {
+    const int64_t n = max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t r = n + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < cap; r += stride) recv_src_idx[r] = -1;
+}
+
+// Final receive row of a packed slot word p from the plan (-1: not selected).
+// A consistent plan gives an expert < E and a row < cap; anything else maps
+// to -1, so no access leaves the workspace or the receive buffer.
+__device__ __forceinline__ int final_row(int p, int64_t t, const int32_t* __restrict__ tile_base, int E,
+                                         const int32_t* __restrict__ expert_offset, int64_t cap) {
+    if (p < 0) return -1;
+    const int ex = p >> kPackBits;
+    const int lr = p & ((1 << kPackBits) - 1);
+    const int d = (ex < E) ? expert_offset[ex] + tile_base[(t / kRankTile) * E + ex] + lr : -1;
+    return (d < 0 || d >= cap) ? -1 : d;
+}
+
 // One wave per (token, column chunk of U*64 16-byte vectors). With PACKED
 // (dispatch apply) the wave turns the plan's packed slot words into final rows
 // (tile base + rank in tile); the token's chunk-0 wave also records dst_row
@@ -216,7 +236,9 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
 // final rows. Lanes 0..K-1 broadcast the K rows; each lane loads its U
 // vectors once and stores them to every destination row with non-temporal
 // stores. Many short waves in token order keep every CU busy even for a few
-// tokens and keep the writes in flight close together.
+// tokens and keep the writes in flight close together. A row is nvec 16-byte
+// vectors of any payload (bf16 rows, or FP8 rows with their scales moved as
+// the side payload by the chunk-0 wave).
 template <int KM, int U, bool PACKED>
 __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t T, int nvec,
                                                                       int nchunk, int K, const int32_t* __restrict__ slot,
@@ -224,15 +246,10 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
                                                                       const int32_t* __restrict__ tile_base, int E,
                                                                       int32_t* __restrict__ recv_src_idx,
                                                                       const int32_t* __restrict__ expert_offset,
-                                                                      int64_t cap, uint4* __restrict__ recv_x) {
+                                                                      int64_t cap, uint4* __restrict__ recv_x,
+                                                                      SideRows side) {
     const int lane = lane_id();
-    if (PACKED) {
-        // rows past the data carry no source token
-        const int64_t n = max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
-        const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-        for (int64_t r = n + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < cap; r += stride)
-            recv_src_idx[r] = -1;
-    }
+    if (PACKED) fill_tail(recv_src_idx, expert_offset, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t t = g / nchunk;
     if (t >= T) return;
@@ -249,14 +266,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
     if (lane < K) {
         const int p = slot[t * K + lane];
         if (PACKED) {
-            if (p >= 0) {
-                const int ex = p >> kPackBits;
-                const int lr = p & ((1 << kPackBits) - 1);
-                // a consistent plan gives ex < E and d < cap; never read or
-                // write outside the workspace or recv_x otherwise
-                d = (ex < E) ? expert_offset[ex] + tile_base[(t / kRankTile) * E + ex] + lr : -1;
-                if (d < 0 || d >= cap) d = -1;
-            }
+            d = final_row(p, t, tile_base, E, expert_offset, cap);
             if (c == 0) {
                 dst_row[t * K + lane] = d;
                 if (d >= 0) recv_src_idx[d] = (int32_t)t;
@@ -288,6 +298,74 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
                     dr[v] = buf[u];
             }
         }
+        if (side.src && c == 0) copy_side_row(side, t, dk[k], lane);
+    }
+}
+
+// Fused FP8 cast and dispatch apply (bf16 x in, e4m3fn rows and per-block
+// scales out). One wave per (token, chunk of U*512 channels): each lane holds
+// 8 channels per 512, so a 16-lane group holds one 128-channel block, whose
+// absolute max comes from a 16-lane reduction. The chunk is quantized once and
+// its 8-byte code vectors and block scales are stored to every destination
+// row. Rows are H bytes; scales are [cap, H/128] (4 bytes, or 1 byte UE8M0).
+template <int KM, int U, int FMT>
+__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
+    const uint4* __restrict__ x, int64_t T, int nvec, int nchunk, int K, const int32_t* __restrict__ slot,
+    int32_t* __restrict__ dst_row, const int32_t* __restrict__ tile_base, int E, int32_t* __restrict__ recv_src_idx,
+    const int32_t* __restrict__ expert_offset, int64_t cap, uint2* __restrict__ recv_q, void* __restrict__ recv_s) {
+    const int lane = lane_id();
+    fill_tail(recv_src_idx, expert_offset, E, cap);
+    const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
+    const int64_t t = g / nchunk;
+    if (t >= T) return;
+    const int c = (int)(g - t * nchunk);
+    const int v0 = c * U * kWave;  // first 8-channel vector of the chunk
+    const int nsb = nvec / (kFp8Block / 8);
+    const uint4* xr = x + t * nvec;
+    uint4 buf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kWave + lane;
+        if (v < nvec) buf[u] = load_nt(xr + v);
+    }
+    int d = -1;
+    if (lane < K) {
+        d = final_row(slot[t * K + lane], t, tile_base, E, expert_offset, cap);
+        if (c == 0) {
+            dst_row[t * K + lane] = d;
+            if (d >= 0) recv_src_idx[d] = (int32_t)t;
+        }
+    }
+    // quantize: a block never straddles lanes of two groups (nvec % 16 == 0)
+    uint2 code[U];
+    Fp8Scale sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kWave + lane;
+        const float m = group16_max(v < nvec ? absmax_bf16x8(buf[u]) : 0.0f);
+        sc[u] = fp8_block_scale(m, FMT);
+        code[u] = quantize_bf16x8(buf[u], sc[u].mul);
+    }
+    int dk[KM];
+#pragma unroll
+    for (int k = 0; k < KM; ++k) dk[k] = __builtin_amdgcn_readlane(d, k);
+#pragma unroll
+    for (int k = 0; k < KM; ++k) {
+        if (dk[k] < 0) continue;
+        uint2* dr = recv_q + (int64_t)dk[k] * nvec;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * kWave + lane;
+            if (v >= nvec) continue;
+            store_nt(dr + v, code[u]);
+            if ((lane & 15) == 0) {
+                const int64_t si = (int64_t)dk[k] * nsb + v / (kFp8Block / 8);
+                if (FMT == 2)
+                    static_cast<uint8_t*>(recv_s)[si] = (uint8_t)sc[u].ue8m0;
+                else
+                    static_cast<float*>(recv_s)[si] = sc[u].scale;
+            }
+        }
     }
 }
 
@@ -306,7 +384,7 @@ size_t dispatch_workspace_bytes(int64_t T, int K, int E) {
 template <bool PACKED, int U>
 static void launch_scatter_u(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
                              int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
-                             int64_t cap, void* recv_x) {
+                             int64_t cap, void* recv_x, const SideRows& side) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t waves = T * nchunk;
     const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
@@ -315,7 +393,7 @@ static void launch_scatter_u(int64_t T, int K, hipStream_t s, const void* x, int
     uint4* rv = reinterpret_cast<uint4*>(recv_x);
 #define CGD_SCATTER(KM)                                                                                            \
     hipLaunchKernelGGL((scatter_kernel<KM, U, PACKED>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot, dst_row,    \
-                       tile_base, E, src, off, cap, rv)
+                       tile_base, E, src, off, cap, rv, side)
     if (K <= 2)
         CGD_SCATTER(2);
     else if (K <= 4)
@@ -334,13 +412,19 @@ constexpr int64_t kMinScatterWaves = 4096;
 template <bool PACKED>
 static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
                            int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
-                           int64_t cap, void* recv_x) {
+                           int64_t cap, void* recv_x, const SideRows& side) {
     constexpr int U = CGD_SCATTER_U;
     const int64_t waves = T * ((nvec + U * kWave - 1) / (U * kWave));
     if (waves >= kMinScatterWaves)
-        launch_scatter_u<PACKED, U>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x);
+        launch_scatter_u<PACKED, U>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x, side);
     else
-        launch_scatter_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x);
+        launch_scatter_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x, side);
+}
+
+static SideRows no_side() { return SideRows{nullptr, 0, 0, 0, 0, nullptr}; }
+
+static SideRows fp8_side(const void* scales, int64_t st, int64_t sb, int H, int fmt, void* recv_scales) {
+    return SideRows{scales, st, sb, H / kFp8Block, fmt == 2 ? 1 : 4, recv_scales};
 }
 
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
@@ -364,14 +448,96 @@ hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, 
     const int32_t* tile_base = reinterpret_cast<const int32_t*>(ws + kTicketBytes);
     const int32_t* slot_pack = reinterpret_cast<const int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
     launch_scatter<true>(T, K, stream, x, H / 8, slot_pack, dst_row, tile_base, E, recv_src_idx, expert_offset, cap,
-                         recv_x);
+                         recv_x, no_side());
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_apply_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
+                                     int H, int K, int E, void* recv_q, void* recv_s, int64_t cap,
+                                     const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
+                                     const void* workspace, hipStream_t stream) {
+    const char* ws = reinterpret_cast<const char*>(workspace);
+    const int32_t* tile_base = reinterpret_cast<const int32_t*>(ws + kTicketBytes);
+    const int32_t* slot_pack = reinterpret_cast<const int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
+    launch_scatter<true>(T, K, stream, xq, H / 16, slot_pack, dst_row, tile_base, E, recv_src_idx, expert_offset,
+                         cap, recv_q, fp8_side(xs, st, sb, H, fmt, recv_s));
+    return hipGetLastError();
+}
+
+template <int U, int FMT>
+static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E, const int32_t* slot,
+                                  int32_t* dst_row, const int32_t* tile_base, int32_t* src, const int32_t* off,
+                                  int64_t cap, void* recv_q, void* recv_s, hipStream_t s) {
+    const int nvec = H / 8;
+    const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
+    const int64_t waves = T * nchunk;
+    const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
+    const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    uint2* qv = reinterpret_cast<uint2*>(recv_q);
+#define CGD_SCATTER_CAST(KM)                                                                                         \
+    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot, dst_row,   \
+                       tile_base, E, src, off, cap, qv, recv_s)
+    if (K <= 2)
+        CGD_SCATTER_CAST(2);
+    else if (K <= 4)
+        CGD_SCATTER_CAST(4);
+    else if (K <= 8)
+        CGD_SCATTER_CAST(8);
+    else
+        CGD_SCATTER_CAST(16);
+#undef CGD_SCATTER_CAST
+}
+
+#ifndef CGD_SCATTER_CAST_U
+#define CGD_SCATTER_CAST_U 2
+#endif
+
+template <int FMT>
+static void launch_scatter_cast(const void* x, int64_t T, int H, int K, int E, const int32_t* slot, int32_t* dst_row,
+                                const int32_t* tile_base, int32_t* src, const int32_t* off, int64_t cap, void* recv_q,
+                                void* recv_s, hipStream_t s) {
+    constexpr int U = CGD_SCATTER_CAST_U;
+    const int64_t waves = T * ((H / 8 + U * kWave - 1) / (U * kWave));
+    if (waves >= kMinScatterWaves)
+        launch_scatter_cast_u<U, FMT>(x, T, H, K, E, slot, dst_row, tile_base, src, off, cap, recv_q, recv_s, s);
+    else
+        launch_scatter_cast_u<1, FMT>(x, T, H, K, E, slot, dst_row, tile_base, src, off, cap, recv_q, recv_s, s);
+}
+
+hipError_t launch_dispatch_apply_cast_fp8(const void* x, int64_t T, int H, int K, int E, int fmt, void* recv_q,
+                                          void* recv_s, int64_t cap, const int32_t* expert_offset,
+                                          int32_t* recv_src_idx, int32_t* dst_row, const void* workspace,
+                                          hipStream_t stream) {
+    const char* ws = reinterpret_cast<const char*>(workspace);
+    const int32_t* tile_base = reinterpret_cast<const int32_t*>(ws + kTicketBytes);
+    const int32_t* slot_pack = reinterpret_cast<const int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
+    if (fmt == 0)
+        launch_scatter_cast<0>(x, T, H, K, E, slot_pack, dst_row, tile_base, recv_src_idx, expert_offset, cap, recv_q,
+                               recv_s, stream);
+    else if (fmt == 1)
+        launch_scatter_cast<1>(x, T, H, K, E, slot_pack, dst_row, tile_base, recv_src_idx, expert_offset, cap, recv_q,
+                               recv_s, stream);
+    else
+        launch_scatter_cast<2>(x, T, H, K, E, slot_pack, dst_row, tile_base, recv_src_idx, expert_offset, cap, recv_q,
+                               recv_s, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
                                   int64_t cap, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    launch_scatter<false>(T, K, stream, x, H / 8, dst_row, nullptr, nullptr, 0, nullptr, nullptr, cap, recv_x);
+    launch_scatter<false>(T, K, stream, x, H / 8, dst_row, nullptr, nullptr, 0, nullptr, nullptr, cap, recv_x,
+                          no_side());
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
+                                      int H, int K, const int32_t* dst_row, void* recv_q, void* recv_s, int64_t cap,
+                                      hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    launch_scatter<false>(T, K, stream, xq, H / 16, dst_row, nullptr, nullptr, 0, nullptr, nullptr, cap, recv_q,
+                          fp8_side(xs, st, sb, H, fmt, recv_s));
     return hipGetLastError();
 }
 

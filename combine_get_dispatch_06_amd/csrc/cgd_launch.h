@@ -55,4 +55,35 @@ hipError_t launch_normal_combine(const void* expert_out, int64_t rows, int H, co
                                  int R, const float* recv_w, int K, const void* bias0, const void* bias1, void* out,
                                  float* out_w, hipStream_t stream);
 
+// FP8 payload (scale format 0 fp32, 1 fp32 power of two, 2 UE8M0 byte).
+hipError_t launch_cast_to_fp8(const void* x, int64_t T, int H, void* q, void* scales, int64_t st, int64_t sb, int fmt,
+                              hipStream_t stream);
+
+hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64_t sb, int fmt, int64_t T, int H,
+                            void* out, hipStream_t stream);
+
+hipError_t launch_dispatch_apply_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
+                                     int H, int K, int E, void* recv_q, void* recv_s, int64_t cap,
+                                     const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
+                                     const void* workspace, hipStream_t stream);
+
+hipError_t launch_dispatch_apply_cast_fp8(const void* x, int64_t T, int H, int K, int E, int fmt, void* recv_q,
+                                          void* recv_s, int64_t cap, const int32_t* expert_offset,
+                                          int32_t* recv_src_idx, int32_t* dst_row, const void* workspace,
+                                          hipStream_t stream);
+
+hipError_t launch_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
+                                      int H, int K, const int32_t* dst_row, void* recv_q, void* recv_s, int64_t cap,
+                                      hipStream_t stream);
+
+hipError_t launch_normal_apply_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T, int H,
+                                   const int64_t* topk_idx, const float* topk_w, int K, int E, int R, void* recv_q,
+                                   void* recv_s, int64_t cap, const int32_t* rank_offset, int32_t* recv_src_idx,
+                                   int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w,
+                                   const void* workspace, hipStream_t stream);
+
+hipError_t launch_normal_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt,
+                                             int64_t T, int H, int R, const int32_t* send_row, void* recv_q,
+                                             void* recv_s, int64_t cap, hipStream_t stream);
+
 }  // namespace cgd

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kNormScatterWaves* kWave) void normal_scatter_kerne
     const int32_t* __restrict__ grp_pre, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ send_row, int32_t* __restrict__ recv_src_idx, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int K, int E, int L, int64_t* __restrict__ recv_topk_idx,
-    float* __restrict__ recv_topk_w, int64_t cap, uint4* __restrict__ recv_x) {
+    float* __restrict__ recv_topk_w, int64_t cap, uint4* __restrict__ recv_x, SideRows side) {
     const int lane = lane_id();
     if (!CACHED) {
         // rows past the data carry no token, no expert and zero weights
@@ -256,6 +256,7 @@ __global__ __launch_bounds__(kNormScatterWaves* kWave) void normal_scatter_kerne
                 const int v = v0 + u * kWave + lane;
                 if (v < nvec) store_nt(dr + v, buf[u]);
             }
+            if (side.src && c == 0) copy_side_row(side, t, dd, lane);
             if (meta) {
                 if (lane == 0) recv_src_idx[dd] = (int32_t)t;
                 if (with_topk && lane < K) {
@@ -386,7 +387,7 @@ static void launch_normal_scatter_u(const void* x, int64_t T, int nvec, int R, c
                                     const int32_t* rank_offset, int32_t* send_row, int32_t* recv_src_idx,
                                     const int64_t* topk_idx, const float* topk_w, int K, int E,
                                     int64_t* recv_topk_idx, float* recv_topk_w, int64_t cap, void* recv_x,
-                                    hipStream_t s) {
+                                    const SideRows& side, hipStream_t s) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t waves = T * nchunk;
     const int64_t blocks = waves <= 0 ? 1 : (waves + kNormScatterWaves - 1) / kNormScatterWaves;
@@ -394,23 +395,26 @@ static void launch_normal_scatter_u(const void* x, int64_t T, int nvec, int R, c
                        s, reinterpret_cast<const uint4*>(x), T, nvec, nchunk, R, w ? w->grp_bal : nullptr,
                        w ? w->grp_pre : nullptr, w ? w->tile_base : nullptr, rank_offset, send_row, recv_src_idx,
                        topk_idx, topk_w, K, E, R > 0 ? E / R : 1, recv_topk_idx, recv_topk_w, cap,
-                       reinterpret_cast<uint4*>(recv_x));
+                       reinterpret_cast<uint4*>(recv_x), side);
 }
 
 template <bool CACHED>
 static void launch_normal_scatter(const void* x, int64_t T, int nvec, int R, const NormalWs* w,
                                   const int32_t* rank_offset, int32_t* send_row, int32_t* recv_src_idx,
                                   const int64_t* topk_idx, const float* topk_w, int K, int E, int64_t* recv_topk_idx,
-                                  float* recv_topk_w, int64_t cap, void* recv_x, hipStream_t s) {
+                                  float* recv_topk_w, int64_t cap, void* recv_x, const SideRows& side,
+                                  hipStream_t s) {
     constexpr int U = CGD_NORMAL_SCATTER_U;
     const int64_t wavesU = T * ((nvec + U * kWave - 1) / (U * kWave));
     if (wavesU >= kNormMinWaves)
         launch_normal_scatter_u<CACHED, U>(x, T, nvec, R, w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w,
-                                           K, E, recv_topk_idx, recv_topk_w, cap, recv_x, s);
+                                           K, E, recv_topk_idx, recv_topk_w, cap, recv_x, side, s);
     else
         launch_normal_scatter_u<CACHED, 1>(x, T, nvec, R, w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w,
-                                           K, E, recv_topk_idx, recv_topk_w, cap, recv_x, s);
+                                           K, E, recv_topk_idx, recv_topk_w, cap, recv_x, side, s);
 }
+
+static SideRows normal_no_side() { return SideRows{nullptr, 0, 0, 0, 0, nullptr}; }
 
 hipError_t launch_normal_plan(const uint8_t* itr, int64_t T, int R, const int32_t* ntpe, int E, int A,
                               int32_t* rank_offset, int32_t* nrecv, void* workspace, hipStream_t stream) {
@@ -428,7 +432,19 @@ hipError_t launch_normal_apply(const void* x, int64_t T, int H, const int64_t* t
                                const void* workspace, hipStream_t stream) {
     const NormalWs w = normal_ws(const_cast<void*>(workspace), T, R);
     launch_normal_scatter<false>(x, T, H / 8, R, &w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w, K, E,
-                                 recv_topk_idx, recv_topk_w, cap, recv_x, stream);
+                                 recv_topk_idx, recv_topk_w, cap, recv_x, normal_no_side(), stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_normal_apply_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T, int H,
+                                   const int64_t* topk_idx, const float* topk_w, int K, int E, int R, void* recv_q,
+                                   void* recv_s, int64_t cap, const int32_t* rank_offset, int32_t* recv_src_idx,
+                                   int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w,
+                                   const void* workspace, hipStream_t stream) {
+    const NormalWs w = normal_ws(const_cast<void*>(workspace), T, R);
+    const SideRows side{xs, st, sb, H / kFp8Block, fmt == 2 ? 1 : 4, recv_s};
+    launch_normal_scatter<false>(xq, T, H / 16, R, &w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w, K, E,
+                                 recv_topk_idx, recv_topk_w, cap, recv_q, side, stream);
     return hipGetLastError();
 }
 
@@ -436,7 +452,17 @@ hipError_t launch_normal_dispatch_cached(const void* x, int64_t T, int H, int R,
                                          void* recv_x, int64_t cap, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     launch_normal_scatter<true>(x, T, H / 8, R, nullptr, nullptr, const_cast<int32_t*>(send_row), nullptr, nullptr,
-                                nullptr, 1, 1, nullptr, nullptr, cap, recv_x, stream);
+                                nullptr, 1, 1, nullptr, nullptr, cap, recv_x, normal_no_side(), stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_normal_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt,
+                                             int64_t T, int H, int R, const int32_t* send_row, void* recv_q,
+                                             void* recv_s, int64_t cap, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    const SideRows side{xs, st, sb, H / kFp8Block, fmt == 2 ? 1 : 4, recv_s};
+    launch_normal_scatter<true>(xq, T, H / 16, R, nullptr, nullptr, const_cast<int32_t*>(send_row), nullptr, nullptr,
+                                nullptr, 1, 1, nullptr, nullptr, cap, recv_q, side, stream);
     return hipGetLastError();
 }
 

@@ -267,6 +267,78 @@ int cgd_normal_combine(const void* expert_out, int64_t recv_rows, int hidden, co
                        const void* bias_0, const void* bias_1, void* combined_x, float* combined_topk_weights,
                        hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 payload (OCP e4m3fn codes with one scale per token and 128 channels).
+ *
+ * The pages' FP8 form of x and recv_x is the tuple (x_e4m3 [T, H],
+ * x_scales [T, H/128] fp32) with H divisible by 128 (Python interface notes,
+ * "Dispatch API"); the scales may be stored column-major and the cast helpers
+ * are per_token_cast_to_fp8 / per_token_cast_back (legacy test analysis page,
+ * test data excerpt); the low-latency dispatch adds round_scale and use_ue8m0.
+ * For each token and block of 128 channels, amax = max |x| floored at 1e-4:
+ *   CGD_SCALE_F32    scale = amax / 448, code = e4m3(x * (448 / amax))
+ *   CGD_SCALE_POW2   scale = 2^k, the smallest power of two >= amax / 448,
+ *                    code = e4m3(x * 2^-k)                      (round_scale)
+ *   CGD_SCALE_UE8M0  as CGD_SCALE_POW2, the scale stored as the byte k + 127
+ * with fp32 arithmetic throughout, correctly rounded division, the product
+ * clamped to [-448, 448] and rounded to the nearest e4m3fn value (ties to
+ * even). The cast back is bf16(code value * scale), the product in fp32.
+ * Scale element (t, b) of an input lives at scales[t * scale_stride_token +
+ * b * scale_stride_block] (row-major: H/128 and 1; column-major: 1 and T);
+ * scales are fp32 (4 bytes) except UE8M0 (1 byte). Received scales are
+ * row-major [recv_capacity, H/128]. All FP8 row pointers must be 16-byte
+ * aligned; strides must be >= 0 and the caller guarantees every addressed
+ * scale lies inside its buffer.
+ * ------------------------------------------------------------------------- */
+
+typedef enum { CGD_SCALE_F32 = 0, CGD_SCALE_POW2 = 1, CGD_SCALE_UE8M0 = 2 } cgd_scale_format;
+
+/* per_token_cast_to_fp8: x bf16 [T, H] -> x_fp8 uint8 [T, H], x_scales. */
+int cgd_cast_to_fp8(const void* x, int64_t num_tokens, int hidden, void* x_fp8, void* x_scales,
+                    int64_t scale_stride_token, int64_t scale_stride_block, int scale_format, hipStream_t stream);
+
+/* per_token_cast_back: (x_fp8, x_scales) -> out bf16 [T, H]. */
+int cgd_cast_back(const void* x_fp8, const void* x_scales, int64_t scale_stride_token, int64_t scale_stride_block,
+                  int scale_format, int64_t num_tokens, int hidden, void* out, hipStream_t stream);
+
+/* Dispatch apply with the FP8 tuple as x: as cgd_dispatch_apply (after
+ * cgd_dispatch_plan), moving rows of H code bytes and the rows' scales:
+ * recv_x_fp8 [recv_capacity, H], recv_scales [recv_capacity, H/128]. */
+int cgd_dispatch_apply_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                           int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
+                           int num_experts, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
+                           const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
+                           const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dispatch apply that casts on the way (the low-latency dispatch with FP8):
+ * x is bf16 [T, H]; each chunk is cast once, exactly as cgd_cast_to_fp8
+ * would, and its codes and scales are written to every destination row. */
+int cgd_dispatch_apply_cast_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
+                                int scale_format, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
+                                const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
+                                const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Cached dispatch of the FP8 tuple with a dst_row from an earlier dispatch. */
+int cgd_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                            int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
+                            const int32_t* dst_row, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                            hipStream_t stream);
+
+/* Normal-mode dispatch apply with the FP8 tuple as x (after
+ * cgd_normal_dispatch_plan), and its cached form. */
+int cgd_normal_dispatch_apply_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                                  int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden,
+                                  const int64_t* topk_idx, const float* topk_weights, int num_topk, int num_experts,
+                                  int num_ranks, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                  const int32_t* rank_offset, int32_t* recv_src_idx, int32_t* send_row,
+                                  int64_t* recv_topk_idx, float* recv_topk_weights, const void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+int cgd_normal_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
+                                   int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden,
+                                   int num_ranks, const int32_t* send_row, void* recv_x_fp8, void* recv_scales,
+                                   int64_t recv_capacity, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

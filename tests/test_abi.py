@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "cgd.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cgd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(cgd_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -26,7 +26,9 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_capacity", "cgd_get_dispatch_layout", "cgd_dispatch", "cgd_dispatch_plan",
         "cgd_dispatch_apply", "cgd_dispatch_cached", "cgd_combine", "cgd_normal_workspace_bytes",
         "cgd_normal_capacity", "cgd_normal_dispatch", "cgd_normal_dispatch_cached", "cgd_normal_combine",
-        "cgd_normal_dispatch_plan", "cgd_normal_dispatch_apply",
+        "cgd_normal_dispatch_plan", "cgd_normal_dispatch_apply", "cgd_cast_to_fp8", "cgd_cast_back",
+        "cgd_dispatch_apply_fp8", "cgd_dispatch_apply_cast_fp8", "cgd_dispatch_cached_fp8",
+        "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8",
     ])
 
 
@@ -231,6 +233,32 @@ def test_normal_cached_and_combine_reject_bad_arguments():
     assert lib.cgd_normal_combine(f, 16, 128, f, 8, 2, None, 2, _vp(FAKE + 8), None, f, None, None) == -1
     assert lib.cgd_normal_combine(f, -1, 128, f, 8, 2, None, 2, None, None, f, None, None) == -2
     assert lib.cgd_normal_combine(f, 16, 128, None, 8, 2, None, 2, None, None, f, None, None) == -1
+
+
+def test_fp8_entry_points_reject_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    # x, T, H, q, s, st, sb, fmt
+    assert lib.cgd_cast_to_fp8(f, 4, 100, f, f, 1, 1, 0, None) == -1      # H % 128
+    assert lib.cgd_cast_to_fp8(f, 4, 256, f, f, 1, 1, 3, None) == -1      # format
+    assert lib.cgd_cast_to_fp8(f, 4, 256, f, f, -1, 1, 0, None) == -1     # negative stride
+    assert lib.cgd_cast_to_fp8(f, 4, 256, f, _vp(FAKE + 2), 2, 1, 0, None) == -1  # fp32 scales misaligned
+    assert lib.cgd_cast_to_fp8(f, 4, 256, f, None, 2, 1, 0, None) == -1
+    assert lib.cgd_cast_to_fp8(f, 0, 256, None, None, 2, 1, 0, None) == 0  # no tokens: nothing enqueued
+    assert lib.cgd_cast_back(f, f, 2, 1, 0, 4, 64, f, None) == -1
+    assert lib.cgd_cast_back(f, f, 2, 1, 2, 0, 256, None, None) == 0
+    # xq, xs, st, sb, fmt, T, H, K, E, cap, rq, rs, off, src, dst, ws, wsb
+    assert lib.cgd_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 200, 4, 16, 256, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, 4, 16, 256, f, None, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, 4, 16, 256, f, f, f, f, f, None, 0, None) == -3
+    # x, T, H, K, E, fmt, cap, rq, rs, off, src, dst, ws, wsb
+    assert lib.cgd_dispatch_apply_cast_fp8(f, 64, 256, 4, 16, 5, 256, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_apply_cast_fp8(f, 64, 256, 4, 16, 2, 256, f, None, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_cached_fp8(f, f, 2, 1, 0, 8, 120, 2, f, f, f, 16, None) == -1
+    assert lib.cgd_normal_dispatch_cached_fp8(f, f, 2, 1, 0, 8, 256, 0, f, f, f, 16, None) == -1
+    assert lib.cgd_normal_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, f, f, 4, 16, 4, f, f, 255, f, f, f, f, f, f,
+                                             1 << 20, None) == -2
+    assert lib.cgd_last_error()
 
 
 def test_product_path_does_not_touch_the_oracle():

@@ -1,0 +1,197 @@
+"""Parity of the FP8 payload HIP path with the CPU oracle.
+
+The per-token cast (codes and scales, every scale format, row- and
+column-major scales) and the cast back must be bit-exact: both sides decide
+each code in fp32 with the same operations. FP8 dispatch (pre-cast tuple,
+cast on the way, cached, rank-granular) must put exactly the oracle's codes
+and scales in exactly the oracle's rows."""
+import numpy as np
+import pytest
+import torch
+
+import combine_get_dispatch_06_amd as cgd
+import oracle
+import synth
+from gpu_util import DEV, bf16_to_f64, dev_bf16, dev_f32, dev_i64, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [cgd.SCALE_F32, cgd.SCALE_POW2, cgd.SCALE_UE8M0]
+
+
+def _x(T, H, seed, spread=True):
+    """N(0,1) bf16 rows, each 128-block scaled by 10^U(-3,3), with an all-zero
+    block, a subnormal and a huge value planted."""
+    w = synth.Workload("fp8", T=T, H=H, K=1, E=1, R=1)
+    x = synth.make_x(w, seed=seed).astype(np.uint16)
+    f = (x.astype(np.uint32) << 16).view(np.float32).reshape(T, H // 128, 128)
+    if spread:
+        rng = np.random.default_rng(seed)
+        f = f * (10.0 ** rng.uniform(-3, 3, (T, H // 128, 1))).astype(np.float32)
+    f = f.reshape(T, H).copy()
+    if T > 2:
+        f[0, :128] = 0.0
+        f[1, 3] = 1e-40
+        f[2, min(130, H - 1)] = -3e38
+    return torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _scales_np(sc: torch.Tensor) -> np.ndarray:
+    return sc.cpu().contiguous().numpy()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,H,colmajor", [(1, 128, False), (37, 256, True), (300, 7168, False),
+                                          (128, 7168, True), (513, 4096, False)])
+def test_cast_parity(fmt, T, H, colmajor):
+    x = _x(T, H, seed=T + H)
+    q, sc = cgd.per_token_cast_to_fp8(dev_bf16(x), fmt, column_major_scales=colmajor)
+    torch.cuda.synchronize()
+    if colmajor:
+        assert sc.stride() == (1, T)
+    oq, osc = oracle.cast_to_fp8(x, fmt)
+    np.testing.assert_array_equal(q.view(torch.uint8).cpu().numpy(), oq)
+    np.testing.assert_array_equal(_scales_np(sc).view(np.uint8), osc.view(np.uint8))
+    back = cgd.per_token_cast_back((q, sc), fmt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_bits(back), oracle.cast_back(oq, osc, fmt))
+
+
+def test_cast_back_all_codes():
+    """Every finite code in every position, with fp32 and UE8M0 scales."""
+    T, H = 8, 1024
+    rng = np.random.default_rng(0)
+    codes = np.tile(np.arange(256, dtype=np.uint8), T * H // 256).reshape(T, H)
+    codes[(codes & 0x7F) == 0x7F] = 0x12  # no NaN codes
+    rng.shuffle(codes, axis=1)
+    sf = (10.0 ** rng.uniform(-6, 6, (T, H // 128))).astype(np.float32)
+    su = rng.integers(100, 150, (T, H // 128)).astype(np.uint8)
+    q = torch.from_numpy(codes).to(DEV).view(torch.float8_e4m3fn)
+    for fmt, s in ((cgd.SCALE_F32, sf), (cgd.SCALE_UE8M0, su)):
+        back = cgd.per_token_cast_back((q, torch.from_numpy(s).to(DEV)), fmt)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(back), oracle.cast_back(codes, s, fmt))
+
+
+def _check_rows(recv, q_np, s_np, dst_np):
+    """Received code rows and scale rows equal the source token's, for every
+    destination row of dst_np ([T, K] or [T, R], -1 = none)."""
+    rq, rs = recv
+    sel_t, sel_k = np.nonzero(dst_np >= 0)
+    rows = dst_np[sel_t, sel_k]
+    got_q = rq.view(torch.uint8).cpu().numpy()[rows]
+    np.testing.assert_array_equal(got_q, q_np[sel_t])
+    np.testing.assert_array_equal(rs.cpu().numpy()[rows].view(np.uint8), s_np[sel_t].view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt,colmajor", [(cgd.SCALE_F32, False), (cgd.SCALE_F32, True), (cgd.SCALE_UE8M0, False),
+                                          (cgd.SCALE_UE8M0, True)])
+def test_fp8_tuple_dispatch_and_cached(fmt, colmajor):
+    w = synth.WORKLOADS["prefill"].replace(T=700, H=1024)
+    idx = synth.make_topk_idx(w.replace(name="prefill"), seed=2)
+    x = _x(w.T, w.H, seed=2)
+    q, sc = cgd.per_token_cast_to_fp8(dev_bf16(x), fmt, column_major_scales=colmajor)
+    recv, h = cgd.dispatch((q, sc), dev_i64(idx), w.E, w.R, expert_alignment=4)
+    torch.cuda.synchronize()
+    o = oracle.dispatch(None, idx, w.E, w.R, align=4, with_rows=False)
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    oq, osc = oracle.cast_to_fp8(x, fmt)
+    _check_rows(recv, oq, osc, o["dst_row"])
+    # cached: a second batch through the same handle
+    x2 = _x(w.T, w.H, seed=3)
+    q2, sc2 = cgd.per_token_cast_to_fp8(dev_bf16(x2), fmt, column_major_scales=colmajor)
+    recv2, _ = cgd.dispatch((q2, sc2), handle=h)
+    torch.cuda.synchronize()
+    oq2, osc2 = oracle.cast_to_fp8(x2, fmt)
+    _check_rows(recv2, oq2, osc2, o["dst_row"])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,K,E,R,H,p_neg", [(1, 8, 256, 8, 7168, 0.0), (700, 8, 256, 8, 1024, 0.0),
+                                             (333, 4, 64, 16, 384, 0.2), (2000, 16, 512, 64, 256, 0.05),
+                                             (64, 1, 8, 2, 128, 0.0)])
+def test_cast_on_dispatch_parity(fmt, T, K, E, R, H, p_neg):
+    rng = np.random.default_rng(T + K)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    idx[rng.random((T, K)) < p_neg] = -1
+    x = _x(T, H, seed=T)
+    recv, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, cast_fp8=fmt)
+    torch.cuda.synchronize()
+    o = oracle.dispatch(None, idx, E, R, with_rows=False)
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    oq, osc = oracle.cast_to_fp8(x, fmt)
+    _check_rows(recv, oq, osc, o["dst_row"])
+
+
+def test_cast_on_dispatch_prefill_round_trip():
+    """Prefill sizes, cast on dispatch; every received row checked on the
+    device against the oracle's codes for a sample of tokens, and the combine
+    of the cast-back rows (identity experts) within the FP8 error bound of x."""
+    w = synth.WORKLOADS["prefill"]
+    inp = synth.make_inputs(w, seed=0)
+    x_dev = dev_bf16(inp["x"])
+    recv, h = cgd.dispatch(x_dev, dev_i64(inp["topk_idx"]), w.E, w.R, cast_fp8=cgd.SCALE_F32)
+    torch.cuda.synchronize()
+    o = oracle.dispatch(None, inp["topk_idx"], w.E, w.R, with_rows=False)
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    tok = np.unique(np.random.default_rng(1).integers(0, w.T, 256))
+    oq, osc = oracle.cast_to_fp8(inp["x"][tok], cgd.SCALE_F32)
+    rows = o["dst_row"][tok]
+    rq = recv[0].view(torch.uint8)
+    for k in range(w.K):
+        r = torch.from_numpy(rows[:, k].astype(np.int64)).to(DEV)
+        np.testing.assert_array_equal(rq.index_select(0, r).cpu().numpy(), oq)
+        np.testing.assert_array_equal(recv[1].index_select(0, r).cpu().numpy(), osc)
+    back = cgd.per_token_cast_back(recv)
+    out = cgd.combine(back, h, dev_f32(inp["topk_weights"]))
+    torch.cuda.synchronize()
+    xf = bf16_to_f64(inp["x"])
+    err = np.abs(bf16_to_f64(host_bits(out)) - xf)
+    _, s_all = oracle.cast_to_fp8(inp["x"], cgd.SCALE_F32)
+    # half an e4m3 spacing (normal and subnormal range) plus two bf16 roundings
+    bound = 2.0 ** -4 * np.abs(xf) * 1.01 + 2.0 ** -10 * np.repeat(s_all.astype(np.float64), 128, axis=1) \
+        + 2.0 ** -6 * np.abs(xf) + 1e-30
+    assert (err <= bound).all(), f"worst excess {np.max(err - bound)}"
+    rel = np.sqrt((err ** 2).sum() / (xf ** 2).sum())
+    say(f"[fp8] prefill cast-on-dispatch round trip relative L2 error {rel:.2e}")
+    assert rel < 0.05
+
+
+@pytest.mark.parametrize("fmt", [cgd.SCALE_F32, cgd.SCALE_UE8M0])
+def test_fp8_normal_dispatch_and_cached(fmt):
+    w = synth.WORKLOADS["prefill"].replace(T=900, H=512)
+    idx = synth.make_topk_idx(w.replace(name="prefill"), seed=4)
+    wts = synth.make_weights(w.replace(name="prefill"), seed=4)
+    x = _x(w.T, w.H, seed=4)
+    _, _, ntpe, itr, _ = cgd.get_dispatch_layout(dev_i64(idx), w.E, w.R)
+    q, sc = cgd.per_token_cast_to_fp8(dev_bf16(x), fmt, column_major_scales=True)
+    recv, ridx, rw, nre, h = cgd.normal_dispatch((q, sc), itr, ntpe, dev_i64(idx), dev_f32(wts), num_experts=w.E)
+    torch.cuda.synchronize()
+    o = oracle.dispatch_normal(None, itr.cpu().numpy(), w.E, w.K, ntpe.cpu().numpy(), idx, wts)
+    np.testing.assert_array_equal(h.send_row.cpu().numpy(), o["send_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    np.testing.assert_array_equal(ridx.cpu().numpy(), o["recv_topk_idx"])
+    oq, osc = oracle.cast_to_fp8(x, fmt)
+    _check_rows(recv, oq, osc, o["send_row"])
+    x2 = _x(w.T, w.H, seed=5)
+    q2, sc2 = cgd.per_token_cast_to_fp8(dev_bf16(x2), fmt)
+    recv2, _, _, _, _ = cgd.normal_dispatch((q2, sc2), handle=h)
+    torch.cuda.synchronize()
+    oq2, osc2 = oracle.cast_to_fp8(x2, fmt)
+    _check_rows(recv2, oq2, osc2, o["send_row"])
+
+
+def test_fp8_zero_tokens():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    q, sc = cgd.per_token_cast_to_fp8(x)
+    idx = torch.empty((0, 4), dtype=torch.int64, device=DEV)
+    recv, h = cgd.dispatch(x, idx, 16, 4, expert_alignment=2, cast_fp8=cgd.SCALE_F32)
+    recv2, _ = cgd.dispatch((q, sc), idx, 16, 4, expert_alignment=2)
+    torch.cuda.synchronize()
+    assert q.shape == (0, 256) and sc.shape == (0, 2)
+    assert recv[0].shape == (16, 256) and recv[1].shape == (16, 2)
+    assert (h.recv_src_idx.cpu().numpy() == -1).all()
+    assert recv2[0].shape == (16, 256)
