@@ -75,6 +75,15 @@ __device__ __forceinline__ float group16_max(float v) {
     return v;
 }
 
+// Max over the 8 lanes of an aligned lane group (one 128-channel block when
+// each lane holds 16 channels).
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 4, kWave));
+    v = fmaxf(v, __shfl_xor(v, 2, kWave));
+    v = fmaxf(v, __shfl_xor(v, 1, kWave));
+    return v;
+}
+
 __device__ __forceinline__ float clamp_e4m3(float v) {
     v = v > kE4m3Max ? kE4m3Max : v;  // NaN passes through unchanged
     return v < -kE4m3Max ? -kE4m3Max : v;
@@ -102,6 +111,12 @@ __device__ __forceinline__ uint2 quantize_bf16x8(const uint4& q, float mul) {
     r.x = pack_e4m3x4(bf16_lo(q.x) * mul, bf16_hi(q.x) * mul, bf16_lo(q.y) * mul, bf16_hi(q.y) * mul);
     r.y = pack_e4m3x4(bf16_lo(q.z) * mul, bf16_hi(q.z) * mul, bf16_lo(q.w) * mul, bf16_hi(q.w) * mul);
     return r;
+}
+
+// 16 bf16 values (two 16-byte vectors) times mul -> 16 e4m3fn bytes.
+__device__ __forceinline__ uint4 quantize_bf16x16(const uint4& a, const uint4& b, float mul) {
+    const uint2 lo = quantize_bf16x8(a, mul), hi = quantize_bf16x8(b, mul);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 // Streaming 16-byte global accesses: data touched once should not displace

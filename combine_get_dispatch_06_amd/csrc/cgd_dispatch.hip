@@ -303,30 +303,40 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
 }
 
 // Fused FP8 cast and dispatch apply (bf16 x in, e4m3fn rows and per-block
-// scales out). One wave per (token, chunk of U*512 channels): each lane holds
-// 8 channels per 512, so a 16-lane group holds one 128-channel block, whose
-// absolute max comes from a 16-lane reduction. The chunk is quantized once and
-// its 8-byte code vectors and block scales are stored to every destination
-// row. Rows are H bytes; scales are [cap, H/128] (4 bytes, or 1 byte UE8M0).
+// scales out). One wave per (token, chunk of U*64 lanes): each lane holds
+// CPL = 16 channels (two 16-byte bf16 vectors in, one 16-byte code vector
+// out), so an 8-lane group holds one 128-channel block, whose absolute max
+// comes from an 8-lane reduction (CPL = 8: 8-byte code vectors, 16-lane
+// groups). The chunk is quantized once and its code vectors and block scales
+// are stored to every destination row with non-temporal stores. Rows are H
+// bytes; scales are [cap, H/128] (4 bytes, or 1 byte UE8M0).
+#ifndef CGD_CAST_CPL
+#define CGD_CAST_CPL 16
+#endif
+constexpr int kCastCpl = CGD_CAST_CPL;  // channels per lane
 template <int KM, int U, int FMT>
 __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
-    const uint4* __restrict__ x, int64_t T, int nvec, int nchunk, int K, const int32_t* __restrict__ slot,
+    const uint4* __restrict__ x, int64_t T, int nlv, int nchunk, int K, const int32_t* __restrict__ slot,
     int32_t* __restrict__ dst_row, const int32_t* __restrict__ tile_base, int E, int32_t* __restrict__ recv_src_idx,
-    const int32_t* __restrict__ expert_offset, int64_t cap, uint2* __restrict__ recv_q, void* __restrict__ recv_s) {
+    const int32_t* __restrict__ expert_offset, int64_t cap, void* __restrict__ recv_q, void* __restrict__ recv_s) {
+    constexpr int kVin = kCastCpl / 8;             // 16-byte bf16 vectors per lane
+    constexpr int kGroup = kFp8Block / kCastCpl;   // lanes per 128-channel block
     const int lane = lane_id();
     fill_tail(recv_src_idx, expert_offset, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t t = g / nchunk;
     if (t >= T) return;
     const int c = (int)(g - t * nchunk);
-    const int v0 = c * U * kWave;  // first 8-channel vector of the chunk
-    const int nsb = nvec / (kFp8Block / 8);
-    const uint4* xr = x + t * nvec;
-    uint4 buf[U];
+    const int v0 = c * U * kWave;  // first lane vector of the chunk (nlv per row)
+    const int nsb = nlv / kGroup;
+    const uint4* xr = x + t * (int64_t)nlv * kVin;
+    uint4 buf[U][kVin];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int v = v0 + u * kWave + lane;
-        if (v < nvec) buf[u] = load_nt(xr + v);
+#pragma unroll
+        for (int i = 0; i < kVin; ++i)
+            if (v < nlv) buf[u][i] = load_nt(xr + (int64_t)v * kVin + i);
     }
     int d = -1;
     if (lane < K) {
@@ -336,15 +346,24 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
             if (d >= 0) recv_src_idx[d] = (int32_t)t;
         }
     }
-    // quantize: a block never straddles lanes of two groups (nvec % 16 == 0)
-    uint2 code[U];
+    // quantize: a block never straddles two lane groups (nlv % kGroup == 0)
     Fp8Scale sc[U];
+    uint4 code16[U];
+    uint2 code8[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int v = v0 + u * kWave + lane;
-        const float m = group16_max(v < nvec ? absmax_bf16x8(buf[u]) : 0.0f);
+        float m = 0.0f;
+        if (v < nlv) {
+#pragma unroll
+            for (int i = 0; i < kVin; ++i) m = fmaxf(m, absmax_bf16x8(buf[u][i]));
+        }
+        m = (kGroup == 8) ? group8_max(m) : group16_max(m);
         sc[u] = fp8_block_scale(m, FMT);
-        code[u] = quantize_bf16x8(buf[u], sc[u].mul);
+        if (kCastCpl == 16)
+            code16[u] = quantize_bf16x16(buf[u][0], buf[u][kVin - 1], sc[u].mul);
+        else
+            code8[u] = quantize_bf16x8(buf[u][0], sc[u].mul);
     }
     int dk[KM];
 #pragma unroll
@@ -352,14 +371,16 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
         if (dk[k] < 0) continue;
-        uint2* dr = recv_q + (int64_t)dk[k] * nvec;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * kWave + lane;
-            if (v >= nvec) continue;
-            store_nt(dr + v, code[u]);
-            if ((lane & 15) == 0) {
-                const int64_t si = (int64_t)dk[k] * nsb + v / (kFp8Block / 8);
+            if (v >= nlv) continue;
+            if (kCastCpl == 16)
+                store_nt(static_cast<uint4*>(recv_q) + (int64_t)dk[k] * nlv + v, code16[u]);
+            else
+                store_nt(static_cast<uint2*>(recv_q) + (int64_t)dk[k] * nlv + v, code8[u]);
+            if ((lane & (kGroup - 1)) == 0) {
+                const int64_t si = (int64_t)dk[k] * nsb + v / kGroup;
                 if (FMT == 2)
                     static_cast<uint8_t*>(recv_s)[si] = (uint8_t)sc[u].ue8m0;
                 else
@@ -468,16 +489,15 @@ template <int U, int FMT>
 static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E, const int32_t* slot,
                                   int32_t* dst_row, const int32_t* tile_base, int32_t* src, const int32_t* off,
                                   int64_t cap, void* recv_q, void* recv_s, hipStream_t s) {
-    const int nvec = H / 8;
-    const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
+    const int nlv = H / kCastCpl;
+    const int nchunk = (nlv + U * kWave - 1) / (U * kWave);
     const int64_t waves = T * nchunk;
     const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
     const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-    uint2* qv = reinterpret_cast<uint2*>(recv_q);
 #define CGD_SCATTER_CAST(KM)                                                                                         \
-    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot, dst_row,   \
-                       tile_base, E, src, off, cap, qv, recv_s)
+    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, T, nlv, nchunk, K, slot, dst_row,    \
+                       tile_base, E, src, off, cap, recv_q, recv_s)
     if (K <= 2)
         CGD_SCATTER_CAST(2);
     else if (K <= 4)
@@ -498,7 +518,7 @@ static void launch_scatter_cast(const void* x, int64_t T, int H, int K, int E, c
                                 const int32_t* tile_base, int32_t* src, const int32_t* off, int64_t cap, void* recv_q,
                                 void* recv_s, hipStream_t s) {
     constexpr int U = CGD_SCATTER_CAST_U;
-    const int64_t waves = T * ((H / 8 + U * kWave - 1) / (U * kWave));
+    const int64_t waves = T * ((H / kCastCpl + U * kWave - 1) / (U * kWave));
     if (waves >= kMinScatterWaves)
         launch_scatter_cast_u<U, FMT>(x, T, H, K, E, slot, dst_row, tile_base, src, off, cap, recv_q, recv_s, s);
     else

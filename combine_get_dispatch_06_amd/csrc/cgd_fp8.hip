@@ -12,21 +12,24 @@
 //   format 2: as format 1, the scale stored as the byte k + 127 (UE8M0).
 // The cast back is bf16(e4m3 value * scale) with the product in fp32.
 //
-// One wave per (token, chunk of 512 channels): each lane holds 8 channels
-// (one 16-byte bf16 vector, one 8-byte code vector), a 16-lane group holds one
-// 128-channel block and reduces its absolute max with lane shuffles. Scales are
-// addressed with element strides (st per token, sb per block), so row-major
-// ([T, H/128]: st = H/128, sb = 1) and column-major (st = 1, sb = T) both work.
+// One wave per (token, chunk of 1024 channels): each lane holds 16 channels
+// (two 16-byte bf16 vectors, one 16-byte code vector), an 8-lane group holds
+// one 128-channel block and reduces its absolute max with lane shuffles.
+// Scales are addressed with element strides (st per token, sb per block), so
+// row-major ([T, H/128]: st = H/128, sb = 1) and column-major (st = 1, sb = T)
+// both work.
 #include "cgd_device.h"
 #include "cgd_launch.h"
 
 namespace cgd {
 
 constexpr int kCastWaves = 4;
+constexpr int kLaneCh = 16;                      // channels per lane
+constexpr int kLaneGroup = kFp8Block / kLaneCh;  // lanes per 128-channel block
 
 template <int FMT>
 __global__ __launch_bounds__(kCastWaves* kWave) void cast_to_fp8_kernel(const uint4* __restrict__ x, int64_t T,
-                                                                        int nvec, int nchunk, uint2* __restrict__ q,
+                                                                        int nlv, int nchunk, uint4* __restrict__ q,
                                                                         void* __restrict__ scales, int64_t st,
                                                                         int64_t sb) {
     const int lane = lane_id();
@@ -34,14 +37,19 @@ __global__ __launch_bounds__(kCastWaves* kWave) void cast_to_fp8_kernel(const ui
     const int64_t t = g / nchunk;
     if (t >= T) return;
     const int v = (int)(g - t * nchunk) * kWave + lane;
-    const bool in = v < nvec;  // whole 16-lane groups are in or out (nvec % 16 == 0)
-    uint4 xv = make_uint4(0, 0, 0, 0);
-    if (in) xv = load_nt(x + t * nvec + v);
-    const Fp8Scale sc = fp8_block_scale(group16_max(in ? absmax_bf16x8(xv) : 0.0f), FMT);
+    const bool in = v < nlv;  // whole lane groups are in or out (nlv % 8 == 0)
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (in) {
+        const uint4* xr = x + (t * nlv + v) * 2;
+        a = load_nt(xr);
+        b = load_nt(xr + 1);
+    }
+    const float m = in ? fmaxf(absmax_bf16x8(a), absmax_bf16x8(b)) : 0.0f;
+    const Fp8Scale sc = fp8_block_scale(group8_max(m), FMT);
     if (!in) return;
-    q[t * nvec + v] = quantize_bf16x8(xv, sc.mul);
-    if ((lane & 15) == 0) {
-        const int64_t i = t * st + (int64_t)(v / (kFp8Block / 8)) * sb;
+    q[t * nlv + v] = quantize_bf16x16(a, b, sc.mul);
+    if ((lane & (kLaneGroup - 1)) == 0) {
+        const int64_t i = t * st + (int64_t)(v / kLaneGroup) * sb;
         if (FMT == 2)
             static_cast<uint8_t*>(scales)[i] = (uint8_t)sc.ue8m0;
         else
@@ -49,56 +57,62 @@ __global__ __launch_bounds__(kCastWaves* kWave) void cast_to_fp8_kernel(const ui
     }
 }
 
+__device__ __forceinline__ uint4 dequantize_x8(uint32_t lo, uint32_t hi, float s) {
+    const int a = (int)lo, b = (int)hi;
+    uint4 r;
+    r.x = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(a, 0) * s, __builtin_amdgcn_cvt_f32_fp8(a, 1) * s);
+    r.y = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(a, 2) * s, __builtin_amdgcn_cvt_f32_fp8(a, 3) * s);
+    r.z = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(b, 0) * s, __builtin_amdgcn_cvt_f32_fp8(b, 1) * s);
+    r.w = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(b, 2) * s, __builtin_amdgcn_cvt_f32_fp8(b, 3) * s);
+    return r;
+}
+
 template <int FMT>
-__global__ __launch_bounds__(kCastWaves* kWave) void cast_back_kernel(const uint2* __restrict__ q,
+__global__ __launch_bounds__(kCastWaves* kWave) void cast_back_kernel(const uint4* __restrict__ q,
                                                                       const void* __restrict__ scales, int64_t st,
-                                                                      int64_t sb, int64_t T, int nvec, int nchunk,
+                                                                      int64_t sb, int64_t T, int nlv, int nchunk,
                                                                       uint4* __restrict__ out) {
     const int lane = lane_id();
     const int64_t g = (int64_t)blockIdx.x * kCastWaves + threadIdx.x / kWave;
     const int64_t t = g / nchunk;
     if (t >= T) return;
     const int v = (int)(g - t * nchunk) * kWave + lane;
-    if (v >= nvec) return;
-    const uint2 w = load_nt(q + t * nvec + v);
-    const int64_t i = t * st + (int64_t)(v / (kFp8Block / 8)) * sb;
+    if (v >= nlv) return;
+    const uint4 w = load_nt(q + t * nlv + v);
+    const int64_t i = t * st + (int64_t)(v / kLaneGroup) * sb;
     const float s = (FMT == 2) ? ldexpf(1.0f, (int)static_cast<const uint8_t*>(scales)[i] - 127)
                                : static_cast<const float*>(scales)[i];
-    const int a = (int)w.x, b = (int)w.y;
-    uint4 r;
-    r.x = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(a, 0) * s, __builtin_amdgcn_cvt_f32_fp8(a, 1) * s);
-    r.y = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(a, 2) * s, __builtin_amdgcn_cvt_f32_fp8(a, 3) * s);
-    r.z = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(b, 0) * s, __builtin_amdgcn_cvt_f32_fp8(b, 1) * s);
-    r.w = pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(b, 2) * s, __builtin_amdgcn_cvt_f32_fp8(b, 3) * s);
-    out[t * nvec + v] = r;
+    uint4* o = out + (t * nlv + v) * 2;
+    o[0] = dequantize_x8(w.x, w.y, s);
+    o[1] = dequantize_x8(w.z, w.w, s);
 }
 
 hipError_t launch_cast_to_fp8(const void* x, int64_t T, int H, void* q, void* scales, int64_t st, int64_t sb, int fmt,
                               hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    const int nvec = H / 8;
-    const int nchunk = (nvec + kWave - 1) / kWave;
+    const int nlv = H / kLaneCh;
+    const int nchunk = (nlv + kWave - 1) / kWave;
     const int64_t blocks = (T * nchunk + kCastWaves - 1) / kCastWaves;
     const dim3 grid((unsigned)blocks), block(kCastWaves * kWave);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
-    uint2* qv = reinterpret_cast<uint2*>(q);
+    uint4* qv = reinterpret_cast<uint4*>(q);
     if (fmt == 0)
-        hipLaunchKernelGGL(cast_to_fp8_kernel<0>, grid, block, 0, stream, xv, T, nvec, nchunk, qv, scales, st, sb);
+        hipLaunchKernelGGL(cast_to_fp8_kernel<0>, grid, block, 0, stream, xv, T, nlv, nchunk, qv, scales, st, sb);
     else if (fmt == 1)
-        hipLaunchKernelGGL(cast_to_fp8_kernel<1>, grid, block, 0, stream, xv, T, nvec, nchunk, qv, scales, st, sb);
+        hipLaunchKernelGGL(cast_to_fp8_kernel<1>, grid, block, 0, stream, xv, T, nlv, nchunk, qv, scales, st, sb);
     else
-        hipLaunchKernelGGL(cast_to_fp8_kernel<2>, grid, block, 0, stream, xv, T, nvec, nchunk, qv, scales, st, sb);
+        hipLaunchKernelGGL(cast_to_fp8_kernel<2>, grid, block, 0, stream, xv, T, nlv, nchunk, qv, scales, st, sb);
     return hipGetLastError();
 }
 
 hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64_t sb, int fmt, int64_t T, int H,
                             void* out, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    const int nvec = H / 8;
+    const int nvec = H / kLaneCh;
     const int nchunk = (nvec + kWave - 1) / kWave;
     const int64_t blocks = (T * nchunk + kCastWaves - 1) / kCastWaves;
     const dim3 grid((unsigned)blocks), block(kCastWaves * kWave);
-    const uint2* qv = reinterpret_cast<const uint2*>(q);
+    const uint4* qv = reinterpret_cast<const uint4*>(q);
     uint4* ov = reinterpret_cast<uint4*>(out);
     if (fmt == 2)
         hipLaunchKernelGGL(cast_back_kernel<2>, grid, block, 0, stream, qv, scales, st, sb, T, nvec, nchunk, ov);
