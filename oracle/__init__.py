@@ -64,6 +64,8 @@ def _load():
         lib.oracle_cast_to_fp8.restype = i32
         lib.oracle_cast_back.argtypes = [vp, vp, i64, i64, i32, vp]
         lib.oracle_cast_back.restype = i32
+        lib.oracle_dispatch_packed.argtypes = [vp, i64, i64, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp]
+        lib.oracle_dispatch_packed.restype = i32
         _lib = lib
     return _lib
 
@@ -238,3 +240,24 @@ def cast_back(q: np.ndarray, scales: np.ndarray, scale_format: int = SCALE_F32) 
     if rc:
         raise OracleError(rc)
     return out
+
+
+def dispatch_packed(x: np.ndarray | None, topk_idx: np.ndarray, num_experts: int, num_ranks: int, cap: int,
+                    hidden: int = 0, stats: np.ndarray | None = None):
+    """Fixed-capacity packed layout. -> dict(packed_recv_count [E], recv_src_info [E, cap], dst_row [T, K],
+    packed_recv_x [E, cap, H] uint16 | None, cumulative_recv_stats (the updated copy of stats) | None)."""
+    idx = _c(topk_idx, np.int64)
+    T, K = idx.shape
+    xs = None if x is None else _c(x, np.uint16)
+    H = hidden if xs is None else xs.shape[1]
+    cnt = np.zeros(num_experts, np.int32)
+    info = np.zeros((num_experts, max(cap, 0)), np.int32)
+    dst = np.zeros((T, K), np.int32)
+    st = None if stats is None else _c(stats, np.int32).copy()
+    recv = None if xs is None else np.zeros((num_experts, max(cap, 0), H), np.uint16)
+    rc = _load().oracle_dispatch_packed(_p(xs), T, H, _p(idx), K, num_experts, num_ranks, cap, _p(cnt), _p(info),
+                                        _p(dst), _p(st), _p(recv))
+    if rc:
+        raise OracleError(rc)
+    return {"packed_recv_count": cnt, "recv_src_info": info, "dst_row": dst, "packed_recv_x": recv,
+            "cumulative_recv_stats": st}

@@ -450,3 +450,49 @@ int oracle_cast_back(const uint8_t* q, const void* scales, int64_t T, int64_t H,
         }
     return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Fixed-capacity packed layout (the low-latency dispatch's receive buffers).
+ *
+ * DeepEP legacy test analysis page, low-latency dispatch call and per-expert
+ * check: packed_recv_x holds one fixed-size buffer per local expert,
+ * packed_recv_count[i] is the number of valid rows of expert i and equals the
+ * number of selected slots naming that expert, and the handle carries
+ * recv_src_info per expert (here the source token of each valid row).
+ * DeepEP Python interface notes, "Dispatch API", num_worst_tokens: a receive
+ * size fixed in advance avoids a host synchronisation.
+ *
+ * Readings: every expert owns rows [e*cap, (e+1)*cap) of a [E*cap, H] buffer;
+ * its valid rows come first, in ascending (token, slot) order as in the
+ * expert-granular dispatch; a slot whose rank inside its expert is >= cap is
+ * dropped (dst_row -1, not counted); rows past an expert's count have
+ * recv_src_info -1 and unspecified contents. With a single source the
+ * layout range per (expert, source) is (0, count), so it is not produced.
+ * cumulative_recv_stats (optional) accumulates packed_recv_count, as the
+ * pages' cumulative_local_expert_recv_stats does.
+ * --------------------------------------------------------------------------- */
+int oracle_dispatch_packed(const uint16_t* x, int64_t T, int64_t H, const int64_t* topk_idx, int K, int E, int R,
+                           int64_t cap, int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
+                           int32_t* cumulative_recv_stats, uint16_t* packed_recv_x) {
+    int rc = check_routing(topk_idx, T, K, E, R);
+    if (rc) return rc;
+    if (cap < 0 || H < 0) return ORACLE_EINVAL;
+    for (int e = 0; e < E; ++e) packed_recv_count[e] = 0;
+    for (int64_t r = 0; r < (int64_t)E * cap; ++r) recv_src_info[r] = -1;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            dst_row[t * K + k] = -1;
+            if (e < 0 || packed_recv_count[e] >= cap) continue;
+            int64_t row = e * cap + packed_recv_count[e];
+            packed_recv_count[e] += 1;
+            dst_row[t * K + k] = (int32_t)row;
+            recv_src_info[row] = (int32_t)t;
+            if (packed_recv_x)
+                for (int64_t h = 0; h < H; ++h) packed_recv_x[row * H + h] = x[t * H + h];
+        }
+    }
+    if (cumulative_recv_stats)
+        for (int e = 0; e < E; ++e) cumulative_recv_stats[e] += packed_recv_count[e];
+    return ORACLE_OK;
+}
