@@ -27,7 +27,8 @@ import torch
 __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply", "combine", "DispatchHandle",
            "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
            "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine",
-           "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0"]
+           "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
+           "PackedHandle", "low_latency_dispatch", "low_latency_combine"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -76,7 +77,14 @@ def load():
     lib.cgd_dispatch.restype = i32
     lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_plan.restype = i32
-    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, sz, vp]
+    lib.cgd_packed_workspace_bytes.restype = sz
+    lib.cgd_packed_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.cgd_dispatch_packed.restype = i32
+    lib.cgd_dispatch_packed.argtypes = [vp, i64, i32, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_packed_cast_fp8.restype = i32
+    lib.cgd_dispatch_packed_cast_fp8.argtypes = [vp, i64, i32, vp, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp,
+                                                 vp, sz, vp]
     lib.cgd_dispatch_apply.restype = i32
     lib.cgd_dispatch_apply.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_cached.restype = i32
@@ -399,7 +407,7 @@ def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expe
         ws = _workspace(dev, "dispatch", nbytes)
         _check("cgd_dispatch_plan",
                lib.cgd_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap, _ptr(off),
-                                     _ptr(src), _ptr(ws), ws.numel(), _stream(dev)))
+                                     _ptr(ws), ws.numel(), _stream(dev)))
     h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
     return DispatchPlan(h, ws, T)
 
@@ -751,3 +759,92 @@ def normal_combine(expert_out: torch.Tensor, handle: NormalHandle, recv_topk_wei
                                       _ptr(recv_topk_weights), K, _ptr(b0), _ptr(b1), _ptr(out), _ptr(cw),
                                       _stream(dev)))
     return out, cw
+
+
+# ---------------------------------------------------------------------------
+# Fixed-capacity packed layout (the low-latency dispatch's receive buffers).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PackedHandle:
+    """recv_src_info int32 [E, cap]: source token of each valid packed row, -1 elsewhere.
+    dst_row int32 [T, K]: packed row (e * cap + i) of each slot, -1 if not selected or dropped."""
+    recv_src_info: torch.Tensor
+    dst_row: torch.Tensor
+    num_experts: int
+    expert_capacity: int
+
+
+def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                         expert_capacity: int | None = None, use_fp8: bool = False, scale_format: int = SCALE_F32,
+                         cumulative_local_expert_recv_stats: torch.Tensor | None = None, out=None):
+    """Dispatch into fixed per-expert buffers (no host synchronisation, graph-capturable).
+
+    expert_capacity defaults to num_tokens (enough unless a token repeats an
+    expert). Returns (packed_recv_x, packed_recv_count int32 [E], PackedHandle);
+    packed_recv_x is bf16 [E, cap, H], or with use_fp8 the tuple
+    (codes float8_e4m3fn [E, cap, H], scales [E, cap, H/128])."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    if topk_idx.shape[0] != T:
+        raise ValueError("topk_idx must be [num_tokens, num_topk]")
+    E = num_experts
+    cap = T if expert_capacity is None else int(expert_capacity)
+    dev = x.device
+    st = cumulative_local_expert_recv_stats
+    if st is not None:
+        _dev_tensor(st, "cumulative_local_expert_recv_stats", torch.int32, 1)
+        if st.shape[0] != E:
+            raise ValueError("cumulative_local_expert_recv_stats must be [num_experts]")
+    with torch.cuda.device(dev):
+        count = torch.empty(E, dtype=torch.int32, device=dev)
+        info = torch.empty((E, max(cap, 0)), dtype=torch.int32, device=dev)
+        dst = torch.empty((T, K), dtype=torch.int32, device=dev)
+        ws = _workspace(dev, "dispatch", lib.cgd_packed_workspace_bytes(T, K, E))
+        if use_fp8:
+            if out is None:
+                q, sc = _fp8_empty(E * cap, H, scale_format, dev)
+            else:
+                q, sc = out
+            _check("cgd_dispatch_packed_cast_fp8",
+                   lib.cgd_dispatch_packed_cast_fp8(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap, scale_format,
+                                                    _ptr(q), _ptr(sc), _ptr(count), _ptr(info), _ptr(dst), _ptr(st),
+                                                    _ptr(ws), ws.numel(), _stream(dev)))
+            recv = (q.view(E, cap, H), sc.view(E, cap, H // 128))
+        else:
+            recv = torch.empty((E, cap, H), dtype=torch.bfloat16, device=dev) if out is None else out
+            _dev_tensor(recv, "out", torch.bfloat16, 3)
+            if recv.shape != (E, cap, H):
+                raise ValueError("out must be [num_experts, expert_capacity, hidden]")
+            _check("cgd_dispatch_packed",
+                   lib.cgd_dispatch_packed(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap, _ptr(recv),
+                                           _ptr(count), _ptr(info), _ptr(dst), _ptr(st), _ptr(ws), ws.numel(),
+                                           _stream(dev)))
+    return recv, count, PackedHandle(info, dst, E, cap)
+
+
+def low_latency_combine(expert_out: torch.Tensor, topk_weights: torch.Tensor, handle: PackedHandle,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """combined[t] = bf16( sum_k w[t,k] * expert_out[packed row of (t, k)] ), fp32 accumulation;
+    expert_out is bf16 [E, cap, H] (the packed layout)."""
+    lib = load()
+    _dev_tensor(expert_out, "expert_out", torch.bfloat16, 3)
+    _dev_tensor(topk_weights, "topk_weights", torch.float32, 2)
+    E, cap, H = expert_out.shape
+    if (E, cap) != (handle.num_experts, handle.expert_capacity):
+        raise ValueError("expert_out must be [num_experts, expert_capacity, hidden] of the handle")
+    T, K = handle.dst_row.shape
+    if topk_weights.shape != (T, K):
+        raise ValueError("topk_weights must be [num_tokens, num_topk]")
+    dev = expert_out.device
+    with torch.cuda.device(dev):
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(out, "out", torch.bfloat16, 2)
+        _check("cgd_combine",
+               lib.cgd_combine(_ptr(expert_out), E * cap, H, _ptr(handle.dst_row), _ptr(topk_weights), T, K,
+                               _ptr(out), _stream(dev)))
+    return out

@@ -127,8 +127,7 @@ int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num
 
 // Checks shared by the dispatch entry points.
 static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
-                           const int32_t* expert_offset, const int32_t* recv_src_idx, const void* workspace,
-                           size_t workspace_bytes) {
+                           const int32_t* expert_offset, const void* workspace, size_t workspace_bytes) {
     int rc = check_routing_sizes(T, K, E, R);
     if (rc) return rc;
     if (A < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
@@ -139,9 +138,7 @@ static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int
                     (long long)cap);
     if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
     if (T > 0 && !topk_idx) return fail(CGD_ERR_INVALID_ARG, "null topk_idx");
-    if (cap > 0 && !recv_src_idx) return fail(CGD_ERR_INVALID_ARG, "null recv_src_idx");
-    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4))
-        return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
+    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
     const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
@@ -172,13 +169,13 @@ static int check_apply_args(const void* x, int64_t T, int H, int K, int E, int64
 }
 
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
-                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, workspace, workspace_bytes);
+                             expert_offset, workspace, workspace_bytes);
     if (rc) return rc;
     hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
-                                               expert_offset, recv_src_idx, workspace, stream);
+                                               expert_offset, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     return CGD_OK;
 }
@@ -200,13 +197,13 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
                  int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, workspace, workspace_bytes);
+                             expert_offset, workspace, workspace_bytes);
     if (rc) return rc;
     if ((rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x, expert_offset,
                                recv_src_idx, dst_row, workspace, workspace_bytes)))
         return rc;
     hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
-                                               expert_offset, recv_src_idx, workspace, stream);
+                                               expert_offset, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     err = cgd::launch_dispatch_apply(x, num_tokens, hidden, num_topk, num_experts, recv_x, recv_capacity,
                                      expert_offset, recv_src_idx, dst_row, workspace, stream);
@@ -558,6 +555,68 @@ int cgd_normal_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int6
                                                             scale_format, num_tokens, hidden, num_ranks, send_row,
                                                             recv_x_fp8, recv_scales, recv_capacity, stream);
     if (err != hipSuccess) return hip_fail(err, "cached FP8 normal dispatch launch");
+    return CGD_OK;
+}
+
+size_t cgd_packed_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
+    return cgd_dispatch_workspace_bytes(num_tokens, num_topk, num_experts);
+}
+
+static int check_packed_args(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int R,
+                             int64_t cap, const void* recv_x, const int32_t* count, const int32_t* info,
+                             const int32_t* dst_row, const int32_t* stats, const void* workspace,
+                             size_t workspace_bytes) {
+    int rc = check_routing_sizes(T, K, E, R);
+    if (rc) return rc;
+    if ((rc = check_hidden(H))) return rc;
+    if (cap < 0 || (int64_t)E * cap > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "expert_capacity must be >= 0 with num_experts * expert_capacity <= INT32_MAX");
+    if (!count) return fail(CGD_ERR_INVALID_ARG, "null packed_recv_count");
+    if (T > 0 && (!x || !topk_idx || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null x, topk_idx or dst_row");
+    if (cap > 0 && (!recv_x || !info)) return fail(CGD_ERR_INVALID_ARG, "null packed receive pointer");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and packed_recv_x must be 16-byte aligned");
+    if (!aligned(topk_idx, 8) || !aligned(count, 4) || !aligned(info, 4) || !aligned(dst_row, 4) || !aligned(stats, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
+    const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "packed dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                    workspace_bytes);
+    return CGD_OK;
+}
+
+int cgd_dispatch_packed(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                        int num_experts, int num_ranks, int64_t expert_capacity, void* packed_recv_x,
+                        int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
+                        int32_t* cumulative_recv_stats, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_packed_args(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks, expert_capacity,
+                               packed_recv_x, packed_recv_count, recv_src_info, dst_row, cumulative_recv_stats,
+                               workspace, workspace_bytes);
+    if (rc) return rc;
+    hipError_t err = cgd::launch_dispatch_packed(x, num_tokens, hidden, topk_idx, num_topk, num_experts,
+                                                 (int)expert_capacity, -1, packed_recv_x, nullptr, packed_recv_count,
+                                                 recv_src_info, dst_row, cumulative_recv_stats, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "packed dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                 int num_topk, int num_experts, int num_ranks, int64_t expert_capacity,
+                                 int scale_format, void* packed_recv_x_fp8, void* packed_recv_scales,
+                                 int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
+                                 int32_t* cumulative_recv_stats, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if ((rc = check_packed_args(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks, expert_capacity,
+                                packed_recv_x_fp8, packed_recv_count, recv_src_info, dst_row, cumulative_recv_stats,
+                                workspace, workspace_bytes)))
+        return rc;
+    if ((rc = check_scales(packed_recv_scales, 0, 0, scale_format, expert_capacity > 0))) return rc;
+    hipError_t err = cgd::launch_dispatch_packed(x, num_tokens, hidden, topk_idx, num_topk, num_experts,
+                                                 (int)expert_capacity, scale_format, packed_recv_x_fp8,
+                                                 packed_recv_scales, packed_recv_count, recv_src_info, dst_row,
+                                                 cumulative_recv_stats, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "packed FP8 dispatch launch");
     return CGD_OK;
 }
 

@@ -64,11 +64,18 @@ __device__ __forceinline__ int slot_expert(int v) { return v < 0 ? -1 : (v & 0xF
 
 // Slot loops read the routing from LDS, which keeps the kernel light on
 // registers for any num_topk.
+// seg_cap >= 0 selects the fixed-capacity packed layout: segment e is rows
+// [e*seg_cap, (e+1)*seg_cap) whatever its count (seg_cap < 0: prefix-summed
+// segments of the aligned counts). counts receives every
+// expert's slot count (workspace, for the apply's -1 fill); packed_count
+// (min(count, seg_cap)) and stats (accumulates packed_count) are optional.
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
-                                                         int ebits, int A, int32_t* __restrict__ slot_pack,
+                                                         int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
                                                          int32_t* __restrict__ tile_base,
                                                          int32_t* __restrict__ expert_offset,
-                                                         int32_t* __restrict__ recv_src_idx,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ packed_count,
+                                                         int32_t* __restrict__ stats,
                                                          unsigned int* __restrict__ ticket) {
     extern __shared__ __align__(16) char lds[];
     unsigned long long* s_tok = reinterpret_cast<unsigned long long*>(lds);
@@ -199,34 +206,64 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         s_pre[x] = run;
     }
     __syncthreads();
-    // segment offsets: exclusive scan of the aligned sizes
-    block_exclusive_scan2(E, [&](int x) { return (s_pre[x] + A - 1) / A * A; }, s_off, s_wsum);
+    if (seg_cap >= 0) {
+        // fixed-capacity segments
+        for (int x = tid; x <= E; x += kRankTile) s_off[x] = x * seg_cap;
+        for (int x = tid; x < E; x += kRankTile) {
+            const int placed = min(s_pre[x], seg_cap);
+            if (packed_count) packed_count[x] = placed;
+            if (stats) stats[x] += placed;
+        }
+    } else {
+        // segment offsets: exclusive scan of the aligned sizes
+        block_exclusive_scan2(E, [&](int x) { return (s_pre[x] + A - 1) / A * A; }, s_off, s_wsum);
+    }
     __syncthreads();
-    // padding rows after each segment's data
-    for (int x = tid; x < E; x += kRankTile)
-        for (int r = s_off[x] + s_pre[x]; r < s_off[x + 1]; ++r) recv_src_idx[r] = -1;
+    for (int x = tid; x < E; x += kRankTile) counts[x] = s_pre[x];
     for (int x = tid; x <= E; x += kRankTile) expert_offset[x] = s_off[x];
     reset_ticket(ticket);
 }
 
-// Rows past the data carry no source token (grid-stride over all threads).
-__device__ __forceinline__ void fill_tail(int32_t* __restrict__ recv_src_idx, const int32_t* __restrict__ expert_offset,
-                                          int E, int64_t cap) {
-    const int64_t n = max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t r = n + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < cap; r += stride) recv_src_idx[r] = -1;
+// recv_src_idx = -1 for every row that holds no data: rows of segment e past
+// its count (alignment padding, unused fixed capacity) and rows past the last
+// segment. Threads are spread over (segment, row) pairs, so each thread needs
+// only its segment's bounds, whatever the grid size.
+__device__ __forceinline__ void fill_unused(int32_t* __restrict__ recv_src_idx,
+                                            const int32_t* __restrict__ expert_offset,
+                                            const int32_t* __restrict__ counts, int E, int64_t cap) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t end = max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
+    if (nth >= E) {
+        const int64_t per = nth / E;  // threads per segment
+        if (gid < per * E) {
+            const int e = (int)(gid % E);
+            const int64_t lo = max<int64_t>(0, (int64_t)expert_offset[e] + max(counts[e], 0));
+            const int64_t hi = min<int64_t>(expert_offset[e + 1], end);
+            for (int64_t r = lo + gid / E; r < hi; r += per) recv_src_idx[r] = -1;
+        }
+    } else {
+        for (int64_t e = gid; e < E; e += nth) {
+            const int64_t lo = max<int64_t>(0, (int64_t)expert_offset[e] + max(counts[e], 0));
+            const int64_t hi = min<int64_t>(expert_offset[e + 1], end);
+            for (int64_t r = lo; r < hi; ++r) recv_src_idx[r] = -1;
+        }
+    }
+    for (int64_t r = end + gid; r < cap; r += nth) recv_src_idx[r] = -1;
 }
 
 // Final receive row of a packed slot word p from the plan (-1: not selected).
-// A consistent plan gives an expert < E and a row < cap; anything else maps
-// to -1, so no access leaves the workspace or the receive buffer.
+// A consistent plan gives an expert < E and a row inside the expert's segment
+// and below cap; anything else maps to -1 (a slot past a fixed capacity is
+// dropped), so no access leaves the workspace or the receive buffer.
 __device__ __forceinline__ int final_row(int p, int64_t t, const int32_t* __restrict__ tile_base, int E,
                                          const int32_t* __restrict__ expert_offset, int64_t cap) {
     if (p < 0) return -1;
     const int ex = p >> kPackBits;
     const int lr = p & ((1 << kPackBits) - 1);
-    const int d = (ex < E) ? expert_offset[ex] + tile_base[(t / kRankTile) * E + ex] + lr : -1;
-    return (d < 0 || d >= cap) ? -1 : d;
+    if (ex >= E) return -1;
+    const int d = expert_offset[ex] + tile_base[(t / kRankTile) * E + ex] + lr;
+    return (d < 0 || d >= cap || d >= expert_offset[ex + 1]) ? -1 : d;
 }
 
 // One wave per (token, column chunk of U*64 16-byte vectors). With PACKED
@@ -246,10 +283,11 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
                                                                       const int32_t* __restrict__ tile_base, int E,
                                                                       int32_t* __restrict__ recv_src_idx,
                                                                       const int32_t* __restrict__ expert_offset,
+                                                                      const int32_t* __restrict__ counts,
                                                                       int64_t cap, uint4* __restrict__ recv_x,
                                                                       SideRows side) {
     const int lane = lane_id();
-    if (PACKED) fill_tail(recv_src_idx, expert_offset, E, cap);
+    if (PACKED) fill_unused(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t t = g / nchunk;
     if (t >= T) return;
@@ -318,11 +356,12 @@ template <int KM, int U, int FMT>
 __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
     const uint4* __restrict__ x, int64_t T, int nlv, int nchunk, int K, const int32_t* __restrict__ slot,
     int32_t* __restrict__ dst_row, const int32_t* __restrict__ tile_base, int E, int32_t* __restrict__ recv_src_idx,
-    const int32_t* __restrict__ expert_offset, int64_t cap, void* __restrict__ recv_q, void* __restrict__ recv_s) {
+    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ counts, int64_t cap,
+    void* __restrict__ recv_q, void* __restrict__ recv_s) {
     constexpr int kVin = kCastCpl / 8;             // 16-byte bf16 vectors per lane
     constexpr int kGroup = kFp8Block / kCastCpl;   // lanes per 128-channel block
     const int lane = lane_id();
-    fill_tail(recv_src_idx, expert_offset, E, cap);
+    fill_unused(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t t = g / nchunk;
     if (t >= T) return;
@@ -391,21 +430,49 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
 }
 
 // Dispatch workspace: ticket | tile bases int32 [tiles, E] | packed slot
-// words int32 [T, K] (plan -> apply).
+// words int32 [T, K] (plan -> apply) | per-expert slot counts int32 [E] |
+// segment offsets int32 [E+1] of the packed layout (its own copy, so the
+// packed entry points need no offsets argument).
+struct DispatchWs {
+    unsigned int* ticket;
+    int32_t* tile_base;
+    int32_t* slot_pack;
+    int32_t* counts;
+    int32_t* packed_offset;
+};
+
+static size_t rnd256(size_t b) { return (b + 255) / 256 * 256; }
+
 static size_t tile_bytes(int64_t T, int E) {
     const int64_t ntiles = T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile;
-    return ((size_t)ntiles * (size_t)E * sizeof(int32_t) + 255) / 256 * 256;
+    return rnd256((size_t)ntiles * (size_t)E * sizeof(int32_t));
 }
 
+static size_t slot_bytes(int64_t T, int K) { return rnd256((size_t)(T > 0 ? T : 0) * (size_t)K * sizeof(int32_t)); }
+
 size_t dispatch_workspace_bytes(int64_t T, int K, int E) {
-    const size_t slots = ((size_t)(T > 0 ? T : 0) * (size_t)K * sizeof(int32_t) + 255) / 256 * 256;
-    return kTicketBytes + tile_bytes(T, E) + slots;
+    return kTicketBytes + tile_bytes(T, E) + slot_bytes(T, K) + rnd256((size_t)E * 4) + rnd256((size_t)(E + 1) * 4);
+}
+
+static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
+    char* p = static_cast<char*>(const_cast<void*>(workspace));
+    DispatchWs w;
+    w.ticket = reinterpret_cast<unsigned int*>(p);
+    p += kTicketBytes;
+    w.tile_base = reinterpret_cast<int32_t*>(p);
+    p += tile_bytes(T, E);
+    w.slot_pack = reinterpret_cast<int32_t*>(p);
+    p += slot_bytes(T, K);
+    w.counts = reinterpret_cast<int32_t*>(p);
+    p += rnd256((size_t)E * 4);
+    w.packed_offset = reinterpret_cast<int32_t*>(p);
+    return w;
 }
 
 template <bool PACKED, int U>
 static void launch_scatter_u(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
                              int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
-                             int64_t cap, void* recv_x, const SideRows& side) {
+                             const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t waves = T * nchunk;
     const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
@@ -414,7 +481,7 @@ static void launch_scatter_u(int64_t T, int K, hipStream_t s, const void* x, int
     uint4* rv = reinterpret_cast<uint4*>(recv_x);
 #define CGD_SCATTER(KM)                                                                                            \
     hipLaunchKernelGGL((scatter_kernel<KM, U, PACKED>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot, dst_row,    \
-                       tile_base, E, src, off, cap, rv, side)
+                       tile_base, E, src, off, counts, cap, rv, side)
     if (K <= 2)
         CGD_SCATTER(2);
     else if (K <= 4)
@@ -433,13 +500,15 @@ constexpr int64_t kMinScatterWaves = 4096;
 template <bool PACKED>
 static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
                            int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
-                           int64_t cap, void* recv_x, const SideRows& side) {
+                           const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
     constexpr int U = CGD_SCATTER_U;
     const int64_t waves = T * ((nvec + U * kWave - 1) / (U * kWave));
     if (waves >= kMinScatterWaves)
-        launch_scatter_u<PACKED, U>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x, side);
+        launch_scatter_u<PACKED, U>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x,
+                                    side);
     else
-        launch_scatter_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, cap, recv_x, side);
+        launch_scatter_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x,
+                                    side);
 }
 
 static SideRows no_side() { return SideRows{nullptr, 0, 0, 0, 0, nullptr}; }
@@ -448,28 +517,30 @@ static SideRows fp8_side(const void* scales, int64_t st, int64_t sb, int H, int 
     return SideRows{scales, st, sb, H / kFp8Block, fmt == 2 ? 1 : 4, recv_scales};
 }
 
-hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
-                                int32_t* recv_src_idx, void* workspace, hipStream_t stream) {
-    char* ws = reinterpret_cast<char*>(workspace);
-    unsigned int* ticket = reinterpret_cast<unsigned int*>(ws);
-    int32_t* tile_base = reinterpret_cast<int32_t*>(ws + kTicketBytes);
-    int32_t* slot_pack = reinterpret_cast<int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
+static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap,
+                              int32_t* expert_offset, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
+                              hipStream_t stream) {
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
     hipLaunchKernelGGL(rank_kernel, dim3(ntiles), dim3(kRankTile), rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
-                       ebits, A, slot_pack, tile_base, expert_offset, recv_src_idx, ticket);
+                       ebits, A, seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                       w.ticket);
     return hipGetLastError();
+}
+
+hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
+                                void* workspace, hipStream_t stream) {
+    return launch_rank(topk_idx, T, K, E, A, -1, expert_offset, nullptr, nullptr, dispatch_ws(workspace, T, K, E),
+                       stream);
 }
 
 hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, void* recv_x, int64_t cap,
                                  const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
                                  const void* workspace, hipStream_t stream) {
-    const char* ws = reinterpret_cast<const char*>(workspace);
-    const int32_t* tile_base = reinterpret_cast<const int32_t*>(ws + kTicketBytes);
-    const int32_t* slot_pack = reinterpret_cast<const int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
-    launch_scatter<true>(T, K, stream, x, H / 8, slot_pack, dst_row, tile_base, E, recv_src_idx, expert_offset, cap,
-                         recv_x, no_side());
+    const DispatchWs w = dispatch_ws(workspace, T, K, E);
+    launch_scatter<true>(T, K, stream, x, H / 8, w.slot_pack, dst_row, w.tile_base, E, recv_src_idx, expert_offset,
+                         w.counts, cap, recv_x, no_side());
     return hipGetLastError();
 }
 
@@ -477,18 +548,16 @@ hipError_t launch_dispatch_apply_fp8(const void* xq, const void* xs, int64_t st,
                                      int H, int K, int E, void* recv_q, void* recv_s, int64_t cap,
                                      const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
                                      const void* workspace, hipStream_t stream) {
-    const char* ws = reinterpret_cast<const char*>(workspace);
-    const int32_t* tile_base = reinterpret_cast<const int32_t*>(ws + kTicketBytes);
-    const int32_t* slot_pack = reinterpret_cast<const int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
-    launch_scatter<true>(T, K, stream, xq, H / 16, slot_pack, dst_row, tile_base, E, recv_src_idx, expert_offset,
-                         cap, recv_q, fp8_side(xs, st, sb, H, fmt, recv_s));
+    const DispatchWs w = dispatch_ws(workspace, T, K, E);
+    launch_scatter<true>(T, K, stream, xq, H / 16, w.slot_pack, dst_row, w.tile_base, E, recv_src_idx, expert_offset,
+                         w.counts, cap, recv_q, fp8_side(xs, st, sb, H, fmt, recv_s));
     return hipGetLastError();
 }
 
 template <int U, int FMT>
-static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E, const int32_t* slot,
-                                  int32_t* dst_row, const int32_t* tile_base, int32_t* src, const int32_t* off,
-                                  int64_t cap, void* recv_q, void* recv_s, hipStream_t s) {
+static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E, const DispatchWs& w,
+                                  int32_t* dst_row, int32_t* src, const int32_t* off, int64_t cap, void* recv_q,
+                                  void* recv_s, hipStream_t s) {
     const int nlv = H / kCastCpl;
     const int nchunk = (nlv + U * kWave - 1) / (U * kWave);
     const int64_t waves = T * nchunk;
@@ -496,8 +565,8 @@ static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E,
     const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
 #define CGD_SCATTER_CAST(KM)                                                                                         \
-    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, T, nlv, nchunk, K, slot, dst_row,    \
-                       tile_base, E, src, off, cap, recv_q, recv_s)
+    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, T, nlv, nchunk, K, w.slot_pack,      \
+                       dst_row, w.tile_base, E, src, off, w.counts, cap, recv_q, recv_s)
     if (K <= 2)
         CGD_SCATTER_CAST(2);
     else if (K <= 4)
@@ -514,41 +583,57 @@ static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E,
 #endif
 
 template <int FMT>
-static void launch_scatter_cast(const void* x, int64_t T, int H, int K, int E, const int32_t* slot, int32_t* dst_row,
-                                const int32_t* tile_base, int32_t* src, const int32_t* off, int64_t cap, void* recv_q,
-                                void* recv_s, hipStream_t s) {
+static void launch_scatter_cast(const void* x, int64_t T, int H, int K, int E, const DispatchWs& w, int32_t* dst_row,
+                                int32_t* src, const int32_t* off, int64_t cap, void* recv_q, void* recv_s,
+                                hipStream_t s) {
     constexpr int U = CGD_SCATTER_CAST_U;
     const int64_t waves = T * ((H / kCastCpl + U * kWave - 1) / (U * kWave));
     if (waves >= kMinScatterWaves)
-        launch_scatter_cast_u<U, FMT>(x, T, H, K, E, slot, dst_row, tile_base, src, off, cap, recv_q, recv_s, s);
+        launch_scatter_cast_u<U, FMT>(x, T, H, K, E, w, dst_row, src, off, cap, recv_q, recv_s, s);
     else
-        launch_scatter_cast_u<1, FMT>(x, T, H, K, E, slot, dst_row, tile_base, src, off, cap, recv_q, recv_s, s);
+        launch_scatter_cast_u<1, FMT>(x, T, H, K, E, w, dst_row, src, off, cap, recv_q, recv_s, s);
 }
 
 hipError_t launch_dispatch_apply_cast_fp8(const void* x, int64_t T, int H, int K, int E, int fmt, void* recv_q,
                                           void* recv_s, int64_t cap, const int32_t* expert_offset,
                                           int32_t* recv_src_idx, int32_t* dst_row, const void* workspace,
                                           hipStream_t stream) {
-    const char* ws = reinterpret_cast<const char*>(workspace);
-    const int32_t* tile_base = reinterpret_cast<const int32_t*>(ws + kTicketBytes);
-    const int32_t* slot_pack = reinterpret_cast<const int32_t*>(ws + kTicketBytes + tile_bytes(T, E));
+    const DispatchWs w = dispatch_ws(workspace, T, K, E);
     if (fmt == 0)
-        launch_scatter_cast<0>(x, T, H, K, E, slot_pack, dst_row, tile_base, recv_src_idx, expert_offset, cap, recv_q,
-                               recv_s, stream);
+        launch_scatter_cast<0>(x, T, H, K, E, w, dst_row, recv_src_idx, expert_offset, cap, recv_q, recv_s, stream);
     else if (fmt == 1)
-        launch_scatter_cast<1>(x, T, H, K, E, slot_pack, dst_row, tile_base, recv_src_idx, expert_offset, cap, recv_q,
-                               recv_s, stream);
+        launch_scatter_cast<1>(x, T, H, K, E, w, dst_row, recv_src_idx, expert_offset, cap, recv_q, recv_s, stream);
     else
-        launch_scatter_cast<2>(x, T, H, K, E, slot_pack, dst_row, tile_base, recv_src_idx, expert_offset, cap, recv_q,
-                               recv_s, stream);
+        launch_scatter_cast<2>(x, T, H, K, E, w, dst_row, recv_src_idx, expert_offset, cap, recv_q, recv_s, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                  int expert_capacity, int fmt, void* recv_x, void* recv_s, int32_t* packed_count,
+                                  int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
+                                  hipStream_t stream) {
+    const DispatchWs w = dispatch_ws(workspace, T, K, E);
+    hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, w.packed_offset, packed_count, stats, w,
+                                 stream);
+    if (err != hipSuccess) return err;
+    const int64_t cap = (int64_t)E * expert_capacity;
+    if (fmt < 0)
+        launch_scatter<true>(T, K, stream, x, H / 8, w.slot_pack, dst_row, w.tile_base, E, recv_src_info,
+                             w.packed_offset, w.counts, cap, recv_x, no_side());
+    else if (fmt == 0)
+        launch_scatter_cast<0>(x, T, H, K, E, w, dst_row, recv_src_info, w.packed_offset, cap, recv_x, recv_s, stream);
+    else if (fmt == 1)
+        launch_scatter_cast<1>(x, T, H, K, E, w, dst_row, recv_src_info, w.packed_offset, cap, recv_x, recv_s, stream);
+    else
+        launch_scatter_cast<2>(x, T, H, K, E, w, dst_row, recv_src_info, w.packed_offset, cap, recv_x, recv_s, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
                                   int64_t cap, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    launch_scatter<false>(T, K, stream, x, H / 8, dst_row, nullptr, nullptr, 0, nullptr, nullptr, cap, recv_x,
-                          no_side());
+    launch_scatter<false>(T, K, stream, x, H / 8, dst_row, nullptr, nullptr, 0, nullptr, nullptr, nullptr, cap,
+                          recv_x, no_side());
     return hipGetLastError();
 }
 
@@ -556,8 +641,8 @@ hipError_t launch_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st
                                       int H, int K, const int32_t* dst_row, void* recv_q, void* recv_s, int64_t cap,
                                       hipStream_t stream) {
     if (T <= 0) return hipSuccess;
-    launch_scatter<false>(T, K, stream, xq, H / 16, dst_row, nullptr, nullptr, 0, nullptr, nullptr, cap, recv_q,
-                          fp8_side(xs, st, sb, H, fmt, recv_s));
+    launch_scatter<false>(T, K, stream, xq, H / 16, dst_row, nullptr, nullptr, 0, nullptr, nullptr, nullptr, cap,
+                          recv_q, fp8_side(xs, st, sb, H, fmt, recv_s));
     return hipGetLastError();
 }
 

@@ -26,7 +26,14 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R
                          uint8_t* itr, void* workspace, hipStream_t stream);
 
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
-                                int32_t* recv_src_idx, void* workspace, hipStream_t stream);
+                                void* workspace, hipStream_t stream);
+
+// Packed fixed-capacity layout: plan + apply; fmt < 0 moves bf16 rows, else
+// casts to FP8 with that scale format.
+hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                  int expert_capacity, int fmt, void* recv_x, void* recv_s, int32_t* packed_count,
+                                  int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
+                                  hipStream_t stream);
 
 hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, void* recv_x, int64_t cap,
                                  const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,

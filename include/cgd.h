@@ -130,17 +130,18 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
  * (the diagnostic-probes PR page, "Implementation": notify kernels before the
  * dispatch data kernels; the first-call latency blog page: tensor sizes are
  * notified in advance), so a caller may enqueue it early.
- *   cgd_dispatch_plan   writes expert_offset, the -1 entries of recv_src_idx
- *                       for alignment padding rows, and each slot's place
- *                       (per-tile bases, packed slot words) in the workspace.
- *   cgd_dispatch_apply  writes dst_row, the recv_src_idx of every data row
- *                       (and -1 past the data), and copies rows.
+ *   cgd_dispatch_plan   writes expert_offset and each slot's place (per-tile
+ *                       bases, packed slot words, per-expert counts) in the
+ *                       workspace.
+ *   cgd_dispatch_apply  writes dst_row, recv_src_idx (the source token of every
+ *                       data row, -1 for padding rows and rows past the data),
+ *                       and copies rows.
  * Between the two calls the workspace and expert_offset must not be modified
  * or used by another call. Mismatched arguments between the calls give wrong
  * rows but never an access outside the given buffers. */
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
-                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
                        int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,
@@ -338,6 +339,46 @@ int cgd_normal_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int6
                                    int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden,
                                    int num_ranks, const int32_t* send_row, void* recv_x_fp8, void* recv_scales,
                                    int64_t recv_capacity, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Fixed-capacity packed layout (the low-latency dispatch's receive buffers:
+ * legacy test analysis page, low-latency dispatch call and per-expert check;
+ * Python interface notes, "Dispatch API", num_worst_tokens).
+ *
+ * Expert e owns rows [e*expert_capacity, (e+1)*expert_capacity) of
+ * packed_recv_x [num_experts, expert_capacity, hidden]; its valid rows come
+ * first, in ascending (token, slot) order; a slot whose rank inside its expert
+ * reaches expert_capacity is dropped (dst_row -1). Shapes depend only on the
+ * sizes, so no host synchronisation is ever needed and a captured graph can
+ * replay the call.
+ *   packed_recv_count      int32 [num_experts] out: valid rows per expert
+ *   recv_src_info          int32 [num_experts, expert_capacity] out: source token of each
+ *                          valid row, -1 elsewhere (with one source the pages' layout range
+ *                          per (expert, source) is (0, count) and is not produced)
+ *   dst_row                int32 [num_tokens, num_topk] out: packed row of each slot, -1 if
+ *                          not selected or dropped; cgd_combine with this dst_row and
+ *                          recv_capacity = num_experts * expert_capacity combines packed
+ *                          expert outputs (the low-latency combine)
+ *   cumulative_recv_stats  int32 [num_experts] or NULL: packed_recv_count is added to it
+ *                          (the pages' cumulative_local_expert_recv_stats)
+ *   workspace              >= cgd_packed_workspace_bytes(...), same rules as the dispatch one
+ * ------------------------------------------------------------------------- */
+size_t cgd_packed_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts);
+
+int cgd_dispatch_packed(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                        int num_experts, int num_ranks, int64_t expert_capacity, void* packed_recv_x,
+                        int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
+                        int32_t* cumulative_recv_stats, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The packed layout with the FP8 cast on the way (the low-latency dispatch
+ * with FP8): packed_recv_x_fp8 [num_experts * expert_capacity, hidden] codes,
+ * packed_recv_scales [num_experts * expert_capacity, hidden/128]. */
+int cgd_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                 int num_topk, int num_experts, int num_ranks, int64_t expert_capacity,
+                                 int scale_format, void* packed_recv_x_fp8, void* packed_recv_scales,
+                                 int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
+                                 int32_t* cumulative_recv_stats, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
         "cgd_normal_capacity", "cgd_normal_dispatch", "cgd_normal_dispatch_cached", "cgd_normal_combine",
         "cgd_normal_dispatch_plan", "cgd_normal_dispatch_apply", "cgd_cast_to_fp8", "cgd_cast_back",
         "cgd_dispatch_apply_fp8", "cgd_dispatch_apply_cast_fp8", "cgd_dispatch_cached_fp8",
-        "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8",
+        "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
+        "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8",
     ])
 
 
@@ -122,14 +123,14 @@ def test_plan_and_apply_reject_bad_arguments():
     lib = cgd.load()
     lib.cgd_dispatch_plan.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                                      ctypes.c_size_t, ctypes.c_void_p]
     lib.cgd_dispatch_apply.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     f = _vp(FAKE)
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, 1 << 20, None) == -2
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, None, 0, None) == -3
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, 1 << 20, None) == -2
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, None, 0, None) == -3
     assert lib.cgd_dispatch_apply(f, 64, 12, 4, 16, 256, f, f, f, f, f, 1 << 20, None) == -1
     assert lib.cgd_dispatch_apply(f, 64, 128, 4, 513, 256, f, f, f, f, f, 1 << 20, None) == -1
     assert lib.cgd_dispatch_apply(f, 64, 128, 4, 16, 256, _vp(FAKE + 4), f, f, f, f, 1 << 20, None) == -1
@@ -258,6 +259,23 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert lib.cgd_normal_dispatch_cached_fp8(f, f, 2, 1, 0, 8, 256, 0, f, f, f, 16, None) == -1
     assert lib.cgd_normal_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, f, f, 4, 16, 4, f, f, 255, f, f, f, f, f, f,
                                              1 << 20, None) == -2
+    assert lib.cgd_last_error()
+
+
+def test_packed_entry_points_reject_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    assert lib.cgd_packed_workspace_bytes(128, 8, 256) >= lib.cgd_dispatch_workspace_bytes(128, 8, 256)
+    # x, T, H, idx, K, E, R, cap, recv, count, info, dst, stats, ws, wsb
+    assert lib.cgd_dispatch_packed(f, 128, 7168, f, 8, 256, 16, -1, f, f, f, f, None, f, 1 << 20, None) == -2
+    assert lib.cgd_dispatch_packed(f, 128, 7168, f, 8, 256, 16, 1 << 24, f, f, f, f, None, f, 1 << 20, None) == -2
+    assert lib.cgd_dispatch_packed(f, 128, 7168, f, 8, 256, 16, 128, f, None, f, f, None, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_packed(f, 128, 7168, f, 8, 256, 15, 128, f, f, f, f, None, f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_packed(f, 128, 7168, f, 8, 256, 16, 128, f, f, f, f, None, None, 0, None) == -3
+    assert lib.cgd_dispatch_packed_cast_fp8(f, 128, 7000, f, 8, 256, 16, 128, 0, f, f, f, f, f, None, f, 1 << 20,
+                                            None) == -1
+    assert lib.cgd_dispatch_packed_cast_fp8(f, 128, 7168, f, 8, 256, 16, 128, 0, f, None, f, f, f, None, f, 1 << 20,
+                                            None) == -1
     assert lib.cgd_last_error()
 
 
