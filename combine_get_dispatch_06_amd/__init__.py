@@ -28,7 +28,7 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
            "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
-           "PackedHandle", "low_latency_dispatch", "low_latency_combine"]
+           "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -78,6 +78,8 @@ def load():
     lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_plan.restype = i32
     lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, sz, vp]
+    lib.cgd_layout_and_dispatch_plan.restype = i32
+    lib.cgd_layout_and_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_packed_workspace_bytes.restype = sz
     lib.cgd_packed_workspace_bytes.argtypes = [i64, i32, i32]
     lib.cgd_dispatch_packed.restype = i32
@@ -410,6 +412,32 @@ def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expe
                                      _ptr(ws), ws.numel(), _stream(dev)))
     h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
     return DispatchPlan(h, ws, T)
+
+
+def layout_and_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expert_alignment: int = 1,
+                             recv_capacity: int | None = None):
+    """get_dispatch_layout and dispatch_plan in one launch.
+    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), DispatchPlan)."""
+    lib = load()
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    with torch.cuda.device(dev):
+        need = int(lib.cgd_dispatch_capacity(T, K, num_experts, expert_alignment))
+        cap = need if recv_capacity is None else int(recv_capacity)
+        ntpr = torch.empty(num_ranks, dtype=torch.int32, device=dev)
+        ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        itr = torch.empty((T, num_ranks), dtype=torch.bool, device=dev)
+        off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        dst = torch.empty((T, K), dtype=torch.int32, device=dev)
+        ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts))
+        _check("cgd_layout_and_dispatch_plan",
+               lib.cgd_layout_and_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap,
+                                                _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(ws), ws.numel(),
+                                                _stream(dev)))
+    h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+    return (ntpr, None, ntpe, itr, None), DispatchPlan(h, ws, T)
 
 
 def dispatch_apply(x, plan: DispatchPlan, recv_x=None, cast_fp8: int | None = None):

@@ -180,6 +180,27 @@ int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
     return CGD_OK;
 }
 
+int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                                 int num_ranks, int expert_alignment, int64_t recv_capacity,
+                                 int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                 uint8_t* is_token_in_rank, int32_t* expert_offset, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
+                             expert_offset, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (!num_tokens_per_rank || !num_tokens_per_expert)
+        return fail(CGD_ERR_INVALID_ARG, "null count output pointer");
+    if (num_tokens > 0 && !is_token_in_rank) return fail(CGD_ERR_INVALID_ARG, "null is_token_in_rank");
+    if (!aligned(num_tokens_per_rank, 4) || !aligned(num_tokens_per_expert, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned count output");
+    if (!aligned(is_token_in_rank, 16)) return fail(CGD_ERR_INVALID_ARG, "is_token_in_rank must be 16-byte aligned");
+    hipError_t err = cgd::launch_layout_and_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                                 expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
+                                                 is_token_in_rank, expert_offset, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "layout and dispatch plan launch");
+    return CGD_OK;
+}
+
 int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
                        int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,
                        int32_t* dst_row, const void* workspace, size_t workspace_bytes, hipStream_t stream) {

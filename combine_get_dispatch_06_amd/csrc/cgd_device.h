@@ -220,6 +220,77 @@ __device__ __forceinline__ bool last_block_done(unsigned int* ticket, unsigned i
 
 __device__ __forceinline__ bool last_block_done(unsigned int* ticket) { return last_block_done(ticket, gridDim.x); }
 
+// ---- Per-tile layout work (shared by the layout kernel and the fused
+// layout + dispatch plan): one token per thread, RW 64-bit words of rank mask
+// per token (1 for R <= 64, 6 for R <= 384).
+
+// Bitmask of the ranks the token's selected experts live on (e[k] < 0: none).
+template <int RW>
+__device__ __forceinline__ void token_rank_mask(const int (&e)[kMaxTopk], const int16_t* s_rank_of, uint64_t (&m)[RW]) {
+#pragma unroll
+    for (int w = 0; w < RW; ++w) m[w] = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) {
+        if (e[k] >= 0) {
+            const int r = s_rank_of[e[k]];
+#pragma unroll
+            for (int w = 0; w < RW; ++w)
+                if ((r >> 6) == w) m[w] |= 1ull << (r & 63);
+        }
+    }
+}
+
+// Distinct tokens per rank, added to s_rank (LDS, [R]): one ballot per rank
+// over the wave's tokens, lane (r % 64) adds the popcount for rank r. Also
+// stores the thread's mask in s_mask[tid * RW + w].
+template <int RW>
+__device__ __forceinline__ void count_rank_tokens(const uint64_t (&m)[RW], int R, int32_t* s_rank, uint64_t* s_mask) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+        const int rbeg = w * kWave;
+        const int rend = min(R, rbeg + kWave);
+        int cnt = 0;
+        for (int r = rbeg; r < rend; ++r) {
+            const uint64_t b = ballot((m[w] >> (r & 63)) & 1ull);
+            if (lane == (r & 63)) cnt = __popcll(b);
+        }
+        if (rbeg + lane < rend && cnt) atomicAdd(&s_rank[rbeg + lane], cnt);
+        s_mask[threadIdx.x * RW + w] = m[w];
+    }
+}
+
+// The tile's is_token_in_rank rows (nt tokens, a contiguous byte range
+// starting at out, 16-byte aligned) from the masks in s_mask, 16 bytes per
+// store; call after a barrier that follows count_rank_tokens.
+template <int RW>
+__device__ __forceinline__ void store_token_in_rank(const uint64_t* s_mask, int nt, int R, uint8_t* out) {
+    const int64_t nbytes = (int64_t)nt * R;
+    for (int64_t c = threadIdx.x; c * 16 < nbytes; c += blockDim.x) {
+        const int64_t b0 = c * 16;
+        int tok = (int)(b0 / R);
+        int r = (int)(b0 - (int64_t)tok * R);
+        const int nb = (int)min<int64_t>(16, nbytes - b0);
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j < nb) {
+                const uint32_t bit = (uint32_t)(s_mask[tok * RW + (r >> 6)] >> (r & 63)) & 1u;
+                wd[j >> 2] |= bit << ((j & 3) * 8);
+            }
+            if (++r == R) {
+                r = 0;
+                ++tok;
+            }
+        }
+        if (nb == 16) {
+            *reinterpret_cast<uint4*>(out + b0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        } else {
+            for (int j = 0; j < nb; ++j) out[b0 + j] = (uint8_t)(wd[j >> 2] >> ((j & 3) * 8));
+        }
+    }
+}
+
 // Exclusive prefix sum of n <= 2 * kRankTile integers v(0..n-1) by a block
 // of kRankTile threads: out[i] = v(0) + ... + v(i-1) for i <= n (out[n] is the
 // total). Thread i owns entries 2i and 2i+1; a wavefront scan with shuffles

@@ -69,6 +69,20 @@ __device__ __forceinline__ int slot_expert(int v) { return v < 0 ? -1 : (v & 0xF
 // segments of the aligned counts). counts receives every
 // expert's slot count (workspace, for the apply's -1 fill); packed_count
 // (min(count, seg_cap)) and stats (accumulates packed_count) are optional.
+// With LAYOUT the kernel also produces get_dispatch_layout's outputs from the
+// same staged tile (rank masks with RW 64-bit words, as the layout kernel):
+// is_token_in_rank rows per tile, per-tile distinct-token counts per rank
+// (rank_part, workspace) summed by the last block into ntpr, and ntpe = the
+// column totals of the tile histograms.
+struct LayoutOut {
+    int R, L;
+    int32_t* ntpr;
+    int32_t* ntpe;
+    uint8_t* itr;
+    int32_t* rank_part;
+};
+
+template <int RW, bool LAYOUT>
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
                                                          int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
                                                          int32_t* __restrict__ tile_base,
@@ -76,7 +90,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ packed_count,
                                                          int32_t* __restrict__ stats,
-                                                         unsigned int* __restrict__ ticket) {
+                                                         unsigned int* __restrict__ ticket, LayoutOut lo) {
     extern __shared__ __align__(16) char lds[];
     unsigned long long* s_tok = reinterpret_cast<unsigned long long*>(lds);
     int32_t* s_pre = reinterpret_cast<int32_t*>(s_tok + kRankWaves * E);
@@ -95,6 +109,13 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     for (int i = tid; i < kRankWaves * E; i += kRankTile) {
         s_tok[i] = 0ull;
         s_pre[i] = 0;
+    }
+    __shared__ uint64_t s_mask[LAYOUT ? kRankTile * RW : 1];
+    __shared__ int32_t s_rank[LAYOUT ? kMaxRanks : 1];
+    __shared__ int16_t s_rank_of[LAYOUT ? kMaxExperts : 1];
+    if (LAYOUT) {
+        for (int i = tid; i < E; i += kRankTile) s_rank_of[i] = (int16_t)(i / lo.L);
+        for (int i = tid; i < lo.R; i += kRankTile) s_rank[i] = 0;
     }
     stage_routing<kMaxTopk>(topk_idx + t0 * K, nt * K, E, s_slot);
     __syncthreads();
@@ -115,7 +136,18 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k)
         if (e[k] >= 0) dup |= (atomicOr(&s_tok[wave * E + e[k]], bit) & bit) != 0;
-    if (!__syncthreads_or(dup)) {
+    if (LAYOUT) {
+        uint64_t m[RW];
+        token_rank_mask<RW>(e, s_rank_of, m);
+        count_rank_tokens<RW>(m, lo.R, s_rank, s_mask);
+    }
+    const bool any_dup = __syncthreads_or(dup);
+    if (LAYOUT) {
+        // t0*R is a multiple of 16 because kRankTile is
+        store_token_in_rank<RW>(s_mask, nt, lo.R, lo.itr + t0 * lo.R);
+        for (int r = tid; r < lo.R; r += kRankTile) lo.rank_part[(int64_t)tile * lo.R + r] = s_rank[r];
+    }
+    if (!any_dup) {
         // Every token holds an expert at most once: the rank of (t,k) among
         // the tile's rows of expert e is the number of earlier tokens holding
         // e: the lanes below mine in my wave's mask plus earlier waves' rows.
@@ -204,6 +236,22 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
             }
         }
         s_pre[x] = run;
+    }
+    if (LAYOUT) {
+        // layout outputs: slot totals per expert, distinct tokens per rank
+        for (int x = tid; x < E; x += kRankTile) lo.ntpe[x] = s_pre[x];
+        for (int r = tid; r < lo.R; r += kRankTile) {
+            int run = 0;
+            for (int b0 = 0; b0 < ntiles; b0 += kBatch) {
+                int v[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    v[j] = (b0 + j < ntiles) ? lo.rank_part[(int64_t)(b0 + j) * lo.R + r] : 0;
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) run += v[j];
+            }
+            lo.ntpr[r] = run;
+        }
     }
     __syncthreads();
     if (seg_cap >= 0) {
@@ -439,6 +487,7 @@ struct DispatchWs {
     int32_t* slot_pack;
     int32_t* counts;
     int32_t* packed_offset;
+    int32_t* rank_part;  // per-tile distinct tokens per rank (fused layout), [tiles, kMaxRanks]
 };
 
 static size_t rnd256(size_t b) { return (b + 255) / 256 * 256; }
@@ -451,7 +500,8 @@ static size_t tile_bytes(int64_t T, int E) {
 static size_t slot_bytes(int64_t T, int K) { return rnd256((size_t)(T > 0 ? T : 0) * (size_t)K * sizeof(int32_t)); }
 
 size_t dispatch_workspace_bytes(int64_t T, int K, int E) {
-    return kTicketBytes + tile_bytes(T, E) + slot_bytes(T, K) + rnd256((size_t)E * 4) + rnd256((size_t)(E + 1) * 4);
+    return kTicketBytes + tile_bytes(T, E) + slot_bytes(T, K) + rnd256((size_t)E * 4) + rnd256((size_t)(E + 1) * 4) +
+           tile_bytes(T, kMaxRanks);
 }
 
 static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
@@ -466,6 +516,8 @@ static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
     w.counts = reinterpret_cast<int32_t*>(p);
     p += rnd256((size_t)E * 4);
     w.packed_offset = reinterpret_cast<int32_t*>(p);
+    p += rnd256((size_t)(E + 1) * 4);
+    w.rank_part = reinterpret_cast<int32_t*>(p);
     return w;
 }
 
@@ -519,14 +571,32 @@ static SideRows fp8_side(const void* scales, int64_t st, int64_t sb, int H, int 
 
 static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap,
                               int32_t* expert_offset, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
-                              hipStream_t stream) {
+                              hipStream_t stream, const LayoutOut* layout = nullptr) {
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
-    hipLaunchKernelGGL(rank_kernel, dim3(ntiles), dim3(kRankTile), rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
-                       ebits, A, seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
-                       w.ticket);
+    const dim3 grid(ntiles), block(kRankTile);
+    const size_t lds = rank_lds_bytes(E, K);
+    if (!layout) {
+        const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
+        hipLaunchKernelGGL((rank_kernel<1, false>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
+                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, none);
+    } else if (layout->R <= 64) {
+        hipLaunchKernelGGL((rank_kernel<1, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
+                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout);
+    } else {
+        hipLaunchKernelGGL((rank_kernel<6, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
+                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout);
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int32_t* ntpr,
+                                  int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, void* workspace,
+                                  hipStream_t stream) {
+    const DispatchWs w = dispatch_ws(workspace, T, K, E);
+    const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
+    return launch_rank(topk_idx, T, K, E, A, -1, expert_offset, nullptr, nullptr, w, stream, &lo);
 }
 
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,

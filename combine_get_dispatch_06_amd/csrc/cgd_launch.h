@@ -28,6 +28,11 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
                                 void* workspace, hipStream_t stream);
 
+// get_dispatch_layout and the dispatch plan in one launch.
+hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int32_t* ntpr,
+                                  int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, void* workspace,
+                                  hipStream_t stream);
+
 // Packed fixed-capacity layout: plan + apply; fmt < 0 moves bf16 rows, else
 // casts to FP8 with that scale format.
 hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,

@@ -50,66 +50,16 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     int e[kMaxTopk];
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) e[k] = (tid < nt && k < K) ? s_idx[tid * K + k] : -1;
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k)
+        if (e[k] >= 0) atomicAdd(&s_hist[e[k]], 1);
     uint64_t m[RW];
-#pragma unroll
-    for (int w = 0; w < RW; ++w) m[w] = 0;
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-        if (e[k] >= 0) {
-            atomicAdd(&s_hist[e[k]], 1);
-            const int r = s_rank_of[e[k]];
-#pragma unroll
-            for (int w = 0; w < RW; ++w)
-                if ((r >> 6) == w) m[w] |= 1ull << (r & 63);
-        }
-    }
-
-    // distinct tokens per rank: ballot over the wave's tokens, lane (r % 64)
-    // keeps the popcount for rank r
-    const int lane = lane_id();
-#pragma unroll
-    for (int w = 0; w < RW; ++w) {
-        const int rbeg = w * kWave;
-        const int rend = min(R, rbeg + kWave);
-        int cnt = 0;
-        for (int r = rbeg; r < rend; ++r) {
-            const uint64_t b = ballot((m[w] >> (r & 63)) & 1ull);
-            if (lane == (r & 63)) cnt = __popcll(b);
-        }
-        if (rbeg + lane < rend && cnt) atomicAdd(&s_rank[rbeg + lane], cnt);
-        s_mask[tid * RW + w] = m[w];
-    }
+    token_rank_mask<RW>(e, s_rank_of, m);
+    count_rank_tokens<RW>(m, R, s_rank, s_mask);
     __syncthreads();
-
-    // is_token_in_rank rows of this tile: bytes [t0*R, (t0+nt)*R), 16 at a time.
-    // t0*R is a multiple of 16 because kLayoutTile is.
-    {
-        const int64_t nbytes = (int64_t)nt * R;
-        uint8_t* out = itr + t0 * R;
-        for (int64_t c = tid; c * 16 < nbytes; c += kLayoutTile) {
-            const int64_t b0 = c * 16;
-            int tok = (int)(b0 / R);
-            int r = (int)(b0 - (int64_t)tok * R);
-            const int nb = (int)min<int64_t>(16, nbytes - b0);
-            uint32_t wd[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                if (j < nb) {
-                    const uint32_t bit = (uint32_t)(s_mask[tok * RW + (r >> 6)] >> (r & 63)) & 1u;
-                    wd[j >> 2] |= bit << ((j & 3) * 8);
-                }
-                if (++r == R) {
-                    r = 0;
-                    ++tok;
-                }
-            }
-            if (nb == 16) {
-                *reinterpret_cast<uint4*>(out + b0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-            } else {
-                for (int j = 0; j < nb; ++j) out[b0 + j] = (uint8_t)(wd[j >> 2] >> ((j & 3) * 8));
-            }
-        }
-    }
+    // is_token_in_rank rows of this tile: t0*R is a multiple of 16 because
+    // kLayoutTile is
+    store_token_in_rank<RW>(s_mask, nt, R, itr + t0 * R);
 
     if (gridDim.x == 1) {
         for (int i = tid; i < E; i += kLayoutTile) ntpe[i] = s_hist[i];

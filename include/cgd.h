@@ -147,6 +147,17 @@ int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_to
                        int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,
                        int32_t* dst_row, const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* cgd_get_dispatch_layout and cgd_dispatch_plan in one launch: both read the
+ * same routing, so one pass over each 256-token tile produces the layout
+ * outputs (as cgd_get_dispatch_layout, same arguments and rules; no layout
+ * workspace is needed) and the plan (as cgd_dispatch_plan, which
+ * cgd_dispatch_apply then completes). */
+int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                                 int num_ranks, int expert_alignment, int64_t recv_capacity,
+                                 int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                 uint8_t* is_token_in_rank, int32_t* expert_offset, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /* Cached dispatch (Python interface notes, "Dispatch API", handle reuse):
  * copies rows with a dst_row from an earlier cgd_dispatch, skipping the
  * layout work. recv_x[dst_row[t,k]] = x[t] for every dst_row[t,k] in

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         "cgd_normal_dispatch_plan", "cgd_normal_dispatch_apply", "cgd_cast_to_fp8", "cgd_cast_back",
         "cgd_dispatch_apply_fp8", "cgd_dispatch_apply_cast_fp8", "cgd_dispatch_cached_fp8",
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
-        "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8",
+        "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan",
     ])
 
 
@@ -260,6 +260,18 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert lib.cgd_normal_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, f, f, 4, 16, 4, f, f, 255, f, f, f, f, f, f,
                                              1 << 20, None) == -2
     assert lib.cgd_last_error()
+
+
+def test_layout_and_plan_rejects_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    # idx, T, K, E, R, A, cap, ntpr, ntpe, itr, off, ws, wsb
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, f, 1 << 20, None) == -2
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 3, 1, 256, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, None, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, _vp(FAKE + 1), f, f, 1 << 20,
+                                            None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, None, 0, None) == -3
 
 
 def test_packed_entry_points_reject_bad_arguments():

@@ -247,3 +247,32 @@ def test_seeds_sweep_prefill_and_skewed():
             o = oracle.dispatch(None, idx, w.E, w.R, with_rows=False)
             np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
             np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+
+
+@pytest.mark.parametrize("case", ["tiny", "prefill", "decode", "skewed", "stress", "R=E=384", "duplicates",
+                                  "ragged_T=1025_neg", "R=1", "K=16_E=512_R=64"])
+def test_layout_and_plan_in_one_launch(case):
+    """The fused launch gives the layout kernel's outputs and the plan that
+    dispatch_apply completes into the same permutation, bit for bit."""
+    if case in synth.WORKLOADS:
+        w = synth.WORKLOADS[case]
+        idx, x = synth.make_topk_idx(w, 0), None
+        align = w.align
+    else:
+        spec = dict(EDGE_CASES[case])
+        spec.pop("cap_extra", None)
+        w, idx, x, _ = _edge(**spec)
+        align = w.align
+    say(f"[fused] {case}")
+    (ntpr, _, ntpe, itr, _), plan = cgd.layout_and_dispatch_plan(dev_i64(idx), w.E, w.R, expert_alignment=align)
+    xs = torch.zeros((w.T, 8), dtype=torch.bfloat16, device=DEV) if x is None else dev_bf16(x[:, :8].copy())
+    _, h = cgd.dispatch_apply(xs, plan)
+    torch.cuda.synchronize()
+    o = oracle.layout(idx, w.E, w.R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), o[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), o[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), o[2])
+    d = oracle.dispatch(None, idx, w.E, w.R, align=align, with_rows=False)
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), d["expert_offset"])
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), d["dst_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), d["recv_src_idx"])
