@@ -5,10 +5,25 @@ module only marshals arguments: every step of the path runs in libcgd's HIP
 kernels, on the caller's current HIP stream. PyTorch supplies device memory
 and streams.
 
+Expert-granular path (one received row per selected expert):
+
     ntpr, _, ntpe, is_token_in_rank, _ = get_dispatch_layout(topk_idx, num_experts, num_ranks)
     recv_x, handle = dispatch(x, topk_idx, num_experts, num_ranks)
     recv_x2, _ = dispatch(x2, handle=handle)            # cached: reuses the layout
     combined = combine(expert_out, handle, topk_weights)
+    layout, plan = layout_and_dispatch_plan(topk_idx, num_experts, num_ranks)   # one launch
+    recv_x, handle = dispatch_apply(x, plan)
+
+Rank-granular path (normal mode, one row per (token, flagged rank)):
+
+    recv_x, recv_topk_idx, recv_topk_weights, num_recv_per_expert, h = normal_dispatch(
+        x, is_token_in_rank, ntpe, topk_idx, topk_weights, num_experts=E)
+    combined_x, combined_topk_weights = normal_combine(expert_out, h, recv_topk_weights, bias=(b0, b1))
+
+FP8 payload: per_token_cast_to_fp8 / per_token_cast_back; every dispatch
+accepts and returns (codes, scales) tuples, and dispatch(..., cast_fp8=fmt)
+casts on the way. Fixed-capacity packed layout (low-latency dispatch):
+low_latency_dispatch / low_latency_combine.
 
 The calls follow the DeepEP-style Buffer API described by the DeepEP Python
 interface notes ("4 Python接口", section "Dispatch API") and the

@@ -27,12 +27,6 @@ namespace cgd {
 #ifndef CGD_COMBINE_U
 #define CGD_COMBINE_U 1
 #endif
-#ifndef CGD_COMBINE_NT
-#define CGD_COMBINE_NT 1
-#endif
-#ifndef CGD_COMBINE_READLANE
-#define CGD_COMBINE_READLANE 1
-#endif
 // Occupancy cap: each block reserves this much (unused) LDS, so at most
 // 160 KB / CGD_COMBINE_LDS_CAP blocks share a CU (5 at 32 KB).
 #ifndef CGD_COMBINE_LDS_CAP
@@ -64,13 +58,8 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void combine_kernel(const uin
         float wk[KM];
 #pragma unroll
         for (int k = 0; k < KM; ++k) {
-#if CGD_COMBINE_READLANE
             dk[k] = __builtin_amdgcn_readlane(d, k);
             wk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), k));
-#else
-            dk[k] = __shfl(d, k, kWave);
-            wk[k] = __shfl(wt, k, kWave);
-#endif
         }
 
         uint4 buf[KM][U];
@@ -81,7 +70,7 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void combine_kernel(const uin
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int v = v0 + u * kWave + lane;
-                if (v < nvec) buf[k][u] = CGD_COMBINE_NT ? load_nt(yr + v) : yr[v];
+                if (v < nvec) buf[k][u] = load_nt(yr + v);
             }
         }
         uint4* orow = out + t * nvec;

@@ -19,15 +19,25 @@
 //                   expert id). It writes a packed (expert, rank-in-tile) word
 //                   per slot and the tile's expert histogram. The last block
 //                   to finish turns the histograms into per-tile bases (rows of
-//                   the expert in earlier tiles, one pass) and the aligned
-//                   segment offsets (block prefix scan), and marks padding rows.
+//                   the expert in earlier tiles, one pass), the per-expert
+//                   counts and the segment offsets: a block prefix scan of the
+//                   aligned counts, or e * capacity for the fixed-capacity
+//                   packed layout. Its LAYOUT form also writes
+//                   get_dispatch_layout's outputs from the same tile.
 //   scatter_kernel  one wave per (token, column chunk): lanes 0..K-1 turn
 //                   their slot into a final row (segment offset + tile base +
 //                   rank in tile); the chunk's 16-byte vectors are loaded once
 //                   and stored to the K destination rows with non-temporal
 //                   stores. Each row is read from HBM once however many
-//                   experts it goes to.
+//                   experts it goes to. The grid also writes recv_src_idx = -1
+//                   for every row without data (padding, unused capacity, tail).
+//                   scatter_cast_kernel is its FP8 form (cast on the way).
 // Cached dispatch runs the scatter kernel on a stored final dst_row.
+//
+// Measured on MI355X: stores into the ~E receive segments that a token-ordered
+// pass keeps open cap near 5 TB/s whatever the wave shape or store policy, and
+// destination-ordered copies (sequential stores) lose more on the 8x scattered
+// re-reads of x; this token-ordered form is the fastest of those tried.
 #include "cgd_device.h"
 #include "cgd_launch.h"
 
@@ -40,12 +50,6 @@ constexpr int kPackBits = 13;  // rank inside a tile < 256 * 16 = 4096 < 2^13
 #endif
 #ifndef CGD_SCATTER_U
 #define CGD_SCATTER_U 4
-#endif
-#ifndef CGD_SCATTER_NT
-#define CGD_SCATTER_NT 1
-#endif
-#ifndef CGD_SCATTER_READLANE
-#define CGD_SCATTER_READLANE 1
 #endif
 constexpr int kScatterWaves = CGD_SCATTER_WAVES;  // tokens (waves) per scatter block
 constexpr int kBatch = 16;                        // loads in flight per thread when summing columns
@@ -364,11 +368,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
     int dk[KM];
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
-#if CGD_SCATTER_READLANE
         dk[k] = __builtin_amdgcn_readlane(d, k);
-#else
-        dk[k] = __shfl(d, k, kWave);
-#endif
     }
 #pragma unroll
     for (int k = 0; k < KM; ++k) {
@@ -377,12 +377,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int v = v0 + u * kWave + lane;
-            if (v < nvec) {
-                if (CGD_SCATTER_NT)
-                    store_nt(dr + v, buf[u]);
-                else
-                    dr[v] = buf[u];
-            }
+            if (v < nvec) store_nt(dr + v, buf[u]);
         }
         if (side.src && c == 0) copy_side_row(side, t, dk[k], lane);
     }

@@ -47,9 +47,6 @@ namespace cgd {
 #ifndef CGD_NORMAL_SCATTER_U
 #define CGD_NORMAL_SCATTER_U 1
 #endif
-#ifndef CGD_NORMAL_READLANE
-#define CGD_NORMAL_READLANE 0
-#endif
 constexpr int kNormGroups = kRankTile / kWave;              // token groups (waves) per tile
 constexpr int kFlagBatch = 16;                               // flag bytes in flight per thread
 constexpr int kTileBatch = 16;                               // tile counts in flight per thread
@@ -310,11 +307,7 @@ __global__ __launch_bounds__(kNormCombineWaves* kWave) void normal_combine_kerne
             for (int i = 0; i < kGatherBatch; ++i) {
                 dk[i] = -1;
                 if (m) {
-#if CGD_NORMAL_READLANE
-                    dk[i] = __builtin_amdgcn_readlane(d, __builtin_ctzll(m));
-#else
                     dk[i] = __shfl(d, __builtin_ctzll(m), kWave);
-#endif
                     m &= m - 1;
                 }
             }
