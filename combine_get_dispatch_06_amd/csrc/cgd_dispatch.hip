@@ -7,37 +7,48 @@
 // a segment, rows follow ascending (token, slot), which makes the permutation
 // unique and independent of scheduling.
 //
-// Two launches, no block ever waits for another:
-//   rank_kernel     one block per tile of 256 tokens (4 waves, one token per
-//                   lane). For each slot it finds the number of earlier slots
-//                   of the tile with the same expert. When no token of the
-//                   tile repeats an expert, each wave sets one bit per (expert,
-//                   lane) in a 64-bit LDS mask per expert; the rank is the
-//                   popcount of the mask below the lane plus the rows of
-//                   earlier waves. Otherwise it counts slot by slot with
-//                   wavefront ballots (a "multi-split" over the bits of the
-//                   expert id). It writes a packed (expert, rank-in-tile) word
-//                   per slot and the tile's expert histogram. The last block
-//                   to finish turns the histograms into per-tile bases (rows of
-//                   the expert in earlier tiles, one pass), the per-expert
-//                   counts and the segment offsets: a block prefix scan of the
-//                   aligned counts, or e * capacity for the fixed-capacity
-//                   packed layout. Its LAYOUT form also writes
-//                   get_dispatch_layout's outputs from the same tile.
-//   scatter_kernel  one wave per (token, column chunk): lanes 0..K-1 turn
-//                   their slot into a final row (segment offset + tile base +
-//                   rank in tile); the chunk's 16-byte vectors are loaded once
-//                   and stored to the K destination rows with non-temporal
-//                   stores. Each row is read from HBM once however many
-//                   experts it goes to. The grid also writes recv_src_idx = -1
-//                   for every row without data (padding, unused capacity, tail).
-//                   scatter_cast_kernel is its FP8 form (cast on the way).
-// Cached dispatch runs the scatter kernel on a stored final dst_row.
+// No block ever waits for another:
+//   rank_kernel     (the plan) one block per tile of 256 tokens (4 waves, one
+//                   token per lane). For each slot it finds the number of
+//                   earlier slots of the tile with the same expert. When no
+//                   token of the tile repeats an expert, each wave sets one
+//                   bit per (expert, lane) in a 64-bit LDS mask per expert;
+//                   the rank is the popcount of the mask below the lane plus
+//                   the rows of earlier waves. Otherwise it counts slot by slot
+//                   with wavefront ballots (a "multi-split" over the bits of
+//                   the expert id). It writes a packed (expert, rank-in-tile)
+//                   word per slot and the tile's expert histogram. The last
+//                   block to finish turns the histograms into per-tile bases
+//                   (rows of the expert in earlier tiles, one pass), the
+//                   per-expert counts and the segment offsets: a block prefix
+//                   scan of the aligned counts, or e * capacity for the
+//                   fixed-capacity packed layout (a one-tile grid finishes
+//                   from LDS without the handshake). Its LAYOUT form also
+//                   writes get_dispatch_layout's outputs from the same tile.
+//   the apply       moves the rows. Each row is read from HBM once however
+//                   many experts it goes to; rows without data get
+//                   recv_src_idx = -1 (padding, unused capacity, tail).
+//                   Batches of >= 16384 slots with top-k <= 8:
+//                     finalize_kernel  one thread per slot: final row =
+//                                      segment offset + tile base + rank,
+//                                      dst_row and recv_src_idx;
+//                     scatter_kernel   one wave per (token, 1 KB chunk, slot)
+//                                      stores the chunk once to its row.
+//                   Otherwise scatter_bcast_kernel: one wave per (token,
+//                   chunk) resolves the K rows inline and stores the chunk to
+//                   each (one launch: decode latency). scatter_cast_kernel is
+//                   the FP8 form (cast on the way).
+// Cached dispatch runs the row copy (or the broadcast kernel) on a stored
+// final dst_row.
 //
-// Measured on MI355X: stores into the ~E receive segments that a token-ordered
-// pass keeps open cap near 5 TB/s whatever the wave shape or store policy, and
-// destination-ordered copies (sequential stores) lose more on the 8x scattered
-// re-reads of x; this token-ordered form is the fastest of those tried.
+// Measured on MI355X: the store pattern bounds the apply. Stores into the ~E
+// receive segments of a token-ordered pass run near 5 TB/s; short waves that
+// store one 1 KB piece each (row copy) do 3-15 % better than long waves that
+// store K pieces, as long as each wave's row comes after one dependent load
+// (hence the finalize launch). Destination-ordered copies (sequential stores)
+// lose more on the 8x scattered re-reads of x than they gain.
+#include <algorithm>
+
 #include "cgd_device.h"
 #include "cgd_launch.h"
 
@@ -45,13 +56,8 @@ namespace cgd {
 
 constexpr int kRankWaves = kRankTile / kWave;
 constexpr int kPackBits = 13;  // rank inside a tile < 256 * 16 = 4096 < 2^13
-#ifndef CGD_SCATTER_WAVES
-#define CGD_SCATTER_WAVES 4
-#endif
-#ifndef CGD_SCATTER_U
-#define CGD_SCATTER_U 4
-#endif
-constexpr int kScatterWaves = CGD_SCATTER_WAVES;  // tokens (waves) per scatter block
+constexpr int kScatterWaves = 4;  // waves per block of the cast-on-dispatch kernel
+constexpr int kSlotWaves = 16;    // waves per block of the row copy
 constexpr int kBatch = 16;                        // loads in flight per thread when summing columns
 
 // LDS of the rank kernel, carved from dynamic shared memory sized for (E, K).
@@ -162,7 +168,8 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
                 s_pre[w * E + x] = run;
                 run += __popcll(s_tok[w * E + x]);
             }
-            tile_base[(int64_t)tile * E + x] = run;
+            if (ntiles > 1) tile_base[(int64_t)tile * E + x] = run;
+            s_off[x] = run;  // the tile's histogram (one-tile grids finish from it)
         }
         __syncthreads();
 #pragma unroll
@@ -201,7 +208,8 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
                 s_pre[w * E + x] = run;
                 run += c;
             }
-            tile_base[(int64_t)tile * E + x] = run;
+            if (ntiles > 1) tile_base[(int64_t)tile * E + x] = run;
+            s_off[x] = run;
         }
         __syncthreads();
         if (mine)
@@ -221,6 +229,17 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         for (int i = tid; i < n; i += kRankTile) out[i] = s_slot[i];
     }
 
+    if (ntiles == 1) {
+        // one tile (decode batches): its histogram, in LDS, is the total and
+        // no other block has to be waited for
+        for (int x = tid; x < E; x += kRankTile) {
+            s_pre[x] = s_off[x];
+            tile_base[x] = 0;
+            if (LAYOUT) lo.ntpe[x] = s_off[x];
+        }
+        if (LAYOUT)
+            for (int r = tid; r < lo.R; r += kRankTile) lo.ntpr[r] = s_rank[r];
+    } else {
     if (!last_block_done(ticket)) return;
 
     // ---- 2. last block: per-tile bases and segment offsets ----
@@ -257,6 +276,8 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
             lo.ntpr[r] = run;
         }
     }
+    reset_ticket(ticket);
+    }
     __syncthreads();
     if (seg_cap >= 0) {
         // fixed-capacity segments
@@ -273,7 +294,6 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     __syncthreads();
     for (int x = tid; x < E; x += kRankTile) counts[x] = s_pre[x];
     for (int x = tid; x <= E; x += kRankTile) expert_offset[x] = s_off[x];
-    reset_ticket(ticket);
 }
 
 // recv_src_idx = -1 for every row that holds no data: rows of segment e past
@@ -282,9 +302,8 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
 // only its segment's bounds, whatever the grid size.
 __device__ __forceinline__ void fill_unused(int32_t* __restrict__ recv_src_idx,
                                             const int32_t* __restrict__ expert_offset,
-                                            const int32_t* __restrict__ counts, int E, int64_t cap) {
-    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                            const int32_t* __restrict__ counts, int E, int64_t cap, int64_t gid,
+                                            int64_t nth) {
     const int64_t end = max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
     if (nth >= E) {
         const int64_t per = nth / E;  // threads per segment
@@ -304,32 +323,47 @@ __device__ __forceinline__ void fill_unused(int32_t* __restrict__ recv_src_idx,
     for (int64_t r = end + gid; r < cap; r += nth) recv_src_idx[r] = -1;
 }
 
+// The first kFillBlocks blocks of an apply grid (all of a smaller grid) do the fill.
+constexpr int kFillBlocks = 1024;
+
+__device__ __forceinline__ void fill_unused_grid(int32_t* __restrict__ recv_src_idx,
+                                                 const int32_t* __restrict__ expert_offset,
+                                                 const int32_t* __restrict__ counts, int E, int64_t cap) {
+    const int nb = min((int)gridDim.x, kFillBlocks);
+    if ((int)blockIdx.x >= nb) return;
+    fill_unused(recv_src_idx, expert_offset, counts, E, cap, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                (int64_t)nb * blockDim.x);
+}
+
 // Final receive row of a packed slot word p from the plan (-1: not selected).
 // A consistent plan gives an expert < E and a row inside the expert's segment
 // and below cap; anything else maps to -1 (a slot past a fixed capacity is
 // dropped), so no access leaves the workspace or the receive buffer.
 __device__ __forceinline__ int final_row(int p, int64_t t, const int32_t* __restrict__ tile_base, int E,
                                          const int32_t* __restrict__ expert_offset, int64_t cap) {
-    if (p < 0) return -1;
+    // the three loads are independent (the expert is clamped into range for
+    // them), so they are issued together
     const int ex = p >> kPackBits;
-    const int lr = p & ((1 << kPackBits) - 1);
-    if (ex >= E) return -1;
-    const int d = expert_offset[ex] + tile_base[(t / kRankTile) * E + ex] + lr;
-    return (d < 0 || d >= cap || d >= expert_offset[ex + 1]) ? -1 : d;
+    const int exc = min(max(ex, 0), E - 1);
+    const int lo = expert_offset[exc], hi = expert_offset[exc + 1];
+    const int tb = tile_base[(t / kRankTile) * E + exc];
+    const int d = lo + tb + (p & ((1 << kPackBits) - 1));
+    return (p < 0 || ex >= E || d < 0 || d >= cap || d >= hi) ? -1 : d;
 }
 
-// One wave per (token, column chunk of U*64 16-byte vectors). With PACKED
+// Small batches (decode): one wave per (token, column chunk of U*64 16-byte
+// vectors) stores its chunk to all K rows, with the plan resolved inline (no
+// finalize launch). With PACKED
 // (dispatch apply) the wave turns the plan's packed slot words into final rows
 // (tile base + rank in tile); the token's chunk-0 wave also records dst_row
 // and recv_src_idx. Without PACKED (cached dispatch) dst_row already holds
 // final rows. Lanes 0..K-1 broadcast the K rows; each lane loads its U
 // vectors once and stores them to every destination row with non-temporal
-// stores. Many short waves in token order keep every CU busy even for a few
-// tokens and keep the writes in flight close together. A row is nvec 16-byte
+// stores. A row is nvec 16-byte
 // vectors of any payload (bf16 rows, or FP8 rows with their scales moved as
 // the side payload by the chunk-0 wave).
 template <int KM, int U, bool PACKED>
-__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t T, int nvec,
+__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(const uint4* __restrict__ x, int64_t T, int nvec,
                                                                       int nchunk, int K, const int32_t* __restrict__ slot,
                                                                       int32_t* __restrict__ dst_row,
                                                                       const int32_t* __restrict__ tile_base, int E,
@@ -339,7 +373,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
                                                                       int64_t cap, uint4* __restrict__ recv_x,
                                                                       SideRows side) {
     const int lane = lane_id();
-    if (PACKED) fill_unused(recv_src_idx, expert_offset, counts, E, cap);
+    if (PACKED) fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t t = g / nchunk;
     if (t >= T) return;
@@ -383,6 +417,67 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_kernel(const uin
     }
 }
 
+// Final rows of every slot (dispatch apply of larger batches): one thread per
+// (token, slot) turns the plan's packed word into the receive row and
+// records dst_row and recv_src_idx; the grid also fills unused rows.
+__global__ __launch_bounds__(256) void finalize_kernel(int64_t T, int K, const int32_t* __restrict__ slot,
+                                                       int32_t* __restrict__ dst_row,
+                                                       const int32_t* __restrict__ tile_base, int E,
+                                                       int32_t* __restrict__ recv_src_idx,
+                                                       const int32_t* __restrict__ expert_offset,
+                                                       const int32_t* __restrict__ counts, int64_t cap) {
+    fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * K) return;
+    const int64_t t = i / K;
+    const int d = final_row(slot[i], t, tile_base, E, expert_offset, cap);
+    dst_row[i] = d;
+    if (d >= 0) recv_src_idx[d] = (int32_t)t;
+}
+
+// Row copy to final rows, one wave per (token, 1 KB column chunk, slot): the
+// wave loads the chunk (64 lanes x 16 bytes) and stores it once, to its
+// slot's receive row, with a non-temporal store. The K waves of a chunk are
+// adjacent (slot fastest), so the chunk comes from HBM once and from L2 for
+// the others. Measured on MI355X, this beats one wave storing its chunk to
+// all K rows by 3-15 % (prefill, Zipf-skewed and large-batch shapes): many
+// short waves that store once and exit keep more stores in flight, spread
+// over more rows, than long waves that issue K stores each. Each wave needs
+// its final row after a single dependent load (dst_row), which keeps the
+// waves short; the plan is resolved beforehand (finalize_kernel). The grid
+// covers tokens [t0, t_end). A row is nvec 16-byte vectors of any payload
+// (bf16 rows, or FP8 rows with their scales moved as the side payload by the
+// chunk-0 wave).
+__global__ __launch_bounds__(kSlotWaves* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t t0,
+                                                                   int64_t t_end, int nvec, int nchunk, int K,
+                                                                   const int32_t* __restrict__ dst_row, int64_t cap,
+                                                                   uint4* __restrict__ recv_x, SideRows side) {
+    const int lane = lane_id();
+    const unsigned wave = __builtin_amdgcn_readfirstlane((unsigned)(threadIdx.x / kWave));
+    const unsigned g = blockIdx.x * (unsigned)kSlotWaves + wave;
+    const unsigned per = (unsigned)(nchunk * K);  // waves per token
+    const unsigned tt = g / per;
+    const int64_t t = t0 + tt;
+    if (t >= t_end) return;
+    const int j = (int)(g - tt * per);
+    const int c = j / K;
+    const int k = j - c * K;
+    const int v = c * kWave + lane;
+    uint4 buf = make_uint4(0, 0, 0, 0);
+    if (v < nvec) buf = x[t * nvec + v];  // issued with the row load
+    // lanes 0..K-1 load the token's rows (per-lane addresses keep the load on
+    // the vector path); the wave keeps row k
+    int dl = -1;
+    if (lane < K) {
+        const int p = dst_row[t * K + lane];
+        dl = (p >= 0 && p < cap) ? p : -1;
+    }
+    const int d = __builtin_amdgcn_readlane(dl, k);
+    if (d < 0) return;
+    if (v < nvec) store_nt(recv_x + (int64_t)d * nvec + v, buf);
+    if (side.src && c == 0) copy_side_row(side, t, d, lane);
+}
+
 // Fused FP8 cast and dispatch apply (bf16 x in, e4m3fn rows and per-block
 // scales out). One wave per (token, chunk of U*64 lanes): each lane holds
 // CPL = 16 channels (two 16-byte bf16 vectors in, one 16-byte code vector
@@ -404,7 +499,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
     constexpr int kVin = kCastCpl / 8;             // 16-byte bf16 vectors per lane
     constexpr int kGroup = kFp8Block / kCastCpl;   // lanes per 128-channel block
     const int lane = lane_id();
-    fill_unused(recv_src_idx, expert_offset, counts, E, cap);
+    fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t t = g / nchunk;
     if (t >= T) return;
@@ -516,19 +611,44 @@ static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
     return w;
 }
 
+// Row copy grids stay below 2^22 blocks (32-bit work-item ids); larger
+// batches are covered by several launches over token ranges.
+constexpr int64_t kMaxScatterBlocks = int64_t(1) << 22;
+// Batches with fewer slots use the broadcast kernel with the plan resolved
+// inline (one launch instead of two: decode latency), and so does top-k above
+// 8: at top-16 (32768 tokens, hidden 4096) the broadcast kernel measured
+// faster than the row copy, whose 16 waves per chunk then cost more than the
+// shorter waves gain.
+constexpr int64_t kRowCopyMinSlots = 16384;
+constexpr int kRowCopyMaxTopk = 8;
+
+static void launch_row_copy(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* dst_row,
+                            int64_t cap, void* recv_x, const SideRows& side) {
+    const int nchunk = (nvec + kWave - 1) / kWave;
+    const int64_t per = (int64_t)nchunk * K;  // waves per token
+    const int64_t tper = std::max<int64_t>(1, kMaxScatterBlocks * kSlotWaves / per);
+    for (int64_t t0 = 0; t0 < T; t0 += tper) {
+        const int64_t nt = std::min<int64_t>(tper, T - t0);
+        const int64_t blocks = (nt * per + kSlotWaves - 1) / kSlotWaves;
+        hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)blocks), dim3(kSlotWaves * kWave), 0, s,
+                           reinterpret_cast<const uint4*>(x), t0, t0 + nt, nvec, nchunk, K, dst_row, cap,
+                           reinterpret_cast<uint4*>(recv_x), side);
+    }
+}
+
 template <bool PACKED, int U>
-static void launch_scatter_u(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
-                             int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
-                             const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
+static void launch_bcast_u(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
+                           int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
+                           const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t waves = T * nchunk;
     const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
     const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint4* rv = reinterpret_cast<uint4*>(recv_x);
-#define CGD_SCATTER(KM)                                                                                            \
-    hipLaunchKernelGGL((scatter_kernel<KM, U, PACKED>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot, dst_row,    \
-                       tile_base, E, src, off, counts, cap, rv, side)
+#define CGD_SCATTER(KM)                                                                                          \
+    hipLaunchKernelGGL((scatter_bcast_kernel<KM, U, PACKED>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot,     \
+                       dst_row, tile_base, E, src, off, counts, cap, rv, side)
     if (K <= 2)
         CGD_SCATTER(2);
     else if (K <= 4)
@@ -540,22 +660,27 @@ static void launch_scatter_u(int64_t T, int K, hipStream_t s, const void* x, int
 #undef CGD_SCATTER
 }
 
-// Chunks of 4 vectors per lane (4 KB per wave) unless that leaves fewer than
-// kMinScatterWaves waves, as for a decode batch: then 1 vector per lane.
-constexpr int64_t kMinScatterWaves = 4096;
-
+// Dispatch apply (PACKED: slot holds the plan's packed words) or cached
+// dispatch (slot is dst_row with final rows). Larger batches: finalize_kernel
+// (PACKED) then the row copy; small ones: the broadcast kernel.
 template <bool PACKED>
 static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
                            int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
                            const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
-    constexpr int U = CGD_SCATTER_U;
-    const int64_t waves = T * ((nvec + U * kWave - 1) / (U * kWave));
-    if (waves >= kMinScatterWaves)
-        launch_scatter_u<PACKED, U>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x,
-                                    side);
-    else
-        launch_scatter_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x,
-                                    side);
+    if (T * K < kRowCopyMinSlots) {
+        launch_bcast_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x, side);
+        return;
+    }
+    if (K > kRowCopyMaxTopk) {
+        launch_bcast_u<PACKED, 4>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x, side);
+        return;
+    }
+    if (PACKED) {
+        const int64_t blocks = (T * K + 255) / 256;
+        hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, T, K, slot, dst_row, tile_base,
+                           E, src, off, counts, cap);
+    }
+    launch_row_copy(T, K, s, x, nvec, PACKED ? dst_row : slot, cap, recv_x, side);
 }
 
 static SideRows no_side() { return SideRows{nullptr, 0, 0, 0, 0, nullptr}; }
@@ -642,6 +767,10 @@ static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E,
         CGD_SCATTER_CAST(16);
 #undef CGD_SCATTER_CAST
 }
+
+// Chunks of U vectors per lane unless that leaves fewer than kMinScatterWaves
+// waves, as for a decode batch: then 1 vector per lane.
+constexpr int64_t kMinScatterWaves = 4096;
 
 #ifndef CGD_SCATTER_CAST_U
 #define CGD_SCATTER_CAST_U 2
