@@ -111,13 +111,19 @@ hipError_t launch_combine(const void* expert_out, int64_t cap, int H, const int3
     const uint4* yv = reinterpret_cast<const uint4*>(expert_out);
     uint4* ov = reinterpret_cast<uint4*>(out);
     const int nvec = H / 8;
+    // token ranges within 32-bit work-item ids; the kernel indexes tokens
+    // relative to the pointers it is given
 #define CGD_COMBINE(KM, U)                                                                                          \
     do {                                                                                                            \
         const int nchunk = (nvec + U * kWave - 1) / (U * kWave);                                                    \
-        const int64_t blocks = (T * nchunk + kCombineWaves - 1) / kCombineWaves;                                    \
-        const dim3 grid((unsigned)blocks), block(kCombineWaves * kWave);                                            \
-        hipLaunchKernelGGL((combine_kernel<KM, U>), grid, block, CGD_COMBINE_LDS_CAP, stream, yv, cap, nvec, nchunk,  \
-                           dst_row, w, T, K, ov);                                                                   \
+        const int64_t tper = tokens_per_launch(nchunk);                                                             \
+        for (int64_t t0 = 0; t0 < T; t0 += tper) {                                                                  \
+            const int64_t nt = T - t0 < tper ? T - t0 : tper;                                                       \
+            const int64_t blocks = (nt * nchunk + kCombineWaves - 1) / kCombineWaves;                               \
+            const dim3 grid((unsigned)blocks), block(kCombineWaves * kWave);                                        \
+            hipLaunchKernelGGL((combine_kernel<KM, U>), grid, block, CGD_COMBINE_LDS_CAP, stream, yv, cap, nvec,    \
+                               nchunk, dst_row + t0 * K, w + t0 * K, nt, K, ov + t0 * nvec);                         \
+        }                                                                                                           \
     } while (0)
     if (K <= 2)
         CGD_COMBINE(2, CGD_COMBINE_U);

@@ -363,21 +363,22 @@ __device__ __forceinline__ int final_row(int p, int64_t t, const int32_t* __rest
 // vectors of any payload (bf16 rows, or FP8 rows with their scales moved as
 // the side payload by the chunk-0 wave).
 template <int KM, int U, bool PACKED>
-__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(const uint4* __restrict__ x, int64_t T, int nvec,
+__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(const uint4* __restrict__ x, int64_t t0, int64_t T, int nvec,
                                                                       int nchunk, int K, const int32_t* __restrict__ slot,
                                                                       int32_t* __restrict__ dst_row,
                                                                       const int32_t* __restrict__ tile_base, int E,
                                                                       int32_t* __restrict__ recv_src_idx,
                                                                       const int32_t* __restrict__ expert_offset,
                                                                       const int32_t* __restrict__ counts,
-                                                                      int64_t cap, uint4* __restrict__ recv_x,
-                                                                      SideRows side) {
+                                                                      int64_t cap, int fill,
+                                                                      uint4* __restrict__ recv_x, SideRows side) {
     const int lane = lane_id();
-    if (PACKED) fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
+    if (PACKED && fill) fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
-    const int64_t t = g / nchunk;
+    const int64_t tr = g / nchunk;
+    const int64_t t = t0 + tr;
     if (t >= T) return;
-    const int c = (int)(g - t * nchunk);
+    const int c = (int)(g - tr * nchunk);
     const int v0 = c * U * kWave;
     const uint4* xr = x + t * nvec;
     uint4 buf[U];  // loaded before the indices arrive
@@ -494,16 +495,17 @@ template <int KM, int U, int FMT>
 __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
     const uint4* __restrict__ x, int64_t T, int nlv, int nchunk, int K, const int32_t* __restrict__ slot,
     int32_t* __restrict__ dst_row, const int32_t* __restrict__ tile_base, int E, int32_t* __restrict__ recv_src_idx,
-    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ counts, int64_t cap,
-    void* __restrict__ recv_q, void* __restrict__ recv_s) {
+    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ counts, int64_t cap, int64_t t0,
+    int fill, void* __restrict__ recv_q, void* __restrict__ recv_s) {
     constexpr int kVin = kCastCpl / 8;             // 16-byte bf16 vectors per lane
     constexpr int kGroup = kFp8Block / kCastCpl;   // lanes per 128-channel block
     const int lane = lane_id();
-    fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
+    if (fill) fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
-    const int64_t t = g / nchunk;
+    const int64_t tr = g / nchunk;
+    const int64_t t = t0 + tr;
     if (t >= T) return;
-    const int c = (int)(g - t * nchunk);
+    const int c = (int)(g - tr * nchunk);
     const int v0 = c * U * kWave;  // first lane vector of the chunk (nlv per row)
     const int nsb = nlv / kGroup;
     const uint4* xr = x + t * (int64_t)nlv * kVin;
@@ -611,9 +613,6 @@ static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
     return w;
 }
 
-// Row copy grids stay below 2^22 blocks (32-bit work-item ids); larger
-// batches are covered by several launches over token ranges.
-constexpr int64_t kMaxScatterBlocks = int64_t(1) << 22;
 // Batches with fewer slots use the broadcast kernel with the plan resolved
 // inline (one launch instead of two: decode latency), and so does top-k above
 // 8: at top-16 (32768 tokens, hidden 4096) the broadcast kernel measured
@@ -626,7 +625,7 @@ static void launch_row_copy(int64_t T, int K, hipStream_t s, const void* x, int 
                             int64_t cap, void* recv_x, const SideRows& side) {
     const int nchunk = (nvec + kWave - 1) / kWave;
     const int64_t per = (int64_t)nchunk * K;  // waves per token
-    const int64_t tper = std::max<int64_t>(1, kMaxScatterBlocks * kSlotWaves / per);
+    const int64_t tper = tokens_per_launch(per);
     for (int64_t t0 = 0; t0 < T; t0 += tper) {
         const int64_t nt = std::min<int64_t>(tper, T - t0);
         const int64_t blocks = (nt * per + kSlotWaves - 1) / kSlotWaves;
@@ -641,23 +640,30 @@ static void launch_bcast_u(int64_t T, int K, hipStream_t s, const void* x, int n
                            int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
                            const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
-    const int64_t waves = T * nchunk;
-    const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
-    const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
+    const int64_t tper = tokens_per_launch(nchunk);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint4* rv = reinterpret_cast<uint4*>(recv_x);
+    const dim3 block(kScatterWaves * kWave);
+    int64_t t0 = 0;
+    do {  // at least one launch: with no token it still fills unused rows
+        const int64_t nt = std::min<int64_t>(tper, T - t0);
+        const int64_t waves = nt * nchunk;
+        const dim3 grid((unsigned)(waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves));
+        const int fill = t0 == 0 ? 1 : 0;
 #define CGD_SCATTER(KM)                                                                                          \
-    hipLaunchKernelGGL((scatter_bcast_kernel<KM, U, PACKED>), grid, block, 0, s, xv, T, nvec, nchunk, K, slot,     \
-                       dst_row, tile_base, E, src, off, counts, cap, rv, side)
-    if (K <= 2)
-        CGD_SCATTER(2);
-    else if (K <= 4)
-        CGD_SCATTER(4);
-    else if (K <= 8)
-        CGD_SCATTER(8);
-    else
-        CGD_SCATTER(16);
+    hipLaunchKernelGGL((scatter_bcast_kernel<KM, U, PACKED>), grid, block, 0, s, xv, t0, t0 + nt, nvec, nchunk, K, \
+                       slot, dst_row, tile_base, E, src, off, counts, cap, fill, rv, side)
+        if (K <= 2)
+            CGD_SCATTER(2);
+        else if (K <= 4)
+            CGD_SCATTER(4);
+        else if (K <= 8)
+            CGD_SCATTER(8);
+        else
+            CGD_SCATTER(16);
 #undef CGD_SCATTER
+        t0 += tper;
+    } while (t0 < T);
 }
 
 // Dispatch apply (PACKED: slot holds the plan's packed words) or cached
@@ -750,22 +756,29 @@ static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E,
                                   void* recv_s, hipStream_t s) {
     const int nlv = H / kCastCpl;
     const int nchunk = (nlv + U * kWave - 1) / (U * kWave);
-    const int64_t waves = T * nchunk;
-    const int64_t blocks = waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves;
-    const dim3 grid((unsigned)blocks), block(kScatterWaves * kWave);
+    const int64_t tper = tokens_per_launch(nchunk);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
+    const dim3 block(kScatterWaves * kWave);
+    int64_t t0 = 0;
+    do {  // at least one launch: with no token it still fills unused rows
+        const int64_t nt = std::min<int64_t>(tper, T - t0);
+        const int64_t waves = nt * nchunk;
+        const dim3 grid((unsigned)(waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves));
+        const int fill = t0 == 0 ? 1 : 0;
 #define CGD_SCATTER_CAST(KM)                                                                                         \
-    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, T, nlv, nchunk, K, w.slot_pack,      \
-                       dst_row, w.tile_base, E, src, off, w.counts, cap, recv_q, recv_s)
-    if (K <= 2)
-        CGD_SCATTER_CAST(2);
-    else if (K <= 4)
-        CGD_SCATTER_CAST(4);
-    else if (K <= 8)
-        CGD_SCATTER_CAST(8);
-    else
-        CGD_SCATTER_CAST(16);
+    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, t0 + nt, nlv, nchunk, K,             \
+                       w.slot_pack, dst_row, w.tile_base, E, src, off, w.counts, cap, t0, fill, recv_q, recv_s)
+        if (K <= 2)
+            CGD_SCATTER_CAST(2);
+        else if (K <= 4)
+            CGD_SCATTER_CAST(4);
+        else if (K <= 8)
+            CGD_SCATTER_CAST(8);
+        else
+            CGD_SCATTER_CAST(16);
 #undef CGD_SCATTER_CAST
+        t0 += tper;
+    } while (t0 < T);
 }
 
 // Chunks of U vectors per lane unless that leaves fewer than kMinScatterWaves

@@ -92,16 +92,22 @@ hipError_t launch_cast_to_fp8(const void* x, int64_t T, int H, void* q, void* sc
     if (T <= 0) return hipSuccess;
     const int nlv = H / kLaneCh;
     const int nchunk = (nlv + kWave - 1) / kWave;
-    const int64_t blocks = (T * nchunk + kCastWaves - 1) / kCastWaves;
-    const dim3 grid((unsigned)blocks), block(kCastWaves * kWave);
-    const uint4* xv = reinterpret_cast<const uint4*>(x);
-    uint4* qv = reinterpret_cast<uint4*>(q);
-    if (fmt == 0)
-        hipLaunchKernelGGL(cast_to_fp8_kernel<0>, grid, block, 0, stream, xv, T, nlv, nchunk, qv, scales, st, sb);
-    else if (fmt == 1)
-        hipLaunchKernelGGL(cast_to_fp8_kernel<1>, grid, block, 0, stream, xv, T, nlv, nchunk, qv, scales, st, sb);
-    else
-        hipLaunchKernelGGL(cast_to_fp8_kernel<2>, grid, block, 0, stream, xv, T, nlv, nchunk, qv, scales, st, sb);
+    const size_t sbytes = fmt == 2 ? 1 : 4;
+    const int64_t tper = tokens_per_launch(nchunk);  // token ranges, pointers offset per range
+    for (int64_t t0 = 0; t0 < T; t0 += tper) {
+        const int64_t nt = T - t0 < tper ? T - t0 : tper;
+        const int64_t blocks = (nt * nchunk + kCastWaves - 1) / kCastWaves;
+        const dim3 grid((unsigned)blocks), block(kCastWaves * kWave);
+        const uint4* xv = reinterpret_cast<const uint4*>(x) + t0 * nlv * 2;
+        uint4* qv = reinterpret_cast<uint4*>(q) + t0 * nlv;
+        void* sc = static_cast<char*>(scales) + (size_t)(t0 * st) * sbytes;
+        if (fmt == 0)
+            hipLaunchKernelGGL(cast_to_fp8_kernel<0>, grid, block, 0, stream, xv, nt, nlv, nchunk, qv, sc, st, sb);
+        else if (fmt == 1)
+            hipLaunchKernelGGL(cast_to_fp8_kernel<1>, grid, block, 0, stream, xv, nt, nlv, nchunk, qv, sc, st, sb);
+        else
+            hipLaunchKernelGGL(cast_to_fp8_kernel<2>, grid, block, 0, stream, xv, nt, nlv, nchunk, qv, sc, st, sb);
+    }
     return hipGetLastError();
 }
 
@@ -110,14 +116,20 @@ hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64
     if (T <= 0) return hipSuccess;
     const int nvec = H / kLaneCh;
     const int nchunk = (nvec + kWave - 1) / kWave;
-    const int64_t blocks = (T * nchunk + kCastWaves - 1) / kCastWaves;
-    const dim3 grid((unsigned)blocks), block(kCastWaves * kWave);
-    const uint4* qv = reinterpret_cast<const uint4*>(q);
-    uint4* ov = reinterpret_cast<uint4*>(out);
-    if (fmt == 2)
-        hipLaunchKernelGGL(cast_back_kernel<2>, grid, block, 0, stream, qv, scales, st, sb, T, nvec, nchunk, ov);
-    else
-        hipLaunchKernelGGL(cast_back_kernel<0>, grid, block, 0, stream, qv, scales, st, sb, T, nvec, nchunk, ov);
+    const size_t sbytes = fmt == 2 ? 1 : 4;
+    const int64_t tper = tokens_per_launch(nchunk);  // token ranges, pointers offset per range
+    for (int64_t t0 = 0; t0 < T; t0 += tper) {
+        const int64_t nt = T - t0 < tper ? T - t0 : tper;
+        const int64_t blocks = (nt * nchunk + kCastWaves - 1) / kCastWaves;
+        const dim3 grid((unsigned)blocks), block(kCastWaves * kWave);
+        const uint4* qv = reinterpret_cast<const uint4*>(q) + t0 * nvec;
+        uint4* ov = reinterpret_cast<uint4*>(out) + t0 * nvec * 2;
+        const void* sc = static_cast<const char*>(scales) + (size_t)(t0 * st) * sbytes;
+        if (fmt == 2)
+            hipLaunchKernelGGL(cast_back_kernel<2>, grid, block, 0, stream, qv, sc, st, sb, nt, nvec, nchunk, ov);
+        else
+            hipLaunchKernelGGL(cast_back_kernel<0>, grid, block, 0, stream, qv, sc, st, sb, nt, nvec, nchunk, ov);
+    }
     return hipGetLastError();
 }
 

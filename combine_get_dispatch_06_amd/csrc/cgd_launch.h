@@ -18,6 +18,14 @@ constexpr int kLayoutTile = 256;
 constexpr int kRankTile = 256;
 constexpr size_t kTicketBytes = 256;  // ticket word, padded to keep arrays 256-B aligned
 
+// Work-item ids of a launch are 32-bit: grids of 64-lane waves stay within
+// 2^31 work-items, and kernels with a wave per (token, chunk) are issued over
+// token ranges of at most this many tokens.
+constexpr int64_t kMaxGridWaves = int64_t(1) << 25;
+inline int64_t tokens_per_launch(int64_t waves_per_token) {
+    return waves_per_token <= 0 ? kMaxGridWaves : (kMaxGridWaves / waves_per_token > 0 ? kMaxGridWaves / waves_per_token : 1);
+}
+
 int64_t layout_blocks(int64_t T);
 size_t layout_workspace_bytes(int64_t T, int E, int R);
 size_t dispatch_workspace_bytes(int64_t T, int K, int E);

@@ -182,9 +182,10 @@ __global__ __launch_bounds__(kNormScatterWaves* kWave) void normal_scatter_kerne
     const int32_t* __restrict__ grp_pre, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ rank_offset,
     int32_t* __restrict__ send_row, int32_t* __restrict__ recv_src_idx, const int64_t* __restrict__ topk_idx,
     const float* __restrict__ topk_w, int K, int E, int L, int64_t* __restrict__ recv_topk_idx,
-    float* __restrict__ recv_topk_w, int64_t cap, uint4* __restrict__ recv_x, SideRows side) {
+    float* __restrict__ recv_topk_w, int64_t cap, int64_t t0, int fill, uint4* __restrict__ recv_x,
+    SideRows side) {
     const int lane = lane_id();
-    if (!CACHED) {
+    if (!CACHED && fill) {
         // rows past the data carry no token, no expert and zero weights
         const int64_t n = max<int64_t>(0, min<int64_t>(rank_offset[R], cap));
         const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -197,9 +198,10 @@ __global__ __launch_bounds__(kNormScatterWaves* kWave) void normal_scatter_kerne
             }
     }
     const int64_t g = (int64_t)blockIdx.x * kNormScatterWaves + threadIdx.x / kWave;
-    const int64_t t = g / nchunk;
+    const int64_t tr = g / nchunk;
+    const int64_t t = t0 + tr;  // T is the end of this launch's token range
     if (t >= T) return;
-    const int c = (int)(g - t * nchunk);
+    const int c = (int)(g - tr * nchunk);
     const int v0 = c * U * kWave;
     const uint4* xr = x + t * nvec;
     uint4 buf[U];  // loaded before the rows are known
@@ -382,13 +384,20 @@ static void launch_normal_scatter_u(const void* x, int64_t T, int nvec, int R, c
                                     int64_t* recv_topk_idx, float* recv_topk_w, int64_t cap, void* recv_x,
                                     const SideRows& side, hipStream_t s) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
-    const int64_t waves = T * nchunk;
-    const int64_t blocks = waves <= 0 ? 1 : (waves + kNormScatterWaves - 1) / kNormScatterWaves;
-    hipLaunchKernelGGL((normal_scatter_kernel<U, CACHED>), dim3((unsigned)blocks), dim3(kNormScatterWaves * kWave), 0,
-                       s, reinterpret_cast<const uint4*>(x), T, nvec, nchunk, R, w ? w->grp_bal : nullptr,
-                       w ? w->grp_pre : nullptr, w ? w->tile_base : nullptr, rank_offset, send_row, recv_src_idx,
-                       topk_idx, topk_w, K, E, R > 0 ? E / R : 1, recv_topk_idx, recv_topk_w, cap,
-                       reinterpret_cast<uint4*>(recv_x), side);
+    const int64_t tper = tokens_per_launch(nchunk);
+    int64_t t0 = 0;
+    do {  // token ranges within 32-bit work-item ids; only the first fills the tail
+        const int64_t nt = T - t0 < tper ? T - t0 : tper;
+        const int64_t waves = nt * nchunk;
+        const int64_t blocks = waves <= 0 ? 1 : (waves + kNormScatterWaves - 1) / kNormScatterWaves;
+        hipLaunchKernelGGL((normal_scatter_kernel<U, CACHED>), dim3((unsigned)blocks),
+                           dim3(kNormScatterWaves * kWave), 0, s, reinterpret_cast<const uint4*>(x), t0 + nt, nvec,
+                           nchunk, R, w ? w->grp_bal : nullptr, w ? w->grp_pre : nullptr,
+                           w ? w->tile_base : nullptr, rank_offset, send_row, recv_src_idx, topk_idx, topk_w, K, E,
+                           R > 0 ? E / R : 1, recv_topk_idx, recv_topk_w, cap, t0, t0 == 0 ? 1 : 0,
+                           reinterpret_cast<uint4*>(recv_x), side);
+        t0 += tper;
+    } while (t0 < T);
 }
 
 template <bool CACHED>
@@ -466,11 +475,17 @@ hipError_t launch_normal_combine(const void* expert_out, int64_t rows, int H, co
     constexpr int U = CGD_NORMAL_COMBINE_U;
     const int nvec = H / 8;
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
-    const int64_t blocks = (T * nchunk + kNormCombineWaves - 1) / kNormCombineWaves;
-    hipLaunchKernelGGL((normal_combine_kernel<U>), dim3((unsigned)blocks), dim3(kNormCombineWaves * kWave),
-                       kNormCombineLds, stream, reinterpret_cast<const uint4*>(expert_out), rows, nvec, nchunk,
-                       send_row, R, T, recv_w, K, reinterpret_cast<const uint4*>(bias0),
-                       reinterpret_cast<const uint4*>(bias1), reinterpret_cast<uint4*>(out), out_w);
+    const int64_t tper = tokens_per_launch(nchunk);
+    for (int64_t t0 = 0; t0 < T; t0 += tper) {  // token ranges; the kernel indexes tokens relative to its pointers
+        const int64_t nt = T - t0 < tper ? T - t0 : tper;
+        const int64_t blocks = (nt * nchunk + kNormCombineWaves - 1) / kNormCombineWaves;
+        const uint4* b0 = bias0 ? reinterpret_cast<const uint4*>(bias0) + t0 * nvec : nullptr;
+        const uint4* b1 = bias1 ? reinterpret_cast<const uint4*>(bias1) + t0 * nvec : nullptr;
+        hipLaunchKernelGGL((normal_combine_kernel<U>), dim3((unsigned)blocks), dim3(kNormCombineWaves * kWave),
+                           kNormCombineLds, stream, reinterpret_cast<const uint4*>(expert_out), rows, nvec, nchunk,
+                           send_row + t0 * R, R, nt, recv_w, K, b0, b1, reinterpret_cast<uint4*>(out) + t0 * nvec,
+                           out_w ? out_w + t0 * K : nullptr);
+    }
     return hipGetLastError();
 }
 

@@ -86,8 +86,9 @@ def _check_rows(recv, q_np, s_np, dst_np):
 
 @pytest.mark.parametrize("fmt,colmajor", [(cgd.SCALE_F32, False), (cgd.SCALE_F32, True), (cgd.SCALE_UE8M0, False),
                                           (cgd.SCALE_UE8M0, True)])
-def test_fp8_tuple_dispatch_and_cached(fmt, colmajor):
-    w = synth.WORKLOADS["prefill"].replace(T=700, H=1024)
+@pytest.mark.parametrize("T", [700, 2500])
+def test_fp8_tuple_dispatch_and_cached(fmt, colmajor, T):
+    w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
     idx = synth.make_topk_idx(w.replace(name="prefill"), seed=2)
     x = _x(w.T, w.H, seed=2)
     q, sc = cgd.per_token_cast_to_fp8(dev_bf16(x), fmt, column_major_scales=colmajor)

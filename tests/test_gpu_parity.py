@@ -103,8 +103,9 @@ def test_workload_parity(name):
     assert frac > 0.99
 
 
-def test_cached_dispatch_matches_fresh_dispatch():
-    w = synth.WORKLOADS["prefill"].replace(T=1000)
+@pytest.mark.parametrize("T", [1000, 2500])
+def test_cached_dispatch_matches_fresh_dispatch(T):
+    w = synth.WORKLOADS["prefill"].replace(T=T)
     inp = synth.make_inputs(w, seed=3)
     x_dev, recv_x, h, o = _dispatch_and_check(w, inp["topk_idx"], inp["x"])
     x2 = synth.make_x(w.replace(name="prefill-second-batch"), seed=3)
@@ -117,8 +118,9 @@ def test_cached_dispatch_matches_fresh_dispatch():
     np.testing.assert_array_equal(g[data], o2["recv_x"][data])
 
 
-def test_plan_then_apply_equals_dispatch():
-    w = synth.WORKLOADS["prefill"].replace(T=1500, H=1024)
+@pytest.mark.parametrize("T", [1500, 2100])
+def test_plan_then_apply_equals_dispatch(T):
+    w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
     inp = synth.make_inputs(w.replace(name="prefill"), seed=9)
     idx, x_np = inp["topk_idx"][:w.T], synth.make_x(w, seed=9)
     plan = cgd.dispatch_plan(dev_i64(idx), w.E, w.R, expert_alignment=4)
@@ -167,6 +169,14 @@ EDGE_CASES = {
     "align32_neg": dict(T=333, K=4, E=64, R=16, H=24, align=32, p_neg=0.2),
     "one_hot_expert": dict(T=2000, K=3, E=64, R=8, H=32, all_to=37),
     "extra_capacity": dict(T=200, K=4, E=32, R=4, H=40, cap_extra=1000),
+    # batches of >= 16384 slots with top-k <= 8 take the finalize + row-copy
+    # apply; the others the single broadcast launch: both sides of the switch
+    "rowcopy_boundary_T=2048": dict(T=2048, K=8, E=32, R=4, H=64, cap_extra=5000),
+    "bcast_boundary_T=2047": dict(T=2047, K=8, E=32, R=4, H=64),
+    "rowcopy_ragged_H=1032_align4_neg": dict(T=2049, K=8, E=256, R=8, H=1032, align=4, p_neg=0.1),
+    "rowcopy_K=5_duplicates": dict(T=4000, K=5, E=64, R=8, H=200, dup=True),
+    "rowcopy_K=1_H=8": dict(T=16385, K=1, E=16, R=4, H=8),
+    "rowcopy_one_hot_expert": dict(T=3000, K=6, E=64, R=8, H=72, all_to=5),
 }
 
 
@@ -276,3 +286,40 @@ def test_layout_and_plan_in_one_launch(case):
     np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), d["expert_offset"])
     np.testing.assert_array_equal(h.dst_row.cpu().numpy(), d["dst_row"])
     np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), d["recv_src_idx"])
+
+
+def test_launches_split_over_token_ranges():
+    """Batches larger than one grid (work-item ids are 32-bit: 2^25 waves per
+    launch) are issued over token ranges. At hidden 8 and top-1 a token is
+    one wave of the row copy, the combine, the rank-granular scatter and its
+    combine, so 2^25 + 4099 tokens take two launches of each. Positions must
+    match the oracle, every received row its token's row, and both combines
+    of identity experts must return x."""
+    T, K, E, R, H = (1 << 25) + 4099, 1, 16, 4, 8
+    say(f"[parity] split launches: T={T} K={K} H={H}")
+    idx = synth.topk_uniform(synth.stream_key(5, 123, 2), T, K, E)
+    x = synth.normal_bf16(synth.stream_key(5, 123, 1), T * H).reshape(T, H)
+    x_dev = dev_bf16(x)
+    idx_dev = dev_i64(idx)
+    recv_x, h = cgd.dispatch(x_dev, idx_dev, E, R)
+    torch.cuda.synchronize()
+    o = oracle.dispatch(None, idx, E, R, with_rows=False)
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    rows = torch.from_numpy(o["dst_row"].reshape(-1).astype(np.int64)).to(DEV)
+    assert torch.equal(recv_x.view(torch.int64).view(-1, 2).index_select(0, rows), x_dev.view(torch.int64).view(T, 2))
+    del rows
+    ones = torch.ones((T, K), dtype=torch.float32, device=DEV)
+    assert torch.equal(cgd.combine(recv_x, h, ones).view(torch.int16), x_dev.view(torch.int16))
+    del recv_x, h
+    say("[parity] split launches: expert path ok")
+    ntpr, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx_dev, E, R)
+    nrecv, _, _, _, nh = cgd.normal_dispatch(x_dev, itr, ntpe, num_experts=E, num_topk=K)
+    torch.cuda.synchronize()
+    on = oracle.dispatch_normal(None, itr.cpu().numpy(), E, K)
+    np.testing.assert_array_equal(nh.send_row.cpu().numpy(), on["send_row"])
+    np.testing.assert_array_equal(nh.recv_src_idx.cpu().numpy(), on["recv_src_idx"])
+    back, _ = cgd.normal_combine(nrecv, nh)
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), x_dev.view(torch.int16))
+    say("[parity] split launches: rank-granular path ok")
