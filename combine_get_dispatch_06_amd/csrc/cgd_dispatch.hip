@@ -302,37 +302,39 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
 // only its segment's bounds, whatever the grid size.
 __device__ __forceinline__ void fill_unused(int32_t* __restrict__ recv_src_idx,
                                             const int32_t* __restrict__ expert_offset,
-                                            const int32_t* __restrict__ counts, int E, int64_t cap, int64_t gid,
-                                            int64_t nth) {
-    const int64_t end = max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
-    if (nth >= E) {
-        const int64_t per = nth / E;  // threads per segment
-        if (gid < per * E) {
-            const int e = (int)(gid % E);
-            const int64_t lo = max<int64_t>(0, (int64_t)expert_offset[e] + max(counts[e], 0));
-            const int64_t hi = min<int64_t>(expert_offset[e + 1], end);
-            for (int64_t r = lo + gid / E; r < hi; r += per) recv_src_idx[r] = -1;
+                                            const int32_t* __restrict__ counts, int E, int64_t cap, uint32_t gid,
+                                            uint32_t nth) {
+    // 32-bit arithmetic: rows < cap <= INT32_MAX, thread ids < 2^32
+    const uint32_t end = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
+    if (nth >= (uint32_t)E) {
+        const uint32_t per = nth / (uint32_t)E;  // threads per segment
+        const uint32_t seg = gid / per;
+        if (seg < (uint32_t)E) {
+            const uint32_t lo = (uint32_t)max(0, expert_offset[seg] + max(counts[seg], 0));
+            const uint32_t hi = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[seg + 1], end));  // <= cap
+            for (uint32_t r = lo + (gid - seg * per); r < hi; r += per) recv_src_idx[r] = -1;
         }
     } else {
-        for (int64_t e = gid; e < E; e += nth) {
-            const int64_t lo = max<int64_t>(0, (int64_t)expert_offset[e] + max(counts[e], 0));
-            const int64_t hi = min<int64_t>(expert_offset[e + 1], end);
-            for (int64_t r = lo; r < hi; ++r) recv_src_idx[r] = -1;
+        for (uint32_t e = gid; e < (uint32_t)E; e += nth) {
+            const uint32_t lo = (uint32_t)max(0, expert_offset[e] + max(counts[e], 0));
+            const uint32_t hi = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[e + 1], end));
+            for (uint32_t r = lo; r < hi; ++r) recv_src_idx[r] = -1;
         }
     }
-    for (int64_t r = end + gid; r < cap; r += nth) recv_src_idx[r] = -1;
+    for (int64_t r = (int64_t)end + gid; r < cap; r += nth) recv_src_idx[r] = -1;
 }
 
-// The first kFillBlocks blocks of an apply grid (all of a smaller grid) do the fill.
+// The first max_blocks blocks of an apply grid (all of a smaller grid) do the fill.
 constexpr int kFillBlocks = 1024;
 
 __device__ __forceinline__ void fill_unused_grid(int32_t* __restrict__ recv_src_idx,
                                                  const int32_t* __restrict__ expert_offset,
-                                                 const int32_t* __restrict__ counts, int E, int64_t cap) {
-    const int nb = min((int)gridDim.x, kFillBlocks);
+                                                 const int32_t* __restrict__ counts, int E, int64_t cap,
+                                                 int max_blocks = kFillBlocks) {
+    const int nb = min((int)gridDim.x, max_blocks);
     if ((int)blockIdx.x >= nb) return;
-    fill_unused(recv_src_idx, expert_offset, counts, E, cap, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
-                (int64_t)nb * blockDim.x);
+    fill_unused(recv_src_idx, expert_offset, counts, E, cap, blockIdx.x * blockDim.x + threadIdx.x,
+                (uint32_t)nb * blockDim.x);
 }
 
 // Final receive row of a packed slot word p from the plan (-1: not selected).
@@ -420,14 +422,15 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(con
 
 // Final rows of every slot (dispatch apply of larger batches): one thread per
 // (token, slot) turns the plan's packed word into the receive row and
-// records dst_row and recv_src_idx; the grid also fills unused rows.
+// records dst_row and recv_src_idx; the whole grid (sized for the receive
+// capacity as well) also fills unused rows.
 __global__ __launch_bounds__(256) void finalize_kernel(int64_t T, int K, const int32_t* __restrict__ slot,
                                                        int32_t* __restrict__ dst_row,
                                                        const int32_t* __restrict__ tile_base, int E,
                                                        int32_t* __restrict__ recv_src_idx,
                                                        const int32_t* __restrict__ expert_offset,
                                                        const int32_t* __restrict__ counts, int64_t cap) {
-    fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
+    fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap, (int)gridDim.x);  // the whole grid fills
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= T * K) return;
     const int64_t t = i / K;
@@ -682,7 +685,8 @@ static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int n
         return;
     }
     if (PACKED) {
-        const int64_t blocks = (T * K + 255) / 256;
+        // a thread per slot; enough threads for the fill of a large fixed capacity too
+        const int64_t blocks = std::max<int64_t>((T * K + 255) / 256, std::min<int64_t>((cap + 255) / 256, 16384));
         hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, T, K, slot, dst_row, tile_base,
                            E, src, off, counts, cap);
     }

@@ -112,7 +112,8 @@ def test_fp8_tuple_dispatch_and_cached(fmt, colmajor, T):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T,K,E,R,H,p_neg", [(1, 8, 256, 8, 7168, 0.0), (700, 8, 256, 8, 1024, 0.0),
                                              (333, 4, 64, 16, 384, 0.2), (2000, 16, 512, 64, 256, 0.05),
-                                             (64, 1, 8, 2, 128, 0.0)])
+                                             (64, 1, 8, 2, 128, 0.0), (2100, 8, 64, 8, 384, 0.1),
+                                             (3000, 6, 96, 12, 1152, 0.0)])
 def test_cast_on_dispatch_parity(fmt, T, K, E, R, H, p_neg):
     rng = np.random.default_rng(T + K)
     idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)

@@ -71,8 +71,9 @@ def test_packed_workload_parity(name, cap):
     say(f"[packed] {name}: ok")
 
 
-def test_packed_fp8_cast():
-    w = synth.WORKLOADS["decode"]
+@pytest.mark.parametrize("T,H", [(128, 7168), (2500, 1024)])
+def test_packed_fp8_cast(T, H):
+    w = synth.WORKLOADS["decode"].replace(T=T, H=H)
     inp = synth.make_inputs(w, seed=1)
     for fmt in (cgd.SCALE_F32, cgd.SCALE_UE8M0):
         (q, sc), count, h = cgd.low_latency_dispatch(dev_bf16(inp["x"]), dev_i64(inp["topk_idx"]), w.E, w.R,
