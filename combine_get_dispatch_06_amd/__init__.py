@@ -43,7 +43,7 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
            "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
-           "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan"]
+           "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -140,6 +140,8 @@ def load():
     lib.cgd_normal_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
     lib.cgd_normal_combine.restype = i32
     lib.cgd_normal_combine.argtypes = [vp, i64, i32, vp, i64, i32, vp, i32, vp, vp, vp, vp, vp]
+    lib.cgd_copy.restype = i32
+    lib.cgd_copy.argtypes = [vp, vp, i64, vp]
     _lib = lib
     return lib
 
@@ -253,6 +255,20 @@ def per_token_cast_back(x, scale_format: int | None = None, out: torch.Tensor | 
         _dev_tensor(out, "out", torch.bfloat16, 2)
         _check("cgd_cast_back", lib.cgd_cast_back(_ptr(q), _ptr(sc), st, sb, fmt, T, H, _ptr(out), _stream(dev)))
     return out
+
+
+def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
+    """dst <- src bitwise with libcgd's plain 16-byte copy (the measured copy
+    ceiling); contiguous device tensors of the same byte size."""
+    lib = load()
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous device tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    with torch.cuda.device(src.device):
+        _check("cgd_copy", lib.cgd_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
+    return dst
 
 
 def dispatch_capacity(num_tokens: int, num_topk: int, num_experts: int, expert_alignment: int = 1) -> int:

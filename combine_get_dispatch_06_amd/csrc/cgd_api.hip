@@ -456,6 +456,16 @@ int cgd_cast_to_fp8(const void* x, int64_t num_tokens, int hidden, void* x_fp8, 
     return CGD_OK;
 }
 
+int cgd_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+    if (bytes < 0 || bytes % 16 != 0) return fail(CGD_ERR_INVALID_ARG, "bytes must be a non-negative multiple of 16");
+    if (bytes == 0) return CGD_OK;
+    if (!src || !dst) return fail(CGD_ERR_INVALID_ARG, "null src or dst");
+    if (!aligned(src, 16) || !aligned(dst, 16)) return fail(CGD_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    hipError_t err = cgd::launch_copy(src, dst, bytes, stream);
+    if (err != hipSuccess) return hip_fail(err, "copy launch");
+    return CGD_OK;
+}
+
 int cgd_cast_back(const void* x_fp8, const void* x_scales, int64_t scale_stride_token, int64_t scale_stride_block,
                   int scale_format, int64_t num_tokens, int hidden, void* out, hipStream_t stream) {
     if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");

@@ -79,6 +79,9 @@ hipError_t launch_normal_combine(const void* expert_out, int64_t rows, int H, co
 hipError_t launch_cast_to_fp8(const void* x, int64_t T, int H, void* q, void* scales, int64_t st, int64_t sb, int fmt,
                               hipStream_t stream);
 
+// Plain 16-byte copy of `bytes` (a multiple of 16).
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64_t sb, int fmt, int64_t T, int H,
                             void* out, hipStream_t stream);
 

@@ -391,6 +391,20 @@ int cgd_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, 
                                  int32_t* cumulative_recv_stats, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* -------------------------------------------------------------------------
+ * cgd_copy: dst[0, bytes) = src[0, bytes), bitwise.
+ * Not an operation of the method: a measured copy ceiling, reported beside
+ * the spec peak that the dispatch and combine bandwidths are measured
+ * against, with the data kernels' memory policy (16-byte non-temporal loads
+ * and stores, one store per lane).
+ *   src, dst  device pointers, 16-byte aligned, not overlapping; may be NULL
+ *             when bytes == 0
+ *   bytes     >= 0, a multiple of 16
+ * Errors: CGD_ERR_INVALID_ARG (negative or unaligned size, misaligned or
+ * null pointer), CGD_ERR_HIP (launch failure). Only enqueues on stream.
+ * ------------------------------------------------------------------------- */
+int cgd_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

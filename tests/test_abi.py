@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
         "cgd_normal_dispatch_plan", "cgd_normal_dispatch_apply", "cgd_cast_to_fp8", "cgd_cast_back",
         "cgd_dispatch_apply_fp8", "cgd_dispatch_apply_cast_fp8", "cgd_dispatch_cached_fp8",
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
-        "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan",
+        "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
     ])
 
 
@@ -300,3 +300,13 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
     assert "oracle" not in open(HEADER).read().lower()
+
+
+def test_copy_rejects_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    assert lib.cgd_copy(f, f, 24, None) == -1              # not a multiple of 16
+    assert lib.cgd_copy(f, f, -16, None) == -1
+    assert lib.cgd_copy(None, f, 32, None) == -1
+    assert lib.cgd_copy(f, _vp(FAKE + 8), 32, None) == -1  # misaligned
+    assert lib.cgd_copy(None, None, 0, None) == 0          # nothing to copy: nothing enqueued

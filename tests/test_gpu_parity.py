@@ -323,3 +323,12 @@ def test_launches_split_over_token_ranges():
     torch.cuda.synchronize()
     assert torch.equal(back.view(torch.int16), x_dev.view(torch.int16))
     say("[parity] split launches: rank-granular path ok")
+
+
+@pytest.mark.parametrize("nbytes", [16, 1 << 20 | 16, 64 << 20])
+def test_copy_is_bitwise(nbytes):
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=DEV)
+    dst = torch.zeros_like(src)
+    cgd.copy_(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
