@@ -225,14 +225,17 @@ __device__ __forceinline__ bool last_block_done(unsigned int* ticket) { return l
 // per token (1 for R <= 64, 6 for R <= 384).
 
 // Bitmask of the ranks the token's selected experts live on (e[k] < 0: none).
+// lshift >= 0: L = 2^lshift experts per rank, the rank is a shift; else the
+// expert -> rank table in LDS.
 template <int RW>
-__device__ __forceinline__ void token_rank_mask(const int (&e)[kMaxTopk], const int16_t* s_rank_of, uint64_t (&m)[RW]) {
+__device__ __forceinline__ void token_rank_mask(const int (&e)[kMaxTopk], const int16_t* s_rank_of, int lshift,
+                                                uint64_t (&m)[RW]) {
 #pragma unroll
     for (int w = 0; w < RW; ++w) m[w] = 0;
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) {
         if (e[k] >= 0) {
-            const int r = s_rank_of[e[k]];
+            const int r = lshift >= 0 ? (e[k] >> lshift) : (int)s_rank_of[e[k]];
 #pragma unroll
             for (int w = 0; w < RW; ++w)
                 if ((r >> 6) == w) m[w] |= 1ull << (r & 63);
@@ -260,17 +263,49 @@ __device__ __forceinline__ void count_rank_tokens(const uint64_t (&m)[RW], int R
     }
 }
 
+// Four rank flags (bits 0..3 of b) as four 0/1 bytes of a little-endian word:
+// the multiplier puts bit i at bit 8i, the mask keeps those bits.
+__device__ __forceinline__ uint32_t flag_bytes4(uint32_t b) { return ((b & 0xFu) * 0x00204081u) & 0x01010101u; }
+
 // The tile's is_token_in_rank rows (nt tokens, a contiguous byte range
-// starting at out, 16-byte aligned) from the masks in s_mask, 16 bytes per
-// store; call after a barrier that follows count_rank_tokens.
+// starting at out, 16-byte aligned). R % 4 == 0, R = 1 or R = 2: each thread
+// stores its own token's row from its mask m (the widest aligned stores);
+// other R: 16 bytes per store across token boundaries from the masks in
+// s_mask (call after a barrier that follows count_rank_tokens).
 template <int RW>
-__device__ __forceinline__ void store_token_in_rank(const uint64_t* s_mask, int nt, int R, uint8_t* out) {
-    const int64_t nbytes = (int64_t)nt * R;
-    for (int64_t c = threadIdx.x; c * 16 < nbytes; c += blockDim.x) {
-        const int64_t b0 = c * 16;
-        int tok = (int)(b0 / R);
-        int r = (int)(b0 - (int64_t)tok * R);
-        const int nb = (int)min<int64_t>(16, nbytes - b0);
+__device__ __forceinline__ void store_token_in_rank(const uint64_t (&m)[RW], const uint64_t* s_mask, int nt, int R,
+                                                    uint8_t* out) {
+    if (R % 4 == 0 || R <= 2) {
+        const int t = threadIdx.x;
+        if (t >= nt) return;
+        uint8_t* row = out + t * R;
+        auto bits4 = [&](int p) {  // flags of ranks p..p+3 (p % 4 == 0: never straddles a word)
+            uint64_t w = 0;
+#pragma unroll
+            for (int i = 0; i < RW; ++i)
+                if ((p >> 6) == i) w = m[i];
+            return flag_bytes4((uint32_t)(w >> (p & 63)));
+        };
+        if (R % 16 == 0) {
+            for (int p = 0; p < R; p += 16)
+                *reinterpret_cast<uint4*>(row + p) = make_uint4(bits4(p), bits4(p + 4), bits4(p + 8), bits4(p + 12));
+        } else if (R % 8 == 0) {
+            for (int p = 0; p < R; p += 8) *reinterpret_cast<uint2*>(row + p) = make_uint2(bits4(p), bits4(p + 4));
+        } else if (R % 4 == 0) {
+            for (int p = 0; p < R; p += 4) *reinterpret_cast<uint32_t*>(row + p) = bits4(p);
+        } else if (R == 2) {
+            *reinterpret_cast<uint16_t*>(row) = (uint16_t)bits4(0);
+        } else {
+            row[0] = (uint8_t)bits4(0);
+        }
+        return;
+    }
+    const int nbytes = nt * R;  // <= 256 * 384
+    for (int c = threadIdx.x; c * 16 < nbytes; c += blockDim.x) {
+        const int b0 = c * 16;
+        int tok = b0 / R;
+        int r = b0 - tok * R;
+        const int nb = min(16, nbytes - b0);
         uint32_t wd[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {

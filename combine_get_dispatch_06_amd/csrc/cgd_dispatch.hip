@@ -142,19 +142,27 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     // Each wave sets one bit per (expert, lane) in a 64-bit LDS mask per
     // expert. The previous mask returned by the atomic also tells whether this
     // token already holds the expert in an earlier slot.
+    // all K atomics are issued before any result is used (an unselected slot
+    // ORs 0 into a word of its wave's row); the results follow together
+    uint64_t prev[kMaxTopk];
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) {
+        prev[k] = 0;
+        if (k < K) prev[k] = atomicOr(&s_tok[wave * E + max(e[k], 0)], e[k] >= 0 ? bit : 0ull);
+    }
     bool dup = false;
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k)
-        if (e[k] >= 0) dup |= (atomicOr(&s_tok[wave * E + e[k]], bit) & bit) != 0;
+    for (int k = 0; k < kMaxTopk; ++k) dup |= e[k] >= 0 && (prev[k] & bit) != 0;
+    uint64_t m[RW];
     if (LAYOUT) {
-        uint64_t m[RW];
-        token_rank_mask<RW>(e, s_rank_of, m);
+        const int lshift = (lo.L & (lo.L - 1)) == 0 ? __builtin_ctz(lo.L) : -1;
+        token_rank_mask<RW>(e, s_rank_of, lshift, m);
         count_rank_tokens<RW>(m, lo.R, s_rank, s_mask);
     }
     const bool any_dup = __syncthreads_or(dup);
     if (LAYOUT) {
         // t0*R is a multiple of 16 because kRankTile is
-        store_token_in_rank<RW>(s_mask, nt, lo.R, lo.itr + t0 * lo.R);
+        store_token_in_rank<RW>(m, s_mask, nt, lo.R, lo.itr + t0 * lo.R);
         for (int r = tid; r < lo.R; r += kRankTile) lo.rank_part[(int64_t)tile * lo.R + r] = s_rank[r];
     }
     if (!any_dup) {

@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     __shared__ int16_t s_rank_of[kMaxExperts];  // rank owning expert e
 
     const int tid = threadIdx.x;
+    const int lshift = (L & (L - 1)) == 0 ? __builtin_ctz(L) : -1;  // power-of-two experts per rank: a shift
     const int64_t t0 = (int64_t)blockIdx.x * kLayoutTile;
     const int nt = (int)max<int64_t>(0, min<int64_t>(kLayoutTile, T - t0));
 
@@ -54,12 +55,12 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     for (int k = 0; k < kMaxTopk; ++k)
         if (e[k] >= 0) atomicAdd(&s_hist[e[k]], 1);
     uint64_t m[RW];
-    token_rank_mask<RW>(e, s_rank_of, m);
+    token_rank_mask<RW>(e, s_rank_of, lshift, m);
     count_rank_tokens<RW>(m, R, s_rank, s_mask);
     __syncthreads();
     // is_token_in_rank rows of this tile: t0*R is a multiple of 16 because
     // kLayoutTile is
-    store_token_in_rank<RW>(s_mask, nt, R, itr + t0 * R);
+    store_token_in_rank<RW>(m, s_mask, nt, R, itr + t0 * R);
 
     if (gridDim.x == 1) {
         for (int i = tid; i < E; i += kLayoutTile) ntpe[i] = s_hist[i];
