@@ -223,8 +223,16 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
     if ((rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x, expert_offset,
                                recv_src_idx, dst_row, workspace, workspace_bytes)))
         return rc;
-    hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
-                                               expert_offset, workspace, stream);
+    hipError_t err;
+    if (cgd::dispatch_fuses(num_tokens)) {  // one tile: plan and apply in one launch
+        err = cgd::launch_dispatch_fused(x, num_tokens, hidden, topk_idx, num_topk, num_experts, expert_alignment,
+                                         recv_x, recv_capacity, expert_offset, recv_src_idx, dst_row, workspace,
+                                         stream);
+        if (err != hipSuccess) return hip_fail(err, "fused dispatch launch");
+        return CGD_OK;
+    }
+    err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment, expert_offset,
+                                    workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     err = cgd::launch_dispatch_apply(x, num_tokens, hidden, num_topk, num_experts, recv_x, recv_capacity,
                                      expert_offset, recv_src_idx, dst_row, workspace, stream);

@@ -84,6 +84,47 @@ __device__ __forceinline__ int slot_expert(int v) { return v < 0 ? -1 : (v & 0xF
 // is_token_in_rank rows per tile, per-tile distinct-token counts per rank
 // (rank_part, workspace) summed by the last block into ntpr, and ntpe = the
 // column totals of the tile histograms.
+// recv_src_idx = -1 for every row that holds no data: rows of segment e past
+// its count (alignment padding, unused fixed capacity) and rows past the last
+// segment. Threads are spread over (segment, row) pairs, so each thread needs
+// only its segment's bounds, whatever the grid size.
+__device__ __forceinline__ void fill_unused(int32_t* __restrict__ recv_src_idx,
+                                            const int32_t* __restrict__ expert_offset,
+                                            const int32_t* __restrict__ counts, int E, int64_t cap, uint32_t gid,
+                                            uint32_t nth) {
+    // 32-bit arithmetic: rows < cap <= INT32_MAX, thread ids < 2^32
+    const uint32_t end = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
+    if (nth >= (uint32_t)E) {
+        const uint32_t per = nth / (uint32_t)E;  // threads per segment
+        const uint32_t seg = gid / per;
+        if (seg < (uint32_t)E) {
+            const uint32_t lo = (uint32_t)max(0, expert_offset[seg] + max(counts[seg], 0));
+            const uint32_t hi = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[seg + 1], end));  // <= cap
+            for (uint32_t r = lo + (gid - seg * per); r < hi; r += per) recv_src_idx[r] = -1;
+        }
+    } else {
+        for (uint32_t e = gid; e < (uint32_t)E; e += nth) {
+            const uint32_t lo = (uint32_t)max(0, expert_offset[e] + max(counts[e], 0));
+            const uint32_t hi = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[e + 1], end));
+            for (uint32_t r = lo; r < hi; ++r) recv_src_idx[r] = -1;
+        }
+    }
+    for (int64_t r = (int64_t)end + gid; r < cap; r += nth) recv_src_idx[r] = -1;
+}
+
+// The first max_blocks blocks of an apply grid (all of a smaller grid) do the fill.
+constexpr int kFillBlocks = 1024;
+
+__device__ __forceinline__ void fill_unused_grid(int32_t* __restrict__ recv_src_idx,
+                                                 const int32_t* __restrict__ expert_offset,
+                                                 const int32_t* __restrict__ counts, int E, int64_t cap,
+                                                 int max_blocks = kFillBlocks) {
+    const int nb = min((int)gridDim.x, max_blocks);
+    if ((int)blockIdx.x >= nb) return;
+    fill_unused(recv_src_idx, expert_offset, counts, E, cap, blockIdx.x * blockDim.x + threadIdx.x,
+                (uint32_t)nb * blockDim.x);
+}
+
 struct LayoutOut {
     int R, L;
     int32_t* ntpr;
@@ -92,7 +133,26 @@ struct LayoutOut {
     int32_t* rank_part;
 };
 
-template <int RW, bool LAYOUT>
+// Row copy of the FUSED form (plan and apply of a one-tile batch in one
+// launch): the grid's waves take the (token, 1 KB chunk) items of x in turn,
+// at most kFusedItems each, and move them to the tokens' receive rows.
+constexpr int kFusedItems = 4;
+struct FusedCopy {
+    const uint4* x;
+    int nvec, nchunk;
+    uint4* recv_x;
+    int32_t* dst_row;
+    int32_t* recv_src_idx;
+    int64_t cap;
+};
+
+// FUSED (batches of at most one tile, e.g. decode): every block plans the
+// whole batch in LDS (the plan is a few microseconds of LDS work, cheaper
+// than a second launch and a second pass over the plan), block 0 alone writes
+// the plan's outputs, and each wave then moves one (token, chunk) item to the
+// token's rows, its x chunk loaded at the start; dst_row and recv_src_idx
+// hold final rows and every block fills a share of the unused rows.
+template <int RW, bool LAYOUT, bool FUSED = false>
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
                                                          int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
                                                          int32_t* __restrict__ tile_base,
@@ -100,21 +160,39 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ packed_count,
                                                          int32_t* __restrict__ stats,
-                                                         unsigned int* __restrict__ ticket, LayoutOut lo) {
+                                                         unsigned int* __restrict__ ticket, LayoutOut lo,
+                                                         FusedCopy fc) {
     extern __shared__ __align__(16) char lds[];
     unsigned long long* s_tok = reinterpret_cast<unsigned long long*>(lds);
     int32_t* s_pre = reinterpret_cast<int32_t*>(s_tok + kRankWaves * E);
     int32_t* s_slot = s_pre + kRankWaves * E;
     int32_t* s_off = s_slot + kRankTile * K;
     int32_t* s_wsum = s_off + E + 1;
-    const int tile = blockIdx.x;
-    const int ntiles = gridDim.x;
+    const int tile = FUSED ? 0 : blockIdx.x;
+    const int ntiles = FUSED ? 1 : gridDim.x;
+    const bool writer = !FUSED || blockIdx.x == 0;  // writes the plan's outputs
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = lane_id();
     const int64_t t0 = (int64_t)tile * kRankTile;
     const int nt = (int)max<int64_t>(0, min<int64_t>(kRankTile, T - t0));
+
+    // FUSED: this wave's items, their x chunks loaded before the plan
+    int64_t ft[kFusedItems];
+    int fv[kFusedItems];
+    uint4 fbuf[kFusedItems];
+    if (FUSED) {
+        const int64_t w0 = (int64_t)blockIdx.x * kRankWaves + __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int j = 0; j < kFusedItems; ++j) {
+            const int64_t item = w0 + (int64_t)j * gridDim.x * kRankWaves;
+            ft[j] = item / fc.nchunk;
+            fv[j] = (int)(item - ft[j] * fc.nchunk) * kWave + lane;
+            fbuf[j] = make_uint4(0, 0, 0, 0);
+            if (ft[j] < T && fv[j] < fc.nvec) fbuf[j] = fc.x[ft[j] * fc.nvec + fv[j]];
+        }
+    }
 
     for (int i = tid; i < kRankWaves * E; i += kRankTile) {
         s_tok[i] = 0ull;
@@ -160,7 +238,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         count_rank_tokens<RW>(m, lo.R, s_rank, s_mask);
     }
     const bool any_dup = __syncthreads_or(dup);
-    if (LAYOUT) {
+    if (LAYOUT && writer) {
         // t0*R is a multiple of 16 because kRankTile is
         store_token_in_rank<RW>(m, s_mask, nt, lo.R, lo.itr + t0 * lo.R);
         for (int r = tid; r < lo.R; r += kRankTile) lo.rank_part[(int64_t)tile * lo.R + r] = s_rank[r];
@@ -231,7 +309,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     }
 
     __syncthreads();
-    {
+    if (!FUSED) {
         int32_t* out = slot_pack + t0 * K;
         const int n = nt * K;
         for (int i = tid; i < n; i += kRankTile) out[i] = s_slot[i];
@@ -242,10 +320,12 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         // no other block has to be waited for
         for (int x = tid; x < E; x += kRankTile) {
             s_pre[x] = s_off[x];
-            tile_base[x] = 0;
-            if (LAYOUT) lo.ntpe[x] = s_off[x];
+            if (writer) {
+                if (!FUSED) tile_base[x] = 0;
+                if (LAYOUT) lo.ntpe[x] = s_off[x];
+            }
         }
-        if (LAYOUT)
+        if (LAYOUT && writer)
             for (int r = tid; r < lo.R; r += kRankTile) lo.ntpr[r] = s_rank[r];
     } else {
     if (!last_block_done(ticket)) return;
@@ -290,7 +370,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     if (seg_cap >= 0) {
         // fixed-capacity segments
         for (int x = tid; x <= E; x += kRankTile) s_off[x] = x * seg_cap;
-        for (int x = tid; x < E; x += kRankTile) {
+        for (int x = tid; x < E && writer; x += kRankTile) {
             const int placed = min(s_pre[x], seg_cap);
             if (packed_count) packed_count[x] = placed;
             if (stats) stats[x] += placed;
@@ -300,49 +380,42 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         block_exclusive_scan2(E, [&](int x) { return (s_pre[x] + A - 1) / A * A; }, s_off, s_wsum);
     }
     __syncthreads();
-    for (int x = tid; x < E; x += kRankTile) counts[x] = s_pre[x];
-    for (int x = tid; x <= E; x += kRankTile) expert_offset[x] = s_off[x];
-}
+    if (writer) {
+        for (int x = tid; x < E; x += kRankTile) counts[x] = s_pre[x];
+        for (int x = tid; x <= E; x += kRankTile) expert_offset[x] = s_off[x];
+    }
+    if (!FUSED) return;
 
-// recv_src_idx = -1 for every row that holds no data: rows of segment e past
-// its count (alignment padding, unused fixed capacity) and rows past the last
-// segment. Threads are spread over (segment, row) pairs, so each thread needs
-// only its segment's bounds, whatever the grid size.
-__device__ __forceinline__ void fill_unused(int32_t* __restrict__ recv_src_idx,
-                                            const int32_t* __restrict__ expert_offset,
-                                            const int32_t* __restrict__ counts, int E, int64_t cap, uint32_t gid,
-                                            uint32_t nth) {
-    // 32-bit arithmetic: rows < cap <= INT32_MAX, thread ids < 2^32
-    const uint32_t end = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[E], cap));
-    if (nth >= (uint32_t)E) {
-        const uint32_t per = nth / (uint32_t)E;  // threads per segment
-        const uint32_t seg = gid / per;
-        if (seg < (uint32_t)E) {
-            const uint32_t lo = (uint32_t)max(0, expert_offset[seg] + max(counts[seg], 0));
-            const uint32_t hi = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[seg + 1], end));  // <= cap
-            for (uint32_t r = lo + (gid - seg * per); r < hi; r += per) recv_src_idx[r] = -1;
-        }
-    } else {
-        for (uint32_t e = gid; e < (uint32_t)E; e += nth) {
-            const uint32_t lo = (uint32_t)max(0, expert_offset[e] + max(counts[e], 0));
-            const uint32_t hi = (uint32_t)max<int64_t>(0, min<int64_t>(expert_offset[e + 1], end));
-            for (uint32_t r = lo; r < hi; ++r) recv_src_idx[r] = -1;
+    // ---- FUSED: final rows, unused rows, then this wave's item ----
+    if (mine) {
+        for (int k = 0; k < K; ++k) {
+            const int v = my[k];
+            int d = -1;
+            if (v >= 0) {
+                const int ex = v >> kPackBits, r = v & ((1 << kPackBits) - 1);
+                d = seg_cap >= 0 ? (r < seg_cap ? ex * seg_cap + r : -1) : s_off[ex] + r;
+                if (d >= fc.cap) d = -1;
+            }
+            my[k] = d;
+            if (writer) {
+                fc.dst_row[(int64_t)tid * K + k] = d;
+                if (d >= 0) fc.recv_src_idx[d] = tid;
+            }
         }
     }
-    for (int64_t r = (int64_t)end + gid; r < cap; r += nth) recv_src_idx[r] = -1;
-}
-
-// The first max_blocks blocks of an apply grid (all of a smaller grid) do the fill.
-constexpr int kFillBlocks = 1024;
-
-__device__ __forceinline__ void fill_unused_grid(int32_t* __restrict__ recv_src_idx,
-                                                 const int32_t* __restrict__ expert_offset,
-                                                 const int32_t* __restrict__ counts, int E, int64_t cap,
-                                                 int max_blocks = kFillBlocks) {
-    const int nb = min((int)gridDim.x, max_blocks);
-    if ((int)blockIdx.x >= nb) return;
-    fill_unused(recv_src_idx, expert_offset, counts, E, cap, blockIdx.x * blockDim.x + threadIdx.x,
-                (uint32_t)nb * blockDim.x);
+    fill_unused(fc.recv_src_idx, s_off, s_pre, E, fc.cap, blockIdx.x * kRankTile + tid, gridDim.x * kRankTile);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kFusedItems; ++j) {
+        if (ft[j] < T) {
+            int dl = -1;
+            if (lane < K) dl = s_slot[ft[j] * K + lane];
+            for (int k = 0; k < K; ++k) {
+                const int d = __builtin_amdgcn_readlane(dl, k);
+                if (d >= 0 && fv[j] < fc.nvec) store_nt(fc.recv_x + (int64_t)d * fc.nvec + fv[j], fbuf[j]);
+            }
+        }
+    }
 }
 
 // Final receive row of a packed slot word p from the plan (-1: not selected).
@@ -718,13 +791,16 @@ static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, 
     if (!layout) {
         const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
         hipLaunchKernelGGL((rank_kernel<1, false>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, none);
+                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, none,
+                           FusedCopy{});
     } else if (layout->R <= 64) {
         hipLaunchKernelGGL((rank_kernel<1, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout);
+                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout,
+                           FusedCopy{});
     } else {
         hipLaunchKernelGGL((rank_kernel<6, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout);
+                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout,
+                           FusedCopy{});
     }
     return hipGetLastError();
 }
@@ -827,11 +903,63 @@ hipError_t launch_dispatch_apply_cast_fp8(const void* x, int64_t T, int H, int K
     return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n
+                                                                                                                   : 256;
+    }
+    return cus[dev];
+}
+
+// Plan and bf16 apply of a batch of at most one tile in one launch (the FUSED
+// rank kernel); seg_cap >= 0 for the fixed-capacity packed layout.
+static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, const void* x,
+                               int H, void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
+                               int32_t* dst_row, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
+                               hipStream_t stream) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    const int nvec = H / 8;
+    const int nchunk = (nvec + kWave - 1) / kWave;
+    // one block per CU where that leaves at most kFusedItems items per wave:
+    // every block plans the whole batch in LDS, so blocks sharing a CU would
+    // share its LDS bandwidth for that
+    const int64_t items = T * nchunk;
+    const int64_t per_block = (int64_t)kRankWaves * kFusedItems;
+    const int64_t blocks = std::max<int64_t>(std::min<int64_t>((items + kRankWaves - 1) / kRankWaves, device_cus()),
+                                             (items + per_block - 1) / per_block);
+    const dim3 grid((unsigned)std::max<int64_t>(1, blocks)), block(kRankTile);
+    const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
+    const FusedCopy fc{reinterpret_cast<const uint4*>(x), nvec, nchunk, reinterpret_cast<uint4*>(recv_x), dst_row,
+                       recv_src_idx, cap};
+    hipLaunchKernelGGL((rank_kernel<1, false, true>), grid, block, rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
+                       ebits, A, seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                       w.ticket, none, fc);
+    return hipGetLastError();
+}
+
+bool dispatch_fuses(int64_t T) { return T <= kRankTile; }
+
+hipError_t launch_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
+                                 void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
+                                 int32_t* dst_row, void* workspace, hipStream_t stream) {
+    return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_x, cap, expert_offset, recv_src_idx, dst_row, nullptr,
+                        nullptr, dispatch_ws(workspace, T, K, E), stream);
+}
+
 hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
                                   int expert_capacity, int fmt, void* recv_x, void* recv_s, int32_t* packed_count,
                                   int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
                                   hipStream_t stream) {
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
+    if (fmt < 0 && dispatch_fuses(T))
+        return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, (int64_t)E * expert_capacity,
+                            w.packed_offset, recv_src_info, dst_row, packed_count, stats, w, stream);
     hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, w.packed_offset, packed_count, stats, w,
                                  stream);
     if (err != hipSuccess) return err;

@@ -33,6 +33,12 @@ size_t dispatch_workspace_bytes(int64_t T, int K, int E);
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R, int32_t* ntpr, int32_t* ntpe,
                          uint8_t* itr, void* workspace, hipStream_t stream);
 
+// Batches of at most one plan tile: plan and apply (bf16) in one launch.
+bool dispatch_fuses(int64_t T);
+hipError_t launch_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
+                                 void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
+                                 int32_t* dst_row, void* workspace, hipStream_t stream);
+
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
                                 void* workspace, hipStream_t stream);
 

@@ -99,6 +99,10 @@ def test_packed_overflow_duplicates_and_zero_capacity():
     _packed_and_check(x, idx, E, R, cap=100)
     _packed_and_check(x, idx, E, R, cap=0)
     _packed_and_check(x[:1], idx[:1], E, R, cap=3)
+    # one-tile batches (plan and copy in one launch), with and without overflow
+    _packed_and_check(x[:200], idx[:200], E, R, cap=10, stats=np.arange(E, dtype=np.int32))
+    _packed_and_check(x[:200], idx[:200], E, R, cap=200)
+    _packed_and_check(x[:256], idx[:256], E, R, cap=0)
 
 
 def _decode_step(x, idx, wt, E, R, cap):

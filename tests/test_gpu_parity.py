@@ -177,6 +177,12 @@ EDGE_CASES = {
     "rowcopy_K=5_duplicates": dict(T=4000, K=5, E=64, R=8, H=200, dup=True),
     "rowcopy_K=1_H=8": dict(T=16385, K=1, E=16, R=4, H=8),
     "rowcopy_one_hot_expert": dict(T=3000, K=6, E=64, R=8, H=72, all_to=5),
+    # batches of at most 256 tokens plan and copy in one launch (every block
+    # plans the whole batch)
+    "fused_duplicates_T=200": dict(T=200, K=8, E=8, R=2, H=64, dup=True),
+    "fused_align8_neg_T=250": dict(T=250, K=6, E=64, R=8, H=1032, align=8, p_neg=0.2),
+    "fused_T=256_K=16_R=64": dict(T=256, K=16, E=512, R=64, H=520),
+    "fused_extra_capacity_T=100": dict(T=100, K=4, E=32, R=4, H=40, cap_extra=300),
 }
 
 
