@@ -23,7 +23,8 @@ Rank-granular path (normal mode, one row per (token, flagged rank)):
 FP8 payload: per_token_cast_to_fp8 / per_token_cast_back; every dispatch
 accepts and returns (codes, scales) tuples, and dispatch(..., cast_fp8=fmt)
 casts on the way. Fixed-capacity packed layout (low-latency dispatch):
-low_latency_dispatch / low_latency_combine.
+low_latency_dispatch / low_latency_combine. copy_(dst, src) is libcgd's plain
+16-byte copy, the measured copy ceiling the bandwidths are compared with.
 
 The calls follow the DeepEP-style Buffer API described by the DeepEP Python
 interface notes ("4 Python接口", section "Dispatch API") and the

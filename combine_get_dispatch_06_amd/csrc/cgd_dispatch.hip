@@ -36,8 +36,11 @@
 //                                      stores the chunk once to its row.
 //                   Otherwise scatter_bcast_kernel: one wave per (token,
 //                   chunk) resolves the K rows inline and stores the chunk to
-//                   each (one launch: decode latency). scatter_cast_kernel is
-//                   the FP8 form (cast on the way).
+//                   each (one launch). scatter_cast_kernel is the FP8 form
+//                   (cast on the way).
+//   FUSED           batches of at most one tile (decode) through cgd_dispatch
+//                   or the bf16 packed dispatch: rank_kernel plans and moves
+//                   the rows in one launch (every block plans the batch).
 // Cached dispatch runs the row copy (or the broadcast kernel) on a stored
 // final dst_row.
 //
@@ -56,7 +59,7 @@ namespace cgd {
 
 constexpr int kRankWaves = kRankTile / kWave;
 constexpr int kPackBits = 13;  // rank inside a tile < 256 * 16 = 4096 < 2^13
-constexpr int kScatterWaves = 4;  // waves per block of the cast-on-dispatch kernel
+constexpr int kScatterWaves = 4;  // waves per block of the broadcast and cast-on-dispatch kernels
 constexpr int kSlotWaves = 16;    // waves per block of the row copy
 constexpr int kBatch = 16;                        // loads in flight per thread when summing columns
 
