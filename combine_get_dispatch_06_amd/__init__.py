@@ -18,6 +18,8 @@ Rank-granular path (normal mode, one row per (token, flagged rank)):
 
     recv_x, recv_topk_idx, recv_topk_weights, num_recv_per_expert, h = normal_dispatch(
         x, is_token_in_rank, ntpe, topk_idx, topk_weights, num_experts=E)
+    layout, plan = layout_and_normal_dispatch_plan(topk_idx, E, R)     # one launch
+    recv_x, recv_topk_idx, recv_topk_weights, _, h = normal_dispatch_apply(x, plan, topk_idx, topk_weights)
     combined_x, combined_topk_weights = normal_combine(expert_out, h, recv_topk_weights, bias=(b0, b1))
 
 FP8 payload: per_token_cast_to_fp8 / per_token_cast_back; every dispatch
@@ -44,7 +46,8 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
            "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
-           "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_"]
+           "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_",
+           "layout_and_normal_dispatch_plan"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcgd.so")
@@ -143,6 +146,10 @@ def load():
     lib.cgd_normal_combine.argtypes = [vp, i64, i32, vp, i64, i32, vp, i32, vp, vp, vp, vp, vp]
     lib.cgd_copy.restype = i32
     lib.cgd_copy.argtypes = [vp, vp, i64, vp]
+    lib.cgd_layout_and_normal_workspace_bytes.restype = sz
+    lib.cgd_layout_and_normal_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.cgd_layout_and_normal_dispatch_plan.restype = i32
+    lib.cgd_layout_and_normal_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -713,6 +720,29 @@ def normal_dispatch_plan(is_token_in_rank: torch.Tensor, num_tokens_per_expert: 
                                             expert_alignment, _ptr(off), _ptr(nre), _ptr(ws), ws.numel(),
                                             _stream(dev)))
     return NormalPlan(off, nre, ws, T, num_experts)
+
+
+def layout_and_normal_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                                    expert_alignment: int = 1, num_recv_tokens_per_expert: bool = True):
+    """get_dispatch_layout and normal_dispatch_plan in one launch.
+    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), NormalPlan)."""
+    lib = load()
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    with torch.cuda.device(dev):
+        ntpr = torch.empty(num_ranks, dtype=torch.int32, device=dev)
+        ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        itr = torch.empty((T, num_ranks), dtype=torch.bool, device=dev)
+        off = torch.empty(num_ranks + 1, dtype=torch.int32, device=dev)
+        nre = torch.empty(num_experts, dtype=torch.int32, device=dev) if num_recv_tokens_per_expert else None
+        need = int(lib.cgd_layout_and_normal_workspace_bytes(T, K, num_experts, num_ranks))
+        ws = _workspace(dev, "layout_normal", max(need, 1))
+        _check("cgd_layout_and_normal_dispatch_plan",
+               lib.cgd_layout_and_normal_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks,
+                                                       expert_alignment, _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off),
+                                                       _ptr(nre), _ptr(ws), ws.numel(), _stream(dev)))
+    return (ntpr, None, ntpe, itr, None), NormalPlan(off, nre, ws, T, num_experts)
 
 
 def normal_dispatch_apply(x: torch.Tensor, plan: NormalPlan, topk_idx: torch.Tensor | None = None,

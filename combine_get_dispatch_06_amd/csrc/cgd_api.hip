@@ -311,6 +311,39 @@ static int check_normal_plan_args(const uint8_t* itr, int64_t T, int R, const in
     return CGD_OK;
 }
 
+size_t cgd_layout_and_normal_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks) {
+    const size_t lw = cgd_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks);
+    return lw == 0 ? 0 : cgd::normal_workspace_bytes(num_tokens, num_ranks) + lw;
+}
+
+int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                                        int num_ranks, int expert_alignment, int32_t* num_tokens_per_rank,
+                                        int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                        int32_t* rank_offset, int32_t* num_recv_tokens_per_expert, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_routing_sizes(num_tokens, num_topk, num_experts, num_ranks);
+    if (rc) return rc;
+    if (expert_alignment < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !rank_offset)
+        return fail(CGD_ERR_INVALID_ARG, "null count or rank_offset pointer");
+    if (num_tokens > 0 && (!topk_idx || !is_token_in_rank))
+        return fail(CGD_ERR_INVALID_ARG, "null topk_idx or is_token_in_rank pointer");
+    if (!aligned(topk_idx, 8) || !aligned(num_tokens_per_rank, 4) || !aligned(num_tokens_per_expert, 4) ||
+        !aligned(rank_offset, 4) || !aligned(num_recv_tokens_per_expert, 4))
+        return fail(CGD_ERR_INVALID_ARG, "misaligned topk_idx or count output");
+    if (!aligned(is_token_in_rank, 16)) return fail(CGD_ERR_INVALID_ARG, "is_token_in_rank must be 16-byte aligned");
+    const size_t need = cgd_layout_and_normal_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(CGD_ERR_WORKSPACE, "layout + normal plan workspace needs %zu bytes, 256-byte aligned (got %zu)",
+                    need, workspace_bytes);
+    hipError_t err = cgd::launch_layout_and_normal_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                                        expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
+                                                        is_token_in_rank, rank_offset, num_recv_tokens_per_expert,
+                                                        workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "layout and normal dispatch plan launch");
+    return CGD_OK;
+}
+
 // Checks of the normal-mode apply (rows and per-row outputs).
 static int check_normal_apply_args(const void* x, int64_t T, int H, const int64_t* topk_idx, const float* topk_w,
                                    int K, int E, int R, const void* recv_x, int64_t cap, const int32_t* rank_offset,

@@ -245,10 +245,14 @@ __device__ __forceinline__ void token_rank_mask(const int (&e)[kMaxTopk], const 
 
 // Distinct tokens per rank, added to s_rank (LDS, [R]): one ballot per rank
 // over the wave's tokens, lane (r % 64) adds the popcount for rank r. Also
-// stores the thread's mask in s_mask[tid * RW + w].
+// stores the thread's mask in s_mask[tid * RW + w]. s_bal (optional, LDS
+// [waves, R]) receives each rank's ballot: the wave's group word of the
+// rank-granular dispatch plan.
 template <int RW>
-__device__ __forceinline__ void count_rank_tokens(const uint64_t (&m)[RW], int R, int32_t* s_rank, uint64_t* s_mask) {
+__device__ __forceinline__ void count_rank_tokens(const uint64_t (&m)[RW], int R, int32_t* s_rank, uint64_t* s_mask,
+                                                  uint64_t* s_bal = nullptr) {
     const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
 #pragma unroll
     for (int w = 0; w < RW; ++w) {
         const int rbeg = w * kWave;
@@ -257,6 +261,7 @@ __device__ __forceinline__ void count_rank_tokens(const uint64_t (&m)[RW], int R
         for (int r = rbeg; r < rend; ++r) {
             const uint64_t b = ballot((m[w] >> (r & 63)) & 1ull);
             if (lane == (r & 63)) cnt = __popcll(b);
+            if (s_bal && lane == 0) s_bal[wave * R + r] = b;
         }
         if (rbeg + lane < rend && cnt) atomicAdd(&s_rank[rbeg + lane], cnt);
         s_mask[threadIdx.x * RW + w] = m[w];

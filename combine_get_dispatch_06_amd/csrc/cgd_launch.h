@@ -39,6 +39,22 @@ hipError_t launch_dispatch_fused(const void* x, int64_t T, int H, const int64_t*
                                  void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
                                  int32_t* dst_row, void* workspace, hipStream_t stream);
 
+// The rank-granular plan's workspace arrays (group words, group bases, tile
+// counts / bases), as launch_normal_plan leaves them.
+struct NormalPlanArrays {
+    unsigned int* ticket;  // at offset 0: a ticket of this workspace never moves with the sizes
+    unsigned long long* grp_bal;
+    int32_t* grp_pre;
+    int32_t* tile_base;
+};
+NormalPlanArrays normal_plan_arrays(void* workspace, int64_t T, int R);
+
+// get_dispatch_layout and the rank-granular dispatch plan in one launch; the
+// workspace holds the plan's workspace followed by the layout's.
+hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A,
+                                         int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
+                                         int32_t* nrecv, void* workspace, hipStream_t stream);
+
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
                                 void* workspace, hipStream_t stream);
 

@@ -81,6 +81,13 @@ size_t normal_workspace_bytes(int64_t T, int R) {
            round256((size_t)tiles * R * 4);
 }
 
+static NormalWs normal_ws(void* workspace, int64_t T, int R);
+
+NormalPlanArrays normal_plan_arrays(void* workspace, int64_t T, int R) {
+    const NormalWs w = normal_ws(workspace, T, R);
+    return NormalPlanArrays{w.ticket, w.grp_bal, w.grp_pre, w.tile_base};
+}
+
 static NormalWs normal_ws(void* workspace, int64_t T, int R) {
     int64_t G, tiles;
     normal_sizes(T, R, &G, &tiles);

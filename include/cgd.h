@@ -68,9 +68,11 @@ const char* cgd_last_error(void);
 
 /* Workspace bytes cgd_get_dispatch_layout needs for these sizes (host only;
  * 0 if the sizes are invalid). The workspace must be zero-filled before its
- * first use; every completed call leaves it zero-filled again, so one
- * workspace serves any number of calls that are ordered on one stream.
- * Calls that may run concurrently need separate workspaces. */
+ * first use; every completed call leaves the words that must start at zero
+ * (a ticket at the start of the workspace) zero again, and everything else
+ * in it is rewritten before it is read, so one workspace serves any number of
+ * calls, of any sizes, that are ordered on one stream. Calls that may run
+ * concurrently need separate workspaces. */
 size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
 
 /* Workspace bytes cgd_dispatch (and the plan/apply pair) needs (host only;
@@ -390,6 +392,29 @@ int cgd_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, 
                                  int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
                                  int32_t* cumulative_recv_stats, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/* get_dispatch_layout and cgd_normal_dispatch_plan in one launch: the plan
+ * needs only is_token_in_rank (and the per-expert counts for the aligned
+ * receive counts), which the layout computes from the same tile of topk_idx
+ * (Layout API "Return Values"; legacy tests, normal-mode dispatch call, whose
+ * inputs are the layout outputs).
+ *   outputs                 as cgd_get_dispatch_layout, and rank_offset [R+1]
+ *                           and num_recv_tokens_per_expert [E] (may be NULL)
+ *                           as cgd_normal_dispatch_plan
+ *   workspace               >= cgd_layout_and_normal_workspace_bytes(...),
+ *                           256-byte aligned; zero-fill and reuse rules as
+ *                           the layout workspace;
+ *                           it begins with the rank-granular plan's workspace:
+ *                           pass the same pointer to cgd_normal_dispatch_apply
+ *                           (or _apply_fp8), which reads the plan from it
+ * Errors as cgd_get_dispatch_layout and cgd_normal_dispatch_plan. */
+size_t cgd_layout_and_normal_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
+
+int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                                        int num_ranks, int expert_alignment, int32_t* num_tokens_per_rank,
+                                        int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                        int32_t* rank_offset, int32_t* num_recv_tokens_per_expert, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 
 /* -------------------------------------------------------------------------
  * cgd_copy: dst[0, bytes) = src[0, bytes), bitwise.

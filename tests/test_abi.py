@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_apply_fp8", "cgd_dispatch_apply_cast_fp8", "cgd_dispatch_cached_fp8",
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
+        "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan",
     ])
 
 
@@ -310,3 +311,19 @@ def test_copy_rejects_bad_arguments():
     assert lib.cgd_copy(None, f, 32, None) == -1
     assert lib.cgd_copy(f, _vp(FAKE + 8), 32, None) == -1  # misaligned
     assert lib.cgd_copy(None, None, 0, None) == 0          # nothing to copy: nothing enqueued
+
+
+def test_layout_and_normal_plan_rejects_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    assert lib.cgd_layout_and_normal_workspace_bytes(100, 8, 256, 8) > lib.cgd_normal_workspace_bytes(100, 8)
+    assert lib.cgd_layout_and_normal_workspace_bytes(100, 8, 256, 7) > 0  # E % R is checked by the call
+    assert lib.cgd_layout_and_normal_workspace_bytes(-1, 8, 256, 8) == 0
+    # idx, T, K, E, R, A, ntpr, ntpe, itr, off, nre, ws, wsb
+    assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 7, 1, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 8, 0, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 8, 1, f, f, f, None, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 8, 1, f, f, _vp(FAKE + 8), f, f, f, 1 << 20,
+                                                   None) == -1
+    assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 8, 1, f, f, f, f, f, f, 16, None) == -3
+    assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 8, 1, f, f, f, f, f, None, 1 << 20, None) == -3

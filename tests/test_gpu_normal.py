@@ -290,3 +290,36 @@ def test_normal_determinism_20_repeats():
         if ref is None:
             ref = hh.hexdigest()
         assert hh.hexdigest() == ref, f"repeat {i} differs"
+
+
+@pytest.mark.parametrize("T,K,E,R,H,align,p_neg", [(4096, 8, 256, 8, 256, 1, 0.0), (128, 8, 256, 16, 1024, 1, 0.0),
+                                                   (1025, 6, 96, 12, 136, 4, 0.3), (700, 16, 384, 384, 64, 1, 0.0),
+                                                   (300, 4, 64, 1, 64, 8, 0.1), (1, 2, 8, 2, 8, 1, 0.0),
+                                                   (0, 4, 16, 4, 64, 1, 0.0)])
+def test_layout_and_normal_plan_in_one_launch(T, K, E, R, H, align, p_neg):
+    """get_dispatch_layout + normal_dispatch_plan in one launch: layout
+    outputs, rank offsets and aligned counts equal the oracle's, and the apply
+    from that plan gives the oracle's rows, send_row and top-k metadata."""
+    rng = np.random.default_rng(T + 7 * R)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64) if T else np.zeros((0, K), np.int64)
+    idx[rng.random((T, K)) < p_neg] = -1
+    x = synth.normal_bf16(synth.stream_key(T, 55, 1), T * H).reshape(T, H)
+    wts = synth.softmax_weights(synth.stream_key(T, 55, 3), T, K)
+    say(f"[normal] fused layout + plan: T={T} K={K} E={E} R={R} H={H} align={align}")
+    idx_dev = dev_i64(idx)
+    (ntpr, _, ntpe, itr, _), plan = cgd.layout_and_normal_dispatch_plan(idx_dev, E, R, expert_alignment=align)
+    recv_x, ridx, rw, _, h = cgd.normal_dispatch_apply(dev_bf16(x), plan, idx_dev, dev_f32(wts))
+    torch.cuda.synchronize()
+    ol = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), ol[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
+    o = oracle.dispatch_normal(x, ol[2], E, K, ol[1], idx, wts, align=align, cap=h.recv_capacity, hidden=H)
+    np.testing.assert_array_equal(plan.rank_offset.cpu().numpy(), o["rank_offset"])
+    np.testing.assert_array_equal(plan.num_recv_tokens_per_expert.cpu().numpy(), o["num_recv_tokens_per_expert"])
+    np.testing.assert_array_equal(h.send_row.cpu().numpy(), o["send_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    np.testing.assert_array_equal(ridx.cpu().numpy(), o["recv_topk_idx"])
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), o["recv_topk_weights"].view(np.uint32))
+    data = o["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
