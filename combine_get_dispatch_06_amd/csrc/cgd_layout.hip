@@ -125,19 +125,14 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
 
     const int nblk = gridDim.x;
     for (int i = tid; i < W; i += kLayoutTile) {
-        // loads issued 16 at a time: few round trips however many blocks;
-        // NPLAN: a rank column's running sum is also each tile's base
-        const bool bases = NPLAN && i >= E;
+        // loads issued 16 at a time: few round trips however many blocks
         int s = 0;
         for (int b0 = 0; b0 < nblk; b0 += 16) {
             int v[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) v[j] = (b0 + j < nblk) ? partial[(int64_t)(b0 + j) * W + i] : 0;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                if (bases && b0 + j < nblk) np.tile_base[(int64_t)(b0 + j) * R + (i - E)] = s;
-                s += v[j];
-            }
+            for (int j = 0; j < 16; ++j) s += v[j];
         }
         if (i < E) {
             ntpe[i] = s;
@@ -148,6 +143,20 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
         }
     }
     if (NPLAN) {
+        // per-tile bases of each rank: running sums down the rank columns
+        for (int r = tid; r < R; r += kLayoutTile) {
+            int run = 0;
+            for (int b0 = 0; b0 < nblk; b0 += 16) {
+                int v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = (b0 + j < nblk) ? partial[(int64_t)(b0 + j) * W + E + r] : 0;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    if (b0 + j < nblk) np.tile_base[(int64_t)(b0 + j) * R + r] = run;
+                    run += v[j];
+                }
+            }
+        }
         __syncthreads();
         block_exclusive_scan2(R, [&](int r) { return s_rank[r]; }, s_off, s_wsum);
         __syncthreads();
