@@ -1,0 +1,67 @@
+"""The steps bench.py times, captured once in a HIP graph and replayed with
+new inputs: every replay must equal the same step run eagerly on those inputs
+(expert-granular step with the finalize + row-copy apply and with the
+one-launch small-batch dispatch; rank-granular step with the fused layout +
+plan)."""
+import pytest
+import torch
+
+import combine_get_dispatch_06_amd as cgd
+import synth
+from gpu_util import dev_bf16, dev_f32, dev_i64, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _expert_step(x, idx, wt, w, out):
+    lay, plan = cgd.layout_and_dispatch_plan(idx, w.E, w.R)
+    recv, h = cgd.dispatch_apply(x, plan)
+    cgd.combine(recv, h, wt, out=out)
+    return list(lay[0::2][:2]) + [lay[3], h.expert_offset, h.dst_row, h.recv_src_idx, out]
+
+
+def _small_step(x, idx, wt, w, out):
+    recv, h = cgd.dispatch(x, idx, w.E, w.R)
+    cgd.combine(recv, h, wt, out=out)
+    return [h.expert_offset, h.dst_row, h.recv_src_idx, out]
+
+
+def _normal_step(x, idx, wt, w, out):
+    (ntpr, _, ntpe, itr, _), plan = cgd.layout_and_normal_dispatch_plan(idx, w.E, w.R)
+    recv, ridx, rw, _, h = cgd.normal_dispatch_apply(x, plan, idx, wt)
+    cgd.normal_combine(recv, h, rw, out=out)
+    return [ntpr, ntpe, itr, plan.rank_offset, h.send_row, h.recv_src_idx, ridx, out]
+
+
+@pytest.mark.parametrize("kind,T", [("expert", 2500), ("small", 200), ("normal", 2500), ("normal", 100)])
+def test_step_replays_from_a_captured_graph(kind, T):
+    w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
+    step = {"expert": _expert_step, "small": _small_step, "normal": _normal_step}[kind]
+    inputs = [synth.make_inputs(w, seed=s) for s in range(5)]
+    sx = dev_bf16(inputs[0]["x"])
+    sidx = dev_i64(inputs[0]["topk_idx"])
+    swt = dev_f32(inputs[0]["topk_weights"])
+    sout = torch.empty_like(sx)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):  # warm-up on the capture stream: its workspaces exist before capture
+            step(sx, sidx, swt, w, sout)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        static = step(sx, sidx, swt, w, sout)
+    torch.cuda.synchronize()
+    for i, inp in enumerate(inputs[1:]):
+        sx.copy_(dev_bf16(inp["x"]))
+        sidx.copy_(dev_i64(inp["topk_idx"]))
+        swt.copy_(dev_f32(inp["topk_weights"]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eout = torch.empty_like(sx)
+        eager = step(dev_bf16(inp["x"]), dev_i64(inp["topk_idx"]), dev_f32(inp["topk_weights"]), w, eout)
+        torch.cuda.synchronize()
+        for a, b in zip(static, eager):
+            assert torch.equal(a, b), f"{kind} replay {i} differs"
+    say(f"[graphs] {kind} T={T}: 4 replays equal eager steps")
