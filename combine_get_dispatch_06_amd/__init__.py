@@ -11,7 +11,7 @@ Expert-granular path (one received row per selected expert):
     recv_x, handle = dispatch(x, topk_idx, num_experts, num_ranks)
     recv_x2, _ = dispatch(x2, handle=handle)            # cached: reuses the layout
     combined = combine(expert_out, handle, topk_weights)
-    layout, plan = layout_and_dispatch_plan(topk_idx, num_experts, num_ranks)   # one launch
+    layout, plan = layout_and_dispatch_plan(topk_idx, num_experts, num_ranks)   # one routing pass
     recv_x, handle = dispatch_apply(x, plan)
 
 Rank-granular path (normal mode, one row per (token, flagged rank)):
@@ -96,9 +96,10 @@ def load():
     lib.cgd_dispatch.restype = i32
     lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_plan.restype = i32
-    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, sz, vp]
+    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp]
     lib.cgd_layout_and_dispatch_plan.restype = i32
-    lib.cgd_layout_and_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.cgd_layout_and_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz,
+                                                 vp]
     lib.cgd_packed_workspace_bytes.restype = sz
     lib.cgd_packed_workspace_bytes.argtypes = [i64, i32, i32]
     lib.cgd_dispatch_packed.restype = i32
@@ -106,8 +107,6 @@ def load():
     lib.cgd_dispatch_packed_cast_fp8.restype = i32
     lib.cgd_dispatch_packed_cast_fp8.argtypes = [vp, i64, i32, vp, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp,
                                                  vp, sz, vp]
-    lib.cgd_dispatch_apply.restype = i32
-    lib.cgd_dispatch_apply.argtypes = [vp, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_cached.restype = i32
     lib.cgd_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
     lib.cgd_combine.restype = i32
@@ -128,11 +127,8 @@ def load():
     lib.cgd_cast_to_fp8.argtypes = [vp, i64, i32, vp, vp, i64, i64, i32, vp]
     lib.cgd_cast_back.restype = i32
     lib.cgd_cast_back.argtypes = [vp, vp, i64, i64, i32, i64, i32, vp, vp]
-    lib.cgd_dispatch_apply_fp8.restype = i32
-    lib.cgd_dispatch_apply_fp8.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp,
-                                           sz, vp]
-    lib.cgd_dispatch_apply_cast_fp8.restype = i32
-    lib.cgd_dispatch_apply_cast_fp8.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_cached_cast_fp8.restype = i32
+    lib.cgd_dispatch_cached_cast_fp8.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, i64, vp]
     lib.cgd_dispatch_cached_fp8.restype = i32
     lib.cgd_dispatch_cached_fp8.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, vp, vp, vp, i64, vp]
     lib.cgd_normal_dispatch_apply_fp8.restype = i32
@@ -380,6 +376,13 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
             if handle.num_tokens != T:
                 raise ValueError("x has a different number of tokens than the handle")
             cap = handle.recv_capacity
+            if cast_fp8 is not None and not fp8:
+                recv_x = _recv_fp8(recv_x, cap, H, cast_fp8, dev)
+                _check("cgd_dispatch_cached_cast_fp8",
+                       lib.cgd_dispatch_cached_cast_fp8(_ptr(x), T, H, handle.num_topk, cast_fp8,
+                                                        _ptr(handle.dst_row), _ptr(recv_x[0]), _ptr(recv_x[1]), cap,
+                                                        _stream(dev)))
+                return recv_x, handle
             if fp8:
                 recv_x = _recv_fp8(recv_x, cap, H, fmt, dev)
                 _check("cgd_dispatch_cached_fp8",
@@ -424,8 +427,8 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
 
 @dataclass
 class DispatchPlan:
-    """Result of dispatch_plan: the handle-to-be plus the workspace that
-    dispatch_apply must receive. Not a valid handle until applied."""
+    """Result of dispatch_plan: the handle (complete once the plan has run on
+    the stream) and the workspace the plan used (not needed afterwards)."""
     handle: DispatchHandle
     workspace: torch.Tensor
     num_tokens: int
@@ -433,7 +436,8 @@ class DispatchPlan:
 
 def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expert_alignment: int = 1,
                   recv_capacity: int | None = None) -> DispatchPlan:
-    """First step of dispatch: receive-buffer layout from the routing alone."""
+    """First step of dispatch: the handle (receive-buffer layout, dst_row,
+    recv_src_idx) from the routing alone."""
     lib = load()
     _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
     T, K = topk_idx.shape
@@ -448,14 +452,14 @@ def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expe
         ws = _workspace(dev, "dispatch", nbytes)
         _check("cgd_dispatch_plan",
                lib.cgd_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap, _ptr(off),
-                                     _ptr(ws), ws.numel(), _stream(dev)))
+                                     _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
     h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
     return DispatchPlan(h, ws, T)
 
 
 def layout_and_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expert_alignment: int = 1,
                              recv_capacity: int | None = None):
-    """get_dispatch_layout and dispatch_plan in one launch.
+    """get_dispatch_layout and dispatch_plan in one pass over the routing.
     -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), DispatchPlan)."""
     lib = load()
     _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
@@ -473,57 +477,21 @@ def layout_and_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks
         ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts))
         _check("cgd_layout_and_dispatch_plan",
                lib.cgd_layout_and_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap,
-                                                _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(ws), ws.numel(),
-                                                _stream(dev)))
+                                                _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(src), _ptr(dst),
+                                                _ptr(ws), ws.numel(), _stream(dev)))
     h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
     return (ntpr, None, ntpe, itr, None), DispatchPlan(h, ws, T)
 
 
 def dispatch_apply(x, plan: DispatchPlan, recv_x=None, cast_fp8: int | None = None):
-    """Second step of dispatch: finalise the handle and copy rows.
-    x: bf16 [T, H] or an FP8 tuple; cast_fp8 (a scale format) casts a bf16 x
-    on the way. Returns (recv_x, handle), recv_x an FP8 tuple for FP8 payloads."""
-    lib = load()
-    h = plan.handle
-    fp8 = isinstance(x, tuple)
-    if fp8:
-        q, sc, fmt, st, sb = _fp8_parts(x)
-        T, H = q.shape
-        dev = q.device
-    else:
-        _dev_tensor(x, "x", torch.bfloat16, 2)
-        T, H = x.shape
-        dev = x.device
+    """Second step of dispatch: copy rows to the plan's handle (the cached
+    dispatch with plan.handle). x: bf16 [T, H] or an FP8 tuple; cast_fp8 (a
+    scale format) casts a bf16 x on the way. Returns (recv_x, handle), recv_x
+    an FP8 tuple for FP8 payloads."""
+    T = (x[0] if isinstance(x, tuple) else x).shape[0]
     if T != plan.num_tokens:
         raise ValueError("x has a different number of tokens than the plan")
-    cap = h.recv_capacity
-    with torch.cuda.device(dev):
-        if fp8:
-            recv_x = _recv_fp8(recv_x, cap, H, fmt, dev)
-            _check("cgd_dispatch_apply_fp8",
-                   lib.cgd_dispatch_apply_fp8(_ptr(q), _ptr(sc), st, sb, fmt, T, H, h.num_topk, h.num_experts, cap,
-                                              _ptr(recv_x[0]), _ptr(recv_x[1]), _ptr(h.expert_offset),
-                                              _ptr(h.recv_src_idx), _ptr(h.dst_row), _ptr(plan.workspace),
-                                              plan.workspace.numel(), _stream(dev)))
-            return recv_x, h
-        if cast_fp8 is not None:
-            recv_x = _recv_fp8(recv_x, cap, H, cast_fp8, dev)
-            _check("cgd_dispatch_apply_cast_fp8",
-                   lib.cgd_dispatch_apply_cast_fp8(_ptr(x), T, H, h.num_topk, h.num_experts, cast_fp8, cap,
-                                                   _ptr(recv_x[0]), _ptr(recv_x[1]), _ptr(h.expert_offset),
-                                                   _ptr(h.recv_src_idx), _ptr(h.dst_row), _ptr(plan.workspace),
-                                                   plan.workspace.numel(), _stream(dev)))
-            return recv_x, h
-        if recv_x is None:
-            recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
-        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
-        if recv_x.shape != (cap, H):
-            raise ValueError("recv_x must be [recv_capacity, hidden]")
-        _check("cgd_dispatch_apply",
-               lib.cgd_dispatch_apply(_ptr(x), T, H, h.num_topk, h.num_experts, cap, _ptr(recv_x),
-                                      _ptr(h.expert_offset), _ptr(h.recv_src_idx), _ptr(h.dst_row),
-                                      _ptr(plan.workspace), plan.workspace.numel(), _stream(dev)))
-    return recv_x, h
+    return dispatch(x, handle=plan.handle, recv_x=recv_x, cast_fp8=cast_fp8)
 
 
 def combine(expert_out: torch.Tensor, handle: DispatchHandle, topk_weights: torch.Tensor,

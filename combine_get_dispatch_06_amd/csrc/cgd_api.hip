@@ -127,7 +127,8 @@ int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num
 
 // Checks shared by the dispatch entry points.
 static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
-                           const int32_t* expert_offset, const void* workspace, size_t workspace_bytes) {
+                           const int32_t* expert_offset, const int32_t* recv_src_idx, const int32_t* dst_row,
+                           const void* workspace, size_t workspace_bytes) {
     int rc = check_routing_sizes(T, K, E, R);
     if (rc) return rc;
     if (A < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
@@ -137,29 +138,9 @@ static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int
         return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [%lld, INT32_MAX] (got %lld)", (long long)need_rows,
                     (long long)cap);
     if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
-    if (T > 0 && !topk_idx) return fail(CGD_ERR_INVALID_ARG, "null topk_idx");
-    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
-    const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-        return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
-                    workspace_bytes);
-    return CGD_OK;
-}
-
-static int check_apply_args(const void* x, int64_t T, int H, int K, int E, int64_t cap, const void* recv_x,
-                            const int32_t* expert_offset, const int32_t* recv_src_idx, const int32_t* dst_row,
-                            const void* workspace, size_t workspace_bytes) {
-    if (T < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
-    if (K < 1 || K > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16] (got %d)", K);
-    if (E < 1 || E > cgd::kMaxExperts) return fail(CGD_ERR_INVALID_ARG, "num_experts must be in [1,512] (got %d)", E);
-    int rc = check_hidden(H);
-    if (rc) return rc;
-    if (cap < 0 || cap > INT32_MAX) return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
-    if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
-    if (T > 0 && (!x || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null x or dst_row");
-    if (cap > 0 && (!recv_x || !recv_src_idx)) return fail(CGD_ERR_INVALID_ARG, "null receive pointer");
-    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
-    if (!aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
+    if (T > 0 && (!topk_idx || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null topk_idx or dst_row");
+    if (cap > 0 && !recv_src_idx) return fail(CGD_ERR_INVALID_ARG, "null recv_src_idx");
+    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
         return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
     const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
@@ -168,14 +149,25 @@ static int check_apply_args(const void* x, int64_t T, int H, int K, int E, int64
     return CGD_OK;
 }
 
+// Checks of the row payload of a dispatch (x in, recv_x out).
+static int check_rows_args(const void* x, int64_t T, int H, int64_t cap, const void* recv_x) {
+    int rc = check_hidden(H);
+    if (rc) return rc;
+    if (T > 0 && !x) return fail(CGD_ERR_INVALID_ARG, "null x");
+    if (cap > 0 && !recv_x) return fail(CGD_ERR_INVALID_ARG, "null recv_x");
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and recv_x must be 16-byte aligned");
+    return CGD_OK;
+}
+
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
-                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
+                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, workspace, workspace_bytes);
+                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
     if (rc) return rc;
     hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
-                                               expert_offset, workspace, stream);
+                                               recv_capacity, expert_offset, recv_src_idx, dst_row, workspace,
+                                               stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     return CGD_OK;
 }
@@ -183,10 +175,10 @@ int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
 int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
                                  int num_ranks, int expert_alignment, int64_t recv_capacity,
                                  int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
-                                 uint8_t* is_token_in_rank, int32_t* expert_offset, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
+                                 uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
+                                 int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, workspace, workspace_bytes);
+                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
     if (rc) return rc;
     if (!num_tokens_per_rank || !num_tokens_per_expert)
         return fail(CGD_ERR_INVALID_ARG, "null count output pointer");
@@ -195,21 +187,10 @@ int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, in
         return fail(CGD_ERR_INVALID_ARG, "misaligned count output");
     if (!aligned(is_token_in_rank, 16)) return fail(CGD_ERR_INVALID_ARG, "is_token_in_rank must be 16-byte aligned");
     hipError_t err = cgd::launch_layout_and_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
-                                                 expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
-                                                 is_token_in_rank, expert_offset, workspace, stream);
+                                                 expert_alignment, recv_capacity, num_tokens_per_rank,
+                                                 num_tokens_per_expert, is_token_in_rank, expert_offset, recv_src_idx,
+                                                 dst_row, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "layout and dispatch plan launch");
-    return CGD_OK;
-}
-
-int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                       int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,
-                       int32_t* dst_row, const void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    int rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x, expert_offset,
-                              recv_src_idx, dst_row, workspace, workspace_bytes);
-    if (rc) return rc;
-    hipError_t err = cgd::launch_dispatch_apply(x, num_tokens, hidden, num_topk, num_experts, recv_x, recv_capacity,
-                                                expert_offset, recv_src_idx, dst_row, workspace, stream);
-    if (err != hipSuccess) return hip_fail(err, "dispatch apply launch");
     return CGD_OK;
 }
 
@@ -218,11 +199,9 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
                  int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
                  size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, workspace, workspace_bytes);
+                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
     if (rc) return rc;
-    if ((rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x, expert_offset,
-                               recv_src_idx, dst_row, workspace, workspace_bytes)))
-        return rc;
+    if ((rc = check_rows_args(x, num_tokens, hidden, recv_capacity, recv_x))) return rc;
     hipError_t err;
     if (cgd::dispatch_fuses(num_tokens)) {  // one tile: plan and apply in one launch
         err = cgd::launch_dispatch_fused(x, num_tokens, hidden, topk_idx, num_topk, num_experts, expert_alignment,
@@ -231,12 +210,11 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
         if (err != hipSuccess) return hip_fail(err, "fused dispatch launch");
         return CGD_OK;
     }
-    err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment, expert_offset,
-                                    workspace, stream);
+    err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment, recv_capacity,
+                                    expert_offset, recv_src_idx, dst_row, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
-    err = cgd::launch_dispatch_apply(x, num_tokens, hidden, num_topk, num_experts, recv_x, recv_capacity,
-                                     expert_offset, recv_src_idx, dst_row, workspace, stream);
-    if (err != hipSuccess) return hip_fail(err, "dispatch apply launch");
+    err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
+    if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
     return CGD_OK;
 }
 
@@ -521,40 +499,24 @@ int cgd_cast_back(const void* x_fp8, const void* x_scales, int64_t scale_stride_
     return CGD_OK;
 }
 
-int cgd_dispatch_apply_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
-                           int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
-                           int num_experts, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
-                           const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                           const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int cgd_dispatch_cached_cast_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk, int scale_format,
+                                 const int32_t* dst_row, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                 hipStream_t stream) {
+    if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
+    if (num_topk < 1 || num_topk > cgd::kMaxTopk) return fail(CGD_ERR_INVALID_ARG, "num_topk must be in [1,16]");
     int rc = check_fp8(hidden, scale_format);
     if (rc) return rc;
-    if ((rc = check_apply_args(x_fp8, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x_fp8,
-                               expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes)))
-        return rc;
-    if ((rc = check_scales(x_scales, scale_stride_token, scale_stride_block, scale_format, num_tokens > 0))) return rc;
-    if ((rc = check_scales(recv_scales, 0, 0, scale_format, recv_capacity > 0))) return rc;
-    hipError_t err = cgd::launch_dispatch_apply_fp8(x_fp8, x_scales, scale_stride_token, scale_stride_block,
-                                                    scale_format, num_tokens, hidden, num_topk, num_experts,
-                                                    recv_x_fp8, recv_scales, recv_capacity, expert_offset,
-                                                    recv_src_idx, dst_row, workspace, stream);
-    if (err != hipSuccess) return hip_fail(err, "FP8 dispatch apply launch");
-    return CGD_OK;
-}
-
-int cgd_dispatch_apply_cast_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                                int scale_format, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
-                                const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                                const void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    int rc = check_fp8(hidden, scale_format);
-    if (rc) return rc;
-    if ((rc = check_apply_args(x, num_tokens, hidden, num_topk, num_experts, recv_capacity, recv_x_fp8, expert_offset,
-                               recv_src_idx, dst_row, workspace, workspace_bytes)))
-        return rc;
-    if ((rc = check_scales(recv_scales, 0, 0, scale_format, recv_capacity > 0))) return rc;
-    hipError_t err = cgd::launch_dispatch_apply_cast_fp8(x, num_tokens, hidden, num_topk, num_experts, scale_format,
-                                                         recv_x_fp8, recv_scales, recv_capacity, expert_offset,
-                                                         recv_src_idx, dst_row, workspace, stream);
-    if (err != hipSuccess) return hip_fail(err, "FP8 cast dispatch apply launch");
+    if (recv_capacity < 0 || recv_capacity > INT32_MAX)
+        return fail(CGD_ERR_CAPACITY, "recv_capacity must be in [0, INT32_MAX]");
+    if (num_tokens > 0 && (!x || !dst_row || (recv_capacity > 0 && !recv_x_fp8)))
+        return fail(CGD_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(x, 16) || !aligned(recv_x_fp8, 16))
+        return fail(CGD_ERR_INVALID_ARG, "x and recv_x_fp8 must be 16-byte aligned");
+    if (!aligned(dst_row, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned dst_row");
+    if ((rc = check_scales(recv_scales, 0, 0, scale_format, num_tokens > 0 && recv_capacity > 0))) return rc;
+    hipError_t err = cgd::launch_dispatch_cached_cast_fp8(x, num_tokens, hidden, num_topk, scale_format, dst_row,
+                                                          recv_x_fp8, recv_scales, recv_capacity, stream);
+    if (err != hipSuccess) return hip_fail(err, "FP8 cast dispatch launch");
     return CGD_OK;
 }
 

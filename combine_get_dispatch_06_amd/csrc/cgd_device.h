@@ -172,20 +172,23 @@ __device__ __forceinline__ void copy_side_row(const SideRows& s, int64_t t, int6
     }
 }
 
-// Copy n (<= ITEMS * blockDim.x) routing entries of one tile into LDS as
-// int32, entries outside [0, E) becoming -1. All global loads of a thread are
-// issued before any LDS store, so the tile costs one memory round trip.
-template <int ITEMS>
+// Copy n (<= ITEMS * BLOCK) routing entries of one tile into LDS as int32,
+// entries outside [0, E) becoming -1, with a block of BLOCK threads. All
+// global loads of a thread are issued before any LDS store, so the tile costs
+// one memory round trip. Block sizes are compile-time constants throughout:
+// blockDim.x would be a vector load from the kernel-argument segment at the
+// start of every wave.
+template <int ITEMS, int BLOCK>
 __device__ __forceinline__ void stage_routing(const int64_t* __restrict__ src, int n, int E, int32_t* dst) {
     int64_t v[ITEMS];
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        const int i = threadIdx.x + j * blockDim.x;
+        const int i = threadIdx.x + j * BLOCK;
         v[j] = (i < n) ? src[i] : -1;
     }
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-        const int i = threadIdx.x + j * blockDim.x;
+        const int i = threadIdx.x + j * BLOCK;
         if (i < n) dst[i] = (v[j] >= 0 && v[j] < E) ? (int32_t)v[j] : -1;
     }
 }
@@ -277,7 +280,7 @@ __device__ __forceinline__ uint32_t flag_bytes4(uint32_t b) { return ((b & 0xFu)
 // stores its own token's row from its mask m (the widest aligned stores);
 // other R: 16 bytes per store across token boundaries from the masks in
 // s_mask (call after a barrier that follows count_rank_tokens).
-template <int RW>
+template <int RW, int BLOCK>
 __device__ __forceinline__ void store_token_in_rank(const uint64_t (&m)[RW], const uint64_t* s_mask, int nt, int R,
                                                     uint8_t* out) {
     if (R % 4 == 0 || R <= 2) {
@@ -306,7 +309,7 @@ __device__ __forceinline__ void store_token_in_rank(const uint64_t (&m)[RW], con
         return;
     }
     const int nbytes = nt * R;  // <= 256 * 384
-    for (int c = threadIdx.x; c * 16 < nbytes; c += blockDim.x) {
+    for (int c = threadIdx.x; c * 16 < nbytes; c += BLOCK) {
         const int b0 = c * 16;
         int tok = b0 / R;
         int r = b0 - tok * R;

@@ -7,7 +7,8 @@
 // a segment, rows follow ascending (token, slot), which makes the permutation
 // unique and independent of scheduling.
 //
-// No block ever waits for another:
+// No block ever waits for another. The plan needs only the routing and
+// writes the whole handle; the apply only moves rows.
 //   rank_kernel     (the plan) one block per tile of 256 tokens (4 waves, one
 //                   token per lane). For each slot it finds the number of
 //                   earlier slots of the tile with the same expert. When no
@@ -22,34 +23,34 @@
 //                   (rows of the expert in earlier tiles, one pass), the
 //                   per-expert counts and the segment offsets: a block prefix
 //                   scan of the aligned counts, or e * capacity for the
-//                   fixed-capacity packed layout (a one-tile grid finishes
-//                   from LDS without the handshake). Its LAYOUT form also
-//                   writes get_dispatch_layout's outputs from the same tile.
-//   the apply       moves the rows. Each row is read from HBM once however
-//                   many experts it goes to; rows without data get
-//                   recv_src_idx = -1 (padding, unused capacity, tail).
-//                   Batches of >= 16384 slots with top-k <= 8:
-//                     finalize_kernel  one thread per slot: final row =
-//                                      segment offset + tile base + rank,
-//                                      dst_row and recv_src_idx;
-//                     scatter_kernel   one wave per (token, 1 KB chunk, slot)
-//                                      stores the chunk once to its row.
-//                   Otherwise scatter_bcast_kernel: one wave per (token,
-//                   chunk) resolves the K rows inline and stores the chunk to
-//                   each (one launch). scatter_cast_kernel is the FP8 form
-//                   (cast on the way).
+//                   fixed-capacity packed layout. A one-tile grid finishes
+//                   from LDS without the handshake and writes dst_row and
+//                   recv_src_idx itself. Its LAYOUT form also writes
+//                   get_dispatch_layout's outputs from the same tile.
+//   finalize_kernel the plan's last step for several tiles: one thread per
+//                   slot turns its packed word into the final row (segment
+//                   offset + tile base + rank) and records dst_row and
+//                   recv_src_idx; rows without data get recv_src_idx = -1
+//                   (padding, unused capacity, tail).
+//   the apply       moves each row to its final rows, reading it from HBM
+//                   once however many experts it goes to. Batches of >= 16384
+//                   slots with top-k <= 8: scatter_kernel, one wave per
+//                   (token, 1 KB chunk, slot), stores the chunk once to its
+//                   row. Otherwise scatter_bcast_kernel: one wave per (token,
+//                   chunk) stores the chunk to each of the K rows.
+//                   scatter_cast_kernel is the FP8 form (cast on the way).
+//                   Cached dispatch is the same apply on a stored dst_row.
 //   FUSED           batches of at most one tile (decode) through cgd_dispatch
 //                   or the bf16 packed dispatch: rank_kernel plans and moves
 //                   the rows in one launch (every block plans the batch).
-// Cached dispatch runs the row copy (or the broadcast kernel) on a stored
-// final dst_row.
 //
 // Measured on MI355X: the store pattern bounds the apply. Stores into the ~E
 // receive segments of a token-ordered pass run near 5 TB/s; short waves that
 // store one 1 KB piece each (row copy) do 3-15 % better than long waves that
 // store K pieces, as long as each wave's row comes after one dependent load
-// (hence the finalize launch). Destination-ordered copies (sequential stores)
-// lose more on the 8x scattered re-reads of x than they gain.
+// (hence the final rows from the plan). Destination-ordered copies
+// (sequential stores) lose more on the 8x scattered re-reads of x than they
+// gain.
 #include <algorithm>
 
 #include "cgd_device.h"
@@ -80,7 +81,7 @@ __device__ __forceinline__ int slot_expert(int v) { return v < 0 ? -1 : (v & 0xF
 // seg_cap >= 0 selects the fixed-capacity packed layout: segment e is rows
 // [e*seg_cap, (e+1)*seg_cap) whatever its count (seg_cap < 0: prefix-summed
 // segments of the aligned counts). counts receives every
-// expert's slot count (workspace, for the apply's -1 fill); packed_count
+// expert's slot count (workspace, for the -1 fill of finalize_kernel); packed_count
 // (min(count, seg_cap)) and stats (accumulates packed_count) are optional.
 // With LAYOUT the kernel also produces get_dispatch_layout's outputs from the
 // same staged tile (rank masks with RW 64-bit words, as the layout kernel):
@@ -115,17 +116,19 @@ __device__ __forceinline__ void fill_unused(int32_t* __restrict__ recv_src_idx,
     for (int64_t r = (int64_t)end + gid; r < cap; r += nth) recv_src_idx[r] = -1;
 }
 
-// The first max_blocks blocks of an apply grid (all of a smaller grid) do the fill.
-constexpr int kFillBlocks = 1024;
+// The first kFillThreads threads of a grid of BLOCK-thread blocks (all of a
+// smaller grid) do the fill: each filling wave reads the same few lines of
+// expert_offset and counts, so only as many waves as the fill needs take
+// part (the rows of a large fixed capacity are then several per thread).
+constexpr int kFillThreads = 32768;
 
+template <int BLOCK>
 __device__ __forceinline__ void fill_unused_grid(int32_t* __restrict__ recv_src_idx,
                                                  const int32_t* __restrict__ expert_offset,
-                                                 const int32_t* __restrict__ counts, int E, int64_t cap,
-                                                 int max_blocks = kFillBlocks) {
-    const int nb = min((int)gridDim.x, max_blocks);
+                                                 const int32_t* __restrict__ counts, int E, int64_t cap) {
+    const int nb = min((int)gridDim.x, kFillThreads / BLOCK);
     if ((int)blockIdx.x >= nb) return;
-    fill_unused(recv_src_idx, expert_offset, counts, E, cap, blockIdx.x * blockDim.x + threadIdx.x,
-                (uint32_t)nb * blockDim.x);
+    fill_unused(recv_src_idx, expert_offset, counts, E, cap, blockIdx.x * BLOCK + threadIdx.x, (uint32_t)nb * BLOCK);
 }
 
 struct LayoutOut {
@@ -136,25 +139,28 @@ struct LayoutOut {
     int32_t* rank_part;
 };
 
-// Row copy of the FUSED form (plan and apply of a one-tile batch in one
-// launch): the grid's waves take the (token, 1 KB chunk) items of x in turn,
-// at most kFusedItems each, and move them to the tokens' receive rows.
+// Outputs of a one-tile batch, which is planned from LDS alone: the handle
+// (dst_row, recv_src_idx, rows below cap) and, in the FUSED form, the row
+// copy: the grid's waves take the (token, 1 KB chunk) items of x in turn, at
+// most kFusedItems each, and move them to the tokens' receive rows.
 constexpr int kFusedItems = 4;
-struct FusedCopy {
-    const uint4* x;
-    int nvec, nchunk;
-    uint4* recv_x;
+struct TileOut {
     int32_t* dst_row;
     int32_t* recv_src_idx;
     int64_t cap;
+    const uint4* x;  // FUSED only
+    int nvec, nchunk;
+    uint4* recv_x;
 };
 
-// FUSED (batches of at most one tile, e.g. decode): every block plans the
-// whole batch in LDS (the plan is a few microseconds of LDS work, cheaper
-// than a second launch and a second pass over the plan), block 0 alone writes
-// the plan's outputs, and each wave then moves one (token, chunk) item to the
-// token's rows, its x chunk loaded at the start; dst_row and recv_src_idx
-// hold final rows and every block fills a share of the unused rows.
+// A batch of one tile (decode) finishes from LDS: the kernel writes the
+// final dst_row and recv_src_idx itself and fills the unused rows. FUSED:
+// every block plans the whole batch in LDS (a few microseconds of LDS work,
+// cheaper than a second launch and a second pass over the plan), block 0
+// alone writes the plan's outputs, every block fills a share of the unused
+// rows, and each wave then moves one (token, chunk) item to the token's
+// rows, its x chunk loaded at the start. Larger batches leave packed slot
+// words and tile bases in the workspace for finalize_kernel.
 template <int RW, bool LAYOUT, bool FUSED = false>
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
                                                          int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
                                                          int32_t* __restrict__ packed_count,
                                                          int32_t* __restrict__ stats,
                                                          unsigned int* __restrict__ ticket, LayoutOut lo,
-                                                         FusedCopy fc) {
+                                                         TileOut fc) {
     extern __shared__ __align__(16) char lds[];
     unsigned long long* s_tok = reinterpret_cast<unsigned long long*>(lds);
     int32_t* s_pre = reinterpret_cast<int32_t*>(s_tok + kRankWaves * E);
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         for (int i = tid; i < E; i += kRankTile) s_rank_of[i] = (int16_t)(i / lo.L);
         for (int i = tid; i < lo.R; i += kRankTile) s_rank[i] = 0;
     }
-    stage_routing<kMaxTopk>(topk_idx + t0 * K, nt * K, E, s_slot);
+    stage_routing<kMaxTopk, kRankTile>(topk_idx + t0 * K, nt * K, E, s_slot);
     __syncthreads();
 
     int32_t* my = s_slot + tid * K;  // this token's K slots
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     const bool any_dup = __syncthreads_or(dup);
     if (LAYOUT && writer) {
         // t0*R is a multiple of 16 because kRankTile is
-        store_token_in_rank<RW>(m, s_mask, nt, lo.R, lo.itr + t0 * lo.R);
+        store_token_in_rank<RW, kRankTile>(m, s_mask, nt, lo.R, lo.itr + t0 * lo.R);
         for (int r = tid; r < lo.R; r += kRankTile) lo.rank_part[(int64_t)tile * lo.R + r] = s_rank[r];
     }
     if (!any_dup) {
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     }
 
     __syncthreads();
-    if (!FUSED) {
+    if (ntiles > 1) {
         int32_t* out = slot_pack + t0 * K;
         const int n = nt * K;
         for (int i = tid; i < n; i += kRankTile) out[i] = s_slot[i];
@@ -323,10 +329,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         // no other block has to be waited for
         for (int x = tid; x < E; x += kRankTile) {
             s_pre[x] = s_off[x];
-            if (writer) {
-                if (!FUSED) tile_base[x] = 0;
-                if (LAYOUT) lo.ntpe[x] = s_off[x];
-            }
+            if (LAYOUT && writer) lo.ntpe[x] = s_off[x];
         }
         if (LAYOUT && writer)
             for (int r = tid; r < lo.R; r += kRankTile) lo.ntpr[r] = s_rank[r];
@@ -387,9 +390,9 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         for (int x = tid; x < E; x += kRankTile) counts[x] = s_pre[x];
         for (int x = tid; x <= E; x += kRankTile) expert_offset[x] = s_off[x];
     }
-    if (!FUSED) return;
+    if (ntiles > 1) return;  // finalize_kernel completes the handle
 
-    // ---- FUSED: final rows, unused rows, then this wave's item ----
+    // ---- one tile: final rows and unused rows; FUSED: this wave's items ----
     if (mine) {
         for (int k = 0; k < K; ++k) {
             const int v = my[k];
@@ -407,6 +410,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         }
     }
     fill_unused(fc.recv_src_idx, s_off, s_pre, E, fc.cap, blockIdx.x * kRankTile + tid, gridDim.x * kRankTile);
+    if (!FUSED) return;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kFusedItems; ++j) {
@@ -437,29 +441,41 @@ __device__ __forceinline__ int final_row(int p, int64_t t, const int32_t* __rest
     return (p < 0 || ex >= E || d < 0 || d >= cap || d >= hi) ? -1 : d;
 }
 
-// Small batches (decode): one wave per (token, column chunk of U*64 16-byte
-// vectors) stores its chunk to all K rows, with the plan resolved inline (no
-// finalize launch). With PACKED
-// (dispatch apply) the wave turns the plan's packed slot words into final rows
-// (tile base + rank in tile); the token's chunk-0 wave also records dst_row
-// and recv_src_idx. Without PACKED (cached dispatch) dst_row already holds
-// final rows. Lanes 0..K-1 broadcast the K rows; each lane loads its U
-// vectors once and stores them to every destination row with non-temporal
-// stores. A row is nvec 16-byte
-// vectors of any payload (bf16 rows, or FP8 rows with their scales moved as
-// the side payload by the chunk-0 wave).
-template <int KM, int U, bool PACKED>
-__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(const uint4* __restrict__ x, int64_t t0, int64_t T, int nvec,
-                                                                      int nchunk, int K, const int32_t* __restrict__ slot,
-                                                                      int32_t* __restrict__ dst_row,
-                                                                      const int32_t* __restrict__ tile_base, int E,
-                                                                      int32_t* __restrict__ recv_src_idx,
-                                                                      const int32_t* __restrict__ expert_offset,
-                                                                      const int32_t* __restrict__ counts,
-                                                                      int64_t cap, int fill,
-                                                                      uint4* __restrict__ recv_x, SideRows side) {
+// Final rows of every slot of a batch of several tiles (the plan's last
+// step): one thread per (token, slot) turns the packed word into the receive
+// row (segment offset + tile base + rank) and records dst_row and
+// recv_src_idx; the first kFillThreads threads then fill unused rows.
+constexpr int kFinalizeThreads = 256;
+__global__ __launch_bounds__(kFinalizeThreads) void finalize_kernel(int64_t T, int K,
+                                                                    const int32_t* __restrict__ slot,
+                                                                    const int32_t* __restrict__ tile_base, int E,
+                                                                    const int32_t* __restrict__ expert_offset,
+                                                                    const int32_t* __restrict__ counts, int64_t cap,
+                                                                    int32_t* __restrict__ dst_row,
+                                                                    int32_t* __restrict__ recv_src_idx) {
+    const int64_t nth = (int64_t)gridDim.x * kFinalizeThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kFinalizeThreads + threadIdx.x; i < T * K; i += nth) {
+        const int64_t t = i / K;
+        const int d = final_row(slot[i], t, tile_base, E, expert_offset, cap);
+        dst_row[i] = d;
+        if (d >= 0) recv_src_idx[d] = (int32_t)t;
+    }
+    fill_unused_grid<kFinalizeThreads>(recv_src_idx, expert_offset, counts, E, cap);
+}
+
+// Small batches (decode) and top-k above 8: one wave per (token, column chunk
+// of U*64 16-byte vectors) stores its chunk to all K rows. Lanes 0..K-1 read
+// the token's final rows and broadcast them; each lane loads its U vectors
+// once and stores them to every destination row with non-temporal stores. A
+// row is nvec 16-byte vectors of any payload (bf16 rows, or FP8 rows with
+// their scales moved as the side payload by the chunk-0 wave).
+template <int KM, int U>
+__global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(const uint4* __restrict__ x, int64_t t0,
+                                                                             int64_t T, int nvec, int nchunk, int K,
+                                                                             const int32_t* __restrict__ dst_row,
+                                                                             int64_t cap, uint4* __restrict__ recv_x,
+                                                                             SideRows side) {
     const int lane = lane_id();
-    if (PACKED && fill) fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t tr = g / nchunk;
     const int64_t t = t0 + tr;
@@ -467,7 +483,7 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(con
     const int c = (int)(g - tr * nchunk);
     const int v0 = c * U * kWave;
     const uint4* xr = x + t * nvec;
-    uint4 buf[U];  // loaded before the indices arrive
+    uint4 buf[U];  // loaded before the rows arrive
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int v = v0 + u * kWave + lane;
@@ -475,16 +491,8 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(con
     }
     int d = -1;
     if (lane < K) {
-        const int p = slot[t * K + lane];
-        if (PACKED) {
-            d = final_row(p, t, tile_base, E, expert_offset, cap);
-            if (c == 0) {
-                dst_row[t * K + lane] = d;
-                if (d >= 0) recv_src_idx[d] = (int32_t)t;
-            }
-        } else {
-            d = (p >= 0 && p < cap) ? p : -1;
-        }
+        const int p = dst_row[t * K + lane];
+        d = (p >= 0 && p < cap) ? p : -1;
     }
     int dk[KM];
 #pragma unroll
@@ -504,25 +512,6 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(con
     }
 }
 
-// Final rows of every slot (dispatch apply of larger batches): one thread per
-// (token, slot) turns the plan's packed word into the receive row and
-// records dst_row and recv_src_idx; the whole grid (sized for the receive
-// capacity as well) also fills unused rows.
-__global__ __launch_bounds__(256) void finalize_kernel(int64_t T, int K, const int32_t* __restrict__ slot,
-                                                       int32_t* __restrict__ dst_row,
-                                                       const int32_t* __restrict__ tile_base, int E,
-                                                       int32_t* __restrict__ recv_src_idx,
-                                                       const int32_t* __restrict__ expert_offset,
-                                                       const int32_t* __restrict__ counts, int64_t cap) {
-    fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap, (int)gridDim.x);  // the whole grid fills
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= T * K) return;
-    const int64_t t = i / K;
-    const int d = final_row(slot[i], t, tile_base, E, expert_offset, cap);
-    dst_row[i] = d;
-    if (d >= 0) recv_src_idx[d] = (int32_t)t;
-}
-
 // Row copy to final rows, one wave per (token, 1 KB column chunk, slot): the
 // wave loads the chunk (64 lanes x 16 bytes) and stores it once, to its
 // slot's receive row, with a non-temporal store. The K waves of a chunk are
@@ -531,11 +520,12 @@ __global__ __launch_bounds__(256) void finalize_kernel(int64_t T, int K, const i
 // all K rows by 3-15 % (prefill, Zipf-skewed and large-batch shapes): many
 // short waves that store once and exit keep more stores in flight, spread
 // over more rows, than long waves that issue K stores each. Each wave needs
-// its final row after a single dependent load (dst_row), which keeps the
-// waves short; the plan is resolved beforehand (finalize_kernel). The grid
-// covers tokens [t0, t_end). A row is nvec 16-byte vectors of any payload
-// (bf16 rows, or FP8 rows with their scales moved as the side payload by the
-// chunk-0 wave).
+// its final row after a single dependent load (dst_row, which the plan
+// resolved), and stores nothing but its chunk: recording dst_row and
+// recv_src_idx here, in the copy waves or in extra blocks, measured 3 us
+// slower at prefill than in the plan. The grid covers tokens [t0, t_end). A
+// row is nvec 16-byte vectors of any payload (bf16 rows, or FP8 rows with
+// their scales moved as the side payload by the chunk-0 wave).
 __global__ __launch_bounds__(kSlotWaves* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t t0,
                                                                    int64_t t_end, int nvec, int nchunk, int K,
                                                                    const int32_t* __restrict__ dst_row, int64_t cap,
@@ -573,21 +563,19 @@ __global__ __launch_bounds__(kSlotWaves* kWave) void scatter_kernel(const uint4*
 // comes from an 8-lane reduction (CPL = 8: 8-byte code vectors, 16-lane
 // groups). The chunk is quantized once and its code vectors and block scales
 // are stored to every destination row with non-temporal stores. Rows are H
-// bytes; scales are [cap, H/128] (4 bytes, or 1 byte UE8M0).
+// bytes; scales are [cap, H/128] (4 bytes, or 1 byte UE8M0). dst_row holds
+// the plan's final rows.
 #ifndef CGD_CAST_CPL
 #define CGD_CAST_CPL 16
 #endif
 constexpr int kCastCpl = CGD_CAST_CPL;  // channels per lane
 template <int KM, int U, int FMT>
 __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
-    const uint4* __restrict__ x, int64_t T, int nlv, int nchunk, int K, const int32_t* __restrict__ slot,
-    int32_t* __restrict__ dst_row, const int32_t* __restrict__ tile_base, int E, int32_t* __restrict__ recv_src_idx,
-    const int32_t* __restrict__ expert_offset, const int32_t* __restrict__ counts, int64_t cap, int64_t t0,
-    int fill, void* __restrict__ recv_q, void* __restrict__ recv_s) {
+    const uint4* __restrict__ x, int64_t T, int nlv, int nchunk, int K, const int32_t* __restrict__ dst_row,
+    int64_t cap, int64_t t0, void* __restrict__ recv_q, void* __restrict__ recv_s) {
     constexpr int kVin = kCastCpl / 8;             // 16-byte bf16 vectors per lane
     constexpr int kGroup = kFp8Block / kCastCpl;   // lanes per 128-channel block
     const int lane = lane_id();
-    if (fill) fill_unused_grid(recv_src_idx, expert_offset, counts, E, cap);
     const int64_t g = (int64_t)blockIdx.x * kScatterWaves + threadIdx.x / kWave;
     const int64_t tr = g / nchunk;
     const int64_t t = t0 + tr;
@@ -606,11 +594,8 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
     }
     int d = -1;
     if (lane < K) {
-        d = final_row(slot[t * K + lane], t, tile_base, E, expert_offset, cap);
-        if (c == 0) {
-            dst_row[t * K + lane] = d;
-            if (d >= 0) recv_src_idx[d] = (int32_t)t;
-        }
+        const int p = dst_row[t * K + lane];
+        d = (p >= 0 && p < cap) ? p : -1;
     }
     // quantize: a block never straddles two lane groups (nlv % kGroup == 0)
     Fp8Scale sc[U];
@@ -700,11 +685,10 @@ static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
     return w;
 }
 
-// Batches with fewer slots use the broadcast kernel with the plan resolved
-// inline (one launch instead of two: decode latency), and so does top-k above
-// 8: at top-16 (32768 tokens, hidden 4096) the broadcast kernel measured
-// faster than the row copy, whose 16 waves per chunk then cost more than the
-// shorter waves gain.
+// Batches with fewer slots use the broadcast kernel (one wave stores its
+// chunk to all K rows), and so does top-k above 8: at top-16 (32768 tokens,
+// hidden 4096) the broadcast kernel measured faster than the row copy, whose
+// 16 waves per chunk then cost more than the shorter waves gain.
 constexpr int64_t kRowCopyMinSlots = 16384;
 constexpr int kRowCopyMaxTopk = 8;
 
@@ -722,24 +706,20 @@ static void launch_row_copy(int64_t T, int K, hipStream_t s, const void* x, int 
     }
 }
 
-template <bool PACKED, int U>
-static void launch_bcast_u(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
-                           int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
-                           const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
+template <int U>
+static void launch_bcast_u(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* dst_row,
+                           int64_t cap, void* recv_x, const SideRows& side) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t tper = tokens_per_launch(nchunk);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     uint4* rv = reinterpret_cast<uint4*>(recv_x);
     const dim3 block(kScatterWaves * kWave);
-    int64_t t0 = 0;
-    do {  // at least one launch: with no token it still fills unused rows
+    for (int64_t t0 = 0; t0 < T; t0 += tper) {
         const int64_t nt = std::min<int64_t>(tper, T - t0);
-        const int64_t waves = nt * nchunk;
-        const dim3 grid((unsigned)(waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves));
-        const int fill = t0 == 0 ? 1 : 0;
-#define CGD_SCATTER(KM)                                                                                          \
-    hipLaunchKernelGGL((scatter_bcast_kernel<KM, U, PACKED>), grid, block, 0, s, xv, t0, t0 + nt, nvec, nchunk, K, \
-                       slot, dst_row, tile_base, E, src, off, counts, cap, fill, rv, side)
+        const dim3 grid((unsigned)((nt * nchunk + kScatterWaves - 1) / kScatterWaves));
+#define CGD_SCATTER(KM)                                                                                            \
+    hipLaunchKernelGGL((scatter_bcast_kernel<KM, U>), grid, block, 0, s, xv, t0, t0 + nt, nvec, nchunk, K, dst_row, \
+                       cap, rv, side)
         if (K <= 2)
             CGD_SCATTER(2);
         else if (K <= 4)
@@ -749,32 +729,21 @@ static void launch_bcast_u(int64_t T, int K, hipStream_t s, const void* x, int n
         else
             CGD_SCATTER(16);
 #undef CGD_SCATTER
-        t0 += tper;
-    } while (t0 < T);
+    }
 }
 
-// Dispatch apply (PACKED: slot holds the plan's packed words) or cached
-// dispatch (slot is dst_row with final rows). Larger batches: finalize_kernel
-// (PACKED) then the row copy; small ones: the broadcast kernel.
-template <bool PACKED>
-static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* slot,
-                           int32_t* dst_row, const int32_t* tile_base, int E, int32_t* src, const int32_t* off,
-                           const int32_t* counts, int64_t cap, void* recv_x, const SideRows& side) {
-    if (T * K < kRowCopyMinSlots) {
-        launch_bcast_u<PACKED, 1>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x, side);
-        return;
-    }
-    if (K > kRowCopyMaxTopk) {
-        launch_bcast_u<PACKED, 4>(T, K, s, x, nvec, slot, dst_row, tile_base, E, src, off, counts, cap, recv_x, side);
-        return;
-    }
-    if (PACKED) {
-        // a thread per slot; enough threads for the fill of a large fixed capacity too
-        const int64_t blocks = std::max<int64_t>((T * K + 255) / 256, std::min<int64_t>((cap + 255) / 256, 16384));
-        hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, s, T, K, slot, dst_row, tile_base,
-                           E, src, off, counts, cap);
-    }
-    launch_row_copy(T, K, s, x, nvec, PACKED ? dst_row : slot, cap, recv_x, side);
+// Rows moved to the final rows of a handle (the apply of a plan, cached
+// dispatch, the packed dispatch): the row copy for larger batches, the
+// broadcast kernel for small ones and for top-k above 8.
+static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* dst_row,
+                           int64_t cap, void* recv_x, const SideRows& side) {
+    if (T <= 0) return;
+    if (T * K < kRowCopyMinSlots)
+        launch_bcast_u<1>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
+    else if (K > kRowCopyMaxTopk)
+        launch_bcast_u<4>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
+    else
+        launch_row_copy(T, K, s, x, nvec, dst_row, cap, recv_x, side);
 }
 
 static SideRows no_side() { return SideRows{nullptr, 0, 0, 0, 0, nullptr}; }
@@ -783,82 +752,74 @@ static SideRows fp8_side(const void* scales, int64_t st, int64_t sb, int H, int 
     return SideRows{scales, st, sb, H / kFp8Block, fmt == 2 ? 1 : 4, recv_scales};
 }
 
-static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap,
-                              int32_t* expert_offset, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
-                              hipStream_t stream, const LayoutOut* layout = nullptr) {
+// The plan, from the routing alone: rank_kernel, which completes the handle
+// (dst_row, recv_src_idx with its -1 fill) of a one-tile batch itself, else
+// finalize_kernel after it.
+static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, int64_t cap,
+                              int32_t* expert_offset, int32_t* dst_row, int32_t* recv_src_idx,
+                              int32_t* packed_count, int32_t* stats, const DispatchWs& w, hipStream_t stream,
+                              const LayoutOut* layout = nullptr) {
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
     const dim3 grid(ntiles), block(kRankTile);
     const size_t lds = rank_lds_bytes(E, K);
+    const TileOut to{dst_row, recv_src_idx, cap, nullptr, 0, 0, nullptr};
     if (!layout) {
         const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
         hipLaunchKernelGGL((rank_kernel<1, false>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, none,
-                           FusedCopy{});
+                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, none, to);
     } else if (layout->R <= 64) {
         hipLaunchKernelGGL((rank_kernel<1, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
                            w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout,
-                           FusedCopy{});
+                           to);
     } else {
         hipLaunchKernelGGL((rank_kernel<6, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
                            w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout,
-                           FusedCopy{});
+                           to);
+    }
+    if (ntiles > 1) {
+        // a thread per slot (grid capped, the kernel strides), and at least
+        // kFillThreads threads for the fill
+        const int64_t n = T * K;
+        const int64_t blocks = std::max<int64_t>(std::min<int64_t>((n + kFinalizeThreads - 1) / kFinalizeThreads, 65536),
+                                                 kFillThreads / kFinalizeThreads);
+        hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)blocks), dim3(kFinalizeThreads), 0, stream, T, K,
+                           w.slot_pack, w.tile_base, E, expert_offset, w.counts, cap, dst_row, recv_src_idx);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int32_t* ntpr,
-                                  int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, void* workspace,
-                                  hipStream_t stream) {
+hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
+                                  int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset,
+                                  int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream) {
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
     const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
-    return launch_rank(topk_idx, T, K, E, A, -1, expert_offset, nullptr, nullptr, w, stream, &lo);
+    return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, dst_row, recv_src_idx, nullptr, nullptr, w,
+                       stream, &lo);
 }
 
-hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
-                                void* workspace, hipStream_t stream) {
-    return launch_rank(topk_idx, T, K, E, A, -1, expert_offset, nullptr, nullptr, dispatch_ws(workspace, T, K, E),
-                       stream);
-}
-
-hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, void* recv_x, int64_t cap,
-                                 const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                                 const void* workspace, hipStream_t stream) {
-    const DispatchWs w = dispatch_ws(workspace, T, K, E);
-    launch_scatter<true>(T, K, stream, x, H / 8, w.slot_pack, dst_row, w.tile_base, E, recv_src_idx, expert_offset,
-                         w.counts, cap, recv_x, no_side());
-    return hipGetLastError();
-}
-
-hipError_t launch_dispatch_apply_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
-                                     int H, int K, int E, void* recv_q, void* recv_s, int64_t cap,
-                                     const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                                     const void* workspace, hipStream_t stream) {
-    const DispatchWs w = dispatch_ws(workspace, T, K, E);
-    launch_scatter<true>(T, K, stream, xq, H / 16, w.slot_pack, dst_row, w.tile_base, E, recv_src_idx, expert_offset,
-                         w.counts, cap, recv_q, fp8_side(xs, st, sb, H, fmt, recv_s));
-    return hipGetLastError();
+hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int64_t cap,
+                                int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                                hipStream_t stream) {
+    return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, dst_row, recv_src_idx, nullptr, nullptr,
+                       dispatch_ws(workspace, T, K, E), stream);
 }
 
 template <int U, int FMT>
-static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E, const DispatchWs& w,
-                                  int32_t* dst_row, int32_t* src, const int32_t* off, int64_t cap, void* recv_q,
-                                  void* recv_s, hipStream_t s) {
+static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, const int32_t* dst_row, int64_t cap,
+                                  void* recv_q, void* recv_s, hipStream_t s) {
     const int nlv = H / kCastCpl;
     const int nchunk = (nlv + U * kWave - 1) / (U * kWave);
     const int64_t tper = tokens_per_launch(nchunk);
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     const dim3 block(kScatterWaves * kWave);
-    int64_t t0 = 0;
-    do {  // at least one launch: with no token it still fills unused rows
+    for (int64_t t0 = 0; t0 < T; t0 += tper) {
         const int64_t nt = std::min<int64_t>(tper, T - t0);
-        const int64_t waves = nt * nchunk;
-        const dim3 grid((unsigned)(waves <= 0 ? 1 : (waves + kScatterWaves - 1) / kScatterWaves));
-        const int fill = t0 == 0 ? 1 : 0;
-#define CGD_SCATTER_CAST(KM)                                                                                         \
-    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, t0 + nt, nlv, nchunk, K,             \
-                       w.slot_pack, dst_row, w.tile_base, E, src, off, w.counts, cap, t0, fill, recv_q, recv_s)
+        const dim3 grid((unsigned)((nt * nchunk + kScatterWaves - 1) / kScatterWaves));
+#define CGD_SCATTER_CAST(KM)                                                                                        \
+    hipLaunchKernelGGL((scatter_cast_kernel<KM, U, FMT>), grid, block, 0, s, xv, t0 + nt, nlv, nchunk, K, dst_row, \
+                       cap, t0, recv_q, recv_s)
         if (K <= 2)
             CGD_SCATTER_CAST(2);
         else if (K <= 4)
@@ -868,8 +829,7 @@ static void launch_scatter_cast_u(const void* x, int64_t T, int H, int K, int E,
         else
             CGD_SCATTER_CAST(16);
 #undef CGD_SCATTER_CAST
-        t0 += tper;
-    } while (t0 < T);
+    }
 }
 
 // Chunks of U vectors per lane unless that leaves fewer than kMinScatterWaves
@@ -880,29 +840,31 @@ constexpr int64_t kMinScatterWaves = 4096;
 #define CGD_SCATTER_CAST_U 2
 #endif
 
-template <int FMT>
-static void launch_scatter_cast(const void* x, int64_t T, int H, int K, int E, const DispatchWs& w, int32_t* dst_row,
-                                int32_t* src, const int32_t* off, int64_t cap, void* recv_q, void* recv_s,
-                                hipStream_t s) {
+static void launch_scatter_cast(const void* x, int64_t T, int H, int K, int fmt, const int32_t* dst_row,
+                                int64_t cap, void* recv_q, void* recv_s, hipStream_t s) {
+    if (T <= 0) return;
     constexpr int U = CGD_SCATTER_CAST_U;
-    const int64_t waves = T * ((H / kCastCpl + U * kWave - 1) / (U * kWave));
-    if (waves >= kMinScatterWaves)
-        launch_scatter_cast_u<U, FMT>(x, T, H, K, E, w, dst_row, src, off, cap, recv_q, recv_s, s);
+    const bool wide = T * ((H / kCastCpl + U * kWave - 1) / (U * kWave)) >= kMinScatterWaves;
+#define CGD_CAST(FMT)                                                                 \
+    do {                                                                              \
+        if (wide)                                                                     \
+            launch_scatter_cast_u<U, FMT>(x, T, H, K, dst_row, cap, recv_q, recv_s, s); \
+        else                                                                          \
+            launch_scatter_cast_u<1, FMT>(x, T, H, K, dst_row, cap, recv_q, recv_s, s); \
+    } while (0)
+    if (fmt == 0)
+        CGD_CAST(0);
+    else if (fmt == 1)
+        CGD_CAST(1);
     else
-        launch_scatter_cast_u<1, FMT>(x, T, H, K, E, w, dst_row, src, off, cap, recv_q, recv_s, s);
+        CGD_CAST(2);
+#undef CGD_CAST
 }
 
-hipError_t launch_dispatch_apply_cast_fp8(const void* x, int64_t T, int H, int K, int E, int fmt, void* recv_q,
-                                          void* recv_s, int64_t cap, const int32_t* expert_offset,
-                                          int32_t* recv_src_idx, int32_t* dst_row, const void* workspace,
-                                          hipStream_t stream) {
-    const DispatchWs w = dispatch_ws(workspace, T, K, E);
-    if (fmt == 0)
-        launch_scatter_cast<0>(x, T, H, K, E, w, dst_row, recv_src_idx, expert_offset, cap, recv_q, recv_s, stream);
-    else if (fmt == 1)
-        launch_scatter_cast<1>(x, T, H, K, E, w, dst_row, recv_src_idx, expert_offset, cap, recv_q, recv_s, stream);
-    else
-        launch_scatter_cast<2>(x, T, H, K, E, w, dst_row, recv_src_idx, expert_offset, cap, recv_q, recv_s, stream);
+hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int K, int fmt, const int32_t* dst_row,
+                                           void* recv_q, void* recv_s, int64_t cap, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;  // nothing to enqueue
+    launch_scatter_cast(x, T, H, K, fmt, dst_row, cap, recv_q, recv_s, stream);
     return hipGetLastError();
 }
 
@@ -938,8 +900,8 @@ static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E,
                                              (items + per_block - 1) / per_block);
     const dim3 grid((unsigned)std::max<int64_t>(1, blocks)), block(kRankTile);
     const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
-    const FusedCopy fc{reinterpret_cast<const uint4*>(x), nvec, nchunk, reinterpret_cast<uint4*>(recv_x), dst_row,
-                       recv_src_idx, cap};
+    const TileOut fc{dst_row, recv_src_idx, cap, reinterpret_cast<const uint4*>(x), nvec, nchunk,
+                     reinterpret_cast<uint4*>(recv_x)};
     hipLaunchKernelGGL((rank_kernel<1, false, true>), grid, block, rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
                        ebits, A, seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
                        w.ticket, none, fc);
@@ -960,39 +922,32 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
                                   int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
                                   hipStream_t stream) {
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
-    if (fmt < 0 && dispatch_fuses(T))
-        return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, (int64_t)E * expert_capacity,
-                            w.packed_offset, recv_src_info, dst_row, packed_count, stats, w, stream);
-    hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, w.packed_offset, packed_count, stats, w,
-                                 stream);
-    if (err != hipSuccess) return err;
     const int64_t cap = (int64_t)E * expert_capacity;
+    if (fmt < 0 && dispatch_fuses(T))
+        return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, cap, w.packed_offset, recv_src_info,
+                            dst_row, packed_count, stats, w, stream);
+    hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, cap, w.packed_offset, dst_row, recv_src_info,
+                                 packed_count, stats, w, stream);
+    if (err != hipSuccess) return err;
     if (fmt < 0)
-        launch_scatter<true>(T, K, stream, x, H / 8, w.slot_pack, dst_row, w.tile_base, E, recv_src_info,
-                             w.packed_offset, w.counts, cap, recv_x, no_side());
-    else if (fmt == 0)
-        launch_scatter_cast<0>(x, T, H, K, E, w, dst_row, recv_src_info, w.packed_offset, cap, recv_x, recv_s, stream);
-    else if (fmt == 1)
-        launch_scatter_cast<1>(x, T, H, K, E, w, dst_row, recv_src_info, w.packed_offset, cap, recv_x, recv_s, stream);
+        launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side());
     else
-        launch_scatter_cast<2>(x, T, H, K, E, w, dst_row, recv_src_info, w.packed_offset, cap, recv_x, recv_s, stream);
+        launch_scatter_cast(x, T, H, K, fmt, dst_row, cap, recv_x, recv_s, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
                                   int64_t cap, hipStream_t stream) {
-    if (T <= 0) return hipSuccess;
-    launch_scatter<false>(T, K, stream, x, H / 8, dst_row, nullptr, nullptr, 0, nullptr, nullptr, nullptr, cap,
-                          recv_x, no_side());
+    if (T <= 0) return hipSuccess;  // nothing to enqueue
+    launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side());
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
                                       int H, int K, const int32_t* dst_row, void* recv_q, void* recv_s, int64_t cap,
                                       hipStream_t stream) {
-    if (T <= 0) return hipSuccess;
-    launch_scatter<false>(T, K, stream, xq, H / 16, dst_row, nullptr, nullptr, 0, nullptr, nullptr, nullptr, cap,
-                          recv_q, fp8_side(xs, st, sb, H, fmt, recv_s));
+    if (T <= 0) return hipSuccess;  // nothing to enqueue
+    launch_scatter(T, K, stream, xq, H / 16, dst_row, cap, recv_q, fp8_side(xs, st, sb, H, fmt, recv_s));
     return hipGetLastError();
 }
 

@@ -55,13 +55,16 @@ hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int
                                          int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
                                          int32_t* nrecv, void* workspace, hipStream_t stream);
 
-hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int32_t* expert_offset,
-                                void* workspace, hipStream_t stream);
+// The dispatch plan: the handle (expert_offset, recv_src_idx, dst_row) from
+// the routing alone.
+hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int64_t cap,
+                                int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                                hipStream_t stream);
 
-// get_dispatch_layout and the dispatch plan in one launch.
-hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int32_t* ntpr,
-                                  int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, void* workspace,
-                                  hipStream_t stream);
+// get_dispatch_layout and the dispatch plan from one pass over the routing.
+hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
+                                  int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset,
+                                  int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream);
 
 // Packed fixed-capacity layout: plan + apply; fmt < 0 moves bf16 rows, else
 // casts to FP8 with that scale format.
@@ -69,10 +72,6 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
                                   int expert_capacity, int fmt, void* recv_x, void* recv_s, int32_t* packed_count,
                                   int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
                                   hipStream_t stream);
-
-hipError_t launch_dispatch_apply(const void* x, int64_t T, int H, int K, int E, void* recv_x, int64_t cap,
-                                 const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                                 const void* workspace, hipStream_t stream);
 
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
                                   int64_t cap, hipStream_t stream);
@@ -107,15 +106,10 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st
 hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64_t sb, int fmt, int64_t T, int H,
                             void* out, hipStream_t stream);
 
-hipError_t launch_dispatch_apply_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
-                                     int H, int K, int E, void* recv_q, void* recv_s, int64_t cap,
-                                     const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                                     const void* workspace, hipStream_t stream);
-
-hipError_t launch_dispatch_apply_cast_fp8(const void* x, int64_t T, int H, int K, int E, int fmt, void* recv_q,
-                                          void* recv_s, int64_t cap, const int32_t* expert_offset,
-                                          int32_t* recv_src_idx, int32_t* dst_row, const void* workspace,
-                                          hipStream_t stream);
+// Cast to FP8 on the way: bf16 x moved to the rows of a handle's dst_row as
+// e4m3 codes and per-block scales.
+hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int K, int fmt, const int32_t* dst_row,
+                                           void* recv_q, void* recv_s, int64_t cap, hipStream_t stream);
 
 hipError_t launch_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
                                       int H, int K, const int32_t* dst_row, void* recv_q, void* recv_s, int64_t cap,

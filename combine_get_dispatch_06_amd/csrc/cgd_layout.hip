@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
         s_rank_of[i] = (int16_t)(i / L);
     }
     for (int i = tid; i < R; i += kLayoutTile) s_rank[i] = 0;
-    stage_routing<kMaxTopk>(topk_idx + t0 * K, nt * K, E, s_idx);
+    stage_routing<kMaxTopk, kLayoutTile>(topk_idx + t0 * K, nt * K, E, s_idx);
     __syncthreads();
 
     int e[kMaxTopk];
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     __syncthreads();
     // is_token_in_rank rows of this tile: t0*R is a multiple of 16 because
     // kLayoutTile is
-    store_token_in_rank<RW>(m, s_mask, nt, R, itr + t0 * R);
+    store_token_in_rank<RW, kLayoutTile>(m, s_mask, nt, R, itr + t0 * R);
     if (NPLAN) {
         // the tile's group words and group bases, rank by rank
         const int64_t G = (T + kWave - 1) / kWave;

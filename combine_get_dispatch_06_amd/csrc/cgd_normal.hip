@@ -195,8 +195,8 @@ __global__ __launch_bounds__(kNormScatterWaves* kWave) void normal_scatter_kerne
     if (!CACHED && fill) {
         // rows past the data carry no token, no expert and zero weights
         const int64_t n = max<int64_t>(0, min<int64_t>(rank_offset[R], cap));
-        const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-        const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        const int64_t stride = (int64_t)gridDim.x * (kNormScatterWaves * kWave);
+        const int64_t i0 = (int64_t)blockIdx.x * (kNormScatterWaves * kWave) + threadIdx.x;
         for (int64_t r = n + i0; r < cap; r += stride) recv_src_idx[r] = -1;
         if (recv_topk_idx)
             for (int64_t i = n * K + i0; i < cap * K; i += stride) {

@@ -126,44 +126,37 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
                  size_t workspace_bytes, hipStream_t stream);
 
 /* Dispatch in two steps on one stream: cgd_dispatch is exactly
- * cgd_dispatch_plan followed by cgd_dispatch_apply with the same sizes,
- * capacity, workspace and output pointers. The plan needs only the routing,
- * like the notify stage that precedes data movement in the pages' dispatch
- * (the diagnostic-probes PR page, "Implementation": notify kernels before the
+ * cgd_dispatch_plan followed by cgd_dispatch_cached with the plan's dst_row
+ * and the same capacity. The plan needs only the routing, like the notify
+ * stage that precedes data movement in the pages' dispatch (the
+ * diagnostic-probes PR page, "Implementation": notify kernels before the
  * dispatch data kernels; the first-call latency blog page: tensor sizes are
- * notified in advance), so a caller may enqueue it early.
- *   cgd_dispatch_plan   writes expert_offset and each slot's place (per-tile
- *                       bases, packed slot words, per-expert counts) in the
- *                       workspace.
- *   cgd_dispatch_apply  writes dst_row, recv_src_idx (the source token of every
- *                       data row, -1 for padding rows and rows past the data),
- *                       and copies rows.
- * Between the two calls the workspace and expert_offset must not be modified
- * or used by another call. Mismatched arguments between the calls give wrong
- * rows but never an access outside the given buffers. */
+ * notified in advance), so a caller may enqueue it early; it writes the whole
+ * handle (expert_offset, recv_src_idx, dst_row, as cgd_dispatch describes),
+ * and the row copy that follows moves data only. Batches of one 256-token
+ * tile are planned in one launch, larger ones in two (per-tile ranks, then
+ * final rows). Arguments and errors as cgd_dispatch; the workspace is not
+ * needed once the plan has run. */
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
-                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
+                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-int cgd_dispatch_apply(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                       int64_t recv_capacity, void* recv_x, const int32_t* expert_offset, int32_t* recv_src_idx,
-                       int32_t* dst_row, const void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* cgd_get_dispatch_layout and cgd_dispatch_plan in one launch: both read the
- * same routing, so one pass over each 256-token tile produces the layout
- * outputs (as cgd_get_dispatch_layout, same arguments and rules; no layout
- * workspace is needed) and the plan (as cgd_dispatch_plan, which
- * cgd_dispatch_apply then completes). */
+/* cgd_get_dispatch_layout and cgd_dispatch_plan in one call: both read the
+ * same routing, so one pass over each 256-token tile (one launch, plus the
+ * final-row launch of a batch of several tiles) produces the layout outputs
+ * (as cgd_get_dispatch_layout, same arguments and rules; no layout workspace
+ * is needed) and the dispatch handle (as cgd_dispatch_plan). */
 int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
                                  int num_ranks, int expert_alignment, int64_t recv_capacity,
                                  int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
-                                 uint8_t* is_token_in_rank, int32_t* expert_offset, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream);
+                                 uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
+                                 int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Cached dispatch (Python interface notes, "Dispatch API", handle reuse):
- * copies rows with a dst_row from an earlier cgd_dispatch, skipping the
- * layout work. recv_x[dst_row[t,k]] = x[t] for every dst_row[t,k] in
- * [0, recv_capacity); other entries are skipped. */
+ * copies rows with a dst_row from an earlier cgd_dispatch or
+ * cgd_dispatch_plan, skipping the layout work. recv_x[dst_row[t,k]] = x[t]
+ * for every dst_row[t,k] in [0, recv_capacity); other entries are skipped.
+ * It is also the second step of a planned dispatch. */
 int cgd_dispatch_cached(const void* x, int64_t num_tokens, int hidden, int num_topk, const int32_t* dst_row,
                         void* recv_x, int64_t recv_capacity, hipStream_t stream);
 
@@ -315,24 +308,18 @@ int cgd_cast_to_fp8(const void* x, int64_t num_tokens, int hidden, void* x_fp8, 
 int cgd_cast_back(const void* x_fp8, const void* x_scales, int64_t scale_stride_token, int64_t scale_stride_block,
                   int scale_format, int64_t num_tokens, int hidden, void* out, hipStream_t stream);
 
-/* Dispatch apply with the FP8 tuple as x: as cgd_dispatch_apply (after
- * cgd_dispatch_plan), moving rows of H code bytes and the rows' scales:
+/* Dispatch that casts on the way (the low-latency dispatch with FP8), to the
+ * rows of a dst_row from cgd_dispatch_plan or an earlier dispatch: x is bf16
+ * [T, H]; each chunk is cast once, exactly as cgd_cast_to_fp8 would, and its
+ * codes and scales are written to every destination row: recv_x_fp8
+ * [recv_capacity, H], recv_scales [recv_capacity, H/128]. */
+int cgd_dispatch_cached_cast_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk, int scale_format,
+                                 const int32_t* dst_row, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                 hipStream_t stream);
+
+/* Cached dispatch of the FP8 tuple with a dst_row from an earlier dispatch
+ * or cgd_dispatch_plan: rows of H code bytes and the rows' scales move to
  * recv_x_fp8 [recv_capacity, H], recv_scales [recv_capacity, H/128]. */
-int cgd_dispatch_apply_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
-                           int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
-                           int num_experts, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
-                           const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                           const void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* Dispatch apply that casts on the way (the low-latency dispatch with FP8):
- * x is bf16 [T, H]; each chunk is cast once, exactly as cgd_cast_to_fp8
- * would, and its codes and scales are written to every destination row. */
-int cgd_dispatch_apply_cast_fp8(const void* x, int64_t num_tokens, int hidden, int num_topk, int num_experts,
-                                int scale_format, int64_t recv_capacity, void* recv_x_fp8, void* recv_scales,
-                                const int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row,
-                                const void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* Cached dispatch of the FP8 tuple with a dst_row from an earlier dispatch. */
 int cgd_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
                             int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
                             const int32_t* dst_row, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,

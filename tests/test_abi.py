@@ -24,10 +24,10 @@ def test_header_declares_the_boundary():
     assert names == sorted([
         "cgd_version", "cgd_last_error", "cgd_layout_workspace_bytes", "cgd_dispatch_workspace_bytes",
         "cgd_dispatch_capacity", "cgd_get_dispatch_layout", "cgd_dispatch", "cgd_dispatch_plan",
-        "cgd_dispatch_apply", "cgd_dispatch_cached", "cgd_combine", "cgd_normal_workspace_bytes",
+        "cgd_dispatch_cached", "cgd_combine", "cgd_normal_workspace_bytes",
         "cgd_normal_capacity", "cgd_normal_dispatch", "cgd_normal_dispatch_cached", "cgd_normal_combine",
         "cgd_normal_dispatch_plan", "cgd_normal_dispatch_apply", "cgd_cast_to_fp8", "cgd_cast_back",
-        "cgd_dispatch_apply_fp8", "cgd_dispatch_apply_cast_fp8", "cgd_dispatch_cached_fp8",
+        "cgd_dispatch_cached_cast_fp8", "cgd_dispatch_cached_fp8",
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan",
@@ -120,22 +120,18 @@ def test_dispatch_rejects_bad_arguments():
     assert call(K=17) == -1
 
 
-def test_plan_and_apply_reject_bad_arguments():
+def test_plan_rejects_bad_arguments():
     lib = cgd.load()
-    lib.cgd_dispatch_plan.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                      ctypes.c_size_t, ctypes.c_void_p]
-    lib.cgd_dispatch_apply.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     f = _vp(FAKE)
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, 1 << 20, None) == -2
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, None, 0, None) == -3
-    assert lib.cgd_dispatch_apply(f, 64, 12, 4, 16, 256, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_apply(f, 64, 128, 4, 513, 256, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_apply(f, 64, 128, 4, 16, 256, _vp(FAKE + 4), f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_apply(f, 64, 128, 4, 16, 256, f, f, f, f, f, 16, None) == -3
+    # idx, T, K, E, R, A, cap, off, src, dst, ws, wsb
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, 1 << 20, None) == -2  # capacity
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, f, f, 1 << 20, None) == -1  # alignment
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, None, 0, None) == -3     # workspace
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, None, f, f, 1 << 20, None) == -1  # recv_src_idx
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, None, f, 1 << 20, None) == -1  # dst_row
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, _vp(FAKE + 2), f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 5, 1, 256, f, f, f, f, 1 << 20, None) == -1  # E % R
+    assert lib.cgd_dispatch_plan(f, 64, 17, 16, 4, 1, 2048, f, f, f, f, 1 << 20, None) == -1  # top-k
 
 
 def test_cached_dispatch_and_combine_reject_bad_arguments():
@@ -249,13 +245,14 @@ def test_fp8_entry_points_reject_bad_arguments():
     assert lib.cgd_cast_to_fp8(f, 0, 256, None, None, 2, 1, 0, None) == 0  # no tokens: nothing enqueued
     assert lib.cgd_cast_back(f, f, 2, 1, 0, 4, 64, f, None) == -1
     assert lib.cgd_cast_back(f, f, 2, 1, 2, 0, 256, None, None) == 0
-    # xq, xs, st, sb, fmt, T, H, K, E, cap, rq, rs, off, src, dst, ws, wsb
-    assert lib.cgd_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 200, 4, 16, 256, f, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, 4, 16, 256, f, None, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, 4, 16, 256, f, f, f, f, f, None, 0, None) == -3
-    # x, T, H, K, E, fmt, cap, rq, rs, off, src, dst, ws, wsb
-    assert lib.cgd_dispatch_apply_cast_fp8(f, 64, 256, 4, 16, 5, 256, f, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_apply_cast_fp8(f, 64, 256, 4, 16, 2, 256, f, None, f, f, f, f, 1 << 20, None) == -1
+    # x, T, H, K, fmt, dst, rq, rs, cap
+    assert lib.cgd_dispatch_cached_cast_fp8(f, 64, 256, 4, 5, f, f, f, 256, None) == -1    # format
+    assert lib.cgd_dispatch_cached_cast_fp8(f, 64, 200, 4, 0, f, f, f, 256, None) == -1    # H % 128
+    assert lib.cgd_dispatch_cached_cast_fp8(f, 64, 256, 4, 2, f, f, None, 256, None) == -1  # scales
+    assert lib.cgd_dispatch_cached_cast_fp8(f, 64, 256, 17, 0, f, f, f, 256, None) == -1   # top-k
+    assert lib.cgd_dispatch_cached_cast_fp8(f, 64, 256, 4, 0, f, f, f, -1, None) == -2     # capacity
+    assert lib.cgd_dispatch_cached_cast_fp8(f, 64, 256, 4, 0, _vp(FAKE + 2), f, f, 256, None) == -1
+    assert lib.cgd_dispatch_cached_cast_fp8(None, 0, 256, 4, 0, None, None, None, 0, None) == 0  # nothing enqueued
     assert lib.cgd_dispatch_cached_fp8(f, f, 2, 1, 0, 8, 120, 2, f, f, f, 16, None) == -1
     assert lib.cgd_normal_dispatch_cached_fp8(f, f, 2, 1, 0, 8, 256, 0, f, f, f, 16, None) == -1
     assert lib.cgd_normal_dispatch_apply_fp8(f, f, 2, 1, 0, 64, 256, f, f, 4, 16, 4, f, f, 255, f, f, f, f, f, f,
@@ -266,13 +263,15 @@ def test_fp8_entry_points_reject_bad_arguments():
 def test_layout_and_plan_rejects_bad_arguments():
     lib = cgd.load()
     f = _vp(FAKE)
-    # idx, T, K, E, R, A, cap, ntpr, ntpe, itr, off, ws, wsb
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, f, 1 << 20, None) == -2
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 3, 1, 256, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, None, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, _vp(FAKE + 1), f, f, 1 << 20,
+    # idx, T, K, E, R, A, cap, ntpr, ntpe, itr, off, src, dst, ws, wsb
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, f, f, f, 1 << 20, None) == -2
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 3, 1, 256, f, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, None, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, _vp(FAKE + 1), f, f, f, f, 1 << 20,
                                             None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, None, 0, None) == -3
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, None, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, f, None, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, f, f, None, 0, None) == -3
 
 
 def test_packed_entry_points_reject_bad_arguments():

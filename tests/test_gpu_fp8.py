@@ -128,6 +128,24 @@ def test_cast_on_dispatch_parity(fmt, T, K, E, R, H, p_neg):
     _check_rows(recv, oq, osc, o["dst_row"])
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,K", [(100, 8), (2100, 8), (1100, 16)])
+def test_cached_cast_on_dispatch_equals_planned(fmt, T, K):
+    """Cast on dispatch to the rows of an existing handle gives the same codes
+    and scales as the cast on a fresh dispatch (same kernel, same rows)."""
+    E, R, H = 64, 8, 512
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x = dev_bf16(_x(T, H, seed=T + 1))
+    (q1, s1), h = cgd.dispatch(x, dev_i64(idx), E, R, cast_fp8=fmt)
+    (q2, s2), h2 = cgd.dispatch(x, handle=h, cast_fp8=fmt)
+    torch.cuda.synchronize()
+    assert h2 is h
+    data = h.recv_src_idx >= 0
+    assert torch.equal(q1.view(torch.uint8)[data], q2.view(torch.uint8)[data])
+    assert torch.equal(s1.view(torch.uint8)[data], s2.view(torch.uint8)[data])
+
+
 def test_cast_on_dispatch_prefill_round_trip():
     """Prefill sizes, cast on dispatch; every received row checked on the
     device against the oracle's codes for a sample of tokens, and the combine

@@ -1,7 +1,7 @@
 """The steps bench.py times, captured once in a HIP graph and replayed with
 new inputs: every replay must equal the same step run eagerly on those inputs
-(expert-granular step with the finalize + row-copy apply and with the
-one-launch small-batch dispatch; rank-granular step with the fused layout +
+(expert-granular step with the final rows in the plan and the row-copy
+apply, and with the one-launch small-batch dispatch; rank-granular step with the fused layout +
 plan)."""
 import pytest
 import torch

@@ -134,6 +134,37 @@ def test_plan_then_apply_equals_dispatch(T):
     np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
 
 
+@pytest.mark.parametrize("T,K,cap_extra", [(0, 4, 40), (1, 8, 0), (256, 8, 300), (257, 8, 0), (1500, 8, 0),
+                                         (2100, 8, 5000), (1100, 16, 0)])
+def test_plan_alone_writes_the_handle(T, K, cap_extra):
+    """The plan needs only the routing and writes the whole handle: one
+    launch for one tile, per-tile ranks then final rows for more (the apply
+    afterwards is the broadcast kernel below 16384 slots or at top-k 16, the
+    row copy above). Spare capacity must come back as -1 rows."""
+    E, R, align = 64, 8, 4
+    rng = np.random.default_rng(T + K)
+    idx = np.array([rng.permutation(E)[:K] for _ in range(T)], dtype=np.int64).reshape(T, K)
+    idx[rng.random((T, K)) < 0.05] = -1
+    cap = cgd.dispatch_capacity(T, K, E, align) + cap_extra
+    say(f"[plan alone] T={T} K={K} cap={cap}")
+    plan = cgd.dispatch_plan(dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap)
+    torch.cuda.synchronize()
+    o = oracle.dispatch(None, idx, E, R, align=align, with_rows=False)
+    h = plan.handle
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    src = h.recv_src_idx.cpu().numpy()
+    n = len(o["recv_src_idx"])
+    np.testing.assert_array_equal(src[:n], o["recv_src_idx"])
+    assert (src[n:] == -1).all()
+    if T:
+        x = synth.make_x(synth.WORKLOADS["tiny"].replace(T=T, H=64), seed=T)
+        recv_x, _ = cgd.dispatch_apply(dev_bf16(x), plan)
+        torch.cuda.synchronize()
+        data = np.nonzero(src >= 0)[0]
+        np.testing.assert_array_equal(host_bits(recv_x)[data], x.view(np.uint16)[src[data]])
+
+
 def _edge(T, K, E, R, H, align=1, p_neg=0.0, dup=False, seed=0, all_to=None, cap_extra=0):
     rng = np.random.default_rng(seed)
     if all_to is not None:
@@ -169,8 +200,9 @@ EDGE_CASES = {
     "align32_neg": dict(T=333, K=4, E=64, R=16, H=24, align=32, p_neg=0.2),
     "one_hot_expert": dict(T=2000, K=3, E=64, R=8, H=32, all_to=37),
     "extra_capacity": dict(T=200, K=4, E=32, R=4, H=40, cap_extra=1000),
-    # batches of >= 16384 slots with top-k <= 8 take the finalize + row-copy
-    # apply; the others the single broadcast launch: both sides of the switch
+    # batches of >= 16384 slots with top-k <= 8 get final rows from the plan
+    # and take the row-copy apply; the others the single broadcast launch:
+    # both sides of the switch
     "rowcopy_boundary_T=2048": dict(T=2048, K=8, E=32, R=4, H=64, cap_extra=5000),
     "bcast_boundary_T=2047": dict(T=2047, K=8, E=32, R=4, H=64),
     "rowcopy_ragged_H=1032_align4_neg": dict(T=2049, K=8, E=256, R=8, H=1032, align=4, p_neg=0.1),
