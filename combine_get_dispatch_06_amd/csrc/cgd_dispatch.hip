@@ -752,9 +752,25 @@ static SideRows fp8_side(const void* scales, int64_t st, int64_t sb, int H, int 
     return SideRows{scales, st, sb, H / kFp8Block, fmt == 2 ? 1 : 4, recv_scales};
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n
+                                                                                                                   : 256;
+    }
+    return cus[dev];
+}
+
 // The plan, from the routing alone: rank_kernel, which completes the handle
 // (dst_row, recv_src_idx with its -1 fill) of a one-tile batch itself, else
-// finalize_kernel after it.
+// finalize_kernel after it. A one-tile batch with many spare rows (a large
+// fixed capacity or alignment) takes the FUSED form without rows to move:
+// every block plans the tile in LDS and fills a share of the spare rows.
+constexpr int64_t kSpareRowsPerBlock = 2048;
 static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, int64_t cap,
                               int32_t* expert_offset, int32_t* dst_row, int32_t* recv_src_idx,
                               int32_t* packed_count, int32_t* stats, const DispatchWs& w, hipStream_t stream,
@@ -764,7 +780,26 @@ static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, 
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
     const dim3 grid(ntiles), block(kRankTile);
     const size_t lds = rank_lds_bytes(E, K);
-    const TileOut to{dst_row, recv_src_idx, cap, nullptr, 0, 0, nullptr};
+    const TileOut to{dst_row, recv_src_idx, cap, nullptr, 0, 1, nullptr};  // no rows to move
+    const int64_t spare = cap - std::min<int64_t>(cap, std::max<int64_t>(T, 0) * K);
+    const int64_t fill_blocks = std::min<int64_t>(spare / kSpareRowsPerBlock, device_cus());
+    if (ntiles == 1 && fill_blocks > 1) {
+        const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
+        const dim3 fgrid((unsigned)fill_blocks);
+        if (!layout)
+            hipLaunchKernelGGL((rank_kernel<1, false, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
+                               seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                               w.ticket, none, to);
+        else if (layout->R <= 64)
+            hipLaunchKernelGGL((rank_kernel<1, true, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
+                               seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                               w.ticket, *layout, to);
+        else
+            hipLaunchKernelGGL((rank_kernel<6, true, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
+                               seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                               w.ticket, *layout, to);
+        return hipGetLastError();
+    }
     if (!layout) {
         const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
         hipLaunchKernelGGL((rank_kernel<1, false>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
@@ -866,19 +901,6 @@ hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int 
     if (T <= 0) return hipSuccess;  // nothing to enqueue
     launch_scatter_cast(x, T, H, K, fmt, dst_row, cap, recv_q, recv_s, stream);
     return hipGetLastError();
-}
-
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n
-                                                                                                                   : 256;
-    }
-    return cus[dev];
 }
 
 // Plan and bf16 apply of a batch of at most one tile in one launch (the FUSED

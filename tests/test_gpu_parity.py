@@ -134,13 +134,14 @@ def test_plan_then_apply_equals_dispatch(T):
     np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
 
 
-@pytest.mark.parametrize("T,K,cap_extra", [(0, 4, 40), (1, 8, 0), (256, 8, 300), (257, 8, 0), (1500, 8, 0),
-                                         (2100, 8, 5000), (1100, 16, 0)])
+@pytest.mark.parametrize("T,K,cap_extra", [(0, 4, 40), (1, 8, 0), (256, 8, 300), (200, 8, 40000), (257, 8, 0),
+                                         (1500, 8, 0), (2100, 8, 5000), (1100, 16, 0)])
 def test_plan_alone_writes_the_handle(T, K, cap_extra):
     """The plan needs only the routing and writes the whole handle: one
     launch for one tile, per-tile ranks then final rows for more (the apply
     afterwards is the broadcast kernel below 16384 slots or at top-k 16, the
-    row copy above). Spare capacity must come back as -1 rows."""
+    row copy above; one tile with many spare rows is planned by several
+    blocks). Spare capacity must come back as -1 rows."""
     E, R, align = 64, 8, 4
     rng = np.random.default_rng(T + K)
     idx = np.array([rng.permutation(E)[:K] for _ in range(T)], dtype=np.int64).reshape(T, K)
@@ -198,6 +199,9 @@ EDGE_CASES = {
     "H=8": dict(T=513, K=2, E=4, R=2, H=8),
     "align16": dict(T=1000, K=8, E=256, R=8, H=64, align=16),
     "align32_neg": dict(T=333, K=4, E=64, R=16, H=24, align=32, p_neg=0.2),
+    # one tile with 32256 alignment-padding rows: the plan spreads the -1 fill
+    # over several blocks, each planning the tile
+    "one_tile_align64": dict(T=100, K=4, E=512, R=8, H=16, align=64),
     "one_hot_expert": dict(T=2000, K=3, E=64, R=8, H=32, all_to=37),
     "extra_capacity": dict(T=200, K=4, E=32, R=4, H=40, cap_extra=1000),
     # batches of >= 16384 slots with top-k <= 8 get final rows from the plan
@@ -298,7 +302,7 @@ def test_seeds_sweep_prefill_and_skewed():
 
 
 @pytest.mark.parametrize("case", ["tiny", "prefill", "decode", "skewed", "stress", "R=E=384", "duplicates",
-                                  "ragged_T=1025_neg", "R=1", "K=16_E=512_R=64"])
+                                  "ragged_T=1025_neg", "R=1", "K=16_E=512_R=64", "one_tile_align64"])
 def test_layout_and_plan_in_one_launch(case):
     """The fused launch gives the layout kernel's outputs and the plan that
     dispatch_apply completes into the same permutation, bit for bit."""
