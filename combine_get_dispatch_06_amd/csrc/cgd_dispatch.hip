@@ -76,18 +76,6 @@ size_t rank_lds_bytes(int E, int K) {
 // Expert of a slot word during the duplicate-aware count (-1: not selected).
 __device__ __forceinline__ int slot_expert(int v) { return v < 0 ? -1 : (v & 0xFFFF); }
 
-// Slot loops read the routing from LDS, which keeps the kernel light on
-// registers for any num_topk.
-// seg_cap >= 0 selects the fixed-capacity packed layout: segment e is rows
-// [e*seg_cap, (e+1)*seg_cap) whatever its count (seg_cap < 0: prefix-summed
-// segments of the aligned counts). counts receives every
-// expert's slot count (workspace, for the -1 fill of finalize_kernel); packed_count
-// (min(count, seg_cap)) and stats (accumulates packed_count) are optional.
-// With LAYOUT the kernel also produces get_dispatch_layout's outputs from the
-// same staged tile (rank masks with RW 64-bit words, as the layout kernel):
-// is_token_in_rank rows per tile, per-tile distinct-token counts per rank
-// (rank_part, workspace) summed by the last block into ntpr, and ntpe = the
-// column totals of the tile histograms.
 // recv_src_idx = -1 for every row that holds no data: rows of segment e past
 // its count (alignment padding, unused fixed capacity) and rows past the last
 // segment. Threads are spread over (segment, row) pairs, so each thread needs
@@ -153,14 +141,29 @@ struct TileOut {
     uint4* recv_x;
 };
 
+// rank_kernel. Slot loops read the routing from LDS, which keeps the kernel
+// light on registers for any num_topk. seg_cap >= 0 selects the
+// fixed-capacity packed layout: segment e is rows [e*seg_cap, (e+1)*seg_cap)
+// whatever its count (seg_cap < 0: prefix-summed segments of the aligned
+// counts). counts receives every expert's slot count (workspace, for the -1
+// fill); packed_count (min(count, seg_cap)) and stats (accumulates
+// packed_count) are optional. With LAYOUT the kernel also produces
+// get_dispatch_layout's outputs from the same staged tile (rank masks with RW
+// 64-bit words, as the layout kernel): is_token_in_rank rows per tile,
+// per-tile distinct-token counts per rank (rank_part, workspace) summed by
+// the last block into ntpr, and ntpe = the column totals of the tile
+// histograms.
+//
 // A batch of one tile (decode) finishes from LDS: the kernel writes the
 // final dst_row and recv_src_idx itself and fills the unused rows. FUSED:
 // every block plans the whole batch in LDS (a few microseconds of LDS work,
 // cheaper than a second launch and a second pass over the plan), block 0
 // alone writes the plan's outputs, every block fills a share of the unused
-// rows, and each wave then moves one (token, chunk) item to the token's
-// rows, its x chunk loaded at the start. Larger batches leave packed slot
-// words and tile bases in the workspace for finalize_kernel.
+// rows, and each wave then moves up to kFusedItems (token, chunk) items to
+// the tokens' rows, their x chunks loaded at the start (none with nvec = 0:
+// the plan alone of a one-tile batch with many spare rows). Larger batches
+// leave packed slot words and tile bases in the workspace for
+// finalize_kernel.
 template <int RW, bool LAYOUT, bool FUSED = false>
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
                                                          int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
@@ -642,9 +645,9 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
 }
 
 // Dispatch workspace: ticket | tile bases int32 [tiles, E] | packed slot
-// words int32 [T, K] (plan -> apply) | per-expert slot counts int32 [E] |
-// segment offsets int32 [E+1] of the packed layout (its own copy, so the
-// packed entry points need no offsets argument).
+// words int32 [T, K] (rank_kernel -> finalize_kernel) | per-expert slot
+// counts int32 [E] | segment offsets int32 [E+1] of the packed layout (its
+// own copy, so the packed entry points need no offsets argument).
 struct DispatchWs {
     unsigned int* ticket;
     int32_t* tile_base;
