@@ -356,6 +356,8 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
     """
     lib = load()
     fp8 = isinstance(x, tuple)
+    if fp8 and cast_fp8 is not None:
+        raise ValueError("cast_fp8 casts a bf16 x; x is already an FP8 tuple")
     if fp8:
         q, sc, fmt, st, sb = _fp8_parts(x)
         T, H = q.shape

@@ -326,3 +326,12 @@ def test_layout_and_normal_plan_rejects_bad_arguments():
                                                    None) == -1
     assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 8, 1, f, f, f, f, f, f, 16, None) == -3
     assert lib.cgd_layout_and_normal_dispatch_plan(f, 100, 8, 256, 8, 1, f, f, f, f, f, None, 1 << 20, None) == -3
+
+
+def test_binding_rejects_cast_of_an_fp8_payload():
+    # checked before any device work: an FP8 tuple cannot be cast again
+    import torch
+    q = torch.zeros((2, 128), dtype=torch.uint8)
+    sc = torch.ones((2, 1), dtype=torch.float32)
+    with pytest.raises(ValueError, match="cast_fp8"):
+        cgd.dispatch((q, sc), torch.zeros((2, 1), dtype=torch.int64), 4, 2, cast_fp8=cgd.SCALE_F32)
