@@ -75,3 +75,79 @@ def test_all_small_routings(R):
             np.testing.assert_array_equal(g_recv[data], d["recv_x"][data], err_msg=f"case {c}")
         exp = oracle.combine(d["recv_x"], d["dst_row"], w_np)
         check_combine(out[c], exp, term_magnitude(d["recv_x"], d["dst_row"], w_np))
+
+
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_all_small_routings_rank_granular(R):
+    """The same routings through the rank-granular path: layout + plan in one
+    launch, the apply (rows, send_row, rank-local top-k ids and weights) and
+    the combine of identity experts (x times the token's rank count, exact),
+    all bit for bit."""
+    cases = np.array(list(itertools.product(ROWS, repeat=T)), dtype=np.int64)
+    rng = np.random.default_rng(10 + R)
+    x_bits = (rng.integers(0, 2, (T, H)) << 15 | rng.integers(0x3C00, 0x4100, (T, H))).astype(np.uint16)
+    w_np = rng.random((T, K)).astype(np.float32)
+    idx_all = dev_i64(cases)
+    x, w = dev_bf16(x_bits), dev_f32(w_np)
+    say(f"[brute force, rank-granular] R={R}: {len(cases)} routings")
+    res = []
+    for c in range(len(cases)):
+        idx = idx_all[c]
+        (ntpr, _, ntpe, itr, _), plan = cgd.layout_and_normal_dispatch_plan(idx, E, R)
+        recv, ridx, rw, _, h = cgd.normal_dispatch_apply(x, plan, idx, w)
+        out, cw = cgd.normal_combine(recv, h, rw)
+        res.append((ntpr, ntpe, itr, plan.rank_offset, plan.num_recv_tokens_per_expert, h.send_row,
+                    h.recv_src_idx, ridx, rw.view(torch.int32), recv, out, cw.view(torch.int32)))
+    torch.cuda.synchronize()
+    (ntpr, ntpe, itr, off, nre, send, src, ridx, rw, recv, out, cw) = (_stack([r[i] for r in res])
+                                                                       for i in range(12))
+    recv, out = recv.view(np.uint16), out.view(np.uint16)
+    for c, idx in enumerate(cases):
+        o_ntpr, o_ntpe, o_itr = oracle.layout(idx, E, R)
+        np.testing.assert_array_equal(ntpr[c], o_ntpr, err_msg=f"case {c}")
+        np.testing.assert_array_equal(ntpe[c], o_ntpe, err_msg=f"case {c}")
+        np.testing.assert_array_equal(itr[c], o_itr, err_msg=f"case {c}")
+        o = oracle.dispatch_normal(x_bits, o_itr, E, K, o_ntpe, idx, w_np)
+        np.testing.assert_array_equal(off[c], o["rank_offset"], err_msg=f"case {c}")
+        np.testing.assert_array_equal(nre[c], o["num_recv_tokens_per_expert"], err_msg=f"case {c}")
+        np.testing.assert_array_equal(send[c], o["send_row"], err_msg=f"case {c}")
+        np.testing.assert_array_equal(src[c], o["recv_src_idx"], err_msg=f"case {c}")
+        np.testing.assert_array_equal(ridx[c], o["recv_topk_idx"], err_msg=f"case {c}")
+        np.testing.assert_array_equal(rw[c], o["recv_topk_weights"].view(np.int32), err_msg=f"case {c}")
+        data = o["recv_src_idx"] >= 0
+        np.testing.assert_array_equal(recv[c][data], o["recv_x"][data], err_msg=f"case {c}")
+        o_out, o_cw = oracle.combine_normal(o["recv_x"], o["send_row"], o["recv_topk_weights"])
+        np.testing.assert_array_equal(out[c], o_out, err_msg=f"case {c}")
+        np.testing.assert_array_equal(cw[c], o_cw.view(np.int32), err_msg=f"case {c}")
+
+
+@pytest.mark.parametrize("R", [1, 2, 4])
+def test_all_small_routings_packed(R):
+    """The same routings through the fixed-capacity packed layout with room
+    for 2 rows per expert (a third token of an expert is dropped) and its
+    combine."""
+    cap = 2
+    cases = np.array(list(itertools.product(ROWS, repeat=T)), dtype=np.int64)
+    rng = np.random.default_rng(20 + R)
+    x_bits = (rng.integers(0, 2, (T, H)) << 15 | rng.integers(0x3C00, 0x4100, (T, H))).astype(np.uint16)
+    w_np = rng.random((T, K)).astype(np.float32)
+    idx_all = dev_i64(cases)
+    x, w = dev_bf16(x_bits), dev_f32(w_np)
+    say(f"[brute force, packed] R={R}: {len(cases)} routings")
+    res = []
+    for c in range(len(cases)):
+        recv, count, h = cgd.low_latency_dispatch(x, idx_all[c], E, R, expert_capacity=cap)
+        out = cgd.low_latency_combine(recv, w, h)
+        res.append((count, h.recv_src_info, h.dst_row, recv, out))
+    torch.cuda.synchronize()
+    count, info, dst, recv, out = (_stack([r[i] for r in res]) for i in range(5))
+    recv, out = recv.view(np.uint16), out.view(np.uint16)
+    for c, idx in enumerate(cases):
+        o = oracle.dispatch_packed(x_bits, idx, E, R, cap)
+        np.testing.assert_array_equal(count[c], o["packed_recv_count"], err_msg=f"case {c}")
+        np.testing.assert_array_equal(info[c], o["recv_src_info"], err_msg=f"case {c}")
+        np.testing.assert_array_equal(dst[c], o["dst_row"], err_msg=f"case {c}")
+        valid = o["recv_src_info"] >= 0
+        np.testing.assert_array_equal(recv[c][valid], o["packed_recv_x"][valid], err_msg=f"case {c}")
+        y = o["packed_recv_x"].reshape(E * cap, H)
+        check_combine(out[c], oracle.combine(y, o["dst_row"], w_np), term_magnitude(y, o["dst_row"], w_np))
