@@ -52,6 +52,7 @@
 // (sequential stores) lose more on the 8x scattered re-reads of x than they
 // gain.
 #include <algorithm>
+#include <atomic>
 
 #include "cgd_device.h"
 #include "cgd_launch.h"
@@ -755,17 +756,18 @@ static SideRows fp8_side(const void* scales, int64_t st, int64_t sb, int H, int 
     return SideRows{scales, st, sb, H / kFp8Block, fmt == 2 ? 1 : 4, recv_scales};
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; host threads may
+// race on the cache, each storing the same value).
 static int device_cus() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n
-                                                                                                                   : 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 // The plan, from the routing alone: rank_kernel, which completes the handle
