@@ -75,7 +75,7 @@ const char* cgd_last_error(void);
  * concurrently need separate workspaces. */
 size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
 
-/* Workspace bytes cgd_dispatch (and the plan/apply pair) needs (host only;
+/* Workspace bytes cgd_dispatch and cgd_dispatch_plan need (host only;
  * 0 if invalid). Same zero-fill and reuse rules as the layout workspace. */
 size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts);
 
