@@ -13,6 +13,7 @@ Expert-granular path (one received row per selected expert):
     combined = combine(expert_out, handle, topk_weights)
     layout, plan = layout_and_dispatch_plan(topk_idx, num_experts, num_ranks)   # one routing pass
     recv_x, handle = dispatch_apply(x, plan)
+    layout, recv_x, handle = layout_and_dispatch(x, topk_idx, num_experts, num_ranks)  # one launch at decode
 
 Rank-granular path (normal mode, one row per (token, flagged rank)):
 
@@ -97,6 +98,9 @@ def load():
     lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_plan.restype = i32
     lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp]
+    lib.cgd_layout_and_dispatch.restype = i32
+    lib.cgd_layout_and_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp,
+                                            sz, vp]
     lib.cgd_layout_and_dispatch_plan.restype = i32
     lib.cgd_layout_and_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz,
                                                  vp]
@@ -483,6 +487,42 @@ def layout_and_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks
                                                 _ptr(ws), ws.numel(), _stream(dev)))
     h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
     return (ntpr, None, ntpe, itr, None), DispatchPlan(h, ws, T)
+
+
+def layout_and_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                        expert_alignment: int = 1, recv_capacity: int | None = None, recv_x: torch.Tensor | None = None):
+    """get_dispatch_layout and dispatch (bf16 x) in one call; a batch of at most
+    256 tokens takes one launch.
+    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), recv_x, DispatchHandle)."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, H = x.shape
+    dev = x.device
+    if topk_idx.shape[0] != T or topk_idx.device != dev:
+        raise ValueError("topk_idx must be [num_tokens, num_topk] on x's device")
+    K = topk_idx.shape[1]
+    with torch.cuda.device(dev):
+        need = int(lib.cgd_dispatch_capacity(T, K, num_experts, expert_alignment))
+        cap = need if recv_capacity is None else int(recv_capacity)
+        if recv_x is None:
+            recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+        if recv_x.shape != (cap, H):
+            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        ntpr = torch.empty(num_ranks, dtype=torch.int32, device=dev)
+        ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        itr = torch.empty((T, num_ranks), dtype=torch.bool, device=dev)
+        off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        dst = torch.empty((T, K), dtype=torch.int32, device=dev)
+        ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts))
+        _check("cgd_layout_and_dispatch",
+               lib.cgd_layout_and_dispatch(_ptr(x), T, H, _ptr(topk_idx), K, num_experts, num_ranks, expert_alignment,
+                                           _ptr(recv_x), cap, _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off),
+                                           _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+    h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+    return (ntpr, None, ntpe, itr, None), recv_x, h
 
 
 def dispatch_apply(x, plan: DispatchPlan, recv_x=None, cast_fp8: int | None = None):

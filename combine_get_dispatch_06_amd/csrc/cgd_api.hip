@@ -172,6 +172,15 @@ int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
     return CGD_OK;
 }
 
+// Checks of get_dispatch_layout's outputs when another entry point produces them too.
+static int check_layout_outputs(int64_t T, const int32_t* ntpr, const int32_t* ntpe, const uint8_t* itr) {
+    if (!ntpr || !ntpe) return fail(CGD_ERR_INVALID_ARG, "null count output pointer");
+    if (T > 0 && !itr) return fail(CGD_ERR_INVALID_ARG, "null is_token_in_rank");
+    if (!aligned(ntpr, 4) || !aligned(ntpe, 4)) return fail(CGD_ERR_INVALID_ARG, "misaligned count output");
+    if (!aligned(itr, 16)) return fail(CGD_ERR_INVALID_ARG, "is_token_in_rank must be 16-byte aligned");
+    return CGD_OK;
+}
+
 int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
                                  int num_ranks, int expert_alignment, int64_t recv_capacity,
                                  int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
@@ -180,12 +189,8 @@ int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, in
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
                              expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
     if (rc) return rc;
-    if (!num_tokens_per_rank || !num_tokens_per_expert)
-        return fail(CGD_ERR_INVALID_ARG, "null count output pointer");
-    if (num_tokens > 0 && !is_token_in_rank) return fail(CGD_ERR_INVALID_ARG, "null is_token_in_rank");
-    if (!aligned(num_tokens_per_rank, 4) || !aligned(num_tokens_per_expert, 4))
-        return fail(CGD_ERR_INVALID_ARG, "misaligned count output");
-    if (!aligned(is_token_in_rank, 16)) return fail(CGD_ERR_INVALID_ARG, "is_token_in_rank must be 16-byte aligned");
+    if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
+        return rc;
     hipError_t err = cgd::launch_layout_and_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
                                                  expert_alignment, recv_capacity, num_tokens_per_rank,
                                                  num_tokens_per_expert, is_token_in_rank, expert_offset, recv_src_idx,
@@ -213,6 +218,35 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
     err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment, recv_capacity,
                                     expert_offset, recv_src_idx, dst_row, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
+    err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
+    if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
+    return CGD_OK;
+}
+
+int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                            int num_experts, int num_ranks, int expert_alignment, void* recv_x,
+                            int64_t recv_capacity, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
+                            int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
+                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+    if (rc) return rc;
+    if ((rc = check_rows_args(x, num_tokens, hidden, recv_capacity, recv_x))) return rc;
+    if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
+        return rc;
+    hipError_t err;
+    if (cgd::dispatch_fuses(num_tokens)) {  // one tile: layout, plan and rows in one launch
+        err = cgd::launch_layout_and_dispatch_fused(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks,
+                                                    expert_alignment, recv_x, recv_capacity, num_tokens_per_rank,
+                                                    num_tokens_per_expert, is_token_in_rank, expert_offset,
+                                                    recv_src_idx, dst_row, workspace, stream);
+        if (err != hipSuccess) return hip_fail(err, "fused layout and dispatch launch");
+        return CGD_OK;
+    }
+    err = cgd::launch_layout_and_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment,
+                                      recv_capacity, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+                                      expert_offset, recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "layout and dispatch plan launch");
     err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
     return CGD_OK;

@@ -909,11 +909,12 @@ hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int 
 }
 
 // Plan and bf16 apply of a batch of at most one tile in one launch (the FUSED
-// rank kernel); seg_cap >= 0 for the fixed-capacity packed layout.
+// rank kernel); seg_cap >= 0 for the fixed-capacity packed layout; with
+// layout, get_dispatch_layout's outputs from the same launch.
 static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, const void* x,
                                int H, void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
                                int32_t* dst_row, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
-                               hipStream_t stream) {
+                               hipStream_t stream, const LayoutOut* layout = nullptr) {
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
     const int nvec = H / 8;
@@ -929,9 +930,17 @@ static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E,
     const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
     const TileOut fc{dst_row, recv_src_idx, cap, reinterpret_cast<const uint4*>(x), nvec, nchunk,
                      reinterpret_cast<uint4*>(recv_x)};
-    hipLaunchKernelGGL((rank_kernel<1, false, true>), grid, block, rank_lds_bytes(E, K), stream, topk_idx, T, K, E,
-                       ebits, A, seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
-                       w.ticket, none, fc);
+    const size_t lds = rank_lds_bytes(E, K);
+#define CGD_FUSED(RW, LAYOUT, LO)                                                                                   \
+    hipLaunchKernelGGL((rank_kernel<RW, LAYOUT, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap, \
+                       w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, LO, fc)
+    if (!layout)
+        CGD_FUSED(1, false, none);
+    else if (layout->R <= 64)
+        CGD_FUSED(1, true, *layout);
+    else
+        CGD_FUSED(6, true, *layout);
+#undef CGD_FUSED
     return hipGetLastError();
 }
 
@@ -942,6 +951,16 @@ hipError_t launch_dispatch_fused(const void* x, int64_t T, int H, const int64_t*
                                  int32_t* dst_row, void* workspace, hipStream_t stream) {
     return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_x, cap, expert_offset, recv_src_idx, dst_row, nullptr,
                         nullptr, dispatch_ws(workspace, T, K, E), stream);
+}
+
+hipError_t launch_layout_and_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                            int R, int A, void* recv_x, int64_t cap, int32_t* ntpr, int32_t* ntpe,
+                                            uint8_t* itr, int32_t* expert_offset, int32_t* recv_src_idx,
+                                            int32_t* dst_row, void* workspace, hipStream_t stream) {
+    const DispatchWs w = dispatch_ws(workspace, T, K, E);
+    const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
+    return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_x, cap, expert_offset, recv_src_idx, dst_row, nullptr,
+                        nullptr, w, stream, &lo);
 }
 
 hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,

@@ -38,6 +38,11 @@ bool dispatch_fuses(int64_t T);
 hipError_t launch_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
                                  void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
                                  int32_t* dst_row, void* workspace, hipStream_t stream);
+// The same with get_dispatch_layout's outputs from the same launch.
+hipError_t launch_layout_and_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                            int R, int A, void* recv_x, int64_t cap, int32_t* ntpr, int32_t* ntpe,
+                                            uint8_t* itr, int32_t* expert_offset, int32_t* recv_src_idx,
+                                            int32_t* dst_row, void* workspace, hipStream_t stream);
 
 // The rank-granular plan's workspace arrays (group words, group bases, tile
 // counts / bases), as launch_normal_plan leaves them.

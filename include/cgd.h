@@ -152,6 +152,18 @@ int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, in
                                  uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
                                  int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* cgd_get_dispatch_layout and cgd_dispatch in one call: the layout outputs
+ * (as cgd_get_dispatch_layout; no layout workspace is needed) and the
+ * dispatch (as cgd_dispatch: handle and rows), same arguments and rules.
+ * A batch of at most 256 tokens takes one launch (layout, plan and rows, the
+ * decode case); larger ones are cgd_layout_and_dispatch_plan followed by
+ * cgd_dispatch_cached. */
+int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                            int num_experts, int num_ranks, int expert_alignment, void* recv_x,
+                            int64_t recv_capacity, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
+                            int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Cached dispatch (Python interface notes, "Dispatch API", handle reuse):
  * copies rows with a dst_row from an earlier cgd_dispatch or
  * cgd_dispatch_plan, skipping the layout work. recv_x[dst_row[t,k]] = x[t]

@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_cached_cast_fp8", "cgd_dispatch_cached_fp8",
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
+        "cgd_layout_and_dispatch",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan",
     ])
 
@@ -335,3 +336,20 @@ def test_binding_rejects_cast_of_an_fp8_payload():
     sc = torch.ones((2, 1), dtype=torch.float32)
     with pytest.raises(ValueError, match="cast_fp8"):
         cgd.dispatch((q, sc), torch.zeros((2, 1), dtype=torch.int64), 4, 2, cast_fp8=cgd.SCALE_F32)
+
+
+def test_layout_and_dispatch_rejects_bad_arguments():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    # x, T, H, idx, K, E, R, A, recv, cap, ntpr, ntpe, itr, off, src, dst, ws, wsb
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 255, f, f, f, f, f, f, f, 1 << 20, None) == -2
+    assert lib.cgd_layout_and_dispatch(f, 64, 100, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 3, 1, f, 256, f, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, None, f, f, f, f, f, f, 1 << 20,
+                                       None) == -1
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, _vp(FAKE + 4), f, f, f, f, 1 << 20,
+                                       None) == -1
+    assert lib.cgd_layout_and_dispatch(_vp(FAKE + 8), 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, 1 << 20,
+                                       None) == -1
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, None, 0, None) == -3
+    assert lib.cgd_last_error()

@@ -1,8 +1,8 @@
 """The steps bench.py times, captured once in a HIP graph and replayed with
 new inputs: every replay must equal the same step run eagerly on those inputs
 (expert-granular step with the final rows in the plan and the row-copy
-apply, and with the one-launch small-batch dispatch; rank-granular step with the fused layout +
-plan)."""
+apply; the one-launch small-batch dispatch, with and without the layout
+outputs; rank-granular step with the fused layout + plan)."""
 import pytest
 import torch
 
@@ -26,6 +26,12 @@ def _small_step(x, idx, wt, w, out):
     return [h.expert_offset, h.dst_row, h.recv_src_idx, out]
 
 
+def _small_layout_step(x, idx, wt, w, out):
+    (ntpr, _, ntpe, itr, _), recv, h = cgd.layout_and_dispatch(x, idx, w.E, w.R)
+    cgd.combine(recv, h, wt, out=out)
+    return [ntpr, ntpe, itr, h.expert_offset, h.dst_row, h.recv_src_idx, out]
+
+
 def _normal_step(x, idx, wt, w, out):
     (ntpr, _, ntpe, itr, _), plan = cgd.layout_and_normal_dispatch_plan(idx, w.E, w.R)
     recv, ridx, rw, _, h = cgd.normal_dispatch_apply(x, plan, idx, wt)
@@ -33,10 +39,12 @@ def _normal_step(x, idx, wt, w, out):
     return [ntpr, ntpe, itr, plan.rank_offset, h.send_row, h.recv_src_idx, ridx, out]
 
 
-@pytest.mark.parametrize("kind,T", [("expert", 2500), ("small", 200), ("normal", 2500), ("normal", 100)])
+@pytest.mark.parametrize("kind,T", [("expert", 2500), ("small", 200), ("small_layout", 128), ("normal", 2500),
+                                    ("normal", 100)])
 def test_step_replays_from_a_captured_graph(kind, T):
     w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
-    step = {"expert": _expert_step, "small": _small_step, "normal": _normal_step}[kind]
+    step = {"expert": _expert_step, "small": _small_step, "small_layout": _small_layout_step,
+            "normal": _normal_step}[kind]
     inputs = [synth.make_inputs(w, seed=s) for s in range(5)]
     sx = dev_bf16(inputs[0]["x"])
     sidx = dev_i64(inputs[0]["topk_idx"])

@@ -330,6 +330,34 @@ def test_layout_and_plan_in_one_launch(case):
     np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), d["recv_src_idx"])
 
 
+@pytest.mark.parametrize("T,K,E,R,align,p_neg", [(1, 8, 256, 16, 1, 0.0), (128, 8, 256, 16, 1, 0.1),
+                                                  (256, 4, 384, 384, 4, 0.2), (200, 16, 512, 64, 1, 0.0),
+                                                  (100, 3, 8, 2, 16, 0.3), (257, 8, 64, 8, 1, 0.0),
+                                                  (2100, 8, 256, 8, 1, 0.05)])
+def test_layout_and_dispatch_in_one_call(T, K, E, R, align, p_neg):
+    """get_dispatch_layout and dispatch in one call (one launch up to 256
+    tokens, else the plan and the row copy): layout outputs, handle and rows
+    equal the oracle's, bit for bit."""
+    rng = np.random.default_rng(7 * T + K)
+    idx = np.array([rng.permutation(E)[:K] for _ in range(T)], dtype=np.int64).reshape(T, K)
+    idx[rng.random((T, K)) < p_neg] = -1
+    x = synth.make_x(synth.WORKLOADS["tiny"].replace(T=T, H=72), seed=T)
+    say(f"[layout and dispatch] T={T} K={K} E={E} R={R} align={align}")
+    (ntpr, _, ntpe, itr, _), recv_x, h = cgd.layout_and_dispatch(dev_bf16(x), dev_i64(idx), E, R,
+                                                                 expert_alignment=align)
+    torch.cuda.synchronize()
+    o = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), o[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), o[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), o[2])
+    d = oracle.dispatch(x, idx, E, R, align=align)
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), d["expert_offset"])
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), d["dst_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), d["recv_src_idx"])
+    data = d["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(host_bits(recv_x)[data], d["recv_x"][data])
+
+
 def test_launches_split_over_token_ranges():
     """Batches larger than one grid (work-item ids are 32-bit: 2^25 waves per
     launch) are issued over token ranges. At hidden 8 and top-1 a token is
