@@ -9,16 +9,16 @@
  *
  *  - layout: from the get_dispatch_layout API page (sgl-kernel-npu deep_ep
  *    docs), sections "Parameters" and "Return Values": topk_idx is int64
- *    [num_tokens, num_topk]; num_tokens_per_rank is int32 [num_ranks], the
- *    number of tokens assigned to each rank; num_tokens_per_expert is int32
- *    [num_experts], the number of tokens each expert receives;
- *    is_token_in_rank is bool [num_tokens, num_ranks]. Section "Notes":
- *    num_experts must divide evenly over the ranks.
+ *    [num_tokens, num_topk]; num_tokens_per_rank is int32 [num_ranks], how
+ *    many tokens go to each rank; num_tokens_per_expert is int32
+ *    [num_experts], how many token slots land on each expert;
+ *    is_token_in_rank is bool [num_tokens, num_ranks]. Section "Notes": the
+ *    expert count is a multiple of the rank count.
  *  - expert -> rank map: DeepEP legacy test analysis page, low-latency
  *    per-expert check excerpt: local expert i of rank r has global id
  *    r * num_local_experts + i, i.e. contiguous blocks, rank(e) = e / L.
- *  - "-1 means not selected": DeepEP Python interface notes ("4 Python接口"),
- *    section "Dispatch API", input parameter topk_idx.
+ *  - a topk_idx entry of -1 marks an unselected slot: DeepEP Python interface
+ *    notes ("4 Python接口"), section "Dispatch API", input parameter topk_idx.
  *  - expert_alignment: same section; per-expert receive counts are rounded up
  *    to a multiple of it (default 1).
  *  - dispatch moves each token's row to the receivers of its selected experts
@@ -214,8 +214,8 @@ int oracle_combine(const uint16_t* y, int64_t rows, int64_t H, const int32_t* ds
  * divides (combined_x - bias_0 - bias_1) by is_token_in_rank.sum(1) to get x
  * back. DeepEP Python interface notes, "Dispatch API": recv_topk_idx
  * [num_recv, num_topk] int64 and recv_topk_weights [num_recv, num_topk]
- * float accompany recv_x; -1 means not selected; the per-expert counts are
- * aligned to expert_alignment.
+ * float accompany recv_x, with -1 for a slot without an expert here; the
+ * per-expert counts are aligned to expert_alignment.
  *
  * Readings: a token is received once by every rank that is_token_in_rank
  * flags for it; rank r's rows form one segment, segments in rank order, rows
