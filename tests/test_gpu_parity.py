@@ -135,7 +135,8 @@ def test_plan_then_apply_equals_dispatch(T):
 
 
 @pytest.mark.parametrize("T,K,cap_extra", [(0, 4, 40), (1, 8, 0), (256, 8, 300), (200, 8, 40000), (257, 8, 0),
-                                         (1500, 8, 0), (2100, 8, 5000), (1100, 16, 0)])
+                                         (1500, 8, 0), (2100, 8, 5000), (1100, 16, 0), (8192, 4, 0),
+                                         (8193, 2, 700)])
 def test_plan_alone_writes_the_handle(T, K, cap_extra):
     """The plan needs only the routing and writes the whole handle: one
     launch for one tile, per-tile ranks then final rows for more (the apply
