@@ -37,7 +37,10 @@
  *   - Device-side data preconditions are not checked on the host: topk_idx
  *     entries are expected in [-1, num_experts). A value outside that range
  *     is treated as -1 (not selected) by every kernel, so it never causes an
- *     out-of-bounds access.
+ *     out-of-bounds access. The pages' routing never repeats an expert within
+ *     a token; if a row does, every selected slot still gets a row of its
+ *     own, in ascending (token, slot) order like any other, and the token
+ *     counts once per rank in the layout.
  */
 #ifndef CGD_H
 #define CGD_H
