@@ -1,0 +1,95 @@
+"""The combines read only rows that hold data.
+
+A receive buffer has rows without data: alignment padding, spare capacity
+past the last segment, the unused tail of each fixed-capacity packed segment
+and the rank-granular buffer's spare rows (recv_src_idx / recv_src_info < 0
+marks them). Each test fills exactly those rows with a bf16 NaN and checks
+that the combine output is bit-identical to the combine of the untouched
+buffer: a NaN in any row that is read, even one weighted by 0, would reach
+the output."""
+import numpy as np
+import pytest
+import torch
+
+import combine_get_dispatch_06_amd as cgd
+import synth
+from gpu_util import DEV, dev_bf16, dev_f32, dev_i64, say
+
+pytestmark = pytest.mark.gpu
+
+NAN_BITS = 0x7FC0  # bf16 quiet NaN
+
+
+def _inputs(T, K, E, H, seed, p_neg=0.2):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    idx[rng.random((T, K)) < p_neg] = -1
+    x = synth.normal_bf16(synth.stream_key(seed, 97, 1), T * H).reshape(T, H)
+    w = synth.softmax_weights(synth.stream_key(seed, 97, 3), T, K)
+    return idx, x, w
+
+
+def _poisoned(buf, no_data):
+    """A copy of buf whose rows flagged in no_data (one flag per row) are NaN."""
+    assert no_data.any(), "the case must have rows without data"
+    y = buf.clone()
+    rows = y.view(torch.int16).view(-1, buf.shape[-1])
+    assert rows.shape[0] == no_data.size
+    rows[torch.from_numpy(no_data.reshape(-1)).to(DEV)] = NAN_BITS
+    return y
+
+
+def _same_bits(a, b):
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.isnan(b.float()).any()
+
+
+@pytest.mark.parametrize("T,K,E,R,H,align,extra", [(300, 4, 64, 8, 64, 16, 500), (2100, 8, 32, 4, 136, 8, 3000),
+                                                   (128, 8, 256, 16, 256, 32, 0)])
+def test_expert_combine_reads_only_rows_with_data(T, K, E, R, H, align, extra):
+    idx, x, w = _inputs(T, K, E, H, seed=T)
+    cap = cgd.dispatch_capacity(T, K, E, align) + extra
+    say(f"[unused rows, expert] T={T} K={K} E={E} align={align} cap={cap}")
+    recv, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap)
+    wd = dev_f32(w)
+    clean = cgd.combine(recv, h, wd)
+    torch.cuda.synchronize()
+    no_data = h.recv_src_idx.cpu().numpy() < 0
+    _same_bits(clean, cgd.combine(_poisoned(recv, no_data), h, wd))
+
+
+@pytest.mark.parametrize("T,K,E,R,H,cap", [(128, 8, 64, 8, 64, 40), (3000, 8, 32, 4, 72, 900),
+                                           (2000, 4, 16, 4, 64, 400)])
+def test_packed_combine_reads_only_rows_with_data(T, K, E, R, H, cap):
+    """The last case overflows some experts' capacity and leaves others
+    with spare rows: the dropped slots are not read either."""
+    idx, x, w = _inputs(T, K, E, H, seed=T + 1)
+    counts = np.bincount(idx[idx >= 0], minlength=E)
+    say(f"[unused rows, packed] T={T} K={K} E={E} cap={cap} counts {counts.min()}..{counts.max()}")
+    if cap == 400:
+        assert counts.max() > cap > counts.min()
+    recv, _, h = cgd.low_latency_dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_capacity=cap)
+    wd = dev_f32(w)
+    clean = cgd.low_latency_combine(recv, wd, h)
+    torch.cuda.synchronize()
+    no_data = h.recv_src_info.cpu().numpy() < 0
+    _same_bits(clean, cgd.low_latency_combine(_poisoned(recv, no_data), wd, h))
+
+
+@pytest.mark.parametrize("T,K,E,R,H,align,extra", [(300, 4, 32, 4, 40, 4, 999), (2000, 8, 64, 8, 64, 8, 100)])
+def test_normal_combine_reads_only_rows_with_data(T, K, E, R, H, align, extra):
+    idx, x, w = _inputs(T, K, E, H, seed=T + 2)
+    idx_d = dev_i64(idx)
+    _, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx_d, E, R)
+    cap = cgd.normal_capacity(T, K, R) + extra
+    say(f"[unused rows, rank-granular] T={T} K={K} E={E} R={R} cap={cap}")
+    recv, _, rw, _, h = cgd.normal_dispatch(dev_bf16(x), itr, num_tokens_per_expert=ntpe, topk_idx=idx_d,
+                                            topk_weights=dev_f32(w), num_experts=E, expert_alignment=align,
+                                            recv_capacity=cap)
+    clean, cw = cgd.normal_combine(recv, h, rw)
+    torch.cuda.synchronize()
+    no_data = h.recv_src_idx.cpu().numpy() < 0
+    bad, cw2 = cgd.normal_combine(_poisoned(recv, no_data), h, rw)
+    _same_bits(clean, bad)
+    assert torch.equal(cw.view(torch.int32), cw2.view(torch.int32))
