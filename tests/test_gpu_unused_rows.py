@@ -1,12 +1,15 @@
-"""The combines read only rows that hold data.
+"""Rows without data are neither read by the combines nor written by the
+dispatches.
 
 A receive buffer has rows without data: alignment padding, spare capacity
 past the last segment, the unused tail of each fixed-capacity packed segment
 and the rank-granular buffer's spare rows (recv_src_idx / recv_src_info < 0
-marks them). Each test fills exactly those rows with a bf16 NaN and checks
-that the combine output is bit-identical to the combine of the untouched
-buffer: a NaN in any row that is read, even one weighted by 0, would reach
-the output."""
+marks them). The combine tests fill exactly those rows with a bf16 NaN and
+check that the combine output is bit-identical to the combine of the
+untouched buffer: a NaN in any row that is read, even one weighted by 0,
+would reach the output. The dispatch tests hand the dispatch a receive
+buffer that is the head of a larger sentinel-filled allocation and check
+that only the rows with data changed, each to its source row."""
 import numpy as np
 import pytest
 import torch
@@ -93,3 +96,66 @@ def test_normal_combine_reads_only_rows_with_data(T, K, E, R, H, align, extra):
     bad, cw2 = cgd.normal_combine(_poisoned(recv, no_data), h, rw)
     _same_bits(clean, bad)
     assert torch.equal(cw.view(torch.int32), cw2.view(torch.int32))
+
+
+# ---- the dispatches write only rows that receive data ----
+SENTINEL = 0x5A5A  # a finite bf16 bit pattern
+GUARD = 64         # rows past the receive buffer, inside the same allocation
+
+
+def _guarded(rows, H):
+    """A receive buffer of `rows` rows, the first rows of a sentinel-filled
+    allocation GUARD rows longer, and that allocation."""
+    big = torch.full((rows + GUARD, H), SENTINEL, dtype=torch.int16, device=DEV)
+    return big[:rows].view(torch.bfloat16), big
+
+
+def _check_writes(big, rows, src, x):
+    """Rows with src >= 0 hold x[src], every other row and the guard rows
+    still hold the sentinel."""
+    torch.cuda.synchronize()
+    g = big.cpu().numpy()
+    assert (g[rows:] == SENTINEL).all(), "write past the receive buffer"
+    src = src.reshape(-1)
+    assert (g[:rows][src < 0] == SENTINEL).all(), "write to a row without data"
+    np.testing.assert_array_equal(g[:rows][src >= 0], x.view(np.int16)[src[src >= 0]])
+
+
+@pytest.mark.parametrize("T,K,E,R,H,align,extra", [(300, 4, 64, 8, 64, 16, 500), (2100, 8, 32, 4, 136, 8, 3000),
+                                                   (128, 8, 256, 16, 256, 32, 0), (1100, 16, 64, 8, 64, 4, 77)])
+def test_expert_dispatch_writes_only_rows_with_data(T, K, E, R, H, align, extra):
+    """The broadcast apply, the row copy, the one-launch dispatch and the
+    top-16 apply."""
+    idx, x, _ = _inputs(T, K, E, H, seed=T + 3)
+    cap = cgd.dispatch_capacity(T, K, E, align) + extra
+    say(f"[writes, expert] T={T} K={K} E={E} align={align} cap={cap}")
+    recv, big = _guarded(cap, H)
+    _, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap, recv_x=recv)
+    torch.cuda.synchronize()
+    _check_writes(big, cap, h.recv_src_idx.cpu().numpy(), x)
+
+
+@pytest.mark.parametrize("T,K,E,R,H,cap", [(128, 8, 64, 8, 64, 40), (2000, 4, 16, 4, 64, 400)])
+def test_packed_dispatch_writes_only_rows_with_data(T, K, E, R, H, cap):
+    idx, x, _ = _inputs(T, K, E, H, seed=T + 4)
+    say(f"[writes, packed] T={T} K={K} E={E} cap={cap}")
+    recv, big = _guarded(E * cap, H)
+    _, _, h = cgd.low_latency_dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_capacity=cap,
+                                       out=recv.view(E, cap, H))
+    torch.cuda.synchronize()
+    _check_writes(big, E * cap, h.recv_src_info.cpu().numpy(), x)
+
+
+@pytest.mark.parametrize("T,K,E,R,H,align,extra", [(300, 4, 32, 4, 40, 4, 999), (2000, 8, 64, 8, 64, 8, 100)])
+def test_normal_dispatch_writes_only_rows_with_data(T, K, E, R, H, align, extra):
+    idx, x, w = _inputs(T, K, E, H, seed=T + 5)
+    idx_d = dev_i64(idx)
+    _, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx_d, E, R)
+    cap = cgd.normal_capacity(T, K, R) + extra
+    say(f"[writes, rank-granular] T={T} K={K} E={E} R={R} cap={cap}")
+    recv, big = _guarded(cap, H)
+    _, _, _, _, h = cgd.normal_dispatch(dev_bf16(x), itr, num_tokens_per_expert=ntpe, topk_idx=idx_d,
+                                        topk_weights=dev_f32(w), num_experts=E, expert_alignment=align,
+                                        recv_capacity=cap, recv_x=recv)
+    torch.cuda.synchronize()
+    _check_writes(big, cap, h.recv_src_idx.cpu().numpy(), x)
