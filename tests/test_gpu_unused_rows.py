@@ -159,3 +159,26 @@ def test_normal_dispatch_writes_only_rows_with_data(T, K, E, R, H, align, extra)
                                         recv_capacity=cap, recv_x=recv)
     torch.cuda.synchronize()
     _check_writes(big, cap, h.recv_src_idx.cpu().numpy(), x)
+
+
+@pytest.mark.parametrize("T,K,E,R,H", [(300, 4, 64, 8, 64), (2100, 8, 32, 4, 136), (100, 16, 64, 8, 256)])
+def test_combines_write_only_their_output(T, K, E, R, H):
+    """Each combine writes its [T, H] output and nothing past it."""
+    idx, x, w = _inputs(T, K, E, H, seed=T + 6)
+    x_d, idx_d, w_d = dev_bf16(x), dev_i64(idx), dev_f32(w)
+    say(f"[writes, combine outputs] T={T} K={K} E={E} R={R} H={H}")
+    recv, h = cgd.dispatch(x_d, idx_d, E, R)
+    out, big = _guarded(T, H)
+    cgd.combine(recv, h, w_d, out=out)
+    precv, _, ph = cgd.low_latency_dispatch(x_d, idx_d, E, R, expert_capacity=T)
+    pout, pbig = _guarded(T, H)
+    cgd.low_latency_combine(precv, w_d, ph, out=pout)
+    _, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx_d, E, R)
+    nrecv, _, rw, _, nh = cgd.normal_dispatch(x_d, itr, num_tokens_per_expert=ntpe, topk_idx=idx_d, topk_weights=w_d,
+                                              num_experts=E)
+    nout, nbig = _guarded(T, H)
+    cgd.normal_combine(nrecv, nh, rw, out=nout)
+    torch.cuda.synchronize()
+    for b in (big, pbig, nbig):
+        assert (b[T:].cpu().numpy() == SENTINEL).all(), "write past the combine output"
+        assert not (b[:T].cpu().numpy() == SENTINEL).all(axis=1).any(), "an output row was not written"
