@@ -182,3 +182,38 @@ def test_combines_write_only_their_output(T, K, E, R, H):
     for b in (big, pbig, nbig):
         assert (b[T:].cpu().numpy() == SENTINEL).all(), "write past the combine output"
         assert not (b[:T].cpu().numpy() == SENTINEL).all(axis=1).any(), "an output row was not written"
+
+
+@pytest.mark.parametrize("T,K,E,R,H,align,extra,cast", [(2100, 8, 32, 4, 256, 8, 3000, True),
+                                                         (300, 4, 64, 8, 384, 16, 500, False),
+                                                         (128, 8, 256, 16, 256, 1, 40, True)])
+def test_fp8_dispatch_writes_only_rows_with_data(T, K, E, R, H, align, extra, cast):
+    """FP8 rows (codes and fp32 block scales), cast on dispatch or dispatched
+    as an FP8 tuple: only the rows with data change, each to its source
+    token's codes and scales from the standalone cast."""
+    idx, x, _ = _inputs(T, K, E, H, seed=T + 7)
+    fmt = cgd.SCALE_F32
+    cap = cgd.dispatch_capacity(T, K, E, align) + extra
+    nb = H // 128
+    say(f"[writes, fp8] T={T} K={K} E={E} H={H} cap={cap} cast_on_dispatch={cast}")
+    qbig = torch.full((cap + GUARD, H), 0x5A, dtype=torch.uint8, device=DEV)
+    sbig = torch.full((cap + GUARD, nb), 12345.0, dtype=torch.float32, device=DEV)
+    recv = (qbig[:cap].view(torch.float8_e4m3fn), sbig[:cap])
+    x_d = dev_bf16(x)
+    q_ref, s_ref = cgd.per_token_cast_to_fp8(x_d, fmt)
+    if cast:
+        _, h = cgd.dispatch(x_d, dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap, recv_x=recv,
+                            cast_fp8=fmt)
+    else:
+        _, h = cgd.dispatch((q_ref, s_ref), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap,
+                            recv_x=recv)
+    torch.cuda.synchronize()
+    src = h.recv_src_idx.cpu().numpy()
+    data = src >= 0
+    q, s = qbig.cpu().numpy(), sbig.cpu().numpy()
+    assert (q[cap:] == 0x5A).all() and (s[cap:] == 12345.0).all(), "write past the receive buffer"
+    assert (q[:cap][~data] == 0x5A).all() and (s[:cap][~data] == 12345.0).all(), "write to a row without data"
+    qr = q_ref.view(torch.uint8).cpu().numpy()
+    sr = s_ref.contiguous().cpu().numpy()
+    np.testing.assert_array_equal(q[:cap][data], qr[src[data]])
+    np.testing.assert_array_equal(s[:cap][data].view(np.int32), sr[src[data]].view(np.int32))
