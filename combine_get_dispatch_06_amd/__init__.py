@@ -8,12 +8,12 @@ and streams.
 Expert-granular path (one received row per selected expert):
 
     ntpr, _, ntpe, is_token_in_rank, _ = get_dispatch_layout(topk_idx, num_experts, num_ranks)
-    recv_x, handle = dispatch(x, topk_idx, num_experts, num_ranks)
-    recv_x2, _ = dispatch(x2, handle=handle)            # cached: reuses the layout
+    recv_x, num_recv_tokens_per_expert, handle = dispatch(x, topk_idx, num_experts, num_ranks)
+    recv_x2, _, _ = dispatch(x2, handle=handle)         # cached: reuses the layout
     combined = combine(expert_out, handle, topk_weights)
     layout, plan = layout_and_dispatch_plan(topk_idx, num_experts, num_ranks)   # one routing pass
-    recv_x, handle = dispatch_apply(x, plan)
-    layout, recv_x, handle = layout_and_dispatch(x, topk_idx, num_experts, num_ranks)  # one launch at decode
+    recv_x, num_recv_tokens_per_expert, handle = dispatch_apply(x, plan)
+    layout, recv_x, num_recv_tokens_per_expert, handle = layout_and_dispatch(x, topk_idx, num_experts, num_ranks)
 
 Rank-granular path (normal mode, one row per (token, flagged rank)):
 
@@ -48,10 +48,14 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
            "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_",
-           "layout_and_normal_dispatch_plan"]
+           "layout_and_normal_dispatch_plan", "layout_and_dispatch", "normal_workspace_bytes",
+           "layout_and_normal_workspace_bytes", "empty_"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libcgd.so")
+_BUILT_LIB = os.path.join(_PKG, "libcgd.so")
+# CGD_LIBRARY names another build of libcgd to load instead (e.g. one with
+# host-side sanitizers); it must exist, nothing is built for it
+_LIB_PATH = os.environ.get("CGD_LIBRARY") or _BUILT_LIB
 
 CGD_OK = 0
 _STATUS = {-1: "invalid argument", -2: "capacity", -3: "workspace", -4: "HIP error"}
@@ -78,9 +82,16 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
+        if _LIB_PATH != _BUILT_LIB:
+            raise FileNotFoundError(f"CGD_LIBRARY names {_LIB_PATH}, which does not exist")
         from . import build as _build
         _build.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def configure(lib):
+    """Declare the C signatures of libcgd's entry points on a loaded library."""
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.cgd_version.restype = ctypes.c_char_p
     lib.cgd_version.argtypes = []
@@ -89,21 +100,21 @@ def load():
     lib.cgd_layout_workspace_bytes.restype = sz
     lib.cgd_layout_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.cgd_dispatch_workspace_bytes.restype = sz
-    lib.cgd_dispatch_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.cgd_dispatch_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.cgd_dispatch_capacity.restype = i64
     lib.cgd_dispatch_capacity.argtypes = [i64, i32, i32, i32]
     lib.cgd_get_dispatch_layout.restype = i32
     lib.cgd_get_dispatch_layout.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch.restype = i32
-    lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_plan.restype = i32
-    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, sz, vp]
+    lib.cgd_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_layout_and_dispatch.restype = i32
     lib.cgd_layout_and_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp,
-                                            sz, vp]
+                                            vp, sz, vp]
     lib.cgd_layout_and_dispatch_plan.restype = i32
-    lib.cgd_layout_and_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, sz,
-                                                 vp]
+    lib.cgd_layout_and_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                 sz, vp]
     lib.cgd_packed_workspace_bytes.restype = sz
     lib.cgd_packed_workspace_bytes.argtypes = [i64, i32, i32]
     lib.cgd_dispatch_packed.restype = i32
@@ -146,11 +157,12 @@ def load():
     lib.cgd_normal_combine.argtypes = [vp, i64, i32, vp, i64, i32, vp, i32, vp, vp, vp, vp, vp]
     lib.cgd_copy.restype = i32
     lib.cgd_copy.argtypes = [vp, vp, i64, vp]
+    lib.cgd_empty.restype = i32
+    lib.cgd_empty.argtypes = [vp]
     lib.cgd_layout_and_normal_workspace_bytes.restype = sz
     lib.cgd_layout_and_normal_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.cgd_layout_and_normal_dispatch_plan.restype = i32
     lib.cgd_layout_and_normal_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
-    _lib = lib
     return lib
 
 
@@ -183,17 +195,48 @@ def _stream(device: torch.device):
 
 # One zero-initialised workspace per (device, stream, kind). libcgd leaves a
 # workspace zeroed after every call, and calls on one stream are ordered, so a
-# workspace is reused for every later call on that stream.
+# workspace is reused for every later call on that stream. A workspace that a
+# larger call outgrows is replaced but kept alive until the process ends: a
+# HIP graph captured earlier still launches kernels on its address. Sizes at
+# least double on each replacement, so few are ever kept.
 _workspaces: dict = {}
+_outgrown: list = []
+
+# Writes of plans into each workspace (by address): a rank-granular plan
+# leaves its group words and tile bases there for the apply, so an apply
+# checks that no later plan has overwritten them.
+_plan_writes: dict = {}
 
 
 def _workspace(device: torch.device, kind: str, nbytes: int) -> torch.Tensor:
     key = (device.index, torch.cuda.current_stream(device).cuda_stream, kind)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        size = max(nbytes, 256) if ws is None else max(nbytes, 2 * ws.numel())
+        if ws is not None:
+            _outgrown.append(ws)
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def _caller_workspace(ws: torch.Tensor, nbytes: int, device: torch.device) -> torch.Tensor:
+    """A workspace the caller owns: uint8, contiguous, on the device, >= nbytes,
+    256-byte aligned; it must be zero-filled before its first use."""
+    _dev_tensor(ws, "workspace", torch.uint8, 1)
+    if ws.device != device:
+        raise ValueError("workspace must be on the inputs' device")
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes (got {ws.numel()})")
+    if ws.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+    return ws
+
+
+def _note_plan_write(ws: torch.Tensor) -> int:
+    n = _plan_writes.get(ws.data_ptr(), 0) + 1
+    _plan_writes[ws.data_ptr()] = n
+    return n
 
 
 # ---------------------------------------------------------------------------
@@ -254,6 +297,8 @@ def per_token_cast_back(x, scale_format: int | None = None, out: torch.Tensor | 
     lib = load()
     q, sc, fmt, st, sb = _fp8_parts(x)
     if scale_format is not None:
+        if sc.dtype != _scale_dtype(scale_format):
+            raise TypeError(f"scales must be {_scale_dtype(scale_format)} for scale format {scale_format}")
         fmt = scale_format
     T, H = q.shape
     dev = q.device
@@ -277,6 +322,17 @@ def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
     with torch.cuda.device(src.device):
         _check("cgd_copy", lib.cgd_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
     return dst
+
+
+def empty_(device: torch.device | str | int | None = None) -> None:
+    """Enqueue libcgd's empty kernel on the current stream of `device` (the
+    launch floor that bench.py times beside the latency-bound calls)."""
+    lib = load()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    if dev.type != "cuda":
+        raise ValueError("empty_ needs a GPU device")
+    with torch.cuda.device(dev):
+        _check("cgd_empty", lib.cgd_empty(_stream(dev)))
 
 
 def dispatch_capacity(num_tokens: int, num_topk: int, num_experts: int, expert_alignment: int = 1) -> int:
@@ -312,10 +368,12 @@ class DispatchHandle:
     expert_offset int32 [E+1]: segment of expert e is rows [off[e], off[e+1]).
     recv_src_idx  int32 [recv_capacity]: source token of each row, -1 if none.
     dst_row       int32 [T, K]: receive row of each slot, -1 if not selected.
+    num_recv_tokens_per_expert int32 [E]: aligned segment sizes (device).
     """
     expert_offset: torch.Tensor
     recv_src_idx: torch.Tensor
     dst_row: torch.Tensor
+    num_recv_tokens_per_expert: torch.Tensor
     num_experts: int
     num_ranks: int
     expert_alignment: int
@@ -331,16 +389,25 @@ class DispatchHandle:
 
     def num_recv_tokens_per_expert_list(self) -> list:
         """Aligned rows per expert as a host list (copies to the host and waits)."""
-        off = self.expert_offset.cpu().tolist()
-        return [b - a for a, b in zip(off[:-1], off[1:])]
+        return self.num_recv_tokens_per_expert.tolist()
+
+
+def _scale_dtype(fmt: int) -> torch.dtype:
+    """Storage of one scale: a UE8M0 byte (format 2), else fp32."""
+    return torch.uint8 if fmt == SCALE_UE8M0 else torch.float32
 
 
 def _recv_fp8(recv_x, cap: int, H: int, fmt: int, dev):
+    """A caller's FP8 receive tuple, checked against the rows and the scale
+    format the kernel will write (1-byte UE8M0 or 4-byte fp32 scales)."""
     if recv_x is None:
         return _fp8_empty(cap, H, fmt, dev)
     q, sc, _, st, sb = _fp8_parts(recv_x, "recv_x")
-    if q.shape != (cap, H) or not sc.is_contiguous():
-        raise ValueError("recv_x must be ([recv_capacity, hidden] codes, row-major [recv_capacity, hidden/128] scales)")
+    if q.shape != (cap, H) or not sc.is_contiguous() or q.device != dev:
+        raise ValueError("recv_x must be ([recv_capacity, hidden] codes, row-major [recv_capacity, hidden/128] scales) "
+                         "on the inputs' device")
+    if sc.dtype != _scale_dtype(fmt):
+        raise TypeError(f"recv_x scales must be {_scale_dtype(fmt)} for scale format {fmt} (got {sc.dtype})")
     return recv_x
 
 
@@ -352,10 +419,14 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
     x is bf16 [T, H], or the FP8 tuple (codes [T, H], scales [T, H/128]);
     with cast_fp8 = a scale format, a bf16 x is cast to FP8 on the way.
     Non-cached (handle=None): needs topk_idx, num_experts, num_ranks; returns
-    (recv_x, DispatchHandle). Cached (handle given, topk_idx None): reuses the
-    handle's layout; returns (recv_x, handle). recv_x is [recv_capacity, H]
-    bf16, or an FP8 tuple for FP8 payloads. recv_capacity defaults to the
-    worst case for the sizes, so no device-to-host copy is needed; rows past
+    (recv_x, num_recv_tokens_per_expert, DispatchHandle), the order of the
+    outputs in the "Dispatch API" section of the DeepEP Python interface notes
+    (num_recv_tokens_per_expert: int32 [E] on the device, each expert's row
+    count rounded up to expert_alignment). Cached (handle given, topk_idx
+    None): reuses the handle's layout; returns (recv_x, the handle's
+    num_recv_tokens_per_expert, handle). recv_x is [recv_capacity, H] bf16, or
+    an FP8 tuple for FP8 payloads. recv_capacity defaults to the worst case for
+    the sizes, so no device-to-host copy is needed; rows past
     handle.expert_offset[-1] are unused.
     """
     lib = load()
@@ -373,6 +444,12 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
     if handle is None and (fp8 or cast_fp8 is not None):
         if topk_idx is None or num_experts is None or num_ranks is None:
             raise ValueError("non-cached dispatch needs topk_idx, num_experts and num_ranks")
+        if recv_x is not None:  # checked before the plan is enqueued
+            _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+            cap = recv_capacity
+            if cap is None:
+                cap = int(lib.cgd_dispatch_capacity(T, topk_idx.shape[1], num_experts, expert_alignment))
+            _recv_fp8(recv_x, cap, H, fmt if fp8 else cast_fp8, dev)
         plan = dispatch_plan(topk_idx, num_experts, num_ranks, expert_alignment, recv_capacity)
         return dispatch_apply(x, plan, recv_x=recv_x, cast_fp8=cast_fp8)
     with torch.cuda.device(dev):
@@ -388,14 +465,14 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
                        lib.cgd_dispatch_cached_cast_fp8(_ptr(x), T, H, handle.num_topk, cast_fp8,
                                                         _ptr(handle.dst_row), _ptr(recv_x[0]), _ptr(recv_x[1]), cap,
                                                         _stream(dev)))
-                return recv_x, handle
+                return recv_x, handle.num_recv_tokens_per_expert, handle
             if fp8:
                 recv_x = _recv_fp8(recv_x, cap, H, fmt, dev)
                 _check("cgd_dispatch_cached_fp8",
                        lib.cgd_dispatch_cached_fp8(_ptr(q), _ptr(sc), st, sb, fmt, T, H, handle.num_topk,
                                                    _ptr(handle.dst_row), _ptr(recv_x[0]), _ptr(recv_x[1]), cap,
                                                    _stream(dev)))
-                return recv_x, handle
+                return recv_x, handle.num_recv_tokens_per_expert, handle
             if recv_x is None:
                 recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
             _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
@@ -404,7 +481,7 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
             _check("cgd_dispatch_cached",
                    lib.cgd_dispatch_cached(_ptr(x), T, H, handle.num_topk, _ptr(handle.dst_row), _ptr(recv_x), cap,
                                            _stream(dev)))
-            return recv_x, handle
+            return recv_x, handle.num_recv_tokens_per_expert, handle
 
         if topk_idx is None or num_experts is None or num_ranks is None:
             raise ValueError("non-cached dispatch needs topk_idx, num_experts and num_ranks")
@@ -420,15 +497,16 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
         if recv_x.shape[1] != H or recv_x.shape[0] != cap:
             raise ValueError("recv_x must be [recv_capacity, hidden]")
         off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
         src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
         dst = torch.empty((T, K), dtype=torch.int32, device=dev)
-        nbytes = lib.cgd_dispatch_workspace_bytes(T, K, num_experts)
+        nbytes = lib.cgd_dispatch_workspace_bytes(T, K, num_experts, num_ranks)
         ws = _workspace(dev, "dispatch", nbytes)
         _check("cgd_dispatch",
                lib.cgd_dispatch(_ptr(x), T, H, _ptr(topk_idx), K, num_experts, num_ranks, expert_alignment,
-                                _ptr(recv_x), cap, _ptr(off), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(),
+                                _ptr(recv_x), cap, _ptr(off), _ptr(nre), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(),
                                 _stream(dev)))
-    return recv_x, DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+    return recv_x, nre, DispatchHandle(off, src, dst, nre, num_experts, num_ranks, expert_alignment, cap)
 
 
 @dataclass
@@ -452,14 +530,15 @@ def dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expe
         need = int(lib.cgd_dispatch_capacity(T, K, num_experts, expert_alignment))
         cap = need if recv_capacity is None else int(recv_capacity)
         off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
         src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
         dst = torch.empty((T, K), dtype=torch.int32, device=dev)
-        nbytes = lib.cgd_dispatch_workspace_bytes(T, K, num_experts)
+        nbytes = lib.cgd_dispatch_workspace_bytes(T, K, num_experts, num_ranks)
         ws = _workspace(dev, "dispatch", nbytes)
         _check("cgd_dispatch_plan",
                lib.cgd_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap, _ptr(off),
-                                     _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
-    h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+                                     _ptr(nre), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+    h = DispatchHandle(off, src, dst, nre, num_experts, num_ranks, expert_alignment, cap)
     return DispatchPlan(h, ws, T)
 
 
@@ -478,14 +557,15 @@ def layout_and_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks
         ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
         itr = torch.empty((T, num_ranks), dtype=torch.bool, device=dev)
         off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
         src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
         dst = torch.empty((T, K), dtype=torch.int32, device=dev)
-        ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts))
+        ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts, num_ranks))
         _check("cgd_layout_and_dispatch_plan",
                lib.cgd_layout_and_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks, expert_alignment, cap,
-                                                _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(src), _ptr(dst),
-                                                _ptr(ws), ws.numel(), _stream(dev)))
-    h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
+                                                _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(nre), _ptr(src),
+                                                _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+    h = DispatchHandle(off, src, dst, nre, num_experts, num_ranks, expert_alignment, cap)
     return (ntpr, None, ntpe, itr, None), DispatchPlan(h, ws, T)
 
 
@@ -493,7 +573,8 @@ def layout_and_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: in
                         expert_alignment: int = 1, recv_capacity: int | None = None, recv_x: torch.Tensor | None = None):
     """get_dispatch_layout and dispatch (bf16 x) in one call; a batch of at most
     256 tokens takes one launch.
-    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), recv_x, DispatchHandle)."""
+    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), recv_x,
+        num_recv_tokens_per_expert, DispatchHandle)."""
     lib = load()
     _dev_tensor(x, "x", torch.bfloat16, 2)
     _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
@@ -514,22 +595,23 @@ def layout_and_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: in
         ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
         itr = torch.empty((T, num_ranks), dtype=torch.bool, device=dev)
         off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
         src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
         dst = torch.empty((T, K), dtype=torch.int32, device=dev)
-        ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts))
+        ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts, num_ranks))
         _check("cgd_layout_and_dispatch",
                lib.cgd_layout_and_dispatch(_ptr(x), T, H, _ptr(topk_idx), K, num_experts, num_ranks, expert_alignment,
                                            _ptr(recv_x), cap, _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off),
-                                           _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
-    h = DispatchHandle(off, src, dst, num_experts, num_ranks, expert_alignment, cap)
-    return (ntpr, None, ntpe, itr, None), recv_x, h
+                                           _ptr(nre), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+    h = DispatchHandle(off, src, dst, nre, num_experts, num_ranks, expert_alignment, cap)
+    return (ntpr, None, ntpe, itr, None), recv_x, nre, h
 
 
 def dispatch_apply(x, plan: DispatchPlan, recv_x=None, cast_fp8: int | None = None):
     """Second step of dispatch: copy rows to the plan's handle (the cached
     dispatch with plan.handle). x: bf16 [T, H] or an FP8 tuple; cast_fp8 (a
-    scale format) casts a bf16 x on the way. Returns (recv_x, handle), recv_x
-    an FP8 tuple for FP8 payloads."""
+    scale format) casts a bf16 x on the way. Returns (recv_x,
+    num_recv_tokens_per_expert, handle), recv_x an FP8 tuple for FP8 payloads."""
     T = (x[0] if isinstance(x, tuple) else x).shape[0]
     if T != plan.num_tokens:
         raise ValueError("x has a different number of tokens than the plan")
@@ -563,6 +645,22 @@ def combine(expert_out: torch.Tensor, handle: DispatchHandle, topk_weights: torc
 # Rank-granular ("normal mode") dispatch and combine: one received row per
 # (token, flagged rank), the DeepEP normal-mode receive layout.
 # ---------------------------------------------------------------------------
+
+def normal_workspace_bytes(num_tokens: int, num_ranks: int) -> int:
+    """Bytes of a workspace of its own for normal_dispatch_plan."""
+    n = int(load().cgd_normal_workspace_bytes(num_tokens, num_ranks))
+    if n == 0:
+        raise ValueError("invalid sizes for a workspace")
+    return n
+
+
+def layout_and_normal_workspace_bytes(num_tokens: int, num_topk: int, num_experts: int, num_ranks: int) -> int:
+    """Bytes of a workspace of its own for layout_and_normal_dispatch_plan."""
+    n = int(load().cgd_layout_and_normal_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks))
+    if n == 0:
+        raise ValueError("invalid sizes for a workspace")
+    return n
+
 
 def normal_capacity(num_tokens: int, num_topk: int, num_ranks: int) -> int:
     cap = int(load().cgd_normal_capacity(num_tokens, num_topk, num_ranks))
@@ -688,6 +786,7 @@ def normal_dispatch(x: torch.Tensor, is_token_in_rank: torch.Tensor | None = Non
             nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
         nbytes = lib.cgd_normal_workspace_bytes(T, R)
         ws = _workspace(dev, "normal", nbytes)
+        _note_plan_write(ws)  # its plan step replaces any plan left there
         _check("cgd_normal_dispatch",
                lib.cgd_normal_dispatch(_ptr(x), T, H, _ptr(is_token_in_rank), _ptr(num_tokens_per_expert),
                                        _ptr(topk_idx), _ptr(topk_weights), K, num_experts, R, expert_alignment,
@@ -699,17 +798,31 @@ def normal_dispatch(x: torch.Tensor, is_token_in_rank: torch.Tensor | None = Non
 @dataclass
 class NormalPlan:
     """Result of normal_dispatch_plan: rank offsets, aligned per-expert counts
-    and the workspace that normal_dispatch_apply must receive."""
+    and the workspace holding the plan's per-token places, which
+    normal_dispatch_apply reads. By default that workspace is the one shared by
+    the plans on the current stream: apply the plan before making the next one
+    there (normal_dispatch_apply raises otherwise), or pass a workspace of the
+    plan's own to keep several plans alive."""
     rank_offset: torch.Tensor
     num_recv_tokens_per_expert: torch.Tensor | None
     workspace: torch.Tensor
     num_tokens: int
     num_experts: int
+    write: int = 0  # the workspace's plan-write count when this plan wrote it
+
+
+def _normal_plan_workspace(workspace, nbytes: int, dev, kind: str) -> torch.Tensor:
+    if workspace is None:
+        return _workspace(dev, kind, nbytes)
+    return _caller_workspace(workspace, nbytes, dev)
 
 
 def normal_dispatch_plan(is_token_in_rank: torch.Tensor, num_tokens_per_expert: torch.Tensor | None = None,
-                         num_experts: int | None = None, expert_alignment: int = 1) -> NormalPlan:
-    """First step of normal dispatch: rank offsets from is_token_in_rank alone."""
+                         num_experts: int | None = None, expert_alignment: int = 1,
+                         workspace: torch.Tensor | None = None) -> NormalPlan:
+    """First step of normal dispatch: rank offsets from is_token_in_rank alone.
+    workspace: None (the stream's shared one), or a zero-filled uint8 device
+    tensor of at least normal_workspace_bytes(T, R) bytes that the plan keeps."""
     lib = load()
     _dev_tensor(is_token_in_rank, "is_token_in_rank", torch.bool, 2)
     T, R = is_token_in_rank.shape
@@ -724,18 +837,21 @@ def normal_dispatch_plan(is_token_in_rank: torch.Tensor, num_tokens_per_expert: 
                 raise ValueError("num_tokens_per_expert must be [num_experts]")
             nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
         off = torch.empty(R + 1, dtype=torch.int32, device=dev)
-        ws = _workspace(dev, "normal", lib.cgd_normal_workspace_bytes(T, R))
+        ws = _normal_plan_workspace(workspace, lib.cgd_normal_workspace_bytes(T, R), dev, "normal")
         _check("cgd_normal_dispatch_plan",
                lib.cgd_normal_dispatch_plan(_ptr(is_token_in_rank), T, R, _ptr(num_tokens_per_expert), num_experts,
                                             expert_alignment, _ptr(off), _ptr(nre), _ptr(ws), ws.numel(),
                                             _stream(dev)))
-    return NormalPlan(off, nre, ws, T, num_experts)
+    return NormalPlan(off, nre, ws, T, num_experts, _note_plan_write(ws))
 
 
 def layout_and_normal_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
-                                    expert_alignment: int = 1, num_recv_tokens_per_expert: bool = True):
+                                    expert_alignment: int = 1, num_recv_tokens_per_expert: bool = True,
+                                    workspace: torch.Tensor | None = None):
     """get_dispatch_layout and normal_dispatch_plan in one launch.
-    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), NormalPlan)."""
+    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), NormalPlan).
+    workspace: as normal_dispatch_plan, at least
+    layout_and_normal_workspace_bytes(T, K, E, R) bytes."""
     lib = load()
     _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
     T, K = topk_idx.shape
@@ -747,12 +863,12 @@ def layout_and_normal_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, nu
         off = torch.empty(num_ranks + 1, dtype=torch.int32, device=dev)
         nre = torch.empty(num_experts, dtype=torch.int32, device=dev) if num_recv_tokens_per_expert else None
         need = int(lib.cgd_layout_and_normal_workspace_bytes(T, K, num_experts, num_ranks))
-        ws = _workspace(dev, "layout_normal", max(need, 1))
+        ws = _normal_plan_workspace(workspace, max(need, 1), dev, "layout_normal")
         _check("cgd_layout_and_normal_dispatch_plan",
                lib.cgd_layout_and_normal_dispatch_plan(_ptr(topk_idx), T, K, num_experts, num_ranks,
                                                        expert_alignment, _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off),
                                                        _ptr(nre), _ptr(ws), ws.numel(), _stream(dev)))
-    return (ntpr, None, ntpe, itr, None), NormalPlan(off, nre, ws, T, num_experts)
+    return (ntpr, None, ntpe, itr, None), NormalPlan(off, nre, ws, T, num_experts, _note_plan_write(ws))
 
 
 def normal_dispatch_apply(x: torch.Tensor, plan: NormalPlan, topk_idx: torch.Tensor | None = None,
@@ -772,6 +888,9 @@ def normal_dispatch_apply(x: torch.Tensor, plan: NormalPlan, topk_idx: torch.Ten
         dev = x.device
     if T != plan.num_tokens:
         raise ValueError("x has a different number of tokens than the plan")
+    if _plan_writes.get(plan.workspace.data_ptr()) != plan.write:
+        raise ValueError("a later plan has overwritten this plan's workspace: apply each plan before the next "
+                         "one is made on the stream, or give the plans workspaces of their own")
     R = plan.rank_offset.shape[0] - 1
     if (topk_idx is None) != (topk_weights is None):
         raise ValueError("topk_idx and topk_weights go together")
@@ -875,6 +994,26 @@ class PackedHandle:
     expert_capacity: int
 
 
+def _packed_fp8_out(out, E: int, cap: int, H: int, fmt: int, dev):
+    """A caller's FP8 packed receive tuple: codes [E*cap, H] or [E, cap, H]
+    (float8_e4m3fn or uint8), scales [E*cap, H/128] or [E, cap, H/128] of the
+    format's storage type, both contiguous on the device."""
+    if not (isinstance(out, tuple) and len(out) == 2):
+        raise TypeError("out must be a (codes, scales) tuple with use_fp8")
+    q, sc = out
+    for t, name in ((q, "codes"), (sc, "scales")):
+        if not isinstance(t, torch.Tensor) or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"out {name} must be a contiguous tensor on the inputs' device")
+    if q.dtype not in (torch.float8_e4m3fn, torch.uint8) or tuple(q.shape) not in ((E * cap, H), (E, cap, H)):
+        raise ValueError("out codes must be float8_e4m3fn (or uint8) [E * expert_capacity, hidden] "
+                         "or [E, expert_capacity, hidden]")
+    if sc.dtype != _scale_dtype(fmt):
+        raise TypeError(f"out scales must be {_scale_dtype(fmt)} for scale format {fmt} (got {sc.dtype})")
+    if tuple(sc.shape) not in ((E * cap, H // 128), (E, cap, H // 128)):
+        raise ValueError("out scales must be [E * expert_capacity, hidden / 128] or [E, expert_capacity, hidden / 128]")
+    return q, sc
+
+
 def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
                          expert_capacity: int | None = None, use_fp8: bool = False, scale_format: int = SCALE_F32,
                          cumulative_local_expert_recv_stats: torch.Tensor | None = None, out=None):
@@ -908,7 +1047,7 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: i
             if out is None:
                 q, sc = _fp8_empty(E * cap, H, scale_format, dev)
             else:
-                q, sc = out
+                q, sc = _packed_fp8_out(out, E, cap, H, scale_format, dev)
             _check("cgd_dispatch_packed_cast_fp8",
                    lib.cgd_dispatch_packed_cast_fp8(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap, scale_format,
                                                     _ptr(q), _ptr(sc), _ptr(count), _ptr(info), _ptr(dst), _ptr(st),

@@ -29,17 +29,21 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
+    """Compile every source into one shared library: the package's libcgd.so,
+    or `out` (e.g. a build with other tuning macros or host sanitizers,
+    given as `extra` flags)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
+    out = out or LIB
+    tmp = out + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *(extra or []), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -93,9 +93,11 @@ size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_expe
     return cgd::layout_workspace_bytes(num_tokens, num_experts, num_ranks);
 }
 
-size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
-    if (num_tokens < 0 || num_topk < 1 || num_experts < 1 || num_experts > cgd::kMaxExperts) return 0;
-    return cgd::dispatch_workspace_bytes(num_tokens, num_topk, num_experts);
+size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks) {
+    if (num_tokens < 0 || num_topk < 1 || num_experts < 1 || num_experts > cgd::kMaxExperts || num_ranks < 1 ||
+        num_ranks > cgd::kMaxRanks)
+        return 0;
+    return cgd::dispatch_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks);
 }
 
 int64_t cgd_dispatch_capacity(int64_t num_tokens, int num_topk, int num_experts, int expert_alignment) {
@@ -127,8 +129,8 @@ int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num
 
 // Checks shared by the dispatch entry points.
 static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
-                           const int32_t* expert_offset, const int32_t* recv_src_idx, const int32_t* dst_row,
-                           const void* workspace, size_t workspace_bytes) {
+                           const int32_t* expert_offset, const int32_t* nrecv, const int32_t* recv_src_idx,
+                           const int32_t* dst_row, const void* workspace, size_t workspace_bytes) {
     int rc = check_routing_sizes(T, K, E, R);
     if (rc) return rc;
     if (A < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
@@ -140,9 +142,10 @@ static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int
     if (!expert_offset) return fail(CGD_ERR_INVALID_ARG, "null expert_offset");
     if (T > 0 && (!topk_idx || !dst_row)) return fail(CGD_ERR_INVALID_ARG, "null topk_idx or dst_row");
     if (cap > 0 && !recv_src_idx) return fail(CGD_ERR_INVALID_ARG, "null recv_src_idx");
-    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(recv_src_idx, 4) || !aligned(dst_row, 4))
+    if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(nrecv, 4) || !aligned(recv_src_idx, 4) ||
+        !aligned(dst_row, 4))
         return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
-    const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
+    const size_t need = cgd::dispatch_workspace_bytes(T, K, E, R);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
@@ -160,14 +163,16 @@ static int check_rows_args(const void* x, int64_t T, int H, int64_t cap, const v
 }
 
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
-                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
-                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset,
+                      int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+                             expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                             workspace_bytes);
     if (rc) return rc;
     hipError_t err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment,
-                                               recv_capacity, expert_offset, recv_src_idx, dst_row, workspace,
-                                               stream);
+                                               recv_capacity, expert_offset, num_recv_tokens_per_expert, recv_src_idx,
+                                               dst_row, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     return CGD_OK;
 }
@@ -184,39 +189,43 @@ static int check_layout_outputs(int64_t T, const int32_t* ntpr, const int32_t* n
 int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
                                  int num_ranks, int expert_alignment, int64_t recv_capacity,
                                  int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
-                                 uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
-                                 int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                 uint8_t* is_token_in_rank, int32_t* expert_offset,
+                                 int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+                             expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                             workspace_bytes);
     if (rc) return rc;
     if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
         return rc;
     hipError_t err = cgd::launch_layout_and_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
                                                  expert_alignment, recv_capacity, num_tokens_per_rank,
-                                                 num_tokens_per_expert, is_token_in_rank, expert_offset, recv_src_idx,
-                                                 dst_row, workspace, stream);
+                                                 num_tokens_per_expert, is_token_in_rank, expert_offset,
+                                                 num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "layout and dispatch plan launch");
     return CGD_OK;
 }
 
 int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
                  int num_experts, int num_ranks, int expert_alignment, void* recv_x, int64_t recv_capacity,
-                 int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream) {
+                 int32_t* expert_offset, int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+                             expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                             workspace_bytes);
     if (rc) return rc;
     if ((rc = check_rows_args(x, num_tokens, hidden, recv_capacity, recv_x))) return rc;
     hipError_t err;
     if (cgd::dispatch_fuses(num_tokens)) {  // one tile: plan and apply in one launch
         err = cgd::launch_dispatch_fused(x, num_tokens, hidden, topk_idx, num_topk, num_experts, expert_alignment,
-                                         recv_x, recv_capacity, expert_offset, recv_src_idx, dst_row, workspace,
-                                         stream);
+                                         recv_x, recv_capacity, expert_offset, num_recv_tokens_per_expert,
+                                         recv_src_idx, dst_row, workspace, stream);
         if (err != hipSuccess) return hip_fail(err, "fused dispatch launch");
         return CGD_OK;
     }
     err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment, recv_capacity,
-                                    expert_offset, recv_src_idx, dst_row, workspace, stream);
+                                    expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                                    stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
@@ -226,10 +235,12 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
 int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
                             int num_experts, int num_ranks, int expert_alignment, void* recv_x,
                             int64_t recv_capacity, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
-                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
-                            int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* num_recv_tokens_per_expert,
+                            int32_t* recv_src_idx, int32_t* dst_row, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
     int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, recv_src_idx, dst_row, workspace, workspace_bytes);
+                             expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                             workspace_bytes);
     if (rc) return rc;
     if ((rc = check_rows_args(x, num_tokens, hidden, recv_capacity, recv_x))) return rc;
     if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
@@ -239,13 +250,15 @@ int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const
         err = cgd::launch_layout_and_dispatch_fused(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks,
                                                     expert_alignment, recv_x, recv_capacity, num_tokens_per_rank,
                                                     num_tokens_per_expert, is_token_in_rank, expert_offset,
-                                                    recv_src_idx, dst_row, workspace, stream);
+                                                    num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                                                    stream);
         if (err != hipSuccess) return hip_fail(err, "fused layout and dispatch launch");
         return CGD_OK;
     }
     err = cgd::launch_layout_and_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment,
                                       recv_capacity, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
-                                      expert_offset, recv_src_idx, dst_row, workspace, stream);
+                                      expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                                      stream);
     if (err != hipSuccess) return hip_fail(err, "layout and dispatch plan launch");
     err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
@@ -519,6 +532,12 @@ int cgd_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
     return CGD_OK;
 }
 
+int cgd_empty(hipStream_t stream) {
+    hipError_t err = cgd::launch_empty(stream);
+    if (err != hipSuccess) return hip_fail(err, "empty kernel launch");
+    return CGD_OK;
+}
+
 int cgd_cast_back(const void* x_fp8, const void* x_scales, int64_t scale_stride_token, int64_t scale_stride_block,
                   int scale_format, int64_t num_tokens, int hidden, void* out, hipStream_t stream) {
     if (num_tokens < 0) return fail(CGD_ERR_INVALID_ARG, "num_tokens must be >= 0");
@@ -627,7 +646,8 @@ int cgd_normal_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int6
 }
 
 size_t cgd_packed_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts) {
-    return cgd_dispatch_workspace_bytes(num_tokens, num_topk, num_experts);
+    // the packed layout has no layout outputs: the per-rank partials are not used
+    return cgd_dispatch_workspace_bytes(num_tokens, num_topk, num_experts, 1);
 }
 
 static int check_packed_args(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int R,
@@ -645,7 +665,7 @@ static int check_packed_args(const void* x, int64_t T, int H, const int64_t* top
     if (!aligned(x, 16) || !aligned(recv_x, 16)) return fail(CGD_ERR_INVALID_ARG, "x and packed_recv_x must be 16-byte aligned");
     if (!aligned(topk_idx, 8) || !aligned(count, 4) || !aligned(info, 4) || !aligned(dst_row, 4) || !aligned(stats, 4))
         return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
-    const size_t need = cgd::dispatch_workspace_bytes(T, K, E);
+    const size_t need = cgd::dispatch_workspace_bytes(T, K, E, 1);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(CGD_ERR_WORKSPACE, "packed dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);

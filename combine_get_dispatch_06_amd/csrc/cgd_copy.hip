@@ -1,8 +1,11 @@
+// Measurement helpers, not operations of the method.
 // Plain device copy with the data kernels' memory policy, the copy ceiling
 // that the dispatch and combine bandwidths are compared with: one 16-byte
 // non-temporal load and one non-temporal store per lane, every wave storing
 // one 1 KB piece and exiting (the store shape of the row copy), issued over
 // ranges within 32-bit work-item ids.
+// The empty kernel: one wave that does nothing, whose launches measure the
+// floor under the latency-bound kernels (layout, plan).
 #include "cgd_device.h"
 #include "cgd_launch.h"
 
@@ -24,6 +27,13 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st
         hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((m + kCopyThreads - 1) / kCopyThreads)), dim3(kCopyThreads), 0,
                            stream, reinterpret_cast<const uint4*>(src) + i0, reinterpret_cast<uint4*>(dst) + i0, m);
     }
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kWave) void empty_kernel() {}
+
+hipError_t launch_empty(hipStream_t stream) {
+    hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(kWave), 0, stream);
     return hipGetLastError();
 }
 

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
                                                          int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
                                                          int32_t* __restrict__ tile_base,
                                                          int32_t* __restrict__ expert_offset,
+                                                         int32_t* __restrict__ nrecv,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ packed_count,
                                                          int32_t* __restrict__ stats,
@@ -391,7 +392,10 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     }
     __syncthreads();
     if (writer) {
-        for (int x = tid; x < E; x += kRankTile) counts[x] = s_pre[x];
+        for (int x = tid; x < E; x += kRankTile) {
+            counts[x] = s_pre[x];
+            if (nrecv) nrecv[x] = (s_pre[x] + A - 1) / A * A;  // aligned segment size
+        }
         for (int x = tid; x <= E; x += kRankTile) expert_offset[x] = s_off[x];
     }
     if (ntiles > 1) return;  // finalize_kernel completes the handle
@@ -655,7 +659,8 @@ struct DispatchWs {
     int32_t* slot_pack;
     int32_t* counts;
     int32_t* packed_offset;
-    int32_t* rank_part;  // per-tile distinct tokens per rank (fused layout), [tiles, kMaxRanks]
+    int32_t* rank_part;  // per-tile distinct tokens per rank (fused layout), [tiles, R]; last, so the
+                         // offsets of the other arrays do not depend on R
 };
 
 static size_t rnd256(size_t b) { return (b + 255) / 256 * 256; }
@@ -667,9 +672,9 @@ static size_t tile_bytes(int64_t T, int E) {
 
 static size_t slot_bytes(int64_t T, int K) { return rnd256((size_t)(T > 0 ? T : 0) * (size_t)K * sizeof(int32_t)); }
 
-size_t dispatch_workspace_bytes(int64_t T, int K, int E) {
+size_t dispatch_workspace_bytes(int64_t T, int K, int E, int R) {
     return kTicketBytes + tile_bytes(T, E) + slot_bytes(T, K) + rnd256((size_t)E * 4) + rnd256((size_t)(E + 1) * 4) +
-           tile_bytes(T, kMaxRanks);
+           tile_bytes(T, R);
 }
 
 static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
@@ -777,7 +782,7 @@ static int device_cus() {
 // every block plans the tile in LDS and fills a share of the spare rows.
 constexpr int64_t kSpareRowsPerBlock = 2048;
 static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, int64_t cap,
-                              int32_t* expert_offset, int32_t* dst_row, int32_t* recv_src_idx,
+                              int32_t* expert_offset, int32_t* nrecv, int32_t* dst_row, int32_t* recv_src_idx,
                               int32_t* packed_count, int32_t* stats, const DispatchWs& w, hipStream_t stream,
                               const LayoutOut* layout = nullptr) {
     int ebits = 0;
@@ -793,29 +798,29 @@ static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, 
         const dim3 fgrid((unsigned)fill_blocks);
         if (!layout)
             hipLaunchKernelGGL((rank_kernel<1, false, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
-                               seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                               seg_cap, w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats,
                                w.ticket, none, to);
         else if (layout->R <= 64)
             hipLaunchKernelGGL((rank_kernel<1, true, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
-                               seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                               seg_cap, w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats,
                                w.ticket, *layout, to);
         else
             hipLaunchKernelGGL((rank_kernel<6, true, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
-                               seg_cap, w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats,
+                               seg_cap, w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats,
                                w.ticket, *layout, to);
         return hipGetLastError();
     }
     if (!layout) {
         const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
         hipLaunchKernelGGL((rank_kernel<1, false>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, none, to);
+                           w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, none, to);
     } else if (layout->R <= 64) {
         hipLaunchKernelGGL((rank_kernel<1, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout,
+                           w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, *layout,
                            to);
     } else {
         hipLaunchKernelGGL((rank_kernel<6, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, *layout,
+                           w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, *layout,
                            to);
     }
     if (ntiles > 1) {
@@ -831,18 +836,18 @@ static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, 
 }
 
 hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
-                                  int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset,
+                                  int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, int32_t* nrecv,
                                   int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream) {
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
     const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
-    return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, dst_row, recv_src_idx, nullptr, nullptr, w,
+    return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, nrecv, dst_row, recv_src_idx, nullptr, nullptr, w,
                        stream, &lo);
 }
 
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int64_t cap,
-                                int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
-                                hipStream_t stream) {
-    return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, dst_row, recv_src_idx, nullptr, nullptr,
+                                int32_t* expert_offset, int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row,
+                                void* workspace, hipStream_t stream) {
+    return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, nrecv, dst_row, recv_src_idx, nullptr, nullptr,
                        dispatch_ws(workspace, T, K, E), stream);
 }
 
@@ -912,7 +917,8 @@ hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int 
 // rank kernel); seg_cap >= 0 for the fixed-capacity packed layout; with
 // layout, get_dispatch_layout's outputs from the same launch.
 static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, const void* x,
-                               int H, void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
+                               int H, void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* nrecv,
+                               int32_t* recv_src_idx,
                                int32_t* dst_row, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
                                hipStream_t stream, const LayoutOut* layout = nullptr) {
     int ebits = 0;
@@ -933,7 +939,7 @@ static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E,
     const size_t lds = rank_lds_bytes(E, K);
 #define CGD_FUSED(RW, LAYOUT, LO)                                                                                   \
     hipLaunchKernelGGL((rank_kernel<RW, LAYOUT, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap, \
-                       w.slot_pack, w.tile_base, expert_offset, w.counts, packed_count, stats, w.ticket, LO, fc)
+                       w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, LO, fc)
     if (!layout)
         CGD_FUSED(1, false, none);
     else if (layout->R <= 64)
@@ -947,20 +953,21 @@ static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E,
 bool dispatch_fuses(int64_t T) { return T <= kRankTile; }
 
 hipError_t launch_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
-                                 void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
-                                 int32_t* dst_row, void* workspace, hipStream_t stream) {
-    return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_x, cap, expert_offset, recv_src_idx, dst_row, nullptr,
-                        nullptr, dispatch_ws(workspace, T, K, E), stream);
+                                 void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* nrecv,
+                                 int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream) {
+    return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_x, cap, expert_offset, nrecv, recv_src_idx, dst_row,
+                        nullptr, nullptr, dispatch_ws(workspace, T, K, E), stream);
 }
 
 hipError_t launch_layout_and_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
                                             int R, int A, void* recv_x, int64_t cap, int32_t* ntpr, int32_t* ntpe,
-                                            uint8_t* itr, int32_t* expert_offset, int32_t* recv_src_idx,
-                                            int32_t* dst_row, void* workspace, hipStream_t stream) {
+                                            uint8_t* itr, int32_t* expert_offset, int32_t* nrecv,
+                                            int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                                            hipStream_t stream) {
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
     const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
-    return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_x, cap, expert_offset, recv_src_idx, dst_row, nullptr,
-                        nullptr, w, stream, &lo);
+    return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_x, cap, expert_offset, nrecv, recv_src_idx, dst_row,
+                        nullptr, nullptr, w, stream, &lo);
 }
 
 hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
@@ -970,10 +977,10 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
     const int64_t cap = (int64_t)E * expert_capacity;
     if (fmt < 0 && dispatch_fuses(T))
-        return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, cap, w.packed_offset, recv_src_info,
-                            dst_row, packed_count, stats, w, stream);
-    hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, cap, w.packed_offset, dst_row, recv_src_info,
-                                 packed_count, stats, w, stream);
+        return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, cap, w.packed_offset, nullptr,
+                            recv_src_info, dst_row, packed_count, stats, w, stream);
+    hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, cap, w.packed_offset, nullptr, dst_row,
+                                 recv_src_info, packed_count, stats, w, stream);
     if (err != hipSuccess) return err;
     if (fmt < 0)
         launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side());

@@ -28,7 +28,7 @@ inline int64_t tokens_per_launch(int64_t waves_per_token) {
 
 int64_t layout_blocks(int64_t T);
 size_t layout_workspace_bytes(int64_t T, int E, int R);
-size_t dispatch_workspace_bytes(int64_t T, int K, int E);
+size_t dispatch_workspace_bytes(int64_t T, int K, int E, int R);
 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R, int32_t* ntpr, int32_t* ntpe,
                          uint8_t* itr, void* workspace, hipStream_t stream);
@@ -36,13 +36,14 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R
 // Batches of at most one plan tile: plan and apply (bf16) in one launch.
 bool dispatch_fuses(int64_t T);
 hipError_t launch_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
-                                 void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* recv_src_idx,
-                                 int32_t* dst_row, void* workspace, hipStream_t stream);
+                                 void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* nrecv,
+                                 int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream);
 // The same with get_dispatch_layout's outputs from the same launch.
 hipError_t launch_layout_and_dispatch_fused(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
                                             int R, int A, void* recv_x, int64_t cap, int32_t* ntpr, int32_t* ntpe,
-                                            uint8_t* itr, int32_t* expert_offset, int32_t* recv_src_idx,
-                                            int32_t* dst_row, void* workspace, hipStream_t stream);
+                                            uint8_t* itr, int32_t* expert_offset, int32_t* nrecv,
+                                            int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                                            hipStream_t stream);
 
 // The rank-granular plan's workspace arrays (group words, group bases, tile
 // counts / bases), as launch_normal_plan leaves them.
@@ -61,14 +62,14 @@ hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int
                                          int32_t* nrecv, void* workspace, hipStream_t stream);
 
 // The dispatch plan: the handle (expert_offset, recv_src_idx, dst_row) from
-// the routing alone.
+// the routing alone, and (nrecv != nullptr) the aligned segment sizes.
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int64_t cap,
-                                int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
-                                hipStream_t stream);
+                                int32_t* expert_offset, int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row,
+                                void* workspace, hipStream_t stream);
 
 // get_dispatch_layout and the dispatch plan from one pass over the routing.
 hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
-                                  int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset,
+                                  int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, int32_t* nrecv,
                                   int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream);
 
 // Packed fixed-capacity layout: plan + apply; fmt < 0 moves bf16 rows, else
@@ -107,6 +108,9 @@ hipError_t launch_cast_to_fp8(const void* x, int64_t T, int H, void* q, void* sc
 
 // Plain 16-byte copy of `bytes` (a multiple of 16).
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+// One empty kernel (the launch floor).
+hipError_t launch_empty(hipStream_t stream);
 
 hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64_t sb, int fmt, int64_t T, int H,
                             void* out, hipStream_t stream);

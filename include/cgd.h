@@ -78,9 +78,11 @@ const char* cgd_last_error(void);
  * concurrently need separate workspaces. */
 size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
 
-/* Workspace bytes cgd_dispatch and cgd_dispatch_plan need (host only;
- * 0 if invalid). Same zero-fill and reuse rules as the layout workspace. */
-size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts);
+/* Workspace bytes cgd_dispatch, cgd_dispatch_plan and their layout-fused
+ * forms need for these sizes (host only; 0 if invalid). Same zero-fill and
+ * reuse rules as the layout workspace. num_ranks sizes the per-rank partial
+ * counts of the layout-fused forms. */
+size_t cgd_dispatch_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
 
 /* Rows a receive buffer needs for ANY routing of these sizes (host only):
  * num_tokens * num_topk + num_experts * (expert_alignment - 1), or -1 if the
@@ -116,17 +118,23 @@ int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num
  *   expert_offset      int32 [num_experts + 1] out: segment e is rows
  *                      [expert_offset[e], expert_offset[e+1]); segments are in
  *                      ascending expert id, hence grouped by rank
+ *   num_recv_tokens_per_expert
+ *                      int32 [num_experts] out, or NULL (not written): the aligned
+ *                      segment sizes, each expert's row count rounded up to
+ *                      expert_alignment (the dispatch output of that name in the
+ *                      "Dispatch API" section); equal to expert_offset[e+1] - expert_offset[e]
  *   recv_src_idx       int32 [recv_capacity] out: source token of each data row, -1 elsewhere
  *   dst_row            int32 [num_tokens, num_topk] out: receive row of each slot, -1 if
  *                      not selected. Inside a segment rows follow ascending (token, slot)
  *   workspace          >= cgd_dispatch_workspace_bytes(...) bytes
  * (expert_offset, recv_src_idx, dst_row) is the handle for cached dispatch and
- * for combine. Counts are derived from topk_idx itself, so the layout outputs
- * are not inputs here and cannot disagree with the routing. */
+ * for combine. Counts are derived from topk_idx itself, so the layout's
+ * num_tokens_per_expert is not an input here and cannot disagree with the
+ * routing (on one GPU no count exchange precedes the data). */
 int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
                  int num_experts, int num_ranks, int expert_alignment, void* recv_x, int64_t recv_capacity,
-                 int32_t* expert_offset, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream);
+                 int32_t* expert_offset, int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Dispatch in two steps on one stream: cgd_dispatch is exactly
  * cgd_dispatch_plan followed by cgd_dispatch_cached with the plan's dst_row
@@ -135,14 +143,16 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
  * diagnostic-probes PR page, "Implementation": notify kernels before the
  * dispatch data kernels; the first-call latency blog page: tensor sizes are
  * notified in advance), so a caller may enqueue it early; it writes the whole
- * handle (expert_offset, recv_src_idx, dst_row, as cgd_dispatch describes),
- * and the row copy that follows moves data only. Batches of one 256-token
+ * handle (expert_offset, recv_src_idx, dst_row, as cgd_dispatch describes)
+ * and num_recv_tokens_per_expert, and the row copy that follows moves data
+ * only. Batches of one 256-token
  * tile are planned in one launch, larger ones in two (per-tile ranks, then
  * final rows). Arguments and errors as cgd_dispatch; the workspace is not
  * needed once the plan has run. */
 int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts, int num_ranks,
-                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset, int32_t* recv_src_idx,
-                      int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                      int expert_alignment, int64_t recv_capacity, int32_t* expert_offset,
+                      int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /* cgd_get_dispatch_layout and cgd_dispatch_plan in one call: both read the
  * same routing, so one pass over each 256-token tile (one launch, plus the
@@ -152,8 +162,9 @@ int cgd_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
 int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
                                  int num_ranks, int expert_alignment, int64_t recv_capacity,
                                  int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
-                                 uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
-                                 int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                 uint8_t* is_token_in_rank, int32_t* expert_offset,
+                                 int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* cgd_get_dispatch_layout and cgd_dispatch in one call: the layout outputs
  * (as cgd_get_dispatch_layout; no layout workspace is needed) and the
@@ -164,8 +175,9 @@ int cgd_layout_and_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, in
 int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
                             int num_experts, int num_ranks, int expert_alignment, void* recv_x,
                             int64_t recv_capacity, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
-                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* recv_src_idx,
-                            int32_t* dst_row, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* num_recv_tokens_per_expert,
+                            int32_t* recv_src_idx, int32_t* dst_row, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Cached dispatch (Python interface notes, "Dispatch API", handle reuse):
  * copies rows with a dst_row from an earlier cgd_dispatch or
@@ -431,6 +443,15 @@ int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tok
  * null pointer), CGD_ERR_HIP (launch failure). Only enqueues on stream.
  * ------------------------------------------------------------------------- */
 int cgd_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+/* -------------------------------------------------------------------------
+ * cgd_empty: enqueues one kernel of one wave that does nothing.
+ * Not an operation of the method: its launches measure the floor under the
+ * latency-bound calls (get_dispatch_layout, the dispatch plan), timed the same
+ * way as they are. Errors: CGD_ERR_HIP (launch failure). Only enqueues on
+ * stream.
+ * ------------------------------------------------------------------------- */
+int cgd_empty(hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -35,9 +35,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("CGD_ORACLE_LIBRARY")  # another build (e.g. with sanitizers); must exist
+        if not path:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_layout.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
         lib.oracle_layout.restype = i32

@@ -46,9 +46,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("CGD_SYNTH_LIBRARY")  # another build (e.g. with sanitizers); must exist
+        if not path:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        lib = ctypes.CDLL(path)
         u64, i64, i32 = ctypes.c_uint64, ctypes.c_int64, ctypes.c_int
         vp = ctypes.c_void_p
         lib.synth_splitmix64.argtypes = [u64, u64]

@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_cached_cast_fp8", "cgd_dispatch_cached_fp8",
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
-        "cgd_layout_and_dispatch",
+        "cgd_layout_and_dispatch", "cgd_empty",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan",
     ])
 
@@ -66,10 +66,15 @@ def test_capacity_and_workspace_sizes():
         ws = lib.cgd_layout_workspace_bytes(T, 8, 256, 8)
         blocks = max(1, -(-T // 256))
         assert ws >= 256 + blocks * (256 + 8) * 4 and ws % 256 == 0
-        wd = lib.cgd_dispatch_workspace_bytes(T, 8, 256)
-        assert wd >= 256 + blocks * 256 * 4 + T * 8 * 4 and wd % 256 == 0
+        wd = lib.cgd_dispatch_workspace_bytes(T, 8, 256, 8)
+        assert wd >= 256 + blocks * 256 * 4 + T * 8 * 4 + blocks * 8 * 4 and wd % 256 == 0
+        # the layout-fused plans keep one partial count per (tile, rank)
+        wr = lib.cgd_dispatch_workspace_bytes(T, 8, 256, 384)
+        assert wr >= 256 + blocks * 256 * 4 + T * 8 * 4 + blocks * 384 * 4 and wr > wd
     assert lib.cgd_layout_workspace_bytes(10, 8, 513, 1) == 0
-    assert lib.cgd_dispatch_workspace_bytes(10, 0, 8) == 0
+    assert lib.cgd_dispatch_workspace_bytes(10, 0, 8, 1) == 0
+    assert lib.cgd_dispatch_workspace_bytes(10, 8, 8, 0) == 0
+    assert lib.cgd_dispatch_workspace_bytes(10, 8, 8, 385) == 0
 
 
 def _vp(v):
@@ -100,14 +105,14 @@ def test_layout_rejects_misaligned_outputs():
 
 def test_dispatch_rejects_bad_arguments():
     lib = cgd.load()
-    ok = dict(x=FAKE, T=64, H=128, idx=FAKE, K=4, E=16, R=4, A=1, recv=FAKE, cap=256, off=FAKE, src=FAKE, dst=FAKE,
-              ws=FAKE, wsb=1 << 20)
+    ok = dict(x=FAKE, T=64, H=128, idx=FAKE, K=4, E=16, R=4, A=1, recv=FAKE, cap=256, off=FAKE, nre=FAKE, src=FAKE,
+              dst=FAKE, ws=FAKE, wsb=1 << 20)
 
     def call(**kw):
         a = dict(ok, **kw)
         return lib.cgd_dispatch(_vp(a["x"]), a["T"], a["H"], _vp(a["idx"]), a["K"], a["E"], a["R"], a["A"],
-                                _vp(a["recv"]), a["cap"], _vp(a["off"]), _vp(a["src"]), _vp(a["dst"]),
-                                _vp(a["ws"]) if a["ws"] else None, a["wsb"], None)
+                                _vp(a["recv"]), a["cap"], _vp(a["off"]), _vp(a["nre"]) if a["nre"] else None,
+                                _vp(a["src"]), _vp(a["dst"]), _vp(a["ws"]) if a["ws"] else None, a["wsb"], None)
 
     assert call(H=12) == -1          # hidden not a multiple of 8
     assert call(H=0) == -1
@@ -119,20 +124,28 @@ def test_dispatch_rejects_bad_arguments():
     assert call(wsb=16) == -3        # workspace too small
     assert call(E=15) == -1          # E % R
     assert call(K=17) == -1
+    assert call(nre=FAKE + 2) == -1  # num_recv_tokens_per_expert misaligned
+    assert call(nre=0, H=12) == -1   # (a null count output is allowed; the other checks still apply)
+    # a workspace sized for 8 ranks is too small for 384 (checked sizes differ)
+    small = lib.cgd_dispatch_workspace_bytes(64, 4, 384, 8)
+    assert small < lib.cgd_dispatch_workspace_bytes(64, 4, 384, 384)
+    assert call(R=384, E=384, wsb=small) == -3
 
 
 def test_plan_rejects_bad_arguments():
     lib = cgd.load()
     f = _vp(FAKE)
-    # idx, T, K, E, R, A, cap, off, src, dst, ws, wsb
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, 1 << 20, None) == -2  # capacity
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, f, f, 1 << 20, None) == -1  # alignment
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, None, 0, None) == -3     # workspace
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, None, f, f, 1 << 20, None) == -1  # recv_src_idx
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, None, f, 1 << 20, None) == -1  # dst_row
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, _vp(FAKE + 2), f, 1 << 20, None) == -1
-    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 5, 1, 256, f, f, f, f, 1 << 20, None) == -1  # E % R
-    assert lib.cgd_dispatch_plan(f, 64, 17, 16, 4, 1, 2048, f, f, f, f, 1 << 20, None) == -1  # top-k
+    # idx, T, K, E, R, A, cap, off, nre, src, dst, ws, wsb
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, f, 1 << 20, None) == -2  # capacity
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 0, 256, f, f, f, f, f, 1 << 20, None) == -1  # alignment
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, None, 0, None) == -3     # workspace
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, None, f, f, 1 << 20, None) == -1  # recv_src_idx
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, None, f, 1 << 20, None) == -1  # dst_row
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, _vp(FAKE + 2), f, 1 << 20, None) == -1
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, _vp(FAKE + 2), f, f, f, 1 << 20, None) == -1  # counts
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 4, 1, 256, None, f, f, f, f, 1 << 20, None) == -1  # expert_offset
+    assert lib.cgd_dispatch_plan(f, 64, 4, 16, 5, 1, 256, f, f, f, f, f, 1 << 20, None) == -1  # E % R
+    assert lib.cgd_dispatch_plan(f, 64, 17, 16, 4, 1, 2048, f, f, f, f, f, 1 << 20, None) == -1  # top-k
 
 
 def test_cached_dispatch_and_combine_reject_bad_arguments():
@@ -264,21 +277,23 @@ def test_fp8_entry_points_reject_bad_arguments():
 def test_layout_and_plan_rejects_bad_arguments():
     lib = cgd.load()
     f = _vp(FAKE)
-    # idx, T, K, E, R, A, cap, ntpr, ntpe, itr, off, src, dst, ws, wsb
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, f, f, f, 1 << 20, None) == -2
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 3, 1, 256, f, f, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, None, f, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, _vp(FAKE + 1), f, f, f, f, 1 << 20,
+    # idx, T, K, E, R, A, cap, ntpr, ntpe, itr, off, nre, src, dst, ws, wsb
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 255, f, f, f, f, f, f, f, f, 1 << 20, None) == -2
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 3, 1, 256, f, f, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, None, f, f, f, f, f, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, _vp(FAKE + 1), f, f, f, f, f, 1 << 20,
                                             None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, None, f, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, f, None, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, f, f, None, 0, None) == -3
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, f, None, f, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, f, f, None, f, 1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, _vp(FAKE + 1), f, f, f, 1 << 20,
+                                            None) == -1  # num_recv_tokens_per_expert misaligned
+    assert lib.cgd_layout_and_dispatch_plan(f, 64, 4, 16, 4, 1, 256, f, f, f, f, f, f, f, None, 0, None) == -3
 
 
 def test_packed_entry_points_reject_bad_arguments():
     lib = cgd.load()
     f = _vp(FAKE)
-    assert lib.cgd_packed_workspace_bytes(128, 8, 256) >= lib.cgd_dispatch_workspace_bytes(128, 8, 256)
+    assert lib.cgd_packed_workspace_bytes(128, 8, 256) >= lib.cgd_dispatch_workspace_bytes(128, 8, 256, 1)
     # x, T, H, idx, K, E, R, cap, recv, count, info, dst, stats, ws, wsb
     assert lib.cgd_dispatch_packed(f, 128, 7168, f, 8, 256, 16, -1, f, f, f, f, None, f, 1 << 20, None) == -2
     assert lib.cgd_dispatch_packed(f, 128, 7168, f, 8, 256, 16, 1 << 24, f, f, f, f, None, f, 1 << 20, None) == -2
@@ -341,15 +356,20 @@ def test_binding_rejects_cast_of_an_fp8_payload():
 def test_layout_and_dispatch_rejects_bad_arguments():
     lib = cgd.load()
     f = _vp(FAKE)
-    # x, T, H, idx, K, E, R, A, recv, cap, ntpr, ntpe, itr, off, src, dst, ws, wsb
-    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 255, f, f, f, f, f, f, f, 1 << 20, None) == -2
-    assert lib.cgd_layout_and_dispatch(f, 64, 100, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 3, 1, f, 256, f, f, f, f, f, f, f, 1 << 20, None) == -1
-    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, None, f, f, f, f, f, f, 1 << 20,
+    # x, T, H, idx, K, E, R, A, recv, cap, ntpr, ntpe, itr, off, nre, src, dst, ws, wsb
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 255, f, f, f, f, f, f, f, f, 1 << 20,
+                                       None) == -2
+    assert lib.cgd_layout_and_dispatch(f, 64, 100, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, f, 1 << 20,
                                        None) == -1
-    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, _vp(FAKE + 4), f, f, f, f, 1 << 20,
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 3, 1, f, 256, f, f, f, f, f, f, f, f, 1 << 20,
                                        None) == -1
-    assert lib.cgd_layout_and_dispatch(_vp(FAKE + 8), 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, 1 << 20,
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, None, f, f, f, f, f, f, f, 1 << 20,
                                        None) == -1
-    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, None, 0, None) == -3
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, _vp(FAKE + 4), f, f, f, f, f,
+                                       1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, _vp(FAKE + 2), f, f, f,
+                                       1 << 20, None) == -1  # num_recv_tokens_per_expert misaligned
+    assert lib.cgd_layout_and_dispatch(_vp(FAKE + 8), 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, f,
+                                       1 << 20, None) == -1
+    assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, None, 0, None) == -3
     assert lib.cgd_last_error()

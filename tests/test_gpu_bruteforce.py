@@ -46,10 +46,10 @@ def test_all_small_routings(R):
         idx = idx_all[c]
         ntpr, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx, E, R)
         lay.append((ntpr, ntpe, itr))
-        recv, h = cgd.dispatch(x, idx, E, R)
+        recv, _, h = cgd.dispatch(x, idx, E, R)
         one.append((recv, h.expert_offset, h.dst_row, h.recv_src_idx))
         (ntpr2, _, ntpe2, itr2, _), plan = cgd.layout_and_dispatch_plan(idx, E, R)
-        recv2, h2 = cgd.dispatch_apply(x, plan)
+        recv2, _, h2 = cgd.dispatch_apply(x, plan)
         two.append((ntpr2, ntpe2, itr2, recv2, h2.expert_offset, h2.dst_row, h2.recv_src_idx))
         comb.append(cgd.combine(recv, h, w))
     torch.cuda.synchronize()

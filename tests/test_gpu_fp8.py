@@ -92,7 +92,7 @@ def test_fp8_tuple_dispatch_and_cached(fmt, colmajor, T):
     idx = synth.make_topk_idx(w.replace(name="prefill"), seed=2)
     x = _x(w.T, w.H, seed=2)
     q, sc = cgd.per_token_cast_to_fp8(dev_bf16(x), fmt, column_major_scales=colmajor)
-    recv, h = cgd.dispatch((q, sc), dev_i64(idx), w.E, w.R, expert_alignment=4)
+    recv, _, h = cgd.dispatch((q, sc), dev_i64(idx), w.E, w.R, expert_alignment=4)
     torch.cuda.synchronize()
     o = oracle.dispatch(None, idx, w.E, w.R, align=4, with_rows=False)
     np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
@@ -103,7 +103,7 @@ def test_fp8_tuple_dispatch_and_cached(fmt, colmajor, T):
     # cached: a second batch through the same handle
     x2 = _x(w.T, w.H, seed=3)
     q2, sc2 = cgd.per_token_cast_to_fp8(dev_bf16(x2), fmt, column_major_scales=colmajor)
-    recv2, _ = cgd.dispatch((q2, sc2), handle=h)
+    recv2, _, _ = cgd.dispatch((q2, sc2), handle=h)
     torch.cuda.synchronize()
     oq2, osc2 = oracle.cast_to_fp8(x2, fmt)
     _check_rows(recv2, oq2, osc2, o["dst_row"])
@@ -119,7 +119,7 @@ def test_cast_on_dispatch_parity(fmt, T, K, E, R, H, p_neg):
     idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
     idx[rng.random((T, K)) < p_neg] = -1
     x = _x(T, H, seed=T)
-    recv, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, cast_fp8=fmt)
+    recv, _, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, cast_fp8=fmt)
     torch.cuda.synchronize()
     o = oracle.dispatch(None, idx, E, R, with_rows=False)
     np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
@@ -137,8 +137,8 @@ def test_cached_cast_on_dispatch_equals_planned(fmt, T, K):
     rng = np.random.default_rng(T)
     idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
     x = dev_bf16(_x(T, H, seed=T + 1))
-    (q1, s1), h = cgd.dispatch(x, dev_i64(idx), E, R, cast_fp8=fmt)
-    (q2, s2), h2 = cgd.dispatch(x, handle=h, cast_fp8=fmt)
+    (q1, s1), _, h = cgd.dispatch(x, dev_i64(idx), E, R, cast_fp8=fmt)
+    (q2, s2), _, h2 = cgd.dispatch(x, handle=h, cast_fp8=fmt)
     torch.cuda.synchronize()
     assert h2 is h
     data = h.recv_src_idx >= 0
@@ -153,7 +153,7 @@ def test_cast_on_dispatch_prefill_round_trip():
     w = synth.WORKLOADS["prefill"]
     inp = synth.make_inputs(w, seed=0)
     x_dev = dev_bf16(inp["x"])
-    recv, h = cgd.dispatch(x_dev, dev_i64(inp["topk_idx"]), w.E, w.R, cast_fp8=cgd.SCALE_F32)
+    recv, _, h = cgd.dispatch(x_dev, dev_i64(inp["topk_idx"]), w.E, w.R, cast_fp8=cgd.SCALE_F32)
     torch.cuda.synchronize()
     o = oracle.dispatch(None, inp["topk_idx"], w.E, w.R, with_rows=False)
     np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
@@ -208,8 +208,8 @@ def test_fp8_zero_tokens():
     x = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
     q, sc = cgd.per_token_cast_to_fp8(x)
     idx = torch.empty((0, 4), dtype=torch.int64, device=DEV)
-    recv, h = cgd.dispatch(x, idx, 16, 4, expert_alignment=2, cast_fp8=cgd.SCALE_F32)
-    recv2, _ = cgd.dispatch((q, sc), idx, 16, 4, expert_alignment=2)
+    recv, _, h = cgd.dispatch(x, idx, 16, 4, expert_alignment=2, cast_fp8=cgd.SCALE_F32)
+    recv2, _, _ = cgd.dispatch((q, sc), idx, 16, 4, expert_alignment=2)
     torch.cuda.synchronize()
     assert q.shape == (0, 256) and sc.shape == (0, 2)
     assert recv[0].shape == (16, 256) and recv[1].shape == (16, 2)

@@ -15,19 +15,19 @@ pytestmark = pytest.mark.gpu
 
 def _expert_step(x, idx, wt, w, out):
     lay, plan = cgd.layout_and_dispatch_plan(idx, w.E, w.R)
-    recv, h = cgd.dispatch_apply(x, plan)
+    recv, _, h = cgd.dispatch_apply(x, plan)
     cgd.combine(recv, h, wt, out=out)
     return list(lay[0::2][:2]) + [lay[3], h.expert_offset, h.dst_row, h.recv_src_idx, out]
 
 
 def _small_step(x, idx, wt, w, out):
-    recv, h = cgd.dispatch(x, idx, w.E, w.R)
+    recv, _, h = cgd.dispatch(x, idx, w.E, w.R)
     cgd.combine(recv, h, wt, out=out)
     return [h.expert_offset, h.dst_row, h.recv_src_idx, out]
 
 
 def _small_layout_step(x, idx, wt, w, out):
-    (ntpr, _, ntpe, itr, _), recv, h = cgd.layout_and_dispatch(x, idx, w.E, w.R)
+    (ntpr, _, ntpe, itr, _), recv, _, h = cgd.layout_and_dispatch(x, idx, w.E, w.R)
     cgd.combine(recv, h, wt, out=out)
     return [ntpr, ntpe, itr, h.expert_offset, h.dst_row, h.recv_src_idx, out]
 

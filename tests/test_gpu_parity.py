@@ -52,7 +52,7 @@ def _check_rows_on_device(recv_x, x_dev, dst_np):
 def _dispatch_and_check(w, idx_np, x_np, align=1, cap=None):
     x_dev = dev_bf16(x_np)
     idx_dev = dev_i64(idx_np)
-    recv_x, h = cgd.dispatch(x_dev, idx_dev, w.E, w.R, expert_alignment=align, recv_capacity=cap)
+    recv_x, _, h = cgd.dispatch(x_dev, idx_dev, w.E, w.R, expert_alignment=align, recv_capacity=cap)
     torch.cuda.synchronize()
     want_rows = x_np.size * w.K <= FULL_ORACLE_ROWS
     o = oracle.dispatch(x_np if want_rows else None, idx_np, w.E, w.R, align=align, cap=h.recv_capacity,
@@ -109,7 +109,7 @@ def test_cached_dispatch_matches_fresh_dispatch(T):
     inp = synth.make_inputs(w, seed=3)
     x_dev, recv_x, h, o = _dispatch_and_check(w, inp["topk_idx"], inp["x"])
     x2 = synth.make_x(w.replace(name="prefill-second-batch"), seed=3)
-    recv2, h2 = cgd.dispatch(dev_bf16(x2), handle=h)
+    recv2, _, h2 = cgd.dispatch(dev_bf16(x2), handle=h)
     torch.cuda.synchronize()
     assert h2 is h
     o2 = oracle.dispatch(x2, inp["topk_idx"], w.E, w.R)
@@ -124,7 +124,7 @@ def test_plan_then_apply_equals_dispatch(T):
     inp = synth.make_inputs(w.replace(name="prefill"), seed=9)
     idx, x_np = inp["topk_idx"][:w.T], synth.make_x(w, seed=9)
     plan = cgd.dispatch_plan(dev_i64(idx), w.E, w.R, expert_alignment=4)
-    recv_x, h = cgd.dispatch_apply(dev_bf16(x_np), plan)
+    recv_x, _, h = cgd.dispatch_apply(dev_bf16(x_np), plan)
     torch.cuda.synchronize()
     o = oracle.dispatch(x_np, idx, w.E, w.R, align=4)
     np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
@@ -161,7 +161,7 @@ def test_plan_alone_writes_the_handle(T, K, cap_extra):
     assert (src[n:] == -1).all()
     if T:
         x = synth.make_x(synth.WORKLOADS["tiny"].replace(T=T, H=64), seed=T)
-        recv_x, _ = cgd.dispatch_apply(dev_bf16(x), plan)
+        recv_x, _, _ = cgd.dispatch_apply(dev_bf16(x), plan)
         torch.cuda.synchronize()
         data = np.nonzero(src >= 0)[0]
         np.testing.assert_array_equal(host_bits(recv_x)[data], x.view(np.uint16)[src[data]])
@@ -247,7 +247,7 @@ def test_zero_tokens():
     w, idx, x, wts = _edge(T=0, K=4, E=16, R=4, H=64)
     ntpr, ntpe, itr = _run_layout(idx, w.E, w.R)
     assert ntpr.tolist() == [0] * 4 and ntpe.tolist() == [0] * 16 and itr.shape == (0, 4)
-    recv_x, h = cgd.dispatch(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
+    recv_x, _, h = cgd.dispatch(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV),
                              torch.empty((0, 4), dtype=torch.int64, device=DEV), 16, 4, expert_alignment=4)
     out = cgd.combine(recv_x, h, torch.empty((0, 4), dtype=torch.float32, device=DEV))
     torch.cuda.synchronize()
@@ -278,7 +278,7 @@ def test_determinism_20_repeats():
     ref = None
     for i in range(20):
         ntpr, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx, w.E, w.R)
-        recv_x, h = cgd.dispatch(x, idx, w.E, w.R)
+        recv_x, _, h = cgd.dispatch(x, idx, w.E, w.R)
         out = cgd.combine(recv_x, h, wt)
         torch.cuda.synchronize()
         d = _digest(ntpr, ntpe, itr, h.expert_offset, h.dst_row, h.recv_src_idx, recv_x, out)
@@ -295,7 +295,7 @@ def test_seeds_sweep_prefill_and_skewed():
             _check_layout(idx, w.E, w.R)
             idx_dev = dev_i64(idx)
             x_small = torch.zeros((w.T, 8), dtype=torch.bfloat16, device=DEV)
-            _, h = cgd.dispatch(x_small, idx_dev, w.E, w.R)
+            _, _, h = cgd.dispatch(x_small, idx_dev, w.E, w.R)
             torch.cuda.synchronize()
             o = oracle.dispatch(None, idx, w.E, w.R, with_rows=False)
             np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
@@ -319,7 +319,7 @@ def test_layout_and_plan_in_one_launch(case):
     say(f"[fused] {case}")
     (ntpr, _, ntpe, itr, _), plan = cgd.layout_and_dispatch_plan(dev_i64(idx), w.E, w.R, expert_alignment=align)
     xs = torch.zeros((w.T, 8), dtype=torch.bfloat16, device=DEV) if x is None else dev_bf16(x[:, :8].copy())
-    _, h = cgd.dispatch_apply(xs, plan)
+    _, _, h = cgd.dispatch_apply(xs, plan)
     torch.cuda.synchronize()
     o = oracle.layout(idx, w.E, w.R)
     np.testing.assert_array_equal(ntpr.cpu().numpy(), o[0])
@@ -344,7 +344,7 @@ def test_layout_and_dispatch_in_one_call(T, K, E, R, align, p_neg):
     idx[rng.random((T, K)) < p_neg] = -1
     x = synth.make_x(synth.WORKLOADS["tiny"].replace(T=T, H=72), seed=T)
     say(f"[layout and dispatch] T={T} K={K} E={E} R={R} align={align}")
-    (ntpr, _, ntpe, itr, _), recv_x, h = cgd.layout_and_dispatch(dev_bf16(x), dev_i64(idx), E, R,
+    (ntpr, _, ntpe, itr, _), recv_x, _, h = cgd.layout_and_dispatch(dev_bf16(x), dev_i64(idx), E, R,
                                                                  expert_alignment=align)
     torch.cuda.synchronize()
     o = oracle.layout(idx, E, R)
@@ -372,7 +372,7 @@ def test_launches_split_over_token_ranges():
     x = synth.normal_bf16(synth.stream_key(5, 123, 1), T * H).reshape(T, H)
     x_dev = dev_bf16(x)
     idx_dev = dev_i64(idx)
-    recv_x, h = cgd.dispatch(x_dev, idx_dev, E, R)
+    recv_x, _, h = cgd.dispatch(x_dev, idx_dev, E, R)
     torch.cuda.synchronize()
     o = oracle.dispatch(None, idx, E, R, with_rows=False)
     np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])

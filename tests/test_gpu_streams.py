@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 def _step(x, idx, wt, E, R):
     ntpr, _, ntpe, itr, _ = cgd.get_dispatch_layout(idx, E, R)
-    recv_x, h = cgd.dispatch(x, idx, E, R)
+    recv_x, _, h = cgd.dispatch(x, idx, E, R)
     out = cgd.combine(recv_x, h, wt)
     _, ridx, rw, _, nh = cgd.normal_dispatch(x, itr, ntpe, idx, wt, num_experts=E)
     nout, _ = cgd.normal_combine(cgd.normal_dispatch(x, handle=nh)[0], nh, rw)

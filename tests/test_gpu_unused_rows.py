@@ -54,7 +54,7 @@ def test_expert_combine_reads_only_rows_with_data(T, K, E, R, H, align, extra):
     idx, x, w = _inputs(T, K, E, H, seed=T)
     cap = cgd.dispatch_capacity(T, K, E, align) + extra
     say(f"[unused rows, expert] T={T} K={K} E={E} align={align} cap={cap}")
-    recv, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap)
+    recv, _, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap)
     wd = dev_f32(w)
     clean = cgd.combine(recv, h, wd)
     torch.cuda.synchronize()
@@ -130,7 +130,7 @@ def test_expert_dispatch_writes_only_rows_with_data(T, K, E, R, H, align, extra)
     cap = cgd.dispatch_capacity(T, K, E, align) + extra
     say(f"[writes, expert] T={T} K={K} E={E} align={align} cap={cap}")
     recv, big = _guarded(cap, H)
-    _, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap, recv_x=recv)
+    _, _, h = cgd.dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap, recv_x=recv)
     torch.cuda.synchronize()
     _check_writes(big, cap, h.recv_src_idx.cpu().numpy(), x)
 
@@ -167,7 +167,7 @@ def test_combines_write_only_their_output(T, K, E, R, H):
     idx, x, w = _inputs(T, K, E, H, seed=T + 6)
     x_d, idx_d, w_d = dev_bf16(x), dev_i64(idx), dev_f32(w)
     say(f"[writes, combine outputs] T={T} K={K} E={E} R={R} H={H}")
-    recv, h = cgd.dispatch(x_d, idx_d, E, R)
+    recv, _, h = cgd.dispatch(x_d, idx_d, E, R)
     out, big = _guarded(T, H)
     cgd.combine(recv, h, w_d, out=out)
     precv, _, ph = cgd.low_latency_dispatch(x_d, idx_d, E, R, expert_capacity=T)
@@ -202,10 +202,10 @@ def test_fp8_dispatch_writes_only_rows_with_data(T, K, E, R, H, align, extra, ca
     x_d = dev_bf16(x)
     q_ref, s_ref = cgd.per_token_cast_to_fp8(x_d, fmt)
     if cast:
-        _, h = cgd.dispatch(x_d, dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap, recv_x=recv,
+        _, _, h = cgd.dispatch(x_d, dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap, recv_x=recv,
                             cast_fp8=fmt)
     else:
-        _, h = cgd.dispatch((q_ref, s_ref), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap,
+        _, _, h = cgd.dispatch((q_ref, s_ref), dev_i64(idx), E, R, expert_alignment=align, recv_capacity=cap,
                             recv_x=recv)
     torch.cuda.synchronize()
     src = h.recv_src_idx.cpu().numpy()
