@@ -4,22 +4,32 @@
 One step = get_dispatch_layout -> dispatch -> combine over one batch of the
 workload (default: prefill, 4096 tokens, hidden 7168, top-8 of 256 experts,
 8 logical ranks), with identity experts (combine reads the dispatched rows)
-and softmax routing weights: layout and dispatch plan (one pass over the
-routing, then the final-row launch), the dispatch apply (the row copy, or one
-broadcast kernel for small batches), combine. Inputs are generated by the seeded
-generator and are resident in HBM before timing starts. The step's wall
-time is taken over replays of the step captured once in a HIP graph (the
-serving setting; --timing eager times Python launches instead); every
-per-kernel figure comes from HIP events around eager launches.
+and softmax routing weights. Inputs come from the seeded generator and are
+resident in HBM before timing starts.
 
-Prints one JSON line with the whole-step token throughput, per-call times
-(and get_dispatch_layout timed alone: layout_us), HBM GB/s of dispatch and
-combine against the MI355X peak (8 TB/s), the roofline entry of the dominant
-kernel, and the CPU oracle's throughput on a bounded sample of the same
-workload. dispatch_GBps / dispatch_frac_of_peak time the whole dispatch of
-the step, plan and rows (the expert and rank-granular paths fuse the layout
-into the plan, so it is counted there too); dispatch_apply_* time the row
-movement alone, i.e. the cached dispatch that reuses a handle.
+Inputs rotate: --sets distinct seeded (x, topk_idx, topk_weights) sets
+(seeds seed..seed+sets-1; 295 MB at prefill, more than the 256 MB Infinity
+Cache), step k running set k mod sets, so each step's x was last touched
+several steps earlier and is read from HBM. The headline is the wall time of
+--steps such steps, each replayed from a HIP graph captured once per set (the
+serving setting; --timing eager times Python launches instead). The same
+figures with one x reused every step (which stays in the Infinity Cache) are
+reported as warm_x, and with the caches swept by a read-only pass before every
+step as cold_cache.
+
+Per-kernel durations come from HIP events around each call of
+--kernel-samples eager steps (rotating sets), on the stream the kernels run
+on; every time, GB/s and fraction of peak is a median over those samples.
+dispatch_* time the whole dispatch of the step, plan and rows (the expert and
+rank-granular paths fuse the layout into the plan, so it is counted there
+too); dispatch_apply_* time the row movement alone, i.e. the cached dispatch
+that reuses a handle. layout_us (get_dispatch_layout alone) and
+launch_floor_us (libcgd's empty kernel) are both wall time per call over
+graph replays of 20 back-to-back calls.
+
+Prints one JSON line with the whole-step token throughput, those figures, the
+roofline entry of the dominant data kernel and the CPU oracle's throughput on
+a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -36,12 +46,18 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public specification
 METRIC = "dispatch+combine HBM GB/s & tokens/s; layout µs at 4096 tok, top-8/256 exp"
+FLUSH_BYTES = 512 << 20  # read-only sweep that evicts the 256 MB Infinity Cache
+FP8_FORMATS = {"f32": 0, "pow2": 1, "ue8m0": 2}
 
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes: each tensor counted once (x read once).
+# ---------------------------------------------------------------------------
 
 def algorithmic_bytes(w, N: int) -> dict:
-    """Bytes each call must move, each tensor counted once. dispatch: x read,
-    rows written, dst_row and recv_src_idx written; its apply (the row copy
-    after the plan) reads x and dst_row and writes the rows."""
+    """dispatch: x read, rows written, dst_row and recv_src_idx written; its
+    apply (the row copy after the plan) reads x and dst_row and writes the
+    rows; combine reads the rows, dst_row and weights and writes the output."""
     T, H, K, E, R = w.T, w.H, w.K, w.E, w.R
     return {
         "layout": T * K * 8 + T * R + (E + R) * 4,
@@ -49,9 +65,6 @@ def algorithmic_bytes(w, N: int) -> dict:
         "apply": T * H * 2 + N * H * 2 + T * K * 4,
         "combine": N * H * 2 + 2 * T * K * 4 + T * H * 2,
     }
-
-
-FP8_FORMATS = {"f32": 0, "pow2": 1, "ue8m0": 2}
 
 
 def fp8_row_bytes(w, fmt: int) -> int:
@@ -68,14 +81,452 @@ def algorithmic_bytes_fp8(w, N: int, fmt: int) -> dict:
     return b
 
 
-def context_measurements(dev) -> dict:
-    """Measured context for the figures: the duration of a minimal kernel
-    (1-element fill: the launch floor the latency-bound kernels sit on) and the
-    device-to-device copy rate of 1 GiB (read + write bytes per second), by
-    torch and by libcgd's own 16-byte copy (cgd_copy)."""
+def algorithmic_bytes_normal(w, N: int, fmt: int | None = None) -> dict:
+    """Rank-granular calls (N = rows sent), each tensor once."""
+    T, H, K, E, R = w.T, w.H, w.K, w.E, w.R
+    b = {
+        "layout": T * K * 8 + T * R + (E + R) * 4,
+        # x, is_token_in_rank, topk_idx/weights in; rows, send_row, recv_src_idx,
+        # recv_topk_idx/weights out
+        "dispatch": T * H * 2 + T * R + T * K * 12 + N * H * 2 + T * R * 4 + N * (4 + K * 12),
+        # rows, send_row, recv_topk_weights in; combined_x, combined_topk_weights out
+        "combine": N * H * 2 + T * R * 4 + N * K * 4 + T * H * 2 + T * K * 4,
+    }
+    if fmt is not None:
+        # codes + scales instead of bf16 rows; the cast reads x and writes the tuple
+        rb = fp8_row_bytes(w, fmt)
+        b["cast"] = T * H * 2 + T * rb
+        b["dispatch"] += T * (rb - 2 * H) + N * (rb - 2 * H)
+    b["apply"] = b["dispatch"]
+    return b
+
+
+# ---------------------------------------------------------------------------
+# The three paths. Each holds --sets input sets on the device and shared
+# outputs; step(i, ev) runs one step on set i, recording ev[j] before call j
+# and ev[-1] after the last call.
+# ---------------------------------------------------------------------------
+
+class _Path:
+    labels: tuple = ()           # one per call of a step
+    dispatch_labels: tuple = ()  # the calls that make up the whole dispatch
+    split_labels: tuple = ()     # calls of split_step, the same work as separate calls (if any)
+    apply_label: str | None = None  # the row movement alone, a label of the split (or plain) step
+    data_kernels: tuple = ()     # (label, bytes key, traffic kernels) of the data-moving calls
+
+    def __init__(self, w, sets, dev, fmt):
+        import numpy as np
+        import torch
+        self.w, self.dev, self.fmt = w, dev, fmt
+        self.inp = sets
+        self.idx = [torch.from_numpy(s["topk_idx"]).to(dev) for s in sets]
+        self.x = [torch.from_numpy(s["x"].view(np.int16)).view(torch.bfloat16).to(dev) for s in sets]
+        self.wt = [torch.from_numpy(s["topk_weights"]).to(dev) for s in sets]
+        self.out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+        self.rows = [0] * len(sets)
+
+    @staticmethod
+    def _rec(ev, j):
+        if ev and ev[j] is not None:
+            ev[j].record()
+
+    @property
+    def dispatch_span(self) -> tuple:
+        """Event indices around the whole dispatch (its calls are consecutive)."""
+        a = self.labels.index(self.dispatch_labels[0])
+        return a, a + len(self.dispatch_labels)
+
+    def nbytes(self, i: int) -> dict:
+        raise NotImplementedError
+
+
+class ExpertPath(_Path):
+    """bf16: layout and dispatch in one call (layout_and_dispatch: the layout,
+    the plan and the rows; one launch for a batch of at most one 256-token
+    tile, such as decode), then combine. The split step makes the same calls
+    separately: layout + plan (layout_and_dispatch_plan), the row movement
+    alone (dispatch_apply, i.e. the cached dispatch), combine. FP8: layout +
+    plan, the cast on dispatch, combine."""
+
+    def __init__(self, w, sets, dev, fmt):
+        import torch
+        import combine_get_dispatch_06_amd as cgd
+        super().__init__(w, sets, dev, fmt)
+        self.cgd = cgd
+        cap = cgd.dispatch_capacity(w.T, w.K, w.E, w.align)
+        self.recv_x = torch.empty((cap, w.H), dtype=torch.bfloat16, device=dev)
+        if fmt is not None:
+            # FP8 rows land in recv_q; the identity expert's bf16 output (the
+            # cast-back rows, made outside the timed steps) is recv_x
+            self.recv_q = (torch.empty((cap, w.H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn),
+                           torch.empty((cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32,
+                                       device=dev))
+        self.one_launch = fmt is None and w.T <= 256
+        self.split_labels = ("layout_and_plan", "dispatch_apply", "combine")
+        if fmt is None:
+            self.labels = ("dispatch", "combine")
+            self.dispatch_labels = ("dispatch",)
+        else:
+            self.labels = self.split_labels
+            self.dispatch_labels = ("layout_and_plan", "dispatch_apply")
+        self.apply_label = "dispatch_apply"
+        # roofline candidates: the longest single kernel (the one-launch
+        # dispatch of a decode batch, else the row movement alone) or combine
+        self.data_kernels = ((("dispatch", "dispatch", ("rank_kernel",)) if self.one_launch else
+                              ("dispatch_apply", "apply", APPLY_KERNELS)),
+                             ("combine", "combine", ("combine_kernel",)))
+        self.handles = [None] * len(sets)
+
+    def step(self, i, ev=None):
+        if self.fmt is not None:
+            return self.split_step(i, ev)
+        cgd, w = self.cgd, self.w
+        self._rec(ev, 0)
+        _, _, _, h = cgd.layout_and_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_alignment=w.align,
+                                             recv_x=self.recv_x)
+        self._rec(ev, 1)
+        cgd.combine(self.recv_x, h, self.wt[i], out=self.out)
+        self._rec(ev, 2)
+        self.handles[i] = h
+
+    def split_step(self, i, ev=None):
+        cgd, w = self.cgd, self.w
+        self._rec(ev, 0)
+        _, plan = cgd.layout_and_dispatch_plan(self.idx[i], w.E, w.R, expert_alignment=w.align)
+        self._rec(ev, 1)
+        if self.fmt is None:
+            _, _, h = cgd.dispatch_apply(self.x[i], plan, recv_x=self.recv_x)
+        else:
+            _, _, h = cgd.dispatch_apply(self.x[i], plan, recv_x=self.recv_q, cast_fp8=self.fmt)
+        self._rec(ev, 2)
+        cgd.combine(self.recv_x, h, self.wt[i], out=self.out)
+        self._rec(ev, 3)
+        self.handles[i] = h
+
+    def check(self, i):
+        """combine(dispatch(x)) returns x: exactly for bf16, within the FP8
+        rounding for FP8 payloads (the cast-back rows of this set's dispatch)."""
+        import torch
+        self.step(i)
+        if self.fmt is not None:
+            self.cgd.per_token_cast_back(self.recv_q, self.fmt, out=self.recv_x)
+            self.step(i)
+        torch.cuda.synchronize()
+        x = self.x[i]
+        if self.fmt is None:
+            assert torch.equal(self.out.view(torch.int16), x.view(torch.int16)), f"round trip failed (set {i})"
+        else:
+            rel = ((self.out.float() - x.float()).norm() / x.float().norm()).item()
+            assert rel < 0.05, f"FP8 round trip error {rel} (set {i})"
+        self.rows[i] = int(self.handles[i].expert_offset[-1].item())
+
+    def nbytes(self, i):
+        n = self.rows[i]
+        return algorithmic_bytes(self.w, n) if self.fmt is None else algorithmic_bytes_fp8(self.w, n, self.fmt)
+
+    def describe(self):
+        return {"dispatch": ("layout_and_dispatch (one launch: layout + plan + rows)" if self.one_launch else
+                             "layout_and_dispatch (layout + plan with x pulled toward the caches, then the rows)"
+                             if self.fmt is None else
+                             "layout + plan (layout_and_dispatch_plan), then the cast on dispatch (dispatch_apply)"),
+                "split": "layout_and_dispatch_plan, then dispatch_apply (the cached dispatch: rows alone)",
+                "experts": "identity (combine reads dispatched rows)" if self.fmt is None else
+                "identity (combine reads the cast-back FP8 rows, made before timing)"}
+
+
+class NormalPath(_Path):
+    """layout + rank-granular plan (one launch), [FP8 cast,] apply, combine
+    (identity experts, no bias)."""
+    labels = ("layout_and_plan", "cast", "dispatch_apply", "combine")
+    dispatch_labels = ("layout_and_plan", "cast", "dispatch_apply")
+    apply_label = "dispatch_apply"
+    data_kernels = (("dispatch_apply", "apply", ("normal_scatter_kernel",)),
+                    ("combine", "combine", ("normal_combine_kernel",)))
+
+    def __init__(self, w, sets, dev, fmt):
+        import torch
+        import combine_get_dispatch_06_amd as cgd
+        super().__init__(w, sets, dev, fmt)
+        self.cgd = cgd
+        cap = cgd.normal_capacity(w.T, w.K, w.R)
+        self.recv_x = torch.empty((cap, w.H), dtype=torch.bfloat16, device=dev)
+        if fmt is not None:
+            self.recv_q = (torch.empty((cap, w.H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn),
+                           torch.empty((cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32,
+                                       device=dev))
+        self.last = [None] * len(sets)
+
+    def step(self, i, ev=None):
+        cgd, w = self.cgd, self.w
+        self._rec(ev, 0)
+        (_, _, _, itr, _), plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R,
+                                                                      expert_alignment=w.align)
+        self._rec(ev, 1)
+        if self.fmt is not None:
+            q, sc = cgd.per_token_cast_to_fp8(self.x[i], self.fmt)
+        self._rec(ev, 2)
+        if self.fmt is None:
+            _, _, rw, _, h = cgd.normal_dispatch_apply(self.x[i], plan, self.idx[i], self.wt[i], recv_x=self.recv_x)
+        else:
+            _, _, rw, _, h = cgd.normal_dispatch_apply((q, sc), plan, self.idx[i], self.wt[i], recv_x=self.recv_q)
+        self._rec(ev, 3)
+        cgd.normal_combine(self.recv_x, h, rw, out=self.out)
+        self._rec(ev, 4)
+        self.last[i] = (h, itr)
+
+    def check(self, i):
+        """each token comes back as bf16(x * ranks it was sent to): exactly for
+        bf16, within the FP8 rounding for FP8 payloads."""
+        import torch
+        self.step(i)
+        if self.fmt is not None:
+            self.cgd.per_token_cast_back(self.recv_q, self.fmt, out=self.recv_x)
+            self.step(i)
+        torch.cuda.synchronize()
+        h, itr = self.last[i]
+        n = itr.sum(dim=1, dtype=torch.float32).unsqueeze(1)
+        want = (self.x[i].float() * n).to(torch.bfloat16)
+        if self.fmt is None:
+            assert torch.equal(self.out.view(torch.int16), want.view(torch.int16)), f"round trip failed (set {i})"
+        else:
+            rel = ((self.out.float() - want.float()).norm() / want.float().norm()).item()
+            assert rel < 0.05, f"FP8 round trip error {rel} (set {i})"
+        self.rows[i] = int(h.rank_offset[-1].item())
+
+    def nbytes(self, i):
+        return algorithmic_bytes_normal(self.w, self.rows[i], self.fmt)
+
+    def describe(self):
+        return {"path": "normal (one row per flagged rank)",
+                "experts": "identity (combine reads dispatched rows), no bias" if self.fmt is None else
+                "identity (combine reads the cast-back FP8 rows, made before timing), no bias"}
+
+
+class PackedPath(_Path):
+    """layout, packed (fixed-capacity) dispatch, combine over the packed rows."""
+    labels = ("layout", "dispatch", "combine")
+    dispatch_labels = ("dispatch",)
+    # the packed dispatch is the plan and the apply: its traffic is their sum
+    data_kernels = (("dispatch", "dispatch", ("rank_kernel", "finalize_kernel", "scatter_kernel",
+                                              "scatter_bcast_kernel", "scatter_cast_kernel")),
+                    ("combine", "combine", ("combine_kernel",)))
+
+    def __init__(self, w, sets, dev, fmt):
+        import numpy as np
+        import torch
+        import combine_get_dispatch_06_amd as cgd
+        super().__init__(w, sets, dev, fmt)
+        self.cgd = cgd
+        # capacity: the largest per-expert count of any set rounded up to 64
+        # (no slot dropped), fixed before timing like any low-latency buffer
+        most = max(int(np.bincount(s["topk_idx"][s["topk_idx"] >= 0], minlength=w.E).max()) for s in sets)
+        self.cap = -(-most // 64) * 64
+        self.recv = torch.empty((w.E, self.cap, w.H), dtype=torch.bfloat16, device=dev)
+        if fmt is not None:
+            self.recv_q = (torch.empty((w.E * self.cap, w.H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn),
+                           torch.empty((w.E * self.cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32,
+                                       device=dev))
+        self.count = [None] * len(sets)
+
+    def step(self, i, ev=None):
+        cgd, w = self.cgd, self.w
+        self._rec(ev, 0)
+        cgd.get_dispatch_layout(self.idx[i], w.E, w.R)
+        self._rec(ev, 1)
+        if self.fmt is None:
+            _, count, h = cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
+                                                   out=self.recv)
+        else:
+            _, count, h = cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
+                                                   use_fp8=True, scale_format=self.fmt, out=self.recv_q)
+        self._rec(ev, 2)
+        cgd.low_latency_combine(self.recv, self.wt[i], h, out=self.out)
+        self._rec(ev, 3)
+        self.count[i] = count
+
+    def check(self, i):
+        import torch
+        self.step(i)
+        if self.fmt is not None:
+            self.cgd.per_token_cast_back(self.recv_q, self.fmt, out=self.recv.view(-1, self.w.H))
+            self.step(i)
+        torch.cuda.synchronize()
+        x = self.x[i]
+        if self.fmt is None:
+            assert torch.equal(self.out.view(torch.int16), x.view(torch.int16)), f"round trip failed (set {i})"
+        else:
+            rel = ((self.out.float() - x.float()).norm() / x.float().norm()).item()
+            assert rel < 0.05, f"FP8 round trip error {rel} (set {i})"
+        self.rows[i] = int(self.count[i].sum().item())
+
+    def nbytes(self, i):
+        n = self.rows[i]
+        return algorithmic_bytes(self.w, n) if self.fmt is None else algorithmic_bytes_fp8(self.w, n, self.fmt)
+
+    def describe(self):
+        return {"path": f"packed (fixed capacity {self.cap} rows per expert)",
+                "experts": "identity (combine reads the packed rows)"}
+
+
+# ---------------------------------------------------------------------------
+# Timing
+# ---------------------------------------------------------------------------
+
+def stats(a) -> dict:
+    import numpy as np
+    a = np.asarray(a, dtype=np.float64)
+    return {"median": float(np.median(a)), "min": float(np.min(a)), "max": float(np.max(a))}
+
+
+def kernel_samples(path, order, flush=None):
+    """Two eager loops of one step per entry of `order` (set indices),
+    optionally after a cache sweep outside the events. The first records
+    events around every call (the per-call split); the second only around the
+    whole dispatch and the combine, since each recorded event adds a few µs
+    of its own to the interval it closes.
+    -> {label: per-sample µs, "dispatch", "combine", "step"}, set index per sample."""
     import numpy as np
     import torch
-    tiny = torch.empty(1, dtype=torch.int32, device=dev)
+    split = getattr(path, "split_step", None) if path.split_labels else None
+    labels = path.split_labels if split else path.labels
+    ns = len(labels) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ns)] for _ in order]
+    for ev, i in zip(evs, order):
+        if flush is not None:
+            flush()
+        (split or path.step)(i, ev)
+    n = len(path.labels) + 1
+    a, b = path.dispatch_span
+    keep = {a, b, n - 2, n - 1}
+    whole = [[torch.cuda.Event(enable_timing=True) if j in keep else None for j in range(n)] for _ in order]
+    for ev, i in zip(whole, order):
+        if flush is not None:
+            flush()
+        path.step(i, ev)
+    torch.cuda.synchronize()
+    us = {lab: np.array([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs]) for j, lab in enumerate(labels)}
+    us["step"] = np.array([e[0].elapsed_time(e[-1]) * 1e3 for e in evs])
+    us["dispatch"] = np.array([e[a].elapsed_time(e[b]) * 1e3 for e in whole])
+    us["combine"] = np.array([e[n - 2].elapsed_time(e[n - 1]) * 1e3 for e in whole])
+    return us, np.asarray(order)
+
+
+def summarize(path, us, sets_of_sample) -> dict:
+    """Medians over samples: per-call µs, whole-dispatch µs, GB/s and
+    fractions of the HBM peak (bytes of each sample's own input set)."""
+    import numpy as np
+    nb = [path.nbytes(int(i)) for i in sets_of_sample]
+    disp = us["dispatch"]  # events only around the whole dispatch
+    comb = us["combine"]
+
+    def rate(key, t):
+        return np.array([b[key] for b in nb]) / (t * 1e-6) / 1e9
+
+    out = {"kernel_us": {lab: stats(us[lab]) for lab in (path.split_labels or path.labels)},
+           "step_us": stats(us["step"]),
+           "dispatch_us": float(np.median(disp)), "combine_us": float(np.median(comb))}
+    out["kernel_us"]["combine"] = stats(comb)  # the whole-dispatch loop's figure (one event fewer)
+    d, c = rate("dispatch", disp), rate("combine", comb)
+    out.update(dispatch_GBps=float(np.median(d)), dispatch_frac_of_peak=float(np.median(d)) / HBM_PEAK_GBPS,
+               combine_GBps=float(np.median(c)), combine_frac_of_peak=float(np.median(c)) / HBM_PEAK_GBPS,
+               dispatch_tokens_per_s=float(np.median(path.w.T / (disp * 1e-6))),
+               combine_tokens_per_s=float(np.median(path.w.T / (comb * 1e-6))))
+    if path.apply_label:
+        a = rate("apply", us[path.apply_label])
+        out.update(dispatch_apply_us=float(np.median(us[path.apply_label])), dispatch_apply_GBps=float(np.median(a)),
+                   dispatch_apply_frac_of_peak=float(np.median(a)) / HBM_PEAK_GBPS)
+    if "layout_and_plan" in us:
+        out["layout_and_plan_us"] = float(np.median(us["layout_and_plan"]))
+    if "dispatch" in out["kernel_us"]:
+        out["kernel_us"]["dispatch"] = stats(disp)
+    return out
+
+
+def graph_wall(path, order, steps: int, warmup: int) -> float:
+    """Capture one step per distinct set of `order` in a HIP graph on a side
+    stream (after untimed steps on that stream, so every workspace exists
+    before capture), then time `steps` replays, step k replaying the graph of
+    set order[k mod len(order)]; returns seconds."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    distinct = sorted(set(order))
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            for i in distinct:
+                path.step(i)
+    s.synchronize()
+    graphs = {}
+    for i in distinct:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            path.step(i)
+        graphs[i] = g
+    seq = [graphs[order[k % len(order)]] for k in range(max(steps, warmup))]
+    for k in range(warmup):
+        seq[k].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        seq[k].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def eager_wall(path, order, steps: int) -> float:
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        path.step(order[k % len(order)])
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def timed_wall(args, path, order):
+    """Wall seconds of args.steps steps and how they were launched."""
+    if args.timing == "graph":
+        try:
+            return graph_wall(path, order, args.steps, args.warmup), "HIP graph replays"
+        except Exception as exc:  # capture unsupported here: time eager launches
+            print(f"graph capture failed ({exc}); timing eager launches", file=sys.stderr)
+    return eager_wall(path, order, args.steps), "eager launches"
+
+
+def per_call_us(fn, calls: int = 20, replays: int = 20) -> dict:
+    """`calls` back-to-back calls of fn captured in a HIP graph, replayed
+    `replays` times: the wall time per call (a launch each, as a serving loop
+    sees it). Eager event pairs would time the host's Python launch cost
+    instead: the GPU finishes such a call before the next one is submitted."""
+    import numpy as np
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(replays):
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        per.append((time.perf_counter() - t0) / calls * 1e6)
+    return {**stats(np.array(per)), "how": f"{calls} calls per HIP graph replay, wall time per call"}
+
+
+def copy_ceilings(dev) -> dict:
+    """Device-to-device copy rate of 1 GiB (read + write bytes per second), by
+    torch and by libcgd's own 16-byte copy (cgd_copy), event-timed medians."""
+    import numpy as np
+    import torch
+    import combine_get_dispatch_06_amd as cgd
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
 
@@ -90,102 +541,16 @@ def context_measurements(dev) -> dict:
         torch.cuda.synchronize()
         return np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
 
-    import combine_get_dispatch_06_amd as cgd
-    floor = timed(lambda: tiny.fill_(1), 50)
     copy = timed(lambda: b.copy_(a), 5)
     own = timed(lambda: cgd.copy_(b, a), 5)
     del a, b
-    return {"launch_floor_us": float(np.median(floor)),
-            "copy_1GiB_GBps": float(2 * (1 << 30) / (np.median(copy) * 1e-6) / 1e9),
+    return {"copy_1GiB_GBps": float(2 * (1 << 30) / (np.median(copy) * 1e-6) / 1e9),
             "cgd_copy_1GiB_GBps": float(2 * (1 << 30) / (np.median(own) * 1e-6) / 1e9)}
-
-
-def layout_us(cgd, idx, w, calls: int = 20, replays: int = 20) -> dict:
-    """get_dispatch_layout alone (the metric's "layout us"): `calls`
-    back-to-back calls captured in a HIP graph, replayed `replays` times; the
-    wall time per call (a launch each, as a serving loop sees it). Eager
-    event pairs would time the host's Python launch cost instead: the GPU
-    finishes a layout before the next call is submitted."""
-    import numpy as np
-    import torch
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(3):
-            cgd.get_dispatch_layout(idx, w.E, w.R)
-    s.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        for _ in range(calls):
-            cgd.get_dispatch_layout(idx, w.E, w.R)
-    g.replay()
-    torch.cuda.synchronize()
-    per = []
-    for _ in range(replays):
-        t0 = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        per.append((time.perf_counter() - t0) / calls * 1e6)
-    return {**stats(np.array(per)), "how": f"{calls} calls per HIP graph replay, wall time per call"}
-
-
-def stats(a) -> dict:
-    import numpy as np
-    return {"median": float(np.median(a)), "min": float(np.min(a)), "max": float(np.max(a))}
 
 
 def input_digests(inp: dict) -> dict:
     import hashlib
     return {k: hashlib.sha256(v.tobytes()).hexdigest()[:16] for k, v in inp.items()}
-
-
-def timed_wall(args, step, eager_wall: float):
-    """Wall seconds for args.steps steps and how they were launched: graph
-    replays (default) or the eager launches already timed."""
-    if args.timing == "graph":
-        try:
-            return graph_wall(step, args.steps, args.warmup), "HIP graph replays"
-        except Exception as exc:  # capture unsupported here: keep the eager figure
-            print(f"graph capture failed ({exc}); reporting eager launches", file=sys.stderr)
-            return eager_wall, "eager launches (graph capture failed)"
-    return eager_wall, "eager launches"
-
-
-def graph_wall(step, steps: int, warmup: int) -> float:
-    """Capture one step in a HIP graph on a side stream (after warm-up steps on
-    that stream, so every workspace exists before capture) and time `steps`
-    replays; returns seconds."""
-    import torch
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(3):
-            step()
-    s.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        step()
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
-    torch.cuda.synchronize()
-    return time.perf_counter() - t0
-
-
-def algorithmic_bytes_normal(w, N: int) -> dict:
-    """Bytes each rank-granular call must move (N = rows sent), each tensor once."""
-    T, H, K, E, R = w.T, w.H, w.K, w.E, w.R
-    return {
-        "layout": T * K * 8 + T * R + (E + R) * 4,
-        # x, is_token_in_rank, topk_idx/weights in; rows, send_row, recv_src_idx,
-        # recv_topk_idx/weights out
-        "dispatch": T * H * 2 + T * R + T * K * 12 + N * H * 2 + T * R * 4 + N * (4 + K * 12),
-        # rows, send_row, recv_topk_weights in; combined_x, combined_topk_weights out
-        "combine": N * H * 2 + T * R * 4 + N * K * 4 + T * H * 2 + T * K * 4,
-    }
 
 
 def cpu_baseline(w, inp, budget_s: float) -> dict:
@@ -202,7 +567,7 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
         if el >= budget_s:
             break
     return {"value": w.T * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} whole steps (layout+dispatch+combine) of the {w.name} workload, "
+            "sample": f"{reps} whole steps (layout+dispatch+combine) of the {w.name} workload (seed 0), "
                       f"single-threaded C oracle, {el:.1f} s on {cpu_model()} ({os.cpu_count()} cpus visible)"}
 
 
@@ -216,6 +581,24 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
+def roofline(path, summary, traffic_json, tkey) -> dict:
+    """The dominant data kernel (longest median) with its achieved GB/s
+    (median over samples of algorithmic bytes / duration) against the peak."""
+    cands = {lab: (summary["dispatch_us"] if lab == "dispatch" else summary["kernel_us"][lab]["median"])
+             for lab, _, _ in path.data_kernels}
+    dom = max(cands, key=cands.get)
+    lab, key, kernels = next(d for d in path.data_kernels if d[0] == dom)
+    if dom == path.apply_label:
+        achieved = summary["dispatch_apply_GBps"]
+    elif dom == "combine":
+        achieved = summary["combine_GBps"]
+    else:
+        achieved = summary["dispatch_GBps"]
+    traffic = lookup_traffic_sum(traffic_json, tkey, kernels)
+    return {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "duration_us": cands[dom]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,16 +606,19 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sets", type=int, default=5,
+                    help="distinct seeded input sets rotated every step (seeds seed..seed+sets-1)")
+    ap.add_argument("--kernel-samples", type=int, default=200,
+                    help="eager steps whose calls are event-timed for the per-kernel medians (>= 200)")
     ap.add_argument("--path", choices=("expert", "normal", "packed"), default="expert",
                     help="expert: one received row per selected expert (default); normal: one per flagged rank; "
                          "packed: fixed-capacity per-expert buffers (the low-latency layout)")
     ap.add_argument("--timing", choices=("graph", "eager"), default="graph",
-                    help="graph (default): time replays of the step captured once in a HIP graph, falling back to "
-                         "eager launches if capture fails; eager: time the Python launches. Per-kernel figures "
-                         "are always event-timed eager launches")
+                    help="graph (default): time replays of steps captured once per input set in HIP graphs; "
+                         "eager: time the Python launches")
     ap.add_argument("--cold-steps", type=int, default=20,
-                    help="extra steps with a 512 MiB write between them (evicts the 256 MB Infinity Cache), "
-                         "reported as cold per-kernel times; 0 skips them")
+                    help="extra event-timed steps, each after a read-only sweep of 512 MiB (evicts the 256 MB "
+                         "Infinity Cache without leaving dirty lines); 0 skips them")
     ap.add_argument("--fp8", choices=tuple(FP8_FORMATS), default=None,
                     help="FP8 (e4m3fn) dispatch payload with this scale format: the expert path casts on "
                          "dispatch, the normal path casts first and dispatches the (codes, scales) tuple")
@@ -272,129 +658,56 @@ def main() -> int:
         return 0
 
     w = synth.WORKLOADS[args.workload]
-    inp = synth.make_inputs(w, seed=args.seed)
-    if args.path == "normal":
-        return run_normal(args, w, inp, dev)
-    if args.path == "packed":
-        return run_packed(args, w, inp, dev)
-    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
-    wt = torch.from_numpy(inp["topk_weights"]).to(dev)
-    cap = cgd.dispatch_capacity(w.T, w.K, w.E, w.align)
     fmt = FP8_FORMATS[args.fp8] if args.fp8 else None
-    recv_x = torch.empty((cap, w.H), dtype=torch.bfloat16, device=dev)
-    if fmt is not None:
-        # FP8 rows land in recv_q; the identity expert's bf16 output (the
-        # cast-back rows, made once outside the timed steps) goes to recv_x
-        recv_q = (torch.empty((cap, w.H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn),
-                  torch.empty((cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32, device=dev))
-    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
-    # a bf16 batch of at most one 256-token tile (decode) takes layout, plan
-    # and rows in one launch (layout_and_dispatch)
-    one_launch = fmt is None and w.T <= 256
-
-    def step(ev=None):
-        # layout + dispatch plan (rank_kernel with the layout outputs, then
-        # finalize_kernel), dispatch apply (scatter_kernel, or
-        # scatter_cast_kernel for FP8), combine; one event pair per call so
-        # each call's duration is measured alone. One launch: the plan's
-        # pair is empty and the apply's pair holds layout_and_dispatch.
-        if ev:
-            ev[0].record()
-            ev[1].record()
-        if one_launch:
-            if ev:
-                ev[2].record()
-            _, _, h = cgd.layout_and_dispatch(x, idx, w.E, w.R, expert_alignment=w.align, recv_x=recv_x)
-        else:
-            _, plan = cgd.layout_and_dispatch_plan(idx, w.E, w.R, expert_alignment=w.align)
-            if ev:
-                ev[2].record()
-            if fmt is None:
-                _, h = cgd.dispatch_apply(x, plan, recv_x=recv_x)
-            else:
-                _, h = cgd.dispatch_apply(x, plan, recv_x=recv_q, cast_fp8=fmt)
-        if ev:
-            ev[3].record()
-        cgd.combine(recv_x, h, wt, out=out)
-        if ev:
-            ev[4].record()
-        return h
+    nsets = max(1, args.sets)
+    sets = [synth.make_inputs(w, seed=args.seed + i) for i in range(nsets)]
+    path = {"expert": ExpertPath, "normal": NormalPath, "packed": PackedPath}[args.path](w, sets, dev, fmt)
+    rotation = list(range(nsets))
+    set_bytes = sum(v.nbytes for s in sets for v in s.values())
 
     # first call timed on its own (cf. the first-call latency discussed on the pages)
     torch.cuda.synchronize()
     t = time.perf_counter()
-    h = step()
+    path.step(0)
     torch.cuda.synchronize()
     first_ms = (time.perf_counter() - t) * 1e3
-    if fmt is not None:
-        cgd.per_token_cast_back(recv_q, fmt, out=recv_x)
-    for _ in range(args.warmup):
-        step()
+    for i in rotation:  # every set must round-trip (identity experts)
+        path.check(i)
+    for k in range(args.warmup):
+        path.step(rotation[k % nsets])
     torch.cuda.synchronize()
-    N = int(h.expert_offset[-1].item())
-    # the step is valid only if combine(dispatch(x)) returns x (identity
-    # experts): exactly for bf16, within the FP8 rounding for FP8 payloads
-    if fmt is None:
-        assert torch.equal(out.view(torch.int16), x.view(torch.int16)), "round trip failed"
-    else:
-        rel = ((out.float() - x.float()).norm() / x.float().norm()).item()
-        assert rel < 0.05, f"FP8 round trip error {rel}"
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    samples = max(args.kernel_samples, 1)
+    us, which = kernel_samples(path, [rotation[k % nsets] for k in range(samples)])
+    rotated = summarize(path, us, which)
+    wall, timing = timed_wall(args, path, rotation)
 
-    def us(a, b):
-        return np.array([e[a].elapsed_time(e[b]) for e in evs]) * 1e3
+    us0, which0 = kernel_samples(path, [0] * samples)
+    warm = summarize(path, us0, which0)
+    wall0, _ = timed_wall(args, path, [0])
+    warm.update(ms_per_step=wall0 / args.steps * 1e3, tokens_per_s=w.T * args.steps / wall0)
 
-    lay, plan_us, apply_us, com = us(0, 1), us(1, 2), us(2, 3), us(3, 4)
-    dis = plan_us + apply_us
     cold = None
     if args.cold_steps > 0:
-        # same steps with the Infinity Cache evicted before each one (the
-        # flush is outside the event brackets)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.cold_steps)]
-        for e in cev:
-            flush.fill_(1)
-            step(e)
-        torch.cuda.synchronize()
-        del flush
+        sweep = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+        sink = torch.empty((), dtype=torch.int64, device=dev)
 
-        def cus(a, b):
-            return np.array([e[a].elapsed_time(e[b]) for e in cev]) * 1e3
+        def flush():
+            torch.sum(sweep, dim=0, dtype=torch.int64, out=sink)  # reads 512 MiB, writes 8 bytes
 
-        cold = {"layout_and_plan_us": stats(cus(1, 2)), "dispatch_apply_us": stats(cus(2, 3)),
-                "combine_us": stats(cus(3, 4)), "step_us": stats(cus(0, 4))}
-    wall, timing = timed_wall(args, step, wall)
-    layout_alone = layout_us(cgd, idx, w)
-    nbytes = algorithmic_bytes(w, N) if fmt is None else algorithmic_bytes_fp8(w, N, fmt)
-    d_gbps = nbytes["dispatch"] / (dis.mean() * 1e-6) / 1e9
-    c_gbps = nbytes["combine"] / (com.mean() * 1e-6) / 1e9
-    ms_per_step = wall / args.steps * 1e3
+        usc, whichc = kernel_samples(path, [rotation[k % nsets] for k in range(args.cold_steps)], flush=flush)
+        cold = summarize(path, usc, whichc)
+        cold["flush"] = "read-only sweep of 512 MiB (a reduction) before every step, outside the events"
+        del sweep
 
-    # dominant kernel: the dispatch apply kernel or combine_kernel
-    # the dispatch apply is one launch: scatter_kernel (row copy),
-    # scatter_bcast_kernel (small batches, top-k > 8) or scatter_cast_kernel
-    # (FP8 cast on dispatch), as the library picks
-    kern = {"dispatch_apply": (apply_us.mean(), nbytes["apply"]),
-            "combine_kernel": (com.mean(), nbytes["combine"])}
-    if one_launch:
-        kern = {"dispatch (one launch: layout + plan + rows)": (apply_us.mean(), nbytes["dispatch"]),
-                "combine_kernel": (com.mean(), nbytes["combine"])}
-    dom = max(kern, key=lambda k: kern[k][0])
-    dom_us, dom_bytes = kern[dom]
-    tkey = w.name + (f":fp8-{args.fp8}" if fmt is not None else "")
-    traffic = (lookup_traffic(args.traffic_json, tkey, "combine_kernel") if dom == "combine_kernel"
-               else lookup_traffic_sum(args.traffic_json, tkey, ("rank_kernel",) if one_launch else APPLY_KERNELS))
-    ctx = context_measurements(dev)
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    layout_alone = per_call_us(lambda: cgd.get_dispatch_layout(path.idx[0], w.E, w.R))
+    floor = per_call_us(lambda: cgd.empty_(dev))
+    ctx = copy_ceilings(dev)
+    tkey = w.name + ("" if args.path == "expert" else ":" + args.path) + (f":fp8-{args.fp8}" if fmt is not None else "")
+    roof = roofline(path, rotated, args.traffic_json, tkey)
+    roof.update(copy_ceiling=ctx["cgd_copy_1GiB_GBps"], frac_of_copy_ceiling=roof["achieved"] / ctx["cgd_copy_1GiB_GBps"])
 
+    dtype = "bf16" if fmt is None else "fp8_e4m3 dispatch / bf16 combine"
     res = {
         "metric": METRIC,
         "value": w.T * args.steps / wall,
@@ -402,297 +715,43 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": wall / args.steps * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if fmt is None else "fp8_e4m3 dispatch / bf16 combine",
-        "data": "synthetic (seeded generator: uniform distinct top-k, N(0,1) bf16 x, softmax weights)",
+        "dtype": dtype,
+        "data": "synthetic (seeded generator: uniform distinct top-k or Zipf(1.2), N(0,1) bf16 x, softmax weights)",
         "config": {"workload": w.name, "num_tokens": w.T, "hidden": w.H, "num_topk": w.K, "num_experts": w.E,
                    "num_ranks": w.R, "expert_alignment": w.align, "routing": w.routing,
-                   "experts": "identity (combine reads dispatched rows)" if fmt is None else
-                   "identity (combine reads the cast-back FP8 rows, made once before timing)",
-                   **({} if fmt is None else {"fp8_scales": args.fp8}),
-                   "dispatch": ("one launch: layout + plan + rows (layout_and_dispatch)" if one_launch else
-                                "layout + plan (layout_and_dispatch_plan), then the row movement (dispatch_apply)"),
-                   "timing": timing},
+                   "inputs": f"{nsets} seeded sets (seeds {args.seed}..{args.seed + nsets - 1}, "
+                             f"{set_bytes / 1e6:.0f} MB) rotated every step",
+                   **path.describe(), **({} if fmt is None else {"fp8_scales": args.fp8}),
+                   "rows_sent": path.rows, "timing": timing},
         "layout_us": layout_alone,
-        "layout_and_plan_us": float(plan_us.mean()),
-        "dispatch_apply_us": float(apply_us.mean()),
-        "combine_us": float(com.mean()),
-        "dispatch_GBps": d_gbps,
-        "combine_GBps": c_gbps,
-        "dispatch_frac_of_peak": d_gbps / HBM_PEAK_GBPS,
-        "combine_frac_of_peak": c_gbps / HBM_PEAK_GBPS,
-        "dispatch_tokens_per_s": w.T / (dis.mean() * 1e-6),
-        "dispatch_apply_GBps": nbytes["apply"] / (apply_us.mean() * 1e-6) / 1e9,
-        "dispatch_apply_frac_of_peak": nbytes["apply"] / (apply_us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-        "combine_tokens_per_s": w.T / (com.mean() * 1e-6),
+        "launch_floor_us": floor,
+        **{k: v for k, v in rotated.items() if k != "kernel_us"},
+        "kernel_us": rotated["kernel_us"],
+        "kernel_samples": samples,
         "first_step_ms": first_ms,
-        "kernel_us": {"layout_and_plan": stats(plan_us), "dispatch_apply": stats(apply_us), "combine": stats(com)},
+        "warm_x": {**warm, "how": "one input set (seed %d) every step: x stays in the Infinity Cache" % args.seed},
         "cold_cache": cold,
         **ctx,
-        "inputs_sha256": input_digests(inp),
-        "bytes_per_call": nbytes,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "copy_ceiling": ctx["cgd_copy_1GiB_GBps"],
-                     "frac_of_copy_ceiling": achieved / ctx["cgd_copy_1GiB_GBps"]},
+        "inputs_sha256": input_digests(sets[0]),
+        "bytes_per_call": path.nbytes(0),
+        "roofline": roof,
     }
     if args.cpu_baseline_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_baseline_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)
     return 0
 
 
-def run_normal(args, w, inp, dev) -> int:
-    """Rank-granular step: layout and normal dispatch plan (one launch) ->
-    [FP8 cast ->] normal dispatch apply -> normal combine (identity experts,
-    no bias), each call bracketed by events."""
-    import numpy as np
-    import torch
+# ---------------------------------------------------------------------------
+# Measured traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE counters)
+# ---------------------------------------------------------------------------
 
-    import combine_get_dispatch_06_amd as cgd
-
-    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
-    wt = torch.from_numpy(inp["topk_weights"]).to(dev)
-    cap = cgd.normal_capacity(w.T, w.K, w.R)
-    fmt = FP8_FORMATS[args.fp8] if args.fp8 else None
-    recv_x = torch.empty((cap, w.H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
-    if fmt is not None:
-        sdt = torch.uint8 if fmt == 2 else torch.float32
-        recv_q = (torch.empty((cap, w.H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn),
-                  torch.empty((cap, w.H // 128), dtype=sdt, device=dev))
-
-    def step(ev=None):
-        # layout + normal dispatch plan (layout_kernel with the plan), [FP8
-        # cast,] apply (normal_scatter_kernel), normal combine; one event pair
-        # per kernel
-        if ev:
-            ev[0].record()
-        (_, _, ntpe, itr, _), plan = cgd.layout_and_normal_dispatch_plan(idx, w.E, w.R, expert_alignment=w.align)
-        if ev:
-            ev[1].record()
-        if fmt is not None:
-            q, sc = cgd.per_token_cast_to_fp8(x, fmt)
-        if ev:
-            ev[2].record()
-            ev[3].record()
-        if fmt is None:
-            _, _, rw, _, h = cgd.normal_dispatch_apply(x, plan, idx, wt, recv_x=recv_x)
-        else:
-            _, _, rw, _, h = cgd.normal_dispatch_apply((q, sc), plan, idx, wt, recv_x=recv_q)
-        if ev:
-            ev[4].record()
-        cgd.normal_combine(recv_x, h, rw, out=out)
-        if ev:
-            ev[5].record()
-        return h, itr
-
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    h, itr = step()
-    torch.cuda.synchronize()
-    first_ms = (time.perf_counter() - t) * 1e3
-    if fmt is not None:
-        cgd.per_token_cast_back(recv_q, fmt, out=recv_x)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    N = int(h.rank_offset[-1].item())
-    # valid only if each token comes back as bf16(x * ranks it was sent to)
-    # (exactly for bf16, within the FP8 rounding for FP8 payloads)
-    n = itr.sum(dim=1, dtype=torch.float32).unsqueeze(1)
-    want = (x.float() * n).to(torch.bfloat16)
-    if fmt is None:
-        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), "round trip failed"
-    else:
-        rel = ((out.float() - want.float()).norm() / want.float().norm()).item()
-        assert rel < 0.05, f"FP8 round trip error {rel}"
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    def us(a, b):
-        return np.array([e[a].elapsed_time(e[b]) for e in evs]) * 1e3
-
-    lay_plan, cast_us, apply_us, com = us(0, 1), us(1, 2), us(3, 4), us(4, 5)
-    dis = lay_plan + cast_us + apply_us
-    wall, timing = timed_wall(args, step, wall)
-    nbytes = algorithmic_bytes_normal(w, N)
-    if fmt is not None:
-        # codes + scales instead of bf16 rows; the cast reads x and writes the tuple
-        rb = fp8_row_bytes(w, fmt)
-        nbytes["cast"] = w.T * w.H * 2 + w.T * rb
-        nbytes["dispatch"] += w.T * (rb - 2 * w.H) + N * (rb - 2 * w.H)
-    d_gbps = nbytes["dispatch"] / (dis.mean() * 1e-6) / 1e9
-    c_gbps = nbytes["combine"] / (com.mean() * 1e-6) / 1e9
-    kern = {"normal_scatter_kernel": (apply_us.mean(), nbytes["dispatch"]),
-            "normal_combine_kernel": (com.mean(), nbytes["combine"])}
-    dom = max(kern, key=lambda k: kern[k][0])
-    dom_us, dom_bytes = kern[dom]
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    traffic = lookup_traffic(args.traffic_json, w.name + ":normal" + (f":fp8-{args.fp8}" if fmt is not None else ""),
-                             dom)
-    res = {
-        "metric": METRIC,
-        "value": w.T * args.steps / wall,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if fmt is None else "fp8_e4m3 dispatch / bf16 combine",
-        "data": "synthetic (seeded generator: uniform distinct top-k, N(0,1) bf16 x, softmax weights)",
-        "config": {"workload": w.name, "path": "normal (one row per flagged rank)", "num_tokens": w.T,
-                   "hidden": w.H, "num_topk": w.K, "num_experts": w.E, "num_ranks": w.R,
-                   "expert_alignment": w.align, "routing": w.routing, "rows_sent": N,
-                   "experts": "identity (combine reads dispatched rows), no bias" if fmt is None else
-                   "identity (combine reads the cast-back FP8 rows, made once before timing), no bias",
-                   **({} if fmt is None else {"fp8_scales": args.fp8}),
-                   "timing": timing},
-        "layout_and_plan_us": float(lay_plan.mean()),
-        "dispatch_us": float(dis.mean()),
-        "dispatch_cast_us": float(cast_us.mean()),
-        "dispatch_apply_us": float(apply_us.mean()),
-        "combine_us": float(com.mean()),
-        "dispatch_GBps": d_gbps,
-        "combine_GBps": c_gbps,
-        "dispatch_frac_of_peak": d_gbps / HBM_PEAK_GBPS,
-        "combine_frac_of_peak": c_gbps / HBM_PEAK_GBPS,
-        "dispatch_apply_GBps": nbytes["dispatch"] / (apply_us.mean() * 1e-6) / 1e9,
-        "dispatch_apply_frac_of_peak": nbytes["dispatch"] / (apply_us.mean() * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-        "first_step_ms": first_ms,
-        "bytes_per_call": nbytes,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
-    }
-    print(json.dumps(res), flush=True)
-    return 0
-
-
-def run_packed(args, w, inp, dev) -> int:
-    """Low-latency step: layout -> packed dispatch (plan + scatter into
-    fixed per-expert buffers) -> combine over the packed rows (identity
-    experts), each call bracketed by events."""
-    import numpy as np
-    import torch
-
-    import combine_get_dispatch_06_amd as cgd
-
-    idx = torch.from_numpy(inp["topk_idx"]).to(dev)
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
-    wt = torch.from_numpy(inp["topk_weights"]).to(dev)
-    # capacity: the routing's largest per-expert count rounded up to 64 (no
-    # slot dropped), fixed before timing like any low-latency buffer size
-    ti = inp["topk_idx"]
-    cap = int(-(-int(np.bincount(ti[ti >= 0], minlength=w.E).max()) // 64) * 64)
-    fmt = FP8_FORMATS[args.fp8] if args.fp8 else None
-    recv = torch.empty((w.E, cap, w.H), dtype=torch.bfloat16, device=dev)
-    if fmt is not None:
-        recv_q = (torch.empty((w.E * cap, w.H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn),
-                  torch.empty((w.E * cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32, device=dev))
-    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
-
-    def step(ev=None):
-        if ev:
-            ev[0].record()
-        cgd.get_dispatch_layout(idx, w.E, w.R)
-        if ev:
-            ev[1].record()
-        if fmt is None:
-            _, count, h = cgd.low_latency_dispatch(x, idx, w.E, w.R, expert_capacity=cap, out=recv)
-        else:
-            _, count, h = cgd.low_latency_dispatch(x, idx, w.E, w.R, expert_capacity=cap, use_fp8=True,
-                                                   scale_format=fmt, out=recv_q)
-        if ev:
-            ev[2].record()
-        cgd.low_latency_combine(recv, wt, h, out=out)
-        if ev:
-            ev[3].record()
-        return h, count
-
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    h, count = step()
-    torch.cuda.synchronize()
-    first_ms = (time.perf_counter() - t) * 1e3
-    if fmt is not None:
-        cgd.per_token_cast_back(recv_q, fmt, out=recv.view(-1, w.H))
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    N = int(count.sum().item())
-    if fmt is None:
-        assert torch.equal(out.view(torch.int16), x.view(torch.int16)), "round trip failed"
-    else:
-        rel = ((out.float() - x.float()).norm() / x.float().norm()).item()
-        assert rel < 0.05, f"FP8 round trip error {rel}"
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    def us(a, b):
-        return np.array([e[a].elapsed_time(e[b]) for e in evs]) * 1e3
-
-    lay, dis, com = us(0, 1), us(1, 2), us(2, 3)
-    wall, timing = timed_wall(args, step, wall)
-    nbytes = algorithmic_bytes(w, N) if fmt is None else algorithmic_bytes_fp8(w, N, fmt)
-    kern = {"dispatch_packed (plan + apply)": (dis.mean(), nbytes["dispatch"]),
-            "combine_kernel": (com.mean(), nbytes["combine"])}
-    dom = max(kern, key=lambda k: kern[k][0])
-    dom_us, dom_bytes = kern[dom]
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    # measured bytes of the same unit: both launches of the packed dispatch,
-    # or the combine
-    tkey = w.name + ":packed" + (f":fp8-{args.fp8}" if fmt is not None else "")
-    traffic = (lookup_traffic(args.traffic_json, tkey, "combine_kernel") if dom == "combine_kernel"
-               else lookup_traffic_sum(args.traffic_json, tkey, PLAN_KERNELS + APPLY_KERNELS))
-    res = {
-        "metric": METRIC,
-        "value": w.T * args.steps / wall,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if fmt is None else "fp8_e4m3 dispatch / bf16 combine",
-        "data": "synthetic (seeded generator: uniform distinct top-k, N(0,1) bf16 x, softmax weights)",
-        "config": {"workload": w.name, "path": f"packed (fixed capacity {cap} rows per expert)", "num_tokens": w.T,
-                   "hidden": w.H, "num_topk": w.K, "num_experts": w.E, "num_ranks": w.R, "rows_sent": N,
-                   "routing": w.routing, "experts": "identity (combine reads the packed rows)",
-                   **({} if fmt is None else {"fp8_scales": args.fp8}),
-                   "timing": timing},
-        "layout_us": float(lay.mean()),
-        "dispatch_us": float(dis.mean()),
-        "combine_us": float(com.mean()),
-        "dispatch_GBps": nbytes["dispatch"] / (dis.mean() * 1e-6) / 1e9,
-        "combine_GBps": nbytes["combine"] / (com.mean() * 1e-6) / 1e9,
-        "first_step_ms": first_ms,
-        "bytes_per_call": nbytes,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
-    }
-    print(json.dumps(res), flush=True)
-    return 0
+APPLY_KERNELS = ("scatter_kernel", "scatter_bcast_kernel", "scatter_cast_kernel")
+PLAN_KERNELS = ("rank_kernel", "finalize_kernel")
 
 
 def lookup_traffic(path: str, key: str, kernel: str):
@@ -707,10 +766,6 @@ def lookup_traffic(path: str, key: str, kernel: str):
     except Exception:
         return None
     return None
-
-
-APPLY_KERNELS = ("scatter_kernel", "scatter_bcast_kernel", "scatter_cast_kernel")
-PLAN_KERNELS = ("rank_kernel", "finalize_kernel")
 
 
 def lookup_traffic_sum(path: str, key: str, kernels) -> float | None:

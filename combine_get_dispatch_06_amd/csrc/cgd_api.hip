@@ -225,7 +225,7 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
     }
     err = cgd::launch_dispatch_plan(topk_idx, num_tokens, num_topk, num_experts, expert_alignment, recv_capacity,
                                     expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
-                                    stream);
+                                    stream, x, num_tokens * (int64_t)hidden * 2);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
     err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
@@ -258,7 +258,7 @@ int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const
     err = cgd::launch_layout_and_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment,
                                       recv_capacity, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
                                       expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
-                                      stream);
+                                      stream, x, num_tokens * (int64_t)hidden * 2);
     if (err != hipSuccess) return hip_fail(err, "layout and dispatch plan launch");
     err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");

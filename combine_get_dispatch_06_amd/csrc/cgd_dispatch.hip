@@ -142,6 +142,34 @@ struct TileOut {
     uint4* recv_x;
 };
 
+// Blocks of the plan past its tiles pull x toward the caches (L2, Infinity
+// Cache) while the plan runs, so that the row copy that follows finds it
+// there: the plan is latency-bound on a few CUs and leaves the others and
+// the memory bandwidth idle, while a row copy reading x from HBM is bound by
+// that latency. Each thread reads vectors b*BLOCK + tid + j*stride with
+// ordinary loads, kInFlight at a time, and discards them.
+#ifndef CGD_PREFETCH_BLOCKS
+#define CGD_PREFETCH_BLOCKS 240
+#endif
+#ifndef CGD_PREFETCH_IN_FLIGHT
+#define CGD_PREFETCH_IN_FLIGHT 8
+#endif
+constexpr int kPrefetchBlocks = CGD_PREFETCH_BLOCKS;
+template <int BLOCK>
+__device__ __forceinline__ void prefetch_rows(const uint4* __restrict__ p, int64_t n, int b, int nb) {
+    constexpr int kInFlight = CGD_PREFETCH_IN_FLIGHT;
+    const int64_t stride = (int64_t)nb * BLOCK;
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)b * BLOCK + threadIdx.x; i < n; i += stride * kInFlight) {
+        uint4 v[kInFlight];
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) v[j] = (i + j * stride < n) ? p[i + j * stride] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    asm volatile("" ::"v"(acc));  // the loaded values are used, so the loads stay
+}
+
 // rank_kernel. Slot loops read the routing from LDS, which keeps the kernel
 // light on registers for any num_topk. seg_cap >= 0 selects the
 // fixed-capacity packed layout: segment e is rows [e*seg_cap, (e+1)*seg_cap)
@@ -164,7 +192,8 @@ struct TileOut {
 // the tokens' rows, their x chunks loaded at the start (none with nvec = 0:
 // the plan alone of a one-tile batch with many spare rows). Larger batches
 // leave packed slot words and tile bases in the workspace for
-// finalize_kernel.
+// finalize_kernel; blocks past the plan_tiles tiles (if any) prefetch x
+// (px, pvecs 16-byte vectors) and take no part in the plan.
 template <int RW, bool LAYOUT, bool FUSED = false>
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
                                                          int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
@@ -175,7 +204,12 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
                                                          int32_t* __restrict__ packed_count,
                                                          int32_t* __restrict__ stats,
                                                          unsigned int* __restrict__ ticket, LayoutOut lo,
-                                                         TileOut fc) {
+                                                         TileOut fc, int plan_tiles, const uint4* __restrict__ px,
+                                                         int64_t pvecs) {
+    if (!FUSED && (int)blockIdx.x >= plan_tiles) {
+        prefetch_rows<kRankTile>(px, pvecs, (int)blockIdx.x - plan_tiles, (int)gridDim.x - plan_tiles);
+        return;
+    }
     extern __shared__ __align__(16) char lds[];
     unsigned long long* s_tok = reinterpret_cast<unsigned long long*>(lds);
     int32_t* s_pre = reinterpret_cast<int32_t*>(s_tok + kRankWaves * E);
@@ -183,7 +217,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     int32_t* s_off = s_slot + kRankTile * K;
     int32_t* s_wsum = s_off + E + 1;
     const int tile = FUSED ? 0 : blockIdx.x;
-    const int ntiles = FUSED ? 1 : gridDim.x;
+    const int ntiles = FUSED ? 1 : plan_tiles;
     const bool writer = !FUSED || blockIdx.x == 0;  // writes the plan's outputs
 
     const int tid = threadIdx.x;
@@ -339,7 +373,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         if (LAYOUT && writer)
             for (int r = tid; r < lo.R; r += kRankTile) lo.ntpr[r] = s_rank[r];
     } else {
-    if (!last_block_done(ticket)) return;
+    if (!last_block_done(ticket, ntiles)) return;
 
     // ---- 2. last block: per-tile bases and segment offsets ----
     // one pass over the tile histograms: each becomes the rows of its expert
@@ -520,48 +554,67 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_bcast_kernel(con
     }
 }
 
-// Row copy to final rows, one wave per (token, 1 KB column chunk, slot): the
-// wave loads the chunk (64 lanes x 16 bytes) and stores it once, to its
-// slot's receive row, with a non-temporal store. The K waves of a chunk are
-// adjacent (slot fastest), so the chunk comes from HBM once and from L2 for
-// the others. Measured on MI355X, this beats one wave storing its chunk to
-// all K rows by 3-15 % (prefill, Zipf-skewed and large-batch shapes): many
-// short waves that store once and exit keep more stores in flight, spread
-// over more rows, than long waves that issue K stores each. Each wave needs
-// its final row after a single dependent load (dst_row, which the plan
-// resolved), and stores nothing but its chunk: recording dst_row and
-// recv_src_idx here, in the copy waves or in extra blocks, measured 3 us
-// slower at prefill than in the plan. The grid covers tokens [t0, t_end). A
-// row is nvec 16-byte vectors of any payload (bf16 rows, or FP8 rows with
-// their scales moved as the side payload by the chunk-0 wave).
-__global__ __launch_bounds__(kSlotWaves* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t t0,
-                                                                   int64_t t_end, int nvec, int nchunk, int K,
-                                                                   const int32_t* __restrict__ dst_row, int64_t cap,
-                                                                   uint4* __restrict__ recv_x, SideRows side) {
+// Row copy to final rows, one wave per (token, U KB column chunk, group of S
+// slots), WPB waves per block: the wave loads its chunk (U vectors of 16
+// bytes per lane) and stores it to its S slots' receive rows with
+// non-temporal stores. The waves of a chunk are adjacent (slot group
+// fastest), so the chunk comes from HBM once and from L2 for the others.
+// Measured on MI355X (prefill unless stated), with inputs that change every
+// step, i.e. x in HBM: the waves of a chunk all wait for its one load, so
+// fewer, fuller waves win: (S, U, WPB) = (2, 1, 16) takes 104 us against
+// 131 us with one store per wave (S = 1) and 104-111 us with one wave
+// storing all K rows; Zipf-skewed 184-186 against 246 us; at top-16 (32768
+// tokens, hidden 4096) (2, 2, 4) takes 851 us against 868 for (2, 1, 16) and
+// 910 for the broadcast kernel. With x in the Infinity Cache the shapes are
+// within 3 %. Each wave needs its final rows after a single dependent load
+// (dst_row, which the plan resolved), and stores nothing but its chunk:
+// recording dst_row and recv_src_idx here, in the copy waves or in extra
+// blocks, measured 3 us slower at prefill than in the plan. The grid covers
+// tokens [t0, t_end). A row is nvec 16-byte vectors of any payload (bf16
+// rows, or FP8 rows with their scales moved as the side payload by the
+// chunk-0 waves).
+template <int S, int U, int WPB>
+__global__ __launch_bounds__(WPB* kWave) void scatter_kernel(const uint4* __restrict__ x, int64_t t0, int64_t t_end,
+                                                            int nvec, int nchunk, int K,
+                                                            const int32_t* __restrict__ dst_row, int64_t cap,
+                                                            uint4* __restrict__ recv_x, SideRows side) {
     const int lane = lane_id();
     const unsigned wave = __builtin_amdgcn_readfirstlane((unsigned)(threadIdx.x / kWave));
-    const unsigned g = blockIdx.x * (unsigned)kSlotWaves + wave;
-    const unsigned per = (unsigned)(nchunk * K);  // waves per token
+    const unsigned g = blockIdx.x * (unsigned)WPB + wave;
+    const int ng = (K + S - 1) / S;                 // slot groups per chunk
+    const unsigned per = (unsigned)(nchunk * ng);  // waves per token
     const unsigned tt = g / per;
     const int64_t t = t0 + tt;
     if (t >= t_end) return;
     const int j = (int)(g - tt * per);
-    const int c = j / K;
-    const int k = j - c * K;
-    const int v = c * kWave + lane;
-    uint4 buf = make_uint4(0, 0, 0, 0);
-    if (v < nvec) buf = x[t * nvec + v];  // issued with the row load
+    const int c = j / ng;
+    const int k0 = (j - c * ng) * S;
+    uint4 buf[U];  // loads issued with the row load
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int v = (c * U + u) * kWave + lane;
+        buf[u] = make_uint4(0, 0, 0, 0);
+        if (v < nvec) buf[u] = x[t * nvec + v];
+    }
     // lanes 0..K-1 load the token's rows (per-lane addresses keep the load on
-    // the vector path); the wave keeps row k
+    // the vector path); the wave keeps rows k0..k0+S-1
     int dl = -1;
     if (lane < K) {
         const int p = dst_row[t * K + lane];
         dl = (p >= 0 && p < cap) ? p : -1;
     }
-    const int d = __builtin_amdgcn_readlane(dl, k);
-    if (d < 0) return;
-    if (v < nvec) store_nt(recv_x + (int64_t)d * nvec + v, buf);
-    if (side.src && c == 0) copy_side_row(side, t, d, lane);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int k = k0 + s;
+        const int d = __builtin_amdgcn_readlane(dl, k < K ? k : 0);
+        if (k >= K || d < 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = (c * U + u) * kWave + lane;
+            if (v < nvec) store_nt(recv_x + (int64_t)d * nvec + v, buf[u]);
+        }
+        if (side.src && c == 0) copy_side_row(side, t, d, lane);
+    }
 }
 
 // Fused FP8 cast and dispatch apply (bf16 x in, e4m3fn rows and per-block
@@ -694,22 +747,26 @@ static DispatchWs dispatch_ws(const void* workspace, int64_t T, int K, int E) {
     return w;
 }
 
-// Batches with fewer slots use the broadcast kernel (one wave stores its
-// chunk to all K rows), and so does top-k above 8: at top-16 (32768 tokens,
-// hidden 4096) the broadcast kernel measured faster than the row copy, whose
-// 16 waves per chunk then cost more than the shorter waves gain.
+// Batches with fewer slots (decode) use the broadcast kernel: one wave per
+// (token, chunk) stores its chunk to all K rows, so a small grid still
+// moves whole rows per wave.
 constexpr int64_t kRowCopyMinSlots = 16384;
-constexpr int kRowCopyMaxTopk = 8;
+constexpr int kRowCopyMaxTopk = 8;  // above: 2 KB chunks, 4 waves per block
+#ifndef CGD_ROW_SLOTS
+#define CGD_ROW_SLOTS 2
+#endif
+constexpr int kRowSlots = CGD_ROW_SLOTS;  // slots per wave of the row copy
 
+template <int S, int U, int WPB>
 static void launch_row_copy(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* dst_row,
                             int64_t cap, void* recv_x, const SideRows& side) {
-    const int nchunk = (nvec + kWave - 1) / kWave;
-    const int64_t per = (int64_t)nchunk * K;  // waves per token
+    const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
+    const int64_t per = (int64_t)nchunk * ((K + S - 1) / S);  // waves per token
     const int64_t tper = tokens_per_launch(per);
     for (int64_t t0 = 0; t0 < T; t0 += tper) {
         const int64_t nt = std::min<int64_t>(tper, T - t0);
-        const int64_t blocks = (nt * per + kSlotWaves - 1) / kSlotWaves;
-        hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)blocks), dim3(kSlotWaves * kWave), 0, s,
+        const int64_t blocks = (nt * per + WPB - 1) / WPB;
+        hipLaunchKernelGGL((scatter_kernel<S, U, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), 0, s,
                            reinterpret_cast<const uint4*>(x), t0, t0 + nt, nvec, nchunk, K, dst_row, cap,
                            reinterpret_cast<uint4*>(recv_x), side);
     }
@@ -750,9 +807,9 @@ static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int n
     if (T * K < kRowCopyMinSlots)
         launch_bcast_u<1>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
     else if (K > kRowCopyMaxTopk)
-        launch_bcast_u<4>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
+        launch_row_copy<kRowSlots, 2, 4>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
     else
-        launch_row_copy(T, K, s, x, nvec, dst_row, cap, recv_x, side);
+        launch_row_copy<kRowSlots, 1, kSlotWaves>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
 }
 
 static SideRows no_side() { return SideRows{nullptr, 0, 0, 0, 0, nullptr}; }
@@ -780,49 +837,48 @@ static int device_cus() {
 // finalize_kernel after it. A one-tile batch with many spare rows (a large
 // fixed capacity or alignment) takes the FUSED form without rows to move:
 // every block plans the tile in LDS and fills a share of the spare rows.
+// px (optional, pbytes of x): a plan of several tiles followed by a row copy
+// of x adds kPrefetchBlocks blocks that pull x toward the caches meanwhile.
 constexpr int64_t kSpareRowsPerBlock = 2048;
 static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, int64_t cap,
                               int32_t* expert_offset, int32_t* nrecv, int32_t* dst_row, int32_t* recv_src_idx,
                               int32_t* packed_count, int32_t* stats, const DispatchWs& w, hipStream_t stream,
-                              const LayoutOut* layout = nullptr) {
+                              const LayoutOut* layout = nullptr, const void* px = nullptr, int64_t pbytes = 0) {
     int ebits = 0;
     while ((1 << ebits) < E) ++ebits;
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
-    const dim3 grid(ntiles), block(kRankTile);
+    const dim3 block(kRankTile);
     const size_t lds = rank_lds_bytes(E, K);
     const TileOut to{dst_row, recv_src_idx, cap, nullptr, 0, 1, nullptr};  // no rows to move
+    const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
+    const LayoutOut& lo = layout ? *layout : none;
     const int64_t spare = cap - std::min<int64_t>(cap, std::max<int64_t>(T, 0) * K);
     const int64_t fill_blocks = std::min<int64_t>(spare / kSpareRowsPerBlock, device_cus());
+    const uint4* pv = reinterpret_cast<const uint4*>(px);
+    const int64_t pvecs = px ? pbytes / 16 : 0;
+#define CGD_RANK(RW, LAYOUT, FUSED, GRID, PV, PN)                                                                       \
+    hipLaunchKernelGGL((rank_kernel<RW, LAYOUT, FUSED>), GRID, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap, \
+                       w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, lo, to,  \
+                       ntiles, PV, PN)
     if (ntiles == 1 && fill_blocks > 1) {
-        const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
         const dim3 fgrid((unsigned)fill_blocks);
         if (!layout)
-            hipLaunchKernelGGL((rank_kernel<1, false, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
-                               seg_cap, w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats,
-                               w.ticket, none, to);
+            CGD_RANK(1, false, true, fgrid, nullptr, 0);
         else if (layout->R <= 64)
-            hipLaunchKernelGGL((rank_kernel<1, true, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
-                               seg_cap, w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats,
-                               w.ticket, *layout, to);
+            CGD_RANK(1, true, true, fgrid, nullptr, 0);
         else
-            hipLaunchKernelGGL((rank_kernel<6, true, true>), fgrid, block, lds, stream, topk_idx, T, K, E, ebits, A,
-                               seg_cap, w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats,
-                               w.ticket, *layout, to);
+            CGD_RANK(6, true, true, fgrid, nullptr, 0);
         return hipGetLastError();
     }
-    if (!layout) {
-        const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
-        hipLaunchKernelGGL((rank_kernel<1, false>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, none, to);
-    } else if (layout->R <= 64) {
-        hipLaunchKernelGGL((rank_kernel<1, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, *layout,
-                           to);
-    } else {
-        hipLaunchKernelGGL((rank_kernel<6, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap,
-                           w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, *layout,
-                           to);
-    }
+    const int extra = (ntiles > 1 && pvecs > 0) ? kPrefetchBlocks : 0;
+    const dim3 grid(ntiles + extra);
+    if (!layout)
+        CGD_RANK(1, false, false, grid, pv, pvecs);
+    else if (layout->R <= 64)
+        CGD_RANK(1, true, false, grid, pv, pvecs);
+    else
+        CGD_RANK(6, true, false, grid, pv, pvecs);
+#undef CGD_RANK
     if (ntiles > 1) {
         // a thread per slot (grid capped, the kernel strides), and at least
         // kFillThreads threads for the fill
@@ -837,18 +893,19 @@ static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, 
 
 hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
                                   int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, int32_t* nrecv,
-                                  int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream) {
+                                  int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream,
+                                  const void* x, int64_t x_bytes) {
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
     const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
     return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, nrecv, dst_row, recv_src_idx, nullptr, nullptr, w,
-                       stream, &lo);
+                       stream, &lo, x, x_bytes);
 }
 
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int64_t cap,
                                 int32_t* expert_offset, int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row,
-                                void* workspace, hipStream_t stream) {
+                                void* workspace, hipStream_t stream, const void* x, int64_t x_bytes) {
     return launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, nrecv, dst_row, recv_src_idx, nullptr, nullptr,
-                       dispatch_ws(workspace, T, K, E), stream);
+                       dispatch_ws(workspace, T, K, E), stream, nullptr, x, x_bytes);
 }
 
 template <int U, int FMT>
@@ -939,7 +996,8 @@ static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E,
     const size_t lds = rank_lds_bytes(E, K);
 #define CGD_FUSED(RW, LAYOUT, LO)                                                                                   \
     hipLaunchKernelGGL((rank_kernel<RW, LAYOUT, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap, \
-                       w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, LO, fc)
+                       w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, LO, fc, \
+                       1, nullptr, 0)
     if (!layout)
         CGD_FUSED(1, false, none);
     else if (layout->R <= 64)
@@ -980,7 +1038,7 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
         return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, cap, w.packed_offset, nullptr,
                             recv_src_info, dst_row, packed_count, stats, w, stream);
     hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, cap, w.packed_offset, nullptr, dst_row,
-                                 recv_src_info, packed_count, stats, w, stream);
+                                 recv_src_info, packed_count, stats, w, stream, nullptr, x, T * (int64_t)H * 2);
     if (err != hipSuccess) return err;
     if (fmt < 0)
         launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side());

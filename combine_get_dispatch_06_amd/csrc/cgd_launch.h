@@ -62,15 +62,18 @@ hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int
                                          int32_t* nrecv, void* workspace, hipStream_t stream);
 
 // The dispatch plan: the handle (expert_offset, recv_src_idx, dst_row) from
-// the routing alone, and (nrecv != nullptr) the aligned segment sizes.
+// the routing alone, and (nrecv != nullptr) the aligned segment sizes. x
+// (optional, x_bytes): the rows a row copy will read next, pulled toward the
+// caches while the plan runs.
 hipError_t launch_dispatch_plan(const int64_t* topk_idx, int64_t T, int K, int E, int A, int64_t cap,
                                 int32_t* expert_offset, int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row,
-                                void* workspace, hipStream_t stream);
+                                void* workspace, hipStream_t stream, const void* x = nullptr, int64_t x_bytes = 0);
 
 // get_dispatch_layout and the dispatch plan from one pass over the routing.
 hipError_t launch_layout_and_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
                                   int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset, int32_t* nrecv,
-                                  int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream);
+                                  int32_t* recv_src_idx, int32_t* dst_row, void* workspace, hipStream_t stream,
+                                  const void* x = nullptr, int64_t x_bytes = 0);
 
 // Packed fixed-capacity layout: plan + apply; fmt < 0 moves bf16 rows, else
 // casts to FP8 with that scale format.
