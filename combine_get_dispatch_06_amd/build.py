@@ -25,6 +25,19 @@ HIPCC_FLAGS = [
 ]
 
 
+# A second launch geometry for the same kernels (waves per block, vectors per
+# lane, slots per wave, chunk widths, no prefetch blocks): a library built
+# with it must produce the same bytes as the default one, which a GPU test
+# checks. It is built beside libcgd.so by the package's build step.
+GEOMETRY_LIB = os.path.join(PKG, "libcgd_geometry.so")
+GEOMETRY_FLAGS = [
+    "-DCGD_COMBINE_WAVES=2", "-DCGD_COMBINE_U=2", "-DCGD_COMBINE_LDS_CAP=16384",
+    "-DCGD_PREFETCH_BLOCKS=0", "-DCGD_ROW_SLOTS=1",
+    "-DCGD_CAST_CPL=8", "-DCGD_SCATTER_CAST_U=1",
+    "-DCGD_NORMAL_COMBINE_U=1", "-DCGD_NORMAL_COMBINE_WAVES=2", "-DCGD_NORMAL_GATHER=4", "-DCGD_NORMAL_SCATTER_U=2",
+]
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -46,5 +59,10 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str | None
     return out
 
 
+def build_geometry_variant(verbose: bool = False) -> str:
+    return build(verbose=verbose, extra=GEOMETRY_FLAGS, out=GEOMETRY_LIB)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_geometry_variant(verbose=True))

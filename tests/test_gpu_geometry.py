@@ -1,0 +1,116 @@
+"""Launch geometry changes no byte: libcgd built with a second set of launch
+parameters (libcgd_geometry.so: waves per block, vectors per lane, slots per
+row-copy wave, FP8 chunk widths, no prefetch blocks; built beside libcgd.so
+by the build step) must give every output of every data path bit for bit as
+the default build does, on the prefill workload and on a ragged top-16 edge
+case with unselected slots and alignment 16. Receive buffers start from the
+same sentinel fill in both runs, so rows that must stay untouched are
+compared too."""
+import contextlib
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import combine_get_dispatch_06_amd as cgd
+from combine_get_dispatch_06_amd import build as hip_build
+import synth
+from gpu_util import DEV, dev_bf16, dev_f32, dev_i64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@contextlib.contextmanager
+def _library(path):
+    """The binding's calls go to the library at `path` inside the block."""
+    assert os.path.exists(path), f"{path} is missing: run the build step (__graft_entry__.build())"
+    saved = cgd.load()
+    cgd._lib = cgd.configure(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        torch.cuda.synchronize()
+        cgd._lib = saved
+
+
+def _sentinel(shape, dtype):
+    """A tensor of `shape` and `dtype` whose bytes are all 0xA5."""
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    t.view(torch.uint8).fill_(0xA5)
+    return t
+
+
+def _run_all(w, idx_np, wts_np, x_np, y_np, align):
+    """Every data path on one input; returns host byte arrays by name."""
+    T, K, E, R, H = w.T, w.K, w.E, w.R, w.H
+    idx, wts, x, y = dev_i64(idx_np), dev_f32(wts_np), dev_bf16(x_np), dev_bf16(y_np)
+    out = {}
+    cap = cgd.dispatch_capacity(T, K, E, align)
+    recv = _sentinel((cap, H), torch.bfloat16)
+    (ntpr, _, ntpe, itr, _), recv, nre, h = cgd.layout_and_dispatch(x, idx, E, R, expert_alignment=align, recv_x=recv)
+    out.update(ntpr=ntpr, ntpe=ntpe, itr=itr, off=h.expert_offset, nre=nre, src=h.recv_src_idx, dst=h.dst_row,
+               recv=recv)
+    recv2 = _sentinel((cap, H), torch.bfloat16)
+    cgd.dispatch(x, handle=h, recv_x=recv2)
+    out["recv_cached"] = recv2
+    out["combined"] = cgd.combine(y[:cap], h, wts)
+    # FP8: cast on dispatch, tuple dispatch, cast back
+    for fmt in (cgd.SCALE_F32, cgd.SCALE_UE8M0):
+        q = _sentinel((cap, H), torch.float8_e4m3fn)
+        sc = _sentinel((cap, H // 128), torch.uint8 if fmt == cgd.SCALE_UE8M0 else torch.float32)
+        (q, sc), _, _ = cgd.dispatch(x, handle=h, recv_x=(q, sc), cast_fp8=fmt)
+        out[f"cast{fmt}_q"], out[f"cast{fmt}_s"] = q, sc
+        xq = cgd.per_token_cast_to_fp8(x, fmt)
+        out[f"xq{fmt}"] = xq[0]
+        out[f"xs{fmt}"] = xq[1]
+        out[f"back{fmt}"] = cgd.per_token_cast_back(xq)
+    # rank-granular path with biases and weights
+    (_, _, _, itr2, _), plan = cgd.layout_and_normal_dispatch_plan(idx, E, R, expert_alignment=align)
+    ncap = cgd.normal_capacity(T, K, R)
+    nrecv = _sentinel((ncap, H), torch.bfloat16)
+    nrecv, ridx, rw, nnre, nh = cgd.normal_dispatch_apply(x, plan, idx, wts, recv_x=nrecv)
+    b0, b1 = x, dev_bf16(y_np[:T])
+    ncomb, ncw = cgd.normal_combine(y[:ncap], nh, rw, bias=(b0, b1))
+    out.update(n_off=nh.rank_offset, n_send=nh.send_row, n_src=nh.recv_src_idx, n_ridx=ridx, n_rw=rw, n_nre=nnre,
+               n_recv=nrecv, n_comb=ncomb, n_cw=ncw)
+    # packed layout, bf16 and FP8
+    pcap = 64
+    precv = _sentinel((E, pcap, H), torch.bfloat16)
+    precv, cnt, ph = cgd.low_latency_dispatch(x, idx, E, R, expert_capacity=pcap, out=precv)
+    out.update(p_recv=precv, p_cnt=cnt, p_info=ph.recv_src_info, p_dst=ph.dst_row,
+               p_comb=cgd.low_latency_combine(y[:E * pcap].view(E, pcap, H), wts, ph))
+    pq = _sentinel((E * pcap, H), torch.float8_e4m3fn)
+    ps = _sentinel((E * pcap, H // 128), torch.float32)
+    (pq, ps), _, _ = cgd.low_latency_dispatch(x, idx, E, R, expert_capacity=pcap, use_fp8=True, out=(pq, ps))
+    out.update(p_q=pq, p_s=ps)
+    torch.cuda.synchronize()
+    return {k: v.contiguous().view(torch.uint8).cpu().numpy() if v.dtype != torch.bool
+            else v.cpu().numpy() for k, v in out.items()}
+
+
+def _cases():
+    pre = synth.WORKLOADS["prefill"]
+    edge = synth.WORKLOADS["stress"].replace(name="stress", T=777)
+    for w, align, drop in ((pre, 1, 0.0), (edge, 16, 0.2)):
+        idx = synth.make_topk_idx(w, seed=5)[:w.T].copy()
+        if drop:
+            rng = np.random.default_rng(5)
+            idx[rng.random(idx.shape) < drop] = -1
+        yield w, idx, synth.make_weights(w, seed=5)[:w.T], synth.make_x(w, seed=5), align
+
+
+@pytest.mark.parametrize("case", [0, 1], ids=["prefill", "top16-ragged"])
+def test_second_launch_geometry_gives_the_same_bytes(case):
+    w, idx, wts, x, align = list(_cases())[case]
+    rows = max(cgd.dispatch_capacity(w.T, w.K, w.E, align), cgd.normal_capacity(w.T, w.K, w.R), w.E * 64)
+    y = synth.make_expert_out(w, rows, seed=5)
+    say(f"launch geometry: {w.name} T={w.T} K={w.K} align={align}")
+    a = _run_all(w, idx, wts, x, y, align)
+    with _library(hip_build.GEOMETRY_LIB):
+        b = _run_all(w, idx, wts, x, y, align)
+    assert a.keys() == b.keys()
+    for k in a:
+        assert a[k].shape == b[k].shape, k
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
