@@ -49,7 +49,7 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
            "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_",
            "layout_and_normal_dispatch_plan", "layout_and_dispatch", "normal_workspace_bytes",
-           "layout_and_normal_workspace_bytes", "empty_"]
+           "layout_and_normal_workspace_bytes", "empty_", "layout_and_dispatch_noalloc"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _BUILT_LIB = os.path.join(_PKG, "libcgd.so")
@@ -112,6 +112,9 @@ def configure(lib):
     lib.cgd_layout_and_dispatch.restype = i32
     lib.cgd_layout_and_dispatch.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp,
                                             vp, sz, vp]
+    lib.cgd_layout_and_dispatch_noalloc.restype = i32
+    lib.cgd_layout_and_dispatch_noalloc.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp, vp,
+                                                    vp, vp, vp]
     lib.cgd_layout_and_dispatch_plan.restype = i32
     lib.cgd_layout_and_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  sz, vp]
@@ -605,6 +608,43 @@ def layout_and_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: in
                                            _ptr(nre), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
     h = DispatchHandle(off, src, dst, nre, num_experts, num_ranks, expert_alignment, cap)
     return (ntpr, None, ntpe, itr, None), recv_x, nre, h
+
+
+def layout_and_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                                expert_alignment: int = 1, *, recv_x: torch.Tensor, num_tokens_per_rank: torch.Tensor,
+                                num_tokens_per_expert: torch.Tensor, is_token_in_rank: torch.Tensor,
+                                expert_offset: torch.Tensor, num_recv_tokens_per_expert: torch.Tensor,
+                                recv_src_idx: torch.Tensor, dst_row: torch.Tensor) -> None:
+    """layout_and_dispatch into the caller's output tensors, with libcgd's
+    static scratch as the workspace: nothing is allocated, here or in the
+    library (for graph capture and loops that must not allocate). Calls that
+    overlap on one GPU share that scratch and race; workspaces above 8 MiB are
+    refused (CgdError with the workspace status)."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    dev = x.device
+    cap = recv_x.shape[0] if isinstance(recv_x, torch.Tensor) else -1
+    want = (("recv_x", recv_x, torch.bfloat16, (cap, H)), ("topk_idx", topk_idx, torch.int64, (T, K)),
+            ("num_tokens_per_rank", num_tokens_per_rank, torch.int32, (num_ranks,)),
+            ("num_tokens_per_expert", num_tokens_per_expert, torch.int32, (num_experts,)),
+            ("is_token_in_rank", is_token_in_rank, torch.bool, (T, num_ranks)),
+            ("expert_offset", expert_offset, torch.int32, (num_experts + 1,)),
+            ("num_recv_tokens_per_expert", num_recv_tokens_per_expert, torch.int32, (num_experts,)),
+            ("recv_src_idx", recv_src_idx, torch.int32, (cap,)), ("dst_row", dst_row, torch.int32, (T, K)))
+    for name, t, dtype, shape in want:
+        _dev_tensor(t, name, dtype, len(shape))
+        if tuple(t.shape) != shape or t.device != dev:
+            raise ValueError(f"{name} must be {list(shape)} on x's device (got {list(t.shape)} on {t.device})")
+    with torch.cuda.device(dev):
+        _check("cgd_layout_and_dispatch_noalloc",
+               lib.cgd_layout_and_dispatch_noalloc(_ptr(x), T, H, _ptr(topk_idx), K, num_experts, num_ranks,
+                                                   expert_alignment, _ptr(recv_x), cap, _ptr(num_tokens_per_rank),
+                                                   _ptr(num_tokens_per_expert), _ptr(is_token_in_rank),
+                                                   _ptr(expert_offset), _ptr(num_recv_tokens_per_expert),
+                                                   _ptr(recv_src_idx), _ptr(dst_row), _stream(dev)))
 
 
 def dispatch_apply(x, plan: DispatchPlan, recv_x=None, cast_fp8: int | None = None):

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "cgd_launch.h"
@@ -127,10 +128,10 @@ int cgd_get_dispatch_layout(const int64_t* topk_idx, int64_t num_tokens, int num
     return CGD_OK;
 }
 
-// Checks shared by the dispatch entry points.
-static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
+// Checks shared by the dispatch entry points (all but the workspace).
+static int check_plan_core(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
                            const int32_t* expert_offset, const int32_t* nrecv, const int32_t* recv_src_idx,
-                           const int32_t* dst_row, const void* workspace, size_t workspace_bytes) {
+                           const int32_t* dst_row) {
     int rc = check_routing_sizes(T, K, E, R);
     if (rc) return rc;
     if (A < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
@@ -145,11 +146,23 @@ static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int
     if (!aligned(topk_idx, 8) || !aligned(expert_offset, 4) || !aligned(nrecv, 4) || !aligned(recv_src_idx, 4) ||
         !aligned(dst_row, 4))
         return fail(CGD_ERR_INVALID_ARG, "misaligned index pointer");
+    return CGD_OK;
+}
+
+static int check_dispatch_workspace(int64_t T, int K, int E, int R, const void* workspace, size_t workspace_bytes) {
     const size_t need = cgd::dispatch_workspace_bytes(T, K, E, R);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(CGD_ERR_WORKSPACE, "dispatch workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                     workspace_bytes);
     return CGD_OK;
+}
+
+static int check_plan_args(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A, int64_t cap,
+                           const int32_t* expert_offset, const int32_t* nrecv, const int32_t* recv_src_idx,
+                           const int32_t* dst_row, const void* workspace, size_t workspace_bytes) {
+    int rc = check_plan_core(topk_idx, T, K, E, R, A, cap, expert_offset, nrecv, recv_src_idx, dst_row);
+    if (rc) return rc;
+    return check_dispatch_workspace(T, K, E, R, workspace, workspace_bytes);
 }
 
 // Checks of the row payload of a dispatch (x in, recv_x out).
@@ -232,19 +245,25 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
     return CGD_OK;
 }
 
-int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
-                            int num_experts, int num_ranks, int expert_alignment, void* recv_x,
-                            int64_t recv_capacity, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
-                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* num_recv_tokens_per_expert,
-                            int32_t* recv_src_idx, int32_t* dst_row, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
-    int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
-                             expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
-                             workspace_bytes);
+// Checks of cgd_layout_and_dispatch's arguments other than the workspace.
+static int check_layout_and_dispatch(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int R,
+                                     int A, const void* recv_x, int64_t cap, const int32_t* ntpr, const int32_t* ntpe,
+                                     const uint8_t* itr, const int32_t* expert_offset, const int32_t* nrecv,
+                                     const int32_t* recv_src_idx, const int32_t* dst_row) {
+    int rc = check_plan_core(topk_idx, T, K, E, R, A, cap, expert_offset, nrecv, recv_src_idx, dst_row);
     if (rc) return rc;
-    if ((rc = check_rows_args(x, num_tokens, hidden, recv_capacity, recv_x))) return rc;
-    if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
-        return rc;
+    if ((rc = check_rows_args(x, T, H, cap, recv_x))) return rc;
+    return check_layout_outputs(T, ntpr, ntpe, itr);
+}
+
+// cgd_layout_and_dispatch's launches, its arguments checked.
+static int layout_and_dispatch_launches(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                        int num_topk, int num_experts, int num_ranks, int expert_alignment,
+                                        void* recv_x, int64_t recv_capacity, int32_t* num_tokens_per_rank,
+                                        int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                        int32_t* expert_offset, int32_t* num_recv_tokens_per_expert,
+                                        int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                                        hipStream_t stream) {
     hipError_t err;
     if (cgd::dispatch_fuses(num_tokens)) {  // one tile: layout, plan and rows in one launch
         err = cgd::launch_layout_and_dispatch_fused(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks,
@@ -263,6 +282,25 @@ int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const
     err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
     return CGD_OK;
+}
+
+int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                            int num_experts, int num_ranks, int expert_alignment, void* recv_x,
+                            int64_t recv_capacity, int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                            uint8_t* is_token_in_rank, int32_t* expert_offset, int32_t* num_recv_tokens_per_expert,
+                            int32_t* recv_src_idx, int32_t* dst_row, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    int rc = check_layout_and_dispatch(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks,
+                                       expert_alignment, recv_x, recv_capacity, num_tokens_per_rank,
+                                       num_tokens_per_expert, is_token_in_rank, expert_offset,
+                                       num_recv_tokens_per_expert, recv_src_idx, dst_row);
+    if (rc) return rc;
+    if ((rc = check_dispatch_workspace(num_tokens, num_topk, num_experts, num_ranks, workspace, workspace_bytes)))
+        return rc;
+    return layout_and_dispatch_launches(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks,
+                                        expert_alignment, recv_x, recv_capacity, num_tokens_per_rank,
+                                        num_tokens_per_expert, is_token_in_rank, expert_offset,
+                                        num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace, stream);
 }
 
 int cgd_dispatch_cached(const void* x, int64_t num_tokens, int hidden, int num_topk, const int32_t* dst_row,
@@ -709,3 +747,77 @@ int cgd_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// cgd_layout_and_dispatch_noalloc: cgd_layout_and_dispatch with its workspace
+// in a file-scope device array instead of a buffer of the caller's, for
+// callers that cannot allocate. Every GPU the library runs on holds its own
+// copy of the array, at its own address, until the process ends; calls on one
+// GPU share it, so calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = size_t(8) << 20;  // the largest workspace the entry point serves
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // device address of `scratch` per device, once set up
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The words of a dispatch workspace that must be zero before its first use
+// (the plan's ticket, first in the workspace); every call leaves them zero.
+__global__ __launch_bounds__(64) void clear_scratch_ticket(unsigned int* words) { words[threadIdx.x] = 0u; }
+
+// The scratch array's address on the current device. The first call on a
+// device looks it up with that device current and enqueues the clearing of
+// the ticket words on `stream`, before the work of the call that set it up.
+// In host code `scratch` names a host-side stand-in, never the device array:
+// only the looked-up address is passed to kernels.
+static int scratch_address(hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(CGD_ERR_HIP, "device %d is beyond the %d devices the static scratch serves", dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return hip_fail(err, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(CGD_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+        static_assert(cgd::kTicketBytes == 256, "one wave clears the ticket words");
+        hipLaunchKernelGGL(clear_scratch_ticket, dim3(1), dim3(64), 0, stream, static_cast<unsigned int*>(p));
+        err = hipGetLastError();
+        if (err != hipSuccess) return hip_fail(err, "static scratch set-up launch");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CGD_OK;
+}
+
+extern "C" int cgd_layout_and_dispatch_noalloc(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                               int num_topk, int num_experts, int num_ranks, int expert_alignment,
+                                               void* recv_x, int64_t recv_capacity, int32_t* num_tokens_per_rank,
+                                               int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                               int32_t* expert_offset, int32_t* num_recv_tokens_per_expert,
+                                               int32_t* recv_src_idx, int32_t* dst_row, hipStream_t stream) {
+    int rc = check_layout_and_dispatch(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks,
+                                       expert_alignment, recv_x, recv_capacity, num_tokens_per_rank,
+                                       num_tokens_per_expert, is_token_in_rank, expert_offset,
+                                       num_recv_tokens_per_expert, recv_src_idx, dst_row);
+    if (rc) return rc;
+    const size_t need = cgd::dispatch_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks);
+    if (need > kScratchBytes)
+        return fail(CGD_ERR_WORKSPACE,
+                    "these sizes need %zu bytes of workspace; the static scratch of "
+                    "cgd_layout_and_dispatch_noalloc holds %zu (use cgd_layout_and_dispatch with a workspace)",
+                    need, kScratchBytes);
+    void* ws = nullptr;
+    if ((rc = scratch_address(stream, &ws))) return rc;
+    return layout_and_dispatch_launches(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks,
+                                        expert_alignment, recv_x, recv_capacity, num_tokens_per_rank,
+                                        num_tokens_per_expert, is_token_in_rank, expert_offset,
+                                        num_recv_tokens_per_expert, recv_src_idx, dst_row, ws, stream);
+}

@@ -179,6 +179,29 @@ int cgd_layout_and_dispatch(const void* x, int64_t num_tokens, int hidden, const
                             int32_t* recv_src_idx, int32_t* dst_row, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* cgd_layout_and_dispatch for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, outputs and errors without the workspace,
+ * which is a file-scope device array inside the library instead; the call
+ * allocates nothing (no hipMalloc, no library allocation). The caller still
+ * passes every input and output.
+ *   Limit: sizes whose workspace (cgd_dispatch_workspace_bytes) exceeds
+ *   8 MiB are rejected with CGD_ERR_WORKSPACE before anything is enqueued
+ *   (about 1.9 million selected slots, num_tokens * num_topk).
+ *   Each GPU the library runs on holds its own 8 MiB copy of the array until
+ *   the process ends. Every call on a GPU shares that GPU's copy: calls that
+ *   overlap on one GPU (different streams, or graphs replayed concurrently)
+ *   race and must be ordered by the caller. The first call on a device looks
+ *   up the array's address there and enqueues, before its own work, one
+ *   one-wave kernel that clears the words that must start at zero; every
+ *   call leaves them zero again. */
+int cgd_layout_and_dispatch_noalloc(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                    int num_topk, int num_experts, int num_ranks, int expert_alignment, void* recv_x,
+                                    int64_t recv_capacity, int32_t* num_tokens_per_rank,
+                                    int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank, int32_t* expert_offset,
+                                    int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                                    hipStream_t stream);
+
 /* Cached dispatch (Python interface notes, "Dispatch API", handle reuse):
  * copies rows with a dst_row from an earlier cgd_dispatch or
  * cgd_dispatch_plan, skipping the layout work. recv_x[dst_row[t,k]] = x[t]

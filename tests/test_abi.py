@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_cached_cast_fp8", "cgd_dispatch_cached_fp8",
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
-        "cgd_layout_and_dispatch", "cgd_empty",
+        "cgd_layout_and_dispatch", "cgd_empty", "cgd_layout_and_dispatch_noalloc",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan",
     ])
 
@@ -373,3 +373,21 @@ def test_layout_and_dispatch_rejects_bad_arguments():
                                        1 << 20, None) == -1
     assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, None, 0, None) == -3
     assert lib.cgd_last_error()
+
+
+def test_noalloc_dispatch_rejects_bad_arguments_and_oversized_work():
+    lib = cgd.load()
+    f = _vp(FAKE)
+    # x, T, H, idx, K, E, R, A, recv, cap, ntpr, ntpe, itr, off, nre, src, dst
+    assert lib.cgd_layout_and_dispatch_noalloc(f, 64, 128, f, 4, 16, 4, 1, f, 255, f, f, f, f, f, f, f, None) == -2
+    assert lib.cgd_layout_and_dispatch_noalloc(f, 64, 100, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, None) == -1
+    assert lib.cgd_layout_and_dispatch_noalloc(f, 64, 128, f, 4, 16, 3, 1, f, 256, f, f, f, f, f, f, f, None) == -1
+    assert lib.cgd_layout_and_dispatch_noalloc(f, 64, 128, f, 4, 16, 4, 1, f, 256, None, f, f, f, f, f, f,
+                                               None) == -1
+    assert lib.cgd_layout_and_dispatch_noalloc(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, _vp(FAKE + 2), f, f,
+                                               None) == -1
+    # valid arguments whose workspace exceeds the static 8 MiB: refused before any HIP call
+    T, K, E, R = 1 << 20, 4, 64, 8
+    assert lib.cgd_dispatch_workspace_bytes(T, K, E, R) > 8 << 20
+    assert lib.cgd_layout_and_dispatch_noalloc(f, T, 8, f, K, E, R, 1, f, T * K, f, f, f, f, f, f, f, None) == -3
+    assert b"8388608" in lib.cgd_last_error()
