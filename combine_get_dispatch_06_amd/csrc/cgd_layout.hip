@@ -124,22 +124,37 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     if (!last_block_done(ticket)) return;
 
     const int nblk = gridDim.x;
-    for (int i = tid; i < W; i += kLayoutTile) {
-        // loads issued 16 at a time: few round trips however many blocks
-        int s = 0;
+    // each thread sums columns tid and tid + 256 (W <= 512 + 384): the loads
+    // of both, 16 blocks at a time, are in flight together, so a column count
+    // just above the block size costs no second round trip
+    for (int i0 = tid; i0 < W; i0 += 2 * kLayoutTile) {
+        const int i1 = i0 + kLayoutTile;
+        int s0 = 0, s1 = 0;
         for (int b0 = 0; b0 < nblk; b0 += 16) {
-            int v[16];
+            int v0[16], v1[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = (b0 + j < nblk) ? partial[(int64_t)(b0 + j) * W + i] : 0;
+            for (int j = 0; j < 16; ++j) {
+                v0[j] = (b0 + j < nblk) ? partial[(int64_t)(b0 + j) * W + i0] : 0;
+                v1[j] = (b0 + j < nblk && i1 < W) ? partial[(int64_t)(b0 + j) * W + i1] : 0;
+            }
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s += v[j];
+            for (int j = 0; j < 16; ++j) {
+                s0 += v0[j];
+                s1 += v1[j];
+            }
         }
-        if (i < E) {
-            ntpe[i] = s;
-            if (NPLAN && np.nrecv) np.nrecv[i] = (s + np.A - 1) / np.A * np.A;
-        } else {
-            ntpr[i - E] = s;
-            if (NPLAN) s_rank[i - E] = s;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int i = h ? i1 : i0;
+            const int s = h ? s1 : s0;
+            if (i >= W) continue;
+            if (i < E) {
+                ntpe[i] = s;
+                if (NPLAN && np.nrecv) np.nrecv[i] = (s + np.A - 1) / np.A * np.A;
+            } else {
+                ntpr[i - E] = s;
+                if (NPLAN) s_rank[i - E] = s;
+            }
         }
     }
     if (NPLAN) {
