@@ -11,21 +11,27 @@ Inputs rotate: --sets distinct seeded (x, topk_idx, topk_weights) sets
 (seeds seed..seed+sets-1; 295 MB at prefill, more than the 256 MB Infinity
 Cache), step k running set k mod sets, so each step's x was last touched
 several steps earlier and is read from HBM. The headline is the wall time of
---steps such steps, each replayed from a HIP graph captured once per set (the
-serving setting; --timing eager times Python launches instead). The same
-figures with one x reused every step (which stays in the Infinity Cache) are
-reported as warm_x, and with the caches swept by a read-only pass before every
-step as cold_cache.
+--steps such steps replayed from HIP graphs, each graph holding whole
+rotations of the sets and at least 10 consecutive steps (the serving
+setting, where one captured model step holds every layer's calls; --timing
+eager times Python launches instead). The same figures with one x reused
+every step (which stays in the Infinity Cache) are reported as warm_x, and
+with the caches swept by a read-only pass before every step as cold_cache.
 
-Per-kernel durations come from HIP events around each call of
---kernel-samples eager steps (rotating sets), on the stream the kernels run
-on; every time, GB/s and fraction of peak is a median over those samples.
+Per-call durations (kernel_us, and the whole dispatch / combine / apply
+figures derived from them) are device times: 20 back-to-back calls of one
+kind captured in a HIP graph (sets rotating), 20 replays each between two HIP
+events recorded on the stream the kernels run on, i.e. 400 launches per
+figure; every time, GB/s and fraction of peak is a median over the replays.
 dispatch_* time the whole dispatch of the step, plan and rows (the expert and
 rank-granular paths fuse the layout into the plan, so it is counted there
 too); dispatch_apply_* time the row movement alone, i.e. the cached dispatch
-that reuses a handle. layout_us (get_dispatch_layout alone) and
-launch_floor_us (libcgd's empty kernel) are both wall time per call over
-graph replays of 20 back-to-back calls.
+that reuses a handle. The same split from HIP events around each call of
+--kernel-samples eager steps is kept under "eager" (it carries each event's
+own few µs and, for small batches, the host's launch cost); the cold_cache
+leg is timed that way, since its sweep runs between steps. layout_us
+(get_dispatch_layout alone) and launch_floor_us (libcgd's empty kernel) are
+per-call device times as above.
 
 Prints one JSON line with the whole-step token throughput, those figures, the
 roofline entry of the dominant data kernel and the CPU oracle's throughput on
@@ -139,6 +145,12 @@ class _Path:
     def nbytes(self, i: int) -> dict:
         raise NotImplementedError
 
+    def graph_calls(self) -> dict:
+        """label -> fn(i), one call each (on set i) for graph_call_us: the
+        whole dispatch ("dispatch"), the combine ("combine") and the calls of
+        the split step. Runs after check(), whose handles they reuse."""
+        raise NotImplementedError
+
 
 class ExpertPath(_Path):
     """bf16: layout and dispatch in one call (layout_and_dispatch: the layout,
@@ -202,6 +214,28 @@ class ExpertPath(_Path):
         cgd.combine(self.recv_x, h, self.wt[i], out=self.out)
         self._rec(ev, 3)
         self.handles[i] = h
+
+    def _dispatch(self, i):
+        cgd, w = self.cgd, self.w
+        if self.fmt is None:
+            return cgd.layout_and_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_alignment=w.align,
+                                           recv_x=self.recv_x)
+        _, plan = cgd.layout_and_dispatch_plan(self.idx[i], w.E, w.R, expert_alignment=w.align)
+        return cgd.dispatch_apply(self.x[i], plan, recv_x=self.recv_q, cast_fp8=self.fmt)
+
+    def _apply(self, i):
+        # the cached dispatch: the handle's rows alone (dispatch_apply's kernels)
+        if self.fmt is None:
+            return self.cgd.dispatch(self.x[i], handle=self.handles[i], recv_x=self.recv_x)
+        return self.cgd.dispatch(self.x[i], handle=self.handles[i], recv_x=self.recv_q, cast_fp8=self.fmt)
+
+    def graph_calls(self):
+        cgd, w = self.cgd, self.w
+        return {"dispatch": self._dispatch,
+                "layout_and_plan": lambda i: cgd.layout_and_dispatch_plan(self.idx[i], w.E, w.R,
+                                                                          expert_alignment=w.align),
+                "dispatch_apply": self._apply,
+                "combine": lambda i: cgd.combine(self.recv_x, self.handles[i], self.wt[i], out=self.out)}
 
     def check(self, i):
         """combine(dispatch(x)) returns x: exactly for bf16, within the FP8
@@ -272,7 +306,38 @@ class NormalPath(_Path):
         self._rec(ev, 3)
         cgd.normal_combine(self.recv_x, h, rw, out=self.out)
         self._rec(ev, 4)
-        self.last[i] = (h, itr)
+        self.last[i] = (h, itr, rw)
+
+    def _dispatch(self, i):
+        cgd, w = self.cgd, self.w
+        _, plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R, expert_alignment=w.align)
+        x = self.x[i] if self.fmt is None else cgd.per_token_cast_to_fp8(self.x[i], self.fmt)
+        return cgd.normal_dispatch_apply(x, plan, self.idx[i], self.wt[i],
+                                         recv_x=self.recv_x if self.fmt is None else self.recv_q)
+
+    def graph_calls(self):
+        import torch
+        cgd, w = self.cgd, self.w
+        # the apply alone needs a plan per set that no later plan overwrites:
+        # each set's plan gets a workspace of its own (made once, here)
+        nws = cgd.layout_and_normal_workspace_bytes(w.T, w.K, w.E, w.R)
+        plans, xs = {}, {}
+        for i in range(len(self.x)):
+            ws = torch.zeros(nws, dtype=torch.uint8, device=self.dev)
+            plans[i] = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R, expert_alignment=w.align,
+                                                           workspace=ws)[1]
+            xs[i] = self.x[i] if self.fmt is None else cgd.per_token_cast_to_fp8(self.x[i], self.fmt)
+        recv = self.recv_x if self.fmt is None else self.recv_q
+        calls = {"dispatch": self._dispatch,
+                 "layout_and_plan": lambda i: cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R,
+                                                                                  expert_alignment=w.align),
+                 "dispatch_apply": lambda i: cgd.normal_dispatch_apply(xs[i], plans[i], self.idx[i], self.wt[i],
+                                                                       recv_x=recv),
+                 "combine": lambda i: cgd.normal_combine(self.recv_x, self.last[i][0], self.last[i][2],
+                                                         out=self.out)}
+        if self.fmt is not None:
+            calls["cast"] = lambda i: cgd.per_token_cast_to_fp8(self.x[i], self.fmt)
+        return calls
 
     def check(self, i):
         """each token comes back as bf16(x * ranks it was sent to): exactly for
@@ -283,7 +348,7 @@ class NormalPath(_Path):
             self.cgd.per_token_cast_back(self.recv_q, self.fmt, out=self.recv_x)
             self.step(i)
         torch.cuda.synchronize()
-        h, itr = self.last[i]
+        h, itr, _ = self.last[i]
         n = itr.sum(dim=1, dtype=torch.float32).unsqueeze(1)
         want = (self.x[i].float() * n).to(torch.bfloat16)
         if self.fmt is None:
@@ -327,6 +392,7 @@ class PackedPath(_Path):
                            torch.empty((w.E * self.cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32,
                                        device=dev))
         self.count = [None] * len(sets)
+        self.handles = [None] * len(sets)
 
     def step(self, i, ev=None):
         cgd, w = self.cgd, self.w
@@ -343,6 +409,18 @@ class PackedPath(_Path):
         cgd.low_latency_combine(self.recv, self.wt[i], h, out=self.out)
         self._rec(ev, 3)
         self.count[i] = count
+        self.handles[i] = h
+
+    def graph_calls(self):
+        cgd, w = self.cgd, self.w
+        if self.fmt is None:
+            disp = lambda i: cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
+                                                      out=self.recv)
+        else:
+            disp = lambda i: cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
+                                                      use_fp8=True, scale_format=self.fmt, out=self.recv_q)
+        return {"layout": lambda i: cgd.get_dispatch_layout(self.idx[i], w.E, w.R), "dispatch": disp,
+                "combine": lambda i: cgd.low_latency_combine(self.recv, self.wt[i], self.handles[i], out=self.out)}
 
     def check(self, i):
         import torch
@@ -442,33 +520,47 @@ def summarize(path, us, sets_of_sample) -> dict:
     return out
 
 
-def graph_wall(path, order, steps: int, warmup: int) -> float:
-    """Capture one step per distinct set of `order` in a HIP graph on a side
-    stream (after untimed steps on that stream, so every workspace exists
-    before capture), then time `steps` replays, step k replaying the graph of
-    set order[k mod len(order)]; returns seconds."""
+STEPS_PER_GRAPH = 10  # at least this many consecutive steps per captured graph
+
+
+def _capture(fn, seq, s):
+    """fn(i) for each i of seq, captured in one HIP graph on stream s."""
     import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in seq:
+            fn(i)
+    return g
+
+
+def graph_wall(path, order, steps: int, warmup: int) -> float:
+    """Wall seconds of `steps` steps, step k on set order[k mod len(order)],
+    replayed from HIP graphs that each hold a whole number of rotations of
+    `order` and at least STEPS_PER_GRAPH steps (a captured model step holds
+    every layer's calls likewise, so one replay's launch cost is shared by
+    many calls), plus one graph for the remainder. Captured on a side stream
+    after untimed steps on it, so every workspace exists before capture."""
+    import torch
+    L = len(order)
+    per = L * -(-STEPS_PER_GRAPH // L)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    distinct = sorted(set(order))
     with torch.cuda.stream(s):
         for _ in range(2):
-            for i in distinct:
+            for i in sorted(set(order)):
                 path.step(i)
     s.synchronize()
-    graphs = {}
-    for i in distinct:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            path.step(i)
-        graphs[i] = g
-    seq = [graphs[order[k % len(order)]] for k in range(max(steps, warmup))]
-    for k in range(warmup):
-        seq[k].replay()
+    full = _capture(path.step, [order[k % L] for k in range(per)], s)
+    rem = steps % per
+    tail = _capture(path.step, [order[k % L] for k in range(rem)], s) if rem else None
+    for _ in range(-(-warmup // per)):
+        full.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(steps):
-        seq[k].replay()
+    for _ in range(steps // per):
+        full.replay()
+    if tail is not None:
+        tail.replay()
     torch.cuda.synchronize()
     return time.perf_counter() - t0
 
@@ -487,38 +579,73 @@ def timed_wall(args, path, order):
     """Wall seconds of args.steps steps and how they were launched."""
     if args.timing == "graph":
         try:
-            return graph_wall(path, order, args.steps, args.warmup), "HIP graph replays"
+            return graph_wall(path, order, args.steps, args.warmup), \
+                f"HIP graph replays, >= {STEPS_PER_GRAPH} steps per graph"
         except Exception as exc:  # capture unsupported here: time eager launches
             print(f"graph capture failed ({exc}); timing eager launches", file=sys.stderr)
     return eager_wall(path, order, args.steps), "eager launches"
 
 
-def per_call_us(fn, calls: int = 20, replays: int = 20) -> dict:
-    """`calls` back-to-back calls of fn captured in a HIP graph, replayed
-    `replays` times: the wall time per call (a launch each, as a serving loop
-    sees it). Eager event pairs would time the host's Python launch cost
-    instead: the GPU finishes such a call before the next one is submitted."""
+GRAPH_CALLS = 20    # back-to-back calls per captured graph
+GRAPH_REPLAYS = 20  # timed replays: GRAPH_CALLS * GRAPH_REPLAYS launches per figure
+
+
+def graph_call_us(fn, order=(0,), calls: int = GRAPH_CALLS, replays: int = GRAPH_REPLAYS) -> dict:
+    """Device time per call of fn(i), i cycling through `order`: `calls`
+    back-to-back calls captured in one HIP graph on a side stream (after
+    untimed calls there, so every workspace exists before capture), replayed
+    `replays` times, each replay between two HIP events recorded on that
+    stream; a replay's interval / calls is one sample. Eager event pairs
+    around a small call time the host's Python launch cost instead (the GPU
+    finishes such a call before the next is submitted), and each recorded
+    event adds a few µs of its own."""
     import numpy as np
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
+    seq = [order[k % len(order)] for k in range(calls)]
     with torch.cuda.stream(s):
-        for _ in range(3):
-            fn()
+        for _ in range(2):
+            for i in sorted(set(seq)):
+                fn(i)
     s.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        for _ in range(calls):
-            fn()
-    g.replay()
-    torch.cuda.synchronize()
-    per = []
-    for _ in range(replays):
-        t0 = time.perf_counter()
+    g = _capture(fn, seq, s)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    with torch.cuda.stream(s):
         g.replay()
-        torch.cuda.synchronize()
-        per.append((time.perf_counter() - t0) / calls * 1e6)
-    return {**stats(np.array(per)), "how": f"{calls} calls per HIP graph replay, wall time per call"}
+        for e0, e1 in ev:
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+    torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) * 1e3 / calls for e0, e1 in ev])
+    return {**stats(per), "launches": calls * replays}
+
+
+def graph_summary(path, order) -> dict:
+    """Per-call device times of the path's calls (graph_call_us, sets cycling
+    through `order`), the whole dispatch and the combine with their GB/s and
+    fractions of the HBM peak (bytes averaged over the sets of `order`)."""
+    import numpy as np
+    per = {lab: graph_call_us(fn, order) for lab, fn in path.graph_calls().items()}
+    nb = [path.nbytes(int(i)) for i in order]
+
+    def rate(key, t):
+        return float(np.mean([b[key] for b in nb])) / (t * 1e-6) / 1e9
+
+    disp, comb = per["dispatch"]["median"], per["combine"]["median"]
+    out = {"kernel_us": per, "dispatch_us": disp, "combine_us": comb,
+           "dispatch_GBps": rate("dispatch", disp), "combine_GBps": rate("combine", comb),
+           "dispatch_tokens_per_s": path.w.T / (disp * 1e-6), "combine_tokens_per_s": path.w.T / (comb * 1e-6)}
+    out["dispatch_frac_of_peak"] = out["dispatch_GBps"] / HBM_PEAK_GBPS
+    out["combine_frac_of_peak"] = out["combine_GBps"] / HBM_PEAK_GBPS
+    if path.apply_label:
+        a = per[path.apply_label]["median"]
+        out.update(dispatch_apply_us=a, dispatch_apply_GBps=rate("apply", a),
+                   dispatch_apply_frac_of_peak=rate("apply", a) / HBM_PEAK_GBPS)
+    if "layout_and_plan" in per:
+        out["layout_and_plan_us"] = per["layout_and_plan"]["median"]
+    return out
 
 
 def copy_ceilings(dev) -> dict:
@@ -679,11 +806,13 @@ def main() -> int:
 
     samples = max(args.kernel_samples, 1)
     us, which = kernel_samples(path, [rotation[k % nsets] for k in range(samples)])
-    rotated = summarize(path, us, which)
+    eager = summarize(path, us, which)
+    rotated = graph_summary(path, rotation)
     wall, timing = timed_wall(args, path, rotation)
 
     us0, which0 = kernel_samples(path, [0] * samples)
-    warm = summarize(path, us0, which0)
+    warm = graph_summary(path, [0])
+    warm["eager"] = summarize(path, us0, which0)
     wall0, _ = timed_wall(args, path, [0])
     warm.update(ms_per_step=wall0 / args.steps * 1e3, tokens_per_s=w.T * args.steps / wall0)
 
@@ -700,8 +829,8 @@ def main() -> int:
         cold["flush"] = "read-only sweep of 512 MiB (a reduction) before every step, outside the events"
         del sweep
 
-    layout_alone = per_call_us(lambda: cgd.get_dispatch_layout(path.idx[0], w.E, w.R))
-    floor = per_call_us(lambda: cgd.empty_(dev))
+    layout_alone = graph_call_us(lambda i: cgd.get_dispatch_layout(path.idx[i], w.E, w.R), rotation)
+    floor = graph_call_us(lambda i: cgd.empty_(dev))
     ctx = copy_ceilings(dev)
     tkey = w.name + ("" if args.path == "expert" else ":" + args.path) + (f":fp8-{args.fp8}" if fmt is not None else "")
     roof = roofline(path, rotated, args.traffic_json, tkey)
@@ -731,6 +860,10 @@ def main() -> int:
         "launch_floor_us": floor,
         **{k: v for k, v in rotated.items() if k != "kernel_us"},
         "kernel_us": rotated["kernel_us"],
+        "kernel_us_how": f"device time per call: {GRAPH_CALLS} back-to-back calls per HIP graph, "
+                         f"{GRAPH_REPLAYS} replays between HIP events on the launch stream, sets rotating",
+        "eager": {**eager, "how": f"HIP events around each call of {samples} eager steps, sets rotating "
+                                  "(host-bound for small batches)"},
         "kernel_samples": samples,
         "first_step_ms": first_ms,
         "warm_x": {**warm, "how": "one input set (seed %d) every step: x stays in the Infinity Cache" % args.seed},
