@@ -375,8 +375,9 @@ static int check_normal_plan_args(const uint8_t* itr, int64_t T, int R, const in
 }
 
 size_t cgd_layout_and_normal_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks) {
-    const size_t lw = cgd_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks);
-    return lw == 0 ? 0 : cgd::normal_workspace_bytes(num_tokens, num_ranks) + lw;
+    if (cgd_layout_workspace_bytes(num_tokens, num_topk, num_experts, num_ranks) == 0) return 0;  // invalid sizes
+    return cgd::normal_workspace_bytes(num_tokens, num_ranks) +
+           cgd::layout_partial_bytes(num_tokens, num_experts, num_ranks);
 }
 
 int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,

@@ -27,7 +27,8 @@ inline int64_t tokens_per_launch(int64_t waves_per_token) {
 }
 
 int64_t layout_blocks(int64_t T);
-size_t layout_workspace_bytes(int64_t T, int E, int R);
+size_t layout_workspace_bytes(int64_t T, int E, int R);  // get_dispatch_layout alone
+size_t layout_partial_bytes(int64_t T, int E, int R);    // per-block partials of the layout + normal plan
 size_t dispatch_workspace_bytes(int64_t T, int K, int E, int R);
 
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R, int32_t* ntpr, int32_t* ntpe,

@@ -5,7 +5,7 @@
 // is_token_in_rank matrix. Rank r owns experts [r*L, (r+1)*L) (DeepEP legacy
 // test analysis page, low-latency per-expert check).
 //
-// One launch. Each block takes 256 tokens, one per thread:
+// One launch. Each block takes a tile of tokens, one per thread:
 //   1. the tile's topk_idx is staged in LDS with coalesced loads;
 //   2. each thread adds its slots to an LDS expert histogram and builds the
 //      bitmask of ranks its token touches;
@@ -13,11 +13,16 @@
 //      of the lanes whose token holds it;
 //   4. the tile's is_token_in_rank rows (a contiguous byte range) are written
 //      with 16-byte stores;
-//   5. blocks publish their partial counts; the last block to finish sums
-//      them into the outputs (no pre-zeroed outputs, no second launch).
+//   5. the tiles' counts are combined across blocks without pre-zeroed
+//      outputs or a second launch: get_dispatch_layout alone
+//      (layout_acc_kernel, 512-token tiles) adds them to counted 64-bit
+//      accumulators, and the block that adds last to a word writes it; the
+//      rank-granular plan form (layout_kernel, 256-token tiles, which also
+//      needs per-tile prefixes) publishes per-block partials that the last
+//      block to finish sums.
 // The NPU implementation on the API page ("Internal Logic", "Multi-Core
 // Strategy") also splits tokens over cores and aggregates partial results
-// across cores; here the aggregation is a last-block-done reduction.
+// across cores.
 //
 // NPLAN form: the rank-granular dispatch plan from the same tile (the plan
 // needs only is_token_in_rank, which the tile has in registers): the
@@ -180,26 +185,114 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     reset_ticket(ticket);
 }
 
+// get_dispatch_layout alone: the same tile work in blocks of TILE tokens,
+// without a last-block handshake. Every block adds, for each expert and rank,
+// (1 << 32) + its count to a 64-bit accumulator in the workspace with one
+// device-scope atomic that returns the previous value: the high word counts
+// the blocks that have added, the low word sums their counts (a total below
+// 2^32, so no carry reaches the high word). The block whose add is the last
+// one of a word (it finds gridDim.x - 1 blocks before it) holds that word's
+// total: it writes the output and zeroes the word for the next call. So the
+// counts are final one atomic round trip after the tile work, with no
+// release / ticket / acquire sequence and no second pass over partials. The
+// is_token_in_rank rows need no ordering with other blocks.
+template <int RW, int TILE>
+__global__ __launch_bounds__(TILE) void layout_acc_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K,
+                                                          int E, int R, int L, int32_t* __restrict__ ntpr,
+                                                          int32_t* __restrict__ ntpe, uint8_t* __restrict__ itr,
+                                                          unsigned long long* __restrict__ acc) {
+    __shared__ int32_t s_idx[TILE * kMaxTopk];
+    __shared__ uint64_t s_mask[TILE * RW];
+    __shared__ int32_t s_hist[kMaxExperts];
+    __shared__ int32_t s_rank[kMaxRanks];
+    __shared__ int16_t s_rank_of[kMaxExperts];
+
+    const int tid = threadIdx.x;
+    const int lshift = (L & (L - 1)) == 0 ? __builtin_ctz(L) : -1;
+    const int64_t t0 = (int64_t)blockIdx.x * TILE;
+    const int nt = (int)max<int64_t>(0, min<int64_t>(TILE, T - t0));
+
+    for (int i = tid; i < E; i += TILE) {
+        s_hist[i] = 0;
+        s_rank_of[i] = (int16_t)(i / L);
+    }
+    for (int i = tid; i < R; i += TILE) s_rank[i] = 0;
+    stage_routing<kMaxTopk, TILE>(topk_idx + t0 * K, nt * K, E, s_idx);
+    __syncthreads();
+
+    int e[kMaxTopk];
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) e[k] = (tid < nt && k < K) ? s_idx[tid * K + k] : -1;
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k)
+        if (e[k] >= 0) atomicAdd(&s_hist[e[k]], 1);
+    uint64_t m[RW];
+    token_rank_mask<RW>(e, s_rank_of, lshift, m);
+    count_rank_tokens<RW>(m, R, s_rank, s_mask);
+    __syncthreads();
+    uint8_t* rows = itr + t0 * R;  // t0*R is a multiple of 16 when TILE is
+
+    if (gridDim.x == 1) {
+        for (int i = tid; i < E; i += TILE) ntpe[i] = s_hist[i];
+        for (int i = tid; i < R; i += TILE) ntpr[i] = s_rank[i];
+        store_token_in_rank<RW, TILE>(m, s_mask, nt, R, rows);
+        return;
+    }
+    constexpr int kPer = (kMaxExperts + kMaxRanks + TILE - 1) / TILE;  // accumulator words per thread
+    const unsigned long long one = 1ull << 32;
+    unsigned long long prev[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {  // all adds in flight together
+        const int i = tid + j * TILE;
+        prev[j] = 0;
+        if (i < E + R) {
+            const int c = i < E ? s_hist[i] : s_rank[i - E];
+            prev[j] = __hip_atomic_fetch_add(acc + i, one + (unsigned)c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    store_token_in_rank<RW, TILE>(m, s_mask, nt, R, rows);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * TILE;
+        if (i >= E + R || (unsigned)(prev[j] >> 32) != gridDim.x - 1) continue;
+        const int total = (int)(unsigned)prev[j] + (i < E ? s_hist[i] : s_rank[i - E]);
+        if (i < E)
+            ntpe[i] = total;
+        else
+            ntpr[i - E] = total;
+        __hip_atomic_store(acc + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+#ifndef CGD_LAYOUT_TILE
+#define CGD_LAYOUT_TILE 512
+#endif
+constexpr int kLayoutAccTile = CGD_LAYOUT_TILE;  // tokens per block of get_dispatch_layout alone
+static_assert(kLayoutAccTile % 16 == 0 && kLayoutAccTile % kWave == 0, "rows of a tile start 16-byte aligned");
+
 int64_t layout_blocks(int64_t T) { return T <= 0 ? 1 : (T + kLayoutTile - 1) / kLayoutTile; }
 
-size_t layout_workspace_bytes(int64_t T, int E, int R) {
+size_t layout_partial_bytes(int64_t T, int E, int R) {
     const size_t arr = (size_t)layout_blocks(T) * (size_t)(E + R) * sizeof(int32_t);
     return kTicketBytes + (arr + 255) / 256 * 256;
 }
 
+size_t layout_workspace_bytes(int64_t, int E, int R) {
+    return ((size_t)(E + R) * sizeof(unsigned long long) + 255) / 256 * 256;
+}
+
 hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R, int32_t* ntpr, int32_t* ntpe,
                          uint8_t* itr, void* workspace, hipStream_t stream) {
-    unsigned int* ticket = reinterpret_cast<unsigned int*>(workspace);
-    int32_t* partial = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + kTicketBytes);
-    const dim3 grid((unsigned)layout_blocks(T)), block(kLayoutTile);
+    unsigned long long* acc = reinterpret_cast<unsigned long long*>(workspace);
+    constexpr int TILE = kLayoutAccTile;
+    const dim3 grid((unsigned)(T <= 0 ? 1 : (T + TILE - 1) / TILE)), block(TILE);
     const int L = E / R;
-    const NormalPlanOut none{nullptr, nullptr, nullptr, nullptr, nullptr, 1};
     if (R <= 64)
-        hipLaunchKernelGGL(layout_kernel<1>, grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
-                           partial, ticket, none);
+        hipLaunchKernelGGL((layout_acc_kernel<1, TILE>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe,
+                           itr, acc);
     else
-        hipLaunchKernelGGL(layout_kernel<6>, grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
-                           partial, ticket, none);
+        hipLaunchKernelGGL((layout_acc_kernel<6, TILE>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe,
+                           itr, acc);
     return hipGetLastError();
 }
 

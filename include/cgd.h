@@ -72,10 +72,11 @@ const char* cgd_last_error(void);
 /* Workspace bytes cgd_get_dispatch_layout needs for these sizes (host only;
  * 0 if the sizes are invalid). The workspace must be zero-filled before its
  * first use; every completed call leaves the words that must start at zero
- * (a ticket at the start of the workspace) zero again, and everything else
- * in it is rewritten before it is read, so one workspace serves any number of
- * calls, of any sizes, that are ordered on one stream. Calls that may run
- * concurrently need separate workspaces. */
+ * (here one count accumulator per expert and rank; in the other workspaces a
+ * ticket at their start) zero again, and everything else in it is rewritten
+ * before it is read, so one workspace serves any number of calls, of any
+ * sizes, that are ordered on one stream. Calls that may run concurrently
+ * need separate workspaces. */
 size_t cgd_layout_workspace_bytes(int64_t num_tokens, int num_topk, int num_experts, int num_ranks);
 
 /* Workspace bytes cgd_dispatch, cgd_dispatch_plan and their layout-fused

@@ -63,9 +63,13 @@ def test_capacity_and_workspace_sizes():
     assert lib.cgd_dispatch_capacity(1 << 30, 16, 8, 1) == -1
     assert cgd.dispatch_capacity(32768, 16, 512) == 524288
     for T in (0, 1, 255, 256, 257, 32768):
+        # get_dispatch_layout: one 64-bit count accumulator per expert and rank
         ws = lib.cgd_layout_workspace_bytes(T, 8, 256, 8)
+        assert ws >= (256 + 8) * 8 and ws % 256 == 0
         blocks = max(1, -(-T // 256))
-        assert ws >= 256 + blocks * (256 + 8) * 4 and ws % 256 == 0
+        # the layout-fused rank-granular plan keeps one partial count per (tile, expert or rank)
+        wn = lib.cgd_layout_and_normal_workspace_bytes(T, 8, 256, 8)
+        assert wn >= lib.cgd_normal_workspace_bytes(T, 8) + blocks * (256 + 8) * 4 and wn % 256 == 0
         wd = lib.cgd_dispatch_workspace_bytes(T, 8, 256, 8)
         assert wd >= 256 + blocks * 256 * 4 + T * 8 * 4 + blocks * 8 * 4 and wd % 256 == 0
         # the layout-fused plans keep one partial count per (tile, rank)

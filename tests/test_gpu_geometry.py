@@ -1,11 +1,11 @@
 """Launch geometry changes no byte: libcgd built with a second set of launch
 parameters (libcgd_geometry.so: waves per block, vectors per lane, slots per
-row-copy wave, FP8 chunk widths, no prefetch blocks; built beside libcgd.so
-by the build step) must give every output of every data path bit for bit as
-the default build does, on the prefill workload and on a ragged top-16 edge
-case with unselected slots and alignment 16. Receive buffers start from the
-same sentinel fill in both runs, so rows that must stay untouched are
-compared too."""
+row-copy wave, FP8 chunk widths, no prefetch blocks, tokens per block of
+get_dispatch_layout; built beside libcgd.so by the build step) must give
+every output of every data path bit for bit as the default build does, on
+the prefill workload and on a ragged top-16 edge case with unselected slots
+and alignment 16. Receive buffers start from the same sentinel fill in both
+runs, so rows that must stay untouched are compared too."""
 import contextlib
 import ctypes
 import os
@@ -52,6 +52,8 @@ def _run_all(w, idx_np, wts_np, x_np, y_np, align):
     (ntpr, _, ntpe, itr, _), recv, nre, h = cgd.layout_and_dispatch(x, idx, E, R, expert_alignment=align, recv_x=recv)
     out.update(ntpr=ntpr, ntpe=ntpe, itr=itr, off=h.expert_offset, nre=nre, src=h.recv_src_idx, dst=h.dst_row,
                recv=recv)
+    lay = cgd.get_dispatch_layout(idx, E, R)
+    out.update(l_ntpr=lay[0], l_ntpe=lay[2], l_itr=lay[3])
     recv2 = _sentinel((cap, H), torch.bfloat16)
     cgd.dispatch(x, handle=h, recv_x=recv2)
     out["recv_cached"] = recv2
