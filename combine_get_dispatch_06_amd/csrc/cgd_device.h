@@ -230,19 +230,27 @@ __device__ __forceinline__ bool last_block_done(unsigned int* ticket) { return l
 // Bitmask of the ranks the token's selected experts live on (e[k] < 0: none).
 // lshift >= 0: L = 2^lshift experts per rank, the rank is a shift; else the
 // expert -> rank table in LDS.
+// Straight-line code: the ranks of all slots first (the table reads, at a
+// valid index for every slot, all in flight together), then selects; a
+// branch per slot around a table read costs a wait per slot.
 template <int RW>
 __device__ __forceinline__ void token_rank_mask(const int (&e)[kMaxTopk], const int16_t* s_rank_of, int lshift,
                                                 uint64_t (&m)[RW]) {
+    int r[kMaxTopk];
+    if (lshift >= 0) {
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k) r[k] = e[k] >> lshift;
+    } else {
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k) r[k] = s_rank_of[max(e[k], 0)];
+    }
 #pragma unroll
     for (int w = 0; w < RW; ++w) m[w] = 0;
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) {
-        if (e[k] >= 0) {
-            const int r = lshift >= 0 ? (e[k] >> lshift) : (int)s_rank_of[e[k]];
 #pragma unroll
-            for (int w = 0; w < RW; ++w)
-                if ((r >> 6) == w) m[w] |= 1ull << (r & 63);
-        }
+        for (int w = 0; w < RW; ++w)
+            m[w] |= (e[k] >= 0 && (r[k] >> 6) == w) ? 1ull << (r[k] & 63) : 0ull;
     }
 }
 

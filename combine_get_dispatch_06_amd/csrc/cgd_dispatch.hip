@@ -187,10 +187,12 @@ __device__ __forceinline__ void prefetch_rows(const uint4* __restrict__ p, int64
 // final dst_row and recv_src_idx itself and fills the unused rows. FUSED:
 // every block plans the whole batch in LDS (a few microseconds of LDS work,
 // cheaper than a second launch and a second pass over the plan), block 0
-// alone writes the plan's outputs, every block fills a share of the unused
-// rows, and each wave then moves up to kFusedItems (token, chunk) items to
-// the tokens' rows, their x chunks loaded at the start (none with nvec = 0:
-// the plan alone of a one-tile batch with many spare rows). Larger batches
+// alone computes and writes the plan's and the layout's outputs, every block
+// fills a share of the unused rows, and each wave of blocks 1.. (of block 0
+// too when it is alone) then moves up to kFusedItems (token, chunk) items to
+// the tokens' rows, their x chunks loaded once the routing is staged (none
+// with nvec = 0: the plan alone of a one-tile batch with many spare rows).
+// Lanes without a token skip the LDS mask atomics. Larger batches
 // leave packed slot words and tile bases in the workspace for
 // finalize_kernel; blocks past the plan_tiles tiles (if any) prefetch x
 // (px, pvecs 16-byte vectors) and take no part in the plan.
@@ -226,22 +228,25 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     const int64_t t0 = (int64_t)tile * kRankTile;
     const int nt = (int)max<int64_t>(0, min<int64_t>(kRankTile, T - t0));
 
-    // FUSED: this wave's items, their x chunks loaded before the plan
+    // FUSED: this wave's (token, chunk) items (a batch of at most one tile:
+    // item numbers fit in 32 bits). In a grid of several blocks, block 0,
+    // which alone also computes and writes the plan's and the layout's
+    // outputs, moves no rows: the others' items end about when it does.
     int64_t ft[kFusedItems];
     int fv[kFusedItems];
-    uint4 fbuf[kFusedItems];
     if (FUSED) {
-        const int64_t w0 = (int64_t)blockIdx.x * kRankWaves + __builtin_amdgcn_readfirstlane(wave);
+        const bool movers = gridDim.x > 1;  // blocks 1.. move the rows
+        const unsigned nbm = movers ? gridDim.x - 1 : 1;
+        const unsigned w0 = (movers ? blockIdx.x - 1 : 0) * kRankWaves + __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int j = 0; j < kFusedItems; ++j) {
-            const int64_t item = w0 + (int64_t)j * gridDim.x * kRankWaves;
-            ft[j] = item / fc.nchunk;
-            fv[j] = (int)(item - ft[j] * fc.nchunk) * kWave + lane;
-            fbuf[j] = make_uint4(0, 0, 0, 0);
-            if (ft[j] < T && fv[j] < fc.nvec) fbuf[j] = fc.x[ft[j] * fc.nvec + fv[j]];
+            unsigned item = w0 + (unsigned)j * nbm * kRankWaves;
+            if (movers && blockIdx.x == 0) item = 0xFFFFFFF0u;  // no items: ft >= T below
+            const unsigned tj = item / (unsigned)fc.nchunk;
+            ft[j] = tj;
+            fv[j] = (int)(item - tj * (unsigned)fc.nchunk) * kWave + lane;
         }
     }
-
     for (int i = tid; i < kRankWaves * E; i += kRankTile) {
         s_tok[i] = 0ull;
         s_pre[i] = 0;
@@ -255,6 +260,18 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     }
     stage_routing<kMaxTopk, kRankTile>(topk_idx + t0 * K, nt * K, E, s_slot);
     __syncthreads();
+    // FUSED: this wave's items, their x chunks loaded now, after the stage:
+    // loads complete in issue order, so x loads issued before the routing
+    // would hold up the stage; the plan's LDS work hides them (the item
+    // indexes were computed while the routing loads were in flight)
+    uint4 fbuf[kFusedItems];
+    if (FUSED) {
+#pragma unroll
+        for (int j = 0; j < kFusedItems; ++j) {
+            fbuf[j] = make_uint4(0, 0, 0, 0);
+            if (ft[j] < T && fv[j] < fc.nvec) fbuf[j] = fc.x[ft[j] * fc.nvec + fv[j]];
+        }
+    }
 
     int32_t* my = s_slot + tid * K;  // this token's K slots
     const bool mine = tid < nt;
@@ -268,19 +285,22 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     // Each wave sets one bit per (expert, lane) in a 64-bit LDS mask per
     // expert. The previous mask returned by the atomic also tells whether this
     // token already holds the expert in an earlier slot.
-    // all K atomics are issued before any result is used (an unselected slot
-    // ORs 0 into a word of its wave's row); the results follow together
+    // all K atomics are issued before any result is used; the results follow
+    // together. Lanes without a selected expert (no token: the idle waves of
+    // a short tile) take no part: as dummy operations on one common word
+    // they would be a 64-way same-address LDS atomic each (about 2 us at
+    // decode).
     uint64_t prev[kMaxTopk];
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) {
         prev[k] = 0;
-        if (k < K) prev[k] = atomicOr(&s_tok[wave * E + max(e[k], 0)], e[k] >= 0 ? bit : 0ull);
+        if (k < K && e[k] >= 0) prev[k] = atomicOr(&s_tok[wave * E + e[k]], bit);
     }
     bool dup = false;
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) dup |= e[k] >= 0 && (prev[k] & bit) != 0;
     uint64_t m[RW];
-    if (LAYOUT) {
+    if (LAYOUT && writer) {  // FUSED: only block 0 writes the layout outputs
         const int lshift = (lo.L & (lo.L - 1)) == 0 ? __builtin_ctz(lo.L) : -1;
         token_rank_mask<RW>(e, s_rank_of, lshift, m);
         count_rank_tokens<RW>(m, lo.R, s_rank, s_mask);
@@ -987,8 +1007,10 @@ static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E,
     // share its LDS bandwidth for that
     const int64_t items = T * nchunk;
     const int64_t per_block = (int64_t)kRankWaves * kFusedItems;
-    const int64_t blocks = std::max<int64_t>(std::min<int64_t>((items + kRankWaves - 1) / kRankWaves, device_cus()),
-                                             (items + per_block - 1) / per_block);
+    int64_t blocks = std::max<int64_t>(std::min<int64_t>((items + kRankWaves - 1) / kRankWaves, device_cus()),
+                                       (items + per_block - 1) / per_block);
+    // in a grid of several blocks block 0 moves no rows: blocks 1.. hold every item
+    if (blocks > 1) blocks = std::max<int64_t>(blocks, 1 + (items + per_block - 1) / per_block);
     const dim3 grid((unsigned)std::max<int64_t>(1, blocks)), block(kRankTile);
     const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
     const TileOut fc{dst_row, recv_src_idx, cap, reinterpret_cast<const uint4*>(x), nvec, nchunk,
