@@ -316,11 +316,14 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         // the tile's rows of expert e is the number of earlier tokens holding
         // e: the lanes below mine in my wave's mask plus earlier waves' rows.
         for (int x = tid; x < E; x += kRankTile) {
+            uint64_t mk[kRankWaves];  // all mask reads before any store (same LDS array)
+#pragma unroll
+            for (int w = 0; w < kRankWaves; ++w) mk[w] = s_tok[w * E + x];
             int run = 0;
 #pragma unroll
             for (int w = 0; w < kRankWaves; ++w) {
                 s_pre[w * E + x] = run;
-                run += __popcll(s_tok[w * E + x]);
+                run += __popcll(mk[w]);
             }
             if (ntiles > 1) tile_base[(int64_t)tile * E + x] = run;
             s_off[x] = run;  // the tile's histogram (one-tile grids finish from it)
