@@ -622,12 +622,12 @@ def graph_call_us(fn, order=(0,), calls: int = GRAPH_CALLS, replays: int = GRAPH
     return {**stats(per), "launches": calls * replays}
 
 
-def graph_summary(path, order) -> dict:
+def graph_summary(path, order, calls: int = GRAPH_CALLS, replays: int = GRAPH_REPLAYS) -> dict:
     """Per-call device times of the path's calls (graph_call_us, sets cycling
     through `order`), the whole dispatch and the combine with their GB/s and
     fractions of the HBM peak (bytes averaged over the sets of `order`)."""
     import numpy as np
-    per = {lab: graph_call_us(fn, order) for lab, fn in path.graph_calls().items()}
+    per = {lab: graph_call_us(fn, order, calls, replays) for lab, fn in path.graph_calls().items()}
     nb = [path.nbytes(int(i)) for i in order]
 
     def rate(key, t):
@@ -746,6 +746,13 @@ def main() -> int:
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra event-timed steps, each after a read-only sweep of 512 MiB (evicts the 256 MB "
                          "Infinity Cache without leaving dirty lines); 0 skips them")
+    ap.add_argument("--graph-calls", type=int, default=GRAPH_CALLS,
+                    help="back-to-back calls per captured graph for the per-call device times")
+    ap.add_argument("--graph-replays", type=int, default=GRAPH_REPLAYS,
+                    help="timed replays of each per-call graph (calls x replays launches per figure)")
+    ap.add_argument("--skip-warm", action="store_true",
+                    help="skip the warm_x leg (one x every step), e.g. so that a profiler's per-kernel averages "
+                         "cover the rotated-input launches alone")
     ap.add_argument("--fp8", choices=tuple(FP8_FORMATS), default=None,
                     help="FP8 (e4m3fn) dispatch payload with this scale format: the expert path casts on "
                          "dispatch, the normal path casts first and dispatches the (codes, scales) tuple")
@@ -807,14 +814,18 @@ def main() -> int:
     samples = max(args.kernel_samples, 1)
     us, which = kernel_samples(path, [rotation[k % nsets] for k in range(samples)])
     eager = summarize(path, us, which)
-    rotated = graph_summary(path, rotation)
+    gc, gr = max(1, args.graph_calls), max(1, args.graph_replays)
+    rotated = graph_summary(path, rotation, gc, gr)
     wall, timing = timed_wall(args, path, rotation)
 
-    us0, which0 = kernel_samples(path, [0] * samples)
-    warm = graph_summary(path, [0])
-    warm["eager"] = summarize(path, us0, which0)
-    wall0, _ = timed_wall(args, path, [0])
-    warm.update(ms_per_step=wall0 / args.steps * 1e3, tokens_per_s=w.T * args.steps / wall0)
+    warm = None
+    if not args.skip_warm:
+        us0, which0 = kernel_samples(path, [0] * samples)
+        warm = graph_summary(path, [0], gc, gr)
+        warm["eager"] = summarize(path, us0, which0)
+        wall0, _ = timed_wall(args, path, [0])
+        warm.update(ms_per_step=wall0 / args.steps * 1e3, tokens_per_s=w.T * args.steps / wall0)
+        warm["how"] = "one input set (seed %d) every step: x stays in the Infinity Cache" % args.seed
 
     cold = None
     if args.cold_steps > 0:
@@ -829,8 +840,8 @@ def main() -> int:
         cold["flush"] = "read-only sweep of 512 MiB (a reduction) before every step, outside the events"
         del sweep
 
-    layout_alone = graph_call_us(lambda i: cgd.get_dispatch_layout(path.idx[i], w.E, w.R), rotation)
-    floor = graph_call_us(lambda i: cgd.empty_(dev))
+    layout_alone = graph_call_us(lambda i: cgd.get_dispatch_layout(path.idx[i], w.E, w.R), rotation, gc, gr)
+    floor = graph_call_us(lambda i: cgd.empty_(dev), (0,), gc, gr)
     ctx = copy_ceilings(dev)
     tkey = w.name + ("" if args.path == "expert" else ":" + args.path) + (f":fp8-{args.fp8}" if fmt is not None else "")
     roof = roofline(path, rotated, args.traffic_json, tkey)
@@ -860,13 +871,13 @@ def main() -> int:
         "launch_floor_us": floor,
         **{k: v for k, v in rotated.items() if k != "kernel_us"},
         "kernel_us": rotated["kernel_us"],
-        "kernel_us_how": f"device time per call: {GRAPH_CALLS} back-to-back calls per HIP graph, "
-                         f"{GRAPH_REPLAYS} replays between HIP events on the launch stream, sets rotating",
+        "kernel_us_how": f"device time per call: {gc} back-to-back calls per HIP graph, "
+                         f"{gr} replays between HIP events on the launch stream, sets rotating",
         "eager": {**eager, "how": f"HIP events around each call of {samples} eager steps, sets rotating "
                                   "(host-bound for small batches)"},
         "kernel_samples": samples,
         "first_step_ms": first_ms,
-        "warm_x": {**warm, "how": "one input set (seed %d) every step: x stays in the Infinity Cache" % args.seed},
+        "warm_x": warm,
         "cold_cache": cold,
         **ctx,
         "inputs_sha256": input_digests(sets[0]),
@@ -951,7 +962,7 @@ def write_traffic(args) -> int:
         shorts = ("normal_scatter_kernel", "normal_combine_kernel", "normal_plan_kernel", "layout_kernel",
                   "cast_to_fp8_kernel")
     else:
-        shorts = APPLY_KERNELS + PLAN_KERNELS + ("combine_kernel", "layout_kernel")
+        shorts = APPLY_KERNELS + PLAN_KERNELS + ("combine_kernel", "layout_acc_kernel")
     for short in shorts:
         fk = [k for k in fetch if "cgd::" + short in k]
         wk = [k for k in write if "cgd::" + short in k]
