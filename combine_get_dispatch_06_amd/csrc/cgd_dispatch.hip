@@ -221,6 +221,11 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     const int tile = FUSED ? 0 : blockIdx.x;
     const int ntiles = FUSED ? 1 : plan_tiles;
     const bool writer = !FUSED || blockIdx.x == 0;  // writes the plan's outputs
+    // FUSED: the blocks before m0 move no rows; block 0 writes the plan's
+    // outputs and, in a grid of three or more, block 1 the layout's (else
+    // block 0 both)
+    const unsigned m0 = !FUSED ? 0u : gridDim.x > 2 && LAYOUT ? 2u : gridDim.x > 1 ? 1u : 0u;
+    const bool lwriter = !FUSED || blockIdx.x == (m0 == 2 ? 1u : 0u);  // writes the layout's outputs
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -229,19 +234,19 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     const int nt = (int)max<int64_t>(0, min<int64_t>(kRankTile, T - t0));
 
     // FUSED: this wave's (token, chunk) items (a batch of at most one tile:
-    // item numbers fit in 32 bits). In a grid of several blocks, block 0,
-    // which alone also computes and writes the plan's and the layout's
-    // outputs, moves no rows: the others' items end about when it does.
+    // item numbers fit in 32 bits). The blocks that alone compute and write
+    // the plan's and the layout's outputs move no rows: the others' items
+    // end about when they do.
     int64_t ft[kFusedItems];
     int fv[kFusedItems];
     if (FUSED) {
-        const bool movers = gridDim.x > 1;  // blocks 1.. move the rows
-        const unsigned nbm = movers ? gridDim.x - 1 : 1;
-        const unsigned w0 = (movers ? blockIdx.x - 1 : 0) * kRankWaves + __builtin_amdgcn_readfirstlane(wave);
+        const unsigned nbm = gridDim.x - m0;  // blocks m0.. move the rows
+        const unsigned w0 = (blockIdx.x >= m0 ? blockIdx.x - m0 : 0u) * kRankWaves +
+                            __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
         for (int j = 0; j < kFusedItems; ++j) {
             unsigned item = w0 + (unsigned)j * nbm * kRankWaves;
-            if (movers && blockIdx.x == 0) item = 0xFFFFFFF0u;  // no items: ft >= T below
+            if (blockIdx.x < m0) item = 0xFFFFFFF0u;  // no items: ft >= T below
             const unsigned tj = item / (unsigned)fc.nchunk;
             ft[j] = tj;
             fv[j] = (int)(item - tj * (unsigned)fc.nchunk) * kWave + lane;
@@ -300,13 +305,13 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) dup |= e[k] >= 0 && (prev[k] & bit) != 0;
     uint64_t m[RW];
-    if (LAYOUT && writer) {  // FUSED: only block 0 writes the layout outputs
+    if (LAYOUT && lwriter) {  // FUSED: only one block writes the layout outputs
         const int lshift = (lo.L & (lo.L - 1)) == 0 ? __builtin_ctz(lo.L) : -1;
         token_rank_mask<RW>(e, s_rank_of, lshift, m);
         count_rank_tokens<RW>(m, lo.R, s_rank, s_mask);
     }
     const bool any_dup = __syncthreads_or(dup);
-    if (LAYOUT && writer) {
+    if (LAYOUT && lwriter) {
         // t0*R is a multiple of 16 because kRankTile is
         store_token_in_rank<RW, kRankTile>(m, s_mask, nt, lo.R, lo.itr + t0 * lo.R);
         for (int r = tid; r < lo.R; r += kRankTile) lo.rank_part[(int64_t)tile * lo.R + r] = s_rank[r];
@@ -391,9 +396,9 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         // no other block has to be waited for
         for (int x = tid; x < E; x += kRankTile) {
             s_pre[x] = s_off[x];
-            if (LAYOUT && writer) lo.ntpe[x] = s_off[x];
+            if (LAYOUT && lwriter) lo.ntpe[x] = s_off[x];
         }
-        if (LAYOUT && writer)
+        if (LAYOUT && lwriter)
             for (int r = tid; r < lo.R; r += kRankTile) lo.ntpr[r] = s_rank[r];
     } else {
     if (!last_block_done(ticket, ntiles)) return;
@@ -458,15 +463,20 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     if (ntiles > 1) return;  // finalize_kernel completes the handle
 
     // ---- one tile: final rows and unused rows; FUSED: this wave's items ----
-    if (mine) {
+    // The final row of a packed (expert, rank) word: segment offset + rank,
+    // or the fixed-capacity row; -1 past the capacity or the buffer.
+    auto row_of = [&](int v) {
+        if (v < 0) return -1;
+        const int ex = v >> kPackBits, r = v & ((1 << kPackBits) - 1);
+        const int d = seg_cap >= 0 ? (r < seg_cap ? ex * seg_cap + r : -1) : s_off[ex] + r;
+        return d < fc.cap ? d : -1;
+    };
+    // the block that writes the handle turns every slot word into its row;
+    // the other blocks of a FUSED grid resolve only their items' rows, below
+    const bool all_rows = !FUSED || writer;
+    if (mine && all_rows) {
         for (int k = 0; k < K; ++k) {
-            const int v = my[k];
-            int d = -1;
-            if (v >= 0) {
-                const int ex = v >> kPackBits, r = v & ((1 << kPackBits) - 1);
-                d = seg_cap >= 0 ? (r < seg_cap ? ex * seg_cap + r : -1) : s_off[ex] + r;
-                if (d >= fc.cap) d = -1;
-            }
+            const int d = row_of(my[k]);
             my[k] = d;
             if (writer) {
                 fc.dst_row[(int64_t)tid * K + k] = d;
@@ -476,12 +486,15 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     }
     fill_unused(fc.recv_src_idx, s_off, s_pre, E, fc.cap, blockIdx.x * kRankTile + tid, gridDim.x * kRankTile);
     if (!FUSED) return;
-    __syncthreads();
+    if (all_rows) __syncthreads();  // the moves below read the rows just written
 #pragma unroll
     for (int j = 0; j < kFusedItems; ++j) {
         if (ft[j] < T) {
             int dl = -1;
-            if (lane < K) dl = s_slot[ft[j] * K + lane];
+            if (lane < K) {
+                const int v = s_slot[ft[j] * K + lane];
+                dl = all_rows ? v : row_of(v);
+            }
             for (int k = 0; k < K; ++k) {
                 const int d = __builtin_amdgcn_readlane(dl, k);
                 if (d >= 0 && fv[j] < fc.nvec) store_nt(fc.recv_x + (int64_t)d * fc.nvec + fv[j], fbuf[j]);
@@ -1012,8 +1025,12 @@ static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E,
     const int64_t per_block = (int64_t)kRankWaves * kFusedItems;
     int64_t blocks = std::max<int64_t>(std::min<int64_t>((items + kRankWaves - 1) / kRankWaves, device_cus()),
                                        (items + per_block - 1) / per_block);
-    // in a grid of several blocks block 0 moves no rows: blocks 1.. hold every item
-    if (blocks > 1) blocks = std::max<int64_t>(blocks, 1 + (items + per_block - 1) / per_block);
+    // in a grid of several blocks the first block (the first two with the
+    // layout outputs, in a grid of three or more) moves no rows: the others
+    // hold every item
+    const int64_t need = (items + per_block - 1) / per_block;
+    if (blocks > 1) blocks = std::max<int64_t>(blocks, 1 + need);
+    if (blocks > 2 && layout) blocks = std::max<int64_t>(blocks, 2 + need);
     const dim3 grid((unsigned)std::max<int64_t>(1, blocks)), block(kRankTile);
     const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
     const TileOut fc{dst_row, recv_src_idx, cap, reinterpret_cast<const uint4*>(x), nvec, nchunk,
