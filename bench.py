@@ -698,6 +698,43 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
                       f"single-threaded C oracle, {el:.1f} s on {cpu_model()} ({os.cpu_count()} cpus visible)"}
 
 
+def _oracle_slice_worker(args) -> tuple:
+    """One process of the parallel CPU baseline: whole oracle steps over its
+    token slice until the budget is used -> (tokens processed, seconds)."""
+    name, seed, lo, hi, budget_s = args
+    import oracle
+    import synth
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w, seed=seed)
+    idx, x, wt = inp["topk_idx"][lo:hi], inp["x"][lo:hi], inp["topk_weights"][lo:hi]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.layout(idx, w.E, w.R)
+        d = oracle.dispatch(x, idx, w.E, w.R)
+        oracle.combine(d["recv_x"], d["dst_row"], wt)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            return reps * (hi - lo), el
+
+
+def cpu_baseline_parallel(w, seed: int, cores: int, budget_s: float) -> dict:
+    """The same oracle steps with the batch's tokens split into `cores`
+    contiguous slices, one process each (the per-core token split of the
+    layout operator's multi-core strategy): the sum of the slices' token
+    rates. Each slice is planned on its own (its own segment offsets), so
+    this is a throughput figure of the same work, not one dispatch."""
+    import multiprocessing as mp
+    bounds = [(w.T * i // cores, w.T * (i + 1) // cores) for i in range(cores)]
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_oracle_slice_worker, [(w.name, seed, lo, hi, budget_s) for lo, hi in bounds])
+    sizes = sorted({hi - lo for lo, hi in bounds})
+    return {"value": sum(tok / el for tok, el in res), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cores} processes, each whole oracle steps (layout+dispatch+combine) over a contiguous "
+                      f"slice of {'-'.join(map(str, sizes))} tokens of the {w.name} workload (seed {seed}) "
+                      f"for {budget_s:.0f} s, on {cpu_model()}"}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -757,6 +794,9 @@ def main() -> int:
                     help="FP8 (e4m3fn) dispatch payload with this scale format: the expert path casts on "
                          "dispatch, the normal path casts first and dispatches the (codes, scales) tuple")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=10.0, help="0 skips the CPU baseline")
+    ap.add_argument("--cpu-baseline-cores", type=int, default=0,
+                    help="also time the oracle over this many token slices in parallel processes "
+                         "(cpu_baseline_parallel); 0 skips it")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch (from rocprofv3 counters), if present")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -886,6 +926,9 @@ def main() -> int:
     }
     if args.cpu_baseline_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_baseline_seconds)
+        if args.cpu_baseline_cores > 1:
+            res["cpu_baseline_parallel"] = cpu_baseline_parallel(w, args.seed, args.cpu_baseline_cores,
+                                                                 args.cpu_baseline_seconds)
     print(json.dumps(res), flush=True)
     return 0
 
