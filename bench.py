@@ -1027,11 +1027,18 @@ def write_traffic(args) -> int:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and layout whitespace
+    removed: measured traffic stays attached to the code it was taken on
+    (any change to the code, not to its comments, invalidates it)."""
     import hashlib
+    import re
     hsh = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_get_dispatch_06_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        hsh.update(open(os.path.join(csrc, f), "rb").read())
+        text = open(os.path.join(csrc, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)               # line comments (no "//" inside strings here)
+        hsh.update(f.encode() + b"\0" + " ".join(text.split()).encode())
     return hsh.hexdigest()[:16]
 
 

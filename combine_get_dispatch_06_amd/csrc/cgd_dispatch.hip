@@ -34,23 +34,26 @@
 //                   (padding, unused capacity, tail).
 //   the apply       moves each row to its final rows, reading it from HBM
 //                   once however many experts it goes to. Batches of >= 16384
-//                   slots with top-k <= 8: scatter_kernel, one wave per
-//                   (token, 1 KB chunk, slot), stores the chunk once to its
-//                   row. Otherwise scatter_bcast_kernel: one wave per (token,
-//                   chunk) stores the chunk to each of the K rows.
-//                   scatter_cast_kernel is the FP8 form (cast on the way).
+//                   slots: scatter_kernel, one wave per (token, U KB chunk,
+//                   group of S slots), the chunk's K/S waves adjacent so that
+//                   they share its load through L2. Smaller batches:
+//                   scatter_bcast_kernel, one wave per (token, chunk) stores
+//                   the chunk to each of the K rows. scatter_cast_kernel is
+//                   the FP8 form (cast on the way, one wave per chunk).
 //                   Cached dispatch is the same apply on a stored dst_row.
 //   FUSED           batches of at most one tile (decode) through cgd_dispatch
 //                   or the bf16 packed dispatch: rank_kernel plans and moves
 //                   the rows in one launch (every block plans the batch).
 //
-// Measured on MI355X: the store pattern bounds the apply. Stores into the ~E
-// receive segments of a token-ordered pass run near 5 TB/s; short waves that
-// store one 1 KB piece each (row copy) do 3-15 % better than long waves that
-// store K pieces, as long as each wave's row comes after one dependent load
-// (hence the final rows from the plan). Destination-ordered copies
-// (sequential stores) lose more on the 8x scattered re-reads of x than they
-// gain.
+// Measured on MI355X: the receive layout bounds the apply. The same 16-byte
+// copy writes token-major destinations (token t's K rows side by side) about
+// 20 % faster than the expert-major rows the method prescribes, at hidden
+// 7168 whatever the grouping of rows up to 896 KB; the apply runs within a
+// few % of the latter. Each wave's rows come after one dependent load (hence
+// the final rows from the plan), and x arrives from HBM into waves that wait
+// for it, which slot groups and the plan's prefetch of x hide. Destination-
+// ordered copies (sequential stores) lose more on the 8x scattered re-reads
+// of x than they gain.
 #include <algorithm>
 #include <atomic>
 
