@@ -76,3 +76,38 @@ def test_counts_of_an_empty_batch_and_of_unselected_slots():
     _, nre0, _ = cgd.dispatch(torch.empty((0, 8), dtype=torch.bfloat16, device=DEV),
                               torch.empty((0, 3), dtype=torch.int64, device=DEV), E, R, expert_alignment=4)
     np.testing.assert_array_equal(nre0.cpu().numpy(), np.zeros(E, np.int32))
+
+
+def test_layout_workspace_returns_to_zero():
+    """get_dispatch_layout combines its blocks' counts in accumulators in the
+    workspace, which every call must leave at zero (include/cgd.h, the
+    workspace rules): calls of several sizes in a row on one caller-owned
+    workspace each match the oracle, and the workspace is all zero after
+    them."""
+    import ctypes
+    lib = cgd.load()
+    E, R = 256, 8
+    sizes = [4096, 700, 1, 9000, 513, 4096]
+    base = synth.WORKLOADS["prefill"]
+    nbytes = max(lib.cgd_layout_workspace_bytes(T, base.K, E, R) for T in sizes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i, T in enumerate(sizes):
+        say(f"layout workspace: call {i}, T={T}")
+        idx_np = synth.make_topk_idx(base.replace(T=T), seed=20 + i)[:T].copy()
+        idx_np[np.random.default_rng(i).random(idx_np.shape) < 0.1] = -1
+        idx = dev_i64(idx_np)
+        ntpr = torch.full((R,), -7, dtype=torch.int32, device=DEV)
+        ntpe = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+        itr = torch.empty((T, R), dtype=torch.bool, device=DEV)
+        rc = lib.cgd_get_dispatch_layout(ctypes.c_void_p(idx.data_ptr()), T, base.K, E, R,
+                                         ctypes.c_void_p(ntpr.data_ptr()), ctypes.c_void_p(ntpe.data_ptr()),
+                                         ctypes.c_void_p(itr.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                                         ctypes.c_size_t(ws.numel()), stream)
+        assert rc == 0, cgd.load().cgd_last_error()
+        torch.cuda.synchronize()
+        o_ntpr, o_ntpe, o_itr = oracle.layout(idx_np, E, R)
+        np.testing.assert_array_equal(ntpr.cpu().numpy(), o_ntpr)
+        np.testing.assert_array_equal(ntpe.cpu().numpy(), o_ntpe)
+        np.testing.assert_array_equal(itr.cpu().numpy(), o_itr)
+        assert int(ws.count_nonzero()) == 0, f"workspace words left non-zero after call {i}"
