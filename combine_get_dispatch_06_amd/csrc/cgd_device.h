@@ -172,6 +172,17 @@ __device__ __forceinline__ void copy_side_row(const SideRows& s, int64_t t, int6
     }
 }
 
+// Up to this top-k, a kernel with one token per thread loads its token's
+// routing straight into registers (the K loads of a wave together use every
+// byte of the lines they touch) instead of staging the tile through LDS:
+// get_dispatch_layout alone measured 4.81 against 5.27 us at prefill and
+// 6.23 against 6.64 Zipf-skewed; at top-16 the staged form is faster (11.9
+// against 12.5 us).
+#ifndef CGD_DIRECT_TOPK
+#define CGD_DIRECT_TOPK 8
+#endif
+constexpr int kDirectTopk = CGD_DIRECT_TOPK;
+
 // Copy n (<= ITEMS * BLOCK) routing entries of one tile into LDS as int32,
 // entries outside [0, E) becoming -1, with a block of BLOCK threads. All
 // global loads of a thread are issued before any LDS store, so the tile costs

@@ -255,6 +255,17 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
             fv[j] = (int)(item - tj * (unsigned)fc.nchunk) * kWave + lane;
         }
     }
+    // top-k <= kDirectTopk: this thread's token's routing straight into
+    // registers, in flight across the barrier that orders the LDS set-up
+    // (the tile's routing reaches LDS from registers below, for the phases
+    // that read other tokens' slots); larger top-k: the coalesced stage
+    const bool direct = K <= kDirectTopk;
+    int64_t raw[kMaxTopk];
+    {
+        const int64_t* tok = topk_idx + (t0 + min(tid, max(nt - 1, 0))) * K;
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k) raw[k] = (direct && tid < nt && k < K) ? tok[k] : -1;
+    }
     for (int i = tid; i < kRankWaves * E; i += kRankTile) {
         s_tok[i] = 0ull;
         s_pre[i] = 0;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
         for (int i = tid; i < E; i += kRankTile) s_rank_of[i] = (int16_t)(i / lo.L);
         for (int i = tid; i < lo.R; i += kRankTile) s_rank[i] = 0;
     }
-    stage_routing<kMaxTopk, kRankTile>(topk_idx + t0 * K, nt * K, E, s_slot);
+    if (!direct) stage_routing<kMaxTopk, kRankTile>(topk_idx + t0 * K, nt * K, E, s_slot);
     __syncthreads();
     // FUSED: this wave's items, their x chunks loaded now, after the stage:
     // loads complete in issue order, so x loads issued before the routing
@@ -287,7 +298,16 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     const uint64_t bit = 1ull << lane;
     int e[kMaxTopk];
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) e[k] = (mine && k < K) ? my[k] : -1;
+    for (int k = 0; k < kMaxTopk; ++k) {
+        if (direct)
+            e[k] = (raw[k] >= 0 && raw[k] < E) ? (int)raw[k] : -1;
+        else
+            e[k] = (mine && k < K) ? my[k] : -1;
+    }
+    if (direct && mine)
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k)
+            if (k < K) my[k] = e[k];
 
     // ---- 1. rank of every slot inside the tile; tile histogram ----
     // Each wave sets one bit per (expert, lane) in a 64-bit LDS mask per

@@ -1,7 +1,8 @@
 """Launch geometry changes no byte: libcgd built with a second set of launch
 parameters (libcgd_geometry.so: waves per block, vectors per lane, slots per
 row-copy wave, FP8 chunk widths, no prefetch blocks, tokens per block of
-get_dispatch_layout; built beside libcgd.so by the build step) must give
+get_dispatch_layout and its routing always staged through LDS; built beside
+libcgd.so by the build step) must give
 every output of every data path bit for bit as the default build does, on
 the prefill workload and on a ragged top-16 edge case with unselected slots
 and alignment 16. Receive buffers start from the same sentinel fill in both
