@@ -66,17 +66,31 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     const int64_t t0 = (int64_t)blockIdx.x * kLayoutTile;
     const int nt = (int)max<int64_t>(0, min<int64_t>(kLayoutTile, T - t0));
 
+    // top-k <= kDirectTopk: the token's routing straight into registers
+    // (as the layout alone below); larger top-k: the coalesced stage
+    const bool direct = K <= kDirectTopk;
+    int64_t raw[kMaxTopk];
+    {
+        const int64_t* tok = topk_idx + (t0 + min(tid, max(nt - 1, 0))) * K;
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k) raw[k] = (direct && tid < nt && k < K) ? tok[k] : -1;
+    }
     for (int i = tid; i < E; i += kLayoutTile) {
         s_hist[i] = 0;
         s_rank_of[i] = (int16_t)(i / L);
     }
     for (int i = tid; i < R; i += kLayoutTile) s_rank[i] = 0;
-    stage_routing<kMaxTopk, kLayoutTile>(topk_idx + t0 * K, nt * K, E, s_idx);
+    if (!direct) stage_routing<kMaxTopk, kLayoutTile>(topk_idx + t0 * K, nt * K, E, s_idx);
     __syncthreads();
 
     int e[kMaxTopk];
 #pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) e[k] = (tid < nt && k < K) ? s_idx[tid * K + k] : -1;
+    for (int k = 0; k < kMaxTopk; ++k) {
+        if (direct)
+            e[k] = (raw[k] >= 0 && raw[k] < E) ? (int)raw[k] : -1;
+        else
+            e[k] = (tid < nt && k < K) ? s_idx[tid * K + k] : -1;
+    }
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k)
         if (e[k] >= 0) atomicAdd(&s_hist[e[k]], 1);
