@@ -839,8 +839,12 @@ def main() -> int:
     rotation = list(range(nsets))
     set_bytes = sum(v.nbytes for s in sets for v in s.values())
 
-    # first call timed on its own (cf. the first-call latency discussed on the pages)
+    # first call timed on its own (cf. the first-call latency discussed on the
+    # pages), after cgd.init has loaded libcgd's GPU code (timed too)
     torch.cuda.synchronize()
+    t = time.perf_counter()
+    cgd.init(dev)
+    init_ms = (time.perf_counter() - t) * 1e3
     t = time.perf_counter()
     path.step(0)
     torch.cuda.synchronize()
@@ -916,6 +920,7 @@ def main() -> int:
         "eager": {**eager, "how": f"HIP events around each call of {samples} eager steps, sets rotating "
                                   "(host-bound for small batches)"},
         "kernel_samples": samples,
+        "init_ms": init_ms,
         "first_step_ms": first_ms,
         "warm_x": warm,
         "cold_cache": cold,

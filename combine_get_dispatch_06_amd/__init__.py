@@ -49,7 +49,7 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
            "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_",
            "layout_and_normal_dispatch_plan", "layout_and_dispatch", "normal_workspace_bytes",
-           "layout_and_normal_workspace_bytes", "empty_", "layout_and_dispatch_noalloc"]
+           "layout_and_normal_workspace_bytes", "empty_", "layout_and_dispatch_noalloc", "init"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _BUILT_LIB = os.path.join(_PKG, "libcgd.so")
@@ -97,6 +97,8 @@ def configure(lib):
     lib.cgd_version.argtypes = []
     lib.cgd_last_error.restype = ctypes.c_char_p
     lib.cgd_last_error.argtypes = []
+    lib.cgd_init.restype = i32
+    lib.cgd_init.argtypes = []
     lib.cgd_layout_workspace_bytes.restype = sz
     lib.cgd_layout_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.cgd_dispatch_workspace_bytes.restype = sz
@@ -325,6 +327,15 @@ def copy_(dst: torch.Tensor, src: torch.Tensor) -> torch.Tensor:
     with torch.cuda.device(src.device):
         _check("cgd_copy", lib.cgd_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
     return dst
+
+
+def init(device: torch.device | str | int | None = None) -> None:
+    """Load libcgd's GPU code on the device now rather than inside the first
+    call of each entry point (optional; allocates and enqueues nothing)."""
+    lib = load()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        _check("cgd_init", lib.cgd_init())
 
 
 def empty_(device: torch.device | str | int | None = None) -> None:

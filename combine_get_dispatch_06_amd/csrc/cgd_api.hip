@@ -822,3 +822,19 @@ extern "C" int cgd_layout_and_dispatch_noalloc(const void* x, int64_t num_tokens
                                         num_tokens_per_expert, is_token_in_rank, expert_offset,
                                         num_recv_tokens_per_expert, recv_src_idx, dst_row, ws, stream);
 }
+
+// Loads every source file's code object on the current device (the runtime
+// loads one on the first use of any of its kernels): hipFuncGetAttributes on
+// one kernel of each file. Nothing is allocated or enqueued.
+extern "C" int cgd_init(void) {
+    hipFuncAttributes a;
+    hipError_t err = hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&clear_scratch_ticket));
+    if (err == hipSuccess) err = cgd::preload_combine();
+    if (err == hipSuccess) err = cgd::preload_copy();
+    if (err == hipSuccess) err = cgd::preload_dispatch();
+    if (err == hipSuccess) err = cgd::preload_fp8();
+    if (err == hipSuccess) err = cgd::preload_normal();
+    if (err == hipSuccess) err = cgd::preload_layout();
+    if (err != hipSuccess) return hip_fail(err, "loading the GPU code");
+    return CGD_OK;
+}

@@ -105,6 +105,11 @@ __global__ __launch_bounds__(kCombineWaves* kWave) void combine_kernel(const uin
     }
 }
 
+hipError_t preload_combine() {
+    hipFuncAttributes a;
+    return hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&combine_kernel<8, CGD_COMBINE_U>));
+}
+
 hipError_t launch_combine(const void* expert_out, int64_t cap, int H, const int32_t* dst_row, const float* w,
                           int64_t T, int K, void* out, hipStream_t stream) {
     if (T <= 0) return hipSuccess;

@@ -32,6 +32,11 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st
 
 __global__ __launch_bounds__(kWave) void empty_kernel() {}
 
+hipError_t preload_copy() {
+    hipFuncAttributes a;
+    return hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&empty_kernel));
+}
+
 hipError_t launch_empty(hipStream_t stream) {
     hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(kWave), 0, stream);
     return hipGetLastError();

@@ -761,6 +761,11 @@ __global__ __launch_bounds__(kScatterWaves* kWave) void scatter_cast_kernel(
     }
 }
 
+hipError_t preload_dispatch() {
+    hipFuncAttributes a;
+    return hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&finalize_kernel));
+}
+
 // Dispatch workspace: ticket | tile bases int32 [tiles, E] | packed slot
 // words int32 [T, K] (rank_kernel -> finalize_kernel) | per-expert slot
 // counts int32 [E] | segment offsets int32 [E+1] of the packed layout (its

@@ -133,4 +133,9 @@ hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64
     return hipGetLastError();
 }
 
+hipError_t preload_fp8() {
+    hipFuncAttributes a;
+    return hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&cast_to_fp8_kernel<0>));
+}
+
 }  // namespace cgd

@@ -138,4 +138,13 @@ hipError_t launch_normal_dispatch_cached_fp8(const void* xq, const void* xs, int
                                              int64_t T, int H, int R, const int32_t* send_row, void* recv_q,
                                              void* recv_s, int64_t cap, hipStream_t stream);
 
+// Load each source file's code object on the current device (the runtime
+// loads a code object on the first use of one of its kernels).
+hipError_t preload_combine();
+hipError_t preload_copy();
+hipError_t preload_dispatch();
+hipError_t preload_fp8();
+hipError_t preload_normal();
+hipError_t preload_layout();
+
 }  // namespace cgd

@@ -346,4 +346,9 @@ hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int
     return hipGetLastError();
 }
 
+hipError_t preload_layout() {
+    hipFuncAttributes a;
+    return hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&layout_acc_kernel<1, kLayoutAccTile>));
+}
+
 }  // namespace cgd

@@ -496,4 +496,9 @@ hipError_t launch_normal_combine(const void* expert_out, int64_t rows, int H, co
     return hipGetLastError();
 }
 
+hipError_t preload_normal() {
+    hipFuncAttributes a;
+    return hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&normal_plan_kernel));
+}
+
 }  // namespace cgd

@@ -65,6 +65,15 @@ typedef enum {
 /* Library version string (host pointer, static storage). */
 const char* cgd_version(void);
 
+/* Loads libcgd's GPU code on the calling thread's current device ahead of
+ * use (the first-call latency page: a process's first dispatch is far slower
+ * than later ones, part of it one-time loading). The runtime otherwise loads
+ * each of libcgd's code objects on the first launch of one of its kernels,
+ * inside that first call. Host only: allocates nothing, enqueues nothing.
+ * Optional; call once per device. Returns CGD_ERR_HIP if the code cannot be
+ * loaded on this device. */
+int cgd_init(void);
+
 /* Message for the last non-OK status returned on the calling thread
  * (host pointer, valid until the next call on that thread). */
 const char* cgd_last_error(void);

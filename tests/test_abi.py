@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
         "cgd_normal_dispatch_apply_fp8", "cgd_normal_dispatch_cached_fp8", "cgd_packed_workspace_bytes",
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
         "cgd_layout_and_dispatch", "cgd_empty", "cgd_layout_and_dispatch_noalloc",
-        "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan",
+        "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan", "cgd_init",
     ])
 
 

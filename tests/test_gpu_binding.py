@@ -168,3 +168,17 @@ def test_outgrown_workspace_stays_valid_for_a_captured_graph():
         np.testing.assert_array_equal(plan.handle.dst_row.cpu().numpy(), want["dst_row"])
         np.testing.assert_array_equal(plan.handle.expert_offset.cpu().numpy(), want["expert_offset"])
         np.testing.assert_array_equal(plan.handle.recv_src_idx.cpu().numpy(), want["recv_src_idx"])
+
+
+def test_init_loads_the_code_ahead_of_the_first_call():
+    say("cgd_init twice, then a layout against the oracle")
+    cgd.init(DEV)
+    cgd.init(DEV)
+    w = synth.WORKLOADS["tiny"]
+    idx_np = synth.make_topk_idx(w, seed=4)
+    ntpr, _, ntpe, itr, _ = cgd.get_dispatch_layout(dev_i64(idx_np), w.E, w.R)
+    torch.cuda.synchronize()
+    o_ntpr, o_ntpe, o_itr = oracle.layout(idx_np, w.E, w.R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), o_ntpr)
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), o_ntpe)
+    np.testing.assert_array_equal(itr.cpu().numpy(), o_itr)
