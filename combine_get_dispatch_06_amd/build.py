@@ -31,10 +31,11 @@ HIPCC_FLAGS = [
 # checks. It is built beside libcgd.so by the package's build step.
 GEOMETRY_LIB = os.path.join(PKG, "libcgd_geometry.so")
 GEOMETRY_FLAGS = [
-    "-DCGD_COMBINE_WAVES=2", "-DCGD_COMBINE_U=2", "-DCGD_COMBINE_LDS_CAP=16384",
+    "-DCGD_COMBINE_WAVES=2", "-DCGD_COMBINE_U=2", "-DCGD_COMBINE_LDS_CAP=16384", "-DCGD_COMBINE_LDS_WIDE=40960",
     "-DCGD_PREFETCH_BLOCKS=0", "-DCGD_ROW_SLOTS=1", "-DCGD_LAYOUT_TILE=128", "-DCGD_DIRECT_TOPK=0",
     "-DCGD_CAST_CPL=8", "-DCGD_SCATTER_CAST_U=1",
     "-DCGD_NORMAL_COMBINE_U=1", "-DCGD_NORMAL_COMBINE_WAVES=2", "-DCGD_NORMAL_GATHER=4", "-DCGD_NORMAL_SCATTER_U=2",
+    "-DCGD_NORMAL_COMBINE_LDS_WIDE=24576",
 ]
 
 

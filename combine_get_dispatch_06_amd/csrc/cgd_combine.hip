@@ -8,9 +8,12 @@
 // Work is split into (token, column chunk) items, a chunk being 64*U
 // 16-byte vectors (1 KB per U) of the row, one wave each; blocks start in
 // item order, so the gathers in flight stay close together. Residency is
-// capped at 5 blocks per CU (an LDS reservation): fewer concurrent gathers per
-// CU and many short items measured faster than one long-lived wave per token
-// or full occupancy.
+// capped by an LDS reservation per block: 5 blocks of 4 waves per CU up to
+// top-8, 3 blocks above (each wave then has twice the loads in flight); fewer
+// concurrent gathers per CU and many short items measured faster than one
+// long-lived wave per token or full occupancy. Top-16, hidden 4096 (32768
+// tokens): 758 us at 8-12 waves per CU against 778-781 at 14 and 794 at 20;
+// top-8 at hidden 7168: 88 us at 20 waves against 97 at 12.
 // Lanes 0..K-1 read the token's K rows and weights and broadcast them; each
 // lane then issues its K*U gathered 16-byte loads before any arithmetic,
 // accumulates in fp32 with fused multiply-add in ascending k from +0,
@@ -28,9 +31,13 @@ namespace cgd {
 #define CGD_COMBINE_U 1
 #endif
 // Occupancy cap: each block reserves this much (unused) LDS, so at most
-// 160 KB / CGD_COMBINE_LDS_CAP blocks share a CU (5 at 32 KB).
+// 160 KB / CGD_COMBINE_LDS_CAP blocks share a CU (5 at 32 KB);
+// CGD_COMBINE_LDS_WIDE is the reservation for top-k above 8 (3 at 54000 B).
 #ifndef CGD_COMBINE_LDS_CAP
 #define CGD_COMBINE_LDS_CAP (32 * 1024)
+#endif
+#ifndef CGD_COMBINE_LDS_WIDE
+#define CGD_COMBINE_LDS_WIDE 54000
 #endif
 constexpr int kCombineWaves = CGD_COMBINE_WAVES;  // waves per block
 
@@ -122,11 +129,12 @@ hipError_t launch_combine(const void* expert_out, int64_t cap, int H, const int3
     do {                                                                                                            \
         const int nchunk = (nvec + U * kWave - 1) / (U * kWave);                                                    \
         const int64_t tper = tokens_per_launch(nchunk);                                                             \
+        constexpr unsigned kLds = KM > 8 ? CGD_COMBINE_LDS_WIDE : CGD_COMBINE_LDS_CAP;                              \
         for (int64_t t0 = 0; t0 < T; t0 += tper) {                                                                  \
             const int64_t nt = T - t0 < tper ? T - t0 : tper;                                                       \
             const int64_t blocks = (nt * nchunk + kCombineWaves - 1) / kCombineWaves;                               \
             const dim3 grid((unsigned)blocks), block(kCombineWaves * kWave);                                        \
-            hipLaunchKernelGGL((combine_kernel<KM, U>), grid, block, CGD_COMBINE_LDS_CAP, stream, yv, cap, nvec,    \
+            hipLaunchKernelGGL((combine_kernel<KM, U>), grid, block, kLds, stream, yv, cap, nvec,                   \
                                nchunk, dst_row + t0 * K, w + t0 * K, nt, K, ov + t0 * nvec);                         \
         }                                                                                                           \
     } while (0)

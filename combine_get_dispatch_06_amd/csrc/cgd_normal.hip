@@ -35,6 +35,9 @@ namespace cgd {
 #ifndef CGD_NORMAL_COMBINE_LDS
 #define CGD_NORMAL_COMBINE_LDS (32 * 1024)
 #endif
+#ifndef CGD_NORMAL_COMBINE_LDS_WIDE
+#define CGD_NORMAL_COMBINE_LDS_WIDE 54000
+#endif
 #ifndef CGD_NORMAL_COMBINE_U
 #define CGD_NORMAL_COMBINE_U 2
 #endif
@@ -53,8 +56,13 @@ constexpr int kTileBatch = 16;                               // tile counts in f
 constexpr int kNormScatterWaves = 4;                         // waves per scatter block
 constexpr int kNormCombineWaves = CGD_NORMAL_COMBINE_WAVES;  // waves per combine block
 constexpr int kGatherBatch = CGD_NORMAL_GATHER;              // rows in flight per combine wave
-// Occupancy cap of the combine: an LDS reservation per block.
+// Occupancy cap of the combine: an LDS reservation per block, 5 blocks per CU
+// while a token has at most one gather batch of rows (min(K, R) <= 8), 3
+// blocks above, where each wave keeps more rows in flight (top-16 over 64
+// ranks: 703.5-703.9 us against 732.3-732.7 with 5 blocks; with 8 rows,
+// prefill: 61.1 against 66.5).
 constexpr size_t kNormCombineLds = CGD_NORMAL_COMBINE_LDS;
+constexpr size_t kNormCombineLdsWide = CGD_NORMAL_COMBINE_LDS_WIDE;
 
 // Normal workspace: ticket | group words u64 [G, R] | group bases int32 [G, R]
 // | tile counts, then tile bases, int32 [tiles, R]; G = ceil(T / 64).
@@ -483,13 +491,14 @@ hipError_t launch_normal_combine(const void* expert_out, int64_t rows, int H, co
     const int nvec = H / 8;
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t tper = tokens_per_launch(nchunk);
+    const size_t lds = (K < R ? K : R) > kGatherBatch ? kNormCombineLdsWide : kNormCombineLds;
     for (int64_t t0 = 0; t0 < T; t0 += tper) {  // token ranges; the kernel indexes tokens relative to its pointers
         const int64_t nt = T - t0 < tper ? T - t0 : tper;
         const int64_t blocks = (nt * nchunk + kNormCombineWaves - 1) / kNormCombineWaves;
         const uint4* b0 = bias0 ? reinterpret_cast<const uint4*>(bias0) + t0 * nvec : nullptr;
         const uint4* b1 = bias1 ? reinterpret_cast<const uint4*>(bias1) + t0 * nvec : nullptr;
         hipLaunchKernelGGL((normal_combine_kernel<U>), dim3((unsigned)blocks), dim3(kNormCombineWaves * kWave),
-                           kNormCombineLds, stream, reinterpret_cast<const uint4*>(expert_out), rows, nvec, nchunk,
+                           lds, stream, reinterpret_cast<const uint4*>(expert_out), rows, nvec, nchunk,
                            send_row + t0 * R, R, nt, recv_w, K, b0, b1, reinterpret_cast<uint4*>(out) + t0 * nvec,
                            out_w ? out_w + t0 * K : nullptr);
     }
