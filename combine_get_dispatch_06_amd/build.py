@@ -35,7 +35,8 @@ GEOMETRY_FLAGS = [
     "-DCGD_PREFETCH_BLOCKS=0", "-DCGD_ROW_SLOTS=1", "-DCGD_LAYOUT_TILE=128", "-DCGD_DIRECT_TOPK=0",
     "-DCGD_CAST_CPL=8", "-DCGD_SCATTER_CAST_U=1",
     "-DCGD_NORMAL_COMBINE_U=1", "-DCGD_NORMAL_COMBINE_WAVES=2", "-DCGD_NORMAL_GATHER=4", "-DCGD_NORMAL_SCATTER_U=2",
-    "-DCGD_NORMAL_COMBINE_LDS_WIDE=24576",
+    "-DCGD_NORMAL_COMBINE_LDS_WIDE=24576", "-DCGD_ROW_COPY_PF_WAVES=8", "-DCGD_ROW_COPY_PF_LDS=0",
+    "-DCGD_ROW_COPY_PF_LDS_WIDE=40960",
 ]
 
 

@@ -240,7 +240,7 @@ int cgd_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* t
                                     expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
                                     stream, x, num_tokens * (int64_t)hidden * 2);
     if (err != hipSuccess) return hip_fail(err, "dispatch plan launch");
-    err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
+    err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream, true);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
     return CGD_OK;
 }
@@ -279,7 +279,7 @@ static int layout_and_dispatch_launches(const void* x, int64_t num_tokens, int h
                                       expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
                                       stream, x, num_tokens * (int64_t)hidden * 2);
     if (err != hipSuccess) return hip_fail(err, "layout and dispatch plan launch");
-    err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream);
+    err = cgd::launch_dispatch_cached(x, num_tokens, hidden, num_topk, dst_row, recv_x, recv_capacity, stream, true);
     if (err != hipSuccess) return hip_fail(err, "dispatch row copy launch");
     return CGD_OK;
 }

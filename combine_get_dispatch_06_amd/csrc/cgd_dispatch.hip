@@ -821,16 +821,36 @@ constexpr int kRowCopyMaxTopk = 8;  // above: 2 KB chunks, 4 waves per block
 #endif
 constexpr int kRowSlots = CGD_ROW_SLOTS;  // slots per wave of the row copy
 
+// The row copy that follows a plan launch which pulled x toward the caches
+// (the non-cached dispatch) runs fewer waves per CU: x then arrives from the
+// Infinity Cache, so fewer stores in flight keep up, and HBM sees fewer
+// concurrent destination streams. Blocks of CGD_ROW_COPY_PF_WAVES waves with
+// an LDS reservation of CGD_ROW_COPY_PF_LDS bytes each (5 blocks of 4 waves
+// per CU), CGD_ROW_COPY_PF_LDS_WIDE above top-8 (6 blocks of 4). Whole
+// dispatch (plan + rows), inputs rotating, us: prefill 103.3 against 107.6
+// with the cached copy's 2 blocks of 16 waves, Zipf-skewed 191.2 against
+// 199.2, top-16 888 against 897. The cached copy (x from HBM) keeps its
+// shape: there the same change costs 120 against 98.7 us at prefill.
+#ifndef CGD_ROW_COPY_PF_WAVES
+#define CGD_ROW_COPY_PF_WAVES 4
+#endif
+#ifndef CGD_ROW_COPY_PF_LDS
+#define CGD_ROW_COPY_PF_LDS 32768
+#endif
+#ifndef CGD_ROW_COPY_PF_LDS_WIDE
+#define CGD_ROW_COPY_PF_LDS_WIDE 27000
+#endif
+
 template <int S, int U, int WPB>
 static void launch_row_copy(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* dst_row,
-                            int64_t cap, void* recv_x, const SideRows& side) {
+                            int64_t cap, void* recv_x, const SideRows& side, size_t lds = 0) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t per = (int64_t)nchunk * ((K + S - 1) / S);  // waves per token
     const int64_t tper = tokens_per_launch(per);
     for (int64_t t0 = 0; t0 < T; t0 += tper) {
         const int64_t nt = std::min<int64_t>(tper, T - t0);
         const int64_t blocks = (nt * per + WPB - 1) / WPB;
-        hipLaunchKernelGGL((scatter_kernel<S, U, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), 0, s,
+        hipLaunchKernelGGL((scatter_kernel<S, U, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), lds, s,
                            reinterpret_cast<const uint4*>(x), t0, t0 + nt, nvec, nchunk, K, dst_row, cap,
                            reinterpret_cast<uint4*>(recv_x), side);
     }
@@ -863,15 +883,20 @@ static void launch_bcast_u(int64_t T, int K, hipStream_t s, const void* x, int n
 }
 
 // Rows moved to the final rows of a handle (the apply of a plan, cached
-// dispatch, the packed dispatch): the row copy for larger batches, the
-// broadcast kernel for small ones and for top-k above 8.
+// dispatch, the packed dispatch): the row copy for larger batches (2 KB
+// chunks in blocks of 4 waves above top-8), the broadcast kernel for small
+// ones. after_plan: the copy follows a plan launch that prefetched x.
 static void launch_scatter(int64_t T, int K, hipStream_t s, const void* x, int nvec, const int32_t* dst_row,
-                           int64_t cap, void* recv_x, const SideRows& side) {
+                           int64_t cap, void* recv_x, const SideRows& side, bool after_plan = false) {
     if (T <= 0) return;
     if (T * K < kRowCopyMinSlots)
         launch_bcast_u<1>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
     else if (K > kRowCopyMaxTopk)
-        launch_row_copy<kRowSlots, 2, 4>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
+        launch_row_copy<kRowSlots, 2, 4>(T, K, s, x, nvec, dst_row, cap, recv_x, side,
+                                         after_plan ? CGD_ROW_COPY_PF_LDS_WIDE : 0);
+    else if (after_plan)
+        launch_row_copy<kRowSlots, 1, CGD_ROW_COPY_PF_WAVES>(T, K, s, x, nvec, dst_row, cap, recv_x, side,
+                                                              CGD_ROW_COPY_PF_LDS);
     else
         launch_row_copy<kRowSlots, 1, kSlotWaves>(T, K, s, x, nvec, dst_row, cap, recv_x, side);
 }
@@ -1111,16 +1136,16 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
                                  recv_src_info, packed_count, stats, w, stream, nullptr, x, T * (int64_t)H * 2);
     if (err != hipSuccess) return err;
     if (fmt < 0)
-        launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side());
+        launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side(), true);
     else
         launch_scatter_cast(x, T, H, K, fmt, dst_row, cap, recv_x, recv_s, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
-                                  int64_t cap, hipStream_t stream) {
+                                  int64_t cap, hipStream_t stream, bool after_plan) {
     if (T <= 0) return hipSuccess;  // nothing to enqueue
-    launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side());
+    launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side(), after_plan);
     return hipGetLastError();
 }
 

@@ -83,8 +83,10 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
                                   int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
                                   hipStream_t stream);
 
+// after_plan: the rows follow a plan launch that pulled x toward the caches
+// (the non-cached dispatch), which takes another launch shape.
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,
-                                  int64_t cap, hipStream_t stream);
+                                  int64_t cap, hipStream_t stream, bool after_plan = false);
 
 hipError_t launch_combine(const void* expert_out, int64_t cap, int H, const int32_t* dst_row, const float* w,
                           int64_t T, int K, void* out, hipStream_t stream);
