@@ -36,7 +36,7 @@ GEOMETRY_FLAGS = [
     "-DCGD_CAST_CPL=8", "-DCGD_SCATTER_CAST_U=1",
     "-DCGD_NORMAL_COMBINE_U=1", "-DCGD_NORMAL_COMBINE_WAVES=2", "-DCGD_NORMAL_GATHER=4", "-DCGD_NORMAL_SCATTER_U=2",
     "-DCGD_NORMAL_COMBINE_LDS_WIDE=24576", "-DCGD_ROW_COPY_PF_WAVES=8", "-DCGD_ROW_COPY_PF_LDS=0",
-    "-DCGD_ROW_COPY_PF_LDS_WIDE=40960",
+    "-DCGD_ROW_COPY_PF_LDS_WIDE=40960", "-DCGD_SCATTER_CAST_LDS=0",
 ]
 
 
