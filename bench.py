@@ -157,8 +157,8 @@ class ExpertPath(_Path):
     the plan and the rows; one launch for a batch of at most one 256-token
     tile, such as decode), then combine. The split step makes the same calls
     separately: layout + plan (layout_and_dispatch_plan), the row movement
-    alone (dispatch_apply, i.e. the cached dispatch), combine. FP8: layout +
-    plan, the cast on dispatch, combine."""
+    alone (dispatch_apply, i.e. the cached dispatch), combine. FP8: the same
+    with the cast on dispatch (layout_and_dispatch with cast_fp8)."""
 
     def __init__(self, w, sets, dev, fmt):
         import torch
@@ -175,12 +175,8 @@ class ExpertPath(_Path):
                                        device=dev))
         self.one_launch = fmt is None and w.T <= 256
         self.split_labels = ("layout_and_plan", "dispatch_apply", "combine")
-        if fmt is None:
-            self.labels = ("dispatch", "combine")
-            self.dispatch_labels = ("dispatch",)
-        else:
-            self.labels = self.split_labels
-            self.dispatch_labels = ("layout_and_plan", "dispatch_apply")
+        self.labels = ("dispatch", "combine")
+        self.dispatch_labels = ("dispatch",)
         self.apply_label = "dispatch_apply"
         # roofline candidates: the longest single kernel (the one-launch
         # dispatch of a decode batch, else the row movement alone) or combine
@@ -190,12 +186,9 @@ class ExpertPath(_Path):
         self.handles = [None] * len(sets)
 
     def step(self, i, ev=None):
-        if self.fmt is not None:
-            return self.split_step(i, ev)
         cgd, w = self.cgd, self.w
         self._rec(ev, 0)
-        _, _, _, h = cgd.layout_and_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_alignment=w.align,
-                                             recv_x=self.recv_x)
+        _, _, _, h = self._dispatch(i)
         self._rec(ev, 1)
         cgd.combine(self.recv_x, h, self.wt[i], out=self.out)
         self._rec(ev, 2)
@@ -220,8 +213,8 @@ class ExpertPath(_Path):
         if self.fmt is None:
             return cgd.layout_and_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_alignment=w.align,
                                            recv_x=self.recv_x)
-        _, plan = cgd.layout_and_dispatch_plan(self.idx[i], w.E, w.R, expert_alignment=w.align)
-        return cgd.dispatch_apply(self.x[i], plan, recv_x=self.recv_q, cast_fp8=self.fmt)
+        return cgd.layout_and_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_alignment=w.align,
+                                       recv_x=self.recv_q, cast_fp8=self.fmt)
 
     def _apply(self, i):
         # the cached dispatch: the handle's rows alone (dispatch_apply's kernels)
@@ -262,7 +255,8 @@ class ExpertPath(_Path):
         return {"dispatch": ("layout_and_dispatch (one launch: layout + plan + rows)" if self.one_launch else
                              "layout_and_dispatch (layout + plan with x pulled toward the caches, then the rows)"
                              if self.fmt is None else
-                             "layout + plan (layout_and_dispatch_plan), then the cast on dispatch (dispatch_apply)"),
+                             "layout_and_dispatch with the cast (layout + plan with x pulled toward the caches, "
+                             "then the cast on dispatch)"),
                 "split": "layout_and_dispatch_plan, then dispatch_apply (the cached dispatch: rows alone)",
                 "experts": "identity (combine reads dispatched rows)" if self.fmt is None else
                 "identity (combine reads the cast-back FP8 rows, made before timing)"}

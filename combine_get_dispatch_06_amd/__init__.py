@@ -149,6 +149,12 @@ def configure(lib):
     lib.cgd_cast_back.argtypes = [vp, vp, i64, i64, i32, i64, i32, vp, vp]
     lib.cgd_dispatch_cached_cast_fp8.restype = i32
     lib.cgd_dispatch_cached_cast_fp8.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, i64, vp]
+    lib.cgd_dispatch_cast_fp8.restype = i32
+    lib.cgd_dispatch_cast_fp8.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp, vp, vp, vp,
+                                          sz, vp]
+    lib.cgd_layout_and_dispatch_cast_fp8.restype = i32
+    lib.cgd_layout_and_dispatch_cast_fp8.argtypes = [vp, i64, i32, vp, i32, i32, i32, i32, i32, vp, vp, i64, vp, vp,
+                                                     vp, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_cached_fp8.restype = i32
     lib.cgd_dispatch_cached_fp8.argtypes = [vp, vp, i64, i64, i32, i64, i32, i32, vp, vp, vp, i64, vp]
     lib.cgd_normal_dispatch_apply_fp8.restype = i32
@@ -455,7 +461,13 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
         _dev_tensor(x, "x", torch.bfloat16, 2)
         T, H = x.shape
         dev = x.device
-    if handle is None and (fp8 or cast_fp8 is not None):
+    if handle is None and cast_fp8 is not None:
+        if topk_idx is None or num_experts is None or num_ranks is None:
+            raise ValueError("non-cached dispatch needs topk_idx, num_experts and num_ranks")
+        _, recv_x, nre, h = _dispatch_cast(x, topk_idx, num_experts, num_ranks, expert_alignment, recv_capacity,
+                                           recv_x, cast_fp8, layout=False)
+        return recv_x, nre, h
+    if handle is None and fp8:
         if topk_idx is None or num_experts is None or num_ranks is None:
             raise ValueError("non-cached dispatch needs topk_idx, num_experts and num_ranks")
         if recv_x is not None:  # checked before the plan is enqueued
@@ -463,9 +475,9 @@ def dispatch(x, topk_idx: torch.Tensor | None = None, num_experts: int | None = 
             cap = recv_capacity
             if cap is None:
                 cap = int(lib.cgd_dispatch_capacity(T, topk_idx.shape[1], num_experts, expert_alignment))
-            _recv_fp8(recv_x, cap, H, fmt if fp8 else cast_fp8, dev)
+            _recv_fp8(recv_x, cap, H, fmt, dev)
         plan = dispatch_plan(topk_idx, num_experts, num_ranks, expert_alignment, recv_capacity)
-        return dispatch_apply(x, plan, recv_x=recv_x, cast_fp8=cast_fp8)
+        return dispatch_apply(x, plan, recv_x=recv_x)
     with torch.cuda.device(dev):
         if handle is not None:
             if topk_idx is not None:
@@ -583,12 +595,60 @@ def layout_and_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, num_ranks
     return (ntpr, None, ntpe, itr, None), DispatchPlan(h, ws, T)
 
 
+def _dispatch_cast(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int, expert_alignment: int,
+                   recv_capacity: int | None, recv_x, fmt: int, layout: bool):
+    """The non-cached cast on dispatch (cgd_dispatch_cast_fp8, or with the
+    layout outputs cgd_layout_and_dispatch_cast_fp8): bf16 x in, the FP8
+    tuple out. -> (layout tuple or None, recv_x, num_recv_tokens_per_expert,
+    DispatchHandle)."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, H = x.shape
+    dev = x.device
+    if topk_idx.shape[0] != T or topk_idx.device != dev:
+        raise ValueError("topk_idx must be [num_tokens, num_topk] on x's device")
+    K = topk_idx.shape[1]
+    with torch.cuda.device(dev):
+        need = int(lib.cgd_dispatch_capacity(T, K, num_experts, expert_alignment))
+        cap = need if recv_capacity is None else int(recv_capacity)
+        recv_x = _recv_fp8(recv_x, max(cap, 0), H, fmt, dev)
+        off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        dst = torch.empty((T, K), dtype=torch.int32, device=dev)
+        ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, num_experts, num_ranks))
+        lay = None
+        if layout:
+            ntpr = torch.empty(num_ranks, dtype=torch.int32, device=dev)
+            ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
+            itr = torch.empty((T, num_ranks), dtype=torch.bool, device=dev)
+            _check("cgd_layout_and_dispatch_cast_fp8",
+                   lib.cgd_layout_and_dispatch_cast_fp8(_ptr(x), T, H, _ptr(topk_idx), K, num_experts, num_ranks,
+                                                        expert_alignment, fmt, _ptr(recv_x[0]), _ptr(recv_x[1]), cap,
+                                                        _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(nre),
+                                                        _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+            lay = (ntpr, None, ntpe, itr, None)
+        else:
+            _check("cgd_dispatch_cast_fp8",
+                   lib.cgd_dispatch_cast_fp8(_ptr(x), T, H, _ptr(topk_idx), K, num_experts, num_ranks,
+                                             expert_alignment, fmt, _ptr(recv_x[0]), _ptr(recv_x[1]), cap, _ptr(off),
+                                             _ptr(nre), _ptr(src), _ptr(dst), _ptr(ws), ws.numel(), _stream(dev)))
+    h = DispatchHandle(off, src, dst, nre, num_experts, num_ranks, expert_alignment, cap)
+    return lay, recv_x, nre, h
+
+
 def layout_and_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
-                        expert_alignment: int = 1, recv_capacity: int | None = None, recv_x: torch.Tensor | None = None):
+                        expert_alignment: int = 1, recv_capacity: int | None = None, recv_x=None,
+                        cast_fp8: int | None = None):
     """get_dispatch_layout and dispatch (bf16 x) in one call; a batch of at most
-    256 tokens takes one launch.
+    256 tokens takes one launch. cast_fp8 (a scale format) casts x to FP8 on
+    the way: recv_x is then the (codes, scales) tuple.
     -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), recv_x,
         num_recv_tokens_per_expert, DispatchHandle)."""
+    if cast_fp8 is not None:
+        return _dispatch_cast(x, topk_idx, num_experts, num_ranks, expert_alignment, recv_capacity, recv_x, cast_fp8,
+                              layout=True)
     lib = load()
     _dev_tensor(x, "x", torch.bfloat16, 2)
     _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)

@@ -612,6 +612,58 @@ int cgd_dispatch_cached_cast_fp8(const void* x, int64_t num_tokens, int hidden, 
     return CGD_OK;
 }
 
+// Checks of a cast-on-dispatch payload: bf16 x in, FP8 rows and scales out.
+static int check_cast_rows(const void* x, int64_t T, int H, int fmt, int64_t cap, const void* recv_q,
+                           const void* recv_s) {
+    int rc = check_fp8(H, fmt);
+    if (rc) return rc;
+    if (T > 0 && !x) return fail(CGD_ERR_INVALID_ARG, "null x");
+    if (cap > 0 && !recv_q) return fail(CGD_ERR_INVALID_ARG, "null recv_x_fp8");
+    if (!aligned(x, 16) || !aligned(recv_q, 16))
+        return fail(CGD_ERR_INVALID_ARG, "x and recv_x_fp8 must be 16-byte aligned");
+    return check_scales(recv_s, 0, 0, fmt, T > 0 && cap > 0);
+}
+
+int cgd_dispatch_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                          int num_experts, int num_ranks, int expert_alignment, int scale_format, void* recv_x_fp8,
+                          void* recv_scales, int64_t recv_capacity, int32_t* expert_offset,
+                          int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
+                             expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                             workspace_bytes);
+    if (rc) return rc;
+    if ((rc = check_cast_rows(x, num_tokens, hidden, scale_format, recv_capacity, recv_x_fp8, recv_scales))) return rc;
+    hipError_t err = cgd::launch_dispatch_cast_fp8(x, num_tokens, hidden, topk_idx, num_topk, num_experts,
+                                                   expert_alignment, scale_format, recv_x_fp8, recv_scales,
+                                                   recv_capacity, expert_offset, num_recv_tokens_per_expert,
+                                                   recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "FP8 cast dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_layout_and_dispatch_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                     int num_topk, int num_experts, int num_ranks, int expert_alignment,
+                                     int scale_format, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                     int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                     uint8_t* is_token_in_rank, int32_t* expert_offset,
+                                     int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks, expert_alignment, recv_capacity,
+                             expert_offset, num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace,
+                             workspace_bytes);
+    if (rc) return rc;
+    if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
+        return rc;
+    if ((rc = check_cast_rows(x, num_tokens, hidden, scale_format, recv_capacity, recv_x_fp8, recv_scales))) return rc;
+    hipError_t err = cgd::launch_layout_and_dispatch_cast_fp8(
+        x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks, expert_alignment, scale_format, recv_x_fp8,
+        recv_scales, recv_capacity, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, expert_offset,
+        num_recv_tokens_per_expert, recv_src_idx, dst_row, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "layout and FP8 cast dispatch launch");
+    return CGD_OK;
+}
+
 int cgd_dispatch_cached_fp8(const void* x_fp8, const void* x_scales, int64_t scale_stride_token,
                             int64_t scale_stride_block, int scale_format, int64_t num_tokens, int hidden, int num_topk,
                             const int32_t* dst_row, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,

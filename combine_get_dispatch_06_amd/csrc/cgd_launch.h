@@ -126,6 +126,19 @@ hipError_t launch_cast_back(const void* q, const void* scales, int64_t st, int64
 hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int K, int fmt, const int32_t* dst_row,
                                            void* recv_q, void* recv_s, int64_t cap, hipStream_t stream);
 
+// The non-cached cast on dispatch: the plan (its spare blocks pull x toward
+// the caches), then the cast to the plan's rows; the second form also writes
+// get_dispatch_layout's outputs from the plan's pass over the routing.
+hipError_t launch_dispatch_cast_fp8(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
+                                    int fmt, void* recv_q, void* recv_s, int64_t cap, int32_t* expert_offset,
+                                    int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row, void* workspace,
+                                    hipStream_t stream);
+hipError_t launch_layout_and_dispatch_cast_fp8(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                               int R, int A, int fmt, void* recv_q, void* recv_s, int64_t cap,
+                                               int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* expert_offset,
+                                               int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row,
+                                               void* workspace, hipStream_t stream);
+
 hipError_t launch_dispatch_cached_fp8(const void* xq, const void* xs, int64_t st, int64_t sb, int fmt, int64_t T,
                                       int H, int K, const int32_t* dst_row, void* recv_q, void* recv_s, int64_t cap,
                                       hipStream_t stream);

@@ -377,6 +377,37 @@ int cgd_dispatch_cached_cast_fp8(const void* x, int64_t num_tokens, int hidden, 
                                  const int32_t* dst_row, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
                                  hipStream_t stream);
 
+/* Non-cached dispatch that casts on the way (the dispatch of the "Dispatch
+ * API" section of the Python interface notes with an FP8 payload, as the
+ * low-latency dispatch with FP8 casts it): the plan of cgd_dispatch_plan
+ * followed by the cast of cgd_dispatch_cached_cast_fp8 to the plan's rows, in
+ * one call, so that the plan's idle compute units pull x into the caches
+ * while it runs and the cast reads it from there. Arguments, outputs and
+ * errors as cgd_dispatch, except: scale_format is 0 (fp32 amax/448), 1 (fp32
+ * power of two) or 2 (UE8M0 byte); hidden must be a positive multiple of 128;
+ * the rows go to recv_x_fp8 (uint8 e4m3fn codes [recv_capacity, hidden],
+ * 16-byte aligned) and recv_scales ([recv_capacity, hidden/128], fp32 or one
+ * byte for format 2), written for rows with data only; x is bf16 [num_tokens,
+ * hidden]. The handle (expert_offset, recv_src_idx, dst_row) and
+ * num_recv_tokens_per_expert are those of cgd_dispatch. */
+int cgd_dispatch_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx, int num_topk,
+                          int num_experts, int num_ranks, int expert_alignment, int scale_format, void* recv_x_fp8,
+                          void* recv_scales, int64_t recv_capacity, int32_t* expert_offset,
+                          int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* cgd_get_dispatch_layout and cgd_dispatch_cast_fp8 in one call: the layout
+ * outputs (as cgd_get_dispatch_layout; no layout workspace is needed) come
+ * from the plan's pass over the routing, as in cgd_layout_and_dispatch_plan;
+ * everything else as cgd_dispatch_cast_fp8. */
+int cgd_layout_and_dispatch_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                     int num_topk, int num_experts, int num_ranks, int expert_alignment,
+                                     int scale_format, void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                     int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                     uint8_t* is_token_in_rank, int32_t* expert_offset,
+                                     int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* dst_row,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Cached dispatch of the FP8 tuple with a dst_row from an earlier dispatch
  * or cgd_dispatch_plan: rows of H code bytes and the rows' scales move to
  * recv_x_fp8 [recv_capacity, H], recv_scales [recv_capacity, H/128]. */

@@ -32,6 +32,7 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
         "cgd_layout_and_dispatch", "cgd_empty", "cgd_layout_and_dispatch_noalloc",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan", "cgd_init",
+        "cgd_dispatch_cast_fp8", "cgd_layout_and_dispatch_cast_fp8",
     ])
 
 
@@ -376,6 +377,45 @@ def test_layout_and_dispatch_rejects_bad_arguments():
     assert lib.cgd_layout_and_dispatch(_vp(FAKE + 8), 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, f,
                                        1 << 20, None) == -1
     assert lib.cgd_layout_and_dispatch(f, 64, 128, f, 4, 16, 4, 1, f, 256, f, f, f, f, f, f, f, None, 0, None) == -3
+    assert lib.cgd_last_error()
+
+
+def test_cast_dispatch_entry_points_reject_bad_arguments():
+    lib = cgd.load()
+    ok = dict(x=FAKE, T=64, H=256, idx=FAKE, K=4, E=16, R=4, A=1, fmt=0, rq=FAKE, rs=FAKE, cap=256, ntpr=FAKE,
+              ntpe=FAKE, itr=FAKE, off=FAKE, nre=FAKE, src=FAKE, dst=FAKE, ws=FAKE, wsb=1 << 20)
+    v = lambda a: _vp(a) if a else None
+
+    def plain(**kw):
+        a = dict(ok, **kw)
+        return lib.cgd_dispatch_cast_fp8(v(a["x"]), a["T"], a["H"], v(a["idx"]), a["K"], a["E"], a["R"], a["A"],
+                                         a["fmt"], v(a["rq"]), v(a["rs"]), a["cap"], v(a["off"]), v(a["nre"]),
+                                         v(a["src"]), v(a["dst"]), v(a["ws"]), a["wsb"], None)
+
+    def with_layout(**kw):
+        a = dict(ok, **kw)
+        return lib.cgd_layout_and_dispatch_cast_fp8(v(a["x"]), a["T"], a["H"], v(a["idx"]), a["K"], a["E"], a["R"],
+                                                    a["A"], a["fmt"], v(a["rq"]), v(a["rs"]), a["cap"], v(a["ntpr"]),
+                                                    v(a["ntpe"]), v(a["itr"]), v(a["off"]), v(a["nre"]), v(a["src"]),
+                                                    v(a["dst"]), v(a["ws"]), a["wsb"], None)
+
+    for call in (plain, with_layout):
+        assert call(H=200) == -1            # FP8 rows need hidden % 128 == 0
+        assert call(fmt=3) == -1            # scale format
+        assert call(rs=0) == -1             # missing scales
+        assert call(fmt=0, rs=FAKE + 2) == -1  # fp32 scales misaligned
+        assert call(rq=FAKE + 8) == -1      # codes not 16-byte aligned
+        assert call(x=FAKE + 8) == -1       # x not 16-byte aligned
+        assert call(x=0) == -1
+        assert call(cap=255) == -2          # capacity below T*K
+        assert call(A=0) == -1
+        assert call(E=15) == -1             # E % R
+        assert call(K=17) == -1
+        assert call(ws=0) == -3             # missing workspace
+        assert call(wsb=16) == -3
+        assert call(nre=FAKE + 2) == -1     # num_recv_tokens_per_expert misaligned
+    assert with_layout(ntpr=0) == -1        # layout outputs
+    assert with_layout(itr=FAKE + 4) == -1
     assert lib.cgd_last_error()
 
 

@@ -215,3 +215,47 @@ def test_fp8_zero_tokens():
     assert recv[0].shape == (16, 256) and recv[1].shape == (16, 2)
     assert (h.recv_src_idx.cpu().numpy() == -1).all()
     assert recv2[0].shape == (16, 256)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,K,E,R,H,A,extra,p_neg", [(100, 8, 256, 8, 1024, 1, 0, 0.0), (2049, 8, 256, 8, 384, 4, 37, 0.1),
+                                                     (1100, 16, 512, 64, 256, 16, 0, 0.0),
+                                                     (4096, 8, 256, 8, 7168, 1, 0, 0.0)])
+def test_layout_and_dispatch_cast_parity(fmt, T, K, E, R, H, A, extra, p_neg):
+    """layout_and_dispatch with the cast on the way (one call: the plan pulls x
+    into the caches, the cast reads it there): layout outputs, handle, aligned
+    counts and every received row's codes and scales as the oracle's; rows
+    without data keep their sentinel bytes."""
+    rng = np.random.default_rng(T + K + A)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    idx[rng.random((T, K)) < p_neg] = -1
+    x = _x(T, H, seed=T + A)
+    cap = cgd.dispatch_capacity(T, K, E, A) + extra
+    rq = torch.full((cap, H), 0xA5, dtype=torch.uint8, device=DEV)
+    rs = torch.full((cap, H // 128), 0x5A, dtype=torch.uint8, device=DEV)
+    if fmt != cgd.SCALE_UE8M0:
+        rs = torch.full((cap, H // 128), -7.0, dtype=torch.float32, device=DEV)
+    say(f"[fp8] layout_and_dispatch cast fmt={fmt} T={T} K={K} E={E} R={R} H={H} A={A}")
+    lay, recv, nre, h = cgd.layout_and_dispatch(dev_bf16(x), dev_i64(idx), E, R, expert_alignment=A,
+                                                recv_capacity=cap, recv_x=(rq, rs), cast_fp8=fmt)
+    torch.cuda.synchronize()
+    ntpr, _, ntpe, itr, _ = lay
+    o_ntpr, o_ntpe, o_itr = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), o_ntpr)
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), o_ntpe)
+    np.testing.assert_array_equal(itr.cpu().numpy(), o_itr)
+    o = oracle.dispatch(None, idx, E, R, align=A, with_rows=False)
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+    src = h.recv_src_idx.cpu().numpy()
+    np.testing.assert_array_equal(src[:len(o["recv_src_idx"])], o["recv_src_idx"])
+    assert (src[len(o["recv_src_idx"]):] == -1).all()
+    np.testing.assert_array_equal(nre.cpu().numpy(), np.diff(o["expert_offset"]))
+    assert recv[0] is rq and recv[1] is rs
+    oq, osc = oracle.cast_to_fp8(x, fmt)
+    _check_rows(recv, oq, osc, o["dst_row"])
+    empty = torch.from_numpy(np.flatnonzero(src < 0)).to(DEV)
+    if empty.numel():
+        assert (rq.index_select(0, empty) == 0xA5).all()
+        sv = rs.index_select(0, empty)
+        assert ((sv == 0x5A) if fmt == cgd.SCALE_UE8M0 else (sv == -7.0)).all()
