@@ -17,7 +17,9 @@
 // one 128-channel block and reduces its absolute max with lane shuffles.
 // Scales are addressed with element strides (st per token, sb per block), so
 // row-major ([T, H/128]: st = H/128, sb = 1) and column-major (st = 1, sb = T)
-// both work.
+// both work. x is read with ordinary loads: prefill cast 17.3 us against 18.6
+// with non-temporal loads (x from HBM), 16.0 against 18.5 with x in the
+// Infinity Cache.
 #include "cgd_device.h"
 #include "cgd_launch.h"
 
@@ -41,8 +43,8 @@ __global__ __launch_bounds__(kCastWaves* kWave) void cast_to_fp8_kernel(const ui
     uint4 a = make_uint4(0, 0, 0, 0), b = a;
     if (in) {
         const uint4* xr = x + (t * nlv + v) * 2;
-        a = load_nt(xr);
-        b = load_nt(xr + 1);
+        a = xr[0];  // ordinary loads: served by the Infinity Cache when x is there
+        b = xr[1];
     }
     const float m = in ? fmaxf(absmax_bf16x8(a), absmax_bf16x8(b)) : 0.0f;
     const Fp8Scale sc = fp8_block_scale(group8_max(m), FMT);
