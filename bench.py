@@ -263,8 +263,11 @@ class ExpertPath(_Path):
 
 
 class NormalPath(_Path):
-    """layout + rank-granular plan (one launch), [FP8 cast,] apply, combine
-    (identity experts, no bias)."""
+    """bf16: layout, rank-granular plan and apply in one call
+    (layout_and_normal_dispatch: the plan pulls x toward the caches for the
+    apply), combine (identity experts, no bias); the split step makes the
+    same calls separately (layout + plan in one launch, the apply). FP8:
+    layout + plan, the per-token cast, the tuple apply, combine."""
     labels = ("layout_and_plan", "cast", "dispatch_apply", "combine")
     dispatch_labels = ("layout_and_plan", "cast", "dispatch_apply")
     apply_label = "dispatch_apply"
@@ -283,9 +286,22 @@ class NormalPath(_Path):
                            torch.empty((cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32,
                                        device=dev))
         self.last = [None] * len(sets)
+        if fmt is None:
+            self.labels = ("dispatch", "combine")
+            self.dispatch_labels = ("dispatch",)
+            self.split_labels = ("layout_and_plan", "dispatch_apply", "combine")
 
     def step(self, i, ev=None):
         cgd, w = self.cgd, self.w
+        if self.fmt is None:
+            self._rec(ev, 0)
+            (_, _, _, itr, _), _, _, rw, _, h = cgd.layout_and_normal_dispatch(
+                self.x[i], self.idx[i], self.wt[i], w.E, w.R, expert_alignment=w.align, recv_x=self.recv_x)
+            self._rec(ev, 1)
+            cgd.normal_combine(self.recv_x, h, rw, out=self.out)
+            self._rec(ev, 2)
+            self.last[i] = (h, itr, rw)
+            return
         self._rec(ev, 0)
         (_, _, _, itr, _), plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R,
                                                                       expert_alignment=w.align)
@@ -302,8 +318,24 @@ class NormalPath(_Path):
         self._rec(ev, 4)
         self.last[i] = (h, itr, rw)
 
+    def split_step(self, i, ev=None):
+        """bf16: the step's work as separate calls (layout + plan, apply, combine)."""
+        cgd, w = self.cgd, self.w
+        self._rec(ev, 0)
+        (_, _, _, itr, _), plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R,
+                                                                      expert_alignment=w.align)
+        self._rec(ev, 1)
+        _, _, rw, _, h = cgd.normal_dispatch_apply(self.x[i], plan, self.idx[i], self.wt[i], recv_x=self.recv_x)
+        self._rec(ev, 2)
+        cgd.normal_combine(self.recv_x, h, rw, out=self.out)
+        self._rec(ev, 3)
+        self.last[i] = (h, itr, rw)
+
     def _dispatch(self, i):
         cgd, w = self.cgd, self.w
+        if self.fmt is None:
+            return cgd.layout_and_normal_dispatch(self.x[i], self.idx[i], self.wt[i], w.E, w.R,
+                                                  expert_alignment=w.align, recv_x=self.recv_x)
         _, plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R, expert_alignment=w.align)
         x = self.x[i] if self.fmt is None else cgd.per_token_cast_to_fp8(self.x[i], self.fmt)
         return cgd.normal_dispatch_apply(x, plan, self.idx[i], self.wt[i],
@@ -357,6 +389,9 @@ class NormalPath(_Path):
 
     def describe(self):
         return {"path": "normal (one row per flagged rank)",
+                "dispatch": ("layout_and_normal_dispatch (layout + rank-granular plan with x pulled toward the "
+                             "caches, then the apply)" if self.fmt is None else
+                             "layout_and_normal_dispatch_plan, per_token_cast_to_fp8, normal_dispatch_apply"),
                 "experts": "identity (combine reads dispatched rows), no bias" if self.fmt is None else
                 "identity (combine reads the cast-back FP8 rows, made before timing), no bias"}
 

@@ -49,7 +49,8 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
            "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_",
            "layout_and_normal_dispatch_plan", "layout_and_dispatch", "normal_workspace_bytes",
-           "layout_and_normal_workspace_bytes", "empty_", "layout_and_dispatch_noalloc", "init"]
+           "layout_and_normal_workspace_bytes", "empty_", "layout_and_dispatch_noalloc", "init",
+           "layout_and_normal_dispatch"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _BUILT_LIB = os.path.join(_PKG, "libcgd.so")
@@ -172,6 +173,9 @@ def configure(lib):
     lib.cgd_empty.argtypes = [vp]
     lib.cgd_layout_and_normal_workspace_bytes.restype = sz
     lib.cgd_layout_and_normal_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.cgd_layout_and_normal_dispatch.restype = i32
+    lib.cgd_layout_and_normal_dispatch.argtypes = [vp, i64, i32, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp,
+                                                   vp, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_layout_and_normal_dispatch_plan.restype = i32
     lib.cgd_layout_and_normal_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     return lib
@@ -980,6 +984,57 @@ def layout_and_normal_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, nu
                                                        expert_alignment, _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off),
                                                        _ptr(nre), _ptr(ws), ws.numel(), _stream(dev)))
     return (ntpr, None, ntpe, itr, None), NormalPlan(off, nre, ws, T, num_experts, _note_plan_write(ws))
+
+
+def layout_and_normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor | None,
+                               num_experts: int, num_ranks: int, expert_alignment: int = 1,
+                               recv_capacity: int | None = None, recv_x: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None):
+    """layout_and_normal_dispatch_plan and normal_dispatch_apply (bf16 x) in one
+    call; the plan pulls x toward the caches for the apply. topk_weights None:
+    no recv_topk_idx / recv_topk_weights.
+    -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), recv_x,
+        recv_topk_idx | None, recv_topk_weights | None, num_recv_tokens_per_expert, NormalHandle)."""
+    lib = load()
+    _dev_tensor(x, "x", torch.bfloat16, 2)
+    _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    dev = x.device
+    if topk_idx.shape[0] != T or topk_idx.device != dev:
+        raise ValueError("topk_idx must be [num_tokens, num_topk] on x's device")
+    if topk_weights is not None:
+        _dev_tensor(topk_weights, "topk_weights", torch.float32, 2)
+        if topk_weights.shape != topk_idx.shape:
+            raise ValueError("topk_weights must be [num_tokens, num_topk]")
+    R = num_ranks
+    with torch.cuda.device(dev):
+        cap = int(lib.cgd_normal_capacity(T, K, R)) if recv_capacity is None else int(recv_capacity)
+        if recv_x is None:
+            recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
+        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+        if recv_x.shape != (cap, H):
+            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        ntpr = torch.empty(R, dtype=torch.int32, device=dev)
+        ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        itr = torch.empty((T, R), dtype=torch.bool, device=dev)
+        off = torch.empty(R + 1, dtype=torch.int32, device=dev)
+        nre = torch.empty(num_experts, dtype=torch.int32, device=dev)
+        src = torch.empty(max(cap, 0), dtype=torch.int32, device=dev)
+        send = torch.empty((T, R), dtype=torch.int32, device=dev)
+        ridx = rw = None
+        if topk_weights is not None:
+            ridx = torch.empty((max(cap, 0), K), dtype=torch.int64, device=dev)
+            rw = torch.empty((max(cap, 0), K), dtype=torch.float32, device=dev)
+        need = int(lib.cgd_layout_and_normal_workspace_bytes(T, K, num_experts, R))
+        ws = _normal_plan_workspace(workspace, max(need, 1), dev, "layout_normal")
+        _check("cgd_layout_and_normal_dispatch",
+               lib.cgd_layout_and_normal_dispatch(_ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K, num_experts,
+                                                  R, expert_alignment, _ptr(recv_x), cap, _ptr(ntpr), _ptr(ntpe),
+                                                  _ptr(itr), _ptr(off), _ptr(nre), _ptr(src), _ptr(send), _ptr(ridx),
+                                                  _ptr(rw), _ptr(ws), ws.numel(), _stream(dev)))
+        _note_plan_write(ws)
+    return (ntpr, None, ntpe, itr, None), recv_x, ridx, rw, nre, NormalHandle(off, src, send, K, cap)
 
 
 def normal_dispatch_apply(x: torch.Tensor, plan: NormalPlan, topk_idx: torch.Tensor | None = None,

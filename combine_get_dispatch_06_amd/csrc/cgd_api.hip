@@ -380,11 +380,14 @@ size_t cgd_layout_and_normal_workspace_bytes(int64_t num_tokens, int num_topk, i
            cgd::layout_partial_bytes(num_tokens, num_experts, num_ranks);
 }
 
-int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
-                                        int num_ranks, int expert_alignment, int32_t* num_tokens_per_rank,
-                                        int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
-                                        int32_t* rank_offset, int32_t* num_recv_tokens_per_expert, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream) {
+// Checks of the layout + rank-granular plan's routing, layout outputs, rank
+// offsets and workspace.
+static int check_layout_and_normal_plan_args(const int64_t* topk_idx, int64_t num_tokens, int num_topk,
+                                             int num_experts, int num_ranks, int expert_alignment,
+                                             const int32_t* num_tokens_per_rank, const int32_t* num_tokens_per_expert,
+                                             const uint8_t* is_token_in_rank, const int32_t* rank_offset,
+                                             const int32_t* num_recv_tokens_per_expert, const void* workspace,
+                                             size_t workspace_bytes) {
     int rc = check_routing_sizes(num_tokens, num_topk, num_experts, num_ranks);
     if (rc) return rc;
     if (expert_alignment < 1) return fail(CGD_ERR_INVALID_ARG, "expert_alignment must be >= 1");
@@ -400,6 +403,19 @@ int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tok
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(CGD_ERR_WORKSPACE, "layout + normal plan workspace needs %zu bytes, 256-byte aligned (got %zu)",
                     need, workspace_bytes);
+    return CGD_OK;
+}
+
+int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tokens, int num_topk, int num_experts,
+                                        int num_ranks, int expert_alignment, int32_t* num_tokens_per_rank,
+                                        int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                        int32_t* rank_offset, int32_t* num_recv_tokens_per_expert, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_layout_and_normal_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                               expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
+                                               is_token_in_rank, rank_offset, num_recv_tokens_per_expert, workspace,
+                                               workspace_bytes);
+    if (rc) return rc;
     hipError_t err = cgd::launch_layout_and_normal_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
                                                         expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
                                                         is_token_in_rank, rank_offset, num_recv_tokens_per_expert,
@@ -472,6 +488,36 @@ int cgd_normal_dispatch_apply(const void* x, int64_t num_tokens, int hidden, con
     hipError_t err = cgd::launch_normal_apply(x, num_tokens, hidden, topk_idx, topk_weights, num_topk, num_experts,
                                               num_ranks, recv_x, recv_capacity, rank_offset, recv_src_idx, send_row,
                                               recv_topk_idx, recv_topk_weights, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal dispatch apply launch");
+    return CGD_OK;
+}
+
+int cgd_layout_and_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                   const float* topk_weights, int num_topk, int num_experts, int num_ranks,
+                                   int expert_alignment, void* recv_x, int64_t recv_capacity,
+                                   int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                   uint8_t* is_token_in_rank, int32_t* rank_offset,
+                                   int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* send_row,
+                                   int64_t* recv_topk_idx, float* recv_topk_weights, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_layout_and_normal_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                               expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
+                                               is_token_in_rank, rank_offset, num_recv_tokens_per_expert, workspace,
+                                               workspace_bytes);
+    if (rc) return rc;
+    if ((rc = check_normal_apply_args(x, num_tokens, hidden, recv_topk_idx ? topk_idx : nullptr, topk_weights,
+                                      num_topk, num_experts, num_ranks, recv_x, recv_capacity, rank_offset,
+                                      recv_src_idx, send_row, recv_topk_idx, recv_topk_weights, workspace,
+                                      workspace_bytes)))
+        return rc;
+    hipError_t err = cgd::launch_layout_and_normal_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                                        expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
+                                                        is_token_in_rank, rank_offset, num_recv_tokens_per_expert,
+                                                        workspace, stream, x, num_tokens * (int64_t)hidden * 2);
+    if (err != hipSuccess) return hip_fail(err, "layout and normal dispatch plan launch");
+    err = cgd::launch_normal_apply(x, num_tokens, hidden, recv_topk_idx ? topk_idx : nullptr, topk_weights, num_topk,
+                                   num_experts, num_ranks, recv_x, recv_capacity, rank_offset, recv_src_idx, send_row,
+                                   recv_topk_idx, recv_topk_weights, workspace, stream);
     if (err != hipSuccess) return hip_fail(err, "normal dispatch apply launch");
     return CGD_OK;
 }

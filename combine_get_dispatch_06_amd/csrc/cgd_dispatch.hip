@@ -145,34 +145,6 @@ struct TileOut {
     uint4* recv_x;
 };
 
-// Blocks of the plan past its tiles pull x toward the caches (L2, Infinity
-// Cache) while the plan runs, so that the row copy that follows finds it
-// there: the plan is latency-bound on a few CUs and leaves the others and
-// the memory bandwidth idle, while a row copy reading x from HBM is bound by
-// that latency. Each thread reads vectors b*BLOCK + tid + j*stride with
-// ordinary loads, kInFlight at a time, and discards them.
-#ifndef CGD_PREFETCH_BLOCKS
-#define CGD_PREFETCH_BLOCKS 240
-#endif
-#ifndef CGD_PREFETCH_IN_FLIGHT
-#define CGD_PREFETCH_IN_FLIGHT 8
-#endif
-constexpr int kPrefetchBlocks = CGD_PREFETCH_BLOCKS;
-template <int BLOCK>
-__device__ __forceinline__ void prefetch_rows(const uint4* __restrict__ p, int64_t n, int b, int nb) {
-    constexpr int kInFlight = CGD_PREFETCH_IN_FLIGHT;
-    const int64_t stride = (int64_t)nb * BLOCK;
-    uint32_t acc = 0;
-    for (int64_t i = (int64_t)b * BLOCK + threadIdx.x; i < n; i += stride * kInFlight) {
-        uint4 v[kInFlight];
-#pragma unroll
-        for (int j = 0; j < kInFlight; ++j) v[j] = (i + j * stride < n) ? p[i + j * stride] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < kInFlight; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
-    }
-    asm volatile("" ::"v"(acc));  // the loaded values are used, so the loads stay
-}
-
 // rank_kernel. Slot loops read the routing from LDS, which keeps the kernel
 // light on registers for any num_topk. seg_cap >= 0 selects the
 // fixed-capacity packed layout: segment e is rows [e*seg_cap, (e+1)*seg_cap)

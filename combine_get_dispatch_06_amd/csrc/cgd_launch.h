@@ -58,9 +58,12 @@ NormalPlanArrays normal_plan_arrays(void* workspace, int64_t T, int R);
 
 // get_dispatch_layout and the rank-granular dispatch plan in one launch; the
 // workspace holds the plan's workspace followed by the layout's.
+// x (optional, x_bytes): the rows the rank-granular apply reads next, pulled
+// toward the caches by blocks past the plan's tiles while the plan runs.
 hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A,
                                          int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
-                                         int32_t* nrecv, void* workspace, hipStream_t stream);
+                                         int32_t* nrecv, void* workspace, hipStream_t stream,
+                                         const void* x = nullptr, int64_t x_bytes = 0);
 
 // The dispatch plan: the handle (expert_offset, recv_src_idx, dst_row) from
 // the routing alone, and (nrecv != nullptr) the aligned segment sizes. x

@@ -45,12 +45,20 @@ struct NormalPlanOut {
     int A;
 };
 
+// Blocks past the first nblk (the tiles) pull px (pvecs 16-byte vectors, the
+// x of the rank-granular apply that follows) toward the caches and take no
+// part in the plan.
 template <int RW, bool NPLAN = false>  // RW: 64-bit words of the rank mask: 1 (R <= 64) or 6 (R <= 384)
 __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K,
                                                              int E, int R, int L, int32_t* __restrict__ ntpr,
                                                              int32_t* __restrict__ ntpe, uint8_t* __restrict__ itr,
                                                              int32_t* __restrict__ partial,
-                                                             unsigned int* __restrict__ ticket, NormalPlanOut np) {
+                                                             unsigned int* __restrict__ ticket, NormalPlanOut np,
+                                                             int nblk, const uint4* __restrict__ px, int64_t pvecs) {
+    if ((int)blockIdx.x >= nblk) {
+        prefetch_rows<kLayoutTile>(px, pvecs, (int)blockIdx.x - nblk, (int)gridDim.x - nblk);
+        return;
+    }
     __shared__ int32_t s_idx[kLayoutTile * kMaxTopk];
     __shared__ uint64_t s_mask[kLayoutTile * RW];
     __shared__ int32_t s_hist[kMaxExperts];
@@ -119,7 +127,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
         }
     }
 
-    if (gridDim.x == 1) {
+    if (nblk == 1) {
         for (int i = tid; i < E; i += kLayoutTile) {
             ntpe[i] = s_hist[i];
             if (NPLAN && np.nrecv) np.nrecv[i] = (s_hist[i] + np.A - 1) / np.A * np.A;
@@ -140,9 +148,8 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     int32_t* mine = partial + (int64_t)blockIdx.x * W;
     for (int i = tid; i < E; i += kLayoutTile) mine[i] = s_hist[i];
     for (int i = tid; i < R; i += kLayoutTile) mine[E + i] = s_rank[i];
-    if (!last_block_done(ticket)) return;
+    if (!last_block_done(ticket, nblk)) return;
 
-    const int nblk = gridDim.x;
     // each thread sums columns tid and tid + 256 (W <= 512 + 384): the loads
     // of both, 16 blocks at a time, are in flight together, so a column count
     // just above the block size costs no second round trip
@@ -325,24 +332,36 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R
     return hipGetLastError();
 }
 
+constexpr int64_t kNormalPrefetchMaxBytes = int64_t(160) << 20;
+
 hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A,
                                          int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
-                                         int32_t* nrecv, void* workspace, hipStream_t stream) {
+                                         int32_t* nrecv, void* workspace, hipStream_t stream, const void* x,
+                                         int64_t x_bytes) {
     // workspace: the rank-granular plan's workspace (its ticket, at offset 0
     // whatever the sizes, is the one this launch takes), then the block
     // partials
     NormalPlanArrays a = normal_plan_arrays(workspace, T, R);
     unsigned int* ticket = a.ticket;
     int32_t* partial = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + normal_workspace_bytes(T, R));
-    const dim3 grid((unsigned)layout_blocks(T)), block(kLayoutTile);
+    const int nblk = (int)layout_blocks(T);
+    const uint4* pv = reinterpret_cast<const uint4*>(x);
+    const int64_t pvecs = x ? x_bytes / 16 : 0;
+    // a one-tile plan prefetches nothing, nor does a plan whose x would not
+    // stay in the Infinity Cache: at top-16 stress (268 MB of x) the
+    // prefetch outlasts the plan and the apply gains nothing (whole dispatch
+    // 869 us against 844 for the two calls), while prefill (59 MB) and
+    // Zipf-skewed (117 MB) gain 7.5 and 9.7 us
+    const int extra = (nblk > 1 && pvecs > 0 && x_bytes <= kNormalPrefetchMaxBytes) ? kPrefetchBlocks : 0;
+    const dim3 grid((unsigned)(nblk + extra)), block(kLayoutTile);
     const NormalPlanOut np{a.grp_bal, a.grp_pre, a.tile_base, rank_offset, nrecv, A};
     const int L = E / R;
     if (R <= 64)
         hipLaunchKernelGGL((layout_kernel<1, true>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
-                           partial, ticket, np);
+                           partial, ticket, np, nblk, pv, pvecs);
     else
         hipLaunchKernelGGL((layout_kernel<6, true>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
-                           partial, ticket, np);
+                           partial, ticket, np, nblk, pv, pvecs);
     return hipGetLastError();
 }
 

@@ -494,6 +494,23 @@ int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tok
                                         int32_t* rank_offset, int32_t* num_recv_tokens_per_expert, void* workspace,
                                         size_t workspace_bytes, hipStream_t stream);
 
+/* cgd_layout_and_normal_dispatch_plan followed by cgd_normal_dispatch_apply
+ * (the normal-mode dispatch of the legacy tests, whose inputs are the layout
+ * outputs) in one call, so that the plan's idle compute units pull x into
+ * the caches while it runs and the apply reads it from there. Arguments,
+ * outputs and errors as those two calls (topk_idx feeds the layout; topk_weights,
+ * recv_topk_idx and recv_topk_weights are all given or all NULL); the
+ * workspace is that of cgd_layout_and_normal_dispatch_plan and afterwards
+ * holds the plan, as there. */
+int cgd_layout_and_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                   const float* topk_weights, int num_topk, int num_experts, int num_ranks,
+                                   int expert_alignment, void* recv_x, int64_t recv_capacity,
+                                   int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                   uint8_t* is_token_in_rank, int32_t* rank_offset,
+                                   int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx, int32_t* send_row,
+                                   int64_t* recv_topk_idx, float* recv_topk_weights, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* -------------------------------------------------------------------------
  * cgd_copy: dst[0, bytes) = src[0, bytes), bitwise.
  * Not an operation of the method: a measured copy ceiling, reported beside

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
         "cgd_dispatch_packed", "cgd_dispatch_packed_cast_fp8", "cgd_layout_and_dispatch_plan", "cgd_copy",
         "cgd_layout_and_dispatch", "cgd_empty", "cgd_layout_and_dispatch_noalloc",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan", "cgd_init",
-        "cgd_dispatch_cast_fp8", "cgd_layout_and_dispatch_cast_fp8",
+        "cgd_dispatch_cast_fp8", "cgd_layout_and_dispatch_cast_fp8", "cgd_layout_and_normal_dispatch",
     ])
 
 
@@ -416,6 +416,37 @@ def test_cast_dispatch_entry_points_reject_bad_arguments():
         assert call(nre=FAKE + 2) == -1     # num_recv_tokens_per_expert misaligned
     assert with_layout(ntpr=0) == -1        # layout outputs
     assert with_layout(itr=FAKE + 4) == -1
+    assert lib.cgd_last_error()
+
+
+def test_layout_and_normal_dispatch_rejects_bad_arguments():
+    lib = cgd.load()
+    ok = dict(x=FAKE, T=64, H=128, idx=FAKE, w=FAKE, K=4, E=16, R=4, A=1, recv=FAKE, cap=256, ntpr=FAKE, ntpe=FAKE,
+              itr=FAKE, off=FAKE, nre=FAKE, src=FAKE, send=FAKE, ridx=FAKE, rw=FAKE, ws=FAKE, wsb=1 << 20)
+    v = lambda a: _vp(a) if a else None
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.cgd_layout_and_normal_dispatch(v(a["x"]), a["T"], a["H"], v(a["idx"]), v(a["w"]), a["K"], a["E"],
+                                                  a["R"], a["A"], v(a["recv"]), a["cap"], v(a["ntpr"]), v(a["ntpe"]),
+                                                  v(a["itr"]), v(a["off"]), v(a["nre"]), v(a["src"]), v(a["send"]),
+                                                  v(a["ridx"]), v(a["rw"]), v(a["ws"]), a["wsb"], None)
+
+    assert call(H=12) == -1            # hidden not a multiple of 8
+    assert call(cap=255) == -2         # capacity below T * min(K, R)
+    assert call(E=15) == -1            # E % R
+    assert call(A=0) == -1
+    assert call(ntpr=0) == -1          # layout outputs
+    assert call(itr=FAKE + 4) == -1
+    assert call(off=0) == -1           # rank_offset
+    assert call(x=0) == -1
+    assert call(x=FAKE + 8) == -1      # x not 16-byte aligned
+    assert call(send=0) == -1
+    assert call(rw=0) == -1            # recv_topk_idx without recv_topk_weights
+    assert call(w=0) == -1             # recv_topk_* without topk_weights
+    assert call(ridx=0, rw=0) == -1    # topk_weights without recv_topk_*
+    assert call(ws=0) == -3            # missing workspace
+    assert call(wsb=16) == -3
     assert lib.cgd_last_error()
 
 

@@ -323,3 +323,49 @@ def test_layout_and_normal_plan_in_one_launch(T, K, E, R, H, align, p_neg):
     np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), o["recv_topk_weights"].view(np.uint32))
     data = o["recv_src_idx"] >= 0
     np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
+
+
+@pytest.mark.parametrize("T,K,E,R,H,align,p_neg,with_topk",
+                         [(4096, 8, 256, 8, 7168, 1, 0.0, True), (128, 8, 256, 16, 1024, 1, 0.0, True),
+                          (2049, 6, 96, 12, 136, 4, 0.2, True), (1500, 16, 512, 64, 256, 8, 0.0, True),
+                          (700, 8, 64, 8, 64, 1, 0.0, False), (0, 4, 16, 4, 64, 2, 0.0, True)])
+def test_layout_and_normal_dispatch_in_one_call(T, K, E, R, H, align, p_neg, with_topk):
+    """layout_and_normal_dispatch (the plan pulls x toward the caches, then the
+    apply): layout outputs, plan, rows and per-row outputs equal the oracle's,
+    and the handle serves the combine."""
+    rng = np.random.default_rng(T + 11 * R)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64) if T else np.zeros((0, K), np.int64)
+    idx[rng.random((T, K)) < p_neg] = -1
+    x = synth.normal_bf16(synth.stream_key(T, 56, 1), T * H).reshape(T, H)
+    wts = synth.softmax_weights(synth.stream_key(T, 56, 3), T, K)
+    say(f"[normal] layout + dispatch in one call: T={T} K={K} E={E} R={R} H={H} align={align} topk={with_topk}")
+    idx_dev = dev_i64(idx)
+    (ntpr, _, ntpe, itr, _), recv_x, ridx, rw, nre, h = cgd.layout_and_normal_dispatch(
+        dev_bf16(x), idx_dev, dev_f32(wts) if with_topk else None, E, R, expert_alignment=align)
+    torch.cuda.synchronize()
+    ol = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), ol[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
+    o = oracle.dispatch_normal(x, ol[2], E, K, ol[1], idx, wts, align=align, cap=h.recv_capacity, hidden=H)
+    np.testing.assert_array_equal(h.rank_offset.cpu().numpy(), o["rank_offset"])
+    np.testing.assert_array_equal(nre.cpu().numpy(), o["num_recv_tokens_per_expert"])
+    np.testing.assert_array_equal(h.send_row.cpu().numpy(), o["send_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    if with_topk:
+        np.testing.assert_array_equal(ridx.cpu().numpy(), o["recv_topk_idx"])
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), o["recv_topk_weights"].view(np.uint32))
+    else:
+        assert ridx is None and rw is None
+    data = o["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
+    if T and with_topk:
+        # the handle drives the combine: identity experts and no bias give
+        # each token times its fan-out, as the two-call path's handle does
+        out, cw = cgd.normal_combine(recv_x, h, rw)
+        (_, _, _, _, _), plan = cgd.layout_and_normal_dispatch_plan(idx_dev, E, R, expert_alignment=align)
+        rx2, _, rw2, _, h2 = cgd.normal_dispatch_apply(dev_bf16(x), plan, idx_dev, dev_f32(wts))
+        out2, cw2 = cgd.normal_combine(rx2, h2, rw2)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+        assert torch.equal(cw.view(torch.int32), cw2.view(torch.int32))
