@@ -1046,13 +1046,16 @@ hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int 
 
 // The non-cached cast on dispatch: the plan (with the layout outputs when
 // `layout` is given), whose spare blocks pull x into the caches while it
-// runs, then the cast to its rows, which then reads x from there.
+// runs when x fits there, then the cast to its rows, which then reads x from
+// there (top-16 stress, 268 MB of x: 561 us with the prefetch against 520
+// for the plan and the cast as two calls).
 static hipError_t launch_plan_and_cast(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E, int A,
                                        int fmt, void* recv_q, void* recv_s, int64_t cap, int32_t* expert_offset,
                                        int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row, const DispatchWs& w,
                                        hipStream_t stream, const LayoutOut* layout) {
+    const int64_t xb = T * (int64_t)H * 2;
     hipError_t err = launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, nrecv, dst_row, recv_src_idx, nullptr,
-                                 nullptr, w, stream, layout, x, T * (int64_t)H * 2);
+                                 nullptr, w, stream, layout, xb <= kPrefetchMaxBytes ? x : nullptr, xb);
     if (err != hipSuccess) return err;
     if (T > 0) launch_scatter_cast(x, T, H, K, fmt, dst_row, cap, recv_q, recv_s, stream);
     return hipGetLastError();
@@ -1150,8 +1153,12 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
     if (fmt < 0 && dispatch_fuses(T))
         return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, cap, w.packed_offset, nullptr,
                             recv_src_info, dst_row, packed_count, stats, w, stream);
+    // the bf16 row copy after the plan wants x in the caches at any size; the
+    // cast only while x stays there (kPrefetchMaxBytes)
+    const int64_t xb = T * (int64_t)H * 2;
+    const void* px = (fmt < 0 || xb <= kPrefetchMaxBytes) ? x : nullptr;
     hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, cap, w.packed_offset, nullptr, dst_row,
-                                 recv_src_info, packed_count, stats, w, stream, nullptr, x, T * (int64_t)H * 2);
+                                 recv_src_info, packed_count, stats, w, stream, nullptr, px, xb);
     if (err != hipSuccess) return err;
     if (fmt < 0)
         launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side(), true);
