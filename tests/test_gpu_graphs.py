@@ -2,7 +2,9 @@
 new inputs: every replay must equal the same step run eagerly on those inputs
 (expert-granular step with the final rows in the plan and the row-copy
 apply; the one-launch small-batch dispatch, with and without the layout
-outputs; rank-granular step with the fused layout + plan)."""
+outputs; rank-granular step with the fused layout + plan; the one-call
+layout + dispatch of larger batches, bf16, rank-granular and with the FP8
+cast, whose plans pull x toward the caches)."""
 import pytest
 import torch
 
@@ -39,12 +41,31 @@ def _normal_step(x, idx, wt, w, out):
     return [ntpr, ntpe, itr, plan.rank_offset, h.send_row, h.recv_src_idx, ridx, out]
 
 
+def _layout_step(x, idx, wt, w, out):
+    (ntpr, _, ntpe, itr, _), recv, nre, h = cgd.layout_and_dispatch(x, idx, w.E, w.R)
+    cgd.combine(recv, h, wt, out=out)
+    return [ntpr, ntpe, itr, h.expert_offset, h.dst_row, h.recv_src_idx, nre, out]
+
+
+def _normal_whole_step(x, idx, wt, w, out):
+    (ntpr, _, ntpe, itr, _), recv, ridx, rw, nre, h = cgd.layout_and_normal_dispatch(x, idx, wt, w.E, w.R)
+    cgd.normal_combine(recv, h, rw, out=out)
+    return [ntpr, ntpe, itr, h.rank_offset, h.send_row, h.recv_src_idx, ridx, nre, out]
+
+
+def _fp8_step(x, idx, wt, w, out):
+    (ntpr, _, ntpe, itr, _), (q, sc), nre, h = cgd.layout_and_dispatch(x, idx, w.E, w.R, cast_fp8=cgd.SCALE_F32)
+    return [ntpr, ntpe, itr, h.expert_offset, h.dst_row, h.recv_src_idx, nre, q.view(torch.uint8), sc]
+
+
 @pytest.mark.parametrize("kind,T", [("expert", 2500), ("small", 200), ("small_layout", 128), ("normal", 2500),
-                                    ("normal", 100)])
+                                    ("normal", 100), ("layout", 2500), ("normal_whole", 2500),
+                                    ("fp8_cast", 2500)])
 def test_step_replays_from_a_captured_graph(kind, T):
     w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
     step = {"expert": _expert_step, "small": _small_step, "small_layout": _small_layout_step,
-            "normal": _normal_step}[kind]
+            "normal": _normal_step, "layout": _layout_step, "normal_whole": _normal_whole_step,
+            "fp8_cast": _fp8_step}[kind]
     inputs = [synth.make_inputs(w, seed=s) for s in range(5)]
     sx = dev_bf16(inputs[0]["x"])
     sidx = dev_i64(inputs[0]["topk_idx"])
