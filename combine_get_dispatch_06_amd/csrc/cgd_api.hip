@@ -517,7 +517,8 @@ int cgd_layout_and_normal_dispatch(const void* x, int64_t num_tokens, int hidden
     if (err != hipSuccess) return hip_fail(err, "layout and normal dispatch plan launch");
     err = cgd::launch_normal_apply(x, num_tokens, hidden, recv_topk_idx ? topk_idx : nullptr, topk_weights, num_topk,
                                    num_experts, num_ranks, recv_x, recv_capacity, rank_offset, recv_src_idx, send_row,
-                                   recv_topk_idx, recv_topk_weights, workspace, stream);
+                                   recv_topk_idx, recv_topk_weights, workspace, stream,
+                                   cgd::normal_plan_prefetches(num_tokens, num_tokens * (int64_t)hidden * 2));
     if (err != hipSuccess) return hip_fail(err, "normal dispatch apply launch");
     return CGD_OK;
 }

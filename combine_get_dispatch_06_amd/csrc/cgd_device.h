@@ -393,11 +393,7 @@ __device__ __forceinline__ void block_exclusive_scan2(int n, F v, int32_t* out, 
 #define CGD_PREFETCH_IN_FLIGHT 8
 #endif
 constexpr int kPrefetchBlocks = CGD_PREFETCH_BLOCKS;
-// Larger inputs would not stay in the Infinity Cache until the kernel that
-// follows the plan reads them: the plans that feed a rank-granular apply or
-// an FP8 cast then prefetch nothing (at top-16 stress, 268 MB of x, the
-// prefetch outlasted the plan and the kernel after it gained nothing).
-constexpr int64_t kPrefetchMaxBytes = int64_t(160) << 20;
+
 template <int BLOCK>
 __device__ __forceinline__ void prefetch_rows(const uint4* __restrict__ p, int64_t n, int b, int nb) {
     constexpr int kInFlight = CGD_PREFETCH_IN_FLIGHT;

@@ -26,6 +26,17 @@ inline int64_t tokens_per_launch(int64_t waves_per_token) {
     return waves_per_token <= 0 ? kMaxGridWaves : (kMaxGridWaves / waves_per_token > 0 ? kMaxGridWaves / waves_per_token : 1);
 }
 
+// Plans that feed an FP8 cast or a rank-granular apply pull x into the
+// caches only up to this size: larger inputs would not stay in the Infinity
+// Cache until the kernel after the plan reads them (at top-16 stress, 268 MB
+// of x, the prefetch outlasted the plan and that kernel gained nothing).
+constexpr int64_t kPrefetchMaxBytes = int64_t(160) << 20;
+// Whether the layout + rank-granular plan of T tokens pulls x_bytes of x
+// into the caches (a plan of one tile never does).
+inline bool normal_plan_prefetches(int64_t T, int64_t x_bytes) {
+    return T > kLayoutTile && x_bytes > 0 && x_bytes <= kPrefetchMaxBytes;
+}
+
 int64_t layout_blocks(int64_t T);
 size_t layout_workspace_bytes(int64_t T, int E, int R);  // get_dispatch_layout alone
 size_t layout_partial_bytes(int64_t T, int E, int R);    // per-block partials of the layout + normal plan
@@ -102,7 +113,7 @@ hipError_t launch_normal_plan(const uint8_t* itr, int64_t T, int R, const int32_
 hipError_t launch_normal_apply(const void* x, int64_t T, int H, const int64_t* topk_idx, const float* topk_w, int K,
                                int E, int R, void* recv_x, int64_t cap, const int32_t* rank_offset,
                                int32_t* recv_src_idx, int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w,
-                               const void* workspace, hipStream_t stream);
+                               const void* workspace, hipStream_t stream, bool after_prefetch = false);
 
 hipError_t launch_normal_dispatch_cached(const void* x, int64_t T, int H, int R, const int32_t* send_row,
                                          void* recv_x, int64_t cap, hipStream_t stream);

@@ -350,7 +350,7 @@ hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int
     // prefetch outlasts the plan and the apply gains nothing (whole dispatch
     // 869 us against 844 for the two calls), while prefill (59 MB) and
     // Zipf-skewed (117 MB) gain 7.5 and 9.7 us
-    const int extra = (nblk > 1 && pvecs > 0 && x_bytes <= kPrefetchMaxBytes) ? kPrefetchBlocks : 0;
+    const int extra = (x && normal_plan_prefetches(T, x_bytes)) ? kPrefetchBlocks : 0;
     const dim3 grid((unsigned)(nblk + extra)), block(kLayoutTile);
     const NormalPlanOut np{a.grp_bal, a.grp_pre, a.tile_base, rank_offset, nrecv, A};
     const int L = E / R;

@@ -392,12 +392,21 @@ __global__ __launch_bounds__(kNormCombineWaves* kWave) void normal_combine_kerne
 // Chunks of 4 vectors per lane unless that leaves fewer than this many waves.
 constexpr int64_t kNormMinWaves = 4096;
 
+// The apply after a plan that pulled x into the caches runs fewer waves per
+// CU: an LDS reservation of this many bytes per 4-wave block leaves 5 blocks.
+// Whole rank-granular dispatch (layout + plan + apply), inputs rotating, us:
+// prefill 68.9 against 69.7-69.9 at full occupancy (6 blocks 66.0, 4 blocks
+// 68.8, 3 blocks 94.7), Zipf-skewed 171.5 against 184.5-184.7 (6 blocks
+// 178.8, 4 blocks 171.5, 3 blocks 234.4).
+#ifndef CGD_NORMAL_PF_LDS
+#define CGD_NORMAL_PF_LDS 32768
+#endif
 template <bool CACHED, int U>
 static void launch_normal_scatter_u(const void* x, int64_t T, int nvec, int R, const NormalWs* w,
                                     const int32_t* rank_offset, int32_t* send_row, int32_t* recv_src_idx,
                                     const int64_t* topk_idx, const float* topk_w, int K, int E,
                                     int64_t* recv_topk_idx, float* recv_topk_w, int64_t cap, void* recv_x,
-                                    const SideRows& side, hipStream_t s) {
+                                    const SideRows& side, hipStream_t s, size_t lds = 0) {
     const int nchunk = (nvec + U * kWave - 1) / (U * kWave);
     const int64_t tper = tokens_per_launch(nchunk);
     int64_t t0 = 0;
@@ -406,7 +415,7 @@ static void launch_normal_scatter_u(const void* x, int64_t T, int nvec, int R, c
         const int64_t waves = nt * nchunk;
         const int64_t blocks = waves <= 0 ? 1 : (waves + kNormScatterWaves - 1) / kNormScatterWaves;
         hipLaunchKernelGGL((normal_scatter_kernel<U, CACHED>), dim3((unsigned)blocks),
-                           dim3(kNormScatterWaves * kWave), 0, s, reinterpret_cast<const uint4*>(x), t0 + nt, nvec,
+                           dim3(kNormScatterWaves * kWave), lds, s, reinterpret_cast<const uint4*>(x), t0 + nt, nvec,
                            nchunk, R, w ? w->grp_bal : nullptr, w ? w->grp_pre : nullptr,
                            w ? w->tile_base : nullptr, rank_offset, send_row, recv_src_idx, topk_idx, topk_w, K, E,
                            R > 0 ? E / R : 1, recv_topk_idx, recv_topk_w, cap, t0, t0 == 0 ? 1 : 0,
@@ -420,12 +429,12 @@ static void launch_normal_scatter(const void* x, int64_t T, int nvec, int R, con
                                   const int32_t* rank_offset, int32_t* send_row, int32_t* recv_src_idx,
                                   const int64_t* topk_idx, const float* topk_w, int K, int E, int64_t* recv_topk_idx,
                                   float* recv_topk_w, int64_t cap, void* recv_x, const SideRows& side,
-                                  hipStream_t s) {
+                                  hipStream_t s, size_t lds = 0) {
     constexpr int U = CGD_NORMAL_SCATTER_U;
     const int64_t wavesU = T * ((nvec + U * kWave - 1) / (U * kWave));
     if (wavesU >= kNormMinWaves)
         launch_normal_scatter_u<CACHED, U>(x, T, nvec, R, w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w,
-                                           K, E, recv_topk_idx, recv_topk_w, cap, recv_x, side, s);
+                                           K, E, recv_topk_idx, recv_topk_w, cap, recv_x, side, s, lds);
     else
         launch_normal_scatter_u<CACHED, 1>(x, T, nvec, R, w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w,
                                            K, E, recv_topk_idx, recv_topk_w, cap, recv_x, side, s);
@@ -446,10 +455,11 @@ hipError_t launch_normal_plan(const uint8_t* itr, int64_t T, int R, const int32_
 hipError_t launch_normal_apply(const void* x, int64_t T, int H, const int64_t* topk_idx, const float* topk_w, int K,
                                int E, int R, void* recv_x, int64_t cap, const int32_t* rank_offset,
                                int32_t* recv_src_idx, int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_w,
-                               const void* workspace, hipStream_t stream) {
+                               const void* workspace, hipStream_t stream, bool after_prefetch) {
     const NormalWs w = normal_ws(const_cast<void*>(workspace), T, R);
     launch_normal_scatter<false>(x, T, H / 8, R, &w, rank_offset, send_row, recv_src_idx, topk_idx, topk_w, K, E,
-                                 recv_topk_idx, recv_topk_w, cap, recv_x, normal_no_side(), stream);
+                                 recv_topk_idx, recv_topk_w, cap, recv_x, normal_no_side(), stream,
+                                 after_prefetch ? CGD_NORMAL_PF_LDS : 0);
     return hipGetLastError();
 }
 
