@@ -263,13 +263,14 @@ class ExpertPath(_Path):
 
 
 class NormalPath(_Path):
-    """bf16: layout, rank-granular plan and apply in one call
+    """layout, rank-granular plan and apply in one call
     (layout_and_normal_dispatch: the plan pulls x toward the caches for the
-    apply), combine (identity experts, no bias); the split step makes the
-    same calls separately (layout + plan in one launch, the apply). FP8:
-    layout + plan, the per-token cast, the tuple apply, combine."""
-    labels = ("layout_and_plan", "cast", "dispatch_apply", "combine")
-    dispatch_labels = ("layout_and_plan", "cast", "dispatch_apply")
+    apply, or with the FP8 payload casts x in its idle blocks), combine
+    (identity experts, no bias); the split step makes the same calls
+    separately (layout + plan in one launch, [the per-token cast,] the
+    apply)."""
+    labels = ("dispatch", "combine")
+    dispatch_labels = ("dispatch",)
     apply_label = "dispatch_apply"
     data_kernels = (("dispatch_apply", "apply", ("normal_scatter_kernel",)),
                     ("combine", "combine", ("normal_combine_kernel",)))
@@ -286,49 +287,36 @@ class NormalPath(_Path):
                            torch.empty((cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32,
                                        device=dev))
         self.last = [None] * len(sets)
-        if fmt is None:
-            self.labels = ("dispatch", "combine")
-            self.dispatch_labels = ("dispatch",)
-            self.split_labels = ("layout_and_plan", "dispatch_apply", "combine")
+        self.split_labels = (("layout_and_plan", "dispatch_apply", "combine") if fmt is None else
+                             ("layout_and_plan", "cast", "dispatch_apply", "combine"))
 
     def step(self, i, ev=None):
-        cgd, w = self.cgd, self.w
-        if self.fmt is None:
-            self._rec(ev, 0)
-            (_, _, _, itr, _), _, _, rw, _, h = cgd.layout_and_normal_dispatch(
-                self.x[i], self.idx[i], self.wt[i], w.E, w.R, expert_alignment=w.align, recv_x=self.recv_x)
-            self._rec(ev, 1)
-            cgd.normal_combine(self.recv_x, h, rw, out=self.out)
-            self._rec(ev, 2)
-            self.last[i] = (h, itr, rw)
-            return
+        cgd = self.cgd
         self._rec(ev, 0)
-        (_, _, _, itr, _), plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R,
-                                                                      expert_alignment=w.align)
+        (_, _, _, itr, _), _, _, rw, _, h = self._dispatch(i)
         self._rec(ev, 1)
-        if self.fmt is not None:
-            q, sc = cgd.per_token_cast_to_fp8(self.x[i], self.fmt)
-        self._rec(ev, 2)
-        if self.fmt is None:
-            _, _, rw, _, h = cgd.normal_dispatch_apply(self.x[i], plan, self.idx[i], self.wt[i], recv_x=self.recv_x)
-        else:
-            _, _, rw, _, h = cgd.normal_dispatch_apply((q, sc), plan, self.idx[i], self.wt[i], recv_x=self.recv_q)
-        self._rec(ev, 3)
         cgd.normal_combine(self.recv_x, h, rw, out=self.out)
-        self._rec(ev, 4)
+        self._rec(ev, 2)
         self.last[i] = (h, itr, rw)
 
     def split_step(self, i, ev=None):
-        """bf16: the step's work as separate calls (layout + plan, apply, combine)."""
+        """The step's work as separate calls (layout + plan, [cast,] apply, combine)."""
         cgd, w = self.cgd, self.w
         self._rec(ev, 0)
         (_, _, _, itr, _), plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R,
                                                                       expert_alignment=w.align)
         self._rec(ev, 1)
-        _, _, rw, _, h = cgd.normal_dispatch_apply(self.x[i], plan, self.idx[i], self.wt[i], recv_x=self.recv_x)
-        self._rec(ev, 2)
+        n = 2
+        if self.fmt is None:
+            x, recv = self.x[i], self.recv_x
+        else:
+            x, recv = cgd.per_token_cast_to_fp8(self.x[i], self.fmt), self.recv_q
+            self._rec(ev, n)
+            n += 1
+        _, _, rw, _, h = cgd.normal_dispatch_apply(x, plan, self.idx[i], self.wt[i], recv_x=recv)
+        self._rec(ev, n)
         cgd.normal_combine(self.recv_x, h, rw, out=self.out)
-        self._rec(ev, 3)
+        self._rec(ev, n + 1)
         self.last[i] = (h, itr, rw)
 
     def _dispatch(self, i):
@@ -336,10 +324,8 @@ class NormalPath(_Path):
         if self.fmt is None:
             return cgd.layout_and_normal_dispatch(self.x[i], self.idx[i], self.wt[i], w.E, w.R,
                                                   expert_alignment=w.align, recv_x=self.recv_x)
-        _, plan = cgd.layout_and_normal_dispatch_plan(self.idx[i], w.E, w.R, expert_alignment=w.align)
-        x = self.x[i] if self.fmt is None else cgd.per_token_cast_to_fp8(self.x[i], self.fmt)
-        return cgd.normal_dispatch_apply(x, plan, self.idx[i], self.wt[i],
-                                         recv_x=self.recv_x if self.fmt is None else self.recv_q)
+        return cgd.layout_and_normal_dispatch(self.x[i], self.idx[i], self.wt[i], w.E, w.R,
+                                              expert_alignment=w.align, recv_x=self.recv_q, cast_fp8=self.fmt)
 
     def graph_calls(self):
         import torch
@@ -391,7 +377,8 @@ class NormalPath(_Path):
         return {"path": "normal (one row per flagged rank)",
                 "dispatch": ("layout_and_normal_dispatch (layout + rank-granular plan with x pulled toward the "
                              "caches, then the apply)" if self.fmt is None else
-                             "layout_and_normal_dispatch_plan, per_token_cast_to_fp8, normal_dispatch_apply"),
+                             "layout_and_normal_dispatch with the cast (layout + rank-granular plan whose idle "
+                             "blocks cast x, then the apply of the FP8 tuple)"),
                 "experts": "identity (combine reads dispatched rows), no bias" if self.fmt is None else
                 "identity (combine reads the cast-back FP8 rows, made before timing), no bias"}
 

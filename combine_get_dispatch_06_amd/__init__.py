@@ -176,6 +176,9 @@ def configure(lib):
     lib.cgd_layout_and_normal_dispatch.restype = i32
     lib.cgd_layout_and_normal_dispatch.argtypes = [vp, i64, i32, vp, vp, i32, i32, i32, i32, vp, i64, vp, vp, vp, vp,
                                                    vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.cgd_layout_and_normal_dispatch_cast_fp8.restype = i32
+    lib.cgd_layout_and_normal_dispatch_cast_fp8.argtypes = [vp, i64, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp,
+                                                            vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_layout_and_normal_dispatch_plan.restype = i32
     lib.cgd_layout_and_normal_dispatch_plan.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     return lib
@@ -988,11 +991,14 @@ def layout_and_normal_dispatch_plan(topk_idx: torch.Tensor, num_experts: int, nu
 
 def layout_and_normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_weights: torch.Tensor | None,
                                num_experts: int, num_ranks: int, expert_alignment: int = 1,
-                               recv_capacity: int | None = None, recv_x: torch.Tensor | None = None,
-                               workspace: torch.Tensor | None = None):
+                               recv_capacity: int | None = None, recv_x=None,
+                               workspace: torch.Tensor | None = None, cast_fp8: int | None = None, x_fp8=None):
     """layout_and_normal_dispatch_plan and normal_dispatch_apply (bf16 x) in one
     call; the plan pulls x toward the caches for the apply. topk_weights None:
-    no recv_topk_idx / recv_topk_weights.
+    no recv_topk_idx / recv_topk_weights. cast_fp8 (a scale format): the plan's
+    idle blocks cast x per token (into x_fp8, a (codes [T, H], row-major scales
+    [T, H/128]) tuple of the caller's, else a new one) and the apply moves that
+    tuple; recv_x is then an FP8 tuple.
     -> ((num_tokens_per_rank, None, num_tokens_per_expert, is_token_in_rank, None), recv_x,
         recv_topk_idx | None, recv_topk_weights | None, num_recv_tokens_per_expert, NormalHandle)."""
     lib = load()
@@ -1010,11 +1016,15 @@ def layout_and_normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_wei
     R = num_ranks
     with torch.cuda.device(dev):
         cap = int(lib.cgd_normal_capacity(T, K, R)) if recv_capacity is None else int(recv_capacity)
-        if recv_x is None:
-            recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
-        _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
-        if recv_x.shape != (cap, H):
-            raise ValueError("recv_x must be [recv_capacity, hidden]")
+        if cast_fp8 is not None:
+            recv_x = _recv_fp8(recv_x, max(cap, 0), H, cast_fp8, dev)
+            x_fp8 = _recv_fp8(x_fp8, T, H, cast_fp8, dev)
+        else:
+            if recv_x is None:
+                recv_x = torch.empty((max(cap, 0), H), dtype=torch.bfloat16, device=dev)
+            _dev_tensor(recv_x, "recv_x", torch.bfloat16, 2)
+            if recv_x.shape != (cap, H):
+                raise ValueError("recv_x must be [recv_capacity, hidden]")
         ntpr = torch.empty(R, dtype=torch.int32, device=dev)
         ntpe = torch.empty(num_experts, dtype=torch.int32, device=dev)
         itr = torch.empty((T, R), dtype=torch.bool, device=dev)
@@ -1028,11 +1038,20 @@ def layout_and_normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_wei
             rw = torch.empty((max(cap, 0), K), dtype=torch.float32, device=dev)
         need = int(lib.cgd_layout_and_normal_workspace_bytes(T, K, num_experts, R))
         ws = _normal_plan_workspace(workspace, max(need, 1), dev, "layout_normal")
-        _check("cgd_layout_and_normal_dispatch",
-               lib.cgd_layout_and_normal_dispatch(_ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K, num_experts,
-                                                  R, expert_alignment, _ptr(recv_x), cap, _ptr(ntpr), _ptr(ntpe),
-                                                  _ptr(itr), _ptr(off), _ptr(nre), _ptr(src), _ptr(send), _ptr(ridx),
-                                                  _ptr(rw), _ptr(ws), ws.numel(), _stream(dev)))
+        if cast_fp8 is not None:
+            _check("cgd_layout_and_normal_dispatch_cast_fp8",
+                   lib.cgd_layout_and_normal_dispatch_cast_fp8(
+                       _ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K, num_experts, R, expert_alignment,
+                       cast_fp8, _ptr(x_fp8[0]), _ptr(x_fp8[1]), _ptr(recv_x[0]), _ptr(recv_x[1]), cap, _ptr(ntpr),
+                       _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(nre), _ptr(src), _ptr(send), _ptr(ridx), _ptr(rw),
+                       _ptr(ws), ws.numel(), _stream(dev)))
+        else:
+            _check("cgd_layout_and_normal_dispatch",
+                   lib.cgd_layout_and_normal_dispatch(_ptr(x), T, H, _ptr(topk_idx), _ptr(topk_weights), K,
+                                                      num_experts, R, expert_alignment, _ptr(recv_x), cap,
+                                                      _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(off), _ptr(nre),
+                                                      _ptr(src), _ptr(send), _ptr(ridx), _ptr(rw), _ptr(ws),
+                                                      ws.numel(), _stream(dev)))
         _note_plan_write(ws)
     return (ntpr, None, ntpe, itr, None), recv_x, ridx, rw, nre, NormalHandle(off, src, send, K, cap)
 

@@ -523,6 +523,49 @@ int cgd_layout_and_normal_dispatch(const void* x, int64_t num_tokens, int hidden
     return CGD_OK;
 }
 
+int cgd_layout_and_normal_dispatch_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                            const float* topk_weights, int num_topk, int num_experts, int num_ranks,
+                                            int expert_alignment, int scale_format, void* x_fp8, void* x_scales,
+                                            void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                            int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                            uint8_t* is_token_in_rank, int32_t* rank_offset,
+                                            int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx,
+                                            int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_weights,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_layout_and_normal_plan_args(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                               expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
+                                               is_token_in_rank, rank_offset, num_recv_tokens_per_expert, workspace,
+                                               workspace_bytes);
+    if (rc) return rc;
+    if ((rc = check_fp8(hidden, scale_format))) return rc;
+    if (num_tokens > 0 && (!x || !x_fp8)) return fail(CGD_ERR_INVALID_ARG, "null x or x_fp8");
+    if (!aligned(x, 16) || !aligned(x_fp8, 16)) return fail(CGD_ERR_INVALID_ARG, "x and x_fp8 must be 16-byte aligned");
+    if ((rc = check_scales(x_scales, 0, 0, scale_format, num_tokens > 0))) return rc;
+    // the apply reads the cast tuple (codes, row-major scales) and writes the FP8 rows
+    if ((rc = check_normal_apply_args(x_fp8, num_tokens, hidden, recv_topk_idx ? topk_idx : nullptr,
+                                      topk_weights, num_topk, num_experts, num_ranks, recv_x_fp8, recv_capacity,
+                                      rank_offset, recv_src_idx, send_row, recv_topk_idx, recv_topk_weights,
+                                      workspace, workspace_bytes)))
+        return rc;
+    if ((rc = check_scales(recv_scales, 0, 0, scale_format, num_tokens > 0 && recv_capacity > 0))) return rc;
+    const cgd::NormalCast cast{x, hidden, scale_format, x_fp8, x_scales};
+    hipError_t err = cgd::launch_layout_and_normal_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
+                                                        expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
+                                                        is_token_in_rank, rank_offset, num_recv_tokens_per_expert,
+                                                        workspace, stream, nullptr, 0, &cast);
+    if (err != hipSuccess) return hip_fail(err, "layout, normal dispatch plan and cast launch");
+    if (num_tokens > 0 && !cgd::normal_plan_casts(num_tokens)) {  // a one-tile plan: the cast on its own
+        err = cgd::launch_cast_to_fp8(x, num_tokens, hidden, x_fp8, x_scales, hidden / 128, 1, scale_format, stream);
+        if (err != hipSuccess) return hip_fail(err, "cast launch");
+    }
+    err = cgd::launch_normal_apply_fp8(x_fp8, x_scales, hidden / 128, 1, scale_format, num_tokens, hidden,
+                                       recv_topk_idx ? topk_idx : nullptr, topk_weights, num_topk, num_experts,
+                                       num_ranks, recv_x_fp8, recv_scales, recv_capacity, rank_offset, recv_src_idx,
+                                       send_row, recv_topk_idx, recv_topk_weights, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "normal FP8 dispatch apply launch");
+    return CGD_OK;
+}
+
 int cgd_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const uint8_t* is_token_in_rank,
                         const int32_t* num_tokens_per_expert, const int64_t* topk_idx, const float* topk_weights,
                         int num_topk, int num_experts, int num_ranks, int expert_alignment, void* recv_x,

@@ -409,6 +409,62 @@ __device__ __forceinline__ void prefetch_rows(const uint4* __restrict__ p, int64
     asm volatile("" ::"v"(acc));  // the loaded values are used, so the loads stay
 }
 
+// Blocks of a plan past its tiles that cast x to FP8 while the plan runs
+// (the rank-granular dispatch with the cast): the (token, 1024-channel chunk)
+// items of x, kCastInFlight per wave at a time, each lane 16 channels (two
+// 16-byte bf16 vectors in, one 16-byte code vector out), an 8-lane group one
+// 128-channel block, exactly as the per-token cast: codes q [T, H] and
+// row-major scales [T, H/128] (fp32, or one UE8M0 byte for fmt 2). b, nb:
+// this block among the nb casting blocks of BLOCK threads.
+#ifndef CGD_CAST_IN_FLIGHT
+#define CGD_CAST_IN_FLIGHT 2
+#endif
+constexpr int kCastInFlight = CGD_CAST_IN_FLIGHT;
+template <int BLOCK>
+__device__ __forceinline__ void cast_rows(const uint4* __restrict__ x, int64_t T, int H, int fmt,
+                                          uint4* __restrict__ q, void* __restrict__ scales, int b, int nb) {
+    const int nlv = H / 16;                  // lane vectors (16 channels) per row
+    const int nchunk = (nlv + kWave - 1) / kWave;
+    const int nsb = H / kFp8Block;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t waves = (int64_t)nb * (BLOCK / kWave);
+    const int64_t w0 = (int64_t)b * (BLOCK / kWave) + (int)(threadIdx.x / kWave);
+    const int64_t items = T * nchunk;
+    for (int64_t i0 = w0; i0 < items; i0 += waves * kCastInFlight) {
+        uint4 a[kCastInFlight], c[kCastInFlight];
+        int64_t t[kCastInFlight];
+        int v[kCastInFlight];
+        bool in[kCastInFlight];
+#pragma unroll
+        for (int j = 0; j < kCastInFlight; ++j) {  // every item's loads first
+            const int64_t it = i0 + j * waves;
+            t[j] = it / nchunk;
+            v[j] = (int)(it - t[j] * nchunk) * kWave + lane;
+            in[j] = it < items && v[j] < nlv;  // whole 8-lane groups are in or out (nlv % 8 == 0)
+            a[j] = c[j] = make_uint4(0, 0, 0, 0);
+            if (in[j]) {
+                const uint4* xr = x + (t[j] * nlv + v[j]) * 2;
+                a[j] = xr[0];
+                c[j] = xr[1];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kCastInFlight; ++j) {
+            const float m = in[j] ? fmaxf(absmax_bf16x8(a[j]), absmax_bf16x8(c[j])) : 0.0f;
+            const Fp8Scale sc = fp8_block_scale(group8_max(m), fmt);
+            if (!in[j]) continue;
+            q[t[j] * nlv + v[j]] = quantize_bf16x16(a[j], c[j], sc.mul);
+            if ((lane & 7) == 0) {
+                const int64_t si = t[j] * nsb + v[j] / 8;
+                if (fmt == 2)
+                    static_cast<uint8_t*>(scales)[si] = (uint8_t)sc.ue8m0;
+                else
+                    static_cast<float*>(scales)[si] = sc.scale;
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ void reset_ticket(unsigned int* ticket) {
     if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

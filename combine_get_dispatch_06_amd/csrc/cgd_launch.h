@@ -37,6 +37,10 @@ inline bool normal_plan_prefetches(int64_t T, int64_t x_bytes) {
     return T > kLayoutTile && x_bytes > 0 && x_bytes <= kPrefetchMaxBytes;
 }
 
+// Whether the layout + rank-granular plan of T tokens casts x in its spare
+// blocks (a plan of one tile has none).
+inline bool normal_plan_casts(int64_t T) { return T > kLayoutTile; }
+
 int64_t layout_blocks(int64_t T);
 size_t layout_workspace_bytes(int64_t T, int E, int R);  // get_dispatch_layout alone
 size_t layout_partial_bytes(int64_t T, int E, int R);    // per-block partials of the layout + normal plan
@@ -71,10 +75,31 @@ NormalPlanArrays normal_plan_arrays(void* workspace, int64_t T, int R);
 // workspace holds the plan's workspace followed by the layout's.
 // x (optional, x_bytes): the rows the rank-granular apply reads next, pulled
 // toward the caches by blocks past the plan's tiles while the plan runs.
+// cast (optional, instead): those blocks cast x to the per-token FP8 tuple
+// (codes q [T, H], row-major scales [T, H/128]) for the apply; a plan of one
+// tile has no such blocks and leaves the cast to the caller.
+struct NormalCast {
+    const void* x;
+    int H, fmt;
+    void* q;
+    void* scales;
+};
+// Casting blocks beside the plan's tiles (4-wave blocks, CGD_CAST_IN_FLIGHT
+// items of 1024 channels per wave at a time). Whole rank-granular FP8
+// dispatch, inputs rotating, us (prefill / top-16 stress): 4096 blocks x 2
+// items 51.4-51.8 / 509.3-509.5; 8192 x 2 54.3 / 510.6; 8192 x 1 53.4 /
+// 505.9; 4096 x 1 52.8 / 510.6; 2048 x 2 52.7 / 519.3; 2048 x 4 52.5 /
+// 522.3; 1024 x 4 54.5 / 532.1; 512 x 4 55.1 / 526.6; the plan, the cast
+// launch and the apply as three calls 59.3-59.5 / 511-520.
+#ifndef CGD_CAST_BLOCKS
+#define CGD_CAST_BLOCKS 4096
+#endif
+constexpr int kCastBlocks = CGD_CAST_BLOCKS;
 hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A,
                                          int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
                                          int32_t* nrecv, void* workspace, hipStream_t stream,
-                                         const void* x = nullptr, int64_t x_bytes = 0);
+                                         const void* x = nullptr, int64_t x_bytes = 0,
+                                         const NormalCast* cast = nullptr);
 
 // The dispatch plan: the handle (expert_offset, recv_src_idx, dst_row) from
 // the routing alone, and (nrecv != nullptr) the aligned segment sizes. x

@@ -45,18 +45,31 @@ struct NormalPlanOut {
     int A;
 };
 
-// Blocks past the first nblk (the tiles) pull px (pvecs 16-byte vectors, the
-// x of the rank-granular apply that follows) toward the caches and take no
-// part in the plan.
-template <int RW, bool NPLAN = false>  // RW: 64-bit words of the rank mask: 1 (R <= 64) or 6 (R <= 384)
+// The per-token FP8 cast that CAST blocks write (codes [T, H], row-major
+// scales [T, H/128]).
+struct CastOut {
+    int H, fmt;
+    uint4* q;
+    void* scales;
+};
+
+// Blocks past the first nblk (the tiles) take no part in the plan: they pull
+// px (pvecs 16-byte vectors, the x of the rank-granular apply that follows)
+// toward the caches, or with CAST cast px (bf16 [T, H]) to FP8 for the apply.
+template <int RW, bool NPLAN = false, bool CAST = false>  // RW: 64-bit words of the rank mask: 1 (R <= 64) or 6 (R <= 384)
 __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K,
                                                              int E, int R, int L, int32_t* __restrict__ ntpr,
                                                              int32_t* __restrict__ ntpe, uint8_t* __restrict__ itr,
                                                              int32_t* __restrict__ partial,
                                                              unsigned int* __restrict__ ticket, NormalPlanOut np,
-                                                             int nblk, const uint4* __restrict__ px, int64_t pvecs) {
+                                                             int nblk, const uint4* __restrict__ px, int64_t pvecs,
+                                                             CastOut co) {
     if ((int)blockIdx.x >= nblk) {
-        prefetch_rows<kLayoutTile>(px, pvecs, (int)blockIdx.x - nblk, (int)gridDim.x - nblk);
+        if (CAST)
+            cast_rows<kLayoutTile>(px, T, co.H, co.fmt, co.q, co.scales, (int)blockIdx.x - nblk,
+                                   (int)gridDim.x - nblk);
+        else
+            prefetch_rows<kLayoutTile>(px, pvecs, (int)blockIdx.x - nblk, (int)gridDim.x - nblk);
         return;
     }
     __shared__ int32_t s_idx[kLayoutTile * kMaxTopk];
@@ -335,7 +348,7 @@ hipError_t launch_layout(const int64_t* topk_idx, int64_t T, int K, int E, int R
 hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A,
                                          int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
                                          int32_t* nrecv, void* workspace, hipStream_t stream, const void* x,
-                                         int64_t x_bytes) {
+                                         int64_t x_bytes, const NormalCast* cast) {
     // workspace: the rank-granular plan's workspace (its ticket, at offset 0
     // whatever the sizes, is the one this launch takes), then the block
     // partials
@@ -343,23 +356,32 @@ hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int
     unsigned int* ticket = a.ticket;
     int32_t* partial = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + normal_workspace_bytes(T, R));
     const int nblk = (int)layout_blocks(T);
-    const uint4* pv = reinterpret_cast<const uint4*>(x);
-    const int64_t pvecs = x ? x_bytes / 16 : 0;
-    // a one-tile plan prefetches nothing, nor does a plan whose x would not
-    // stay in the Infinity Cache: at top-16 stress (268 MB of x) the
-    // prefetch outlasts the plan and the apply gains nothing (whole dispatch
-    // 869 us against 844 for the two calls), while prefill (59 MB) and
-    // Zipf-skewed (117 MB) gain 7.5 and 9.7 us
-    const int extra = (x && normal_plan_prefetches(T, x_bytes)) ? kPrefetchBlocks : 0;
-    const dim3 grid((unsigned)(nblk + extra)), block(kLayoutTile);
     const NormalPlanOut np{a.grp_bal, a.grp_pre, a.tile_base, rank_offset, nrecv, A};
     const int L = E / R;
+    if (cast) {  // the spare blocks cast x (nothing to do for them in a one-tile plan: the caller casts)
+        const CastOut co{cast->H, cast->fmt, reinterpret_cast<uint4*>(cast->q), cast->scales};
+        const int extra = nblk > 1 ? kCastBlocks : 0;
+        const dim3 grid((unsigned)(nblk + extra)), block(kLayoutTile);
+        const uint4* xv = reinterpret_cast<const uint4*>(cast->x);
+        if (R <= 64)
+            hipLaunchKernelGGL((layout_kernel<1, true, true>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr,
+                               ntpe, itr, partial, ticket, np, nblk, xv, 0, co);
+        else
+            hipLaunchKernelGGL((layout_kernel<6, true, true>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr,
+                               ntpe, itr, partial, ticket, np, nblk, xv, 0, co);
+        return hipGetLastError();
+    }
+    const uint4* pv = reinterpret_cast<const uint4*>(x);
+    const int64_t pvecs = x ? x_bytes / 16 : 0;
+    const int extra = (x && normal_plan_prefetches(T, x_bytes)) ? kPrefetchBlocks : 0;
+    const dim3 grid((unsigned)(nblk + extra)), block(kLayoutTile);
+    const CastOut none{0, 0, nullptr, nullptr};
     if (R <= 64)
         hipLaunchKernelGGL((layout_kernel<1, true>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
-                           partial, ticket, np, nblk, pv, pvecs);
+                           partial, ticket, np, nblk, pv, pvecs, none);
     else
         hipLaunchKernelGGL((layout_kernel<6, true>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
-                           partial, ticket, np, nblk, pv, pvecs);
+                           partial, ticket, np, nblk, pv, pvecs, none);
     return hipGetLastError();
 }
 

@@ -511,6 +511,26 @@ int cgd_layout_and_normal_dispatch(const void* x, int64_t num_tokens, int hidden
                                    int64_t* recv_topk_idx, float* recv_topk_weights, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/* cgd_layout_and_normal_dispatch with the FP8 payload cast on the way: the
+ * plan's idle compute units cast x (bf16 [num_tokens, hidden]) per token, as
+ * cgd_cast_to_fp8 would, into x_fp8 (e4m3fn codes [num_tokens, hidden],
+ * 16-byte aligned) and x_scales (row-major [num_tokens, hidden/128], fp32, or
+ * one byte for scale_format 2) while the plan runs, and the apply then moves
+ * that tuple, as cgd_normal_dispatch_apply_fp8, to recv_x_fp8
+ * [recv_capacity, hidden] and recv_scales [recv_capacity, hidden/128] (legacy
+ * tests, normal-mode dispatch with the FP8 tuple as x; Python notes "Dispatch
+ * API", the FP8 form of x). hidden must be a positive multiple of 128;
+ * everything else as cgd_layout_and_normal_dispatch. */
+int cgd_layout_and_normal_dispatch_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                            const float* topk_weights, int num_topk, int num_experts, int num_ranks,
+                                            int expert_alignment, int scale_format, void* x_fp8, void* x_scales,
+                                            void* recv_x_fp8, void* recv_scales, int64_t recv_capacity,
+                                            int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                            uint8_t* is_token_in_rank, int32_t* rank_offset,
+                                            int32_t* num_recv_tokens_per_expert, int32_t* recv_src_idx,
+                                            int32_t* send_row, int64_t* recv_topk_idx, float* recv_topk_weights,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* -------------------------------------------------------------------------
  * cgd_copy: dst[0, bytes) = src[0, bytes), bitwise.
  * Not an operation of the method: a measured copy ceiling, reported beside

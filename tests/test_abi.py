@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
         "cgd_layout_and_dispatch", "cgd_empty", "cgd_layout_and_dispatch_noalloc",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan", "cgd_init",
         "cgd_dispatch_cast_fp8", "cgd_layout_and_dispatch_cast_fp8", "cgd_layout_and_normal_dispatch",
+        "cgd_layout_and_normal_dispatch_cast_fp8",
     ])
 
 
@@ -447,6 +448,37 @@ def test_layout_and_normal_dispatch_rejects_bad_arguments():
     assert call(ridx=0, rw=0) == -1    # topk_weights without recv_topk_*
     assert call(ws=0) == -3            # missing workspace
     assert call(wsb=16) == -3
+    assert lib.cgd_last_error()
+
+
+def test_layout_and_normal_dispatch_cast_rejects_bad_arguments():
+    lib = cgd.load()
+    ok = dict(x=FAKE, T=64, H=256, idx=FAKE, w=FAKE, K=4, E=16, R=4, A=1, fmt=0, xq=FAKE, xs=FAKE, rq=FAKE, rs=FAKE,
+              cap=256, ntpr=FAKE, ntpe=FAKE, itr=FAKE, off=FAKE, nre=FAKE, src=FAKE, send=FAKE, ridx=FAKE, rw=FAKE,
+              ws=FAKE, wsb=1 << 20)
+    v = lambda a: _vp(a) if a else None
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.cgd_layout_and_normal_dispatch_cast_fp8(
+            v(a["x"]), a["T"], a["H"], v(a["idx"]), v(a["w"]), a["K"], a["E"], a["R"], a["A"], a["fmt"], v(a["xq"]),
+            v(a["xs"]), v(a["rq"]), v(a["rs"]), a["cap"], v(a["ntpr"]), v(a["ntpe"]), v(a["itr"]), v(a["off"]),
+            v(a["nre"]), v(a["src"]), v(a["send"]), v(a["ridx"]), v(a["rw"]), v(a["ws"]), a["wsb"], None)
+
+    assert call(H=200) == -1            # FP8 rows need hidden % 128 == 0
+    assert call(fmt=3) == -1            # scale format
+    assert call(xq=0) == -1             # missing cast codes
+    assert call(xq=FAKE + 8) == -1      # codes not 16-byte aligned
+    assert call(xs=0) == -1             # missing cast scales
+    assert call(xs=FAKE + 2) == -1      # fp32 scales misaligned
+    assert call(rq=0) == -1             # missing receive codes
+    assert call(rs=0) == -1             # missing receive scales
+    assert call(x=0) == -1
+    assert call(cap=255) == -2
+    assert call(E=15) == -1
+    assert call(ntpr=0) == -1
+    assert call(rw=0) == -1             # recv_topk_idx without recv_topk_weights
+    assert call(ws=0) == -3
     assert lib.cgd_last_error()
 
 

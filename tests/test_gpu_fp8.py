@@ -259,3 +259,60 @@ def test_layout_and_dispatch_cast_parity(fmt, T, K, E, R, H, A, extra, p_neg):
         assert (rq.index_select(0, empty) == 0xA5).all()
         sv = rs.index_select(0, empty)
         assert ((sv == 0x5A) if fmt == cgd.SCALE_UE8M0 else (sv == -7.0)).all()
+
+
+@pytest.mark.parametrize("fmt,T,K,E,R,H,A,p_neg", [(cgd.SCALE_F32, 4096, 8, 256, 8, 7168, 1, 0.0),
+                                                   (cgd.SCALE_UE8M0, 2049, 6, 96, 12, 384, 4, 0.2),
+                                                   (cgd.SCALE_POW2, 1500, 16, 512, 64, 256, 8, 0.0),
+                                                   (cgd.SCALE_F32, 128, 8, 256, 16, 1024, 1, 0.0),
+                                                   (cgd.SCALE_UE8M0, 300, 4, 64, 8, 128, 1, 0.1),
+                                                   (cgd.SCALE_F32, 0, 4, 16, 4, 256, 2, 0.0)])
+def test_layout_and_normal_dispatch_cast_parity(fmt, T, K, E, R, H, A, p_neg):
+    """Rank-granular layout + dispatch with the cast done by the plan's idle
+    blocks (by a cast launch for a one-tile batch): the cast tuple equals the
+    oracle's per-token cast, the layout and handle the oracle's, and every
+    received row holds its token's codes and scales."""
+    rng = np.random.default_rng(T + 3 * K)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64) if T else np.zeros((0, K), np.int64)
+    idx[rng.random((T, K)) < p_neg] = -1
+    x = _x(T, H, seed=T + 9) if T else np.zeros((0, H), np.uint16)
+    wts = synth.softmax_weights(synth.stream_key(T, 57, 3), T, K)
+    say(f"[fp8] layout_and_normal_dispatch cast fmt={fmt} T={T} K={K} E={E} R={R} H={H} A={A}")
+    lay, recv, ridx, rw, nre, h = cgd.layout_and_normal_dispatch(dev_bf16(x), dev_i64(idx), dev_f32(wts), E, R,
+                                                                 expert_alignment=A, cast_fp8=fmt)
+    torch.cuda.synchronize()
+    ntpr, _, ntpe, itr, _ = lay
+    ol = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), ol[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
+    o = oracle.dispatch_normal(None, ol[2], E, K, ol[1], idx, wts, align=A, cap=h.recv_capacity)
+    np.testing.assert_array_equal(h.rank_offset.cpu().numpy(), o["rank_offset"])
+    np.testing.assert_array_equal(nre.cpu().numpy(), o["num_recv_tokens_per_expert"])
+    np.testing.assert_array_equal(h.send_row.cpu().numpy(), o["send_row"])
+    np.testing.assert_array_equal(h.recv_src_idx.cpu().numpy(), o["recv_src_idx"])
+    np.testing.assert_array_equal(ridx.cpu().numpy(), o["recv_topk_idx"])
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), o["recv_topk_weights"].view(np.uint32))
+    if T:
+        oq, osc = oracle.cast_to_fp8(x, fmt)
+        _check_rows(recv, oq, osc, o["send_row"])
+        # the library's standalone cast gives the same tuple the plan's blocks wrote
+        q2, s2 = cgd.per_token_cast_to_fp8(dev_bf16(x), fmt)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(q2.view(torch.uint8).cpu().numpy(), oq)
+        np.testing.assert_array_equal(_scales_np(s2).view(np.uint8), osc.view(np.uint8))
+
+
+def test_layout_and_normal_dispatch_cast_writes_the_callers_tuple():
+    """x_fp8 given: the plan's blocks cast into the caller's (codes, scales)."""
+    T, K, E, R, H = 1000, 8, 64, 8, 512
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    x = _x(T, H, seed=5)
+    q = torch.full((T, H), 0x7E, dtype=torch.uint8, device=DEV)
+    sc = torch.zeros((T, H // 128), dtype=torch.float32, device=DEV)
+    cgd.layout_and_normal_dispatch(dev_bf16(x), dev_i64(idx), None, E, R, cast_fp8=cgd.SCALE_F32, x_fp8=(q, sc))
+    torch.cuda.synchronize()
+    oq, osc = oracle.cast_to_fp8(x, cgd.SCALE_F32)
+    np.testing.assert_array_equal(q.cpu().numpy(), oq)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
