@@ -58,14 +58,22 @@ def _fp8_step(x, idx, wt, w, out):
     return [ntpr, ntpe, itr, h.expert_offset, h.dst_row, h.recv_src_idx, nre, q.view(torch.uint8), sc]
 
 
+def _normal_fp8_step(x, idx, wt, w, out):
+    (ntpr, _, ntpe, itr, _), (q, sc), ridx, rw, nre, h = cgd.layout_and_normal_dispatch(x, idx, wt, w.E, w.R,
+                                                                                        cast_fp8=cgd.SCALE_F32)
+    data = (h.recv_src_idx >= 0).unsqueeze(1)  # rows past the data are not written: compare them as zero
+    return [ntpr, ntpe, itr, h.rank_offset, h.send_row, h.recv_src_idx, ridx, nre,
+            q.view(torch.uint8) * data.to(torch.uint8), torch.where(data, sc, torch.zeros_like(sc))]
+
+
 @pytest.mark.parametrize("kind,T", [("expert", 2500), ("small", 200), ("small_layout", 128), ("normal", 2500),
                                     ("normal", 100), ("layout", 2500), ("normal_whole", 2500),
-                                    ("fp8_cast", 2500)])
+                                    ("fp8_cast", 2500), ("normal_fp8", 2500)])
 def test_step_replays_from_a_captured_graph(kind, T):
     w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
     step = {"expert": _expert_step, "small": _small_step, "small_layout": _small_layout_step,
             "normal": _normal_step, "layout": _layout_step, "normal_whole": _normal_whole_step,
-            "fp8_cast": _fp8_step}[kind]
+            "fp8_cast": _fp8_step, "normal_fp8": _normal_fp8_step}[kind]
     inputs = [synth.make_inputs(w, seed=s) for s in range(5)]
     sx = dev_bf16(inputs[0]["x"])
     sidx = dev_i64(inputs[0]["topk_idx"])
