@@ -266,7 +266,8 @@ def test_layout_and_dispatch_cast_parity(fmt, T, K, E, R, H, A, extra, p_neg):
                                                    (cgd.SCALE_POW2, 1500, 16, 512, 64, 256, 8, 0.0),
                                                    (cgd.SCALE_F32, 128, 8, 256, 16, 1024, 1, 0.0),
                                                    (cgd.SCALE_UE8M0, 300, 4, 64, 8, 128, 1, 0.1),
-                                                   (cgd.SCALE_F32, 0, 4, 16, 4, 256, 2, 0.0)])
+                                                   (cgd.SCALE_F32, 0, 4, 16, 4, 256, 2, 0.0),
+                                                   (cgd.SCALE_POW2, 700, 9, 384, 384, 128, 1, 0.05)])
 def test_layout_and_normal_dispatch_cast_parity(fmt, T, K, E, R, H, A, p_neg):
     """Rank-granular layout + dispatch with the cast done by the plan's idle
     blocks (by a cast launch for a one-tile batch): the cast tuple equals the

@@ -328,7 +328,8 @@ def test_layout_and_normal_plan_in_one_launch(T, K, E, R, H, align, p_neg):
 @pytest.mark.parametrize("T,K,E,R,H,align,p_neg,with_topk",
                          [(4096, 8, 256, 8, 7168, 1, 0.0, True), (128, 8, 256, 16, 1024, 1, 0.0, True),
                           (2049, 6, 96, 12, 136, 4, 0.2, True), (1500, 16, 512, 64, 256, 8, 0.0, True),
-                          (700, 8, 64, 8, 64, 1, 0.0, False), (0, 4, 16, 4, 64, 2, 0.0, True)])
+                          (700, 8, 64, 8, 64, 1, 0.0, False), (0, 4, 16, 4, 64, 2, 0.0, True),
+                          (700, 9, 384, 384, 64, 1, 0.05, True)])
 def test_layout_and_normal_dispatch_in_one_call(T, K, E, R, H, align, p_neg, with_topk):
     """layout_and_normal_dispatch (the plan pulls x toward the caches, then the
     apply): layout outputs, plan, rows and per-row outputs equal the oracle's,
