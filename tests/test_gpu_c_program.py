@@ -1,7 +1,9 @@
 """The boundary from C: tests/c/cgd_c_roundtrip.c includes only cgd.h (and the
 HIP runtime header it needs), links libcgd, and checks layout, dispatch and
 combine against the oracle on seeded inputs (one-launch, several-tile and
-top-16 batches) with no Python or torch in the process. The CPU suite
+top-16 batches), and the one-call rank-granular layout + dispatch in bf16 and
+with the FP8 cast (one tile and several), with no Python or torch in the
+process. The CPU suite
 compiles and links it; the GPU suite runs it."""
 import os
 import subprocess
