@@ -510,6 +510,14 @@ int cgd_layout_and_normal_dispatch(const void* x, int64_t num_tokens, int hidden
                                       recv_src_idx, send_row, recv_topk_idx, recv_topk_weights, workspace,
                                       workspace_bytes)))
         return rc;
+    if (cgd::normal_dispatch_fuses(num_tokens)) {  // one tile (decode): layout, plan and rows in one launch
+        const hipError_t err = cgd::launch_layout_and_normal_fused(
+            x, num_tokens, hidden, topk_idx, recv_topk_idx ? topk_weights : nullptr, num_topk, num_experts, num_ranks,
+            expert_alignment, recv_x, recv_capacity, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank,
+            rank_offset, num_recv_tokens_per_expert, recv_src_idx, send_row, recv_topk_idx, recv_topk_weights,
+            workspace, stream);
+        return err == hipSuccess ? CGD_OK : hip_fail(err, "layout and normal dispatch launch");
+    }
     hipError_t err = cgd::launch_layout_and_normal_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
                                                         expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
                                                         is_token_in_rank, rank_offset, num_recv_tokens_per_expert,

@@ -887,7 +887,7 @@ static SideRows fp8_side(const void* scales, int64_t st, int64_t sb, int H, int 
 
 // Compute units of the current device (cached per device; host threads may
 // race on the cache, each storing the same value).
-static int device_cus() {
+int device_cus() {
     static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -219,6 +219,209 @@ __global__ __launch_bounds__(kLayoutTile) void layout_kernel(const int64_t* __re
     reset_ticket(ticket);
 }
 
+// Rows of the one-launch rank-granular dispatch (normal_fused_kernel).
+struct NormalRowsOut {
+    const uint4* x;  // bf16 [T, H] as nvec 16-byte vectors per token
+    int nvec, nchunk;
+    const float* topk_w;  // read only with recv_topk_idx
+    uint4* recv_x;
+    int64_t cap;
+    int32_t* send_row;
+    int32_t* recv_src_idx;
+    int64_t* recv_topk_idx;  // nullptr: no top-k metadata
+    float* recv_topk_w;
+};
+constexpr int kNormalFusedItems = 4;  // (token, 1 KB chunk) items per wave at most
+
+// A batch of at most one tile (decode), rank-granular, in one launch: the
+// layout, the plan and the rows. Every block plans the whole tile in LDS (the
+// same tile work as layout_kernel: rank masks, per-wave ballots per rank as
+// group words, per-rank distinct-token counts, and a block scan of those
+// counts into the rank offsets), which costs less than a second launch. In a
+// grid of several blocks, block 0 alone writes the layout and plan outputs
+// (the workspace's plan included, so that a later apply can read it) and
+// moves no rows; the waves of the other blocks each take up to
+// kNormalFusedItems (token, chunk) items. A token's row on rank r is the rank
+// offset + the rank's tokens in earlier waves + the popcount of the group word
+// below the token, as the two-launch path computes it from the workspace.
+// Each item's x chunk is loaded once (after the routing is staged: loads
+// complete in issue order) and stored to every row of the token with
+// non-temporal stores; a token's chunk-0 item writes its send_row entries,
+// recv_src_idx and each row's rank-local top-k ids and weights. Every block
+// fills a share of the rows past the data.
+template <int RW>
+__global__ __launch_bounds__(kLayoutTile) void normal_fused_kernel(const int64_t* __restrict__ topk_idx, int64_t T,
+                                                                   int K, int E, int R, int L,
+                                                                   int32_t* __restrict__ ntpr,
+                                                                   int32_t* __restrict__ ntpe,
+                                                                   uint8_t* __restrict__ itr, NormalPlanOut np,
+                                                                   NormalRowsOut ro) {
+    constexpr int kGroups = kLayoutTile / kWave;
+    __shared__ int32_t s_idx[kLayoutTile * kMaxTopk];
+    __shared__ uint64_t s_mask[kLayoutTile * RW];
+    __shared__ int32_t s_hist[kMaxExperts];
+    __shared__ int32_t s_rank[kMaxRanks];
+    __shared__ int16_t s_rank_of[kMaxExperts];
+    __shared__ uint64_t s_bal[kGroups * kMaxRanks];
+    __shared__ int32_t s_gpre[kGroups * kMaxRanks];
+    __shared__ int32_t s_off[kMaxRanks + 1];
+    __shared__ int32_t s_wsum[kGroups];
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int nt = (int)T;  // 1 <= T <= kLayoutTile
+    const bool writer = blockIdx.x == 0;
+    const unsigned m0 = gridDim.x > 1 ? 1u : 0u;  // blocks m0.. move the rows
+    const int lshift = (L & (L - 1)) == 0 ? __builtin_ctz(L) : -1;
+
+    // this wave's items: token (-1: none) and the lane's vector of the chunk
+    int it[kNormalFusedItems], iv[kNormalFusedItems];
+    {
+        const unsigned nbm = gridDim.x - m0;
+        const unsigned w0 = (blockIdx.x - m0) * kGroups + __builtin_amdgcn_readfirstlane(tid / kWave);
+#pragma unroll
+        for (int j = 0; j < kNormalFusedItems; ++j) {
+            const unsigned item = w0 + (unsigned)j * nbm * kGroups;
+            const unsigned tj = item / (unsigned)ro.nchunk;
+            it[j] = (blockIdx.x >= m0 && tj < (unsigned)nt) ? (int)tj : -1;
+            iv[j] = (int)(item - tj * (unsigned)ro.nchunk) * kWave + lane;
+        }
+    }
+    const bool direct = K <= kDirectTopk;
+    int64_t raw[kMaxTopk];
+    {
+        const int64_t* tok = topk_idx + min(tid, nt - 1) * K;
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k) raw[k] = (direct && tid < nt && k < K) ? tok[k] : -1;
+    }
+    for (int i = tid; i < E; i += kLayoutTile) {
+        s_hist[i] = 0;
+        s_rank_of[i] = (int16_t)(i / L);
+    }
+    for (int i = tid; i < R; i += kLayoutTile) s_rank[i] = 0;
+    if (!direct) stage_routing<kMaxTopk, kLayoutTile>(topk_idx, nt * K, E, s_idx);
+    __syncthreads();
+    uint4 buf[kNormalFusedItems];
+    float wk[kNormalFusedItems];
+    const bool with_topk = ro.recv_topk_idx != nullptr;
+#pragma unroll
+    for (int j = 0; j < kNormalFusedItems; ++j) {
+        buf[j] = make_uint4(0, 0, 0, 0);
+        if (it[j] >= 0 && iv[j] < ro.nvec) buf[j] = ro.x[(int64_t)it[j] * ro.nvec + iv[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < kNormalFusedItems; ++j) {
+        wk[j] = 0.0f;
+        if (with_topk && it[j] >= 0 && iv[j] < kWave && lane < K) wk[j] = ro.topk_w[(int64_t)it[j] * K + lane];
+    }
+
+    int e[kMaxTopk];
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) {
+        if (direct)
+            e[k] = (raw[k] >= 0 && raw[k] < E) ? (int)raw[k] : -1;
+        else
+            e[k] = (tid < nt && k < K) ? s_idx[tid * K + k] : -1;
+    }
+    if (direct && tid < nt)  // the rows' top-k metadata reads other tokens' slots
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k)
+            if (k < K) s_idx[tid * K + k] = e[k];
+    if (writer)
+#pragma unroll
+        for (int k = 0; k < kMaxTopk; ++k)
+            if (e[k] >= 0) atomicAdd(&s_hist[e[k]], 1);
+    uint64_t m[RW];
+    token_rank_mask<RW>(e, s_rank_of, lshift, m);
+    count_rank_tokens<RW>(m, R, s_rank, s_mask, s_bal);
+    __syncthreads();
+    // rows of each rank in earlier waves (group bases), then the rank offsets
+    for (int r = tid; r < R; r += kLayoutTile) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kGroups; ++w) {
+            s_gpre[w * R + r] = run;
+            run += __popcll(s_bal[w * R + r]);
+        }
+    }
+    block_exclusive_scan2(R, [&](int r) { return s_rank[r]; }, s_off, s_wsum);
+    __syncthreads();
+
+    if (writer) {
+        store_token_in_rank<RW, kLayoutTile>(m, s_mask, nt, R, itr);
+        for (int i = tid; i < E; i += kLayoutTile) {
+            ntpe[i] = s_hist[i];
+            if (np.nrecv) np.nrecv[i] = (s_hist[i] + np.A - 1) / np.A * np.A;
+        }
+        for (int i = tid; i < R; i += kLayoutTile) {
+            ntpr[i] = s_rank[i];
+            np.tile_base[i] = 0;
+        }
+        for (int r = tid; r <= R; r += kLayoutTile) np.rank_offset[r] = s_off[r];
+        const int gr = (nt + kWave - 1) / kWave * R;  // the plan's group words and bases, [groups, R]
+        for (int i = tid; i < gr; i += kLayoutTile) {
+            np.grp_bal[i] = s_bal[i];
+            np.grp_pre[i] = s_gpre[i];
+        }
+    }
+    {  // rows past the data carry no token, no expert and zero weights
+        const int64_t n = min((int64_t)s_off[R], ro.cap);
+        const int64_t stride = (int64_t)gridDim.x * kLayoutTile;
+        const int64_t i0 = (int64_t)blockIdx.x * kLayoutTile + tid;
+        for (int64_t r = n + i0; r < ro.cap; r += stride) ro.recv_src_idx[r] = -1;
+        if (with_topk)
+            for (int64_t i = n * K + i0; i < ro.cap * K; i += stride) {
+                ro.recv_topk_idx[i] = -1;
+                ro.recv_topk_w[i] = 0.0f;
+            }
+    }
+
+#pragma unroll
+    for (int j = 0; j < kNormalFusedItems; ++j) {
+        const int t = it[j];
+        if (t < 0) continue;
+        const bool first = iv[j] < kWave;  // the token's chunk-0 item (wave-uniform)
+        const int g = t / kWave;
+        const int bitpos = t % kWave;
+        const uint64_t below = (1ull << bitpos) - 1ull;
+        int er = -1, el = -1;  // rank and rank-local id of this lane's slot
+        if (first && with_topk && lane < K) {
+            const int ex = s_idx[t * K + lane];
+            if (ex >= 0) {
+                er = lshift >= 0 ? ex >> lshift : ex / L;
+                el = ex - er * L;
+            }
+        }
+        for (int rb = 0; rb < R; rb += kWave) {
+            const int r = rb + lane;
+            int d = -1;
+            if (r < R) {
+                const uint64_t b = s_bal[g * R + r];
+                if ((b >> bitpos) & 1ull) {
+                    const int64_t p = (int64_t)s_off[r] + s_gpre[g * R + r] + __popcll(b & below);
+                    d = p < ro.cap ? (int)p : -1;
+                }
+                if (first) ro.send_row[(int64_t)t * R + r] = d;
+            }
+            uint64_t msk = ballot(d >= 0);
+            while (msk) {
+                const int jj = __builtin_ctzll(msk);
+                msk &= msk - 1;
+                const int dd = __shfl(d, jj, kWave);
+                if (iv[j] < ro.nvec) store_nt(ro.recv_x + (int64_t)dd * ro.nvec + iv[j], buf[j]);
+                if (first) {
+                    if (lane == 0) ro.recv_src_idx[dd] = t;
+                    if (with_topk && lane < K) {
+                        const bool on = er == rb + jj;
+                        ro.recv_topk_idx[(int64_t)dd * K + lane] = on ? el : -1;
+                        ro.recv_topk_w[(int64_t)dd * K + lane] = on ? wk[j] : 0.0f;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // get_dispatch_layout alone: the same tile work in blocks of TILE tokens,
 // without a last-block handshake. Every block adds, for each expert and rank,
 // (1 << 32) + its count to a 64-bit accumulator in the workspace with one
@@ -382,6 +585,39 @@ hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int
     else
         hipLaunchKernelGGL((layout_kernel<6, true>), grid, block, 0, stream, topk_idx, T, K, E, R, L, ntpr, ntpe, itr,
                            partial, ticket, np, nblk, pv, pvecs, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_and_normal_fused(const void* x, int64_t T, int H, const int64_t* topk_idx,
+                                          const float* topk_w, int K, int E, int R, int A, void* recv_x, int64_t cap,
+                                          int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
+                                          int32_t* nrecv, int32_t* recv_src_idx, int32_t* send_row,
+                                          int64_t* recv_topk_idx, float* recv_topk_w, void* workspace,
+                                          hipStream_t stream) {
+    const NormalPlanArrays a = normal_plan_arrays(workspace, T, R);
+    const NormalPlanOut np{a.grp_bal, a.grp_pre, a.tile_base, rank_offset, nrecv, A};
+    const int nvec = H / 8;
+    const int nchunk = (nvec + kWave - 1) / kWave;
+    // one block per CU where that leaves at most kNormalFusedItems items per
+    // wave (every block plans the tile in LDS: blocks sharing a CU would share
+    // its LDS bandwidth for that); block 0 of a grid of several moves no rows
+    constexpr int kWaves = kLayoutTile / kWave;
+    const int64_t items = T * nchunk;
+    const int64_t per_block = (int64_t)kWaves * kNormalFusedItems;
+    const int64_t need = (items + per_block - 1) / per_block;
+    const int64_t fill = (items + kWaves - 1) / kWaves;
+    int64_t blocks = fill < device_cus() ? fill : device_cus();
+    if (blocks < need) blocks = need;
+    if (blocks > 1 && blocks < 1 + need) blocks = 1 + need;
+    const NormalRowsOut ro{reinterpret_cast<const uint4*>(x), nvec, nchunk, topk_w, reinterpret_cast<uint4*>(recv_x),
+                           cap, send_row, recv_src_idx, recv_topk_idx, recv_topk_w};
+    const dim3 grid((unsigned)(blocks < 1 ? 1 : blocks)), block(kLayoutTile);
+    if (R <= 64)
+        hipLaunchKernelGGL((normal_fused_kernel<1>), grid, block, 0, stream, topk_idx, T, K, E, R, E / R, ntpr, ntpe,
+                           itr, np, ro);
+    else
+        hipLaunchKernelGGL((normal_fused_kernel<6>), grid, block, 0, stream, topk_idx, T, K, E, R, E / R, ntpr, ntpe,
+                           itr, np, ro);
     return hipGetLastError();
 }
 

@@ -216,7 +216,8 @@ static void run_case(const char* name, int64_t T, int K, int E, int R, int H, in
 
 /* Rank-granular layout + dispatch in one call (bf16), and with the FP8 cast
  * done by the plan's idle blocks: layout, plan, rows and per-row outputs
- * against the oracle's rank-granular dispatch and per-token cast. */
+ * against the oracle's rank-granular dispatch and per-token cast; an apply
+ * from the plan the bf16 call leaves in the workspace gives the same rows. */
 static void run_normal_case(const char* name, int64_t T, int K, int E, int R, int H, int A, uint64_t seed,
                             hipStream_t stream) {
     printf("[%s] T=%lld K=%d E=%d R=%d H=%d alignment=%d\n", name, (long long)T, K, E, R, H, A);
@@ -326,6 +327,26 @@ static void run_normal_case(const char* name, int64_t T, int K, int E, int R, in
         }
         expect(meta_ok, "recv_topk_idx / recv_topk_weights", name);
         expect(rows_ok, fp8 ? "received FP8 rows" : "received rows", name);
+        if (!fp8) {
+            /* the workspace now holds the plan: an apply from it gives the same rows */
+            void* d_recv2 = dev_alloc(sizeof(uint16_t) * (size_t)(cap * H));
+            int32_t* d_src2 = dev_alloc(sizeof(int32_t) * (size_t)cap);
+            int32_t* d_send2 = dev_alloc(sizeof(int32_t) * (size_t)(T * R));
+            CGD_OK_(cgd_normal_dispatch_apply(d_x, T, H, NULL, NULL, K, E, R, d_recv2, cap, d_roff, d_src2, d_send2,
+                                              NULL, NULL, d_ws, ws_bytes, stream));
+            HIP_OK(hipStreamSynchronize(stream));
+            int32_t* g_send2 = host_copy(d_send2, sizeof(int32_t) * (size_t)(T * R));
+            int32_t* g_src2 = host_copy(d_src2, sizeof(int32_t) * (size_t)cap);
+            uint16_t* g_recv2 = host_copy(d_recv2, sizeof(uint16_t) * (size_t)(cap * H));
+            expect(!memcmp(g_send2, o_send, sizeof(int32_t) * (size_t)(T * R)), "send_row of the plan left", name);
+            expect(!memcmp(g_src2, o_src, sizeof(int32_t) * (size_t)cap), "recv_src_idx of the plan left", name);
+            int ok2 = 1;
+            for (int64_t r = 0; r < cap; ++r)
+                if (o_src[r] >= 0) ok2 &= !memcmp(g_recv2 + r * H, o_recv + r * H, sizeof(uint16_t) * (size_t)H);
+            expect(ok2, "rows of the plan left in the workspace", name);
+            free(g_send2); free(g_src2); free(g_recv2);
+            HIP_OK(hipFree(d_recv2)); HIP_OK(hipFree(d_src2)); HIP_OK(hipFree(d_send2));
+        }
         free(g_ntpr); free(g_ntpe); free(g_itr); free(g_roff); free(g_nre); free(g_src); free(g_send);
         free(g_ridx); free(g_rw);
     }

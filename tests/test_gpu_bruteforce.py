@@ -82,7 +82,8 @@ def test_all_small_routings_rank_granular(R):
     """The same routings through the rank-granular path: layout + plan in one
     launch, the apply (rows, send_row, rank-local top-k ids and weights) and
     the combine of identity experts (x times the token's rank count, exact),
-    all bit for bit."""
+    and the one-call layout + dispatch (one launch at this size), all bit for
+    bit."""
     cases = np.array(list(itertools.product(ROWS, repeat=T)), dtype=np.int64)
     rng = np.random.default_rng(10 + R)
     x_bits = (rng.integers(0, 2, (T, H)) << 15 | rng.integers(0x3C00, 0x4100, (T, H))).astype(np.uint16)
@@ -96,12 +97,16 @@ def test_all_small_routings_rank_granular(R):
         (ntpr, _, ntpe, itr, _), plan = cgd.layout_and_normal_dispatch_plan(idx, E, R)
         recv, ridx, rw, _, h = cgd.normal_dispatch_apply(x, plan, idx, w)
         out, cw = cgd.normal_combine(recv, h, rw)
+        (ntpr2, _, ntpe2, itr2, _), recv2, ridx2, rw2, nre2, h2 = cgd.layout_and_normal_dispatch(x, idx, w, E, R)
         res.append((ntpr, ntpe, itr, plan.rank_offset, plan.num_recv_tokens_per_expert, h.send_row,
-                    h.recv_src_idx, ridx, rw.view(torch.int32), recv, out, cw.view(torch.int32)))
+                    h.recv_src_idx, ridx, rw.view(torch.int32), recv, out, cw.view(torch.int32),
+                    ntpr2, ntpe2, itr2, h2.rank_offset, nre2, h2.send_row, h2.recv_src_idx, ridx2,
+                    rw2.view(torch.int32), recv2))
     torch.cuda.synchronize()
-    (ntpr, ntpe, itr, off, nre, send, src, ridx, rw, recv, out, cw) = (_stack([r[i] for r in res])
-                                                                       for i in range(12))
-    recv, out = recv.view(np.uint16), out.view(np.uint16)
+    (ntpr, ntpe, itr, off, nre, send, src, ridx, rw, recv, out, cw,
+     ntpr2, ntpe2, itr2, off2, nre2, send2, src2, ridx2, rw2, recv2) = (_stack([r[i] for r in res])
+                                                                        for i in range(22))
+    recv, out, recv2 = recv.view(np.uint16), out.view(np.uint16), recv2.view(np.uint16)
     for c, idx in enumerate(cases):
         o_ntpr, o_ntpe, o_itr = oracle.layout(idx, E, R)
         np.testing.assert_array_equal(ntpr[c], o_ntpr, err_msg=f"case {c}")
@@ -119,6 +124,12 @@ def test_all_small_routings_rank_granular(R):
         o_out, o_cw = oracle.combine_normal(o["recv_x"], o["send_row"], o["recv_topk_weights"])
         np.testing.assert_array_equal(out[c], o_out, err_msg=f"case {c}")
         np.testing.assert_array_equal(cw[c], o_cw.view(np.int32), err_msg=f"case {c}")
+        for got, want in ((ntpr2, o_ntpr), (ntpe2, o_ntpe), (itr2, o_itr), (off2, o["rank_offset"]),
+                          (nre2, o["num_recv_tokens_per_expert"]), (send2, o["send_row"]),
+                          (src2, o["recv_src_idx"]), (ridx2, o["recv_topk_idx"]),
+                          (rw2, o["recv_topk_weights"].view(np.int32))):
+            np.testing.assert_array_equal(got[c], want, err_msg=f"one call, case {c}")
+        np.testing.assert_array_equal(recv2[c][data], o["recv_x"][data], err_msg=f"one call, case {c}")
 
 
 @pytest.mark.parametrize("R", [1, 2, 4])

@@ -329,11 +329,15 @@ def test_layout_and_normal_plan_in_one_launch(T, K, E, R, H, align, p_neg):
                          [(4096, 8, 256, 8, 7168, 1, 0.0, True), (128, 8, 256, 16, 1024, 1, 0.0, True),
                           (2049, 6, 96, 12, 136, 4, 0.2, True), (1500, 16, 512, 64, 256, 8, 0.0, True),
                           (700, 8, 64, 8, 64, 1, 0.0, False), (0, 4, 16, 4, 64, 2, 0.0, True),
-                          (700, 9, 384, 384, 64, 1, 0.05, True)])
+                          (700, 9, 384, 384, 64, 1, 0.05, True),
+                          # one tile: layout, plan and rows in one launch
+                          (256, 8, 256, 8, 7168, 1, 0.0, True), (1, 8, 256, 16, 7168, 1, 0.0, True),
+                          (200, 9, 384, 384, 64, 1, 0.05, True), (100, 6, 90, 6, 136, 4, 0.2, True),
+                          (64, 16, 512, 64, 256, 8, 0.0, False), (65, 3, 48, 3, 8, 2, 0.3, True)])
 def test_layout_and_normal_dispatch_in_one_call(T, K, E, R, H, align, p_neg, with_topk):
     """layout_and_normal_dispatch (the plan pulls x toward the caches, then the
-    apply): layout outputs, plan, rows and per-row outputs equal the oracle's,
-    and the handle serves the combine."""
+    apply; a batch of one tile in one launch): layout outputs, plan, rows and
+    per-row outputs equal the oracle's, and the handle serves the combine."""
     rng = np.random.default_rng(T + 11 * R)
     idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64) if T else np.zeros((0, K), np.int64)
     idx[rng.random((T, K)) < p_neg] = -1

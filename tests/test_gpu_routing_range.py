@@ -100,7 +100,7 @@ def test_out_of_range_routing_in_layout_and_dispatch(T, K, E, R):
     say(f"[routing range] T={T}: packed layout ok")
 
 
-@pytest.mark.parametrize("T,K,E,R", CASES[:3])
+@pytest.mark.parametrize("T,K,E,R", CASES[:4])
 def test_out_of_range_routing_in_rank_granular_dispatch(T, K, E, R):
     idx_bad, clean = _routing(T, K, E, seed=3 * T + K)
     H = 64
@@ -133,4 +133,13 @@ def test_out_of_range_routing_in_rank_granular_dispatch(T, K, E, R):
     np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
     np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
     check(plan.rank_offset, nre, h, recv_x, ridx, rw)
+
+    # layout, plan and rows in one call (one launch for a batch of one tile)
+    (ntpr, _, ntpe, itr, _), recv_x, ridx, rw, nre, h = cgd.layout_and_normal_dispatch(dev_bf16(x), idx_dev,
+                                                                                       dev_f32(wts), E, R)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), ol[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
+    check(h.rank_offset, nre, h, recv_x, ridx, rw)
     say(f"[routing range, normal] T={T}: ok")
