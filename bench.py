@@ -379,8 +379,10 @@ class NormalPath(_Path):
                               if self.w.T <= 256 else
                               "layout_and_normal_dispatch (layout + rank-granular plan with x pulled toward the "
                               "caches, then the apply)") if self.fmt is None else
-                             "layout_and_normal_dispatch with the cast (layout + rank-granular plan whose idle "
-                             "blocks cast x, then the apply of the FP8 tuple)"),
+                             ("layout_and_normal_dispatch with the cast (layout, rank-granular plan, cast and rows "
+                              "in one launch)" if self.w.T <= 256 else
+                              "layout_and_normal_dispatch with the cast (layout + rank-granular plan whose idle "
+                              "blocks cast x, then the apply of the FP8 tuple)")),
                 "experts": "identity (combine reads dispatched rows), no bias" if self.fmt is None else
                 "identity (combine reads the cast-back FP8 rows, made before timing), no bias"}
 

@@ -557,6 +557,14 @@ int cgd_layout_and_normal_dispatch_cast_fp8(const void* x, int64_t num_tokens, i
         return rc;
     if ((rc = check_scales(recv_scales, 0, 0, scale_format, num_tokens > 0 && recv_capacity > 0))) return rc;
     const cgd::NormalCast cast{x, hidden, scale_format, x_fp8, x_scales};
+    if (cgd::normal_dispatch_fuses(num_tokens)) {  // one tile (decode): layout, plan, cast and rows in one launch
+        const hipError_t err = cgd::launch_layout_and_normal_fused(
+            x, num_tokens, hidden, topk_idx, recv_topk_idx ? topk_weights : nullptr, num_topk, num_experts, num_ranks,
+            expert_alignment, recv_x_fp8, recv_capacity, num_tokens_per_rank, num_tokens_per_expert,
+            is_token_in_rank, rank_offset, num_recv_tokens_per_expert, recv_src_idx, send_row, recv_topk_idx,
+            recv_topk_weights, workspace, stream, &cast, recv_scales);
+        return err == hipSuccess ? CGD_OK : hip_fail(err, "layout, normal dispatch and cast launch");
+    }
     hipError_t err = cgd::launch_layout_and_normal_plan(topk_idx, num_tokens, num_topk, num_experts, num_ranks,
                                                         expert_alignment, num_tokens_per_rank, num_tokens_per_expert,
                                                         is_token_in_rank, rank_offset, num_recv_tokens_per_expert,

@@ -95,17 +95,21 @@ struct NormalCast {
 #define CGD_CAST_BLOCKS 4096
 #endif
 constexpr int kCastBlocks = CGD_CAST_BLOCKS;
+
 // Rank-granular layout + plan + apply of a batch of at most one layout tile
 // in one launch (every block plans the tile in LDS; block 0 writes the
 // layout and plan outputs, the workspace's plan included; the others move
 // the rows). recv_topk_idx == nullptr: no top-k metadata (topk_w unused).
+// With cast: x is cast to FP8 into cast->q / cast->scales on the way and
+// recv_x / recv_scales receive the codes and scales.
 inline bool normal_dispatch_fuses(int64_t T) { return T > 0 && T <= kLayoutTile; }
 hipError_t launch_layout_and_normal_fused(const void* x, int64_t T, int H, const int64_t* topk_idx,
                                           const float* topk_w, int K, int E, int R, int A, void* recv_x, int64_t cap,
                                           int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
                                           int32_t* nrecv, int32_t* recv_src_idx, int32_t* send_row,
                                           int64_t* recv_topk_idx, float* recv_topk_w, void* workspace,
-                                          hipStream_t stream);
+                                          hipStream_t stream, const NormalCast* cast = nullptr,
+                                          void* recv_scales = nullptr);
 int device_cus();  // compute units of the current device
 
 hipError_t launch_layout_and_normal_plan(const int64_t* topk_idx, int64_t T, int K, int E, int R, int A,

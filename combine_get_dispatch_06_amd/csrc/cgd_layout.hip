@@ -230,6 +230,14 @@ struct NormalRowsOut {
     int32_t* recv_src_idx;
     int64_t* recv_topk_idx;  // nullptr: no top-k metadata
     float* recv_topk_w;
+    // CAST form: the per-token FP8 cast of x (codes [T, H] as nvec 8-byte
+    // vectors per token, row-major scales [T, nsb], fp32 or one UE8M0 byte
+    // for fmt 2), and the receive rows of codes and scales in place of recv_x
+    int fmt, nsb;
+    uint2* xq;
+    void* xs;
+    uint2* rq;
+    void* rs;
 };
 constexpr int kNormalFusedItems = 4;  // (token, 1 KB chunk) items per wave at most
 
@@ -248,8 +256,11 @@ constexpr int kNormalFusedItems = 4;  // (token, 1 KB chunk) items per wave at m
 // complete in issue order) and stored to every row of the token with
 // non-temporal stores; a token's chunk-0 item writes its send_row entries,
 // recv_src_idx and each row's rank-local top-k ids and weights. Every block
-// fills a share of the rows past the data.
-template <int RW>
+// fills a share of the rows past the data. CAST: each item also casts its
+// chunk to FP8 as the per-token cast does (a 16-lane group holds one
+// 128-channel block), writes the codes and scales to the cast tuple, and
+// moves them, not the bf16 chunk, to the token's rows.
+template <int RW, bool CAST>
 __global__ __launch_bounds__(kLayoutTile) void normal_fused_kernel(const int64_t* __restrict__ topk_idx, int64_t T,
                                                                    int K, int E, int R, int L,
                                                                    int32_t* __restrict__ ntpr,
@@ -392,6 +403,23 @@ __global__ __launch_bounds__(kLayoutTile) void normal_fused_kernel(const int64_t
                 el = ex - er * L;
             }
         }
+        const bool in = iv[j] < ro.nvec;  // whole 16-lane groups are in or out (H % 128 == 0 with CAST)
+        uint2 code = make_uint2(0, 0);
+        Fp8Scale sc{0.0f, 0.0f, 0u};
+        if (CAST) {
+            sc = fp8_block_scale(group16_max(in ? absmax_bf16x8(buf[j]) : 0.0f), ro.fmt);
+            code = quantize_bf16x8(buf[j], sc.mul);
+            if (in) {
+                ro.xq[(int64_t)t * ro.nvec + iv[j]] = code;
+                if ((lane & 15) == 0) {
+                    const int64_t si = (int64_t)t * ro.nsb + iv[j] / 16;
+                    if (ro.fmt == 2)
+                        static_cast<uint8_t*>(ro.xs)[si] = (uint8_t)sc.ue8m0;
+                    else
+                        static_cast<float*>(ro.xs)[si] = sc.scale;
+                }
+            }
+        }
         for (int rb = 0; rb < R; rb += kWave) {
             const int r = rb + lane;
             int d = -1;
@@ -408,7 +436,20 @@ __global__ __launch_bounds__(kLayoutTile) void normal_fused_kernel(const int64_t
                 const int jj = __builtin_ctzll(msk);
                 msk &= msk - 1;
                 const int dd = __shfl(d, jj, kWave);
-                if (iv[j] < ro.nvec) store_nt(ro.recv_x + (int64_t)dd * ro.nvec + iv[j], buf[j]);
+                if (CAST) {
+                    if (in) {
+                        store_nt(ro.rq + (int64_t)dd * ro.nvec + iv[j], code);
+                        if ((lane & 15) == 0) {
+                            const int64_t si = (int64_t)dd * ro.nsb + iv[j] / 16;
+                            if (ro.fmt == 2)
+                                static_cast<uint8_t*>(ro.rs)[si] = (uint8_t)sc.ue8m0;
+                            else
+                                static_cast<float*>(ro.rs)[si] = sc.scale;
+                        }
+                    }
+                } else if (in) {
+                    store_nt(ro.recv_x + (int64_t)dd * ro.nvec + iv[j], buf[j]);
+                }
                 if (first) {
                     if (lane == 0) ro.recv_src_idx[dd] = t;
                     if (with_topk && lane < K) {
@@ -593,7 +634,7 @@ hipError_t launch_layout_and_normal_fused(const void* x, int64_t T, int H, const
                                           int32_t* ntpr, int32_t* ntpe, uint8_t* itr, int32_t* rank_offset,
                                           int32_t* nrecv, int32_t* recv_src_idx, int32_t* send_row,
                                           int64_t* recv_topk_idx, float* recv_topk_w, void* workspace,
-                                          hipStream_t stream) {
+                                          hipStream_t stream, const NormalCast* cast, void* recv_scales) {
     const NormalPlanArrays a = normal_plan_arrays(workspace, T, R);
     const NormalPlanOut np{a.grp_bal, a.grp_pre, a.tile_base, rank_offset, nrecv, A};
     const int nvec = H / 8;
@@ -609,15 +650,34 @@ hipError_t launch_layout_and_normal_fused(const void* x, int64_t T, int H, const
     int64_t blocks = fill < device_cus() ? fill : device_cus();
     if (blocks < need) blocks = need;
     if (blocks > 1 && blocks < 1 + need) blocks = 1 + need;
-    const NormalRowsOut ro{reinterpret_cast<const uint4*>(x), nvec, nchunk, topk_w, reinterpret_cast<uint4*>(recv_x),
-                           cap, send_row, recv_src_idx, recv_topk_idx, recv_topk_w};
+    NormalRowsOut ro{reinterpret_cast<const uint4*>(x), nvec, nchunk, topk_w, reinterpret_cast<uint4*>(recv_x),
+                     cap, send_row, recv_src_idx, recv_topk_idx, recv_topk_w, 0, 0, nullptr, nullptr, nullptr,
+                     nullptr};
+    if (cast) {  // recv_x holds the codes
+        ro.recv_x = nullptr;
+        ro.fmt = cast->fmt;
+        ro.nsb = H / kFp8Block;
+        ro.xq = reinterpret_cast<uint2*>(cast->q);
+        ro.xs = cast->scales;
+        ro.rq = reinterpret_cast<uint2*>(recv_x);
+        ro.rs = recv_scales;
+    }
     const dim3 grid((unsigned)(blocks < 1 ? 1 : blocks)), block(kLayoutTile);
-    if (R <= 64)
-        hipLaunchKernelGGL((normal_fused_kernel<1>), grid, block, 0, stream, topk_idx, T, K, E, R, E / R, ntpr, ntpe,
-                           itr, np, ro);
-    else
-        hipLaunchKernelGGL((normal_fused_kernel<6>), grid, block, 0, stream, topk_idx, T, K, E, R, E / R, ntpr, ntpe,
-                           itr, np, ro);
+#define CGD_NFUSED(RW, CAST)                                                                                         \
+    hipLaunchKernelGGL((normal_fused_kernel<RW, CAST>), grid, block, 0, stream, topk_idx, T, K, E, R, E / R, ntpr, \
+                       ntpe, itr, np, ro)
+    if (R <= 64) {
+        if (cast)
+            CGD_NFUSED(1, true);
+        else
+            CGD_NFUSED(1, false);
+    } else {
+        if (cast)
+            CGD_NFUSED(6, true);
+        else
+            CGD_NFUSED(6, false);
+    }
+#undef CGD_NFUSED
     return hipGetLastError();
 }
 

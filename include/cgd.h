@@ -501,7 +501,7 @@ int cgd_layout_and_normal_dispatch_plan(const int64_t* topk_idx, int64_t num_tok
  * outputs and errors as those two calls (topk_idx feeds the layout; topk_weights,
  * recv_topk_idx and recv_topk_weights are all given or all NULL); the
  * workspace is that of cgd_layout_and_normal_dispatch_plan and afterwards
- * holds the plan, as there. */
+ * holds the plan, as there. A batch of at most 256 tokens takes one launch. */
 int cgd_layout_and_normal_dispatch(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
                                    const float* topk_weights, int num_topk, int num_experts, int num_ranks,
                                    int expert_alignment, void* recv_x, int64_t recv_capacity,

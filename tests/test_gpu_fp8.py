@@ -267,10 +267,15 @@ def test_layout_and_dispatch_cast_parity(fmt, T, K, E, R, H, A, extra, p_neg):
                                                    (cgd.SCALE_F32, 128, 8, 256, 16, 1024, 1, 0.0),
                                                    (cgd.SCALE_UE8M0, 300, 4, 64, 8, 128, 1, 0.1),
                                                    (cgd.SCALE_F32, 0, 4, 16, 4, 256, 2, 0.0),
-                                                   (cgd.SCALE_POW2, 700, 9, 384, 384, 128, 1, 0.05)])
+                                                   (cgd.SCALE_POW2, 700, 9, 384, 384, 128, 1, 0.05),
+                                                   # one tile: layout, plan, cast and rows in one launch
+                                                   (cgd.SCALE_UE8M0, 200, 9, 384, 384, 128, 1, 0.05),
+                                                   (cgd.SCALE_POW2, 1, 8, 256, 16, 7168, 1, 0.0),
+                                                   (cgd.SCALE_F32, 256, 8, 256, 8, 7168, 1, 0.0),
+                                                   (cgd.SCALE_F32, 100, 6, 90, 6, 384, 4, 0.2)])
 def test_layout_and_normal_dispatch_cast_parity(fmt, T, K, E, R, H, A, p_neg):
     """Rank-granular layout + dispatch with the cast done by the plan's idle
-    blocks (by a cast launch for a one-tile batch): the cast tuple equals the
+    blocks (in the one launch of a one-tile batch): the cast tuple equals the
     oracle's per-token cast, the layout and handle the oracle's, and every
     received row holds its token's codes and scales."""
     rng = np.random.default_rng(T + 3 * K)
@@ -304,16 +309,20 @@ def test_layout_and_normal_dispatch_cast_parity(fmt, T, K, E, R, H, A, p_neg):
         np.testing.assert_array_equal(_scales_np(s2).view(np.uint8), osc.view(np.uint8))
 
 
-def test_layout_and_normal_dispatch_cast_writes_the_callers_tuple():
-    """x_fp8 given: the plan's blocks cast into the caller's (codes, scales)."""
-    T, K, E, R, H = 1000, 8, 64, 8, 512
+@pytest.mark.parametrize("T,fmt", [(1000, cgd.SCALE_F32), (200, cgd.SCALE_F32), (200, cgd.SCALE_UE8M0)])
+def test_layout_and_normal_dispatch_cast_writes_the_callers_tuple(T, fmt):
+    """x_fp8 given: the plan's blocks (for one tile, the one launch's moving
+    waves) cast into the caller's (codes, scales)."""
+    K, E, R, H = 8, 64, 8, 512
     rng = np.random.default_rng(5)
     idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
     x = _x(T, H, seed=5)
     q = torch.full((T, H), 0x7E, dtype=torch.uint8, device=DEV)
-    sc = torch.zeros((T, H // 128), dtype=torch.float32, device=DEV)
-    cgd.layout_and_normal_dispatch(dev_bf16(x), dev_i64(idx), None, E, R, cast_fp8=cgd.SCALE_F32, x_fp8=(q, sc))
+    sc = (torch.zeros((T, H // 128), dtype=torch.uint8, device=DEV) if fmt == cgd.SCALE_UE8M0 else
+          torch.zeros((T, H // 128), dtype=torch.float32, device=DEV))
+    say(f"[fp8] layout_and_normal_dispatch cast into the caller's tuple T={T} fmt={fmt}")
+    cgd.layout_and_normal_dispatch(dev_bf16(x), dev_i64(idx), None, E, R, cast_fp8=fmt, x_fp8=(q, sc))
     torch.cuda.synchronize()
-    oq, osc = oracle.cast_to_fp8(x, cgd.SCALE_F32)
+    oq, osc = oracle.cast_to_fp8(x, fmt)
     np.testing.assert_array_equal(q.cpu().numpy(), oq)
-    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint8), osc.view(np.uint8))
