@@ -143,6 +143,12 @@ struct TileOut {
     const uint4* x;  // FUSED only
     int nvec, nchunk;
     uint4* recv_x;
+    // FUSED with CAST: the rows receive x's FP8 codes (nvec 8-byte vectors
+    // per row, rq) and scales (nsb per row, rs: fp32, or a UE8M0 byte for
+    // fmt 2) in place of the bf16 rows
+    int fmt, nsb;
+    uint2* rq;
+    void* rs;
 };
 
 // rank_kernel. Slot loops read the routing from LDS, which keeps the kernel
@@ -170,8 +176,10 @@ struct TileOut {
 // Lanes without a token skip the LDS mask atomics. Larger batches
 // leave packed slot words and tile bases in the workspace for
 // finalize_kernel; blocks past the plan_tiles tiles (if any) prefetch x
-// (px, pvecs 16-byte vectors) and take no part in the plan.
-template <int RW, bool LAYOUT, bool FUSED = false>
+// (px, pvecs 16-byte vectors) and take no part in the plan. FUSED with CAST:
+// each item's chunk is cast to FP8 as the per-token cast does (a 16-lane
+// group holds one 128-channel block) and its codes and scales go to the rows.
+template <int RW, bool LAYOUT, bool FUSED = false, bool CAST = false>
 __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restrict__ topk_idx, int64_t T, int K, int E,
                                                          int ebits, int A, int seg_cap, int32_t* __restrict__ slot_pack,
                                                          int32_t* __restrict__ tile_base,
@@ -484,15 +492,34 @@ __global__ __launch_bounds__(kRankTile) void rank_kernel(const int64_t* __restri
     if (all_rows) __syncthreads();  // the moves below read the rows just written
 #pragma unroll
     for (int j = 0; j < kFusedItems; ++j) {
-        if (ft[j] < T) {
+        if (ft[j] < T) {  // wave-uniform
             int dl = -1;
             if (lane < K) {
                 const int v = s_slot[ft[j] * K + lane];
                 dl = all_rows ? v : row_of(v);
             }
+            const bool in = fv[j] < fc.nvec;  // with CAST whole 16-lane groups are in or out (H % 128 == 0)
+            uint2 code = make_uint2(0, 0);
+            Fp8Scale sc{0.0f, 0.0f, 0u};
+            if (CAST) {
+                sc = fp8_block_scale(group16_max(in ? absmax_bf16x8(fbuf[j]) : 0.0f), fc.fmt);
+                code = quantize_bf16x8(fbuf[j], sc.mul);
+            }
             for (int k = 0; k < K; ++k) {
                 const int d = __builtin_amdgcn_readlane(dl, k);
-                if (d >= 0 && fv[j] < fc.nvec) store_nt(fc.recv_x + (int64_t)d * fc.nvec + fv[j], fbuf[j]);
+                if (d < 0 || !in) continue;
+                if (CAST) {
+                    store_nt(fc.rq + (int64_t)d * fc.nvec + fv[j], code);
+                    if ((lane & 15) == 0) {
+                        const int64_t si = (int64_t)d * fc.nsb + fv[j] / 16;
+                        if (fc.fmt == 2)
+                            static_cast<uint8_t*>(fc.rs)[si] = (uint8_t)sc.ue8m0;
+                        else
+                            static_cast<float*>(fc.rs)[si] = sc.scale;
+                    }
+                } else {
+                    store_nt(fc.recv_x + (int64_t)d * fc.nvec + fv[j], fbuf[j]);
+                }
             }
         }
     }
@@ -916,7 +943,7 @@ static hipError_t launch_rank(const int64_t* topk_idx, int64_t T, int K, int E, 
     const int ntiles = (int)(T <= 0 ? 1 : (T + kRankTile - 1) / kRankTile);
     const dim3 block(kRankTile);
     const size_t lds = rank_lds_bytes(E, K);
-    const TileOut to{dst_row, recv_src_idx, cap, nullptr, 0, 1, nullptr};  // no rows to move
+    const TileOut to{dst_row, recv_src_idx, cap, nullptr, 0, 1, nullptr, -1, 0, nullptr, nullptr};  // no rows to move
     const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
     const LayoutOut& lo = layout ? *layout : none;
     const int64_t spare = cap - std::min<int64_t>(cap, std::max<int64_t>(T, 0) * K);
@@ -1044,6 +1071,64 @@ hipError_t launch_dispatch_cached_cast_fp8(const void* x, int64_t T, int H, int 
     return hipGetLastError();
 }
 
+// Plan and bf16 apply of a batch of at most one tile in one launch (the FUSED
+// rank kernel); seg_cap >= 0 for the fixed-capacity packed layout; with
+// layout, get_dispatch_layout's outputs from the same launch; fmt >= 0: the
+// rows receive x cast to FP8 (codes in recv_x, scales in recv_s).
+static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, const void* x,
+                               int H, void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* nrecv,
+                               int32_t* recv_src_idx,
+                               int32_t* dst_row, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
+                               hipStream_t stream, const LayoutOut* layout = nullptr, int fmt = -1,
+                               void* recv_s = nullptr) {
+    int ebits = 0;
+    while ((1 << ebits) < E) ++ebits;
+    const int nvec = H / 8;
+    const int nchunk = (nvec + kWave - 1) / kWave;
+    // one block per CU where that leaves at most kFusedItems items per wave:
+    // every block plans the whole batch in LDS, so blocks sharing a CU would
+    // share its LDS bandwidth for that
+    const int64_t items = T * nchunk;
+    const int64_t per_block = (int64_t)kRankWaves * kFusedItems;
+    int64_t blocks = std::max<int64_t>(std::min<int64_t>((items + kRankWaves - 1) / kRankWaves, device_cus()),
+                                       (items + per_block - 1) / per_block);
+    // in a grid of several blocks the first block (the first two with the
+    // layout outputs, in a grid of three or more) moves no rows: the others
+    // hold every item
+    const int64_t need = (items + per_block - 1) / per_block;
+    if (blocks > 1) blocks = std::max<int64_t>(blocks, 1 + need);
+    if (blocks > 2 && layout) blocks = std::max<int64_t>(blocks, 2 + need);
+    const dim3 grid((unsigned)std::max<int64_t>(1, blocks)), block(kRankTile);
+    const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
+    const bool cast = fmt >= 0;
+    const TileOut fc{dst_row, recv_src_idx, cap, reinterpret_cast<const uint4*>(x), nvec, nchunk,
+                     cast ? nullptr : reinterpret_cast<uint4*>(recv_x), fmt, H / kFp8Block,
+                     cast ? reinterpret_cast<uint2*>(recv_x) : nullptr, cast ? recv_s : nullptr};
+    const size_t lds = rank_lds_bytes(E, K);
+#define CGD_FUSED(RW, LAYOUT, CAST, LO)                                                                       \
+    hipLaunchKernelGGL((rank_kernel<RW, LAYOUT, true, CAST>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, \
+                       seg_cap, w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats,       \
+                       w.ticket, LO, fc, 1, nullptr, 0)
+    if (!layout) {
+        if (cast)
+            CGD_FUSED(1, false, true, none);
+        else
+            CGD_FUSED(1, false, false, none);
+    } else if (layout->R <= 64) {
+        if (cast)
+            CGD_FUSED(1, true, true, *layout);
+        else
+            CGD_FUSED(1, true, false, *layout);
+    } else {
+        if (cast)
+            CGD_FUSED(6, true, true, *layout);
+        else
+            CGD_FUSED(6, true, false, *layout);
+    }
+#undef CGD_FUSED
+    return hipGetLastError();
+}
+
 // The non-cached cast on dispatch: the plan (with the layout outputs when
 // `layout` is given), whose spare blocks pull x into the caches while it
 // runs when x fits there, then the cast to its rows, which then reads x from
@@ -1053,6 +1138,9 @@ static hipError_t launch_plan_and_cast(const void* x, int64_t T, int H, const in
                                        int fmt, void* recv_q, void* recv_s, int64_t cap, int32_t* expert_offset,
                                        int32_t* nrecv, int32_t* recv_src_idx, int32_t* dst_row, const DispatchWs& w,
                                        hipStream_t stream, const LayoutOut* layout) {
+    if (T > 0 && dispatch_fuses(T))  // one tile (decode): plan, cast and rows in one launch
+        return launch_fused(topk_idx, T, K, E, A, -1, x, H, recv_q, cap, expert_offset, nrecv, recv_src_idx, dst_row,
+                            nullptr, nullptr, w, stream, layout, fmt, recv_s);
     const int64_t xb = T * (int64_t)H * 2;
     hipError_t err = launch_rank(topk_idx, T, K, E, A, -1, cap, expert_offset, nrecv, dst_row, recv_src_idx, nullptr,
                                  nullptr, w, stream, layout, xb <= kPrefetchMaxBytes ? x : nullptr, xb);
@@ -1078,50 +1166,6 @@ hipError_t launch_layout_and_dispatch_cast_fp8(const void* x, int64_t T, int H, 
     const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
     return launch_plan_and_cast(x, T, H, topk_idx, K, E, A, fmt, recv_q, recv_s, cap, expert_offset, nrecv,
                                 recv_src_idx, dst_row, w, stream, &lo);
-}
-
-// Plan and bf16 apply of a batch of at most one tile in one launch (the FUSED
-// rank kernel); seg_cap >= 0 for the fixed-capacity packed layout; with
-// layout, get_dispatch_layout's outputs from the same launch.
-static hipError_t launch_fused(const int64_t* topk_idx, int64_t T, int K, int E, int A, int seg_cap, const void* x,
-                               int H, void* recv_x, int64_t cap, int32_t* expert_offset, int32_t* nrecv,
-                               int32_t* recv_src_idx,
-                               int32_t* dst_row, int32_t* packed_count, int32_t* stats, const DispatchWs& w,
-                               hipStream_t stream, const LayoutOut* layout = nullptr) {
-    int ebits = 0;
-    while ((1 << ebits) < E) ++ebits;
-    const int nvec = H / 8;
-    const int nchunk = (nvec + kWave - 1) / kWave;
-    // one block per CU where that leaves at most kFusedItems items per wave:
-    // every block plans the whole batch in LDS, so blocks sharing a CU would
-    // share its LDS bandwidth for that
-    const int64_t items = T * nchunk;
-    const int64_t per_block = (int64_t)kRankWaves * kFusedItems;
-    int64_t blocks = std::max<int64_t>(std::min<int64_t>((items + kRankWaves - 1) / kRankWaves, device_cus()),
-                                       (items + per_block - 1) / per_block);
-    // in a grid of several blocks the first block (the first two with the
-    // layout outputs, in a grid of three or more) moves no rows: the others
-    // hold every item
-    const int64_t need = (items + per_block - 1) / per_block;
-    if (blocks > 1) blocks = std::max<int64_t>(blocks, 1 + need);
-    if (blocks > 2 && layout) blocks = std::max<int64_t>(blocks, 2 + need);
-    const dim3 grid((unsigned)std::max<int64_t>(1, blocks)), block(kRankTile);
-    const LayoutOut none{1, 1, nullptr, nullptr, nullptr, nullptr};
-    const TileOut fc{dst_row, recv_src_idx, cap, reinterpret_cast<const uint4*>(x), nvec, nchunk,
-                     reinterpret_cast<uint4*>(recv_x)};
-    const size_t lds = rank_lds_bytes(E, K);
-#define CGD_FUSED(RW, LAYOUT, LO)                                                                                   \
-    hipLaunchKernelGGL((rank_kernel<RW, LAYOUT, true>), grid, block, lds, stream, topk_idx, T, K, E, ebits, A, seg_cap, \
-                       w.slot_pack, w.tile_base, expert_offset, nrecv, w.counts, packed_count, stats, w.ticket, LO, fc, \
-                       1, nullptr, 0)
-    if (!layout)
-        CGD_FUSED(1, false, none);
-    else if (layout->R <= 64)
-        CGD_FUSED(1, true, *layout);
-    else
-        CGD_FUSED(6, true, *layout);
-#undef CGD_FUSED
-    return hipGetLastError();
 }
 
 bool dispatch_fuses(int64_t T) { return T <= kRankTile; }
@@ -1150,9 +1194,9 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
                                   hipStream_t stream) {
     const DispatchWs w = dispatch_ws(workspace, T, K, E);
     const int64_t cap = (int64_t)E * expert_capacity;
-    if (fmt < 0 && dispatch_fuses(T))
+    if (dispatch_fuses(T) && (fmt < 0 || T > 0))  // one tile: plan (cast) and rows in one launch
         return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, cap, w.packed_offset, nullptr,
-                            recv_src_info, dst_row, packed_count, stats, w, stream);
+                            recv_src_info, dst_row, packed_count, stats, w, stream, nullptr, fmt, recv_s);
     // the bf16 row copy after the plan wants x in the caches at any size; the
     // cast only while x stays there (kPrefetchMaxBytes)
     const int64_t xb = T * (int64_t)H * 2;

@@ -220,10 +220,14 @@ def test_fp8_zero_tokens():
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T,K,E,R,H,A,extra,p_neg", [(100, 8, 256, 8, 1024, 1, 0, 0.0), (2049, 8, 256, 8, 384, 4, 37, 0.1),
                                                      (1100, 16, 512, 64, 256, 16, 0, 0.0),
-                                                     (4096, 8, 256, 8, 7168, 1, 0, 0.0)])
+                                                     (4096, 8, 256, 8, 7168, 1, 0, 0.0),
+                                                     # one tile: plan, cast and rows in one launch
+                                                     (200, 9, 384, 384, 128, 1, 5000, 0.05),
+                                                     (1, 8, 256, 8, 7168, 1, 0, 0.0)])
 def test_layout_and_dispatch_cast_parity(fmt, T, K, E, R, H, A, extra, p_neg):
     """layout_and_dispatch with the cast on the way (one call: the plan pulls x
-    into the caches, the cast reads it there): layout outputs, handle, aligned
+    into the caches, the cast reads it there; a batch of one tile casts in the
+    plan's own launch): layout outputs, handle, aligned
     counts and every received row's codes and scales as the oracle's; rows
     without data keep their sentinel bytes."""
     rng = np.random.default_rng(T + K + A)

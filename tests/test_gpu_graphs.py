@@ -68,7 +68,7 @@ def _normal_fp8_step(x, idx, wt, w, out):
 
 @pytest.mark.parametrize("kind,T", [("expert", 2500), ("small", 200), ("small_layout", 128), ("normal", 2500),
                                     ("normal", 100), ("layout", 2500), ("normal_whole", 2500), ("normal_whole", 200),
-                                    ("fp8_cast", 2500), ("normal_fp8", 2500), ("normal_fp8", 200)])
+                                    ("fp8_cast", 2500), ("fp8_cast", 200), ("normal_fp8", 2500), ("normal_fp8", 200)])
 def test_step_replays_from_a_captured_graph(kind, T):
     w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
     step = {"expert": _expert_step, "small": _small_step, "small_layout": _small_layout_step,

@@ -71,7 +71,7 @@ def test_packed_workload_parity(name, cap):
     say(f"[packed] {name}: ok")
 
 
-@pytest.mark.parametrize("T,H", [(128, 7168), (2500, 1024)])
+@pytest.mark.parametrize("T,H", [(128, 7168), (2500, 1024), (1, 7168), (256, 512)])
 def test_packed_fp8_cast(T, H):
     w = synth.WORKLOADS["decode"].replace(T=T, H=H)
     inp = synth.make_inputs(w, seed=1)
