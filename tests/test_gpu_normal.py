@@ -199,6 +199,43 @@ def test_normal_edge_case_parity(case):
             assert (host_bits(out)[itr.sum(axis=1) == 0] == 0).all()
 
 
+ONE_TILE_EDGE = {
+    "one_tile_duplicates": dict(T=200, K=8, E=8, R=2, H=64, dup=True),
+    "one_tile_neg_T=256": dict(T=256, K=6, E=96, R=12, H=136, p_neg=0.3),
+    "one_tile_all_minus_one": dict(T=100, K=4, E=16, R=4, H=64, p_neg=0.9),
+    "one_tile_R=1": dict(T=100, K=4, E=64, R=1, H=64),
+    "one_tile_H=8": dict(T=64, K=2, E=4, R=2, H=8),
+    "one_tile_R>64": dict(T=250, K=9, E=384, R=384, H=64, dup=True),
+    "one_tile_align16": dict(T=130, K=8, E=256, R=8, H=64, align=16),
+}
+
+
+@pytest.mark.parametrize("case", list(NORMAL_EDGE) + list(ONE_TILE_EDGE))
+def test_normal_edge_case_one_call(case):
+    """The edge cases through layout_and_normal_dispatch (layout, plan and
+    rows in one call; one launch up to 256 tokens): every output equals the
+    oracle's."""
+    spec = dict(NORMAL_EDGE.get(case) or ONE_TILE_EDGE[case])
+    align = spec.pop("align", 1)
+    say(f"[normal-edge, one call] {case}")
+    idx, x, wts = _edge(**spec)
+    E, R, K, H = spec["E"], spec["R"], spec["K"], spec["H"]
+    (ntpr, _, ntpe, itr, _), recv_x, ridx, rw, nre, h = cgd.layout_and_normal_dispatch(
+        dev_bf16(x), dev_i64(idx), dev_f32(wts), E, R, expert_alignment=align)
+    torch.cuda.synchronize()
+    ol = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), ol[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
+    o = oracle.dispatch_normal(x, ol[2], E, K, ol[1], idx, wts, align=align, cap=h.recv_capacity, hidden=H)
+    for got, key in ((h.rank_offset, "rank_offset"), (h.send_row, "send_row"), (h.recv_src_idx, "recv_src_idx"),
+                     (ridx, "recv_topk_idx"), (nre, "num_recv_tokens_per_expert")):
+        np.testing.assert_array_equal(got.cpu().numpy(), o[key], err_msg=key)
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), o["recv_topk_weights"].view(np.uint32))
+    data = o["recv_src_idx"] >= 0
+    np.testing.assert_array_equal(host_bits(recv_x)[data], o["recv_x"][data])
+
+
 def test_normal_without_topk_and_counts():
     idx, x, wts = _edge(T=700, K=6, E=48, R=6, H=72, seed=3, p_neg=0.2)
     _normal_and_check(x, idx, wts, 48, 6, with_topk=False, with_counts=False)
