@@ -330,3 +330,66 @@ def test_layout_and_normal_dispatch_cast_writes_the_callers_tuple(T, fmt):
     oq, osc = oracle.cast_to_fp8(x, fmt)
     np.testing.assert_array_equal(q.cpu().numpy(), oq)
     np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint8), osc.view(np.uint8))
+
+
+# Routing edge cases for the cast on dispatch (hidden 128 or 256); up to 256
+# tokens the plan, the cast and the rows take one launch.
+CAST_EDGE = {
+    "T=1": dict(T=1, K=8, E=256, R=8),
+    "one_tile_duplicates": dict(T=200, K=8, E=8, R=2, dup=True),
+    "duplicates_T=513": dict(T=513, K=8, E=8, R=2, dup=True),
+    "one_tile_all_minus_one": dict(T=100, K=4, E=16, R=4, p_neg=0.9),
+    "one_tile_R=E=384_K=9": dict(T=200, K=9, E=384, R=384),
+    "one_tile_align64_spare_rows": dict(T=100, K=4, E=512, R=8, align=64),
+    "one_tile_extra_capacity": dict(T=100, K=4, E=32, R=4, extra=300),
+    "one_tile_E=1": dict(T=100, K=1, E=1, R=1),
+    "align32_neg_T=333": dict(T=333, K=4, E=64, R=16, align=32, p_neg=0.2),
+}
+
+
+@pytest.mark.parametrize("fmt", [cgd.SCALE_F32, cgd.SCALE_UE8M0])
+@pytest.mark.parametrize("case", list(CAST_EDGE))
+def test_cast_on_dispatch_edge_cases(case, fmt):
+    """layout_and_dispatch with the cast over routing edge cases (repeated
+    experts, empty routings, R > 64, alignment padding, spare rows): layout,
+    handle and received codes and scales as the oracle's; rows without data
+    keep their sentinel bytes."""
+    spec = dict(CAST_EDGE[case])
+    T, K, E, R = spec["T"], spec["K"], spec["E"], spec["R"]
+    A, extra = spec.get("align", 1), spec.get("extra", 0)
+    H = 256 if T <= 256 else 128
+    rng = np.random.default_rng(T + 13 * K)
+    if spec.get("dup"):
+        idx = rng.integers(0, E, size=(T, K)).astype(np.int64)
+    else:
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+    if spec.get("p_neg"):
+        idx[rng.random((T, K)) < spec["p_neg"]] = -1
+    x = _x(T, H, seed=T + 17)
+    cap = cgd.dispatch_capacity(T, K, E, A) + extra
+    rq = torch.full((cap, H), 0xA5, dtype=torch.uint8, device=DEV)
+    rs = (torch.full((cap, H // 128), 0x5A, dtype=torch.uint8, device=DEV) if fmt == cgd.SCALE_UE8M0 else
+          torch.full((cap, H // 128), -7.0, dtype=torch.float32, device=DEV))
+    say(f"[fp8] cast on dispatch edge case {case} fmt={fmt}")
+    (ntpr, _, ntpe, itr, _), recv, nre, h = cgd.layout_and_dispatch(dev_bf16(x), dev_i64(idx), E, R,
+                                                                    expert_alignment=A, recv_capacity=cap,
+                                                                    recv_x=(rq, rs), cast_fp8=fmt)
+    torch.cuda.synchronize()
+    ol = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), ol[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
+    o = oracle.dispatch(None, idx, E, R, align=A, with_rows=False)
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    np.testing.assert_array_equal(h.expert_offset.cpu().numpy(), o["expert_offset"])
+    src = h.recv_src_idx.cpu().numpy()
+    np.testing.assert_array_equal(src[:len(o["recv_src_idx"])], o["recv_src_idx"])
+    assert (src[len(o["recv_src_idx"]):] == -1).all()
+    np.testing.assert_array_equal(nre.cpu().numpy(), np.diff(o["expert_offset"]))
+    oq, osc = oracle.cast_to_fp8(x, fmt)
+    _check_rows(recv, oq, osc, o["dst_row"])
+    empty = torch.from_numpy(np.flatnonzero(src < 0)).to(DEV)
+    if empty.numel():
+        assert (rq.index_select(0, empty) == 0xA5).all()
+        sv = rs.index_select(0, empty)
+        assert ((sv == 0x5A) if fmt == cgd.SCALE_UE8M0 else (sv == -7.0)).all()
