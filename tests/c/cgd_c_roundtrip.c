@@ -3,8 +3,9 @@
  * infrastructure, not part of the library: tests/test_gpu_c_program.py
  * builds it with gcc and runs it. Inputs come from the seeded generator
  * (libsynth); every output is checked against the CPU oracle (liboracle):
- * layout, handle and received rows bit for bit (expert-granular, and
- * rank-granular in bf16 and with the FP8 cast), the combine within
+ * layout, handle and received rows bit for bit (expert-granular, also with
+ * the FP8 cast on dispatch, and rank-granular in bf16 and with the FP8
+ * cast), the combine within
  * 1e-2 of the sum of its terms' magnitudes with > 99 % of values
  * bit-identical. Exit status 0 and a last line "ok" when every check passes. */
 #include <math.h>
@@ -177,6 +178,38 @@ static void run_case(const char* name, int64_t T, int K, int E, int R, int H, in
         if (o_src[r] >= 0) rows_ok &= !memcmp(g_recv + r * H, o_recv + r * H, sizeof(uint16_t) * (size_t)H);
     expect(counts_ok, "num_recv_tokens_per_expert", name);
     expect(rows_ok, "received rows", name);
+
+    /* the same call with the FP8 cast on the way (UE8M0 scales): handle as
+     * above, every received row the oracle's per-token cast of its token */
+    if (H % 128 == 0) {
+        const int nsb = H / 128;
+        uint8_t* o_q = malloc((size_t)(T * H));
+        uint8_t* o_s = malloc((size_t)(T * nsb));
+        if (oracle_cast_to_fp8(x, T, H, CGD_SCALE_UE8M0, o_q, o_s) != 0) exit(5);
+        void* d_rq = dev_alloc((size_t)(cap * H));
+        void* d_rs = dev_alloc((size_t)(cap * nsb));
+        CGD_OK_(cgd_layout_and_dispatch_cast_fp8(d_x, T, H, d_idx, K, E, R, A, CGD_SCALE_UE8M0, d_rq, d_rs, cap,
+                                                 d_ntpr, d_ntpe, d_itr, d_off, d_counts, d_src, d_dst, d_ws, ws_bytes,
+                                                 stream));
+        HIP_OK(hipStreamSynchronize(stream));
+        int32_t* f_dst = host_copy(d_dst, sizeof(int32_t) * (size_t)TK);
+        int32_t* f_src = host_copy(d_src, sizeof(int32_t) * (size_t)cap);
+        uint8_t* f_q = host_copy(d_rq, (size_t)(cap * H));
+        uint8_t* f_s = host_copy(d_rs, (size_t)(cap * nsb));
+        expect(!memcmp(f_dst, o_dst, sizeof(int32_t) * (size_t)TK), "FP8 dst_row", name);
+        expect(!memcmp(f_src, o_src, sizeof(int32_t) * (size_t)cap), "FP8 recv_src_idx", name);
+        int fp8_ok = 1;
+        for (int64_t i = 0; i < TK; ++i) {
+            const int32_t r = o_dst[i];
+            if (r < 0) continue;
+            fp8_ok &= !memcmp(f_q + (int64_t)r * H, o_q + (i / K) * H, (size_t)H);
+            fp8_ok &= !memcmp(f_s + (int64_t)r * nsb, o_s + (i / K) * nsb, (size_t)nsb);
+        }
+        expect(fp8_ok, "received FP8 codes and UE8M0 scales", name);
+        printf("[%s] cast on dispatch: FP8 rows as the oracle's cast\n", name);
+        free(f_dst); free(f_src); free(f_q); free(f_s); free(o_q); free(o_s);
+        HIP_OK(hipFree(d_rq)); HIP_OK(hipFree(d_rs));
+    }
 
     /* combine of independent expert outputs */
     uint16_t* y = malloc(sizeof(uint16_t) * (size_t)(cap * H));

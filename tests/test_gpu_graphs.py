@@ -4,7 +4,8 @@ new inputs: every replay must equal the same step run eagerly on those inputs
 apply; the one-launch small-batch dispatch, with and without the layout
 outputs; rank-granular step with the fused layout + plan; the one-call
 layout + dispatch of larger batches, bf16, rank-granular and with the FP8
-cast, whose plans pull x toward the caches)."""
+cast, whose plans pull x toward the caches; the one-launch FP8 forms of
+small batches, packed included)."""
 import pytest
 import torch
 
@@ -66,14 +67,23 @@ def _normal_fp8_step(x, idx, wt, w, out):
             q.view(torch.uint8) * data.to(torch.uint8), torch.where(data, sc, torch.zeros_like(sc))]
 
 
+def _packed_fp8_step(x, idx, wt, w, out):
+    (q, sc), count, h = cgd.low_latency_dispatch(x, idx, w.E, w.R, expert_capacity=64, use_fp8=True,
+                                                 scale_format=cgd.SCALE_UE8M0)
+    data = (h.recv_src_info.reshape(-1) >= 0).unsqueeze(1)  # rows past each count are not written
+    return [count, h.recv_src_info, h.dst_row, q.view(torch.uint8).reshape(data.shape[0], -1) * data.to(torch.uint8),
+            sc.reshape(data.shape[0], -1) * data.to(torch.uint8)]
+
+
 @pytest.mark.parametrize("kind,T", [("expert", 2500), ("small", 200), ("small_layout", 128), ("normal", 2500),
                                     ("normal", 100), ("layout", 2500), ("normal_whole", 2500), ("normal_whole", 200),
-                                    ("fp8_cast", 2500), ("fp8_cast", 200), ("normal_fp8", 2500), ("normal_fp8", 200)])
+                                    ("fp8_cast", 2500), ("fp8_cast", 200), ("normal_fp8", 2500), ("normal_fp8", 200),
+                                    ("packed_fp8", 128)])
 def test_step_replays_from_a_captured_graph(kind, T):
     w = synth.WORKLOADS["prefill"].replace(T=T, H=1024)
     step = {"expert": _expert_step, "small": _small_step, "small_layout": _small_layout_step,
             "normal": _normal_step, "layout": _layout_step, "normal_whole": _normal_whole_step,
-            "fp8_cast": _fp8_step, "normal_fp8": _normal_fp8_step}[kind]
+            "fp8_cast": _fp8_step, "normal_fp8": _normal_fp8_step, "packed_fp8": _packed_fp8_step}[kind]
     inputs = [synth.make_inputs(w, seed=s) for s in range(5)]
     sx = dev_bf16(inputs[0]["x"])
     sidx = dev_i64(inputs[0]["topk_idx"])
