@@ -388,8 +388,10 @@ class NormalPath(_Path):
 
 
 class PackedPath(_Path):
-    """layout, packed (fixed-capacity) dispatch, combine over the packed rows."""
-    labels = ("layout", "dispatch", "combine")
+    """layout and packed (fixed-capacity) dispatch in one call
+    (layout_and_low_latency_dispatch; one launch up to 256 tokens), combine
+    over the packed rows."""
+    labels = ("dispatch", "combine")
     dispatch_labels = ("dispatch",)
     # the packed dispatch is the plan and the apply: its traffic is their sum
     data_kernels = (("dispatch", "dispatch", ("rank_kernel", "finalize_kernel", "scatter_kernel",
@@ -414,32 +416,27 @@ class PackedPath(_Path):
         self.count = [None] * len(sets)
         self.handles = [None] * len(sets)
 
+    def _dispatch(self, i):
+        cgd, w = self.cgd, self.w
+        if self.fmt is None:
+            return cgd.layout_and_low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
+                                                       out=self.recv)
+        return cgd.layout_and_low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
+                                                   use_fp8=True, scale_format=self.fmt, out=self.recv_q)
+
     def step(self, i, ev=None):
         cgd, w = self.cgd, self.w
         self._rec(ev, 0)
-        cgd.get_dispatch_layout(self.idx[i], w.E, w.R)
+        _, _, count, h = self._dispatch(i)
         self._rec(ev, 1)
-        if self.fmt is None:
-            _, count, h = cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
-                                                   out=self.recv)
-        else:
-            _, count, h = cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
-                                                   use_fp8=True, scale_format=self.fmt, out=self.recv_q)
-        self._rec(ev, 2)
         cgd.low_latency_combine(self.recv, self.wt[i], h, out=self.out)
-        self._rec(ev, 3)
+        self._rec(ev, 2)
         self.count[i] = count
         self.handles[i] = h
 
     def graph_calls(self):
         cgd, w = self.cgd, self.w
-        if self.fmt is None:
-            disp = lambda i: cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
-                                                      out=self.recv)
-        else:
-            disp = lambda i: cgd.low_latency_dispatch(self.x[i], self.idx[i], w.E, w.R, expert_capacity=self.cap,
-                                                      use_fp8=True, scale_format=self.fmt, out=self.recv_q)
-        return {"layout": lambda i: cgd.get_dispatch_layout(self.idx[i], w.E, w.R), "dispatch": disp,
+        return {"layout": lambda i: cgd.get_dispatch_layout(self.idx[i], w.E, w.R), "dispatch": self._dispatch,
                 "combine": lambda i: cgd.low_latency_combine(self.recv, self.wt[i], self.handles[i], out=self.out)}
 
     def check(self, i):
@@ -463,6 +460,7 @@ class PackedPath(_Path):
 
     def describe(self):
         return {"path": f"packed (fixed capacity {self.cap} rows per expert)",
+                "dispatch": "layout_and_low_latency_dispatch (layout, plan and rows; one launch up to 256 tokens)",
                 "experts": "identity (combine reads the packed rows)"}
 
 

@@ -47,7 +47,7 @@ __all__ = ["get_dispatch_layout", "dispatch", "dispatch_plan", "dispatch_apply",
            "CgdError", "library_path", "dispatch_capacity", "load", "normal_capacity", "NormalHandle",
            "normal_dispatch", "normal_dispatch_plan", "normal_dispatch_apply", "NormalPlan", "normal_combine",
            "per_token_cast_to_fp8", "per_token_cast_back", "SCALE_F32", "SCALE_POW2", "SCALE_UE8M0",
-           "PackedHandle", "low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_",
+           "PackedHandle", "low_latency_dispatch", "layout_and_low_latency_dispatch", "low_latency_combine", "layout_and_dispatch_plan", "copy_",
            "layout_and_normal_dispatch_plan", "layout_and_dispatch", "normal_workspace_bytes",
            "layout_and_normal_workspace_bytes", "empty_", "layout_and_dispatch_noalloc", "init",
            "layout_and_normal_dispatch"]
@@ -128,6 +128,12 @@ def configure(lib):
     lib.cgd_dispatch_packed_cast_fp8.restype = i32
     lib.cgd_dispatch_packed_cast_fp8.argtypes = [vp, i64, i32, vp, i32, i32, i32, i64, i32, vp, vp, vp, vp, vp, vp,
                                                  vp, sz, vp]
+    lib.cgd_layout_and_dispatch_packed.restype = i32
+    lib.cgd_layout_and_dispatch_packed.argtypes = [vp, i64, i32, vp, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp,
+                                                   vp, vp, sz, vp]
+    lib.cgd_layout_and_dispatch_packed_cast_fp8.restype = i32
+    lib.cgd_layout_and_dispatch_packed_cast_fp8.argtypes = [vp, i64, i32, vp, i32, i32, i32, i64, i32, vp, vp, vp,
+                                                            vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.cgd_dispatch_cached.restype = i32
     lib.cgd_dispatch_cached.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp]
     lib.cgd_combine.restype = i32
@@ -1208,6 +1214,23 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: i
     expert). Returns (packed_recv_x, packed_recv_count int32 [E], PackedHandle);
     packed_recv_x is bf16 [E, cap, H], or with use_fp8 the tuple
     (codes float8_e4m3fn [E, cap, H], scales [E, cap, H/128])."""
+    return _low_latency_dispatch(x, topk_idx, num_experts, num_ranks, expert_capacity, use_fp8, scale_format,
+                                 cumulative_local_expert_recv_stats, out, False)
+
+
+def layout_and_low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                                    expert_capacity: int | None = None, use_fp8: bool = False,
+                                    scale_format: int = SCALE_F32,
+                                    cumulative_local_expert_recv_stats: torch.Tensor | None = None, out=None):
+    """get_dispatch_layout and low_latency_dispatch in one call (one launch up
+    to 256 tokens). -> ((num_tokens_per_rank, None, num_tokens_per_expert,
+    is_token_in_rank, None), packed_recv_x, packed_recv_count, PackedHandle)."""
+    return _low_latency_dispatch(x, topk_idx, num_experts, num_ranks, expert_capacity, use_fp8, scale_format,
+                                 cumulative_local_expert_recv_stats, out, True)
+
+
+def _low_latency_dispatch(x, topk_idx, num_experts, num_ranks, expert_capacity, use_fp8, scale_format,
+                          cumulative_local_expert_recv_stats, out, with_layout):
     lib = load()
     _dev_tensor(x, "x", torch.bfloat16, 2)
     _dev_tensor(topk_idx, "topk_idx", torch.int64, 2)
@@ -1227,26 +1250,49 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: i
         count = torch.empty(E, dtype=torch.int32, device=dev)
         info = torch.empty((E, max(cap, 0)), dtype=torch.int32, device=dev)
         dst = torch.empty((T, K), dtype=torch.int32, device=dev)
-        ws = _workspace(dev, "dispatch", lib.cgd_packed_workspace_bytes(T, K, E))
+        if with_layout:
+            R = num_ranks
+            ntpr = torch.empty(R, dtype=torch.int32, device=dev)
+            ntpe = torch.empty(E, dtype=torch.int32, device=dev)
+            itr = torch.empty((T, R), dtype=torch.bool, device=dev)
+            ws = _workspace(dev, "dispatch", lib.cgd_dispatch_workspace_bytes(T, K, E, R))
+        else:
+            ws = _workspace(dev, "dispatch", lib.cgd_packed_workspace_bytes(T, K, E))
         if use_fp8:
             if out is None:
                 q, sc = _fp8_empty(E * cap, H, scale_format, dev)
             else:
                 q, sc = _packed_fp8_out(out, E, cap, H, scale_format, dev)
-            _check("cgd_dispatch_packed_cast_fp8",
-                   lib.cgd_dispatch_packed_cast_fp8(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap, scale_format,
-                                                    _ptr(q), _ptr(sc), _ptr(count), _ptr(info), _ptr(dst), _ptr(st),
-                                                    _ptr(ws), ws.numel(), _stream(dev)))
+            if with_layout:
+                _check("cgd_layout_and_dispatch_packed_cast_fp8",
+                       lib.cgd_layout_and_dispatch_packed_cast_fp8(
+                           _ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap, scale_format, _ptr(q), _ptr(sc),
+                           _ptr(count), _ptr(info), _ptr(dst), _ptr(st), _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(ws),
+                           ws.numel(), _stream(dev)))
+            else:
+                _check("cgd_dispatch_packed_cast_fp8",
+                       lib.cgd_dispatch_packed_cast_fp8(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap,
+                                                        scale_format, _ptr(q), _ptr(sc), _ptr(count), _ptr(info),
+                                                        _ptr(dst), _ptr(st), _ptr(ws), ws.numel(), _stream(dev)))
             recv = (q.view(E, cap, H), sc.view(E, cap, H // 128))
         else:
             recv = torch.empty((E, cap, H), dtype=torch.bfloat16, device=dev) if out is None else out
             _dev_tensor(recv, "out", torch.bfloat16, 3)
             if recv.shape != (E, cap, H):
                 raise ValueError("out must be [num_experts, expert_capacity, hidden]")
-            _check("cgd_dispatch_packed",
-                   lib.cgd_dispatch_packed(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap, _ptr(recv),
-                                           _ptr(count), _ptr(info), _ptr(dst), _ptr(st), _ptr(ws), ws.numel(),
-                                           _stream(dev)))
+            if with_layout:
+                _check("cgd_layout_and_dispatch_packed",
+                       lib.cgd_layout_and_dispatch_packed(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap,
+                                                          _ptr(recv), _ptr(count), _ptr(info), _ptr(dst), _ptr(st),
+                                                          _ptr(ntpr), _ptr(ntpe), _ptr(itr), _ptr(ws), ws.numel(),
+                                                          _stream(dev)))
+            else:
+                _check("cgd_dispatch_packed",
+                       lib.cgd_dispatch_packed(_ptr(x), T, H, _ptr(topk_idx), K, E, num_ranks, cap, _ptr(recv),
+                                               _ptr(count), _ptr(info), _ptr(dst), _ptr(st), _ptr(ws), ws.numel(),
+                                               _stream(dev)))
+    if with_layout:
+        return (ntpr, None, ntpe, itr, None), recv, count, PackedHandle(info, dst, E, cap)
     return recv, count, PackedHandle(info, dst, E, cap)
 
 

@@ -905,6 +905,54 @@ int cgd_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, 
     return CGD_OK;
 }
 
+int cgd_layout_and_dispatch_packed(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                   int num_topk, int num_experts, int num_ranks, int64_t expert_capacity,
+                                   void* packed_recv_x, int32_t* packed_recv_count, int32_t* recv_src_info,
+                                   int32_t* dst_row, int32_t* cumulative_recv_stats, int32_t* num_tokens_per_rank,
+                                   int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_packed_args(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks, expert_capacity,
+                               packed_recv_x, packed_recv_count, recv_src_info, dst_row, cumulative_recv_stats,
+                               workspace, workspace_bytes);
+    if (rc) return rc;
+    if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
+        return rc;
+    if ((rc = check_dispatch_workspace(num_tokens, num_topk, num_experts, num_ranks, workspace, workspace_bytes)))
+        return rc;
+    hipError_t err = cgd::launch_layout_and_dispatch_packed(
+        x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks, (int)expert_capacity, -1, packed_recv_x,
+        nullptr, packed_recv_count, recv_src_info, dst_row, cumulative_recv_stats, num_tokens_per_rank,
+        num_tokens_per_expert, is_token_in_rank, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "layout and packed dispatch launch");
+    return CGD_OK;
+}
+
+int cgd_layout_and_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                            int num_topk, int num_experts, int num_ranks, int64_t expert_capacity,
+                                            int scale_format, void* packed_recv_x_fp8, void* packed_recv_scales,
+                                            int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
+                                            int32_t* cumulative_recv_stats, int32_t* num_tokens_per_rank,
+                                            int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_fp8(hidden, scale_format);
+    if (rc) return rc;
+    if ((rc = check_packed_args(x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks, expert_capacity,
+                                packed_recv_x_fp8, packed_recv_count, recv_src_info, dst_row, cumulative_recv_stats,
+                                workspace, workspace_bytes)))
+        return rc;
+    if ((rc = check_scales(packed_recv_scales, 0, 0, scale_format, expert_capacity > 0))) return rc;
+    if ((rc = check_layout_outputs(num_tokens, num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank)))
+        return rc;
+    if ((rc = check_dispatch_workspace(num_tokens, num_topk, num_experts, num_ranks, workspace, workspace_bytes)))
+        return rc;
+    hipError_t err = cgd::launch_layout_and_dispatch_packed(
+        x, num_tokens, hidden, topk_idx, num_topk, num_experts, num_ranks, (int)expert_capacity, scale_format,
+        packed_recv_x_fp8, packed_recv_scales, packed_recv_count, recv_src_info, dst_row, cumulative_recv_stats,
+        num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank, workspace, stream);
+    if (err != hipSuccess) return hip_fail(err, "layout and packed FP8 dispatch launch");
+    return CGD_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -1188,27 +1188,45 @@ hipError_t launch_layout_and_dispatch_fused(const void* x, int64_t T, int H, con
                         nullptr, nullptr, w, stream, &lo);
 }
 
-hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+static hipError_t packed_launches(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
                                   int expert_capacity, int fmt, void* recv_x, void* recv_s, int32_t* packed_count,
-                                  int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
-                                  hipStream_t stream) {
-    const DispatchWs w = dispatch_ws(workspace, T, K, E);
+                                  int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, const DispatchWs& w,
+                                  hipStream_t stream, const LayoutOut* layout) {
     const int64_t cap = (int64_t)E * expert_capacity;
     if (dispatch_fuses(T) && (fmt < 0 || T > 0))  // one tile: plan (cast) and rows in one launch
         return launch_fused(topk_idx, T, K, E, 1, expert_capacity, x, H, recv_x, cap, w.packed_offset, nullptr,
-                            recv_src_info, dst_row, packed_count, stats, w, stream, nullptr, fmt, recv_s);
+                            recv_src_info, dst_row, packed_count, stats, w, stream, layout, fmt, recv_s);
     // the bf16 row copy after the plan wants x in the caches at any size; the
     // cast only while x stays there (kPrefetchMaxBytes)
     const int64_t xb = T * (int64_t)H * 2;
     const void* px = (fmt < 0 || xb <= kPrefetchMaxBytes) ? x : nullptr;
     hipError_t err = launch_rank(topk_idx, T, K, E, 1, expert_capacity, cap, w.packed_offset, nullptr, dst_row,
-                                 recv_src_info, packed_count, stats, w, stream, nullptr, px, xb);
+                                 recv_src_info, packed_count, stats, w, stream, layout, px, xb);
     if (err != hipSuccess) return err;
     if (fmt < 0)
         launch_scatter(T, K, stream, x, H / 8, dst_row, cap, recv_x, no_side(), true);
     else
         launch_scatter_cast(x, T, H, K, fmt, dst_row, cap, recv_x, recv_s, stream);
     return hipGetLastError();
+}
+
+hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                  int expert_capacity, int fmt, void* recv_x, void* recv_s, int32_t* packed_count,
+                                  int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
+                                  hipStream_t stream) {
+    return packed_launches(x, T, H, topk_idx, K, E, expert_capacity, fmt, recv_x, recv_s, packed_count,
+                           recv_src_info, dst_row, stats, dispatch_ws(workspace, T, K, E), stream, nullptr);
+}
+
+hipError_t launch_layout_and_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                             int R, int expert_capacity, int fmt, void* recv_x, void* recv_s,
+                                             int32_t* packed_count, int32_t* recv_src_info, int32_t* dst_row,
+                                             int32_t* stats, int32_t* ntpr, int32_t* ntpe, uint8_t* itr,
+                                             void* workspace, hipStream_t stream) {
+    const DispatchWs w = dispatch_ws(workspace, T, K, E);
+    const LayoutOut lo{R, E / R, ntpr, ntpe, itr, w.rank_part};
+    return packed_launches(x, T, H, topk_idx, K, E, expert_capacity, fmt, recv_x, recv_s, packed_count,
+                           recv_src_info, dst_row, stats, w, stream, &lo);
 }
 
 hipError_t launch_dispatch_cached(const void* x, int64_t T, int H, int K, const int32_t* dst_row, void* recv_x,

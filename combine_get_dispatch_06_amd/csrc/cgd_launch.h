@@ -138,6 +138,13 @@ hipError_t launch_dispatch_packed(const void* x, int64_t T, int H, const int64_t
                                   int expert_capacity, int fmt, void* recv_x, void* recv_s, int32_t* packed_count,
                                   int32_t* recv_src_info, int32_t* dst_row, int32_t* stats, void* workspace,
                                   hipStream_t stream);
+// The same with get_dispatch_layout's outputs from the plan's pass over the
+// routing (workspace of dispatch_workspace_bytes(T, K, E, R)).
+hipError_t launch_layout_and_dispatch_packed(const void* x, int64_t T, int H, const int64_t* topk_idx, int K, int E,
+                                             int R, int expert_capacity, int fmt, void* recv_x, void* recv_s,
+                                             int32_t* packed_count, int32_t* recv_src_info, int32_t* dst_row,
+                                             int32_t* stats, int32_t* ntpr, int32_t* ntpe, uint8_t* itr,
+                                             void* workspace, hipStream_t stream);
 
 // after_plan: the rows follow a plan launch that pulled x toward the caches
 // (the non-cached dispatch), which takes another launch shape.

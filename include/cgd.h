@@ -471,6 +471,31 @@ int cgd_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, 
                                  int32_t* cumulative_recv_stats, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
+/* cgd_get_dispatch_layout and the packed dispatch in one call: the layout
+ * outputs (as cgd_get_dispatch_layout; no layout workspace is needed) come
+ * from the plan's pass over the routing, as in cgd_layout_and_dispatch (the
+ * low-latency dispatch of the legacy tests, which follows the layout call of
+ * the same routing); a batch of at most 256 tokens takes one launch.
+ *   num_tokens_per_rank, num_tokens_per_expert, is_token_in_rank
+ *                           out, as cgd_get_dispatch_layout
+ *   workspace               >= cgd_dispatch_workspace_bytes(num_tokens, num_topk,
+ *                           num_experts, num_ranks), rules as the dispatch one
+ * Everything else as cgd_dispatch_packed / cgd_dispatch_packed_cast_fp8. */
+int cgd_layout_and_dispatch_packed(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                   int num_topk, int num_experts, int num_ranks, int64_t expert_capacity,
+                                   void* packed_recv_x, int32_t* packed_recv_count, int32_t* recv_src_info,
+                                   int32_t* dst_row, int32_t* cumulative_recv_stats, int32_t* num_tokens_per_rank,
+                                   int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+int cgd_layout_and_dispatch_packed_cast_fp8(const void* x, int64_t num_tokens, int hidden, const int64_t* topk_idx,
+                                            int num_topk, int num_experts, int num_ranks, int64_t expert_capacity,
+                                            int scale_format, void* packed_recv_x_fp8, void* packed_recv_scales,
+                                            int32_t* packed_recv_count, int32_t* recv_src_info, int32_t* dst_row,
+                                            int32_t* cumulative_recv_stats, int32_t* num_tokens_per_rank,
+                                            int32_t* num_tokens_per_expert, uint8_t* is_token_in_rank,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* get_dispatch_layout and cgd_normal_dispatch_plan in one launch: the plan
  * needs only is_token_in_rank (and the per-expert counts for the aligned
  * receive counts), which the layout computes from the same tile of topk_idx

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
         "cgd_layout_and_dispatch", "cgd_empty", "cgd_layout_and_dispatch_noalloc",
         "cgd_layout_and_normal_workspace_bytes", "cgd_layout_and_normal_dispatch_plan", "cgd_init",
         "cgd_dispatch_cast_fp8", "cgd_layout_and_dispatch_cast_fp8", "cgd_layout_and_normal_dispatch",
-        "cgd_layout_and_normal_dispatch_cast_fp8",
+        "cgd_layout_and_normal_dispatch_cast_fp8", "cgd_layout_and_dispatch_packed",
+        "cgd_layout_and_dispatch_packed_cast_fp8",
     ])
 
 
@@ -310,6 +311,35 @@ def test_packed_entry_points_reject_bad_arguments():
                                             None) == -1
     assert lib.cgd_dispatch_packed_cast_fp8(f, 128, 7168, f, 8, 256, 16, 128, 0, f, None, f, f, f, None, f, 1 << 20,
                                             None) == -1
+    assert lib.cgd_last_error()
+
+
+def test_layout_and_packed_entry_points_reject_bad_arguments():
+    """The layout form of the packed dispatch checks the layout outputs and
+    needs the dispatch workspace of its rank count (larger than the packed
+    one once the batch has several tiles); nothing is launched."""
+    lib = cgd.load()
+    f = _vp(FAKE)
+    T, K, E, R = 4096, 8, 256, 16
+    small = lib.cgd_packed_workspace_bytes(T, K, E)
+    need = lib.cgd_dispatch_workspace_bytes(T, K, E, R)
+    assert need > small
+    # x, T, H, idx, K, E, R, cap, recv, count, info, dst, stats, ntpr, ntpe, itr, ws, wsb
+    assert lib.cgd_layout_and_dispatch_packed(f, T, 7168, f, K, E, R, 64, f, f, f, f, None, f, f, f, f, small,
+                                              None) == -3
+    assert lib.cgd_layout_and_dispatch_packed(f, T, 7168, f, K, E, R, 64, f, f, f, f, None, None, f, f, f, need,
+                                              None) == -1
+    assert lib.cgd_layout_and_dispatch_packed(f, T, 7168, f, K, E, R, 64, f, f, f, f, None, f, f, None, f, need,
+                                              None) == -1
+    assert lib.cgd_layout_and_dispatch_packed(f, T, 7168, f, K, E, R, -1, f, f, f, f, None, f, f, f, f, need,
+                                              None) == -2
+    # ... scale_format, codes, scales, count, info, dst, stats, ntpr, ntpe, itr, ws, wsb
+    assert lib.cgd_layout_and_dispatch_packed_cast_fp8(f, T, 7000, f, K, E, R, 64, 0, f, f, f, f, f, None, f, f, f,
+                                                       f, need, None) == -1
+    assert lib.cgd_layout_and_dispatch_packed_cast_fp8(f, T, 7168, f, K, E, R, 64, 0, f, f, f, f, f, None, f, None,
+                                                       f, f, need, None) == -1
+    assert lib.cgd_layout_and_dispatch_packed_cast_fp8(f, T, 7168, f, K, E, R, 64, 0, f, f, f, f, f, None, f, f, f,
+                                                       f, small, None) == -3
     assert lib.cgd_last_error()
 
 

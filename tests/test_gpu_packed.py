@@ -150,3 +150,58 @@ def test_decode_step_replays_from_a_captured_graph():
         o = oracle.dispatch_packed(None, inp["topk_idx"], w.E, w.R, cap)
         np.testing.assert_array_equal(static_out[6].cpu().numpy(), o["dst_row"])
     say("[packed] graph replays ok")
+
+
+@pytest.mark.parametrize("name,T,H,cap,fp8,dup", [("decode", None, None, None, None, False),
+                                                  ("decode", None, None, None, cgd.SCALE_UE8M0, False),
+                                                  ("tiny", None, None, None, None, False),
+                                                  ("prefill", 2500, 1024, 300, None, False),
+                                                  ("prefill", 2500, 1024, 300, cgd.SCALE_F32, False),
+                                                  ("edge", 200, 256, 30, cgd.SCALE_POW2, True),
+                                                  ("edge", 700, 128, 40, None, True)])
+def test_layout_and_packed_dispatch(name, T, H, cap, fp8, dup):
+    """layout_and_low_latency_dispatch: the layout outputs equal the oracle's
+    get_dispatch_layout, the packed handle and rows (or FP8 codes and scales)
+    the oracle's packed dispatch (one launch up to 256 tokens; repeated
+    experts overflow the capacity in the edge cases)."""
+    if name == "edge":
+        rng = np.random.default_rng(T)
+        E, R, K = 16, 4, 6
+        idx = rng.integers(0, E, (T, K)).astype(np.int64) if dup else \
+            np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int64)
+        idx[rng.random((T, K)) < 0.1] = -1
+        x = synth.normal_bf16(synth.stream_key(T, 96, 1), T * H).reshape(T, H)
+    else:
+        w = synth.WORKLOADS[name]
+        w = w.replace(T=T or w.T, H=H or w.H)
+        inp = synth.make_inputs(w, seed=2)
+        idx, x, E, R = inp["topk_idx"], inp["x"], w.E, w.R
+        T, H = w.T, w.H
+    cap = cap or T
+    say(f"[packed] layout + packed dispatch {name} T={T} H={H} cap={cap} fp8={fp8}")
+    x_dev = dev_bf16(x)
+    if fp8 is None:
+        lay, recv, count, h = cgd.layout_and_low_latency_dispatch(x_dev, dev_i64(idx), E, R, expert_capacity=cap)
+    else:
+        lay, recv, count, h = cgd.layout_and_low_latency_dispatch(x_dev, dev_i64(idx), E, R, expert_capacity=cap,
+                                                                  use_fp8=True, scale_format=fp8)
+    torch.cuda.synchronize()
+    ntpr, _, ntpe, itr, _ = lay
+    ol = oracle.layout(idx, E, R)
+    np.testing.assert_array_equal(ntpr.cpu().numpy(), ol[0])
+    np.testing.assert_array_equal(ntpe.cpu().numpy(), ol[1])
+    np.testing.assert_array_equal(itr.cpu().numpy(), ol[2])
+    o = oracle.dispatch_packed(None, idx, E, R, cap)
+    np.testing.assert_array_equal(h.dst_row.cpu().numpy(), o["dst_row"])
+    np.testing.assert_array_equal(count.cpu().numpy(), o["packed_recv_count"])
+    np.testing.assert_array_equal(h.recv_src_info.cpu().numpy(), o["recv_src_info"])
+    if fp8 is None:
+        _check_packed_rows(recv, x_dev, o["dst_row"])
+    else:
+        q, sc = recv
+        oq, osc = oracle.cast_to_fp8(x, fp8)
+        sel_t, sel_k = np.nonzero(o["dst_row"] >= 0)
+        rows = o["dst_row"][sel_t, sel_k]
+        np.testing.assert_array_equal(q.view(torch.uint8).reshape(-1, H).cpu().numpy()[rows], oq[sel_t])
+        np.testing.assert_array_equal(sc.reshape(-1, H // 128).cpu().numpy()[rows].view(np.uint8),
+                                      osc[sel_t].view(np.uint8))
