@@ -173,7 +173,7 @@ class ExpertPath(_Path):
             self.recv_q = (torch.empty((cap, w.H), dtype=torch.uint8, device=dev).view(torch.float8_e4m3fn),
                            torch.empty((cap, w.H // 128), dtype=torch.uint8 if fmt == 2 else torch.float32,
                                        device=dev))
-        self.one_launch = fmt is None and w.T <= 256
+        self.one_launch = w.T <= 256  # plan (cast) and rows in one launch
         self.split_labels = ("layout_and_plan", "dispatch_apply", "combine")
         self.labels = ("dispatch", "combine")
         self.dispatch_labels = ("dispatch",)
@@ -252,7 +252,9 @@ class ExpertPath(_Path):
         return algorithmic_bytes(self.w, n) if self.fmt is None else algorithmic_bytes_fp8(self.w, n, self.fmt)
 
     def describe(self):
-        return {"dispatch": ("layout_and_dispatch (one launch: layout + plan + rows)" if self.one_launch else
+        return {"dispatch": (("layout_and_dispatch (one launch: layout + plan + rows)" if self.fmt is None else
+                              "layout_and_dispatch with the cast (one launch: layout + plan + cast rows)")
+                             if self.one_launch else
                              "layout_and_dispatch (layout + plan with x pulled toward the caches, then the rows)"
                              if self.fmt is None else
                              "layout_and_dispatch with the cast (layout + plan with x pulled toward the caches, "
